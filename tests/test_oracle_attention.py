@@ -1,0 +1,206 @@
+"""Pins of the oracle's attention steps and composed paths.
+
+Anchor: torch's scaled_dot_product_attention in float64 on the CPU (a library
+routine) with explicit boolean or additive masks, plus special cases (constant
+values, a single visible key, constant CIS)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+
+def _sdpa(q, k, v, mask, scale):
+    """q [H, D]; k, v [L, H, D] (already expanded per query head); mask [H, L]."""
+    qt = torch.from_numpy(q)[:, None, :]                      # [H, 1, D]
+    kt = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))   # [H, L, D]
+    vt = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))
+    m = torch.from_numpy(mask)[:, None, :]
+    return F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)[:, 0].numpy()
+
+
+def _expand(x, G):
+    return np.repeat(x, G, axis=1)
+
+
+def _case(rng, L, H=8, H_kv=2, D=32):
+    q = rng.standard_normal((H, D))
+    k = rng.standard_normal((L, H_kv, D))
+    v = rng.standard_normal((L, H_kv, D))
+    return q, k, v
+
+
+@pytest.mark.parametrize("L,t", [(1, 0), (64, 63), (200, 150), (777, 776), (1024, 1000)])
+def test_all_blocks_selected_equals_dense_causal(L, t):
+    rng = np.random.default_rng(L)
+    q, k, v = _case(rng, L)
+    nb = -(-L // 64)
+    idx = np.tile(np.arange(nb, dtype=np.int32), (2, 1))
+    scale = 1 / math.sqrt(q.shape[1])
+    got = oracle.selected_attention_row(q, k, v, idx, t, 64, scale)
+    mask = np.zeros((8, L), dtype=bool)
+    mask[:, :t + 1] = True
+    want = _sdpa(q, _expand(k, 4), _expand(v, 4), mask, scale)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_selected_equals_masked_sdpa_with_skips():
+    rng = np.random.default_rng(7)
+    L, t = 700, 650
+    q, k, v = _case(rng, L)
+    # group 0: blocks 0, 3, 10 (its causal part) and an out-of-range id; group 1: -1 padded
+    idx = np.array([[0, 3, 10, 11], [2, 5, -1, -1]], dtype=np.int32)
+    scale = 0.17
+    got = oracle.selected_attention_row(q, k, v, idx, t, 64, scale)
+    mask = np.zeros((8, L), dtype=bool)
+    for h in range(8):
+        g = h // 4
+        for blk in idx[g]:
+            if blk < 0 or 64 * blk > t:
+                continue
+            mask[h, 64 * blk:min(64 * blk + 64, t + 1)] = True
+    want = _sdpa(q, _expand(k, 4), _expand(v, 4), mask, scale)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # block 10 starts at 640 <= 650: only tokens 640..650 count
+    assert oracle.selected_keys(idx[0], t, L, 64)[-11:] == list(range(640, 651))
+
+
+def test_constant_values_and_single_key():
+    rng = np.random.default_rng(8)
+    q, k, v = _case(rng, 300)
+    v[:] = 2.5
+    idx = np.array([[0, 2], [1, 4]], dtype=np.int32)
+    got = oracle.selected_attention_row(q, k, v, idx, 299, 64, 0.3)
+    np.testing.assert_allclose(got, 2.5, rtol=1e-14)
+    q, k, v = _case(rng, 300)
+    got = oracle.selected_attention_row(q, k, v, np.array([[0], [0]]), 0, 64, 0.3)
+    np.testing.assert_allclose(got, _expand(v[0:1], 4)[0], rtol=1e-14)
+    # nothing visible -> zeros
+    got = oracle.selected_attention_row(q, k, v, np.array([[-1], [3]]), 100, 64, 0.3)
+    assert np.all(got == 0)
+
+
+def test_cis_mode_is_softmax_with_log_cis_bias():
+    rng = np.random.default_rng(9)
+    L, t = 500, 499
+    q, k, v = _case(rng, L)
+    cis = 1.0 / (1.0 + np.exp(-rng.standard_normal((L, 2))))
+    idx = np.array([[0, 1, 4, 7], [0, 2, 5, 6]], dtype=np.int32)
+    scale = 0.2
+    got = oracle.selected_attention_row(q, k, v, idx, t, 64, scale, cis)
+    bias = np.full((8, L), -np.inf)
+    for h in range(8):
+        g = h // 4
+        for blk in idx[g]:
+            sl = slice(64 * blk, min(64 * blk + 64, t + 1))
+            bias[h, sl] = np.log(cis[sl, g])
+    want = _sdpa(q, _expand(k, 4), _expand(v, 4), bias, scale)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # constant CIS reduces to plain selected attention
+    plain = oracle.selected_attention_row(q, k, v, idx, t, 64, scale)
+    const = oracle.selected_attention_row(q, k, v, idx, t, 64, scale, np.full((L, 2), 0.37))
+    np.testing.assert_allclose(const, plain, rtol=1e-13, atol=1e-14)
+
+
+def test_window_branch_equals_banded_sdpa():
+    rng = np.random.default_rng(10)
+    L = 900
+    q, k, v = _case(rng, L)
+    for t in (0, 100, 511, 512, 899):
+        got = oracle.window_attention_row(q, k, v, t, 512, 0.2)
+        mask = np.zeros((8, L), dtype=bool)
+        mask[:, max(0, t - 511):t + 1] = True
+        want = _sdpa(q, _expand(k, 4), _expand(v, 4), mask, 0.2)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_compressed_branch_equals_sdpa_over_pooled_kv():
+    rng = np.random.default_rng(11)
+    L = 400
+    q, k, v = _case(rng, L)
+    nc = oracle.n_windows(L, 32, 16)
+    kc = torch.nn.functional.avg_pool1d(torch.from_numpy(k.reshape(L, -1).T[None]), 32, 16)[0].T
+    vc = torch.nn.functional.avg_pool1d(torch.from_numpy(v.reshape(L, -1).T[None]), 32, 16)[0].T
+    kc = kc.numpy().reshape(nc, 2, -1)
+    vc = vc.numpy().reshape(nc, 2, -1)
+    for t in (31, 32, 47, 200, 399):
+        got = oracle.compressed_attention_row(q, kc, vc, t, 32, 16, 0.2)
+        mask = np.zeros((8, nc), dtype=bool)
+        mask[:, :(t - 31) // 16 + 1] = True
+        want = _sdpa(q, _expand(kc, 4), _expand(vc, 4), mask, 0.2)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert np.all(oracle.compressed_attention_row(q, kc, vc, 30, 32, 16, 0.2) == 0)
+
+
+def test_decode_step_with_full_coverage_equals_dense():
+    rng = np.random.default_rng(12)
+    lengths = [70, 256, 300]
+    H, H_kv, D = 8, 2, 16
+    N = sum(lengths)
+    q = rng.standard_normal((3, H, D))
+    k = rng.standard_normal((N, H_kv, D))
+    v = rng.standard_normal((N, H_kv, D))
+    cis = 1.0 / (1.0 + np.exp(-rng.standard_normal((N, H_kv))))
+    cu = oracle.cu_from_lengths(lengths)
+    scale = 1 / math.sqrt(D)
+    for cis_values in (False, True):
+        res = oracle.decode_step(q, k, v, cu, topk=8, n_init=1, n_local=2, cis=cis,
+                                 cis_select=True, cis_values=cis_values)
+        for b, L in enumerate(lengths):
+            ks, vs = k[cu[b]:cu[b + 1]], v[cu[b]:cu[b + 1]]
+            bias = np.zeros((H, L))
+            if cis_values:
+                bias = np.log(_expand(cis[cu[b]:cu[b + 1]][:, :, None], 4)[:, :, 0].T)
+            want = _sdpa(q[b], _expand(ks, 4), _expand(vs, 4), bias, scale)
+            np.testing.assert_allclose(res["out"][b], want, rtol=1e-12, atol=1e-12)
+            assert np.all(res["indices"][b][:, :-(-L // 64)] >= 0)
+
+
+def test_decode_step_pooled_caches_equal_avg_pool1d():
+    rng = np.random.default_rng(13)
+    lengths = [100, 64]
+    N = sum(lengths)
+    k = rng.standard_normal((N, 2, 8))
+    cis = rng.random((N, 2))
+    res = oracle.decode_step(rng.standard_normal((2, 4, 8)), k, k, oracle.cu_from_lengths(lengths),
+                             topk=2, n_init=1, n_local=1, cis=cis, cis_select=True)
+    cuc = res["cu_seqlens_c"]
+    for b, s0 in ((0, 0), (1, 100)):
+        L = lengths[b]
+        kk = torch.nn.functional.avg_pool1d(torch.from_numpy(k[s0:s0 + L].reshape(L, -1).T[None]), 32, 16)
+        np.testing.assert_allclose(res["kc"][cuc[b]:cuc[b + 1]].reshape(-1, 16), kk[0].T.numpy(), rtol=1e-13)
+        cc = torch.nn.functional.avg_pool1d(torch.from_numpy(cis[s0:s0 + L].T[None]), 32, 16)
+        np.testing.assert_allclose(res["cis_pooled"][cuc[b]:cuc[b + 1]], cc[0].T.numpy(), rtol=1e-13)
+
+
+def test_three_branch_gates_and_dense_equivalence():
+    rng = np.random.default_rng(14)
+    L, H, H_kv, D = 1100, 8, 2, 16
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, H_kv, D))
+    v = rng.standard_normal((L, H_kv, D))
+    rows = [0, 40, 511, 700, 1023, 1099]
+    for one in range(3):
+        g = np.zeros((L, H, 3))
+        g[:, :, one] = 1.0
+        res = oracle.nsa_prefill_rows(q, k, v, g, rows, topk=16, window=512)
+        branch = ("o_cmp", "o_sel", "o_win")[one]
+        np.testing.assert_array_equal(res["out"], res[branch])
+    g = rng.random((L, H, 3))
+    res = oracle.nsa_prefill_rows(q, k, v, g, rows, topk=16, window=512)
+    scale = 1 / math.sqrt(D)
+    for i, t in enumerate(rows):
+        mask = np.zeros((H, L), dtype=bool)
+        mask[:, :t + 1] = True
+        dense = _sdpa(q[t], _expand(k, 4), _expand(v, 4), mask, scale)
+        if t < 1024:        # 16 blocks of 64 cover every causal block
+            np.testing.assert_allclose(res["o_sel"][i], dense, rtol=1e-12, atol=1e-12)
+        if t < 512:         # the window covers the whole prefix
+            np.testing.assert_allclose(res["o_win"][i], dense, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(
+            res["out"][i],
+            g[t][:, 0:1] * res["o_cmp"][i] + g[t][:, 1:2] * res["o_sel"][i] + g[t][:, 2:3] * res["o_win"][i],
+            rtol=1e-14)

@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the native-sparse-attention hot path on one MI355X.
+
+Workload: the NOSA-1B-shaped batched decode (batch 8, contexts uniform in
+[8192, 32768] packed by cu_seqlens, 16 query heads, 2 KV heads, head_dim 128,
+bf16, compression 32/16, CIS pooled and fused into the block scores, top-64
+blocks of 64 tokens with the init block and a 1024-token local window forced).
+
+One step = one decode step of one attention layer over the whole batch: refresh
+of the newest compressed window (keys and CIS), compressed scores, block scores
+and top-k, selected-block attention.  Steps rotate over 28 distinct layer
+buffers (the NOSA-1B layer count; ~4.7 GB of KV) so every step reads KV that is
+not resident in the 256 MB last-level cache.  The timed steps are replayed from
+one HIP graph.  value = decode tokens/s = batch / step time.
+
+Printed: one JSON line (rank 0).  `roofline` is the selected-attention kernel:
+algorithmic bytes per launch (selected K and V tokens, queries, outputs,
+indices) over its mean duration, measured by HIP events recorded at the
+kernel's own start and end.  `cpu_baseline` times the float64 oracle on the
+host cores for layer 0 of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "decode tokens/s + achieved HBM GB/s, selected-block attn at 32K ctx, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2800)
+    ap.add_argument("--warmup", type=int, default=280)
+    ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--pinned-32k", action="store_true", help="all contexts 32768")
+    ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--profile-steps", type=int, default=280)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this build runs on one GPU only "
+              "(no multi-GPU path exists; DESIGN.md describes how the path would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_compress_amd as nsa
+    from gen import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = W.nosa1b_decode(pinned_32k=args.pinned_32k)
+    B, H, Hkv, D = w.batch, w.heads, w.kv_heads, w.head_dim
+    lengths = list(w.lengths)
+    nc = [nsa.full_windows(L) for L in lengths]
+    cu_k = nsa.cu_seqlens_of(lengths, dev)
+    cu_c = nsa.cu_seqlens_of(nc, dev)
+    max_len = max(lengths)
+    kc_dt = torch.float32 if args.kc_dtype == "f32" else torch.bfloat16
+    print(f"[bench] workload {w.name} lengths={lengths} layers={args.layers}", file=sys.stderr, flush=True)
+
+    layers = []
+    for li in range(args.layers):
+        q = W.decode_query(w, dev, layer=li)
+        k, v = W.keys_values(w, dev, layer=li)
+        cis = W.cis_scores(w, dev, layer=li)
+        kc = torch.empty((sum(nc), Hkv, D), dtype=kc_dt, device=dev)
+        cp = torch.empty((sum(nc), Hkv), dtype=torch.float32, device=dev)
+        nsa.nsa_compress_k(k, kc, cu_k, cu_c, max(nc))
+        nsa.nsa_cis_mean_pool_varlen(cis, cp, cu_k, cu_c, max(nc))
+        out = torch.empty((B, H, D), dtype=w.dtype, device=dev)
+        idx = torch.empty((B, Hkv, w.topk), dtype=torch.int32, device=dev)
+        p = nsa.decode_params(q, k, v, kc, cu_k, cu_c, max_len, out, topk=w.topk, n_init=w.n_init,
+                              n_local=w.n_local, cis=cis, cis_pooled=cp, cis_weight=w.cis_weight,
+                              cis_values=w.cis_values, append_window=True, indices=idx)
+        layers.append(dict(q=q, k=k, v=v, cis=cis, kc=kc, cp=cp, out=out, idx=idx, p=p))
+    torch.cuda.synchronize()
+    ws = torch.zeros(nsa.decode_workspace_size(layers[0]["p"]), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    nl = len(layers)
+
+    def step(i):
+        nsa.nsa_decode_step(layers[i % nl]["p"], workspace=ws)
+
+    with torch.cuda.stream(stream):
+        for i in range(nl):
+            step(i)
+    torch.cuda.synchronize()
+    print("[bench] eager steps done; capturing graphs", file=sys.stderr, flush=True)
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                step(i)
+        return g
+
+    g_warm = capture(max(1, args.warmup))
+    g_timed = capture(args.steps)
+    torch.cuda.synchronize()
+    g_warm.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    g_timed.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_s * 1e3 / args.steps
+    tokens_per_s = B * args.steps / wall_s
+    print(f"[bench] timed {args.steps} steps: wall {wall_s * 1e3:.2f} ms, events {gpu_ms:.2f} ms",
+          file=sys.stderr, flush=True)
+
+    # per-kernel durations, from events recorded at each kernel's own start and end
+    kinds = {"logits_and_refresh": nsa.KERNEL_LOGITS, "block_scores_topk": nsa.KERNEL_BLOCK_SCORES,
+             "selected_attn": nsa.KERNEL_SELECTED_ATTN, "combine": nsa.KERNEL_COMBINE}
+    n_prof = max(1, args.profile_steps)
+    evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(n_prof)] for name in kinds}
+    with torch.cuda.stream(stream):
+        for name in kinds:
+            for a, b in evs[name]:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(n_prof):
+            for name, kind in kinds.items():
+                a, b = evs[name][i]
+                nsa.nsa_profile_next_launch(kind, a, b)
+            step(i)
+    torch.cuda.synchronize()
+    kern_us = {name: float(np.mean([a.elapsed_time(b) for a, b in evs[name]])) * 1e3 for name in kinds}
+
+    # algorithmic bytes of one selected-attention launch (identical for every layer)
+    idx0 = layers[0]["idx"].cpu().numpy()
+    sel_tokens = 0
+    for b_, L in enumerate(lengths):
+        for g in range(Hkv):
+            for blk in idx0[b_, g]:
+                if blk >= 0:
+                    sel_tokens += min(64, L - 64 * int(blk))
+    elt = 2  # bf16
+    attn_bytes = (sel_tokens * D * elt * 2            # selected K and V rows
+                  + 2 * B * H * D * elt               # queries in, outputs out
+                  + B * Hkv * w.topk * 4)             # block ids
+    kc_elt = 4 if kc_dt == torch.float32 else 2
+    score_bytes = (sum(nc) * Hkv * D * kc_elt         # compressed keys
+                   + sum(nc) * Hkv * 4                # pooled CIS
+                   + B * H * D * elt)                 # queries
+    refresh_bytes = B * (32 * Hkv * D * elt + 32 * Hkv * 4 + Hkv * D * kc_elt + Hkv * 4)
+    step_bytes = attn_bytes + score_bytes + refresh_bytes
+    attn_gbs = attn_bytes / (kern_us["selected_attn"] * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, sigmoid(N(0,1)) CIS; no dataset)",
+        "config": {
+            "workload": w.name,
+            "batch": B, "context_lengths": lengths, "heads": H, "kv_heads": Hkv, "head_dim": D,
+            "compress_kernel": w.kernel, "compress_stride": w.stride, "block": w.block,
+            "topk": w.topk, "forced_init_blocks": w.n_init, "forced_local_blocks": w.n_local,
+            "cis_fused": True, "compressed_key_dtype": args.kc_dtype,
+            "layer_buffers_rotated": nl, "step": "one layer, whole batch, HIP-graph replay",
+        },
+        "roofline": {
+            "kernel": "selected_attn_kernel (decode, split over selected blocks)",
+            "bound": "hbm",
+            "achieved": round(attn_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "mean_kernel_us": round(kern_us["selected_attn"], 3),
+        },
+        "kernel_us": {k_: round(v_, 3) for k_, v_ in kern_us.items()},
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "tokens_per_s_28_layers": round(tokens_per_s / 28.0, 1),
+        "timed_gpu_ms": round(gpu_ms, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity_layer0"] = cpu_baseline(w, layers[0], lengths, args)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, layer, lengths, args):
+    """Time the float64 oracle on one core for layer 0 and compare the GPU output."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+
+    def f64(t):
+        return t.detach().float().cpu().numpy().astype(np.float64)
+
+    q, k, v, cis = f64(layer["q"]), f64(layer["k"]), f64(layer["v"]), f64(layer["cis"])
+    cu = oracle.cu_from_lengths(lengths)
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    reps, t_total, res = 0, 0.0, None
+    try:
+        if ctx:
+            ctx.__enter__()
+        while reps == 0 or t_total < args.cpu_seconds:
+            t0 = time.perf_counter()
+            res = oracle.decode_step(q, k, v, cu, kernel=w.kernel, stride=w.stride, block=w.block,
+                                     topk=w.topk, n_init=w.n_init, n_local=w.n_local, cis=cis,
+                                     cis_select=w.cis_select, cis_values=w.cis_values,
+                                     cis_weight=w.cis_weight)
+            t_total += time.perf_counter() - t0
+            reps += 1
+            if reps >= 20:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    base = {
+        "value": round(w.batch * reps / t_total, 3),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"layer 0 of the same workload, full batch of {w.batch} sequences, "
+                  f"{reps} decode step(s), {t_total:.1f} s on one host thread",
+    }
+    got_idx = layer["idx"].cpu().numpy()
+    got = f64(layer["out"])
+    same = 0
+    err = 0.0
+    G = w.heads // w.kv_heads
+    for b in range(w.batch):
+        for g in range(w.kv_heads):
+            if got_idx[b, g].tolist() == res["indices"][b, g].tolist():
+                same += 1
+                err = max(err, float(np.abs(got[b, g * G:(g + 1) * G] - res["out"][b, g * G:(g + 1) * G]).max()))
+    parity = {"index_sets_identical": f"{same}/{w.batch * w.kv_heads}",
+              "max_abs_err_out_on_identical_sets": err}
+    return base, parity
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) native-sparse-attention hot path.
+ *
+ * The path, as the source pages describe it:
+ *   1. mean-pool keys into overlapping windows (32 tokens, stride 16)
+ *      [NOSA-1B core components, component 1 "Key compressor"];
+ *   2. score each query against the compressed keys and sum the softmax
+ *      probabilities over the query heads of a GQA group, then max-pool the
+ *      window scores onto 64-token blocks
+ *      [NOSA-1B core components, component 3; NOSA-1B source analysis part 3,
+ *      "beyond the kernel"];
+ *   3. mean-pool the per-token CIS importance scores over the same windows,
+ *      varlen by cu_seqlens, dividing by the count of valid tokens
+ *      [NOSA-1B source analysis part 3, grid / block-load / varlen-mask
+ *      sections; NOSA-1B core components, component 2];
+ *   4. keep the init and local blocks and the top-k of the rest, indices sorted
+ *      [NOSA-1B source analysis part 3, "beyond the kernel"; component 3];
+ *   5. GQA-grouped attention over only the selected blocks, optionally with CIS-
+ *      scaled values and the ones-value normaliser
+ *      [NOSA-1B core components, decode-stage section; TileLang NSA, section 2].
+ *   The three-branch NSA prefill (compressed, selected and sliding-window
+ *   branches summed with gates) follows DeepSeek NSA with Triton, section 1.1.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL is the default stream) and the call returns at once.
+ *   - Packed variable-length batches: sequence b occupies rows
+ *     cu_seqlens[b] .. cu_seqlens[b+1]-1 of a packed tensor.  cu_seqlens arrays
+ *     are device int32 [batch+1], non-decreasing, starting at 0.  The max_*
+ *     sizes passed by value are host-side upper bounds used to size the grid;
+ *     a smaller real size is fine, a larger one is undefined behaviour.
+ *   - Layouts (row-major, innermost last):
+ *       Q          [rows, heads, head_dim]       (decode: rows = batch)
+ *       K, V       [N_k, kv_heads, head_dim]
+ *       K_c        [N_c, kv_heads, head_dim]     window c of sequence b at row
+ *                                                cu_seqlens_c[b] + c
+ *       cis        [N_k, kv_heads] float32;  cis_pooled [N_c, kv_heads] float32
+ *       block_scores [rows, kv_heads, n_blocks_max] float32
+ *       indices    [rows, kv_heads, k] int32, block ids local to the sequence,
+ *                  ascending, -1 padded
+ *   - Window c of a sequence of length L covers its tokens
+ *     stride*c .. stride*c+kernel-1 that exist (< L).  The number of windows of
+ *     sequence b is cu_seqlens_c[b+1]-cu_seqlens_c[b]; the usual choice is the
+ *     full-window count floor((L-kernel)/stride)+1 (0 when L < kernel).
+ *   - A query at position t (0-based, within its sequence) sees window c when
+ *     stride*c+kernel-1 <= t, and block i when 0 <= block_size*i <= t; inside a
+ *     selected block only tokens j <= t are attended.  Decode queries sit at
+ *     t = L-1.  Prefill rows (cu_seqlens_q given) of sequence b sit at
+ *     t = (row - cu_seqlens_q[b]) + (L_k - L_q).
+ *   - softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *   - Supported: head_dim 128; heads/kv_heads in {1, 2, 4, 8, 16}; kernel 32,
+ *     stride 16 for the scoring paths (pooling accepts any kernel >= stride >= 1);
+ *     block_size 64.  Others return NSA_ERR_UNSUPPORTED without launching.
+ *   - Workspaces are caller-allocated device memory of at least the size the
+ *     matching *_workspace_size query returns, ZERO-FILLED ONCE after
+ *     allocation; each call leaves its completion counters at zero again, so a
+ *     workspace can be reused by later calls on the same stream.  Calls that
+ *     share one workspace must not run concurrently.
+ *   - Errors: every entry point validates its arguments on the host before
+ *     launching and returns a non-zero nsa_status on failure; nsa_last_error()
+ *     then describes it (thread-local string, valid until the next call on
+ *     that thread).  NSA_ERR_HIP reports a launch error from hipGetLastError.
+ *     Preconditions NOT checked (undefined behaviour if broken): cu_seqlens
+ *     contents, unique block ids within one index row, finite inputs.
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nsa_status {
+  NSA_OK = 0,
+  NSA_ERR_INVALID_ARG = 1,
+  NSA_ERR_UNSUPPORTED = 2,
+  NSA_ERR_WORKSPACE = 3,
+  NSA_ERR_HIP = 4
+} nsa_status;
+
+typedef enum nsa_dtype {
+  NSA_F32 = 0,  /* IEEE float32 */
+  NSA_BF16 = 1  /* bfloat16 */
+} nsa_dtype;
+
+/* Thread-local text of the last error (empty string after a successful call). */
+const char* nsa_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t nsa_version(void);
+
+/*
+ * nsa_profile_next_launch -- measurement hook (not part of the method).  Arms
+ * the next launch, on the calling host thread, of one kernel kind so that it
+ * records `start` and `stop` at the kernel's own begin and end
+ * (hipExtLaunchKernelGGL); the request is consumed by that launch.  Kinds:
+ * 0 pooling (nsa_compress_k, nsa_cis_mean_pool_varlen), 1 compressed-key
+ * logits (with the decode window refresh), 2 block scores and top-k
+ * selection, 3 selected attention, 4 merge of split partial states (decode).
+ * The events are owned by the caller
+ * and must have timing enabled; a launch made during stream capture must not
+ * be armed.
+ */
+typedef enum nsa_kernel_kind {
+  NSA_KERNEL_POOL = 0,
+  NSA_KERNEL_LOGITS = 1,
+  NSA_KERNEL_BLOCK_SCORES = 2,
+  NSA_KERNEL_SELECTED_ATTN = 3,
+  NSA_KERNEL_COMBINE = 4
+} nsa_kernel_kind;
+nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
+
+/*
+ * nsa_compress_k -- mean-pool keys (or values) into compressed windows.
+ * [NOSA-1B core components, component 1: CompressK, 32-token windows, stride 16,
+ *  one mean per window.]
+ *   x      [N, heads, head_dim] of dtype x_dtype
+ *   x_c    [N_c, heads, head_dim] of dtype xc_dtype (written); float32 keeps the
+ *          full-precision mean, bfloat16 rounds it to nearest even.
+ *   max_windows  >= every sequence's window count.
+ * Each window is the sum of its valid tokens divided by their number, 0 if none.
+ */
+nsa_status nsa_compress_k(const void* x, nsa_dtype x_dtype, void* x_c, nsa_dtype xc_dtype,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_c,
+                          int32_t batch, int32_t max_windows, int32_t heads,
+                          int32_t head_dim, int32_t kernel, int32_t stride,
+                          hipStream_t stream);
+
+/*
+ * nsa_cis_mean_pool_varlen -- sliding-window mean of per-token importance scores.
+ * [NOSA-1B source analysis part 3: grid (head, batch, window), masked load of the
+ *  window, sum divided by the valid count; NOSA-1B core components, component 2:
+ *  kernel 32 / stride 16, aligned with the key compressor.]
+ *   cis        [N, heads] float32
+ *   cis_pooled [N_c, heads] float32 (written)
+ */
+nsa_status nsa_cis_mean_pool_varlen(const float* cis, float* cis_pooled,
+                                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_c,
+                                    int32_t batch, int32_t max_windows, int32_t heads,
+                                    int32_t kernel, int32_t stride, hipStream_t stream);
+
+/*
+ * nsa_compressed_scores -- block scores of decode queries (one query per
+ * sequence, at t = L-1).
+ * [NOSA-1B core components, component 3, stage 1: attention of the query against
+ *  the compressed keys gives block scores; NOSA-1B source analysis part 3, "beyond
+ *  the kernel": window scores max-pooled to blocks and fused with the pooled CIS.]
+ *   q            [batch, heads, head_dim], dtype q_dtype
+ *   k_c          [N_c, kv_heads, head_dim], dtype kc_dtype
+ *   cis_pooled   nullable [N_c, kv_heads] float32; with it the block score gains
+ *                cis_weight * (max of cis_pooled over the block's windows)
+ *   block_scores [batch, kv_heads, n_blocks_max] float32 (written), with
+ *                n_blocks_max = ceil(max_seqlen_k / block_size); entries past a
+ *                sequence's own block count are written as 0
+ *   window_probs nullable [batch, kv_heads, max_windows] float32 (written): the
+ *                group-summed probabilities, 0 past a sequence's window count
+ *   For query head h (group g = h / (heads/kv_heads)): P_h = softmax over visible
+ *   windows of scale * q_h . K_c[c]; P_g = sum of P_h over the group; block score
+ *   = max of P_g over windows overlapping the block (0 if none).
+ *   workspace: nsa_compressed_scores_workspace_size(...) bytes, zero-filled once.
+ */
+size_t nsa_compressed_scores_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t heads,
+                                            int32_t kv_heads, int32_t kernel, int32_t stride);
+nsa_status nsa_compressed_scores(const void* q, nsa_dtype q_dtype, const void* k_c,
+                                 nsa_dtype kc_dtype, const float* cis_pooled, float cis_weight,
+                                 float* block_scores, float* window_probs,
+                                 const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_c,
+                                 int32_t batch, int32_t max_seqlen_k, int32_t heads,
+                                 int32_t kv_heads, int32_t head_dim, int32_t kernel,
+                                 int32_t stride, int32_t block_size, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nsa_select_topk -- top-k block selection with forced init and local blocks.
+ * [NOSA-1B source analysis part 3, "beyond the kernel": init and local blocks are
+ *  kept, other positions compete by score, top-k picks the ids, ids are sorted;
+ *  NOSA-1B core components, component 3: k = 64.]
+ *   block_scores [rows, kv_heads, n_blocks_max] float32, NaN-free
+ *   indices      [rows, kv_heads, k] int32 (written)
+ *   cu_seqlens_q NULL: decode, rows = batch, t = L_b - 1.  Otherwise prefill rows.
+ *   Eligible blocks: block_size*i <= t.  Forced: the first n_init and the last
+ *   n_local eligible blocks (n_init + n_local <= k).  The other k - |forced|
+ *   places go to the best-scoring eligible blocks, ties to the lower id.  Output
+ *   ascending, padded with -1 when fewer than k blocks are eligible.
+ *   rows_total: number of rows (batch for decode; cu_seqlens_q[batch] otherwise).
+ */
+nsa_status nsa_select_topk(const float* block_scores, int32_t* indices,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                           int32_t kv_heads, int32_t n_blocks_max, int32_t k, int32_t n_init,
+                           int32_t n_local, int32_t block_size, hipStream_t stream);
+
+/*
+ * nsa_selected_attn_fwd -- attention of each query row over its selected blocks.
+ * [NOSA-1B core components, decode stage: sparse FlashAttention over the topk_idx
+ *  blocks, values scaled by CIS and a ones-value normaliser; TileLang NSA,
+ *  section 2: BlockIndices[b, t, h_kv, :], block start id*64 used when
+ *  0 <= start <= t, query heads of one KV group share the KV blocks.]
+ *   q, out   [rows, heads, head_dim] of `dtype` (out written)
+ *   k, v     [N_k, kv_heads, head_dim] of `dtype`
+ *   indices  [rows, kv_heads, k_sel] int32
+ *   cis      nullable [N_k, kv_heads] float32.  NULL: out = softmax(s) . V.
+ *            Given: out = sum_j p_j cis_j v_j / sum_j p_j cis_j (the CIS-scaled
+ *            values divided by the same attention over all-ones values).
+ *   lse      nullable [rows, heads] float32 (written): natural log of the
+ *            normaliser sum_j exp(s_j) (times cis_j in CIS mode); -inf when the
+ *            row sees no key (its output row is then 0).
+ *   cu_seqlens_q NULL: decode (rows = batch, t = L_b - 1); else prefill rows.
+ *   workspace: nsa_selected_attn_workspace_size(...) bytes, zero-filled once.
+ */
+size_t nsa_selected_attn_workspace_size(int32_t rows_total, int32_t heads, int32_t kv_heads,
+                                        int32_t head_dim, int32_t k_sel, int32_t decode);
+nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
+                                 const int32_t* indices, int32_t k_sel, const float* cis,
+                                 void* out, float* lse, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t batch, int32_t rows_total,
+                                 int32_t max_seqlen_k, int32_t heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t block_size, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nsa_decode_step -- one decode step of the whole path for a packed batch: the
+ * newest token of every sequence (t = L_b - 1) scores the compressed keys,
+ * selects k blocks and attends to them.
+ * [NOSA-1B core components, components 1-3 and the decode stage.]
+ * With append_window != 0 the step first (re)computes the newest full window
+ * (index n_c-1) of the K_c and pooled-CIS caches from the K and CIS caches, so a
+ * caller that appended tokens completing a window gets an up-to-date cache.
+ */
+typedef struct nsa_decode_params {
+  const void* q;            /* [batch, heads, head_dim], dtype */
+  const void* k;            /* [N_k, kv_heads, head_dim], dtype */
+  const void* v;            /* [N_k, kv_heads, head_dim], dtype */
+  void* k_c;                /* [N_c, kv_heads, head_dim], kc_dtype (read; written if append) */
+  const float* cis;         /* nullable [N_k, kv_heads]: importance scores */
+  float* cis_pooled;        /* nullable [N_c, kv_heads] (read; written if append) */
+  const int32_t* cu_seqlens_k; /* [batch+1] */
+  const int32_t* cu_seqlens_c; /* [batch+1] full-window counts */
+  void* out;                /* [batch, heads, head_dim], dtype (written) */
+  float* block_scores;      /* nullable [batch, kv_heads, n_blocks_max] debug output */
+  int32_t* indices;         /* nullable [batch, kv_heads, topk] debug output */
+  nsa_dtype dtype;          /* q, k, v, out */
+  nsa_dtype kc_dtype;       /* k_c */
+  int32_t batch, max_seqlen_k, heads, kv_heads, head_dim;
+  int32_t kernel, stride, block_size;
+  int32_t topk, n_init, n_local;
+  float cis_weight;         /* weight of the pooled CIS in the block score (needs cis_pooled) */
+  int32_t cis_values;       /* != 0: CIS-scaled values with the ones normaliser (needs cis) */
+  int32_t append_window;    /* != 0: refresh window n_c-1 of k_c / cis_pooled first */
+  float softmax_scale;
+} nsa_decode_params;
+
+size_t nsa_decode_workspace_size(const nsa_decode_params* p);
+nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H */

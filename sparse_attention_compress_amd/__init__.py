@@ -1,0 +1,273 @@
+"""Python binding of libnsa (the gfx950 native-sparse-attention hot path).
+
+Argument marshalling only: every function takes torch tensors that already live
+on the GPU, passes their device pointers and sizes to the C ABI declared in
+``include/nsa.h`` and enqueues the work on torch's current HIP stream.  All
+computation happens in the HIP kernels of ``libnsa.so``; if the library is not
+built this module raises instead of falling back to anything else.
+
+Workspaces: functions that need one accept ``workspace=`` (a zero-filled uint8
+CUDA tensor of at least the queried size).  When it is omitted the binding keeps
+one zero-filled buffer per (device, size) and reuses it; the kernels leave their
+counters at zero after every call, so reuse on one stream is safe.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnsa.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "nsa.h")
+
+NSA_F32, NSA_BF16 = 0, 1
+STATUS = {0: "NSA_OK", 1: "NSA_ERR_INVALID_ARG", 2: "NSA_ERR_UNSUPPORTED", 3: "NSA_ERR_WORKSPACE",
+          4: "NSA_ERR_HIP"}
+
+_lib = None
+
+
+class NsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+c_i32, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class DecodeParams(ctypes.Structure):
+    """Mirror of ``nsa_decode_params``."""
+    _fields_ = [
+        ("q", c_vp), ("k", c_vp), ("v", c_vp), ("k_c", c_vp), ("cis", c_vp), ("cis_pooled", c_vp),
+        ("cu_seqlens_k", c_vp), ("cu_seqlens_c", c_vp), ("out", c_vp), ("block_scores", c_vp),
+        ("indices", c_vp), ("dtype", ctypes.c_int), ("kc_dtype", ctypes.c_int),
+        ("batch", c_i32), ("max_seqlen_k", c_i32), ("heads", c_i32), ("kv_heads", c_i32),
+        ("head_dim", c_i32), ("kernel", c_i32), ("stride", c_i32), ("block_size", c_i32),
+        ("topk", c_i32), ("n_init", c_i32), ("n_local", c_i32), ("cis_weight", c_f32),
+        ("cis_values", c_i32), ("append_window", c_i32), ("softmax_scale", c_f32),
+    ]
+
+
+_SIGS = {
+    "nsa_last_error": (ctypes.c_char_p, []),
+    "nsa_version": (c_i32, []),
+    "nsa_profile_next_launch": (ctypes.c_int, [c_i32, c_vp, c_vp]),
+    "nsa_compress_k": (ctypes.c_int, [c_vp, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_i32,
+                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "nsa_cis_mean_pool_varlen": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                                c_i32, c_vp]),
+    "nsa_compressed_scores_workspace_size": (c_sz, [c_i32] * 6),
+    "nsa_compressed_scores": (ctypes.c_int, [c_vp, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_f32,
+                                             c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                             c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
+    "nsa_select_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                       c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "nsa_selected_attn_workspace_size": (c_sz, [c_i32] * 6),
+    "nsa_selected_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i32, c_vp,
+                                             c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                             c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
+    "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
+    "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
+}
+
+
+def lib():
+    """The loaded libnsa (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_attention_compress_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().nsa_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise NsaError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return NSA_BF16
+    if t.dtype == torch.float32:
+        return NSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    key = (str(device), nbytes)
+    buf = _ws_cache.get(key)
+    if buf is None:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf, nbytes
+
+
+# ----------------------------------------------------------------------------- host helpers
+
+
+def full_windows(length: int, kernel: int = 32, stride: int = 16) -> int:
+    return 0 if length < kernel else (length - kernel) // stride + 1
+
+
+def cu_seqlens_of(lengths, device) -> torch.Tensor:
+    out = [0]
+    for L in lengths:
+        out.append(out[-1] + int(L))
+    return torch.tensor(out, dtype=torch.int32, device=device)
+
+
+# ----------------------------------------------------------------------------- entry points
+
+
+def nsa_compress_k(x, x_c, cu_seqlens, cu_seqlens_c, max_windows, kernel=32, stride=16, stream=None):
+    """x [N, heads, D] -> x_c [N_c, heads, D] (window means)."""
+    heads, head_dim = x.shape[1], x.shape[2]
+    _check(lib().nsa_compress_k(_ptr(x), _dt(x), _ptr(x_c), _dt(x_c), _ptr(cu_seqlens),
+                                _ptr(cu_seqlens_c), cu_seqlens.numel() - 1, int(max_windows), heads,
+                                head_dim, kernel, stride, _stream(stream)))
+    return x_c
+
+
+def nsa_cis_mean_pool_varlen(cis, cis_pooled, cu_seqlens, cu_seqlens_c, max_windows, kernel=32,
+                             stride=16, stream=None):
+    """cis [N, heads] float32 -> cis_pooled [N_c, heads] float32."""
+    heads = cis.shape[1] if cis.dim() == 2 else 1
+    _check(lib().nsa_cis_mean_pool_varlen(_ptr(cis), _ptr(cis_pooled), _ptr(cu_seqlens),
+                                          _ptr(cu_seqlens_c), cu_seqlens.numel() - 1,
+                                          int(max_windows), heads, kernel, stride, _stream(stream)))
+    return cis_pooled
+
+
+def compressed_scores_workspace_size(batch, max_seqlen_k, heads, kv_heads, kernel=32, stride=16):
+    return lib().nsa_compressed_scores_workspace_size(batch, max_seqlen_k, heads, kv_heads, kernel,
+                                                      stride)
+
+
+def nsa_compressed_scores(q, k_c, cu_seqlens_k, cu_seqlens_c, max_seqlen_k, block_scores,
+                          window_probs=None, cis_pooled=None, cis_weight=1.0, softmax_scale=0.0,
+                          kernel=32, stride=16, block_size=64, workspace=None, stream=None):
+    """Decode queries q [B, H, D] against k_c [N_c, H_kv, D] -> block_scores [B, H_kv, nb_max]."""
+    B, H, D = q.shape
+    H_kv = k_c.shape[1]
+    need = compressed_scores_workspace_size(B, max_seqlen_k, H, H_kv, kernel, stride)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check(lib().nsa_compressed_scores(_ptr(q), _dt(q), _ptr(k_c), _dt(k_c), _ptr(cis_pooled),
+                                       float(cis_weight), _ptr(block_scores), _ptr(window_probs),
+                                       _ptr(cu_seqlens_k), _ptr(cu_seqlens_c), B, int(max_seqlen_k),
+                                       H, H_kv, D, kernel, stride, block_size, float(softmax_scale),
+                                       _ptr(ws), nbytes, _stream(stream)))
+    return block_scores
+
+
+def nsa_select_topk(block_scores, indices, cu_seqlens_k, max_seqlen_k, k, n_init=0, n_local=0,
+                    cu_seqlens_q=None, block_size=64, stream=None):
+    """block_scores [rows, H_kv, nb_max] -> indices [rows, H_kv, k] (ascending, -1 padded)."""
+    rows, H_kv, nb_max = block_scores.shape
+    batch = cu_seqlens_k.numel() - 1
+    _check(lib().nsa_select_topk(_ptr(block_scores), _ptr(indices), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), batch, rows, int(max_seqlen_k), H_kv, nb_max,
+                                 int(k), int(n_init), int(n_local), block_size, _stream(stream)))
+    return indices
+
+
+def selected_attn_workspace_size(rows, heads, kv_heads, head_dim, k_sel, decode):
+    return lib().nsa_selected_attn_workspace_size(rows, heads, kv_heads, head_dim, k_sel, int(decode))
+
+
+def nsa_selected_attn_fwd(q, k, v, indices, cu_seqlens_k, max_seqlen_k, out, cis=None, lse=None,
+                          cu_seqlens_q=None, softmax_scale=0.0, block_size=64, workspace=None,
+                          stream=None):
+    """q [rows, H, D]; k, v [N_k, H_kv, D]; indices [rows, H_kv, k_sel] -> out [rows, H, D]."""
+    rows, H, D = q.shape
+    H_kv = k.shape[1]
+    k_sel = indices.shape[2]
+    batch = cu_seqlens_k.numel() - 1
+    decode = cu_seqlens_q is None
+    need = selected_attn_workspace_size(rows, H, H_kv, D, k_sel, decode)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check(lib().nsa_selected_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(indices), k_sel,
+                                       _ptr(cis), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                       _ptr(cu_seqlens_k), batch, rows, int(max_seqlen_k), H, H_kv,
+                                       D, block_size, float(softmax_scale), _ptr(ws), nbytes,
+                                       _stream(stream)))
+    return out
+
+
+def decode_params(q, k, v, k_c, cu_seqlens_k, cu_seqlens_c, max_seqlen_k, out, topk=64, n_init=1,
+                  n_local=16, cis=None, cis_pooled=None, cis_weight=1.0, cis_values=False,
+                  append_window=False, block_scores=None, indices=None, softmax_scale=0.0,
+                  kernel=32, stride=16, block_size=64) -> DecodeParams:
+    B, H, D = q.shape
+    p = DecodeParams()
+    p.q, p.k, p.v, p.k_c = q.data_ptr(), k.data_ptr(), v.data_ptr(), k_c.data_ptr()
+    p.cis = cis.data_ptr() if cis is not None else None
+    p.cis_pooled = cis_pooled.data_ptr() if cis_pooled is not None else None
+    p.cu_seqlens_k, p.cu_seqlens_c = cu_seqlens_k.data_ptr(), cu_seqlens_c.data_ptr()
+    p.out = out.data_ptr()
+    p.block_scores = block_scores.data_ptr() if block_scores is not None else None
+    p.indices = indices.data_ptr() if indices is not None else None
+    p.dtype, p.kc_dtype = _dt(q), _dt(k_c)
+    p.batch, p.max_seqlen_k, p.heads, p.kv_heads, p.head_dim = B, int(max_seqlen_k), H, k.shape[1], D
+    p.kernel, p.stride, p.block_size = kernel, stride, block_size
+    p.topk, p.n_init, p.n_local = int(topk), int(n_init), int(n_local)
+    p.cis_weight = float(cis_weight)
+    p.cis_values = int(bool(cis_values))
+    p.append_window = int(bool(append_window))
+    p.softmax_scale = float(softmax_scale)
+    return p
+
+
+def decode_workspace_size(params: DecodeParams) -> int:
+    return lib().nsa_decode_workspace_size(ctypes.byref(params))
+
+
+def nsa_decode_step(params: DecodeParams, workspace=None, device=None, stream=None):
+    """Enqueue one decode step described by ``params`` (see :func:`decode_params`)."""
+    need = decode_workspace_size(params)
+    ws, nbytes = _workspace(need, device or torch.device("cuda"), workspace)
+    _check(lib().nsa_decode_step(ctypes.byref(params), _ptr(ws), nbytes, _stream(stream)))
+
+
+KERNEL_POOL, KERNEL_LOGITS, KERNEL_BLOCK_SCORES, KERNEL_SELECTED_ATTN, KERNEL_COMBINE = 0, 1, 2, 3, 4
+
+
+def nsa_profile_next_launch(kind: int, start: torch.cuda.Event, stop: torch.cuda.Event):
+    """Arm the next launch of one kernel kind to record the two (timing) events at
+    the kernel's own start and end.  The events must already exist (recorded once)."""
+    _check(lib().nsa_profile_next_launch(int(kind), ctypes.c_void_p(start.cuda_event),
+                                         ctypes.c_void_p(stop.cuda_event)))
+
+
+def softmax_scale_default(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

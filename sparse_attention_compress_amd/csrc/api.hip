@@ -1,0 +1,348 @@
+// Host side of the C ABI declared in include/nsa.h: argument validation, grid
+// sizing, workspace carve-up and kernel launches on the caller's stream.  No
+// allocation, no synchronisation.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/nsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local nsa::ProfSlot g_prof[nsa::kKindCount];
+
+nsa_status fail(nsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+nsa_status ok() {
+  g_err.clear();
+  return NSA_OK;
+}
+
+nsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int d) { return d == NSA_F32 || d == NSA_BF16; }
+bool group_ok(int heads, int kv_heads) {
+  if (kv_heads <= 0 || heads <= 0 || heads % kv_heads) return false;
+  const int g = heads / kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+}
+// Selected blocks per row: a prefill workgroup stages all of its row's ids at
+// once; decode splits a row over at most kMaxSplits workgroups.
+constexpr int kMaxPrefillSel = 64;
+constexpr int kMaxDecodeSel = 64 * nsa::kMaxSplits;
+
+int full_windows(int len, int kernel, int stride) {
+  return len >= kernel ? (len - kernel) / stride + 1 : 0;
+}
+float scale_log2_of(float softmax_scale, int head_dim) {
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
+  return sc * nsa::kLog2eHost;
+}
+
+#define NSA_REQUIRE(cond, st, ...) \
+  do {                             \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+nsa_status check_geometry(const char* fn, int head_dim, int kernel, int stride, int block) {
+  NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
+  NSA_REQUIRE(kernel == nsa::kKernel && stride == nsa::kStride, NSA_ERR_UNSUPPORTED,
+              "%s: window %d/stride %d unsupported (32/16 only)", fn, kernel, stride);
+  NSA_REQUIRE(block == nsa::kBlock, NSA_ERR_UNSUPPORTED, "%s: block_size %d unsupported (64 only)", fn, block);
+  return NSA_OK;
+}
+
+}  // namespace
+
+nsa::ProfSlot& nsa::prof_slot(int kind) { return g_prof[kind]; }
+
+extern "C" {
+
+const char* nsa_last_error(void) { return g_err.c_str(); }
+
+nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop) {
+  NSA_REQUIRE(kernel_kind >= 0 && kernel_kind < nsa::kKindCount, NSA_ERR_INVALID_ARG,
+              "nsa_profile_next_launch: unknown kernel kind %d", kernel_kind);
+  NSA_REQUIRE(start != nullptr && stop != nullptr, NSA_ERR_INVALID_ARG,
+              "nsa_profile_next_launch: null event");
+  nsa::ProfSlot& p = g_prof[kernel_kind];
+  p.start = start;
+  p.stop = stop;
+  p.armed = true;
+  return ok();
+}
+
+int32_t nsa_version(void) { return 100; }
+
+nsa_status nsa_compress_k(const void* x, nsa_dtype x_dtype, void* x_c, nsa_dtype xc_dtype,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_c, int32_t batch,
+                          int32_t max_windows, int32_t heads, int32_t head_dim, int32_t kernel,
+                          int32_t stride, hipStream_t stream) {
+  NSA_REQUIRE(batch >= 0 && max_windows >= 0, NSA_ERR_INVALID_ARG, "nsa_compress_k: negative batch or max_windows");
+  NSA_REQUIRE(heads > 0 && head_dim > 0, NSA_ERR_INVALID_ARG, "nsa_compress_k: heads and head_dim must be positive");
+  NSA_REQUIRE(kernel >= 1 && stride >= 1, NSA_ERR_INVALID_ARG, "nsa_compress_k: kernel and stride must be >= 1");
+  NSA_REQUIRE(dtype_ok(x_dtype) && dtype_ok(xc_dtype), NSA_ERR_UNSUPPORTED, "nsa_compress_k: unknown dtype");
+  if (batch == 0 || max_windows == 0) return ok();
+  NSA_REQUIRE(x && x_c && cu_seqlens && cu_seqlens_c, NSA_ERR_INVALID_ARG, "nsa_compress_k: null pointer");
+  NSA_REQUIRE(aligned16(x) && aligned16(x_c), NSA_ERR_INVALID_ARG, "nsa_compress_k: tensors must be 16-byte aligned");
+  const long width = long(heads) * head_dim;
+  NSA_REQUIRE(width < (1L << 30), NSA_ERR_INVALID_ARG, "nsa_compress_k: row too wide");
+  return hip_status(nsa::launch_mean_pool(x, x_dtype == NSA_BF16, x_c, xc_dtype == NSA_BF16,
+                                          cu_seqlens, cu_seqlens_c, batch, max_windows,
+                                          int(width), kernel, stride, 0, stream),
+                    "nsa_compress_k");
+}
+
+nsa_status nsa_cis_mean_pool_varlen(const float* cis, float* cis_pooled, const int32_t* cu_seqlens,
+                                    const int32_t* cu_seqlens_c, int32_t batch,
+                                    int32_t max_windows, int32_t heads, int32_t kernel,
+                                    int32_t stride, hipStream_t stream) {
+  NSA_REQUIRE(batch >= 0 && max_windows >= 0, NSA_ERR_INVALID_ARG, "nsa_cis_mean_pool_varlen: negative batch or max_windows");
+  NSA_REQUIRE(heads > 0, NSA_ERR_INVALID_ARG, "nsa_cis_mean_pool_varlen: heads must be positive");
+  NSA_REQUIRE(kernel >= 1 && stride >= 1, NSA_ERR_INVALID_ARG, "nsa_cis_mean_pool_varlen: kernel and stride must be >= 1");
+  if (batch == 0 || max_windows == 0) return ok();
+  NSA_REQUIRE(cis && cis_pooled && cu_seqlens && cu_seqlens_c, NSA_ERR_INVALID_ARG, "nsa_cis_mean_pool_varlen: null pointer");
+  return hip_status(nsa::launch_mean_pool(cis, 0, cis_pooled, 0, cu_seqlens, cu_seqlens_c, batch,
+                                          max_windows, heads, kernel, stride, 0, stream),
+                    "nsa_cis_mean_pool_varlen");
+}
+
+size_t nsa_compressed_scores_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t heads,
+                                            int32_t kv_heads, int32_t kernel, int32_t stride) {
+  if (batch <= 0 || kv_heads <= 0 || heads <= 0 || kernel < 1 || stride < 1) return 0;
+  const int nc_max = full_windows(max_seqlen_k, kernel, stride);
+  return nsa::scores_ws_bytes(batch, kv_heads, heads / kv_heads, nc_max);
+}
+
+nsa_status nsa_compressed_scores(const void* q, nsa_dtype q_dtype, const void* k_c,
+                                 nsa_dtype kc_dtype, const float* cis_pooled, float cis_weight,
+                                 float* block_scores, float* window_probs,
+                                 const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_c,
+                                 int32_t batch, int32_t max_seqlen_k, int32_t heads,
+                                 int32_t kv_heads, int32_t head_dim, int32_t kernel,
+                                 int32_t stride, int32_t block_size, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_compressed_scores";
+  NSA_REQUIRE(batch >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG, "%s: negative batch or max_seqlen_k", fn);
+  NSA_REQUIRE(group_ok(heads, kv_heads), NSA_ERR_UNSUPPORTED, "%s: heads %d / kv_heads %d unsupported", fn, heads, kv_heads);
+  NSA_REQUIRE(dtype_ok(q_dtype) && dtype_ok(kc_dtype), NSA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  nsa_status st = check_geometry(fn, head_dim, kernel, stride, block_size);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(std::isfinite(cis_weight), NSA_ERR_INVALID_ARG, "%s: cis_weight must be finite", fn);
+  NSA_REQUIRE((max_seqlen_k + block_size - 1) / block_size <= nsa::kMaxSortBlocks, NSA_ERR_UNSUPPORTED,
+              "%s: more than %d blocks per sequence", fn, nsa::kMaxSortBlocks);
+  if (batch == 0) return ok();
+  NSA_REQUIRE(q && k_c && block_scores && cu_seqlens_k && cu_seqlens_c, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k_c), NSA_ERR_INVALID_ARG, "%s: q and k_c must be 16-byte aligned", fn);
+  const size_t need = nsa_compressed_scores_workspace_size(batch, max_seqlen_k, heads, kv_heads, kernel, stride);
+  NSA_REQUIRE(workspace != nullptr || need == 0, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  const int nc_max = full_windows(max_seqlen_k, kernel, stride);
+  nsa::DecodeScoresArgs a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == NSA_BF16;
+  a.kc = const_cast<void*>(k_c);
+  a.kc_bf16 = kc_dtype == NSA_BF16;
+  a.cis_pooled = cis_pooled;
+  a.cis_weight = cis_weight;
+  a.block_scores = block_scores;
+  a.window_probs = window_probs;
+  a.cu_k = cu_seqlens_k;
+  a.cu_c = cu_seqlens_c;
+  a.batch = batch;
+  a.max_seqlen_k = max_seqlen_k;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
+  a.ws = nsa::scores_ws_carve(workspace, batch, kv_heads, heads / kv_heads, nc_max);
+  return hip_status(nsa::launch_decode_scores(a, stream), fn);
+}
+
+nsa_status nsa_select_topk(const float* block_scores, int32_t* indices, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int32_t batch, int32_t rows_total,
+                           int32_t max_seqlen_k, int32_t kv_heads, int32_t n_blocks_max, int32_t k,
+                           int32_t n_init, int32_t n_local, int32_t block_size, hipStream_t stream) {
+  const char* fn = "nsa_select_topk";
+  NSA_REQUIRE(batch >= 0 && rows_total >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(kv_heads > 0, NSA_ERR_INVALID_ARG, "%s: kv_heads must be positive", fn);
+  NSA_REQUIRE(block_size == nsa::kBlock, NSA_ERR_UNSUPPORTED, "%s: block_size %d unsupported (64 only)", fn, block_size);
+  NSA_REQUIRE(k >= 1, NSA_ERR_INVALID_ARG, "%s: k must be >= 1", fn);
+  NSA_REQUIRE(n_init >= 0 && n_local >= 0 && n_init + n_local <= k, NSA_ERR_INVALID_ARG,
+              "%s: need 0 <= n_init, 0 <= n_local, n_init + n_local <= k", fn);
+  NSA_REQUIRE(n_blocks_max >= (max_seqlen_k + block_size - 1) / block_size, NSA_ERR_INVALID_ARG,
+              "%s: n_blocks_max %d < ceil(max_seqlen_k / block_size)", fn, n_blocks_max);
+  NSA_REQUIRE(n_blocks_max <= nsa::kMaxSortBlocks, NSA_ERR_UNSUPPORTED,
+              "%s: %d blocks per row exceed the supported %d", fn, n_blocks_max, nsa::kMaxSortBlocks);
+  if (cu_seqlens_q == nullptr)
+    NSA_REQUIRE(rows_total == batch, NSA_ERR_INVALID_ARG, "%s: decode needs rows_total == batch", fn);
+  if (rows_total == 0 || batch == 0) return ok();
+  NSA_REQUIRE(block_scores && indices && cu_seqlens_k, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  return hip_status(nsa::launch_select_topk(block_scores, indices, cu_seqlens_q, cu_seqlens_k, batch,
+                                            rows_total, kv_heads, n_blocks_max, k, n_init, n_local,
+                                            stream),
+                    fn);
+}
+
+size_t nsa_selected_attn_workspace_size(int32_t rows_total, int32_t heads, int32_t kv_heads,
+                                        int32_t head_dim, int32_t k_sel, int32_t decode) {
+  if (rows_total <= 0 || kv_heads <= 0 || heads <= 0 || k_sel <= 0 || head_dim != nsa::kHeadDim) return 0;
+  return nsa::attn_ws_bytes(rows_total, kv_heads, heads / kv_heads, k_sel, decode);
+}
+
+nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
+                                 const int32_t* indices, int32_t k_sel, const float* cis,
+                                 void* out, float* lse, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t batch, int32_t rows_total,
+                                 int32_t max_seqlen_k, int32_t heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t block_size, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_selected_attn_fwd";
+  NSA_REQUIRE(batch >= 0 && rows_total >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(dtype_ok(dtype), NSA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  NSA_REQUIRE(group_ok(heads, kv_heads), NSA_ERR_UNSUPPORTED, "%s: heads %d / kv_heads %d unsupported", fn, heads, kv_heads);
+  NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
+  NSA_REQUIRE(block_size == nsa::kBlock, NSA_ERR_UNSUPPORTED, "%s: block_size %d unsupported (64 only)", fn, block_size);
+  NSA_REQUIRE(k_sel >= 1, NSA_ERR_INVALID_ARG, "%s: k_sel must be >= 1", fn);
+  const int decode = cu_seqlens_q == nullptr;
+  NSA_REQUIRE(k_sel <= (decode ? kMaxDecodeSel : kMaxPrefillSel), NSA_ERR_UNSUPPORTED,
+              "%s: k_sel %d above the supported %d", fn, k_sel, decode ? kMaxDecodeSel : kMaxPrefillSel);
+  if (decode)
+    NSA_REQUIRE(rows_total == batch, NSA_ERR_INVALID_ARG, "%s: decode needs rows_total == batch", fn);
+  NSA_REQUIRE(!decode || rows_total <= 65535, NSA_ERR_UNSUPPORTED, "%s: decode batch above 65535", fn);
+  if (rows_total == 0 || batch == 0) return ok();
+  NSA_REQUIRE(q && k && v && indices && out && cu_seqlens_k, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), NSA_ERR_INVALID_ARG,
+              "%s: q, k, v, out must be 16-byte aligned", fn);
+  const size_t need = nsa_selected_attn_workspace_size(rows_total, heads, kv_heads, head_dim, k_sel, decode);
+  NSA_REQUIRE(workspace != nullptr || need == 0, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  const nsa::AttnWs ws = nsa::attn_ws_carve(workspace, rows_total, kv_heads, heads / kv_heads, k_sel, decode);
+  return hip_status(nsa::launch_selected_attn(q, k, v, dtype == NSA_BF16, indices, k_sel, cis, out,
+                                              lse, cu_seqlens_q, cu_seqlens_k, batch, rows_total,
+                                              heads, kv_heads, scale_log2_of(softmax_scale, head_dim),
+                                              ws, stream),
+                    fn);
+}
+
+// ------------------------------------------------------------------ decode step
+
+namespace {
+
+struct DecodeLayout {
+  size_t scores, indices, attn, total;
+};
+
+DecodeLayout decode_layout(const nsa_decode_params* p) {
+  DecodeLayout L{};
+  const int G = p->heads / p->kv_heads;
+  const int nc_max = full_windows(p->max_seqlen_k, p->kernel, p->stride);
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  L.scores = 0;
+  size_t off = up(nsa::scores_ws_bytes(p->batch, p->kv_heads, G, nc_max));
+  L.indices = off;
+  off += up(size_t(p->batch) * p->kv_heads * p->topk * sizeof(int32_t));
+  L.attn = off;
+  off += up(nsa::attn_ws_bytes(p->batch, p->kv_heads, G, p->topk, 1));
+  L.total = off;
+  return L;
+}
+
+nsa_status check_decode(const nsa_decode_params* p) {
+  const char* fn = "nsa_decode_step";
+  NSA_REQUIRE(p != nullptr, NSA_ERR_INVALID_ARG, "%s: params is null", fn);
+  NSA_REQUIRE(p->batch >= 0 && p->batch <= 65535 && p->max_seqlen_k >= 0, NSA_ERR_INVALID_ARG, "%s: bad batch or max_seqlen_k", fn);
+  NSA_REQUIRE(dtype_ok(p->dtype) && dtype_ok(p->kc_dtype), NSA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  NSA_REQUIRE(group_ok(p->heads, p->kv_heads), NSA_ERR_UNSUPPORTED, "%s: heads %d / kv_heads %d unsupported", fn, p->heads, p->kv_heads);
+  nsa_status st = check_geometry(fn, p->head_dim, p->kernel, p->stride, p->block_size);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(p->topk >= 1, NSA_ERR_INVALID_ARG, "%s: topk must be >= 1", fn);
+  NSA_REQUIRE(p->topk <= kMaxDecodeSel, NSA_ERR_UNSUPPORTED, "%s: topk %d above the supported %d", fn, p->topk, kMaxDecodeSel);
+  NSA_REQUIRE(p->n_init >= 0 && p->n_local >= 0 && p->n_init + p->n_local <= p->topk, NSA_ERR_INVALID_ARG,
+              "%s: need 0 <= n_init, 0 <= n_local, n_init + n_local <= topk", fn);
+  const int nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
+  NSA_REQUIRE(nb_max <= nsa::kMaxSortBlocks, NSA_ERR_UNSUPPORTED, "%s: %d blocks per sequence exceed the supported %d", fn, nb_max, nsa::kMaxSortBlocks);
+  NSA_REQUIRE(std::isfinite(p->cis_weight), NSA_ERR_INVALID_ARG, "%s: cis_weight must be finite", fn);
+  if (p->batch == 0) return NSA_OK;
+  NSA_REQUIRE(p->q && p->k && p->v && p->k_c && p->cu_seqlens_k && p->cu_seqlens_c && p->out,
+              NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(p->q) && aligned16(p->k) && aligned16(p->v) && aligned16(p->k_c) && aligned16(p->out),
+              NSA_ERR_INVALID_ARG, "%s: q, k, v, k_c, out must be 16-byte aligned", fn);
+  NSA_REQUIRE(!p->cis_values || p->cis != nullptr, NSA_ERR_INVALID_ARG, "%s: cis_values needs cis", fn);
+  NSA_REQUIRE(!(p->append_window && p->cis_pooled && !p->cis), NSA_ERR_INVALID_ARG,
+              "%s: refreshing cis_pooled needs cis", fn);
+  return NSA_OK;
+}
+
+}  // namespace
+
+size_t nsa_decode_workspace_size(const nsa_decode_params* p) {
+  if (check_decode(p) != NSA_OK || p->batch == 0) return 0;
+  return decode_layout(p).total;
+}
+
+nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* fn = "nsa_decode_step";
+  nsa_status st = check_decode(p);
+  if (st != NSA_OK) return st;
+  if (p->batch == 0) return ok();
+  const DecodeLayout lay = decode_layout(p);
+  NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= lay.total, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, lay.total);
+  char* base = static_cast<char*>(workspace);
+  const int G = p->heads / p->kv_heads;
+  const int nc_max = full_windows(p->max_seqlen_k, p->kernel, p->stride);
+  int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.indices);
+  const float sl2 = scale_log2_of(p->softmax_scale, p->head_dim);
+  nsa::DecodeScoresArgs a{};
+  a.q = p->q;
+  a.q_bf16 = p->dtype == NSA_BF16;
+  a.kc = p->k_c;
+  a.kc_bf16 = p->kc_dtype == NSA_BF16;
+  a.cis_pooled = p->cis_pooled;
+  a.cis_weight = p->cis_weight;
+  a.block_scores = p->block_scores;
+  a.window_probs = nullptr;
+  a.cu_k = p->cu_seqlens_k;
+  a.cu_c = p->cu_seqlens_c;
+  a.batch = p->batch;
+  a.max_seqlen_k = p->max_seqlen_k;
+  a.heads = p->heads;
+  a.kv_heads = p->kv_heads;
+  a.scale_log2 = sl2;
+  a.ws = nsa::scores_ws_carve(base + lay.scores, p->batch, p->kv_heads, G, nc_max);
+  a.indices = idx;
+  a.topk = p->topk;
+  a.n_init = p->n_init;
+  a.n_local = p->n_local;
+  if (p->append_window) {
+    a.refresh_k = p->k;
+    a.refresh_cis = p->cis_pooled ? p->cis : nullptr;
+    a.refresh_cis_pooled = p->cis_pooled;
+  }
+  hipError_t e = nsa::launch_decode_scores(a, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  const nsa::AttnWs aws = nsa::attn_ws_carve(base + lay.attn, p->batch, p->kv_heads, G, p->topk, 1);
+  e = nsa::launch_selected_attn(p->q, p->k, p->v, p->dtype == NSA_BF16, idx, p->topk,
+                                p->cis_values ? p->cis : nullptr, p->out, nullptr, nullptr,
+                                p->cu_seqlens_k, p->batch, p->batch, p->heads, p->kv_heads, sl2,
+                                aws, stream);
+  return hip_status(e, fn);
+}
+
+}  // extern "C"

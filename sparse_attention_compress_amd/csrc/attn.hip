@@ -1,0 +1,436 @@
+// Attention over selected KV blocks, GQA-grouped.
+//
+// What is computed (NOSA-1B core components, decode stage; TileLang NSA,
+// section 2): for a query row at position t and KV head g, the G query heads of
+// group g attend to every token j <= t of every listed block id (ids < 0 or with
+// 64*id > t are skipped), softmax(scale * q.k) . v; in CIS mode the softmax
+// weights are multiplied by cis_j and renormalised (values scaled by CIS,
+// divided by the same attention over all-ones values).
+//
+// Design (gfx950; decode is HBM-bound): one workgroup of 4 waves serves one
+// (row, kv head) and a run of selected blocks.  Wave w owns tokens 16w..16w+15
+// of every block and keeps its own online-softmax state, so the block loop has
+// no workgroup barrier.  For q.k a quad of lanes shares a key row (each lane a
+// 32-dim slice via 16-byte loads; the G query heads come from LDS; bf16 products
+// use v_dot2_f32_bf16); for p.v each lane owns 8 dims of 4 tokens, so V rows
+// are read as whole 256-byte lines.  The K/V of the next block are loaded into a
+// second register buffer while the current block is computed.  Every selected
+// K/V byte is fetched from HBM once for the whole query group.  Softmax runs in
+// the exp2 domain (log2 e folded into the scale).
+// Decode splits the selected blocks of a (row, kv head) over several workgroups
+// that write partial (max, sum, acc); combine_kernel merges them.  Prefill rows
+// use one workgroup per (row, kv head) and write the output directly.
+#include "common.h"
+#include "launch.h"
+
+namespace nsa {
+
+template <typename T>
+struct Row8;
+
+template <>
+struct Row8<bf16_t> {
+  uint4 r;
+  __device__ __forceinline__ void load(const bf16_t* p) { r = ld16(p); }
+  __device__ __forceinline__ void zero() { r = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ float f(int e) const {
+    const uint32_t x = (e >> 1) == 0 ? r.x : (e >> 1) == 1 ? r.y : (e >> 1) == 2 ? r.z : r.w;
+    return (e & 1) ? bf16hi(x) : bf16lo(x);
+  }
+};
+
+template <>
+struct Row8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() {
+    a = make_float4(0.f, 0.f, 0.f, 0.f);
+    b = a;
+  }
+  __device__ __forceinline__ float f(int e) const {
+    switch (e) {
+      case 0: return a.x; case 1: return a.y; case 2: return a.z; case 3: return a.w;
+      case 4: return b.x; case 5: return b.y; case 6: return b.z; default: return b.w;
+    }
+  }
+};
+
+template <typename T>
+struct BlockRegs {
+  Row8<T> k[4];  // q.k slice of this lane's token
+  Row8<T> v[4];  // p.v slice of this lane's 4 tokens
+  float cw;      // CIS weight of this lane's q.k token
+};
+
+__device__ __forceinline__ void attn_row_position(int row, const int* __restrict__ cu_q,
+                                                  const int* __restrict__ cu_k, int batch,
+                                                  int& b, int& t) {
+  if (cu_q == nullptr) {
+    b = row;
+    t = cu_k[b + 1] - cu_k[b] - 1;
+    return;
+  }
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  b = lo;
+  t = (row - cu_q[b]) + ((cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]));
+}
+
+constexpr int kMaxWgSlots = 64;  // selected-block slots one workgroup stages at once
+
+template <int G, typename T, bool CIS, bool SPLIT>
+__global__ __launch_bounds__(256) void selected_attn_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
+    T* __restrict__ out, float* __restrict__ lse, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int batch, int kv_heads, float scale_log2, int bpw,
+    float2* __restrict__ part_ml, float* __restrict__ part_acc) {
+  constexpr int D = kHeadDim;
+  constexpr bool kBF16 = sizeof(T) == 2;
+  __shared__ uint32_t q_s[kBF16 ? G * D / 2 : G * D];  // bf16 pairs or fp32 values
+  __shared__ float p_s[4][16][G];
+  __shared__ float m_s[4][G], l_s[4][G];
+  __shared__ float acc_s[4][G][D];
+  __shared__ int ids_s[kMaxWgSlots];
+  __shared__ int nv_s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kv = blockIdx.y;
+  const int row = SPLIT ? int(blockIdx.z) : int(blockIdx.x);
+  const int split = SPLIT ? int(blockIdx.x) : 0;
+  int b, t;
+  attn_row_position(row, cu_q, cu_k, batch, b, t);
+  const int kstart = cu_k[b];
+  const size_t unit = size_t(row) * kv_heads + kv;
+  const int s_begin = split * bpw;
+  const int s_end = SPLIT ? min(k_sel, s_begin + bpw) : k_sel;
+
+  // stage the usable block ids of this workgroup (in list order) and the queries
+  if (wave == 0) {
+    int base = 0;
+    for (int s0 = s_begin; s0 < s_end; s0 += kWave) {
+      const int sl = s0 + lane;
+      const int id = sl < s_end ? indices[unit * k_sel + sl] : -1;
+      const bool ok = id >= 0 && id * kBlock <= t;
+      const unsigned long long mask = __ballot(ok);
+      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+      if (ok && pos < kMaxWgSlots) ids_s[pos] = id;
+      base += __popcll(mask);
+    }
+    if (lane == 0) nv_s = min(base, kMaxWgSlots);
+  }
+  {
+    const uint32_t* qg = reinterpret_cast<const uint32_t*>(q + unit * G * D);
+    constexpr int kWords = kBF16 ? G * D / 2 : G * D;
+#pragma unroll
+    for (int i = 0; i < (kWords + 255) / 256; ++i)
+      if (tid + 256 * i < kWords) q_s[tid + 256 * i] = qg[tid + 256 * i];
+  }
+  __syncthreads();
+  const int nv = nv_s;
+
+  const int tok = lane >> 2, r = lane & 3;   // q.k: token of the wave, 32-dim slice
+  const int u = lane >> 4, o = lane & 15;    // p.v: token quarter, 8-dim slice
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+  }
+  const size_t rs = size_t(kv_heads) * D;  // elements between consecutive tokens
+  const T* kbase = k + size_t(kstart) * rs + size_t(kv) * D;
+  const T* vbase = v + size_t(kstart) * rs + size_t(kv) * D;
+
+  auto load_block = [&](int id, BlockRegs<T>& R) {
+    const int j0 = id * kBlock + wave * 16;
+    const int jq = j0 + tok;
+    if (jq <= t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.k[i].load(kbase + size_t(jq) * rs + 32 * i + 8 * r);
+      if (CIS) R.cw = cis[(size_t(kstart) + jq) * kv_heads + kv];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.k[i].zero();
+      R.cw = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jv = j0 + 4 * u + e;
+      if (jv <= t) R.v[e].load(vbase + size_t(jv) * rs + 8 * o); else R.v[e].zero();
+    }
+  };
+
+  auto compute_block = [&](int id, const BlockRegs<T>& R) {
+    const bool qvalid = id * kBlock + wave * 16 + tok <= t;
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if constexpr (kBF16) {
+          const uint4 qv = *reinterpret_cast<const uint4*>(&q_s[h * (D / 2) + 16 * i + 4 * r]);
+          const uint4 kk = reinterpret_cast<const Row8<bf16_t>&>(R.k[i]).r;
+          s[h] = dot2_bf16(qv.x, kk.x, s[h]);
+          s[h] = dot2_bf16(qv.y, kk.y, s[h]);
+          s[h] = dot2_bf16(qv.z, kk.z, s[h]);
+          s[h] = dot2_bf16(qv.w, kk.w, s[h]);
+        } else {
+          const float* qq = reinterpret_cast<const float*>(&q_s[h * D + 32 * i + 8 * r]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[h] = fmaf(qq[e], R.k[i].f(e), s[h]);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s[h] += __shfl_xor(s[h], 1, kWave);
+      s[h] += __shfl_xor(s[h], 2, kWave);
+      s[h] = qvalid ? s[h] * scale_log2 : -INFINITY;
+    }
+    const float cw = CIS ? R.cw : 1.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(m[h], wave_max(s[h]));
+      float alpha = 1.f, p = 0.f;
+      if (mn != -INFINITY) {
+        alpha = fast_exp2(m[h] - mn);
+        p = fast_exp2(s[h] - mn) * cw;
+      }
+      l[h] = l[h] * alpha + p;
+      m[h] = mn;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] *= alpha;
+      if (r == 0) p_s[wave][tok][h] = p;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float pe[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pe[h] = p_s[wave][4 * u + e][h];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const float vf = R.v[e].f(d);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h][d] = fmaf(pe[h], vf, acc[h][d]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  BlockRegs<T> A, B;
+  if (nv > 0) load_block(ids_s[0], A);
+  for (int i = 0; i < nv; i += 2) {
+    const int id0 = ids_s[i];
+    const bool has1 = i + 1 < nv;
+    const int id1 = has1 ? ids_s[i + 1] : 0;
+    if (has1) load_block(id1, B);
+    compute_block(id0, A);
+    if (has1) {
+      if (i + 2 < nv) load_block(ids_s[i + 2], A);
+      compute_block(id1, B);
+    }
+  }
+
+  // wave totals: l counted once per quad lane, acc summed over the 4 token quarters
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float lw = wave_sum(l[h]) * 0.25f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      acc[h][d] += __shfl_xor(acc[h][d], 16, kWave);
+      acc[h][d] += __shfl_xor(acc[h][d], 32, kWave);
+    }
+    if (lane == 0) {
+      m_s[wave][h] = m[h];
+      l_s[wave][h] = lw;
+    }
+    if (u == 0) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc_s[wave][h][8 * o + d] = acc[h][d];
+    }
+  }
+  __syncthreads();
+
+  const int n_split = SPLIT ? int(gridDim.x) : 1;
+#pragma unroll
+  for (int it = 0; it < G * D / 256; ++it) {
+    const int i = tid + 256 * it;
+    const int h = i / D, d = i % D;
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = m_s[w][h];
+      M = fmaxf(M, mw[w]);
+    }
+    float L = 0.f, Acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = fast_exp2(mw[w] - M);
+        L += f * l_s[w][h];
+        Acc += f * acc_s[w][h][d];
+      }
+    }
+    if constexpr (SPLIT) {
+      const size_t ps = unit * n_split + split;
+      part_acc[(ps * G + h) * D + d] = Acc;
+      if (d == 0) part_ml[ps * G + h] = make_float2(M, L);
+    } else {
+      store_f32(out + (unit * G + h) * D + d, L > 0.f ? Acc / L : 0.f);
+      if (lse != nullptr && d == 0)
+        lse[unit * G + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// Merge the per-split partial states of one (row, kv head, query head): grid
+// (units, G), one thread per output dim.
+template <typename T>
+__global__ __launch_bounds__(kHeadDim) void combine_kernel(const float2* __restrict__ part_ml,
+                                                           const float* __restrict__ part_acc,
+                                                           T* __restrict__ out,
+                                                           float* __restrict__ lse, int n_split,
+                                                           int G) {
+  constexpr int D = kHeadDim;
+  __shared__ float f_s[kMaxSplits];
+  __shared__ float ML_s[2];
+  const size_t unit = blockIdx.x;
+  const int h = blockIdx.y, d = threadIdx.x;
+  float2 ml = make_float2(-INFINITY, 0.f);
+  if (d < n_split) ml = part_ml[(unit * n_split + d) * G + h];
+  // max and normaliser over the splits (n_split <= 64: one wave holds them all)
+  float M = ml.x;
+  if (d < kWave) {
+    M = wave_max(d < n_split ? ml.x : -INFINITY);
+    const float f = (d < n_split && M != -INFINITY) ? fast_exp2(ml.x - M) : 0.f;
+    const float L = wave_sum(f * ml.y);
+    if (d < n_split) f_s[d] = f;
+    if (d == 0) {
+      ML_s[0] = M;
+      ML_s[1] = L;
+    }
+  }
+  __syncthreads();
+  const float L = ML_s[1];
+  float accv = 0.f;
+  const float* src = part_acc + (unit * n_split * G + h) * D + d;
+  const size_t stride = size_t(G) * D;
+  int sp = 0;
+  for (; sp + 8 <= n_split; sp += 8) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = src[(sp + e) * stride];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accv += f_s[sp + e] * x[e];
+  }
+  for (; sp < n_split; ++sp) accv += f_s[sp] * src[sp * stride];
+  store_f32(out + (unit * G + h) * D + d, L > 0.f ? accv / L : 0.f);
+  if (lse != nullptr && d == 0) lse[unit * G + h] = L > 0.f ? (ML_s[0] + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// --------------------------------------------------------------------------- host
+
+int attn_split_blocks(int batch, int kv_heads, int k_sel) {
+  // enough workgroups to give every CU two, at most 8 blocks each, <= kMaxSplits splits
+  const int units = batch * kv_heads;
+  int bpw = 8;
+  while (bpw > 1 && units * ((k_sel + bpw - 1) / bpw) < 512) bpw >>= 1;
+  while ((k_sel + bpw - 1) / bpw > kMaxSplits) bpw <<= 1;
+  return bpw;
+}
+
+size_t attn_ws_bytes(int rows_total, int kv_heads, int group, int k_sel, int decode) {
+  if (!decode) return 0;
+  const size_t units = size_t(rows_total) * kv_heads;
+  const int bpw = attn_split_blocks(rows_total, kv_heads, k_sel);
+  const size_t n_split = (size_t(k_sel) + bpw - 1) / bpw;
+  size_t bytes = ((units * n_split * group * sizeof(float2)) + 255) & ~size_t(255);
+  bytes += ((units * n_split * group * kHeadDim * sizeof(float)) + 255) & ~size_t(255);
+  return bytes;
+}
+
+AttnWs attn_ws_carve(void* base, int rows_total, int kv_heads, int group, int k_sel, int decode) {
+  AttnWs ws{nullptr, nullptr};
+  if (!decode) return ws;
+  const size_t units = size_t(rows_total) * kv_heads;
+  const int bpw = attn_split_blocks(rows_total, kv_heads, k_sel);
+  const size_t n_split = (size_t(k_sel) + bpw - 1) / bpw;
+  char* p = static_cast<char*>(base);
+  ws.part_ml = reinterpret_cast<float2*>(p);
+  p += (units * n_split * group * sizeof(float2) + 255) & ~size_t(255);
+  ws.part_acc = reinterpret_cast<float*>(p);
+  return ws;
+}
+
+template <int G, typename T, bool CIS>
+static hipError_t launch_attn_g(const void* q, const void* k, const void* v, const int* indices,
+                                int k_sel, const float* cis, void* out, float* lse,
+                                const int* cu_q, const int* cu_k, int batch, int rows_total,
+                                int kv_heads, float scale_log2, const AttnWs& ws, hipStream_t s) {
+  if (rows_total == 0 || k_sel == 0) return hipSuccess;
+  if (cu_q == nullptr) {
+    const int bpw = attn_split_blocks(rows_total, kv_heads, k_sel);
+    const int n_split = (k_sel + bpw - 1) / bpw;
+    hipError_t e = launch_kernel(
+        kKindAttn, selected_attn_kernel<G, T, CIS, true>, dim3(n_split, kv_heads, rows_total),
+        dim3(256), s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+        indices, k_sel, cis, static_cast<T*>(out), lse, cu_q, cu_k, batch, kv_heads, scale_log2,
+        bpw, ws.part_ml, ws.part_acc);
+    if (e != hipSuccess) return e;
+    return launch_kernel(kKindCombine, combine_kernel<T>, dim3(rows_total * kv_heads, G),
+                         dim3(kHeadDim), s, static_cast<const float2*>(ws.part_ml),
+                         static_cast<const float*>(ws.part_acc), static_cast<T*>(out), lse,
+                         n_split, G);
+  }
+  return launch_kernel(kKindAttn, selected_attn_kernel<G, T, CIS, false>,
+                       dim3(rows_total, kv_heads, 1), dim3(256), s, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), indices, k_sel, cis,
+                       static_cast<T*>(out), lse, cu_q, cu_k, batch, kv_heads, scale_log2, k_sel,
+                       static_cast<float2*>(nullptr), static_cast<float*>(nullptr));
+}
+
+template <typename T, bool CIS>
+static hipError_t launch_attn_t(int G, const void* q, const void* k, const void* v,
+                                const int* idx, int k_sel, const float* cis, void* out, float* lse,
+                                const int* cu_q, const int* cu_k, int batch, int rows,
+                                int kvh, float sl2, const AttnWs& ws, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_attn_g<1, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
+    case 2: return launch_attn_g<2, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
+    case 4: return launch_attn_g<4, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
+    case 8: return launch_attn_g<8, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
+    case 16: return launch_attn_g<16, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int bf16,
+                                const int* indices, int k_sel, const float* cis, void* out,
+                                float* lse, const int* cu_q, const int* cu_k, int batch,
+                                int rows_total, int heads, int kv_heads, float scale_log2,
+                                const AttnWs& ws, hipStream_t s) {
+  const int G = heads / kv_heads;
+  if (bf16) {
+    if (cis) return launch_attn_t<bf16_t, true>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
+    return launch_attn_t<bf16_t, false>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
+  }
+  if (cis) return launch_attn_t<float, true>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
+  return launch_attn_t<float, false>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
+}
+
+}  // namespace nsa

@@ -1,0 +1,114 @@
+// Internal launchers behind the C ABI (host side).  Arguments are validated by
+// the API layer before any of these is called.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nsa {
+
+// Window geometry the scoring kernels are compiled for.
+constexpr int kKernel = 32;
+constexpr int kStride = 16;
+constexpr int kBlock = 64;
+constexpr int kHeadDim = 128;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Windows per workgroup of the logits kernel; blocks per workgroup of the
+// block-score kernel; the largest per-row block count the top-k sort holds.
+constexpr int kChunkWindows = 64;
+constexpr int kBlocksPerWG = 256;
+constexpr int kMaxSortBlocks = 4096;
+// Partial states one decode (row, kv head) may be split into.
+constexpr int kMaxSplits = 64;
+
+// Kernel kinds that a profiling request can target.
+enum KernelKind {
+  kKindPool = 0,
+  kKindLogits = 1,
+  kKindBlockScores = 2,
+  kKindAttn = 3,
+  kKindCombine = 4,
+  kKindCount = 5
+};
+
+// One armed (start, stop) event pair per kernel kind, per host thread.
+struct ProfSlot {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  bool armed = false;
+};
+ProfSlot& prof_slot(int kind);
+
+// Launch `kernel`; if a profiling request is armed for `kind`, the launch records
+// its events at the kernel's own start and end (hipExtLaunchKernelGGL) and the
+// request is consumed.
+template <typename Kernel, typename... Args>
+hipError_t launch_kernel(int kind, Kernel kernel, dim3 grid, dim3 block, hipStream_t s,
+                         Args... args) {
+  ProfSlot& p = prof_slot(kind);
+  if (p.armed) {
+    p.armed = false;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, p.start, p.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mean_pool(const void* x, int x_bf16, void* y, int y_bf16, const int* cu,
+                            const int* cuc, int batch, int max_windows, int width, int kernel,
+                            int stride, int last_n, hipStream_t s);
+
+// Scoring workspace carve-up (decode rows).
+struct ScoresWs {
+  float* logits;  // [batch, kv_heads, G, nc_max] scaled log2-domain logits
+  float2* part;   // [batch, kv_heads, n_chunk_max, G] chunk (max, sum of exp2)
+};
+size_t scores_ws_bytes(int batch, int kv_heads, int group, int nc_max);
+ScoresWs scores_ws_carve(void* base, int batch, int kv_heads, int group, int nc_max);
+
+struct DecodeScoresArgs {
+  const void* q;
+  int q_bf16;
+  void* kc;  // compressed keys; its newest window is rewritten when refresh_k is set
+  int kc_bf16;
+  const float* cis_pooled;  // nullable: fused into the block score with cis_weight
+  float cis_weight;
+  float* block_scores;  // nullable output
+  float* window_probs;  // nullable output
+  const int* cu_k;
+  const int* cu_c;
+  int batch, max_seqlen_k, heads, kv_heads;
+  float scale_log2;
+  ScoresWs ws;
+  int* indices;  // nullable: no selection
+  int topk, n_init, n_local;
+  const void* refresh_k;       // nullable: recompute the newest window from these keys
+  const float* refresh_cis;    // nullable: and the newest pooled CIS from these scores
+  float* refresh_cis_pooled;   // where that pooled CIS goes
+};
+hipError_t launch_decode_scores(const DecodeScoresArgs& a, hipStream_t s);
+
+hipError_t launch_select_topk(const float* block_scores, int* indices, const int* cu_q,
+                              const int* cu_k, int batch, int rows_total, int kv_heads,
+                              int nb_max, int topk, int n_init, int n_local, hipStream_t s);
+
+// Attention workspace carve-up.
+struct AttnWs {
+  float2* part_ml;  // [units, n_split, G] (max, sum) per split
+  float* part_acc;  // [units, n_split, G, D]
+};
+int attn_split_blocks(int batch, int kv_heads, int k_sel);  // selected blocks per workgroup
+size_t attn_ws_bytes(int rows_total, int kv_heads, int group, int k_sel, int decode);
+AttnWs attn_ws_carve(void* base, int rows_total, int kv_heads, int group, int k_sel, int decode);
+
+hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int bf16,
+                                const int* indices, int k_sel, const float* cis, void* out,
+                                float* lse, const int* cu_q, const int* cu_k, int batch,
+                                int rows_total, int heads, int kv_heads, float scale_log2,
+                                const AttnWs& ws, hipStream_t s);
+
+}  // namespace nsa

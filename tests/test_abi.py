@@ -1,0 +1,119 @@
+"""The C ABI: the built library loads, exports every function include/nsa.h
+declares, and rejects bad arguments on the host (before any launch), so these
+run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_compress_amd as nsa
+
+pytestmark = pytest.mark.skipif(not os.path.exists(nsa.LIB_PATH), reason="libnsa.so not built")
+
+
+def _declared():
+    text = open(nsa.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_hot_path():
+    names = _declared()
+    for n in ("nsa_compress_k", "nsa_compressed_scores", "nsa_cis_mean_pool_varlen",
+              "nsa_select_topk", "nsa_selected_attn_fwd", "nsa_decode_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(nsa.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+    assert nsa.lib().nsa_version() >= 100
+
+
+def test_binding_covers_every_declared_entry_point():
+    for n in _declared():
+        assert n in nsa._SIGS, n
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def test_unsupported_geometry_is_rejected():
+    L = nsa.lib()
+    st = L.nsa_compressed_scores(FAKE, 1, FAKE, 0, None, 1.0, FAKE, None, FAKE, FAKE, 2, 4096, 16, 2,
+                                 64, 32, 16, 64, 0.0, FAKE, 1 << 20, None)
+    assert st == 2 and "head_dim" in nsa.last_error()
+    st = L.nsa_compressed_scores(FAKE, 1, FAKE, 0, None, 1.0, FAKE, None, FAKE, FAKE, 2, 4096, 16, 2,
+                                 128, 64, 32, 64, 0.0, FAKE, 1 << 20, None)
+    assert st == 2 and "window" in nsa.last_error()
+    st = L.nsa_compressed_scores(FAKE, 1, FAKE, 0, None, 1.0, FAKE, None, FAKE, FAKE, 2, 4096, 16, 3,
+                                 128, 32, 16, 64, 0.0, FAKE, 1 << 20, None)
+    assert st == 2
+
+
+def test_workspace_too_small_and_nulls():
+    L = nsa.lib()
+    need = L.nsa_compressed_scores_workspace_size(2, 4096, 16, 2, 32, 16)
+    assert need > 0
+    st = L.nsa_compressed_scores(FAKE, 1, FAKE, 0, None, 1.0, FAKE, None, FAKE, FAKE, 2, 4096, 16, 2,
+                                 128, 32, 16, 64, 0.0, FAKE, need - 1, None)
+    assert st == 3
+    st = L.nsa_compressed_scores(None, 1, FAKE, 0, None, 1.0, FAKE, None, FAKE, FAKE, 2, 4096, 16, 2,
+                                 128, 32, 16, 64, 0.0, FAKE, need, None)
+    assert st == 1
+
+
+def test_select_argument_checks():
+    L = nsa.lib()
+    # forced blocks larger than k
+    assert L.nsa_select_topk(FAKE, FAKE, None, FAKE, 1, 1, 4096, 2, 64, 4, 2, 3, 64, None) == 1
+    # n_blocks_max too small for max_seqlen_k
+    assert L.nsa_select_topk(FAKE, FAKE, None, FAKE, 1, 1, 4096, 2, 63, 16, 1, 2, 64, None) == 1
+    # too many blocks per row for the in-LDS sort
+    assert L.nsa_select_topk(FAKE, FAKE, None, FAKE, 1, 1, 1 << 20, 2, 1 << 14, 16, 1, 2, 64, None) == 2
+    # decode needs rows == batch
+    assert L.nsa_select_topk(FAKE, FAKE, None, FAKE, 2, 3, 4096, 2, 64, 16, 1, 2, 64, None) == 1
+    # empty batch is a no-op
+    assert L.nsa_select_topk(None, None, None, None, 0, 0, 0, 2, 0, 16, 1, 2, 64, None) == 0
+
+
+def test_attention_and_pool_checks():
+    L = nsa.lib()
+    st = L.nsa_selected_attn_fwd(FAKE, FAKE, FAKE, 1, FAKE, 16, None, FAKE, None, None, FAKE, 2, 2, 4096,
+                                 16, 2, 96, 64, 0.0, FAKE, 1 << 20, None)
+    assert st == 2
+    st = L.nsa_selected_attn_fwd(FAKE, FAKE, FAKE, 7, FAKE, 16, None, FAKE, None, None, FAKE, 2, 2, 4096,
+                                 16, 2, 128, 64, 0.0, FAKE, 1 << 20, None)
+    assert st == 2
+    misaligned = ctypes.c_void_p(0x1008)
+    st = L.nsa_selected_attn_fwd(misaligned, FAKE, FAKE, 1, FAKE, 16, None, FAKE, None, None, FAKE, 2, 2,
+                                 4096, 16, 2, 128, 64, 0.0, FAKE, 1 << 20, None)
+    assert st == 1 and "aligned" in nsa.last_error()
+    assert L.nsa_compress_k(FAKE, 1, FAKE, 0, FAKE, FAKE, 1, 10, 2, 128, 0, 16, None) == 1
+    assert L.nsa_cis_mean_pool_varlen(None, FAKE, FAKE, FAKE, 1, 10, 2, 32, 16, None) == 1
+    assert L.nsa_cis_mean_pool_varlen(None, None, None, None, 0, 0, 2, 32, 16, None) == 0
+
+
+def test_decode_step_checks():
+    import torch
+    p = nsa.DecodeParams()
+    p.batch, p.max_seqlen_k, p.heads, p.kv_heads, p.head_dim = 2, 4096, 16, 2, 128
+    p.kernel, p.stride, p.block_size = 32, 16, 64
+    p.topk, p.n_init, p.n_local = 16, 1, 2
+    p.dtype, p.kc_dtype = nsa.NSA_BF16, nsa.NSA_F32
+    # all pointers null -> invalid argument, and no workspace size
+    assert nsa.decode_workspace_size(p) == 0
+    assert nsa.lib().nsa_decode_step(ctypes.byref(p), None, 0, None) == 1
+    for f in ("q", "k", "v", "k_c", "cu_seqlens_k", "cu_seqlens_c", "out"):
+        setattr(p, f, 0x1000)
+    need = nsa.decode_workspace_size(p)
+    assert need > 0
+    assert nsa.lib().nsa_decode_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need - 1, None) == 3
+    p.cis_values = 1   # CIS values without cis
+    assert nsa.lib().nsa_decode_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 1
+    p.cis_values = 0
+    p.n_local = 16     # forced blocks exceed topk
+    assert nsa.lib().nsa_decode_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 1
+    assert torch is not None

@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=280)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps one by one instead of from a HIP graph "
+                         "(for counter-collection runs, which serialise dispatches)")
     return ap.parse_args()
 
 
@@ -110,16 +113,30 @@ def main():
                 step(i)
         return g
 
-    g_warm = capture(max(1, args.warmup))
-    g_timed = capture(args.steps)
+    if args.eager:
+        def run(n):
+            with torch.cuda.stream(stream):
+                for i in range(n):
+                    step(i)
+    else:
+        g_warm = capture(max(1, args.warmup))
+        g_timed = capture(args.steps)
+        run = None
     torch.cuda.synchronize()
-    g_warm.replay()
+    if args.eager:
+        run(args.warmup)
+    else:
+        g_warm.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    g_timed.replay()
+    if args.eager:
+        run(args.steps)
+    else:
+        with torch.cuda.stream(stream):
+            g_timed.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()

@@ -125,8 +125,7 @@ nsa_status nsa_cis_mean_pool_varlen(const float* cis, float* cis_pooled, const i
 size_t nsa_compressed_scores_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t heads,
                                             int32_t kv_heads, int32_t kernel, int32_t stride) {
   if (batch <= 0 || kv_heads <= 0 || heads <= 0 || kernel < 1 || stride < 1) return 0;
-  const int nc_max = full_windows(max_seqlen_k, kernel, stride);
-  return nsa::scores_ws_bytes(batch, kv_heads, heads / kv_heads, nc_max);
+  return nsa::scores_ws_bytes(batch, kv_heads, heads / kv_heads, max_seqlen_k);
 }
 
 nsa_status nsa_compressed_scores(const void* q, nsa_dtype q_dtype, const void* k_c,
@@ -152,13 +151,12 @@ nsa_status nsa_compressed_scores(const void* q, nsa_dtype q_dtype, const void* k
   const size_t need = nsa_compressed_scores_workspace_size(batch, max_seqlen_k, heads, kv_heads, kernel, stride);
   NSA_REQUIRE(workspace != nullptr || need == 0, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
   NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
-  const int nc_max = full_windows(max_seqlen_k, kernel, stride);
   nsa::DecodeScoresArgs a{};
   a.q = q;
   a.q_bf16 = q_dtype == NSA_BF16;
   a.kc = const_cast<void*>(k_c);
   a.kc_bf16 = kc_dtype == NSA_BF16;
-  a.cis_pooled = cis_pooled;
+  a.cis_pooled = const_cast<float*>(cis_pooled);  // read only: no refresh here
   a.cis_weight = cis_weight;
   a.block_scores = block_scores;
   a.window_probs = window_probs;
@@ -169,7 +167,7 @@ nsa_status nsa_compressed_scores(const void* q, nsa_dtype q_dtype, const void* k
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
-  a.ws = nsa::scores_ws_carve(workspace, batch, kv_heads, heads / kv_heads, nc_max);
+  a.ws = nsa::scores_ws_carve(workspace, batch, kv_heads, heads / kv_heads, max_seqlen_k);
   return hip_status(nsa::launch_decode_scores(a, stream), fn);
 }
 
@@ -250,10 +248,9 @@ struct DecodeLayout {
 DecodeLayout decode_layout(const nsa_decode_params* p) {
   DecodeLayout L{};
   const int G = p->heads / p->kv_heads;
-  const int nc_max = full_windows(p->max_seqlen_k, p->kernel, p->stride);
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   L.scores = 0;
-  size_t off = up(nsa::scores_ws_bytes(p->batch, p->kv_heads, G, nc_max));
+  size_t off = up(nsa::scores_ws_bytes(p->batch, p->kv_heads, G, p->max_seqlen_k));
   L.indices = off;
   off += up(size_t(p->batch) * p->kv_heads * p->topk * sizeof(int32_t));
   L.attn = off;
@@ -306,7 +303,6 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
   NSA_REQUIRE(workspace_bytes >= lay.total, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, lay.total);
   char* base = static_cast<char*>(workspace);
   const int G = p->heads / p->kv_heads;
-  const int nc_max = full_windows(p->max_seqlen_k, p->kernel, p->stride);
   int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.indices);
   const float sl2 = scale_log2_of(p->softmax_scale, p->head_dim);
   nsa::DecodeScoresArgs a{};
@@ -325,7 +321,7 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
   a.heads = p->heads;
   a.kv_heads = p->kv_heads;
   a.scale_log2 = sl2;
-  a.ws = nsa::scores_ws_carve(base + lay.scores, p->batch, p->kv_heads, G, nc_max);
+  a.ws = nsa::scores_ws_carve(base + lay.scores, p->batch, p->kv_heads, G, p->max_seqlen_k);
   a.indices = idx;
   a.topk = p->topk;
   a.n_init = p->n_init;
@@ -333,7 +329,6 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
   if (p->append_window) {
     a.refresh_k = p->k;
     a.refresh_cis = p->cis_pooled ? p->cis : nullptr;
-    a.refresh_cis_pooled = p->cis_pooled;
   }
   hipError_t e = nsa::launch_decode_scores(a, stream);
   if (e != hipSuccess) return hip_status(e, fn);

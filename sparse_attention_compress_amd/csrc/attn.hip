@@ -85,7 +85,7 @@ __device__ __forceinline__ void attn_row_position(int row, const int* __restrict
 constexpr int kMaxWgSlots = 64;  // selected-block slots one workgroup stages at once
 
 template <int G, typename T, bool CIS, bool SPLIT>
-__global__ __launch_bounds__(256) void selected_attn_kernel(
+__global__ __launch_bounds__(256) void selected_attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
     T* __restrict__ out, float* __restrict__ lse, const int* __restrict__ cu_q,
@@ -298,6 +298,220 @@ __global__ __launch_bounds__(256) void selected_attn_kernel(
   }
 }
 
+// bf16 variant on the matrix cores.  Per wave and block: the wave's 16 tokens
+// against the group's query heads padded to 16 columns, S^T = K Q^T with four
+// v_mfma_f32_16x16x32_bf16 (K rows straight from HBM in the A-operand layout,
+// Q^T held in registers); lane (row r, column c) then holds the scores of tokens
+// 4r..4r+3 for head c, so the softmax needs only in-lane work plus two lane
+// swaps for the wave maximum; O^T += V^T P^T with eight v_mfma_f32_16x16x16_bf16
+// takes P^T in exactly that layout (two packed conversions) and V^T from 2-byte
+// loads.  No LDS and no shuffles inside the block loop.  The running maximum is
+// only raised when a block exceeds it by more than 2^8, so rescaling is rare.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool CIS>
+struct MfmaBlockRegs {
+  uint4 k[4];      // A operand of S^T = K Q^T: token c16, dims 32i + 8 r4 .. +8
+  uint32_t v[16];  // A operand of O^T = V^T P^T: dim 16n + c16, tokens 4 r4 + 2m, +1
+  float cw[4];     // CIS of tokens 4 r4 + e
+};
+
+__device__ __forceinline__ uint32_t ld_u16(const bf16_t* p) {
+  return uint32_t(*reinterpret_cast<const uint16_t*>(p));
+}
+
+template <int G, bool CIS, bool SPLIT>
+__global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
+    bf16_t* __restrict__ out, float* __restrict__ lse, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int batch, int kv_heads, float scale_log2, int bpw,
+    float2* __restrict__ part_ml, float* __restrict__ part_acc) {
+  static_assert(G <= 16, "one MFMA column per query head");
+  constexpr int D = kHeadDim;
+  constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
+  __shared__ float m_s[4][G], l_s[4][G];
+  __shared__ float acc_s[4][G][D];
+  __shared__ int ids_s[kMaxWgSlots];
+  __shared__ int nv_s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const int kv = blockIdx.y;
+  const int row = SPLIT ? int(blockIdx.z) : int(blockIdx.x);
+  const int split = SPLIT ? int(blockIdx.x) : 0;
+  int b, t;
+  attn_row_position(row, cu_q, cu_k, batch, b, t);
+  const int kstart = cu_k[b];
+  const size_t unit = size_t(row) * kv_heads + kv;
+  const int s_begin = split * bpw;
+  const int s_end = SPLIT ? min(k_sel, s_begin + bpw) : k_sel;
+
+  if (wave == 0) {
+    int base = 0;
+    for (int s0 = s_begin; s0 < s_end; s0 += kWave) {
+      const int sl = s0 + lane;
+      const int id = sl < s_end ? indices[unit * k_sel + sl] : -1;
+      const bool ok = id >= 0 && id * kBlock <= t;
+      const unsigned long long mask = __ballot(ok);
+      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+      if (ok && pos < kMaxWgSlots) ids_s[pos] = id;
+      base += __popcll(mask);
+    }
+    if (lane == 0) nv_s = min(base, kMaxWgSlots);
+  }
+  // B operand of S^T = K Q^T: Q^T[dims 32i + 8 r4 .. +8][head c16] (zero past G)
+  uint4 qb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    qb[i] = c16 < G ? ld16(q + (unit * G + c16) * D + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  const int nv = nv_s;
+
+  const size_t rs = size_t(kv_heads) * D;
+  const bf16_t* kbase = k + size_t(kstart) * rs + size_t(kv) * D;
+  const bf16_t* vbase = v + size_t(kstart) * rs + size_t(kv) * D;
+
+  // Token rows past t are clamped to t: they lie inside the sequence (finite
+  // data) and their probabilities are 0, so no per-load branches are needed.
+  auto load_block = [&](int id, MfmaBlockRegs<CIS>& R) {
+    const int j0 = id * kBlock + wave * 16;
+    const bf16_t* kr = kbase + size_t(min(j0 + c16, t)) * rs + 8 * r4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R.k[i] = ld16(kr + 32 * i);
+    const bf16_t* vr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vr[e] = vbase + size_t(min(j0 + 4 * r4 + e, t)) * rs + c16;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2)
+        R.v[2 * n + e2] = ld_u16(vr[2 * e2] + 16 * n) | (ld_u16(vr[2 * e2 + 1] + 16 * n) << 16);
+    if (CIS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        R.cw[e] = cis[(size_t(kstart) + min(j0 + 4 * r4 + e, t)) * kv_heads + kv];
+    }
+  };
+
+  float m_run = -INFINITY;  // running max of head c16 (same in the wave's 4 rows)
+  float l_run = 0.f;        // this lane's share of the normaliser (its row's tokens)
+  f32x4_t acc[8];           // O^T[dims 16n + 4 r4 + e][head c16]
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_block = [&](int id, const MfmaBlockRegs<CIS>& R) {
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.k[i]),
+                                                     __builtin_bit_cast(bf16x8_t, qb[i]), sacc,
+                                                     0, 0, 0);
+    const int jrow = id * kBlock + wave * 16 + 4 * r4;
+    float sv[4];
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = jrow + e <= t ? sacc[e] * scale_log2 : -INFINITY;
+      rmax = fmaxf(rmax, sv[e]);
+    }
+    // wave max of head c16: rows pair up through the two lane swaps
+    {
+      auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+      rmax = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+      auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+      rmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+    }
+    if (rmax > m_run + kLazy) {  // also true for the first block with a valid token
+      const float alpha = fast_exp2(m_run - rmax);
+      m_run = rmax;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run);
+      if (CIS) p[e] *= R.cw[e];
+      l_run += p[e];
+    }
+    const bf16x2_t p01 = {(__bf16)p[0], (__bf16)p[1]};
+    const bf16x2_t p23 = {(__bf16)p[2], (__bf16)p[3]};
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(__builtin_bit_cast(uint32_t, p01),
+                                                              __builtin_bit_cast(uint32_t, p23)));
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(R.v[2 * n], R.v[2 * n + 1]));
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[n], 0, 0, 0);
+    }
+  };
+
+  MfmaBlockRegs<CIS> A, B;
+  if (nv > 0) load_block(ids_s[0], A);
+  for (int i = 0; i < nv; i += 2) {
+    const int id0 = ids_s[i];
+    const bool has1 = i + 1 < nv;
+    const int id1 = has1 ? ids_s[i + 1] : 0;
+    if (has1) load_block(id1, B);
+    compute_block(id0, A);
+    if (has1) {
+      if (i + 2 < nv) load_block(ids_s[i + 2], A);
+      compute_block(id1, B);
+    }
+  }
+
+  // wave state of head c16: normaliser summed over the 4 rows
+  {
+    auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    float l2 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
+    l_run = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  }
+  if (c16 < G) {
+    if (r4 == 0) {
+      m_s[wave][c16] = m_run;
+      l_s[wave][c16] = l_run;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc_s[wave][c16][16 * n + 4 * r4 + e] = acc[n][e];
+  }
+  __syncthreads();
+
+  const int n_split = SPLIT ? int(gridDim.x) : 1;
+  for (int i = tid; i < G * D; i += 256) {
+    const int h = i / D, d = i % D;
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = m_s[w][h];
+      M = fmaxf(M, mw[w]);
+    }
+    float L = 0.f, Acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
+        L += f * l_s[w][h];
+        Acc += f * acc_s[w][h][d];
+      }
+    }
+    if constexpr (SPLIT) {
+      const size_t ps = unit * n_split + split;
+      part_acc[(ps * G + h) * D + d] = Acc;
+      if (d == 0) part_ml[ps * G + h] = make_float2(M, L);
+    } else {
+      store_f32(out + (unit * G + h) * D + d, L > 0.f ? Acc / L : 0.f);
+      if (lse != nullptr && d == 0)
+        lse[unit * G + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 // Merge the per-split partial states of one (row, kv head, query head): grid
 // (units, G), one thread per output dim.
 template <typename T>
@@ -377,6 +591,18 @@ AttnWs attn_ws_carve(void* base, int rows_total, int kv_heads, int group, int k_
   return ws;
 }
 
+template <typename T>
+using AttnKernelFn = void (*)(const T*, const T*, const T*, const int*, int, const float*, T*,
+                              float*, const int*, const int*, int, int, float, int, float2*,
+                              float*);
+
+// bf16 runs on the matrix cores; float32 on the vector ALUs.
+template <int G, typename T, bool CIS, bool SPLIT>
+static AttnKernelFn<T> attn_kernel_for() {
+  if constexpr (sizeof(T) == 2) return selected_attn_mfma_kernel<G, CIS, SPLIT>;
+  else return selected_attn_valu_kernel<G, T, CIS, SPLIT>;
+}
+
 template <int G, typename T, bool CIS>
 static hipError_t launch_attn_g(const void* q, const void* k, const void* v, const int* indices,
                                 int k_sel, const float* cis, void* out, float* lse,
@@ -387,7 +613,7 @@ static hipError_t launch_attn_g(const void* q, const void* k, const void* v, con
     const int bpw = attn_split_blocks(rows_total, kv_heads, k_sel);
     const int n_split = (k_sel + bpw - 1) / bpw;
     hipError_t e = launch_kernel(
-        kKindAttn, selected_attn_kernel<G, T, CIS, true>, dim3(n_split, kv_heads, rows_total),
+        kKindAttn, attn_kernel_for<G, T, CIS, true>(), dim3(n_split, kv_heads, rows_total),
         dim3(256), s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
         indices, k_sel, cis, static_cast<T*>(out), lse, cu_q, cu_k, batch, kv_heads, scale_log2,
         bpw, ws.part_ml, ws.part_acc);
@@ -397,7 +623,7 @@ static hipError_t launch_attn_g(const void* q, const void* k, const void* v, con
                          static_cast<const float*>(ws.part_acc), static_cast<T*>(out), lse,
                          n_split, G);
   }
-  return launch_kernel(kKindAttn, selected_attn_kernel<G, T, CIS, false>,
+  return launch_kernel(kKindAttn, attn_kernel_for<G, T, CIS, false>(),
                        dim3(rows_total, kv_heads, 1), dim3(256), s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), indices, k_sel, cis,
                        static_cast<T*>(out), lse, cu_q, cu_k, batch, kv_heads, scale_log2, k_sel,

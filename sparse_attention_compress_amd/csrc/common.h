@@ -64,15 +64,122 @@ __device__ __forceinline__ void store_f32(float* p, float x) { *p = x; }
 __device__ __forceinline__ void store_f32(bf16_t* p, float x) { p->bits = f32_to_bf16(x); }
 
 // --------------------------------------------------------------- reductions
+//
+// Cross-lane steps use DPP row operations and the gfx950 row-pair swaps, all of
+// them VALU instructions (no LDS round trip): within a row of 16 lanes
+// quad_perm / row_half_mirror / row_mirror / row_ror, across rows
+// v_permlane16_swap (rows 0<->1, 2<->3) and v_permlane32_swap (lanes L<->L^32).
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
-  return x;
+enum : int {
+  kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+  kDppRowRor2 = 0x122,
+  kDppRowRor4 = 0x124,
+  kDppRowRor8 = 0x128,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+
+// For a commutative op the two swap results together are {own, partner}, so
+// op(r0, r1) = op(own, partner) with no select needed.
+template <typename Op>
+__device__ __forceinline__ float cross16(float x, Op op) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float cross32(float x, Op op) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ int cross16i(int x, Op op) {
+  auto r = __builtin_amdgcn_permlane16_swap(unsigned(x), unsigned(x), false, false);
+  return op(int(r[0]), int(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ int cross32i(int x, Op op) {
+  auto r = __builtin_amdgcn_permlane32_swap(unsigned(x), unsigned(x), false, false);
+  return op(int(r[0]), int(r[1]));
+}
+
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpSum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpSumI {
+  __device__ __forceinline__ int operator()(int a, int b) const { return a + b; }
+};
+
+// Reduction over the 4 lanes of a quad (result in all 4).
+template <typename Op>
+__device__ __forceinline__ float quad_reduce(float x, Op op) {
+  x = op(x, dpp<kDppQuadXor1>(x));
+  return op(x, dpp<kDppQuadXor2>(x));
+}
+// Reduction over a row of 16 lanes (result in all 16).
+template <typename Op>
+__device__ __forceinline__ float row_reduce(float x, Op op) {
+  x = quad_reduce(x, op);
+  x = op(x, dpp<kDppRowHalfMirror>(x));
+  return op(x, dpp<kDppRowMirror>(x));
+}
+// Reduction over the whole wave (result in all 64 lanes).
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = row_reduce(x, op);
+  x = cross16(x, op);
+  return cross32(x, op);
+}
+__device__ __forceinline__ float wave_max(float x) { return wave_reduce(x, OpMax()); }
+__device__ __forceinline__ float wave_sum(float x) { return wave_reduce(x, OpSum()); }
+
+// Reduction over the lanes that share lane % G (G a power of two <= 64): the
+// result for column (lane % G) lands in every lane of that column.
+template <int G, typename Op>
+__device__ __forceinline__ float column_reduce(float x, Op op) {
+  if constexpr (G == 1) {
+    return wave_reduce(x, op);
+  } else {
+    // rotations by 2, 4, 8 inside a row accumulate every lane of the column
+    if constexpr (G <= 2) x = op(x, dpp<kDppRowRor2>(x));
+    if constexpr (G <= 4) x = op(x, dpp<kDppRowRor4>(x));
+    if constexpr (G <= 8) x = op(x, dpp<kDppRowRor8>(x));
+    if constexpr (G <= 16) x = cross16(x, op);
+    if constexpr (G <= 32) x = cross32(x, op);
+    return x;
+  }
+}
+
+// Inclusive prefix sum over the wave (lane order), 6 DPP / swap steps.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+  // within rows: shift-right by 1, 2, 4, 8 with zero fill
+  int y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += y;
+  // across rows: add the totals of all earlier rows
+  const int r15 = __builtin_amdgcn_readlane(x, 15), r31 = __builtin_amdgcn_readlane(x, 31),
+            r47 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  x += (row >= 1 ? r15 : 0) + (row >= 2 ? r31 : 0) + (row >= 3 ? r47 : 0);
   return x;
 }
 

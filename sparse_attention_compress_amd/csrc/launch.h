@@ -64,18 +64,19 @@ hipError_t launch_mean_pool(const void* x, int x_bf16, void* y, int y_bf16, cons
 
 // Scoring workspace carve-up (decode rows).
 struct ScoresWs {
-  float* logits;  // [batch, kv_heads, G, nc_max] scaled log2-domain logits
+  float* logits;  // [batch, kv_heads, G, n_chunk_max*64] scaled log2-domain logits
   float2* part;   // [batch, kv_heads, n_chunk_max, G] chunk (max, sum of exp2)
+  float* cisb;    // [batch, kv_heads, n_chunk_max*16+1] per-block CIS maxima
 };
-size_t scores_ws_bytes(int batch, int kv_heads, int group, int nc_max);
-ScoresWs scores_ws_carve(void* base, int batch, int kv_heads, int group, int nc_max);
+size_t scores_ws_bytes(int batch, int kv_heads, int group, int max_seqlen_k);
+ScoresWs scores_ws_carve(void* base, int batch, int kv_heads, int group, int max_seqlen_k);
 
 struct DecodeScoresArgs {
   const void* q;
   int q_bf16;
   void* kc;  // compressed keys; its newest window is rewritten when refresh_k is set
   int kc_bf16;
-  const float* cis_pooled;  // nullable: fused into the block score with cis_weight
+  float* cis_pooled;  // nullable: fused with cis_weight; newest window rewritten with refresh_cis
   float cis_weight;
   float* block_scores;  // nullable output
   float* window_probs;  // nullable output
@@ -88,7 +89,6 @@ struct DecodeScoresArgs {
   int topk, n_init, n_local;
   const void* refresh_k;       // nullable: recompute the newest window from these keys
   const float* refresh_cis;    // nullable: and the newest pooled CIS from these scores
-  float* refresh_cis_pooled;   // where that pooled CIS goes
 };
 hipError_t launch_decode_scores(const DecodeScoresArgs& a, hipStream_t s);
 

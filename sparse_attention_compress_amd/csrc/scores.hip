@@ -8,24 +8,33 @@
 // with stride 16); plus w * the same max of the pooled CIS; then the init and
 // local blocks forced in and the best other blocks picked, ids ascending.
 //
-// window_logits_kernel -- grid (chunk of 64 windows, kv head, sequence).  Each
-//   wave scores 16 windows; a quad of lanes shares one compressed-key row (each
-//   lane a 32-dim slice, 16-byte loads) and the G query heads of the group come
-//   from LDS, so each compressed key is read from HBM once for the whole group.
-//   It writes log2-domain logits and a per-chunk (max, sum of exp2) per head.
-//   Optionally the workgroup owning the newest window first recomputes that
-//   window of the K_c and pooled-CIS caches from K and CIS (decode refresh).
-// select_kernel -- one workgroup of 1024 threads per (row, kv head).  Either
-//   derives the block scores from the logits (decode) or reads given scores,
-//   then selects: forced blocks, and among the others a histogram of the scores
-//   over [min, max] locates the bin holding the k-th best, blocks above it are
-//   taken and the bin's candidates are ranked exactly by (score desc, id asc);
-//   chosen ids are written in ascending order by a workgroup scan.
-// No kernel waits on another workgroup: every hand-off is a kernel boundary.
+// window_logits_kernel -- grid (chunk of 64 windows, kv head, sequence), 4 waves
+//   of 16 windows.  bf16 queries and keys run on the matrix cores (S^T = Kc Q^T
+//   with four v_mfma_f32_16x16x32_bf16 per wave, the compressed-key rows loaded
+//   straight into the A operand); other dtypes use fp32 FMAs with the queries
+//   in LDS.  Each compressed key is read from HBM once for the whole GQA group.
+//   Outputs: log2-domain logits, a per-chunk (max, sum of exp2) per head, and the
+//   CIS maximum of the blocks the chunk owns (blocks 16j..16j+15, the last chunk
+//   also block 16*n_chunks).  The workgroup owning the newest window can first
+//   recompute that window of the K_c and pooled-CIS caches (decode refresh).
+// select_kernel -- one workgroup of 512 threads per (row, kv head).  Derives the
+//   block scores (group probabilities of all windows staged in LDS) or reads
+//   given scores, then selects: forced blocks, and among the others a 1024-bin
+//   histogram of the scores over [min, max] locates the bin holding the k-th
+//   best; blocks above it are taken, blocks below dropped, and the bin is
+//   refined the same way until at most 512 candidates remain, which are ranked
+//   exactly by (score desc, id asc); exactly equal scores go to the lower ids.
+//   Chosen ids are written in ascending order by a workgroup scan.
+// Every load phase is branch-free (indices clamped into range, values masked)
+// so all of a thread's loads are in flight together.  No kernel waits on another
+// workgroup: each hand-off is a kernel boundary.
 #include "common.h"
 #include "launch.h"
 
 namespace nsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int full_windows_dev(int len) {
   return len >= kKernel ? (len - kKernel) / kStride + 1 : 0;
@@ -50,16 +59,22 @@ __device__ __forceinline__ void row_position(int row, const int* __restrict__ cu
 
 // ------------------------------------------------------------ kernel 1: logits
 
+constexpr int kCisSpan = kChunkWindows + 5;  // windows c0-1 .. c0+67 (17 owned blocks)
+
 template <int G, typename TQ, typename TKC>
 __global__ __launch_bounds__(256) void window_logits_kernel(
     const TQ* __restrict__ q, TKC* __restrict__ kc, const int* __restrict__ cu_k,
     const int* __restrict__ cu_c, float* __restrict__ logits, float2* __restrict__ part,
-    int kv_heads, int nc_max, int n_chunk_max, float scale_log2,
-    const TQ* __restrict__ k_src, const float* __restrict__ cis_src, float* __restrict__ cis_pooled) {
-  __shared__ float q_s[G][kHeadDim];
-  __shared__ float new_s[kHeadDim];
-  __shared__ float red_s[4][G];
-  __shared__ float m_s[G];
+    float* __restrict__ cisb, float* __restrict__ cis_pooled, int kv_heads, int ldc,
+    int n_chunk_max, int ldb, float scale_log2, const TQ* __restrict__ k_src,
+    const float* __restrict__ cis_src) {
+  constexpr bool kMfma = sizeof(TQ) == 2 && sizeof(TKC) == 2;
+  constexpr int D = kHeadDim;
+  __shared__ float q_s[kMfma ? 1 : G][D];
+  __shared__ uint32_t new_s[D / 2];  // refreshed compressed key, bf16 pairs
+  __shared__ float newf_s[D];        // refreshed compressed key as the cache holds it
+  __shared__ float cisw_s[kCisSpan];
+  __shared__ float red_s[2][4][16];
   const int b = blockIdx.z, kv = blockIdx.y, chunk = blockIdx.x;
   const int start = cu_k[b];
   const int len = cu_k[b + 1] - start;
@@ -68,31 +83,51 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
   const int nvis = min(nc, full_windows_dev(len));  // decode query at t = len-1
   const int c0 = chunk * kChunkWindows;
   if (c0 >= nvis) return;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int c = c0 + wave * 16 + (lane >> 2);
-  const int r = lane & 3;
-  const bool valid = c < nvis;
-  // window refreshed from K in this workgroup (decode append), else -1
+  const int n_chunk = (nvis + kChunkWindows - 1) / kChunkWindows;
+  const int nb = (len + kBlock - 1) / kBlock;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t unit = size_t(b) * kv_heads + kv;
+  // the newest window, recomputed from K in this workgroup (decode append), else -1
   const int rw = (k_src != nullptr && nvis == nc && nc - 1 >= c0 && nc - 1 < c0 + kChunkWindows)
                      ? nc - 1 : -1;
 
-  // issue every global load of the workgroup before the first use
-  float kf[4][8];
-  if (valid && c != rw) {
-    const TKC* row = kc + (size_t(cbase + c) * kv_heads + kv) * kHeadDim;
+  // ---- every global load of the workgroup, before the first use
+  // compressed keys: MFMA path lane (c16, r4) holds window c0+16w+c16, dims 32i+8r4;
+  // FMA path lane (window c0+16w+lane/4, slice lane%4) holds dims 32i+8(lane%4)
+  const int ca = kMfma ? c0 + 16 * wave + (lane & 15) : c0 + 16 * wave + (lane >> 2);
+  const int sl = kMfma ? (lane >> 4) : (lane & 3);
+  const TKC* krow = kc + (size_t(cbase + min(ca, nvis - 1)) * kv_heads + kv) * D;
+  uint4 ka[4];     // MFMA path (bf16)
+  float kf[4][8];  // FMA path
+  if constexpr (kMfma) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load8f(row + 32 * i + 8 * r, kf[i]);
+    for (int i = 0; i < 4; ++i) ka[i] = ld16(krow + 32 * i + 8 * sl);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load8f(krow + 32 * i + 8 * sl, kf[i]);
+  }
+  uint4 qb[4];
+  const int c16 = lane & 15, r4 = lane >> 4;
+  if constexpr (kMfma) {
+    const TQ* qh = q + (unit * G + min(c16, G - 1)) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = c16 < G ? ld16(qh + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float cisv = -INFINITY;
+  if (cis_pooled != nullptr && tid < kCisSpan) {
+    const int cw = c0 - 1 + tid;
+    cisv = cis_pooled[(size_t(cbase) + min(max(cw, 0), nvis - 1)) * kv_heads + kv];
+    if (cw < 0 || cw >= nvis) cisv = -INFINITY;
   }
   float racc = 0.f, rcis = 0.f;
   if (rw >= 0) {
     const int j0 = start + kStride * rw;
-    if (tid < kHeadDim) {
-      // same summation order as the pooling kernel: token by token
+    if (tid < D) {
       float xv[kKernel];
 #pragma unroll
       for (int j = 0; j < kKernel; ++j)
-        xv[j] = to_f32(k_src[(size_t(j0 + j) * kv_heads + kv) * kHeadDim + tid]);
+        xv[j] = to_f32(k_src[(size_t(j0 + j) * kv_heads + kv) * D + tid]);
+      // same summation order as the pooling kernel: token by token
 #pragma unroll
       for (int j = 0; j < kKernel; ++j) racc += xv[j];
       racc = racc / float(kKernel);
@@ -100,251 +135,379 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
       rcis = cis_src[size_t(j0 + tid - 128) * kv_heads + kv];
     }
   }
-  const TQ* qg = q + (size_t(b) * kv_heads + kv) * G * kHeadDim;
-  for (int i = tid; i < G * kHeadDim; i += 256) q_s[i / kHeadDim][i % kHeadDim] = to_f32(qg[i]);
+  if constexpr (!kMfma) {
+    const TQ* qg = q + unit * G * D;
+    constexpr int kVecs = G * D / 8;
+    float qv[(kVecs + 255) / 256][8];
+#pragma unroll
+    for (int u = 0; u < (kVecs + 255) / 256; ++u)
+      if (tid + 256 * u < kVecs) load8f(qg + 8 * (tid + 256 * u), qv[u]);
+#pragma unroll
+    for (int u = 0; u < (kVecs + 255) / 256; ++u)
+      if (tid + 256 * u < kVecs)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) (&q_s[0][0])[8 * (tid + 256 * u) + e] = qv[u][e];
+  }
+
+  // ---- refresh of the newest window, CIS of the windows around the chunk
+  if (tid < kCisSpan && (rw < 0 || c0 - 1 + tid != rw)) cisw_s[tid] = cisv;
   if (rw >= 0) {
-    if (tid < kHeadDim) {
-      new_s[tid] = racc;
-      store_f32(kc + (size_t(cbase + rw) * kv_heads + kv) * kHeadDim + tid, racc);
+    if (tid < D) {
+      TKC st;
+      store_f32(&st, racc);
+      newf_s[tid] = to_f32(st);  // what a reader of the cache sees
+      kc[(size_t(cbase + rw) * kv_heads + kv) * D + tid] = st;
     }
-    if (cis_src != nullptr && cis_pooled != nullptr && wave == 2) {
-      // lanes 0..31 of wave 2 hold the window's 32 scores, in token order
-      float x = lane < kKernel ? rcis : 0.f;
+    if (wave == 2) {
+      // lanes 0..31 of wave 2 hold the window's 32 scores; summed in token order
       float acc = 0.f;
-      for (int j = 0; j < kKernel; ++j) acc += __shfl(x, j, kWave);
-      if (lane == 0) cis_pooled[size_t(cbase + rw) * kv_heads + kv] = acc / float(kKernel);
+#pragma unroll
+      for (int j = 0; j < kKernel; ++j)
+        acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rcis), j));
+      const float pooled = acc / float(kKernel);
+      if (lane == 0 && cis_pooled != nullptr) {
+        if (cis_src != nullptr) cis_pooled[size_t(cbase + rw) * kv_heads + kv] = pooled;
+        cisw_s[rw - c0 + 1] =
+            cis_src != nullptr ? pooled : cis_pooled[size_t(cbase + rw) * kv_heads + kv];
+      }
     }
   }
   __syncthreads();
-  if (valid && c == rw) {
+  if constexpr (kMfma) {
+    if (rw >= 0) {
+      // pack the refreshed row (already bf16-exact) for the lane that owns it
+      if (tid < D / 2) new_s[tid] = pack_bf16x2(newf_s[2 * tid], newf_s[2 * tid + 1]);
+      __syncthreads();
+      if (ca == rw) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float tmp[8];
+        for (int i = 0; i < 4; ++i)
+          ka[i] = *reinterpret_cast<const uint4*>(&new_s[(32 * i + 8 * sl) / 2]);
+      }
+    }
+  } else {
+    if (ca == rw) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tmp[e] = new_s[32 * i + 8 * r + e];
-      // what a reader of the cache sees: the value rounded to the cache dtype
-      TKC st[8];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) store_f32(&st[e], tmp[e]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[i][e] = to_f32(st[e]);
+        for (int e = 0; e < 8; ++e) kf[i][e] = newf_s[32 * i + 8 * sl + e];
     }
   }
-  float s[G];
+
+  // ---- block CIS maxima of the blocks this chunk owns
+  if (cis_pooled != nullptr && tid < 17) {
+    const int i = 16 * chunk + tid;
+    if ((tid < 16 || chunk == n_chunk - 1) && i < nb) {
+      float m = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) s[h] = 0.f;
-  if (valid) {
+      for (int e = 0; e < 5; ++e) m = fmaxf(m, cisw_s[4 * tid + e]);
+      cisb[unit * ldb + i] = m == -INFINITY ? 0.f : m;
+    }
+  }
+
+  // ---- logits, chunk max and sum of exp2 per head
+  float* lrow = logits + unit * G * ldc;
+  if constexpr (kMfma) {
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
+                                                     __builtin_bit_cast(bf16x8_t, qb[i]), sacc,
+                                                     0, 0, 0);
+    // lane (c16, r4): windows cw0 .. cw0+3 of head c16
+    const int cw0 = c0 + 16 * wave + 4 * r4;
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = cw0 + e < nvis ? sacc[e] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[e]);
+    }
+    if (c16 < G)
+      *reinterpret_cast<float4*>(lrow + size_t(c16) * ldc + cw0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+    mx = cross32(cross16(mx, OpMax()), OpMax());
+    if (r4 == 0) red_s[0][wave][c16] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red_s[0][0][c16], red_s[0][1][c16]),
+                          fmaxf(red_s[0][2][c16], red_s[0][3][c16]));
+    float l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - M);
+    l = cross32(cross16(l, OpSum()), OpSum());
+    if (r4 == 0) red_s[1][wave][c16] = l;
+    __syncthreads();
+    if (tid < G)
+      part[(unit * n_chunk_max + chunk) * G + tid] =
+          make_float2(M, red_s[1][0][tid] + red_s[1][1][tid] + red_s[1][2][tid] + red_s[1][3][tid]);
+  } else {
+    const bool valid = ca < nvis;
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float* qq = &q_s[h][32 * i + 8 * r];
+        const float* qq = &q_s[h][32 * i + 8 * sl];
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[h] = fmaf(qq[e], kf[i][e], s[h]);
       }
-  }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    s[h] += __shfl_xor(s[h], 1, kWave);
-    s[h] += __shfl_xor(s[h], 2, kWave);
-    s[h] = valid ? s[h] * scale_log2 : -INFINITY;
-  }
-  const size_t unit = size_t(b) * kv_heads + kv;
-  if (valid) {
+    for (int h = 0; h < G; ++h) {
+      s[h] = quad_reduce(s[h], OpSum());
+      s[h] = valid ? s[h] * scale_log2 : -INFINITY;
+    }
+    if (valid) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if ((h & 3) == sl) lrow[size_t(h) * ldc + ca] = s[h];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m = wave_max(s[h]);
+      if (lane == 0) red_s[0][wave][h] = m;
+    }
+    __syncthreads();
+    float M[G];
 #pragma unroll
     for (int h = 0; h < G; ++h)
-      if ((h & 3) == r) logits[(unit * G + h) * nc_max + c] = s[h];
-  }
+      M[h] = fmaxf(fmaxf(red_s[0][0][h], red_s[0][1][h]), fmaxf(red_s[0][2][h], red_s[0][3][h]));
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float m = wave_max(s[h]);
-    if (lane == 0) red_s[wave][h] = m;
+    for (int h = 0; h < G; ++h) {
+      const float p = (valid && sl == 0) ? fast_exp2(s[h] - M[h]) : 0.f;
+      const float l = wave_sum(p);
+      if (lane == 0) red_s[1][wave][h] = l;
+    }
+    __syncthreads();
+    if (tid < G)
+      part[(unit * n_chunk_max + chunk) * G + tid] =
+          make_float2(M[tid], red_s[1][0][tid] + red_s[1][1][tid] + red_s[1][2][tid] + red_s[1][3][tid]);
   }
-  __syncthreads();
-  if (tid < G) m_s[tid] = fmaxf(fmaxf(red_s[0][tid], red_s[1][tid]), fmaxf(red_s[2][tid], red_s[3][tid]));
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float p = (valid && r == 0) ? fast_exp2(s[h] - m_s[h]) : 0.f;
-    const float l = wave_sum(p);
-    if (lane == 0) red_s[wave][h] = l;
-  }
-  __syncthreads();
-  if (tid < G)
-    part[(unit * n_chunk_max + chunk) * G + tid] =
-        make_float2(m_s[tid], red_s[0][tid] + red_s[1][tid] + red_s[2][tid] + red_s[3][tid]);
 }
 
 // ------------------------------------------------------------ kernel 2: select
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 1024;
+constexpr int kCandMax = kSelThreads;  // candidates ranked exactly, one per thread
+constexpr int kWinLds = 4 * kMaxSortBlocks;  // every window of the longest sequence
+constexpr int kBlkPer = kMaxSortBlocks / kSelThreads;  // strided blocks per thread
 
 struct SelShared {
-  float sc[kMaxSortBlocks];                 // block scores of the row
-  unsigned long long cand[kMaxSortBlocks];  // candidate keys (score key, ~id)
+  float sc[kMaxSortBlocks];            // block scores of the row
+  float pg[kWinLds];                   // group probabilities of the windows
   int hist[kBins];
-  unsigned char sel[kMaxSortBlocks];
-  float wred[2][kSelWaves];
-  int wsum[kSelWaves + 1];
+  unsigned char sel[kMaxSortBlocks];   // 0 out, 1 chosen, 2 still a candidate
+  int cand[kCandMax];
+  float wred[2][kSelWaves][16];
+  int wsum[kSelWaves];
   int misc[4];
-  float fmisc[4];
 };
 
-__device__ __forceinline__ float block_reduce_max(float x, SelShared& S, int slot) {
-  x = wave_max(x);
+// Exclusive scan of per-thread counts in thread order; returns the thread's
+// offset and, in every thread, the total.  Two barriers (the second keeps
+// S.wsum stable until every thread has read it).
+__device__ __forceinline__ int block_exclusive_scan(int cnt, SelShared& S, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) S.wred[slot][wave] = x;
-  __syncthreads();
-  float m = S.wred[slot][0];
-  for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, S.wred[slot][w]);
-  return m;
-}
-
-// exclusive scan of per-thread counts over the workgroup; returns the thread's
-// offset, total in S.wsum[kSelWaves]
-__device__ __forceinline__ int block_exclusive_scan(int cnt, SelShared& S) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = cnt;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += y;
-  }
+  const int incl = wave_inclusive_scan(cnt);
   if (lane == kWave - 1) S.wsum[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int v = S.wsum[w];
-      S.wsum[w] = run;
-      run += v;
-    }
-    S.wsum[kSelWaves] = run;
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int v = S.wsum[w];
+    before += w < wave ? v : 0;
+    total += v;
   }
   __syncthreads();
-  return S.wsum[wave] + incl - cnt;
+  return before + incl - cnt;
 }
 
-// Top-k of S.sc[0..nb) for query position t; writes topk ids to out.
-__device__ void topk_select(SelShared& S, int nb, int t, int topk, int n_init, int n_local,
-                            int* __restrict__ out) {
-  const int tid = threadIdx.x;
-  const int n_elig = t >= 0 ? min(nb, t / kBlock + 1) : 0;
-  const int f_init = min(n_init, n_elig);
-  const int f_loc = max(max(0, n_elig - n_local), f_init);  // forced local: [f_loc, n_elig)
-  const int n_forced = f_init + (n_elig - f_loc);
-  const int n_free = n_elig - n_forced;
-  const int kf = max(0, min(topk - n_forced, n_free));
-  for (int i = tid; i < n_elig; i += kSelThreads)
-    S.sel[i] = (i < f_init || i >= f_loc || kf == n_free) ? 1 : 0;
-  if (kf > 0 && kf < n_free) {
-    // range of the free scores
-    float lo = INFINITY, hi = -INFINITY;
-    for (int i = f_init + tid; i < f_loc; i += kSelThreads) {
-      lo = fminf(lo, S.sc[i]);
-      hi = fmaxf(hi, S.sc[i]);
-    }
-    const float vmax = block_reduce_max(hi, S, 0);
-    const float vmin = -block_reduce_max(-lo, S, 1);
-    const float width = vmax - vmin;
-    const float scale = float(kBins) / width;
-    const bool binned = width > 0.f && isfinite(scale) && isfinite(width);
-    int above = 0, bstar = 0;
-    if (binned) {
-      for (int i = tid; i < kBins; i += kSelThreads) S.hist[i] = 0;
-      __syncthreads();
-      for (int i = f_init + tid; i < f_loc; i += kSelThreads) {
-        const int bin = min(kBins - 1, int((S.sc[i] - vmin) * scale));
-        atomicAdd(&S.hist[bin], 1);
-      }
-      __syncthreads();
-      // suffix counts from the top bin: thread j owns bin kBins-1-j
-      const int j = tid;
-      const int cnt = j < kBins ? S.hist[kBins - 1 - j] : 0;
-      const int excl = block_exclusive_scan(cnt, S);  // blocks in higher bins
-      if (j < kBins && excl < kf && kf <= excl + cnt) {
-        S.misc[0] = kBins - 1 - j;
-        S.misc[1] = excl;
-      }
-      __syncthreads();
-      bstar = S.misc[0];
-      above = S.misc[1];
-    }
-    // candidates: the bin holding the k-th best (every free block when unbinned)
-    if (tid == 0) S.misc[2] = 0;
-    __syncthreads();
-    for (int i = f_init + tid; i < f_loc; i += kSelThreads) {
-      const float v = S.sc[i];
-      const int bin = binned ? min(kBins - 1, int((v - vmin) * scale)) : 0;
-      if (bin > bstar) {
-        S.sel[i] = 1;
-      } else if (bin == bstar) {
-        const int pos = atomicAdd(&S.misc[2], 1);
-        S.cand[pos] = (static_cast<unsigned long long>(float_key(v)) << 32) |
-                      static_cast<unsigned long long>(0xffffffffu - unsigned(i));
-      }
-    }
-    __syncthreads();
-    const int m = S.misc[2];
-    const int need = kf - above;
-    if (m <= kSelThreads) {
-      // exact rank among the candidates (keys are distinct)
-      if (tid < m) {
-        const unsigned long long mine = S.cand[tid];
-        int rank = 0;
-        for (int o = 0; o < m; ++o) rank += S.cand[o] > mine ? 1 : 0;
-        if (rank < need) S.sel[0xffffffffu - unsigned(mine & 0xffffffffull)] = 1;
-      }
-    } else {
-      // many candidates: bitonic sort of their keys, descending
-      int n = 64;
-      while (n < m) n <<= 1;
-      for (int i = m + tid; i < n; i += kSelThreads) S.cand[i] = 0ull;
-      __syncthreads();
-      for (int k2 = 2; k2 <= n; k2 <<= 1) {
-        for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-          for (int i = tid; i < (n >> 1); i += kSelThreads) {
-            const int a_i = ((i & ~(jj - 1)) << 1) | (i & (jj - 1));
-            const int b_i = a_i | jj;
-            const unsigned long long a = S.cand[a_i], c = S.cand[b_i];
-            if ((a < c) == ((a_i & k2) == 0)) {
-              S.cand[a_i] = c;
-              S.cand[b_i] = a;
-            }
-          }
-          __syncthreads();
-        }
-      }
-      for (int i = tid; i < need; i += kSelThreads)
-        S.sel[0xffffffffu - unsigned(S.cand[i] & 0xffffffffull)] = 1;
-    }
+__device__ __forceinline__ void block_minmax(float lo, float hi, SelShared& S, float& vmin,
+                                             float& vmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  lo = -wave_max(-lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    S.wred[0][wave][0] = lo;
+    S.wred[1][wave][0] = hi;
   }
   __syncthreads();
-  // ordered compaction: thread tid owns ids [tid*per, tid*per+per)
+  vmin = INFINITY;
+  vmax = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    vmin = fminf(vmin, S.wred[0][w][0]);
+    vmax = fmaxf(vmax, S.wred[1][w][0]);
+  }
+}
+
+// Top-k over S.sc[0..n_elig) with S.sel marking forced (1), free candidates (2)
+// and the rest (0); kf free places to fill; lo/hi: per-thread min/max of the
+// free scores.  Writes topk ascending ids (-1 padded) to out.
+__device__ void topk_finish(SelShared& S, int n_elig, int kf, int n_free, float lo, float hi,
+                            int topk, int* __restrict__ out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  float vmin, vmax;
+  block_minmax(lo, hi, S, vmin, vmax);
+  int need = kf;
+  bool take_rest = false;  // every remaining candidate is chosen
+  bool by_index = false;   // all free scores equal: the lowest ids are chosen
+  bool by_rank = false;    // few candidates: exact rank among them
+  bool by_scan = false;    // otherwise: exact rank against every candidate
+  if (kf > 0 && kf < n_free) {
+    float base = vmin, width = vmax - vmin;
+    for (int level = 0; level < 12; ++level) {
+      const float scale = float(kBins) / width;
+      if (width == 0.f) {
+        by_index = true;
+        break;
+      }
+      if (!isfinite(width) || !isfinite(scale) || !(width > 0.f)) {
+        by_scan = true;
+        break;
+      }
+      // histogram of the candidates over [base, base + width)
+#pragma unroll
+      for (int u = 0; u < kBlkPer; ++u) {
+        const int i = tid + kSelThreads * u;
+        if (i < n_elig && S.sel[i] == 2) {
+          const int bin = min(kBins - 1, max(0, int((S.sc[i] - base) * scale)));
+          atomicAdd(&S.hist[bin], 1);
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        if (tid == 0) {  // found below; defaults keep every later step in range
+          S.misc[0] = 0;
+          S.misc[1] = 0;
+          S.misc[2] = need;
+        }
+        // lane l owns bins 1023-16l .. 1008-16l (descending scores)
+        int cnt[16], tot = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          cnt[e] = S.hist[kBins - 1 - 16 * lane - e];
+          tot += cnt[e];
+        }
+        const int incl = wave_inclusive_scan(tot);
+        int above = incl - tot;  // candidates in higher bins
+        if (above < need && need <= incl) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (above < need && need <= above + cnt[e]) {
+              S.misc[0] = kBins - 1 - 16 * lane - e;
+              S.misc[1] = above;
+              S.misc[2] = cnt[e];
+            }
+            above += cnt[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S.hist[kBins - 1 - 16 * lane - e] = 0;
+      }
+      __syncthreads();
+      const int bstar = S.misc[0], above = S.misc[1], m = S.misc[2];
+#pragma unroll
+      for (int u = 0; u < kBlkPer; ++u) {
+        const int i = tid + kSelThreads * u;
+        if (i < n_elig && S.sel[i] == 2) {
+          const int bin = min(kBins - 1, max(0, int((S.sc[i] - base) * scale)));
+          if (bin != bstar) S.sel[i] = bin > bstar ? 1 : 0;
+        }
+      }
+      need -= above;
+      if (m == need) {
+        take_rest = true;
+        break;
+      }
+      if (m <= kCandMax) {
+        by_rank = true;
+        break;
+      }
+      base = base + float(bstar) / scale;
+      width = 1.f / scale;
+    }
+    if (!take_rest && !by_rank && !by_index) by_scan = true;  // refinement did not settle
+  }
+  __syncthreads();
+  if (by_scan) {
+    // each remaining candidate counts the candidates that beat it
+    unsigned char keep[kBlkPer];
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u) {
+      const int i = tid + kSelThreads * u;
+      keep[u] = 0;
+      if (i < n_elig && S.sel[i] == 2) {
+        const float v = S.sc[i];
+        int rank = 0;
+        for (int o = 0; o < n_elig; ++o) {
+          if (S.sel[o] != 2) continue;
+          const float w = S.sc[o];
+          rank += (w > v || (w == v && o < i)) ? 1 : 0;
+        }
+        keep[u] = rank < need ? 1 : 0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u) {
+      const int i = tid + kSelThreads * u;
+      if (i < n_elig && S.sel[i] == 2) S.sel[i] = keep[u];
+    }
+    __syncthreads();
+  }
+  // candidates listed in id order (thread tid owns a contiguous run of ids)
   const int per = (n_elig + kSelThreads - 1) / kSelThreads;
-  const int i0 = tid * per;
+  const int i0 = tid * per, i1 = min(i0 + per, n_elig);
+  if (by_rank || by_index) {
+    int cnt = 0;
+    for (int i = i0; i < i1; ++i) cnt += S.sel[i] == 2;
+    int m = 0;
+    int pos = block_exclusive_scan(cnt, S, m);
+    for (int i = i0; i < i1; ++i) {
+      if (S.sel[i] != 2) continue;
+      if (by_index) S.sel[i] = pos < need ? 1 : 0;
+      else if (pos < kCandMax) S.cand[pos] = i;
+      ++pos;
+    }
+    m = min(m, kCandMax);
+    __syncthreads();
+    if (by_rank && tid < m) {
+      const int i = S.cand[tid];
+      const float v = S.sc[i];
+      int rank = 0;
+      for (int c = 0; c < m; ++c) {
+        const int o = S.cand[c];
+        const float w = S.sc[o];
+        rank += (w > v || (w == v && o < i)) ? 1 : 0;
+      }
+      S.sel[i] = rank < need ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  // ordered compaction of the chosen ids
   int cnt = 0;
-  for (int i = i0; i < min(i0 + per, n_elig); ++i) cnt += S.sel[i];
-  int pos = block_exclusive_scan(cnt, S);
-  for (int i = i0; i < min(i0 + per, n_elig); ++i)
-    if (S.sel[i]) out[pos++] = i;
-  const int total = S.wsum[kSelWaves];
-  for (int i = total + tid; i < topk; i += kSelThreads) out[i] = -1;
+  for (int i = i0; i < i1; ++i) cnt += (S.sel[i] == 1 || (take_rest && S.sel[i] == 2));
+  int total = 0;
+  int pos = block_exclusive_scan(cnt, S, total);
+  // writes stay inside the row's topk slots even if the count were wrong
+  for (int i = i0; i < i1; ++i)
+    if ((S.sel[i] == 1 || (take_rest && S.sel[i] == 2)) && pos < topk) out[pos++] = i;
+  for (int i = max(0, total) + tid; i < topk; i += kSelThreads) out[i] = -1;
+  (void)lane;
 }
 
 template <int G, bool FROM_LOGITS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
-    const float* __restrict__ cis_pooled, float cis_weight, const int* __restrict__ cu_q,
+    const float* __restrict__ cisb, float cis_weight, const int* __restrict__ cu_q,
     const int* __restrict__ cu_k, const int* __restrict__ cu_c, int batch,
     float* __restrict__ block_scores, float* __restrict__ window_probs, int kv_heads,
-    int nc_max, int nb_max, int n_chunk_max, int* __restrict__ indices, int topk, int n_init,
-    int n_local) {
+    int nc_max, int ldc, int nb_max, int n_chunk_max, int ldb, int* __restrict__ indices,
+    int topk, int n_init, int n_local) {
   __shared__ SelShared S;
-  __shared__ float hm_s[kSelWaves][G], hl_s[kSelWaves][G];
-  __shared__ float M_s[G], invL_s[G];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x, kv = blockIdx.y;
   int b, t;
@@ -352,103 +515,135 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int len = cu_k[b + 1] - cu_k[b];
   const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
   const size_t unit = size_t(row) * kv_heads + kv;
+  // selection geometry
+  const int n_elig = t >= 0 ? min(nb, t / kBlock + 1) : 0;
+  const int f_init = min(n_init, n_elig);
+  const int f_loc = max(max(0, n_elig - n_local), f_init);  // forced local: [f_loc, n_elig)
+  const int n_forced = f_init + (n_elig - f_loc);
+  const int n_free = n_elig - n_forced;
+  const int kf = max(0, min(topk - n_forced, n_free));
+  const unsigned char free_mark = kf == n_free ? 1 : (kf == 0 ? 0 : 2);
+  for (int i = tid; i < kBins; i += kSelThreads) S.hist[i] = 0;
+
+  float lo = INFINITY, hi = -INFINITY;  // free-score range seen by this thread
+  auto put = [&](int i, float sc) {
+    S.sc[i] = sc;
+    const bool forced = i < f_init || (i >= f_loc && i < n_elig);
+    S.sel[i] = i >= n_elig ? 0 : (forced ? 1 : free_mark);
+    if (i < n_elig && !forced) {
+      lo = fminf(lo, sc);
+      hi = fmaxf(hi, sc);
+    }
+  };
 
   if constexpr (FROM_LOGITS) {
-    const int cbase = cu_c[b];
-    const int nc = cu_c[b + 1] - cbase;
+    const int nc = cu_c[b + 1] - cu_c[b];
     const int nvis = min(nc, full_windows_dev(len));
     const int n_chunk = (nvis + kChunkWindows - 1) / kChunkWindows;
-    // per-head softmax normaliser from the chunk (max, sum) pairs
-    constexpr int kPer = 4;  // chunk pairs per thread (n_chunk * G <= 4096)
-    float2 ml[kPer];
+    // per-head softmax normaliser from the chunk (max, sum) pairs; pair i of this
+    // thread belongs to head i % G == tid % G.  Loads clamped into range, masked.
+    constexpr int kPairs = 4096 / kSelThreads;
+    const int n_pairs = n_chunk * G, pair_cap = max(n_chunk_max * G, 1);
+    const float2* prow = part + unit * n_chunk_max * G;
+    float2 ml[kPairs];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = tid + u * kSelThreads;
-      ml[u] = i < n_chunk * G ? part[(unit * n_chunk_max + i / G) * G + i % G]
+    for (int u = 0; u < kPairs; ++u)
+      ml[u] = n_chunk_max > 0 ? prow[min(tid + kSelThreads * u, pair_cap - 1)]
                               : make_float2(-INFINITY, 0.f);
-    }
-    // thread tid always sees head tid % G (kSelThreads is a multiple of G)
     float m = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) m = fmaxf(m, ml[u].x);
+    for (int u = 0; u < kPairs; ++u)
+      m = fmaxf(m, tid + kSelThreads * u < n_pairs ? ml[u].x : -INFINITY);
+    m = column_reduce<G>(m, OpMax());
+    if (lane < G) S.wred[0][wave][lane] = m;
+    __syncthreads();
+    float Mh = -INFINITY;
 #pragma unroll
-    for (int o = G; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    if (lane < G) hm_s[wave][lane] = m;
-    __syncthreads();
-    if (tid < G) {
-      float mm = hm_s[0][tid];
-      for (int w = 1; w < kSelWaves; ++w) mm = fmaxf(mm, hm_s[w][tid]);
-      M_s[tid] = mm;
-    }
-    __syncthreads();
-    const float Mh = M_s[tid % G];
+    for (int w = 0; w < kSelWaves; ++w) Mh = fmaxf(Mh, S.wred[0][w][tid % G]);
     float l = 0.f;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      if (ml[u].x != -INFINITY) l += ml[u].y * fast_exp2(ml[u].x - Mh);
-#pragma unroll
-    for (int o = G; o < kWave; o <<= 1) l += __shfl_xor(l, o, kWave);
-    if (lane < G) hl_s[wave][lane] = l;
+    for (int u = 0; u < kPairs; ++u)
+      l += (tid + kSelThreads * u < n_pairs && ml[u].x != -INFINITY)
+               ? ml[u].y * fast_exp2(ml[u].x - Mh) : 0.f;
+    l = column_reduce<G>(l, OpSum());
+    if (lane < G) S.wred[1][wave][lane] = l;
     __syncthreads();
-    if (tid < G) {
-      float ll = 0.f;
-      for (int w = 0; w < kSelWaves; ++w) ll += hl_s[w][tid];
-      invL_s[tid] = 1.f / ll;
+    float M[G], invL[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mm = -INFINITY, ll = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) {
+        mm = fmaxf(mm, S.wred[0][w][h]);
+        ll += S.wred[1][w][h];
+      }
+      M[h] = mm;
+      invL[h] = 1.f / ll;
     }
+    // group probabilities of every visible window into LDS, 4 windows per
+    // thread per round, all of a round's loads in flight together
+    const float* lrow = logits + unit * G * ldc;
+    const int cmax = max(nvis - 1, 0);
+    for (int r0 = 0; r0 < nvis; r0 += 4 * kSelThreads) {
+      float lg[4][G];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = min(r0 + tid + kSelThreads * u, cmax);
+#pragma unroll
+        for (int h = 0; h < G; ++h) lg[u][h] = lrow[size_t(h) * ldc + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = r0 + tid + kSelThreads * u;
+        float pg = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) pg += fast_exp2(lg[u][h] - M[h]) * invL[h];
+        if (c < nvis) S.pg[c] = pg;
+      }
+    }
+    // block CIS maxima written by the logits kernel (blocks up to 16*n_chunk)
+    float cv[kBlkPer];
+    const int owned = (cisb != nullptr && n_chunk > 0) ? min(nb, 16 * n_chunk + 1) : 0;
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u)
+      cv[u] = cisb != nullptr ? cisb[unit * ldb + min(tid + kSelThreads * u, ldb - 1)] : 0.f;
     __syncthreads();
-    // block scores: windows 4i-1 .. 4i+3 overlap block i
-    for (int i = tid; i < nb; i += kSelThreads) {
-      float lg[5][G];
 #pragma unroll
-      for (int e = 0; e < 5; ++e) {
-        const int c = 4 * i - 1 + e;
+    for (int u = 0; u < kBlkPer; ++u) {
+      const int i = tid + kSelThreads * u;
+      if (i < nb) {
+        float pm = -INFINITY;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-          lg[e][h] = (c >= 0 && c < nvis) ? logits[(unit * G + h) * nc_max + c] : -INFINITY;
-      }
-      float cw[5];
-#pragma unroll
-      for (int e = 0; e < 5; ++e) {
-        const int c = 4 * i - 1 + e;
-        cw[e] = (cis_pooled != nullptr && c >= 0 && c < nc)
-                    ? cis_pooled[(size_t(cbase) + c) * kv_heads + kv] : -INFINITY;
-      }
-      float pm = -INFINITY, cm = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 5; ++e) {
-        const int c = 4 * i - 1 + e;
-        if (c >= 0 && c < nvis) {
-          float pg = 0.f;
-#pragma unroll
-          for (int h = 0; h < G; ++h) pg += fast_exp2(lg[e][h] - M_s[h]) * invL_s[h];
-          pm = fmaxf(pm, pg);
+        for (int e = 0; e < 5; ++e) {
+          const int c = 4 * i - 1 + e;
+          const float pg = S.pg[min(max(c, 0), kWinLds - 1)];
+          if (c >= 0 && c < nvis) pm = fmaxf(pm, pg);
         }
-        cm = fmaxf(cm, cw[e]);
+        float sc = pm == -INFINITY ? 0.f : pm;
+        if (cisb != nullptr) sc += cis_weight * (i < owned ? cv[u] : 0.f);
+        put(i, sc);
+        if (block_scores != nullptr) block_scores[unit * nb_max + i] = sc;
       }
-      float sc = pm == -INFINITY ? 0.f : pm;
-      if (cis_pooled != nullptr) sc += cis_weight * (cm == -INFINITY ? 0.f : cm);
-      S.sc[i] = sc;
-      if (block_scores != nullptr) block_scores[unit * nb_max + i] = sc;
     }
     if (block_scores != nullptr)
       for (int i = nb + tid; i < nb_max; i += kSelThreads) block_scores[unit * nb_max + i] = 0.f;
-    if (window_probs != nullptr) {
-      for (int c = tid; c < nc_max; c += kSelThreads) {
-        float pg = 0.f;
-        if (c < nvis) {
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-            pg += fast_exp2(logits[(unit * G + h) * nc_max + c] - M_s[h]) * invL_s[h];
-        }
-        window_probs[unit * nc_max + c] = pg;
-      }
-    }
+    if (window_probs != nullptr)
+      for (int c = tid; c < nc_max; c += kSelThreads)
+        window_probs[unit * nc_max + c] = c < nvis ? S.pg[c] : 0.f;
   } else {
-    for (int i = tid; i < nb; i += kSelThreads) S.sc[i] = block_scores[unit * nb_max + i];
+    float v[kBlkPer];
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u)
+      v[u] = nb > 0 ? block_scores[unit * nb_max + min(tid + kSelThreads * u, nb - 1)] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u) {
+      const int i = tid + kSelThreads * u;
+      if (i < nb) put(i, v[u]);
+    }
   }
   if (indices == nullptr) return;
   __syncthreads();
-  topk_select(S, nb, t, topk, n_init, n_local, indices + unit * topk);
+  topk_finish(S, n_elig, kf, n_free, lo, hi, topk, indices + unit * topk);
 }
 
 // --------------------------------------------------------------------------- host
@@ -457,43 +652,60 @@ static int n_windows_max(int max_seqlen_k) {
   return max_seqlen_k >= kKernel ? (max_seqlen_k - kKernel) / kStride + 1 : 0;
 }
 
-size_t scores_ws_bytes(int batch, int kv_heads, int group, int nc_max) {
-  const size_t units = size_t(batch) * kv_heads;
-  const size_t n_chunk = (size_t(nc_max) + kChunkWindows - 1) / kChunkWindows;
-  size_t bytes = (units * group * size_t(nc_max) * sizeof(float) + 255) & ~size_t(255);
-  bytes += (units * n_chunk * group * sizeof(float2) + 255) & ~size_t(255);
-  return bytes;
+struct ScoreDims {
+  int nc_max, nb_max, n_chunk_max, ldc, ldb;
+};
+static ScoreDims score_dims(int max_seqlen_k) {
+  ScoreDims d;
+  d.nc_max = n_windows_max(max_seqlen_k);
+  d.nb_max = (max_seqlen_k + kBlock - 1) / kBlock;
+  d.n_chunk_max = (d.nc_max + kChunkWindows - 1) / kChunkWindows;
+  d.ldc = d.n_chunk_max * kChunkWindows;
+  d.ldb = d.n_chunk_max * 16 + 1;
+  return d;
 }
 
-ScoresWs scores_ws_carve(void* base, int batch, int kv_heads, int group, int nc_max) {
+static size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t scores_ws_bytes(int batch, int kv_heads, int group, int max_seqlen_k) {
+  const ScoreDims d = score_dims(max_seqlen_k);
+  const size_t units = size_t(batch) * kv_heads;
+  return up256(units * group * size_t(d.ldc) * sizeof(float)) +
+         up256(units * d.n_chunk_max * group * sizeof(float2)) +
+         up256(units * size_t(d.ldb) * sizeof(float));
+}
+
+ScoresWs scores_ws_carve(void* base, int batch, int kv_heads, int group, int max_seqlen_k) {
+  const ScoreDims d = score_dims(max_seqlen_k);
   const size_t units = size_t(batch) * kv_heads;
   char* p = static_cast<char*>(base);
   ScoresWs ws;
   ws.logits = reinterpret_cast<float*>(p);
-  p += (units * group * size_t(nc_max) * sizeof(float) + 255) & ~size_t(255);
+  p += up256(units * group * size_t(d.ldc) * sizeof(float));
   ws.part = reinterpret_cast<float2*>(p);
+  p += up256(units * d.n_chunk_max * group * sizeof(float2));
+  ws.cisb = reinterpret_cast<float*>(p);
   return ws;
 }
 
 template <int G, typename TQ, typename TKC>
 static hipError_t launch_scores_g(const DecodeScoresArgs& a, hipStream_t s) {
-  const int nc_max = n_windows_max(a.max_seqlen_k);
-  const int nb_max = (a.max_seqlen_k + kBlock - 1) / kBlock;
-  const int n_chunk_max = (nc_max + kChunkWindows - 1) / kChunkWindows;
-  if (n_chunk_max > 0) {
+  const ScoreDims d = score_dims(a.max_seqlen_k);
+  float* cisb = a.cis_pooled != nullptr ? a.ws.cisb : nullptr;
+  if (d.n_chunk_max > 0) {
     hipError_t e = launch_kernel(
-        kKindLogits, window_logits_kernel<G, TQ, TKC>, dim3(n_chunk_max, a.kv_heads, a.batch),
+        kKindLogits, window_logits_kernel<G, TQ, TKC>, dim3(d.n_chunk_max, a.kv_heads, a.batch),
         dim3(256), s, static_cast<const TQ*>(a.q), static_cast<TKC*>(a.kc), a.cu_k, a.cu_c,
-        a.ws.logits, a.ws.part, a.kv_heads, nc_max, n_chunk_max, a.scale_log2,
-        static_cast<const TQ*>(a.refresh_k), a.refresh_cis, a.refresh_cis_pooled);
+        a.ws.logits, a.ws.part, cisb, a.cis_pooled, a.kv_heads, d.ldc, d.n_chunk_max, d.ldb,
+        a.scale_log2, static_cast<const TQ*>(a.refresh_k), a.refresh_cis);
     if (e != hipSuccess) return e;
   }
   return launch_kernel(kKindBlockScores, select_kernel<G, true>, dim3(a.batch, a.kv_heads),
                        dim3(kSelThreads), s, static_cast<const float*>(a.ws.logits),
-                       static_cast<const float2*>(a.ws.part), a.cis_pooled, a.cis_weight,
-                       static_cast<const int*>(nullptr), a.cu_k, a.cu_c, a.batch, a.block_scores,
-                       a.window_probs, a.kv_heads, nc_max, nb_max, n_chunk_max, a.indices, a.topk,
-                       a.n_init, a.n_local);
+                       static_cast<const float2*>(a.ws.part), static_cast<const float*>(cisb),
+                       a.cis_weight, static_cast<const int*>(nullptr), a.cu_k, a.cu_c, a.batch,
+                       a.block_scores, a.window_probs, a.kv_heads, d.nc_max, d.ldc, d.nb_max,
+                       d.n_chunk_max, d.ldb, a.indices, a.topk, a.n_init, a.n_local);
 }
 
 template <typename TQ, typename TKC>
@@ -527,7 +739,7 @@ hipError_t launch_select_topk(const float* block_scores, int* indices, const int
                        static_cast<const float2*>(nullptr), static_cast<const float*>(nullptr),
                        0.f, cu_q, cu_k, static_cast<const int*>(nullptr), batch,
                        const_cast<float*>(block_scores), static_cast<float*>(nullptr), kv_heads,
-                       0, nb_max, 0, indices, topk, n_init, n_local);
+                       0, 0, nb_max, 0, 0, indices, topk, n_init, n_local);
 }
 
 }  // namespace nsa

@@ -137,6 +137,41 @@ def test_select_topk_decode_bit_exact(k, n_init, n_local):
             assert got[b, g].tolist() == ref.tolist(), (b, g)
 
 
+@pytest.mark.parametrize("dist", ["tiny_wide_range", "with_infinities", "all_equal", "two_values"])
+def test_select_topk_edge_distributions(dist):
+    """Score sets that stress the histogram selection: distinct values spread over
+    many binades (deep refinement), +/-inf (no finite range), all equal and two
+    values (pure ties, decided by the lower id)."""
+    lengths = [4096, 65536, 131072, 20000]
+    B = len(lengths)
+    nb_max = -(-max(lengths) // 64)
+    z = np64(gen.normal(SEED + 12, 1, (B, 2, nb_max)))
+    if dist == "tiny_wide_range":
+        sc = np.exp2(np.floor(z * 40.0)) * (1.0 + 0.5 * np.tanh(z))      # 2^-160 .. 2^160
+        sc = sc.astype(np.float32)
+    elif dist == "with_infinities":
+        sc = z.astype(np.float32)
+        sc[:, :, ::97] = np.inf
+        sc[:, :, 5::89] = -np.inf
+    elif dist == "all_equal":
+        sc = np.full(z.shape, 0.25, dtype=np.float32)
+    else:
+        sc = np.where(z > 0.3, 1.0, 0.5).astype(np.float32)
+    scores = torch.from_numpy(sc).to(DEV)
+    idx = torch.full((B, 2, 64), -7, dtype=torch.int32, device=DEV)
+    cu_k = cu(lengths)
+    log(f"select edge distribution {dist}")
+    nsa.nsa_select_topk(scores, idx, cu_k, max(lengths), 64, 1, 16)
+    torch.cuda.synchronize()
+    s64 = sc.astype(np.float64)
+    got = idx.cpu().numpy()
+    for b, L in enumerate(lengths):
+        nb = -(-L // 64)
+        for g in range(2):
+            ref = oracle.select_blocks(s64[b, g, :nb], L - 1, nb, 64, 1, 16, 64)
+            assert got[b, g].tolist() == ref.tolist(), (dist, b, g)
+
+
 def test_select_topk_prefill_bit_exact():
     lengths = [100, 3000]
     rows = sum(lengths)

@@ -38,14 +38,58 @@ def parse():
     ap.add_argument("--warmup", type=int, default=280)
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--pinned-32k", action="store_true", help="all contexts 32768")
-    ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="bf16")
     ap.add_argument("--profile-steps", type=int, default=280)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of from a HIP graph "
                          "(for counter-collection runs, which serialise dispatches)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="finish with three streaming kernels (fp32 negation) that read and "
+                         "write 256 MiB each, the reference dispatch that scales the HBM "
+                         "byte counters")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "selected_attn_decode_nosa1b_counters.md")
+ATTN_SOURCES = ["sparse_attention_compress_amd/csrc/attn.hip",
+                "sparse_attention_compress_amd/csrc/common.h"]
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per selected-attention launch from the committed counter summary.
+
+    The summary holds FETCH_SIZE and WRITE_SIZE of the kernel, each scaled by what
+    the same counter reads for a plain copy of known size, and the hash of the
+    kernel sources it was taken with.  None when it is missing or the sources
+    have changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`")
+        if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", "traffic_bytes_per_launch"):
+            k_, v_ = line.split(":", 1)
+            vals[k_.strip()] = v_.strip()
+    if vals.get("source_hash") != attn_source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
 
 
 def main():
@@ -215,9 +259,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(),
             "algorithmic_bytes_per_launch": attn_bytes,
             "mean_kernel_us": round(kern_us["selected_attn"], 3),
+            "source_hash": attn_source_hash(),
         },
         "kernel_us": {k_: round(v_, 3) for k_, v_ in kern_us.items()},
         "step_algorithmic_bytes": step_bytes,
@@ -226,6 +271,18 @@ def main():
         "timed_gpu_ms": round(gpu_ms, 3),
     }
 
+    if args.calibrate_copy:
+        # a plain elementwise kernel (a device-to-device copy_ would be a DMA
+        # blit, not a kernel dispatch the counters see)
+        src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration: 3 fp32 negations reading and writing {COPY_BYTES} bytes each",
+              file=sys.stderr, flush=True)
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_layer0"] = cpu_baseline(w, layers[0], lengths, args)
     print(json.dumps(result), flush=True)

@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=280)
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--pinned-32k", action="store_true", help="all contexts 32768")
-    ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="bf16")
+    ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--profile-steps", type=int, default=280)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -332,8 +332,8 @@ __global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
   static_assert(G <= 16, "one MFMA column per query head");
   constexpr int D = kHeadDim;
   constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
-  __shared__ float m_s[4][G], l_s[4][G];
-  __shared__ float acc_s[4][G][D];
+  __shared__ float m_s[4][16], l_s[4][16];
+  __shared__ float accx_s[4][32][kWave];  // [wave][tile element 4n + e][lane]
   __shared__ int ids_s[kMaxWgSlots];
   __shared__ int nv_s;
 
@@ -470,44 +470,58 @@ __global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
     auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
     l_run = __uint_as_float(y[0]) + __uint_as_float(y[1]);
   }
-  if (c16 < G) {
-    if (r4 == 0) {
-      m_s[wave][c16] = m_run;
-      l_s[wave][c16] = l_run;
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc_s[wave][c16][16 * n + 4 * r4 + e] = acc[n][e];
+  if (r4 == 0) {
+    m_s[wave][c16] = m_run;
+    l_s[wave][c16] = l_run;
   }
+  // every wave holds the same tile layout: lane-minor staging is conflict-free
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) accx_s[wave][4 * n + e][lane] = acc[n][e];
   __syncthreads();
 
+  // wave w merges tiles n = 2w, 2w+1 of the four waves for its lane's entries
+  // (head c16, dims 16n + 4 r4 .. +3) and writes them as one 16-byte run each
+  float f[4], M = -INFINITY, L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[w] = m_s[w][c16];
+    M = fmaxf(M, f[w]);
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[w] = (M == -INFINITY || f[w] == -INFINITY) ? 0.f : fast_exp2(f[w] - M);
+    L += f[w] * l_s[w][c16];
+  }
   const int n_split = SPLIT ? int(gridDim.x) : 1;
-  for (int i = tid; i < G * D; i += 256) {
-    const int h = i / D, d = i % D;
-    float mw[4], M = -INFINITY;
+  const size_t ps = unit * n_split + split;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      mw[w] = m_s[w][h];
-      M = fmaxf(M, mw[w]);
+  for (int nn = 0; nn < 2; ++nn) {
+    const int n = 2 * wave + nn;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[e] += f[w] * accx_s[w][4 * n + e][lane];
     }
-    float L = 0.f, Acc = 0.f;
-    if (M != -INFINITY) {
+    if (c16 < G) {
+      if constexpr (SPLIT) {
+        *reinterpret_cast<float4*>(part_acc + (ps * G + c16) * D + 16 * n + 4 * r4) =
+            make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        bf16_t* dst = out + (unit * G + c16) * D + 16 * n + 4 * r4;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
-        L += f * l_s[w][h];
-        Acc += f * acc_s[w][h][d];
+        for (int e = 0; e < 4; ++e) store_f32(dst + e, L > 0.f ? o[e] / L : 0.f);
       }
     }
+  }
+  if (wave == 0 && r4 == 0 && c16 < G) {
     if constexpr (SPLIT) {
-      const size_t ps = unit * n_split + split;
-      part_acc[(ps * G + h) * D + d] = Acc;
-      if (d == 0) part_ml[ps * G + h] = make_float2(M, L);
-    } else {
-      store_f32(out + (unit * G + h) * D + d, L > 0.f ? Acc / L : 0.f);
-      if (lse != nullptr && d == 0)
-        lse[unit * G + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      part_ml[ps * G + c16] = make_float2(M, L);
+    } else if (lse != nullptr) {
+      lse[unit * G + c16] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -525,15 +539,20 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float2* __restr
   __shared__ float ML_s[2];
   const size_t unit = blockIdx.x;
   const int h = blockIdx.y, d = threadIdx.x;
-  float2 ml = make_float2(-INFINITY, 0.f);
-  if (d < n_split) ml = part_ml[(unit * n_split + d) * G + h];
+  // every load first: the (max, sum) pair of split d and this dim of every split
+  const float2 ml0 = part_ml[(unit * n_split + min(d, n_split - 1)) * G + h];
+  const float* src = part_acc + (unit * n_split * G + h) * D + d;
+  const size_t stride = size_t(G) * D;
+  float x[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) x[sp] = sp < n_split ? src[sp * stride] : 0.f;
   // max and normaliser over the splits (n_split <= 64: one wave holds them all)
-  float M = ml.x;
   if (d < kWave) {
-    M = wave_max(d < n_split ? ml.x : -INFINITY);
-    const float f = (d < n_split && M != -INFINITY) ? fast_exp2(ml.x - M) : 0.f;
-    const float L = wave_sum(f * ml.y);
-    if (d < n_split) f_s[d] = f;
+    const float mx = d < n_split ? ml0.x : -INFINITY;
+    const float M = wave_max(mx);
+    const float f = (d < n_split && M != -INFINITY && mx != -INFINITY) ? fast_exp2(mx - M) : 0.f;
+    const float L = wave_sum(f * (d < n_split ? ml0.y : 0.f));
+    f_s[d] = f;
     if (d == 0) {
       ML_s[0] = M;
       ML_s[1] = L;
@@ -542,17 +561,9 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float2* __restr
   __syncthreads();
   const float L = ML_s[1];
   float accv = 0.f;
-  const float* src = part_acc + (unit * n_split * G + h) * D + d;
-  const size_t stride = size_t(G) * D;
-  int sp = 0;
-  for (; sp + 8 <= n_split; sp += 8) {
-    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = src[(sp + e) * stride];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) accv += f_s[sp + e] * x[e];
-  }
-  for (; sp < n_split; ++sp) accv += f_s[sp] * src[sp * stride];
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < n_split) accv += f_s[sp] * x[sp];
   store_f32(out + (unit * G + h) * D + d, L > 0.f ? accv / L : 0.f);
   if (lse != nullptr && d == 0) lse[unit * G + h] = L > 0.f ? (ML_s[0] + __log2f(L)) * kLn2 : -INFINITY;
 }

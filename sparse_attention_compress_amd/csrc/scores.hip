@@ -9,10 +9,11 @@
 // local blocks forced in and the best other blocks picked, ids ascending.
 //
 // window_logits_kernel -- grid (chunk of 64 windows, kv head, sequence), 4 waves
-//   of 16 windows.  bf16 queries and keys run on the matrix cores (S^T = Kc Q^T
-//   with four v_mfma_f32_16x16x32_bf16 per wave, the compressed-key rows loaded
-//   straight into the A operand); other dtypes use fp32 FMAs with the queries
-//   in LDS.  Each compressed key is read from HBM once for the whole GQA group.
+//   of 16 windows, on the matrix cores: S^T = Kc Q^T with the compressed-key rows
+//   loaded straight into the A operand and the group's queries as the B operand
+//   (four v_mfma_f32_16x16x32_bf16 per wave when both are bf16, else thirty-two
+//   v_mfma_f32_16x16x4_f32 in full fp32).  Each compressed key is read from HBM
+//   once for the whole GQA group.
 //   Outputs: log2-domain logits, a per-chunk (max, sum of exp2) per head, and the
 //   CIS maximum of the blocks the chunk owns (blocks 16j..16j+15, the last chunk
 //   also block 16*n_chunks).  The workgroup owning the newest window can first
@@ -24,7 +25,9 @@
 //   best; blocks above it are taken, blocks below dropped, and the bin is
 //   refined the same way until at most 512 candidates remain, which are ranked
 //   exactly by (score desc, id asc); exactly equal scores go to the lower ids.
-//   Chosen ids are written in ascending order by a workgroup scan.
+//   Thread tid keeps the scores and states of ids tid + 512u in registers; the
+//   chosen ids are written in ascending order from wave ballots and one scan of
+//   the per-(slab, wave) counts.
 // Every load phase is branch-free (indices clamped into range, values masked)
 // so all of a thread's loads are in flight together.  No kernel waits on another
 // workgroup: each hand-off is a kernel boundary.
@@ -68,9 +71,9 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
     float* __restrict__ cisb, float* __restrict__ cis_pooled, int kv_heads, int ldc,
     int n_chunk_max, int ldb, float scale_log2, const TQ* __restrict__ k_src,
     const float* __restrict__ cis_src) {
-  constexpr bool kMfma = sizeof(TQ) == 2 && sizeof(TKC) == 2;
+  // bf16 queries and keys: 16x16x32 bf16 tiles; an fp32 operand: 16x16x4 fp32 tiles
+  constexpr bool kBf16 = sizeof(TQ) == 2 && sizeof(TKC) == 2;
   constexpr int D = kHeadDim;
-  __shared__ float q_s[kMfma ? 1 : G][D];
   __shared__ uint32_t new_s[D / 2];  // refreshed compressed key, bf16 pairs
   __shared__ float newf_s[D];        // refreshed compressed key as the cache holds it
   __shared__ float cisw_s[kCisSpan];
@@ -86,32 +89,34 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
   const int n_chunk = (nvis + kChunkWindows - 1) / kChunkWindows;
   const int nb = (len + kBlock - 1) / kBlock;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
   const size_t unit = size_t(b) * kv_heads + kv;
   // the newest window, recomputed from K in this workgroup (decode append), else -1
   const int rw = (k_src != nullptr && nvis == nc && nc - 1 >= c0 && nc - 1 < c0 + kChunkWindows)
                      ? nc - 1 : -1;
 
-  // ---- every global load of the workgroup, before the first use
-  // compressed keys: MFMA path lane (c16, r4) holds window c0+16w+c16, dims 32i+8r4;
-  // FMA path lane (window c0+16w+lane/4, slice lane%4) holds dims 32i+8(lane%4)
-  const int ca = kMfma ? c0 + 16 * wave + (lane & 15) : c0 + 16 * wave + (lane >> 2);
-  const int sl = kMfma ? (lane >> 4) : (lane & 3);
+  // ---- every global load of the workgroup, before the first use.  Lane (c16, r4)
+  // holds row c16 of the A operand (window ca) and column c16 of the B operand
+  // (query head c16; zero past G).  bf16 tiles: dims 32i + 8 r4 .. +8 form the k
+  // range of tile i.  fp32 tiles: dims 32 r4 .. 32 r4 + 31, dim 32 r4 + j being
+  // the k index r4 of tile j, so the 32 tiles cover every dim once.
+  const int ca = c0 + 16 * wave + c16;
   const TKC* krow = kc + (size_t(cbase + min(ca, nvis - 1)) * kv_heads + kv) * D;
-  uint4 ka[4];     // MFMA path (bf16)
-  float kf[4][8];  // FMA path
-  if constexpr (kMfma) {
+  const TQ* qrow = q + (unit * G + min(c16, G - 1)) * D;
+  uint4 ka[4], qb[4];
+  float kf[32], qf[32];
+  if constexpr (kBf16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ka[i] = ld16(krow + 32 * i + 8 * sl);
+    for (int i = 0; i < 4; ++i) {
+      ka[i] = ld16(krow + 32 * i + 8 * r4);
+      qb[i] = ld16(qrow + 32 * i + 8 * r4);
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load8f(krow + 32 * i + 8 * sl, kf[i]);
-  }
-  uint4 qb[4];
-  const int c16 = lane & 15, r4 = lane >> 4;
-  if constexpr (kMfma) {
-    const TQ* qh = q + (unit * G + min(c16, G - 1)) * D;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qb[i] = c16 < G ? ld16(qh + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 4; ++i) {
+      load8f(krow + 32 * r4 + 8 * i, &kf[8 * i]);
+      load8f(qrow + 32 * r4 + 8 * i, &qf[8 * i]);
+    }
   }
   float cisv = -INFINITY;
   if (cis_pooled != nullptr && tid < kCisSpan) {
@@ -134,19 +139,6 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
     } else if (cis_src != nullptr && tid >= 128 && tid < 128 + kKernel) {
       rcis = cis_src[size_t(j0 + tid - 128) * kv_heads + kv];
     }
-  }
-  if constexpr (!kMfma) {
-    const TQ* qg = q + unit * G * D;
-    constexpr int kVecs = G * D / 8;
-    float qv[(kVecs + 255) / 256][8];
-#pragma unroll
-    for (int u = 0; u < (kVecs + 255) / 256; ++u)
-      if (tid + 256 * u < kVecs) load8f(qg + 8 * (tid + 256 * u), qv[u]);
-#pragma unroll
-    for (int u = 0; u < (kVecs + 255) / 256; ++u)
-      if (tid + 256 * u < kVecs)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) (&q_s[0][0])[8 * (tid + 256 * u) + e] = qv[u][e];
   }
 
   // ---- refresh of the newest window, CIS of the windows around the chunk
@@ -173,7 +165,7 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
     }
   }
   __syncthreads();
-  if constexpr (kMfma) {
+  if constexpr (kBf16) {
     if (rw >= 0) {
       // pack the refreshed row (already bf16-exact) for the lane that owns it
       if (tid < D / 2) new_s[tid] = pack_bf16x2(newf_s[2 * tid], newf_s[2 * tid + 1]);
@@ -181,16 +173,20 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
       if (ca == rw) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ka[i] = *reinterpret_cast<const uint4*>(&new_s[(32 * i + 8 * sl) / 2]);
+          ka[i] = *reinterpret_cast<const uint4*>(&new_s[(32 * i + 8 * r4) / 2]);
       }
+    }
+    if (c16 >= G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qb[i] = make_uint4(0u, 0u, 0u, 0u);
     }
   } else {
     if (ca == rw) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kf[i][e] = newf_s[32 * i + 8 * sl + e];
+      for (int j = 0; j < 32; ++j) kf[j] = newf_s[32 * r4 + j];
     }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) qf[j] = c16 < G ? qf[j] : 0.f;
   }
 
   // ---- block CIS maxima of the blocks this chunk owns
@@ -204,84 +200,45 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
     }
   }
 
-  // ---- logits, chunk max and sum of exp2 per head
-  float* lrow = logits + unit * G * ldc;
-  if constexpr (kMfma) {
-    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+  // ---- S^T = Kc Q^T on the matrix cores, then chunk max and sum of exp2 per head
+  f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kBf16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
                                                      __builtin_bit_cast(bf16x8_t, qb[i]), sacc,
                                                      0, 0, 0);
-    // lane (c16, r4): windows cw0 .. cw0+3 of head c16
-    const int cw0 = c0 + 16 * wave + 4 * r4;
-    float sv[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = cw0 + e < nvis ? sacc[e] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[e]);
-    }
-    if (c16 < G)
-      *reinterpret_cast<float4*>(lrow + size_t(c16) * ldc + cw0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
-    mx = cross32(cross16(mx, OpMax()), OpMax());
-    if (r4 == 0) red_s[0][wave][c16] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red_s[0][0][c16], red_s[0][1][c16]),
-                          fmaxf(red_s[0][2][c16], red_s[0][3][c16]));
-    float l = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) l += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - M);
-    l = cross32(cross16(l, OpSum()), OpSum());
-    if (r4 == 0) red_s[1][wave][c16] = l;
-    __syncthreads();
-    if (tid < G)
-      part[(unit * n_chunk_max + chunk) * G + tid] =
-          make_float2(M, red_s[1][0][tid] + red_s[1][1][tid] + red_s[1][2][tid] + red_s[1][3][tid]);
   } else {
-    const bool valid = ca < nvis;
-    float s[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float* qq = &q_s[h][32 * i + 8 * sl];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[h] = fmaf(qq[e], kf[i][e], s[h]);
-      }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s[h] = quad_reduce(s[h], OpSum());
-      s[h] = valid ? s[h] * scale_log2 : -INFINITY;
-    }
-    if (valid) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        if ((h & 3) == sl) lrow[size_t(h) * ldc + ca] = s[h];
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float m = wave_max(s[h]);
-      if (lane == 0) red_s[0][wave][h] = m;
-    }
-    __syncthreads();
-    float M[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      M[h] = fmaxf(fmaxf(red_s[0][0][h], red_s[0][1][h]), fmaxf(red_s[0][2][h], red_s[0][3][h]));
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = (valid && sl == 0) ? fast_exp2(s[h] - M[h]) : 0.f;
-      const float l = wave_sum(p);
-      if (lane == 0) red_s[1][wave][h] = l;
-    }
-    __syncthreads();
-    if (tid < G)
-      part[(unit * n_chunk_max + chunk) * G + tid] =
-          make_float2(M[tid], red_s[1][0][tid] + red_s[1][1][tid] + red_s[1][2][tid] + red_s[1][3][tid]);
+    for (int j = 0; j < 32; ++j)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[j], qf[j], sacc, 0, 0, 0);
   }
+  // lane (c16, r4): windows cw0 .. cw0+3 of head c16
+  float* lrow = logits + unit * G * ldc;
+  const int cw0 = c0 + 16 * wave + 4 * r4;
+  float sv[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sv[e] = cw0 + e < nvis ? sacc[e] * scale_log2 : -INFINITY;
+    mx = fmaxf(mx, sv[e]);
+  }
+  if (c16 < G)
+    *reinterpret_cast<float4*>(lrow + size_t(c16) * ldc + cw0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+  mx = cross32(cross16(mx, OpMax()), OpMax());
+  if (r4 == 0) red_s[0][wave][c16] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red_s[0][0][c16], red_s[0][1][c16]),
+                        fmaxf(red_s[0][2][c16], red_s[0][3][c16]));
+  float l = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) l += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - M);
+  l = cross32(cross16(l, OpSum()), OpSum());
+  if (r4 == 0) red_s[1][wave][c16] = l;
+  __syncthreads();
+  if (tid < G)
+    part[(unit * n_chunk_max + chunk) * G + tid] =
+        make_float2(M, red_s[1][0][tid] + red_s[1][1][tid] + red_s[1][2][tid] + red_s[1][3][tid]);
 }
 
 // ------------------------------------------------------------ kernel 2: select
@@ -291,37 +248,41 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 1024;
 constexpr int kCandMax = kSelThreads;  // candidates ranked exactly, one per thread
 constexpr int kWinLds = 4 * kMaxSortBlocks;  // every window of the longest sequence
-constexpr int kBlkPer = kMaxSortBlocks / kSelThreads;  // strided blocks per thread
+constexpr int kBlkPer = kMaxSortBlocks / kSelThreads;  // slabs: thread tid owns ids tid + 512u
+static_assert(kBlkPer * kSelWaves == kWave, "one lane per (slab, wave) count");
 
 struct SelShared {
-  float sc[kMaxSortBlocks];            // block scores of the row
-  float pg[kWinLds];                   // group probabilities of the windows
+  float pg[kWinLds];                  // group probabilities of the windows
+  float sc[kMaxSortBlocks];           // scores and states, staged only for the
+  unsigned char st[kMaxSortBlocks];   //   exact fallback ranking
   int hist[kBins];
-  unsigned char sel[kMaxSortBlocks];   // 0 out, 1 chosen, 2 still a candidate
-  int cand[kCandMax];
+  float cand_sc[kCandMax];            // candidates of the exact ranking, id order
+  unsigned char cand_keep[kCandMax];
+  int cnt[2][kWave];                  // per (slab, wave) counts of the ordered scans
   float wred[2][kSelWaves][16];
-  int wsum[kSelWaves];
   int misc[4];
 };
 
-// Exclusive scan of per-thread counts in thread order; returns the thread's
-// offset and, in every thread, the total.  Two barriers (the second keeps
-// S.wsum stable until every thread has read it).
-__device__ __forceinline__ int block_exclusive_scan(int cnt, SelShared& S, int& total) {
+// Positions, in ascending id order, of the flagged ids (thread tid, slab u owns id
+// tid + 512u); returns the number flagged, in every thread.  One barrier; `cnt`
+// must not be written again before another barrier.
+__device__ __forceinline__ int ordered_positions(const bool (&flag)[kBlkPer], int (&pos)[kBlkPer],
+                                                 int* cnt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_inclusive_scan(cnt);
-  if (lane == kWave - 1) S.wsum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  total = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int v = S.wsum[w];
-    before += w < wave ? v : 0;
-    total += v;
+  for (int u = 0; u < kBlkPer; ++u) {
+    const unsigned long long m = __ballot(flag[u]);
+    pos[u] = __popcll(m & below);
+    if (lane == 0) cnt[u * kSelWaves + wave] = __popcll(m);
   }
   __syncthreads();
-  return before + incl - cnt;
+  const int c = cnt[lane];  // lane = slab * waves + wave: the id order of the runs
+  const int incl = wave_inclusive_scan(c);
+  const int excl = incl - c;
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) pos[u] += __builtin_amdgcn_readlane(excl, u * kSelWaves + wave);
+  return __builtin_amdgcn_readlane(incl, kWave - 1);
 }
 
 __device__ __forceinline__ void block_minmax(float lo, float hi, SelShared& S, float& vmin,
@@ -343,17 +304,24 @@ __device__ __forceinline__ void block_minmax(float lo, float hi, SelShared& S, f
   }
 }
 
-// Top-k over S.sc[0..n_elig) with S.sel marking forced (1), free candidates (2)
-// and the rest (0); kf free places to fill; lo/hi: per-thread min/max of the
-// free scores.  Writes topk ascending ids (-1 padded) to out.
-__device__ void topk_finish(SelShared& S, int n_elig, int kf, int n_free, float lo, float hi,
-                            int topk, int* __restrict__ out) {
+__device__ __forceinline__ int bin_of(float v, float base, float scale) {
+  return min(kBins - 1, max(0, int((v - base) * scale)));
+}
+
+// Top-k over the eligible ids with scores sc and states st held in registers
+// (0 out, 1 chosen, 2 free candidate); kf free places to fill among n_free
+// candidates whose scores lie in [lo, hi] per thread.  Writes topk ascending ids
+// (-1 padded) to out.
+__device__ __forceinline__ void topk_select(SelShared& S, const float (&sc)[kBlkPer],
+                                            int (&st)[kBlkPer], int n_elig, int kf, int n_free,
+                                            float lo, float hi, int topk,
+                                            int* __restrict__ out) {
   const int tid = threadIdx.x, lane = tid & 63;
   float vmin, vmax;
   block_minmax(lo, hi, S, vmin, vmax);
   int need = kf;
   bool take_rest = false;  // every remaining candidate is chosen
-  bool by_index = false;   // all free scores equal: the lowest ids are chosen
+  bool by_index = false;   // all remaining scores equal: the lowest ids are chosen
   bool by_rank = false;    // few candidates: exact rank among them
   bool by_scan = false;    // otherwise: exact rank against every candidate
   if (kf > 0 && kf < n_free) {
@@ -370,13 +338,8 @@ __device__ void topk_finish(SelShared& S, int n_elig, int kf, int n_free, float 
       }
       // histogram of the candidates over [base, base + width)
 #pragma unroll
-      for (int u = 0; u < kBlkPer; ++u) {
-        const int i = tid + kSelThreads * u;
-        if (i < n_elig && S.sel[i] == 2) {
-          const int bin = min(kBins - 1, max(0, int((S.sc[i] - base) * scale)));
-          atomicAdd(&S.hist[bin], 1);
-        }
-      }
+      for (int u = 0; u < kBlkPer; ++u)
+        if (st[u] == 2) atomicAdd(&S.hist[bin_of(sc[u], base, scale)], 1);
       __syncthreads();
       if (tid < kWave) {
         if (tid == 0) {  // found below; defaults keep every later step in range
@@ -411,10 +374,9 @@ __device__ void topk_finish(SelShared& S, int n_elig, int kf, int n_free, float 
       const int bstar = S.misc[0], above = S.misc[1], m = S.misc[2];
 #pragma unroll
       for (int u = 0; u < kBlkPer; ++u) {
-        const int i = tid + kSelThreads * u;
-        if (i < n_elig && S.sel[i] == 2) {
-          const int bin = min(kBins - 1, max(0, int((S.sc[i] - base) * scale)));
-          if (bin != bstar) S.sel[i] = bin > bstar ? 1 : 0;
+        if (st[u] == 2) {
+          const int bin = bin_of(sc[u], base, scale);
+          if (bin != bstar) st[u] = bin > bstar ? 1 : 0;
         }
       }
       need -= above;
@@ -431,70 +393,78 @@ __device__ void topk_finish(SelShared& S, int n_elig, int kf, int n_free, float 
     }
     if (!take_rest && !by_rank && !by_index) by_scan = true;  // refinement did not settle
   }
-  __syncthreads();
   if (by_scan) {
     // each remaining candidate counts the candidates that beat it
-    unsigned char keep[kBlkPer];
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u) {
+      const int i = tid + kSelThreads * u;
+      if (i < n_elig) {
+        S.sc[i] = sc[u];
+        S.st[i] = static_cast<unsigned char>(st[u]);
+      }
+    }
+    __syncthreads();
+    int keep[kBlkPer];
 #pragma unroll
     for (int u = 0; u < kBlkPer; ++u) {
       const int i = tid + kSelThreads * u;
       keep[u] = 0;
-      if (i < n_elig && S.sel[i] == 2) {
-        const float v = S.sc[i];
+      if (st[u] == 2) {
+        const float v = sc[u];
         int rank = 0;
         for (int o = 0; o < n_elig; ++o) {
-          if (S.sel[o] != 2) continue;
+          if (S.st[o] != 2) continue;
           const float w = S.sc[o];
           rank += (w > v || (w == v && o < i)) ? 1 : 0;
         }
         keep[u] = rank < need ? 1 : 0;
       }
     }
-    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kBlkPer; ++u) {
-      const int i = tid + kSelThreads * u;
-      if (i < n_elig && S.sel[i] == 2) S.sel[i] = keep[u];
-    }
-    __syncthreads();
+    for (int u = 0; u < kBlkPer; ++u)
+      if (st[u] == 2) st[u] = keep[u];
   }
-  // candidates listed in id order (thread tid owns a contiguous run of ids)
-  const int per = (n_elig + kSelThreads - 1) / kSelThreads;
-  const int i0 = tid * per, i1 = min(i0 + per, n_elig);
   if (by_rank || by_index) {
-    int cnt = 0;
-    for (int i = i0; i < i1; ++i) cnt += S.sel[i] == 2;
-    int m = 0;
-    int pos = block_exclusive_scan(cnt, S, m);
-    for (int i = i0; i < i1; ++i) {
-      if (S.sel[i] != 2) continue;
-      if (by_index) S.sel[i] = pos < need ? 1 : 0;
-      else if (pos < kCandMax) S.cand[pos] = i;
-      ++pos;
-    }
-    m = min(m, kCandMax);
-    __syncthreads();
-    if (by_rank && tid < m) {
-      const int i = S.cand[tid];
-      const float v = S.sc[i];
-      int rank = 0;
-      for (int c = 0; c < m; ++c) {
-        const int o = S.cand[c];
-        const float w = S.sc[o];
-        rank += (w > v || (w == v && o < i)) ? 1 : 0;
+    bool f[kBlkPer];
+    int pos[kBlkPer];
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u) f[u] = st[u] == 2;
+    const int m = min(ordered_positions(f, pos, S.cnt[0]), kCandMax);
+    if (by_index) {
+#pragma unroll
+      for (int u = 0; u < kBlkPer; ++u)
+        if (f[u]) st[u] = pos[u] < need ? 1 : 0;
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBlkPer; ++u)
+        if (f[u] && pos[u] < kCandMax) S.cand_sc[pos[u]] = sc[u];
+      __syncthreads();
+      if (tid < m) {
+        // candidates sit in id order, so the lower id of a tie is the lower slot
+        const float v = S.cand_sc[tid];
+        int rank = 0;
+        for (int c = 0; c < m; ++c) {
+          const float w = S.cand_sc[c];
+          rank += (w > v || (w == v && c < tid)) ? 1 : 0;
+        }
+        S.cand_keep[tid] = rank < need ? 1 : 0;
       }
-      S.sel[i] = rank < need ? 1 : 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kBlkPer; ++u)
+        if (f[u]) st[u] = (pos[u] < m && S.cand_keep[pos[u]]) ? 1 : 0;
     }
-    __syncthreads();
   }
   // ordered compaction of the chosen ids
-  int cnt = 0;
-  for (int i = i0; i < i1; ++i) cnt += (S.sel[i] == 1 || (take_rest && S.sel[i] == 2));
-  int total = 0;
-  int pos = block_exclusive_scan(cnt, S, total);
+  bool f[kBlkPer];
+  int pos[kBlkPer];
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) f[u] = st[u] == 1 || (take_rest && st[u] == 2);
+  const int total = ordered_positions(f, pos, S.cnt[1]);
   // writes stay inside the row's topk slots even if the count were wrong
-  for (int i = i0; i < i1; ++i)
-    if ((S.sel[i] == 1 || (take_rest && S.sel[i] == 2)) && pos < topk) out[pos++] = i;
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u)
+    if (f[u] && pos[u] < topk) out[pos[u]] = tid + kSelThreads * u;
   for (int i = max(0, total) + tid; i < topk; i += kSelThreads) out[i] = -1;
   (void)lane;
 }
@@ -514,6 +484,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   row_position(row, cu_q, cu_k, batch, b, t);
   const int len = cu_k[b + 1] - cu_k[b];
   const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
+  const int n_slab = (nb + kSelThreads - 1) / kSelThreads;  // uniform
   const size_t unit = size_t(row) * kv_heads + kv;
   // selection geometry
   const int n_elig = t >= 0 ? min(nb, t / kBlock + 1) : 0;
@@ -522,34 +493,45 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int n_forced = f_init + (n_elig - f_loc);
   const int n_free = n_elig - n_forced;
   const int kf = max(0, min(topk - n_forced, n_free));
-  const unsigned char free_mark = kf == n_free ? 1 : (kf == 0 ? 0 : 2);
+  const int free_mark = kf == n_free ? 1 : (kf == 0 ? 0 : 2);
   for (int i = tid; i < kBins; i += kSelThreads) S.hist[i] = 0;
 
-  float lo = INFINITY, hi = -INFINITY;  // free-score range seen by this thread
-  auto put = [&](int i, float sc) {
-    S.sc[i] = sc;
-    const bool forced = i < f_init || (i >= f_loc && i < n_elig);
-    S.sel[i] = i >= n_elig ? 0 : (forced ? 1 : free_mark);
-    if (i < n_elig && !forced) {
-      lo = fminf(lo, sc);
-      hi = fmaxf(hi, sc);
-    }
-  };
-
+  float sc[kBlkPer];
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) sc[u] = 0.f;
   if constexpr (FROM_LOGITS) {
     const int nc = cu_c[b + 1] - cu_c[b];
     const int nvis = min(nc, full_windows_dev(len));
     const int n_chunk = (nvis + kChunkWindows - 1) / kChunkWindows;
-    // per-head softmax normaliser from the chunk (max, sum) pairs; pair i of this
-    // thread belongs to head i % G == tid % G.  Loads clamped into range, masked.
+    // ---- every load at once: the chunk (max, sum) pairs, the first round of
+    // logits and the block CIS maxima.  Counts of load rounds are uniform;
+    // indices inside a round are clamped into range and the values masked.
     constexpr int kPairs = 4096 / kSelThreads;
-    const int n_pairs = n_chunk * G, pair_cap = max(n_chunk_max * G, 1);
+    const int n_pairs = n_chunk * G;
+    const int n_pu = (n_pairs + kSelThreads - 1) / kSelThreads;
     const float2* prow = part + unit * n_chunk_max * G;
     float2 ml[kPairs];
 #pragma unroll
     for (int u = 0; u < kPairs; ++u)
-      ml[u] = n_chunk_max > 0 ? prow[min(tid + kSelThreads * u, pair_cap - 1)]
-                              : make_float2(-INFINITY, 0.f);
+      ml[u] = u < n_pu ? prow[min(tid + kSelThreads * u, n_pairs - 1)] : make_float2(-INFINITY, 0.f);
+    const float* lrow = logits + unit * G * ldc;
+    const int cmax = max(nvis - 1, 0);
+    const int n_wu = min(4, (nvis + kSelThreads - 1) / kSelThreads);  // first round only
+    float lg[4][G];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = min(tid + kSelThreads * u, cmax);
+#pragma unroll
+      for (int h = 0; h < G; ++h) lg[u][h] = u < n_wu ? lrow[size_t(h) * ldc + c] : 0.f;
+    }
+    float cv[kBlkPer];
+    const bool with_cis = cisb != nullptr && n_chunk > 0;
+#pragma unroll
+    for (int u = 0; u < kBlkPer; ++u)
+      cv[u] = (with_cis && u < n_slab) ? cisb[unit * ldb + min(tid + kSelThreads * u, ldb - 1)] : 0.f;
+
+    // per-head softmax normaliser from the chunk pairs; pair i of this thread
+    // belongs to head i % G == tid % G
     float m = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kPairs; ++u)
@@ -580,17 +562,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       M[h] = mm;
       invL[h] = 1.f / ll;
     }
-    // group probabilities of every visible window into LDS, 4 windows per
-    // thread per round, all of a round's loads in flight together
-    const float* lrow = logits + unit * G * ldc;
-    const int cmax = max(nvis - 1, 0);
+    // group probabilities of every visible window into LDS, 4 windows per thread
+    // per round; rounds after the first load their logits here
     for (int r0 = 0; r0 < nvis; r0 += 4 * kSelThreads) {
-      float lg[4][G];
+      if (r0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = min(r0 + tid + kSelThreads * u, cmax);
+        for (int u = 0; u < 4; ++u) {
+          const int c = min(r0 + tid + kSelThreads * u, cmax);
 #pragma unroll
-        for (int h = 0; h < G; ++h) lg[u][h] = lrow[size_t(h) * ldc + c];
+          for (int h = 0; h < G; ++h) lg[u][h] = lrow[size_t(h) * ldc + c];
+        }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -601,17 +582,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (c < nvis) S.pg[c] = pg;
       }
     }
-    // block CIS maxima written by the logits kernel (blocks up to 16*n_chunk)
-    float cv[kBlkPer];
-    const int owned = (cisb != nullptr && n_chunk > 0) ? min(nb, 16 * n_chunk + 1) : 0;
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u)
-      cv[u] = cisb != nullptr ? cisb[unit * ldb + min(tid + kSelThreads * u, ldb - 1)] : 0.f;
     __syncthreads();
+    // blocks up to 16 * n_chunk carry a CIS maximum from the logits kernel
+    const int owned = with_cis ? min(nb, 16 * n_chunk + 1) : 0;
 #pragma unroll
     for (int u = 0; u < kBlkPer; ++u) {
       const int i = tid + kSelThreads * u;
-      if (i < nb) {
+      if (u < n_slab) {
         float pm = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 5; ++e) {
@@ -619,10 +596,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           const float pg = S.pg[min(max(c, 0), kWinLds - 1)];
           if (c >= 0 && c < nvis) pm = fmaxf(pm, pg);
         }
-        float sc = pm == -INFINITY ? 0.f : pm;
-        if (cisb != nullptr) sc += cis_weight * (i < owned ? cv[u] : 0.f);
-        put(i, sc);
-        if (block_scores != nullptr) block_scores[unit * nb_max + i] = sc;
+        float s = pm == -INFINITY ? 0.f : pm;
+        if (cisb != nullptr) s += cis_weight * (i < owned ? cv[u] : 0.f);
+        sc[u] = s;
+        if (block_scores != nullptr && i < nb) block_scores[unit * nb_max + i] = s;
       }
     }
     if (block_scores != nullptr)
@@ -631,19 +608,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int c = tid; c < nc_max; c += kSelThreads)
         window_probs[unit * nc_max + c] = c < nvis ? S.pg[c] : 0.f;
   } else {
-    float v[kBlkPer];
 #pragma unroll
     for (int u = 0; u < kBlkPer; ++u)
-      v[u] = nb > 0 ? block_scores[unit * nb_max + min(tid + kSelThreads * u, nb - 1)] : 0.f;
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u) {
-      const int i = tid + kSelThreads * u;
-      if (i < nb) put(i, v[u]);
-    }
+      if (u < n_slab) sc[u] = block_scores[unit * nb_max + min(tid + kSelThreads * u, nb - 1)];
   }
   if (indices == nullptr) return;
-  __syncthreads();
-  topk_finish(S, n_elig, kf, n_free, lo, hi, topk, indices + unit * topk);
+
+  int st[kBlkPer];
+  float lo = INFINITY, hi = -INFINITY;  // free-score range seen by this thread
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) {
+    const int i = tid + kSelThreads * u;
+    const bool forced = i < f_init || (i >= f_loc && i < n_elig);
+    st[u] = i >= n_elig ? 0 : (forced ? 1 : free_mark);
+    if (i < n_elig && !forced) {
+      lo = fminf(lo, sc[u]);
+      hi = fmaxf(hi, sc[u]);
+    }
+  }
+  topk_select(S, sc, st, n_elig, kf, n_free, lo, hi, topk, indices + unit * topk);
 }
 
 // --------------------------------------------------------------------------- host

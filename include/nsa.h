@@ -53,10 +53,10 @@
  *     stride 16 for the scoring paths (pooling accepts any kernel >= stride >= 1);
  *     block_size 64.  Others return NSA_ERR_UNSUPPORTED without launching.
  *   - Workspaces are caller-allocated device memory of at least the size the
- *     matching *_workspace_size query returns, ZERO-FILLED ONCE after
- *     allocation; each call leaves its completion counters at zero again, so a
- *     workspace can be reused by later calls on the same stream.  Calls that
- *     share one workspace must not run concurrently.
+ *     matching *_workspace_size query returns.  They need no initialisation:
+ *     every call writes each workspace byte it later reads.  A workspace can be
+ *     reused by later calls on the same stream; calls that share one workspace
+ *     must not run concurrently.
  *   - Errors: every entry point validates its arguments on the host before
  *     launching and returns a non-zero nsa_status on failure; nsa_last_error()
  *     then describes it (thread-local string, valid until the next call on
@@ -163,7 +163,7 @@ nsa_status nsa_cis_mean_pool_varlen(const float* cis, float* cis_pooled,
  *   For query head h (group g = h / (heads/kv_heads)): P_h = softmax over visible
  *   windows of scale * q_h . K_c[c]; P_g = sum of P_h over the group; block score
  *   = max of P_g over windows overlapping the block (0 if none).
- *   workspace: nsa_compressed_scores_workspace_size(...) bytes, zero-filled once.
+ *   workspace: nsa_compressed_scores_workspace_size(...) bytes.
  */
 size_t nsa_compressed_scores_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t heads,
                                             int32_t kv_heads, int32_t kernel, int32_t stride);
@@ -212,7 +212,7 @@ nsa_status nsa_select_topk(const float* block_scores, int32_t* indices,
  *            normaliser sum_j exp(s_j) (times cis_j in CIS mode); -inf when the
  *            row sees no key (its output row is then 0).
  *   cu_seqlens_q NULL: decode (rows = batch, t = L_b - 1); else prefill rows.
- *   workspace: nsa_selected_attn_workspace_size(...) bytes, zero-filled once.
+ *   workspace: nsa_selected_attn_workspace_size(...) bytes.
  */
 size_t nsa_selected_attn_workspace_size(int32_t rows_total, int32_t heads, int32_t kv_heads,
                                         int32_t head_dim, int32_t k_sel, int32_t decode);

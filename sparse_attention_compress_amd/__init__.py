@@ -6,10 +6,10 @@ on the GPU, passes their device pointers and sizes to the C ABI declared in
 computation happens in the HIP kernels of ``libnsa.so``; if the library is not
 built this module raises instead of falling back to anything else.
 
-Workspaces: functions that need one accept ``workspace=`` (a zero-filled uint8
-CUDA tensor of at least the queried size).  When it is omitted the binding keeps
-one zero-filled buffer per (device, size) and reuses it; the kernels leave their
-counters at zero after every call, so reuse on one stream is safe.
+Workspaces: functions that need one accept ``workspace=`` (a uint8 CUDA tensor
+of at least the queried size; no initialisation needed).  When it is omitted the
+binding keeps one buffer per (device, size) and reuses it, which is safe for
+calls on one stream.
 """
 from __future__ import annotations
 

@@ -102,8 +102,10 @@ int32_t nsa_version(void);
  * (hipExtLaunchKernelGGL); the request is consumed by that launch.  Kinds:
  * 0 pooling (nsa_compress_k, nsa_cis_mean_pool_varlen), 1 compressed-key
  * logits (with the decode window refresh), 2 block scores and top-k
- * selection, 3 selected attention, 4 merge of split partial states (decode).
- * The events are owned by the caller
+ * selection, 3 selected attention, 4 merge of split partial states (decode),
+ * 5 compressed-attention normaliser pass (prefill), 6 compressed-attention
+ * output and block-score pass (prefill), 7 sliding-window attention (prefill,
+ * with the gated sum in nsa_prefill_step).  The events are owned by the caller
  * and must have timing enabled; a launch made during stream capture must not
  * be armed.
  */
@@ -112,7 +114,10 @@ typedef enum nsa_kernel_kind {
   NSA_KERNEL_LOGITS = 1,
   NSA_KERNEL_BLOCK_SCORES = 2,
   NSA_KERNEL_SELECTED_ATTN = 3,
-  NSA_KERNEL_COMBINE = 4
+  NSA_KERNEL_COMBINE = 4,
+  NSA_KERNEL_COMPRESSED_LSE = 5,
+  NSA_KERNEL_COMPRESSED_ATTN = 6,
+  NSA_KERNEL_WINDOW_ATTN = 7
 } nsa_kernel_kind;
 nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
 
@@ -259,6 +264,89 @@ typedef struct nsa_decode_params {
 size_t nsa_decode_workspace_size(const nsa_decode_params* p);
 nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * nsa_compressed_attn_fwd -- compressed-branch attention of prefill rows, and
+ * the block scores the selection reuses.
+ * [DeepSeek NSA with Triton, section 1.1: the compressed branch attends to
+ *  mean-pooled keys and values; the selected branch ranks blocks by the
+ *  compressed-attention probabilities of the GQA group.]
+ *   q            [rows, heads, head_dim] bfloat16 (prefill rows: cu_seqlens_q)
+ *   k_c, v_c     [N_c, kv_heads, head_dim] bfloat16 (nsa_compress_k of K and V)
+ *   o_cmp        [rows, heads, head_dim] of out_dtype (written): for query head h
+ *                at position t, softmax over the windows visible to t of
+ *                scale * q_h . k_c[c], times v_c; 0 when no window is visible
+ *   lse          nullable [rows, heads] float32 (written): natural log of that
+ *                softmax's normaliser, -inf when no window is visible
+ *   block_scores nullable [rows, kv_heads, n_blocks_max] float32 (written): for
+ *                block i, the max over the windows overlapping it of the group
+ *                sum of the heads' probabilities; 0 past the row's windows and
+ *                past the sequence's blocks
+ *   workspace:   nsa_compressed_attn_workspace_size(rows_total, heads) bytes.
+ *   bfloat16 only (the tiles run on the bf16 matrix cores); cu_seqlens_q is
+ *   required.
+ */
+size_t nsa_compressed_attn_workspace_size(int32_t rows_total, int32_t heads);
+nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v_c,
+                                   nsa_dtype dtype, void* o_cmp, nsa_dtype out_dtype, float* lse,
+                                   float* block_scores, int32_t n_blocks_max,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   const int32_t* cu_seqlens_c, int32_t batch, int32_t rows_total,
+                                   int32_t max_seqlen_k, int32_t heads, int32_t kv_heads,
+                                   int32_t head_dim, int32_t kernel, int32_t stride,
+                                   int32_t block_size, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nsa_window_attn_fwd -- sliding-window attention of prefill rows.
+ * [DeepSeek NSA with Triton, section 1.1: the sliding-window branch attends to
+ *  the most recent tokens, 512 in the pages' example.]
+ *   Query position t attends to keys max(0, t - window + 1) .. t of its sequence
+ *   (window keys including itself).  q [rows, heads, head_dim], k, v
+ *   [N_k, kv_heads, head_dim], all bfloat16; out [rows, heads, head_dim] of
+ *   out_dtype (written); lse nullable [rows, heads] float32 (natural log).
+ */
+nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
+                               void* out, nsa_dtype out_dtype, float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                               int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t window,
+                               float softmax_scale, hipStream_t stream);
+
+/*
+ * nsa_prefill_step -- the three-branch NSA prefill of packed query rows.
+ * [DeepSeek NSA with Triton, section 1.1: o = g_cmp * o_cmp + g_sel * o_sel +
+ *  g_win * o_win, gates per token and head; selection from the compressed
+ *  probabilities of the group; TileLang NSA, section 2, for the selected blocks.]
+ * Steps: mean-pool K and V into k_c, v_c (written); compressed attention with
+ * block scores; top-`topk` blocks per (row, kv head) with n_init / n_local forced
+ * blocks (0 and 0 for the pages' configuration); attention over the selected
+ * blocks; sliding-window attention; the gated sum into out.  Branch outputs
+ * stay float32 in the workspace until the sum.  bfloat16 only.
+ */
+typedef struct nsa_prefill_params {
+  const void* q;               /* [rows, heads, head_dim] bf16 */
+  const void* k;               /* [N_k, kv_heads, head_dim] bf16 */
+  const void* v;               /* [N_k, kv_heads, head_dim] bf16 */
+  void* k_c;                   /* [N_c, kv_heads, head_dim] bf16 (written) */
+  void* v_c;                   /* [N_c, kv_heads, head_dim] bf16 (written) */
+  const float* gates;          /* [rows, heads, 3]: compressed, selected, window */
+  const int32_t* cu_seqlens_q; /* [batch+1] */
+  const int32_t* cu_seqlens_k; /* [batch+1] */
+  const int32_t* cu_seqlens_c; /* [batch+1] full-window counts */
+  void* out;                   /* [rows, heads, head_dim] bf16 (written) */
+  float* block_scores;         /* nullable [rows, kv_heads, n_blocks_max] debug output */
+  int32_t* indices;            /* nullable [rows, kv_heads, topk] debug output */
+  nsa_dtype dtype;             /* must be NSA_BF16 */
+  int32_t batch, rows_total, max_seqlen_k, heads, kv_heads, head_dim;
+  int32_t kernel, stride, block_size;
+  int32_t topk, n_init, n_local, window;
+  float softmax_scale;
+} nsa_prefill_params;
+
+size_t nsa_prefill_workspace_size(const nsa_prefill_params* p);
+nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

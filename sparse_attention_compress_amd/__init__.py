@@ -52,6 +52,19 @@ class DecodeParams(ctypes.Structure):
     ]
 
 
+class PrefillParams(ctypes.Structure):
+    """Mirror of ``nsa_prefill_params``."""
+    _fields_ = [
+        ("q", c_vp), ("k", c_vp), ("v", c_vp), ("k_c", c_vp), ("v_c", c_vp), ("gates", c_vp),
+        ("cu_seqlens_q", c_vp), ("cu_seqlens_k", c_vp), ("cu_seqlens_c", c_vp), ("out", c_vp),
+        ("block_scores", c_vp), ("indices", c_vp), ("dtype", ctypes.c_int),
+        ("batch", c_i32), ("rows_total", c_i32), ("max_seqlen_k", c_i32), ("heads", c_i32),
+        ("kv_heads", c_i32), ("head_dim", c_i32), ("kernel", c_i32), ("stride", c_i32),
+        ("block_size", c_i32), ("topk", c_i32), ("n_init", c_i32), ("n_local", c_i32),
+        ("window", c_i32), ("softmax_scale", c_f32),
+    ]
+
+
 _SIGS = {
     "nsa_last_error": (ctypes.c_char_p, []),
     "nsa_version": (c_i32, []),
@@ -72,6 +85,16 @@ _SIGS = {
                                              c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
     "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
+    "nsa_compressed_attn_workspace_size": (c_sz, [c_i32, c_i32]),
+    "nsa_compressed_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_int,
+                                               c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                               c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                               c_f32, c_vp, c_sz, c_vp]),
+    "nsa_window_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_int,
+                                           c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                           c_i32, c_i32, c_f32, c_vp]),
+    "nsa_prefill_workspace_size": (c_sz, [ctypes.POINTER(PrefillParams)]),
+    "nsa_prefill_step": (ctypes.c_int, [ctypes.POINTER(PrefillParams), c_vp, c_sz, c_vp]),
 }
 
 
@@ -260,6 +283,76 @@ def nsa_decode_step(params: DecodeParams, workspace=None, device=None, stream=No
 
 
 KERNEL_POOL, KERNEL_LOGITS, KERNEL_BLOCK_SCORES, KERNEL_SELECTED_ATTN, KERNEL_COMBINE = 0, 1, 2, 3, 4
+KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN = 5, 6, 7
+
+
+def compressed_attn_workspace_size(rows, heads):
+    return lib().nsa_compressed_attn_workspace_size(int(rows), int(heads))
+
+
+def nsa_compressed_attn_fwd(q, k_c, v_c, cu_seqlens_q, cu_seqlens_k, cu_seqlens_c, max_seqlen_k,
+                            o_cmp, lse=None, block_scores=None, softmax_scale=0.0, kernel=32,
+                            stride=16, block_size=64, workspace=None, stream=None):
+    """Compressed-branch attention of prefill rows: q [rows, H, D] bf16, k_c/v_c
+    [N_c, H_kv, D] bf16 -> o_cmp [rows, H, D] (bf16 or fp32); optional lse
+    [rows, H] and block_scores [rows, H_kv, n_blocks_max]."""
+    rows, H, D = q.shape
+    H_kv = k_c.shape[1]
+    batch = cu_seqlens_k.numel() - 1
+    nb_max = block_scores.shape[2] if block_scores is not None else 0
+    ws, nbytes = _workspace(compressed_attn_workspace_size(rows, H), q.device, workspace)
+    _check(lib().nsa_compressed_attn_fwd(_ptr(q), _ptr(k_c), _ptr(v_c), _dt(q), _ptr(o_cmp),
+                                         _dt(o_cmp), _ptr(lse), _ptr(block_scores), nb_max,
+                                         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(cu_seqlens_c),
+                                         batch, rows, int(max_seqlen_k), H, H_kv, D, kernel,
+                                         stride, block_size, float(softmax_scale), _ptr(ws),
+                                         nbytes, _stream(stream)))
+    return o_cmp
+
+
+def nsa_window_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_k, out, window=512,
+                        lse=None, softmax_scale=0.0, stream=None):
+    """Sliding-window attention of prefill rows over keys t-window+1 .. t."""
+    rows, H, D = q.shape
+    H_kv = k.shape[1]
+    batch = cu_seqlens_k.numel() - 1
+    _check(lib().nsa_window_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(out), _dt(out),
+                                     _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, rows,
+                                     int(max_seqlen_k), H, H_kv, D, int(window),
+                                     float(softmax_scale), _stream(stream)))
+    return out
+
+
+def prefill_params(q, k, v, k_c, v_c, gates, cu_seqlens_q, cu_seqlens_k, cu_seqlens_c,
+                   max_seqlen_k, out, topk=16, n_init=0, n_local=0, window=512,
+                   block_scores=None, indices=None, softmax_scale=0.0, kernel=32, stride=16,
+                   block_size=64) -> PrefillParams:
+    rows, H, D = q.shape
+    p = PrefillParams()
+    p.q, p.k, p.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    p.k_c, p.v_c, p.gates = k_c.data_ptr(), v_c.data_ptr(), gates.data_ptr()
+    p.cu_seqlens_q, p.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    p.cu_seqlens_c, p.out = cu_seqlens_c.data_ptr(), out.data_ptr()
+    p.block_scores = block_scores.data_ptr() if block_scores is not None else None
+    p.indices = indices.data_ptr() if indices is not None else None
+    p.dtype = _dt(q)
+    p.batch, p.rows_total, p.max_seqlen_k = cu_seqlens_k.numel() - 1, rows, int(max_seqlen_k)
+    p.heads, p.kv_heads, p.head_dim = H, k.shape[1], D
+    p.kernel, p.stride, p.block_size = kernel, stride, block_size
+    p.topk, p.n_init, p.n_local, p.window = int(topk), int(n_init), int(n_local), int(window)
+    p.softmax_scale = float(softmax_scale)
+    return p
+
+
+def prefill_workspace_size(params: PrefillParams) -> int:
+    return lib().nsa_prefill_workspace_size(ctypes.byref(params))
+
+
+def nsa_prefill_step(params: PrefillParams, workspace=None, device=None, stream=None):
+    """Enqueue the three-branch prefill described by ``params`` (see :func:`prefill_params`)."""
+    need = prefill_workspace_size(params)
+    ws, nbytes = _workspace(need, device or torch.device("cuda"), workspace)
+    _check(lib().nsa_prefill_step(ctypes.byref(params), _ptr(ws), nbytes, _stream(stream)))
 
 
 def nsa_profile_next_launch(kind: int, start: torch.cuda.Event, stop: torch.cuda.Event):

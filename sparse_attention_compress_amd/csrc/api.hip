@@ -340,4 +340,250 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
   return hip_status(e, fn);
 }
 
+// ----------------------------------------------------------------- prefill branches
+
+size_t nsa_compressed_attn_workspace_size(int32_t rows_total, int32_t heads) {
+  if (rows_total <= 0 || heads <= 0) return 0;
+  return (size_t(rows_total) * heads * sizeof(float) + 255) & ~size_t(255);
+}
+
+}  // extern "C"
+
+namespace {
+
+nsa_status check_prefill_common(const char* fn, nsa_dtype dtype, int batch, int rows_total,
+                                int max_seqlen_k, int heads, int kv_heads, int head_dim) {
+  NSA_REQUIRE(batch >= 0 && rows_total >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(dtype == NSA_BF16, NSA_ERR_UNSUPPORTED, "%s: bfloat16 inputs only", fn);
+  NSA_REQUIRE(group_ok(heads, kv_heads), NSA_ERR_UNSUPPORTED, "%s: heads %d / kv_heads %d unsupported", fn, heads, kv_heads);
+  NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
+  return NSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v_c,
+                                   nsa_dtype dtype, void* o_cmp, nsa_dtype out_dtype, float* lse,
+                                   float* block_scores, int32_t n_blocks_max,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   const int32_t* cu_seqlens_c, int32_t batch, int32_t rows_total,
+                                   int32_t max_seqlen_k, int32_t heads, int32_t kv_heads,
+                                   int32_t head_dim, int32_t kernel, int32_t stride,
+                                   int32_t block_size, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_compressed_attn_fwd";
+  nsa_status st = check_prefill_common(fn, dtype, batch, rows_total, max_seqlen_k, heads, kv_heads, head_dim);
+  if (st != NSA_OK) return st;
+  st = check_geometry(fn, head_dim, kernel, stride, block_size);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(dtype_ok(out_dtype), NSA_ERR_UNSUPPORTED, "%s: unknown output dtype", fn);
+  NSA_REQUIRE(cu_seqlens_q != nullptr, NSA_ERR_INVALID_ARG, "%s: cu_seqlens_q is required (prefill rows)", fn);
+  if (block_scores != nullptr)
+    NSA_REQUIRE(n_blocks_max >= (max_seqlen_k + block_size - 1) / block_size, NSA_ERR_INVALID_ARG,
+                "%s: n_blocks_max %d < ceil(max_seqlen_k / block_size)", fn, n_blocks_max);
+  if (rows_total == 0 || batch == 0) return ok();
+  NSA_REQUIRE(q && k_c && v_c && o_cmp && cu_seqlens_k && cu_seqlens_c, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k_c) && aligned16(v_c) && aligned16(o_cmp), NSA_ERR_INVALID_ARG,
+              "%s: q, k_c, v_c, o_cmp must be 16-byte aligned", fn);
+  const size_t need = nsa_compressed_attn_workspace_size(rows_total, heads);
+  NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  nsa::CompressedPrefillArgs a{};
+  a.q = static_cast<const nsa::bf16_t*>(q);
+  a.kc = static_cast<const nsa::bf16_t*>(k_c);
+  a.vc = static_cast<const nsa::bf16_t*>(v_c);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.cu_c = cu_seqlens_c;
+  a.batch = batch;
+  a.rows_total = rows_total;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
+  a.lse2 = static_cast<float*>(workspace);
+  a.o_cmp = o_cmp;
+  a.out_f32 = out_dtype == NSA_F32;
+  a.lse_nat = lse;
+  a.block_scores = block_scores;
+  a.nb_max = n_blocks_max;
+  return hip_status(nsa::launch_compressed_prefill(a, stream), fn);
+}
+
+nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
+                               void* out, nsa_dtype out_dtype, float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                               int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t window,
+                               float softmax_scale, hipStream_t stream) {
+  const char* fn = "nsa_window_attn_fwd";
+  nsa_status st = check_prefill_common(fn, dtype, batch, rows_total, max_seqlen_k, heads, kv_heads, head_dim);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(dtype_ok(out_dtype), NSA_ERR_UNSUPPORTED, "%s: unknown output dtype", fn);
+  NSA_REQUIRE(window >= 1, NSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
+  NSA_REQUIRE(cu_seqlens_q != nullptr, NSA_ERR_INVALID_ARG, "%s: cu_seqlens_q is required (prefill rows)", fn);
+  if (rows_total == 0 || batch == 0) return ok();
+  NSA_REQUIRE(q && k && v && out && cu_seqlens_k, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), NSA_ERR_INVALID_ARG,
+              "%s: q, k, v, out must be 16-byte aligned", fn);
+  nsa::WindowPrefillArgs a{};
+  a.q = static_cast<const nsa::bf16_t*>(q);
+  a.k = static_cast<const nsa::bf16_t*>(k);
+  a.v = static_cast<const nsa::bf16_t*>(v);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.rows_total = rows_total;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.window = window;
+  a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
+  a.out = out;
+  a.out_f32 = out_dtype == NSA_F32;
+  a.lse_nat = lse;
+  return hip_status(nsa::launch_window_prefill(a, stream), fn);
+}
+
+}  // extern "C"
+
+namespace {
+
+struct PrefillLayout {
+  size_t lse2, o_cmp, o_sel, scores, indices, total;
+  int nb_max, max_windows;
+};
+
+PrefillLayout prefill_layout(const nsa_prefill_params* p) {
+  PrefillLayout L{};
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t rows = size_t(p->rows_total), H = size_t(p->heads);
+  L.nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
+  L.max_windows = full_windows(p->max_seqlen_k, p->kernel, p->stride);
+  size_t off = 0;
+  L.lse2 = off;
+  off += up(rows * H * sizeof(float));
+  L.o_cmp = off;
+  off += up(rows * H * p->head_dim * sizeof(float));
+  L.o_sel = off;
+  off += up(rows * H * p->head_dim * sizeof(float));
+  L.scores = off;
+  if (p->block_scores == nullptr) off += up(rows * p->kv_heads * size_t(L.nb_max) * sizeof(float));
+  L.indices = off;
+  if (p->indices == nullptr) off += up(rows * p->kv_heads * size_t(p->topk) * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+nsa_status check_prefill(const nsa_prefill_params* p) {
+  const char* fn = "nsa_prefill_step";
+  NSA_REQUIRE(p != nullptr, NSA_ERR_INVALID_ARG, "%s: params is null", fn);
+  nsa_status st = check_prefill_common(fn, p->dtype, p->batch, p->rows_total, p->max_seqlen_k,
+                                       p->heads, p->kv_heads, p->head_dim);
+  if (st != NSA_OK) return st;
+  st = check_geometry(fn, p->head_dim, p->kernel, p->stride, p->block_size);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(p->topk >= 1 && p->topk <= kMaxPrefillSel, NSA_ERR_UNSUPPORTED, "%s: topk must be in [1, %d]", fn, kMaxPrefillSel);
+  NSA_REQUIRE(p->n_init >= 0 && p->n_local >= 0 && p->n_init + p->n_local <= p->topk, NSA_ERR_INVALID_ARG,
+              "%s: need 0 <= n_init, 0 <= n_local, n_init + n_local <= topk", fn);
+  NSA_REQUIRE(p->window >= 1, NSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
+  NSA_REQUIRE((p->max_seqlen_k + p->block_size - 1) / p->block_size <= nsa::kMaxSortBlocks, NSA_ERR_UNSUPPORTED,
+              "%s: more than %d blocks per sequence", fn, nsa::kMaxSortBlocks);
+  if (p->batch == 0 || p->rows_total == 0) return NSA_OK;
+  NSA_REQUIRE(p->q && p->k && p->v && p->k_c && p->v_c && p->gates && p->cu_seqlens_q && p->cu_seqlens_k &&
+              p->cu_seqlens_c && p->out, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(p->q) && aligned16(p->k) && aligned16(p->v) && aligned16(p->k_c) &&
+              aligned16(p->v_c) && aligned16(p->out), NSA_ERR_INVALID_ARG,
+              "%s: q, k, v, k_c, v_c, out must be 16-byte aligned", fn);
+  return NSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nsa_prefill_workspace_size(const nsa_prefill_params* p) {
+  if (check_prefill(p) != NSA_OK || p->batch == 0 || p->rows_total == 0) return 0;
+  return prefill_layout(p).total;
+}
+
+nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  const char* fn = "nsa_prefill_step";
+  nsa_status st = check_prefill(p);
+  if (st != NSA_OK) return st;
+  if (p->batch == 0 || p->rows_total == 0) return ok();
+  const PrefillLayout lay = prefill_layout(p);
+  NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= lay.total, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, lay.total);
+  char* base = static_cast<char*>(workspace);
+  float* o_cmp = reinterpret_cast<float*>(base + lay.o_cmp);
+  float* o_sel = reinterpret_cast<float*>(base + lay.o_sel);
+  float* bs = p->block_scores ? p->block_scores : reinterpret_cast<float*>(base + lay.scores);
+  int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.indices);
+  const float sl2 = scale_log2_of(p->softmax_scale, p->head_dim);
+  const int width = p->kv_heads * p->head_dim;
+  // 1. compressed keys and values
+  hipError_t e = hipSuccess;
+  if (lay.max_windows > 0) {
+    e = nsa::launch_mean_pool(p->k, 1, p->k_c, 1, p->cu_seqlens_k, p->cu_seqlens_c, p->batch,
+                              lay.max_windows, width, p->kernel, p->stride, 0, stream);
+    if (e == hipSuccess)
+      e = nsa::launch_mean_pool(p->v, 1, p->v_c, 1, p->cu_seqlens_k, p->cu_seqlens_c, p->batch,
+                                lay.max_windows, width, p->kernel, p->stride, 0, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  // 2. compressed branch and the block scores
+  nsa::CompressedPrefillArgs c{};
+  c.q = static_cast<const nsa::bf16_t*>(p->q);
+  c.kc = static_cast<const nsa::bf16_t*>(p->k_c);
+  c.vc = static_cast<const nsa::bf16_t*>(p->v_c);
+  c.cu_q = p->cu_seqlens_q;
+  c.cu_k = p->cu_seqlens_k;
+  c.cu_c = p->cu_seqlens_c;
+  c.batch = p->batch;
+  c.rows_total = p->rows_total;
+  c.heads = p->heads;
+  c.kv_heads = p->kv_heads;
+  c.scale_log2 = sl2;
+  c.lse2 = reinterpret_cast<float*>(base + lay.lse2);
+  c.o_cmp = o_cmp;
+  c.out_f32 = 1;
+  c.lse_nat = nullptr;
+  c.block_scores = bs;
+  c.nb_max = lay.nb_max;
+  e = nsa::launch_compressed_prefill(c, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  // 3. selection
+  e = nsa::launch_select_topk(bs, idx, p->cu_seqlens_q, p->cu_seqlens_k, p->batch, p->rows_total,
+                              p->kv_heads, lay.nb_max, p->topk, p->n_init, p->n_local, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  // 4. selected branch (float32 rows)
+  e = nsa::launch_selected_attn(p->q, p->k, p->v, 1, idx, p->topk, nullptr, p->out, nullptr,
+                                p->cu_seqlens_q, p->cu_seqlens_k, p->batch, p->rows_total,
+                                p->heads, p->kv_heads, sl2, nsa::AttnWs{nullptr, nullptr}, stream,
+                                o_sel);
+  if (e != hipSuccess) return hip_status(e, fn);
+  // 5. window branch and the gated sum
+  nsa::WindowPrefillArgs w{};
+  w.q = c.q;
+  w.k = static_cast<const nsa::bf16_t*>(p->k);
+  w.v = static_cast<const nsa::bf16_t*>(p->v);
+  w.cu_q = p->cu_seqlens_q;
+  w.cu_k = p->cu_seqlens_k;
+  w.batch = p->batch;
+  w.rows_total = p->rows_total;
+  w.heads = p->heads;
+  w.kv_heads = p->kv_heads;
+  w.window = p->window;
+  w.scale_log2 = sl2;
+  w.out = p->out;
+  w.out_f32 = 0;
+  w.lse_nat = nullptr;
+  w.gates = p->gates;
+  w.o_cmp = o_cmp;
+  w.o_sel = o_sel;
+  return hip_status(nsa::launch_window_prefill(w, stream), fn);
+}
+
 }  // extern "C"

@@ -510,6 +510,11 @@ __global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
       if constexpr (SPLIT) {
         *reinterpret_cast<float4*>(part_acc + (ps * G + c16) * D + 16 * n + 4 * r4) =
             make_float4(o[0], o[1], o[2], o[3]);
+      } else if (part_acc != nullptr) {
+        // unsplit rows may ask for float32 output rows (passed in part_acc)
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        *reinterpret_cast<float4*>(part_acc + (unit * G + c16) * D + 16 * n + 4 * r4) =
+            make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
       } else {
         bf16_t* dst = out + (unit * G + c16) * D + 16 * n + 4 * r4;
 #pragma unroll
@@ -618,7 +623,8 @@ template <int G, typename T, bool CIS>
 static hipError_t launch_attn_g(const void* q, const void* k, const void* v, const int* indices,
                                 int k_sel, const float* cis, void* out, float* lse,
                                 const int* cu_q, const int* cu_k, int batch, int rows_total,
-                                int kv_heads, float scale_log2, const AttnWs& ws, hipStream_t s) {
+                                int kv_heads, float scale_log2, const AttnWs& ws, hipStream_t s,
+                                float* out_f32) {
   if (rows_total == 0 || k_sel == 0) return hipSuccess;
   if (cu_q == nullptr) {
     const int bpw = attn_split_blocks(rows_total, kv_heads, k_sel);
@@ -638,20 +644,21 @@ static hipError_t launch_attn_g(const void* q, const void* k, const void* v, con
                        dim3(rows_total, kv_heads, 1), dim3(256), s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), indices, k_sel, cis,
                        static_cast<T*>(out), lse, cu_q, cu_k, batch, kv_heads, scale_log2, k_sel,
-                       static_cast<float2*>(nullptr), static_cast<float*>(nullptr));
+                       static_cast<float2*>(nullptr), out_f32);
 }
 
 template <typename T, bool CIS>
 static hipError_t launch_attn_t(int G, const void* q, const void* k, const void* v,
                                 const int* idx, int k_sel, const float* cis, void* out, float* lse,
                                 const int* cu_q, const int* cu_k, int batch, int rows,
-                                int kvh, float sl2, const AttnWs& ws, hipStream_t s) {
+                                int kvh, float sl2, const AttnWs& ws, hipStream_t s,
+                                float* out_f32) {
   switch (G) {
-    case 1: return launch_attn_g<1, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
-    case 2: return launch_attn_g<2, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
-    case 4: return launch_attn_g<4, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
-    case 8: return launch_attn_g<8, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
-    case 16: return launch_attn_g<16, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s);
+    case 1: return launch_attn_g<1, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s, out_f32);
+    case 2: return launch_attn_g<2, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s, out_f32);
+    case 4: return launch_attn_g<4, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s, out_f32);
+    case 8: return launch_attn_g<8, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s, out_f32);
+    case 16: return launch_attn_g<16, T, CIS>(q, k, v, idx, k_sel, cis, out, lse, cu_q, cu_k, batch, rows, kvh, sl2, ws, s, out_f32);
     default: return hipErrorInvalidValue;
   }
 }
@@ -660,14 +667,15 @@ hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int
                                 const int* indices, int k_sel, const float* cis, void* out,
                                 float* lse, const int* cu_q, const int* cu_k, int batch,
                                 int rows_total, int heads, int kv_heads, float scale_log2,
-                                const AttnWs& ws, hipStream_t s) {
+                                const AttnWs& ws, hipStream_t s, float* out_f32) {
   const int G = heads / kv_heads;
+  if (!bf16) out_f32 = nullptr;  // float32 inputs write float32 rows to out already
   if (bf16) {
-    if (cis) return launch_attn_t<bf16_t, true>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
-    return launch_attn_t<bf16_t, false>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
+    if (cis) return launch_attn_t<bf16_t, true>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s, out_f32);
+    return launch_attn_t<bf16_t, false>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s, out_f32);
   }
-  if (cis) return launch_attn_t<float, true>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
-  return launch_attn_t<float, false>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s);
+  if (cis) return launch_attn_t<float, true>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s, out_f32);
+  return launch_attn_t<float, false>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s, out_f32);
 }
 
 }  // namespace nsa

@@ -121,6 +121,9 @@ struct OpSum {
 struct OpSumI {
   __device__ __forceinline__ int operator()(int a, int b) const { return a + b; }
 };
+struct OpMinI {
+  __device__ __forceinline__ int operator()(int a, int b) const { return min(a, b); }
+};
 
 // Reduction over the 4 lanes of a quad (result in all 4).
 template <typename Op>
@@ -143,6 +146,16 @@ __device__ __forceinline__ float wave_reduce(float x, Op op) {
   return cross32(x, op);
 }
 __device__ __forceinline__ float wave_max(float x) { return wave_reduce(x, OpMax()); }
+// Integer minimum over the whole wave (result in all 64 lanes).
+__device__ __forceinline__ int wave_min_i(int x) {
+  const OpMinI op;
+  x = op(x, dpp<kDppQuadXor1>(x));
+  x = op(x, dpp<kDppQuadXor2>(x));
+  x = op(x, dpp<kDppRowHalfMirror>(x));
+  x = op(x, dpp<kDppRowMirror>(x));
+  x = cross16i(x, op);
+  return cross32i(x, op);
+}
 __device__ __forceinline__ float wave_sum(float x) { return wave_reduce(x, OpSum()); }
 
 // Reduction over the lanes that share lane % G (G a power of two <= 64): the

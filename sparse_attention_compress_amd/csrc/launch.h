@@ -9,6 +9,8 @@
 
 namespace nsa {
 
+struct bf16_t;
+
 // Window geometry the scoring kernels are compiled for.
 constexpr int kKernel = 32;
 constexpr int kStride = 16;
@@ -31,7 +33,10 @@ enum KernelKind {
   kKindBlockScores = 2,
   kKindAttn = 3,
   kKindCombine = 4,
-  kKindCount = 5
+  kKindCmpLse = 5,
+  kKindCmpProbs = 6,
+  kKindWindow = 7,
+  kKindCount = 8
 };
 
 // One armed (start, stop) event pair per kernel kind, per host thread.
@@ -105,10 +110,47 @@ int attn_split_blocks(int batch, int kv_heads, int k_sel);  // selected blocks p
 size_t attn_ws_bytes(int rows_total, int kv_heads, int group, int k_sel, int decode);
 AttnWs attn_ws_carve(void* base, int rows_total, int kv_heads, int group, int k_sel, int decode);
 
+// out_f32: prefill rows only (bf16 inputs): write float32 rows there instead of out.
 hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int bf16,
                                 const int* indices, int k_sel, const float* cis, void* out,
                                 float* lse, const int* cu_q, const int* cu_k, int batch,
                                 int rows_total, int heads, int kv_heads, float scale_log2,
-                                const AttnWs& ws, hipStream_t s);
+                                const AttnWs& ws, hipStream_t s, float* out_f32 = nullptr);
+
+// Prefill branches (bf16, prefill rows).
+struct CompressedPrefillArgs {
+  const bf16_t* q;
+  const bf16_t* kc;
+  const bf16_t* vc;
+  const int* cu_q;
+  const int* cu_k;
+  const int* cu_c;
+  int batch, rows_total, heads, kv_heads;
+  float scale_log2;
+  float* lse2;           // [rows, heads] workspace: log2-domain normaliser
+  void* o_cmp;           // [rows, heads, 128]
+  int out_f32;           // o_cmp dtype: 1 float32, 0 bfloat16
+  float* lse_nat;        // nullable [rows, heads]
+  float* block_scores;   // nullable [rows, kv_heads, nb_max]
+  int nb_max;
+};
+hipError_t launch_compressed_prefill(const CompressedPrefillArgs& a, hipStream_t s);
+
+struct WindowPrefillArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const int* cu_q;
+  const int* cu_k;
+  int batch, rows_total, heads, kv_heads, window;
+  float scale_log2;
+  void* out;
+  int out_f32;
+  float* lse_nat;        // nullable
+  const float* gates;    // nullable [rows, heads, 3]: gated sum with o_cmp and o_sel
+  const float* o_cmp;    // [rows, heads, 128] float32 (with gates)
+  const float* o_sel;    // [rows, heads, 128] float32 (with gates)
+};
+hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s);
 
 }  // namespace nsa

@@ -629,6 +629,81 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   topk_select(S, sc, st, n_elig, kf, n_free, lo, hi, topk, indices + unit * topk);
 }
 
+// ------------------------------------------------- kernel 3: select, one wave per row
+
+// Top-k of given block scores with one wave per (row, kv head), for many short
+// rows (prefill): lane l holds ids l + 64j (j < PER) in registers; the free
+// places are filled one per round with the best remaining score (ties to the
+// lower id) by a wave max and a wave min of the candidate ids.  Same rules and
+// output as select_kernel.
+template <int PER>
+__global__ __launch_bounds__(256) void select_wave_kernel(
+    const float* __restrict__ block_scores, int* __restrict__ indices, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int batch, int units, int kv_heads, int nb_max, int topk,
+    int n_init, int n_local) {
+  static_assert(PER <= 64, "one id bit per slot");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + wave;
+  if (unit >= units) return;  // whole wave; the kernel has no barriers
+  int b, t;
+  row_position(unit / kv_heads, cu_q, cu_k, batch, b, t);
+  const int len = cu_k[b + 1] - cu_k[b];
+  const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
+  const int n_elig = t >= 0 ? min(nb, t / kBlock + 1) : 0;
+  const int f_init = min(n_init, n_elig);
+  const int f_loc = max(max(0, n_elig - n_local), f_init);
+  const int n_forced = f_init + (n_elig - f_loc);
+  const int n_free = n_elig - n_forced;
+  const int kf = max(0, min(topk - n_forced, n_free));
+  const float* srow = block_scores + size_t(unit) * nb_max;
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = nb > 0 ? srow[min(lane + kWave * j, nb - 1)] : 0.f;
+  unsigned long long chosen = 0ull, cand = 0ull;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = lane + kWave * j;
+    const bool forced = i < f_init || (i >= f_loc && i < n_elig);
+    if (i < n_elig) {
+      if (forced) chosen |= 1ull << j; else cand |= 1ull << j;
+    }
+  }
+  if (kf == n_free) {
+    chosen |= cand;
+  } else {
+    for (int r = 0; r < kf; ++r) {
+      float bv = -INFINITY;
+      int bj = -1;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (((cand >> j) & 1ull) && (bj < 0 || v[j] > bv)) {
+          bv = v[j];
+          bj = j;
+        }
+      const float M = wave_max(bj >= 0 ? bv : -INFINITY);
+      const int win = wave_min_i((bj >= 0 && bv == M) ? lane + kWave * bj : 0x7fffffff);
+      if (lane == (win & (kWave - 1))) {
+        const int j = win / kWave;
+        chosen |= 1ull << j;
+        cand &= ~(1ull << j);
+      }
+    }
+  }
+  // ascending ids: slot j then lane
+  int* out = indices + size_t(unit) * topk;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool f = (chosen >> j) & 1ull;
+    const unsigned long long m = __ballot(f);
+    const int pos = base + __popcll(m & below);
+    if (f && pos < topk) out[pos] = lane + kWave * j;
+    base += __popcll(m);
+  }
+  for (int i = base + lane; i < topk; i += kWave) out[i] = -1;
+}
+
 // --------------------------------------------------------------------------- host
 
 static int n_windows_max(int max_seqlen_k) {
@@ -713,10 +788,31 @@ hipError_t launch_decode_scores(const DecodeScoresArgs& a, hipStream_t s) {
   return launch_scores_t<float, float>(G, a, s);
 }
 
+template <int PER>
+static hipError_t launch_select_wave(const float* block_scores, int* indices, const int* cu_q,
+                                     const int* cu_k, int batch, int units, int kv_heads,
+                                     int nb_max, int topk, int n_init, int n_local, hipStream_t s) {
+  return launch_kernel(kKindBlockScores, select_wave_kernel<PER>, dim3((units + 3) / 4),
+                       dim3(256), s, block_scores, indices, cu_q, cu_k, batch, units, kv_heads,
+                       nb_max, topk, n_init, n_local);
+}
+
 hipError_t launch_select_topk(const float* block_scores, int* indices, const int* cu_q,
                               const int* cu_k, int batch, int rows_total, int kv_heads,
                               int nb_max, int topk, int n_init, int n_local, hipStream_t s) {
   if (rows_total == 0) return hipSuccess;
+  if (cu_q != nullptr) {
+    // prefill rows: many short rows, one wave each
+    const int units = rows_total * kv_heads;
+    const int per = (nb_max + kWave - 1) / kWave;
+    if (per <= 1) return launch_select_wave<1>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
+    if (per <= 2) return launch_select_wave<2>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
+    if (per <= 4) return launch_select_wave<4>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
+    if (per <= 8) return launch_select_wave<8>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
+    if (per <= 16) return launch_select_wave<16>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
+    if (per <= 32) return launch_select_wave<32>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
+    return launch_select_wave<64>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
+  }
   return launch_kernel(kKindBlockScores, select_kernel<1, false>, dim3(rows_total, kv_heads),
                        dim3(kSelThreads), s, static_cast<const float*>(nullptr),
                        static_cast<const float2*>(nullptr), static_cast<const float*>(nullptr),

@@ -117,3 +117,59 @@ def test_decode_step_checks():
     p.n_local = 16     # forced blocks exceed topk
     assert nsa.lib().nsa_decode_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 1
     assert torch is not None
+
+
+def test_prefill_branch_checks():
+    L = nsa.lib()
+    need = L.nsa_compressed_attn_workspace_size(100, 64)
+    assert need >= 100 * 64 * 4
+    args = [FAKE, FAKE, FAKE, nsa.NSA_BF16, FAKE, nsa.NSA_F32, None, None, 0, FAKE, FAKE, FAKE,
+            1, 100, 100, 64, 4, 128, 32, 16, 64, 0.0, FAKE, need, None]
+    bad = list(args)
+    bad[3] = nsa.NSA_F32          # fp32 inputs: the tiles are bf16
+    assert L.nsa_compressed_attn_fwd(*bad) == 2
+    bad = list(args)
+    bad[9] = None                 # prefill rows need cu_seqlens_q
+    assert L.nsa_compressed_attn_fwd(*bad) == 1
+    bad = list(args)
+    bad[7], bad[8] = FAKE, 1      # n_blocks_max below ceil(max_seqlen_k / 64)
+    assert L.nsa_compressed_attn_fwd(*bad) == 1
+    bad = list(args)
+    bad[23] = need - 1            # workspace too small
+    assert L.nsa_compressed_attn_fwd(*bad) == 3
+    bad = list(args)
+    bad[15] = 3                   # 64 heads / 3 kv heads
+    assert L.nsa_compressed_attn_fwd(*bad) == 2
+    wargs = [FAKE, FAKE, FAKE, nsa.NSA_BF16, FAKE, nsa.NSA_BF16, None, FAKE, FAKE, 1, 100, 100, 64,
+             4, 128, 512, 0.0, None]
+    bad = list(wargs)
+    bad[15] = 0                   # empty window
+    assert L.nsa_window_attn_fwd(*bad) == 1
+    bad = list(wargs)
+    bad[7] = None
+    assert L.nsa_window_attn_fwd(*bad) == 1
+    bad = list(wargs)
+    bad[0] = ctypes.c_void_p(0x1008)
+    assert L.nsa_window_attn_fwd(*bad) == 1 and "aligned" in nsa.last_error()
+
+
+def test_prefill_step_checks():
+    p = nsa.PrefillParams()
+    p.batch, p.rows_total, p.max_seqlen_k, p.heads, p.kv_heads, p.head_dim = 1, 1000, 1000, 64, 4, 128
+    p.kernel, p.stride, p.block_size = 32, 16, 64
+    p.topk, p.n_init, p.n_local, p.window = 16, 0, 0, 512
+    p.dtype = nsa.NSA_BF16
+    assert nsa.prefill_workspace_size(p) == 0           # null pointers
+    assert nsa.lib().nsa_prefill_step(ctypes.byref(p), None, 0, None) == 1
+    for f in ("q", "k", "v", "k_c", "v_c", "gates", "cu_seqlens_q", "cu_seqlens_k",
+              "cu_seqlens_c", "out"):
+        setattr(p, f, 0x1000)
+    need = nsa.prefill_workspace_size(p)
+    # lse + o_cmp + o_sel + block scores + indices
+    assert need >= 1000 * 64 * 4 + 2 * 1000 * 64 * 128 * 4 + 1000 * 4 * 16 * 4 + 1000 * 4 * 16 * 4
+    assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need - 1, None) == 3
+    p.topk = 65                                          # above the per-row staging limit
+    assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 2
+    p.topk = 16
+    p.dtype = nsa.NSA_F32
+    assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 2

@@ -1,0 +1,188 @@
+"""GPU parity of the three-branch NSA prefill (compressed, selected and
+sliding-window branches with gates) against the float64 CPU oracle.  Inputs
+follow the three-branch prefill recipe (64 query heads over 4 KV heads, window
+512, top-16 blocks, gates sigmoid(N(0,1))) at lengths the oracle finishes in
+seconds, plus sampled rows of the full 65536-token case.  Calls go through the
+C ABI."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_compress_amd as nsa
+from gen import workloads as W
+from parity import assert_close, check_index_sets, cu, log, np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def _inputs(w, q_scale=1.0):
+    q = W.prefill_query(w, DEV)
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(BF16)
+    k, v = W.keys_values(w, DEV)
+    g = W.gates(w, DEV)
+    lengths = list(w.lengths)
+    nc = [oracle.n_windows(L, 32, 16) for L in lengths]
+    cu_k = cu(lengths)
+    cu_c = cu(nc)
+    kc = torch.empty((max(1, sum(nc)), w.kv_heads, 128), dtype=BF16, device=DEV)
+    vc = torch.empty_like(kc)
+    nsa.nsa_compress_k(k, kc, cu_k, cu_c, max(nc))
+    nsa.nsa_compress_k(v, vc, cu_k, cu_c, max(nc))
+    return dict(q=q, k=k, v=v, g=g, kc=kc, vc=vc, cu_k=cu_k, cu_c=cu_c, nc=nc, lengths=lengths)
+
+
+def _rows_of(L, n_extra, _unused):
+    """Rows that cover the branch boundaries plus an even spread."""
+    fixed = [0, 1, 30, 31, 32, 47, 48, 63, 64, 65, 127, 128, 511, 512, 513, 1023, 1024, 1025,
+             L - 1, L - 2, L - 64, L - 65]
+    rows = {r for r in fixed if 0 <= r < L}
+    rows |= set(int(x) for x in np.linspace(0, L - 1, n_extra).round())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("group", [16, 8])
+def test_compressed_branch_and_block_scores(group):
+    H = 32
+    w = W.scaled(W.nsa_prefill(), [700, 1500])
+    w = dataclasses.replace(w, heads=H, kv_heads=H // group)
+    d = _inputs(w)
+    rows, Hkv = w.total_tokens, w.kv_heads
+    nb_max = -(-max(w.lengths) // 64)
+    o = torch.full((rows, H, 128), float("nan"), device=DEV)
+    lse = torch.full((rows, H), float("nan"), device=DEV)
+    bs = torch.full((rows, Hkv, nb_max), float("nan"), device=DEV)
+    log(f"compressed branch G={group} lengths={w.lengths}")
+    nsa.nsa_compressed_attn_fwd(d["q"], d["kc"], d["vc"], d["cu_k"], d["cu_k"], d["cu_c"],
+                                max(w.lengths), o, lse=lse, block_scores=bs)
+    torch.cuda.synchronize()
+    q, k, v = np64(d["q"]), np64(d["k"]), np64(d["v"])
+    o, lse, bs = np64(o), np64(lse), np64(bs)
+    scale = 1 / math.sqrt(128)
+    s0 = 0
+    for L, nc in zip(w.lengths, d["nc"]):
+        kc = oracle.mean_pool_varlen(k[s0:s0 + L], [0, L], [0, nc], 32, 16)
+        vc = oracle.mean_pool_varlen(v[s0:s0 + L], [0, L], [0, nc], 32, 16)
+        nb = -(-L // 64)
+        rows_t = _rows_of(L, 80, None)
+        ref_o = np.zeros((len(rows_t), H, 128))
+        ref_bs = np.zeros((len(rows_t), Hkv, nb_max))
+        ref_lse = np.full((len(rows_t), H), -np.inf)
+        for i, t in enumerate(rows_t):
+            ref_o[i] = oracle.compressed_attention_row(q[s0 + t], kc, vc, t, 32, 16, scale)
+            pg = oracle.group_window_probs(q[s0 + t], kc, t, 32, 16, scale)
+            ref_bs[i, :, :nb] = oracle.block_max(pg, nb, 32, 16, 64)
+            vis = [c for c in range(nc) if oracle.window_visible(c, t, 32, 16)]
+            if vis:
+                for h in range(H):
+                    s = kc[vis, h // group] @ q[s0 + t, h] * scale
+                    ref_lse[i, h] = s.max() + math.log(np.exp(s - s.max()).sum())
+        got = [s0 + t for t in rows_t]
+        assert_close(f"o_cmp[L={L}]", o[got], ref_o, atol=2e-2)
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(lse[got]), fin), "lse -inf pattern"
+        assert_close(f"lse[L={L}]", lse[got][fin], ref_lse[fin], atol=1e-2)
+        assert_close(f"block_scores[L={L}]", bs[got], ref_bs, atol=1e-5, rtol=1e-2)
+        s0 += L
+
+
+@pytest.mark.parametrize("window", [512, 64])
+def test_window_branch(window):
+    w = W.scaled(W.nsa_prefill(), [100, 700, 1300])
+    w = dataclasses.replace(w, heads=32, kv_heads=2)
+    d = _inputs(w)
+    rows, H = w.total_tokens, w.heads
+    o = torch.full((rows, H, 128), float("nan"), dtype=BF16, device=DEV)
+    lse = torch.full((rows, H), float("nan"), device=DEV)
+    log(f"window branch W={window} lengths={w.lengths}")
+    nsa.nsa_window_attn_fwd(d["q"], d["k"], d["v"], d["cu_k"], d["cu_k"], max(w.lengths), o,
+                            window=window, lse=lse)
+    torch.cuda.synchronize()
+    q, k, v = np64(d["q"]), np64(d["k"]), np64(d["v"])
+    o, lse = np64(o), np64(lse)
+    scale = 1 / math.sqrt(128)
+    s0 = 0
+    for L in w.lengths:
+        rows_t = _rows_of(L, 48, None)
+        ref = np.stack([oracle.window_attention_row(q[s0 + t], k[s0:s0 + L], v[s0:s0 + L], t,
+                                                    window, scale) for t in rows_t])
+        assert_close(f"o_win[L={L}]", o[[s0 + t for t in rows_t]], ref, atol=2e-2)
+        for t in rows_t[:8]:
+            J = list(range(max(0, t - window + 1), t + 1))
+            for h in (0, H - 1):
+                s = k[s0 + np.array(J), h // 16] @ q[s0 + t, h] * scale
+                assert abs(lse[s0 + t, h] - (s.max() + math.log(np.exp(s - s.max()).sum()))) < 1e-2
+        s0 += L
+
+
+def _check_step(w, d, rows_sample, out, idx, bs, min_identical):
+    """Oracle rows vs the GPU step: index sets by the tie-band rule, outputs on
+    rows whose index sets all agree."""
+    q, k, v, g = np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"])
+    out, idx = np64(out), idx.cpu().numpy()
+    L = w.lengths[0]
+    ref = oracle.nsa_prefill_rows(q, k, v, g, rows_sample, topk=w.topk, window=w.window)
+    nb = -(-L // 64)
+    identical_rows, band = 0, 0
+    same_rows = []
+    for i, t in enumerate(rows_sample):
+        all_same = True
+        for kv in range(w.kv_heads):
+            same, pop = check_index_sets(f"row {t} kv {kv}", idx[t, kv], ref["indices"][i, kv],
+                                         ref["block_scores"][i, kv], t, nb, w.topk, 0, 0)
+            band = max(band, pop)
+            all_same &= same
+        if all_same:
+            identical_rows += 1
+            same_rows.append(i)
+    log(f"index sets identical on {identical_rows}/{len(rows_sample)} rows (max tie-band population {band})")
+    assert identical_rows >= min_identical * len(rows_sample)
+    sel = np.array(same_rows)
+    got = out[[rows_sample[i] for i in sel]]
+    assert_close("prefill out", got, ref["out"][sel], atol=2e-2)
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_prefill_step_small(q_scale):
+    # the three-branch recipe (64 heads over 4 KV heads, window 512, top-16) at 2048 tokens;
+    # q_scale 4 sharpens the compressed softmax so the selection has few near-ties
+    w = W.scaled(W.nsa_prefill(), [2048])
+    d = _inputs(w, q_scale)
+    L = w.lengths[0]
+    nb_max = -(-L // 64)
+    out = torch.full((L, w.heads, 128), float("nan"), dtype=BF16, device=DEV)
+    idx = torch.full((L, w.kv_heads, w.topk), -7, dtype=torch.int32, device=DEV)
+    bs = torch.full((L, w.kv_heads, nb_max), float("nan"), device=DEV)
+    p = nsa.prefill_params(d["q"], d["k"], d["v"], d["kc"], d["vc"], d["g"], d["cu_k"], d["cu_k"],
+                           d["cu_c"], L, out, topk=w.topk, window=w.window, block_scores=bs,
+                           indices=idx)
+    log(f"prefill step L={L} q_scale={q_scale}")
+    nsa.nsa_prefill_step(p)
+    torch.cuda.synchronize()
+    rows_sample = _rows_of(L, 40, None)
+    _check_step(w, d, rows_sample, out, idx, bs, 0.3)
+
+
+def test_prefill_step_full_size_sampled_rows():
+    """The full three-branch case: one sequence of 65536 tokens, 64 query heads,
+    4 KV heads; 24 sampled rows checked against the oracle."""
+    w = W.nsa_prefill()
+    d = _inputs(w)
+    L = w.lengths[0]
+    out = torch.empty((L, w.heads, 128), dtype=BF16, device=DEV)
+    idx = torch.empty((L, w.kv_heads, w.topk), dtype=torch.int32, device=DEV)
+    p = nsa.prefill_params(d["q"], d["k"], d["v"], d["kc"], d["vc"], d["g"], d["cu_k"], d["cu_k"],
+                           d["cu_c"], L, out, topk=w.topk, window=w.window, indices=idx)
+    log(f"prefill step full size L={L} H={w.heads} H_kv={w.kv_heads}")
+    nsa.nsa_prefill_step(p)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rows_sample = [0, 31, 32, 511, 512, 1023, 1024, 4095, 4096, 20000, 32767, 32768, 50001,
+                   65472, 65534, 65535] + [int(x) for x in np.linspace(100, 65000, 8)]
+    _check_step(w, d, sorted(set(rows_sample)), out, idx, None, 0.3)

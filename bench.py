@@ -45,6 +45,11 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of from a HIP graph "
                          "(for counter-collection runs, which serialise dispatches)")
+    ap.add_argument("--workload", choices=["decode", "prefill-selected", "prefill-nsa"],
+                    default="decode",
+                    help="decode: the headline NOSA-1B-shaped decode (default); prefill-selected: "
+                         "selected-block attention prefill with given indices (batch 8 x 16384); "
+                         "prefill-nsa: the three-branch prefill (65536 tokens, 64 heads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with three streaming kernels (fp32 negation) that read and "
                          "write 256 MiB each, the reference dispatch that scales the HBM "
@@ -111,6 +116,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.workload != "decode":
+        prefill_main(args, dev)
+        return
     w = W.nosa1b_decode(pinned_32k=args.pinned_32k)
     B, H, Hkv, D = w.batch, w.heads, w.kv_heads, w.head_dim
     lengths = list(w.lengths)
@@ -285,6 +293,164 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_layer0"] = cpu_baseline(w, layers[0], lengths, args)
+    print(json.dumps(result), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _timed(fn, steps, warmup, stream):
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, ev0.elapsed_time(ev1)
+
+
+def _kernel_us(nsa, fn, kinds, reps, stream):
+    """Mean duration of each armed kernel kind over `reps` eager calls of fn."""
+    import numpy as np
+    import torch
+    evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)] for n in kinds}
+    with torch.cuda.stream(stream):
+        for n in kinds:
+            for a, b in evs[n]:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            for n, kind in kinds.items():
+                a, b = evs[n][i]
+                nsa.nsa_profile_next_launch(kind, a, b)
+            fn()
+    torch.cuda.synchronize()
+    return {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) * 1e3 for n in kinds}
+
+
+def prefill_main(args, dev):
+    """Prefill workloads: one step = the whole batch's prefill; value = prefill
+    tokens/s; roofline = the dominant kernel's algorithmic bf16 MFMA flops."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_compress_amd as nsa
+    from gen import workloads as W
+
+    stream = torch.cuda.Stream(device=dev)
+    steps = args.steps if args.steps != 2800 else (20 if args.workload == "prefill-selected" else 5)
+    warmup = args.warmup if args.warmup != 280 else 2
+    D = 128
+    if args.workload == "prefill-selected":
+        w = W.selected_prefill()
+        print(f"[bench] workload {w.name}", file=sys.stderr, flush=True)
+        q = W.prefill_query(w, dev)
+        k, v = W.keys_values(w, dev)
+        idx = W.given_block_indices(w, dev)
+        cu = nsa.cu_seqlens_of(w.lengths, dev)
+        out = torch.empty_like(q)
+        torch.cuda.synchronize()
+
+        def fn():
+            nsa.nsa_selected_attn_fwd(q, k, v, idx, cu, max(w.lengths), out, cu_seqlens_q=cu)
+        kinds = {"selected_attn": nsa.KERNEL_SELECTED_ATTN}
+        # algorithmic work: every (row, head) attends to the tokens j <= t of its blocks
+        ids = idx.cpu().numpy().astype(np.int64).reshape(-1, w.topk)
+        pos = np.concatenate([np.arange(L) for L in w.lengths])
+        t = np.repeat(pos, w.kv_heads).reshape(-1, 1)
+        keys = np.where(ids >= 0, np.clip(t - 64 * ids + 1, 0, 64), 0).sum()
+        G = w.heads // w.kv_heads
+        flops = {"selected_attn": 4.0 * D * G * float(keys)}
+        gathered = float(keys) * D * 2 * 2  # K and V rows of every (row, kv head)
+        dominant = "selected_attn"
+    else:
+        w = W.nsa_prefill()
+        print(f"[bench] workload {w.name}", file=sys.stderr, flush=True)
+        q = W.prefill_query(w, dev)
+        k, v = W.keys_values(w, dev)
+        g = W.gates(w, dev)
+        L = w.lengths[0]
+        nc = nsa.full_windows(L)
+        cu = nsa.cu_seqlens_of(w.lengths, dev)
+        cuc = nsa.cu_seqlens_of([nc], dev)
+        kc = torch.empty((nc, w.kv_heads, D), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        out = torch.empty_like(q)
+        idx = torch.empty((L, w.kv_heads, w.topk), dtype=torch.int32, device=dev)
+        p = nsa.prefill_params(q, k, v, kc, vc, g, cu, cu, cuc, L, out, topk=w.topk,
+                               window=w.window, indices=idx)
+        ws = torch.empty(nsa.prefill_workspace_size(p), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+        def fn():
+            nsa.nsa_prefill_step(p, workspace=ws)
+        kinds = {"pool": nsa.KERNEL_POOL, "compressed_lse": nsa.KERNEL_COMPRESSED_LSE,
+                 "compressed_attn": nsa.KERNEL_COMPRESSED_ATTN,
+                 "select": nsa.KERNEL_BLOCK_SCORES, "selected_attn": nsa.KERNEL_SELECTED_ATTN,
+                 "window_attn": nsa.KERNEL_WINDOW_ATTN}
+        fn()
+        torch.cuda.synchronize()
+        t = np.arange(L, dtype=np.int64)
+        nvis = np.where(t >= 31, np.minimum(nc, (t - 31) // 16 + 1), 0)
+        win = np.minimum(t + 1, w.window)
+        ids = idx.cpu().numpy().astype(np.int64)
+        sel = np.where(ids >= 0, np.clip(t[:, None, None] - 64 * ids + 1, 0, 64), 0).sum()
+        H = w.heads
+        G = H // w.kv_heads
+        flops = {"compressed_lse": 2.0 * D * H * float(nvis.sum()),
+                 "compressed_attn": 4.0 * D * H * float(nvis.sum()),
+                 "selected_attn": 4.0 * D * G * float(sel),
+                 "window_attn": 4.0 * D * H * float(win.sum())}
+        gathered = float(sel) * D * 2 * 2
+        dominant = "compressed_attn"
+    wall_s, gpu_ms = _timed(fn, steps, warmup, stream)
+    kern = _kernel_us(nsa, fn, kinds, 3, stream)
+    tokens = w.total_tokens
+    ms_per_step = wall_s * 1e3 / steps
+    tflops = {n: flops[n] / (kern[n] * 1e-6) / 1e12 for n in flops}
+    algo_flops = sum(v for n, v in flops.items() if n != "compressed_lse")
+    result = {
+        "metric": f"prefill tokens/s ({w.name})",
+        "value": round(tokens * steps / wall_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V" + (", sigmoid(N(0,1)) gates" if args.workload == "prefill-nsa" else ", uniform causal block indices") + "; no dataset)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": max(w.lengths), "heads": w.heads,
+                   "kv_heads": w.kv_heads, "head_dim": D, "topk": w.topk,
+                   **({"window": w.window} if args.workload == "prefill-nsa" else {})},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(tflops[dominant], 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops[dominant],
+            "mean_kernel_us": round(kern[dominant], 1),
+        },
+        "kernel_us": {n: round(x, 1) for n, x in kern.items()},
+        "kernel_tflops": {n: round(x, 2) for n, x in tflops.items()},
+        "step_algorithmic_tflops": round(algo_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "selected_gathered_gbs": round(gathered / (kern["selected_attn"] * 1e-6) / 1e9, 1),
+        "timed_gpu_ms": round(gpu_ms, 3),
+    }
     print(json.dumps(result), flush=True)
 
 

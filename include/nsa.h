@@ -282,11 +282,14 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
  *                block i, the max over the windows overlapping it of the group
  *                sum of the heads' probabilities; 0 past the row's windows and
  *                past the sequence's blocks
- *   workspace:   nsa_compressed_attn_workspace_size(rows_total, heads) bytes.
+ *   workspace:   nsa_compressed_attn_workspace_size(...) bytes (the per-head
+ *                normalisers and a transposed copy of v_c).
  *   bfloat16 only (the tiles run on the bf16 matrix cores); cu_seqlens_q is
  *   required.
  */
-size_t nsa_compressed_attn_workspace_size(int32_t rows_total, int32_t heads);
+size_t nsa_compressed_attn_workspace_size(int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                                          int32_t heads, int32_t kv_heads, int32_t kernel,
+                                          int32_t stride);
 nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v_c,
                                    nsa_dtype dtype, void* o_cmp, nsa_dtype out_dtype, float* lse,
                                    float* block_scores, int32_t n_blocks_max,
@@ -305,13 +308,16 @@ nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v
  *   (window keys including itself).  q [rows, heads, head_dim], k, v
  *   [N_k, kv_heads, head_dim], all bfloat16; out [rows, heads, head_dim] of
  *   out_dtype (written); lse nullable [rows, heads] float32 (natural log).
+ *   workspace: nsa_window_attn_workspace_size(...) bytes (a transposed copy of v).
  */
+size_t nsa_window_attn_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t kv_heads);
 nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
                                void* out, nsa_dtype out_dtype, float* lse,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
                                int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t window,
-                               float softmax_scale, hipStream_t stream);
+                               float softmax_scale, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /*
  * nsa_prefill_step -- the three-branch NSA prefill of packed query rows.

@@ -85,14 +85,15 @@ _SIGS = {
                                              c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
     "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
-    "nsa_compressed_attn_workspace_size": (c_sz, [c_i32, c_i32]),
+    "nsa_compressed_attn_workspace_size": (c_sz, [c_i32] * 7),
+    "nsa_window_attn_workspace_size": (c_sz, [c_i32] * 3),
     "nsa_compressed_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_int,
                                                c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32,
                                                c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                                c_f32, c_vp, c_sz, c_vp]),
     "nsa_window_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_int,
                                            c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
-                                           c_i32, c_i32, c_f32, c_vp]),
+                                           c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "nsa_prefill_workspace_size": (c_sz, [ctypes.POINTER(PrefillParams)]),
     "nsa_prefill_step": (ctypes.c_int, [ctypes.POINTER(PrefillParams), c_vp, c_sz, c_vp]),
 }
@@ -286,8 +287,13 @@ KERNEL_POOL, KERNEL_LOGITS, KERNEL_BLOCK_SCORES, KERNEL_SELECTED_ATTN, KERNEL_CO
 KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN = 5, 6, 7
 
 
-def compressed_attn_workspace_size(rows, heads):
-    return lib().nsa_compressed_attn_workspace_size(int(rows), int(heads))
+def compressed_attn_workspace_size(batch, rows, max_seqlen_k, heads, kv_heads, kernel=32, stride=16):
+    return lib().nsa_compressed_attn_workspace_size(int(batch), int(rows), int(max_seqlen_k),
+                                                    int(heads), int(kv_heads), kernel, stride)
+
+
+def window_attn_workspace_size(batch, max_seqlen_k, kv_heads):
+    return lib().nsa_window_attn_workspace_size(int(batch), int(max_seqlen_k), int(kv_heads))
 
 
 def nsa_compressed_attn_fwd(q, k_c, v_c, cu_seqlens_q, cu_seqlens_k, cu_seqlens_c, max_seqlen_k,
@@ -300,7 +306,8 @@ def nsa_compressed_attn_fwd(q, k_c, v_c, cu_seqlens_q, cu_seqlens_k, cu_seqlens_
     H_kv = k_c.shape[1]
     batch = cu_seqlens_k.numel() - 1
     nb_max = block_scores.shape[2] if block_scores is not None else 0
-    ws, nbytes = _workspace(compressed_attn_workspace_size(rows, H), q.device, workspace)
+    need = compressed_attn_workspace_size(batch, rows, max_seqlen_k, H, H_kv, kernel, stride)
+    ws, nbytes = _workspace(need, q.device, workspace)
     _check(lib().nsa_compressed_attn_fwd(_ptr(q), _ptr(k_c), _ptr(v_c), _dt(q), _ptr(o_cmp),
                                          _dt(o_cmp), _ptr(lse), _ptr(block_scores), nb_max,
                                          _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(cu_seqlens_c),
@@ -311,15 +318,16 @@ def nsa_compressed_attn_fwd(q, k_c, v_c, cu_seqlens_q, cu_seqlens_k, cu_seqlens_
 
 
 def nsa_window_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_k, out, window=512,
-                        lse=None, softmax_scale=0.0, stream=None):
+                        lse=None, softmax_scale=0.0, workspace=None, stream=None):
     """Sliding-window attention of prefill rows over keys t-window+1 .. t."""
     rows, H, D = q.shape
     H_kv = k.shape[1]
     batch = cu_seqlens_k.numel() - 1
+    ws, nbytes = _workspace(window_attn_workspace_size(batch, max_seqlen_k, H_kv), q.device, workspace)
     _check(lib().nsa_window_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(out), _dt(out),
                                      _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, rows,
                                      int(max_seqlen_k), H, H_kv, D, int(window),
-                                     float(softmax_scale), _stream(stream)))
+                                     float(softmax_scale), _ptr(ws), nbytes, _stream(stream)))
     return out
 
 

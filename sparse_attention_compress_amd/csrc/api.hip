@@ -342,9 +342,18 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
 
 // ----------------------------------------------------------------- prefill branches
 
-size_t nsa_compressed_attn_workspace_size(int32_t rows_total, int32_t heads) {
-  if (rows_total <= 0 || heads <= 0) return 0;
-  return (size_t(rows_total) * heads * sizeof(float) + 255) & ~size_t(255);
+size_t nsa_compressed_attn_workspace_size(int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                                          int32_t heads, int32_t kv_heads, int32_t kernel,
+                                          int32_t stride) {
+  if (batch <= 0 || rows_total <= 0 || heads <= 0 || kv_heads <= 0 || kernel < 1 || stride < 1) return 0;
+  const int max_windows = full_windows(max_seqlen_k, kernel, stride);
+  return ((size_t(rows_total) * heads * sizeof(float) + 255) & ~size_t(255)) +
+         ((nsa::transposed_bytes(batch, kv_heads, max_windows) + 255) & ~size_t(255));
+}
+
+size_t nsa_window_attn_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t kv_heads) {
+  if (batch <= 0 || kv_heads <= 0 || max_seqlen_k <= 0) return 0;
+  return (nsa::transposed_bytes(batch, kv_heads, max_seqlen_k) + 255) & ~size_t(255);
 }
 
 }  // extern "C"
@@ -387,7 +396,8 @@ nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v
   NSA_REQUIRE(q && k_c && v_c && o_cmp && cu_seqlens_k && cu_seqlens_c, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
   NSA_REQUIRE(aligned16(q) && aligned16(k_c) && aligned16(v_c) && aligned16(o_cmp), NSA_ERR_INVALID_ARG,
               "%s: q, k_c, v_c, o_cmp must be 16-byte aligned", fn);
-  const size_t need = nsa_compressed_attn_workspace_size(rows_total, heads);
+  const size_t need = nsa_compressed_attn_workspace_size(batch, rows_total, max_seqlen_k, heads, kv_heads,
+                                                        kernel, stride);
   NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
   NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
   nsa::CompressedPrefillArgs a{};
@@ -399,10 +409,14 @@ nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v
   a.cu_c = cu_seqlens_c;
   a.batch = batch;
   a.rows_total = rows_total;
+  a.max_seqlen_q = max_seqlen_k;  // a sequence has no more query rows than keys
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
+  a.max_windows = full_windows(max_seqlen_k, kernel, stride);
   a.lse2 = static_cast<float*>(workspace);
+  a.vct = reinterpret_cast<nsa::bf16_t*>(static_cast<char*>(workspace) +
+                                         ((size_t(rows_total) * heads * sizeof(float) + 255) & ~size_t(255)));
   a.o_cmp = o_cmp;
   a.out_f32 = out_dtype == NSA_F32;
   a.lse_nat = lse;
@@ -416,7 +430,8 @@ nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
                                int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t window,
-                               float softmax_scale, hipStream_t stream) {
+                               float softmax_scale, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   const char* fn = "nsa_window_attn_fwd";
   nsa_status st = check_prefill_common(fn, dtype, batch, rows_total, max_seqlen_k, heads, kv_heads, head_dim);
   if (st != NSA_OK) return st;
@@ -427,6 +442,9 @@ nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_
   NSA_REQUIRE(q && k && v && out && cu_seqlens_k, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
   NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), NSA_ERR_INVALID_ARG,
               "%s: q, k, v, out must be 16-byte aligned", fn);
+  const size_t need = nsa_window_attn_workspace_size(batch, max_seqlen_k, kv_heads);
+  NSA_REQUIRE(workspace != nullptr || need == 0, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
   nsa::WindowPrefillArgs a{};
   a.q = static_cast<const nsa::bf16_t*>(q);
   a.k = static_cast<const nsa::bf16_t*>(k);
@@ -435,9 +453,12 @@ nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_
   a.cu_k = cu_seqlens_k;
   a.batch = batch;
   a.rows_total = rows_total;
+  a.max_seqlen_q = max_seqlen_k;
+  a.max_seqlen_k = max_seqlen_k;
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.window = window;
+  a.vt = static_cast<nsa::bf16_t*>(workspace);
   a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
   a.out = out;
   a.out_f32 = out_dtype == NSA_F32;
@@ -450,7 +471,7 @@ nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_
 namespace {
 
 struct PrefillLayout {
-  size_t lse2, o_cmp, o_sel, scores, indices, total;
+  size_t lse2, vct, vt, o_cmp, o_sel, scores, indices, total;
   int nb_max, max_windows;
 };
 
@@ -463,6 +484,10 @@ PrefillLayout prefill_layout(const nsa_prefill_params* p) {
   size_t off = 0;
   L.lse2 = off;
   off += up(rows * H * sizeof(float));
+  L.vct = off;
+  off += up(nsa::transposed_bytes(p->batch, p->kv_heads, L.max_windows));
+  L.vt = off;
+  off += up(nsa::transposed_bytes(p->batch, p->kv_heads, p->max_seqlen_k));
   L.o_cmp = off;
   off += up(rows * H * p->head_dim * sizeof(float));
   L.o_sel = off;
@@ -543,10 +568,13 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   c.cu_c = p->cu_seqlens_c;
   c.batch = p->batch;
   c.rows_total = p->rows_total;
+  c.max_seqlen_q = p->max_seqlen_k;
   c.heads = p->heads;
   c.kv_heads = p->kv_heads;
   c.scale_log2 = sl2;
+  c.max_windows = lay.max_windows;
   c.lse2 = reinterpret_cast<float*>(base + lay.lse2);
+  c.vct = reinterpret_cast<nsa::bf16_t*>(base + lay.vct);
   c.o_cmp = o_cmp;
   c.out_f32 = 1;
   c.lse_nat = nullptr;
@@ -573,6 +601,9 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   w.cu_k = p->cu_seqlens_k;
   w.batch = p->batch;
   w.rows_total = p->rows_total;
+  w.max_seqlen_q = p->max_seqlen_k;
+  w.max_seqlen_k = p->max_seqlen_k;
+  w.vt = reinterpret_cast<nsa::bf16_t*>(base + lay.vt);
   w.heads = p->heads;
   w.kv_heads = p->kv_heads;
   w.window = p->window;

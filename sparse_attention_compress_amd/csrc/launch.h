@@ -125,9 +125,10 @@ struct CompressedPrefillArgs {
   const int* cu_q;
   const int* cu_k;
   const int* cu_c;
-  int batch, rows_total, heads, kv_heads;
+  int batch, rows_total, max_seqlen_q, max_windows, heads, kv_heads;
   float scale_log2;
   float* lse2;           // [rows, heads] workspace: log2-domain normaliser
+  bf16_t* vct;           // workspace: v_c transposed, transposed_bytes(batch, kv, max_windows)
   void* o_cmp;           // [rows, heads, 128]
   int out_f32;           // o_cmp dtype: 1 float32, 0 bfloat16
   float* lse_nat;        // nullable [rows, heads]
@@ -142,8 +143,9 @@ struct WindowPrefillArgs {
   const bf16_t* v;
   const int* cu_q;
   const int* cu_k;
-  int batch, rows_total, heads, kv_heads, window;
+  int batch, rows_total, max_seqlen_q, max_seqlen_k, heads, kv_heads, window;
   float scale_log2;
+  bf16_t* vt;            // workspace: v transposed, transposed_bytes(batch, kv, max_seqlen_k)
   void* out;
   int out_f32;
   float* lse_nat;        // nullable
@@ -152,5 +154,9 @@ struct WindowPrefillArgs {
   const float* o_sel;    // [rows, heads, 128] float32 (with gates)
 };
 hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s);
+
+// Values transposed per (sequence, KV head, dim) for the prefill branches.
+int transposed_ld(int max_len);
+size_t transposed_bytes(int batch, int kv_heads, int max_len);
 
 }  // namespace nsa

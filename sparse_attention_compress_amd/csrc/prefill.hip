@@ -12,89 +12,186 @@
 //   o_win(t, h) = softmax over keys max(0, t-W+1) .. t, times V;
 //   o(t, h)     = g0 o_cmp + g1 o_sel + g2 o_win.
 //
-// Design (gfx950): one wave per query token and KV group; the group's G <= 16
-// query heads are the 16 columns of the MFMA tiles, keys (or windows) go 16 at a
-// time as the rows: S^T = K Q^T with four v_mfma_f32_16x16x32_bf16 (key rows
-// loaded straight into the A operand, Q^T kept in registers), then
-// O^T += V^T P^T with eight v_mfma_f32_16x16x16_bf16 (P^T is already in the
-// operand layout).  A workgroup holds 4 waves = 4 consecutive tokens of one KV
-// group, so the key tiles they share are served from L1/L2.  No LDS, no
-// workgroup barriers.  The compressed branch runs in two passes: the first finds
-// each head's log2 normaliser, the second forms normalised probabilities, which
-// give o_cmp directly and, summed over the 16 head columns with DPP, the window
+// Design (gfx950): one wave per 4 consecutive query tokens of one sequence and
+// KV group; for each token the group's G <= 16 query heads are the 16 columns
+// of the MFMA tiles, keys (or windows) go 16 at a time as the rows:
+// S^T = K Q^T with four v_mfma_f32_16x16x32_bf16 (key rows loaded straight into
+// the A operand, Q^T kept in registers), then O^T += V^T P^T with eight
+// v_mfma_f32_16x16x16_bf16 (P^T is already in the operand layout).  Each key
+// tile a wave loads serves its 4 tokens, and the next tile is in flight while
+// the current one is computed.  A workgroup holds 4 waves = 16 consecutive
+// tokens, so the tiles they share come from L1/L2.  No LDS, no workgroup
+// barriers.  The compressed branch runs in two passes: the first finds each
+// head's log2 normaliser, the second forms normalised probabilities, which give
+// o_cmp directly and, summed over the 16 head columns with DPP, the window
 // scores of the group.
 #include "common.h"
 #include "launch.h"
 
 namespace nsa {
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void prefill_row_position(int row, const int* __restrict__ cu_q,
-                                                     const int* __restrict__ cu_k, int batch,
-                                                     int& b, int& t) {
-  int lo = 0, hi = batch - 1;  // last sequence whose first row is <= row
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+// ------------------------------------------------------------ transposed values
+
+// X [N, kv_heads, 128] packed by cu -> XT [batch][kv_heads][128][ld]: one row per
+// (sequence, KV head, dim) holding that dim of every token, zero past the
+// sequence.  ld is a multiple of 64.  Grid (ld / 64, kv heads, sequences); each
+// workgroup moves a 64-token x 128-dim tile through LDS.
+__global__ __launch_bounds__(256) void transpose_values_kernel(const bf16_t* __restrict__ x,
+                                                               const int* __restrict__ cu,
+                                                               int kv_heads, int ld,
+                                                               bf16_t* __restrict__ xt) {
+  constexpr int D = kHeadDim;
+  __shared__ uint16_t tile[64][D + 8];  // rows padded to spread the column reads over banks
+  const int tid = threadIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tok0 = blockIdx.x * 64;
+  const int start = cu[b], len = cu[b + 1] - start;
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i, r = idx >> 4, c = idx & 15;
+    const int tok = min(tok0 + r, max(len - 1, 0));
+    v[i] = len > 0 ? ld16(x + (size_t(start + tok) * kv_heads + kv) * D + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    if (tok0 + r >= len) v[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  b = lo;
-  t = (row - cu_q[b]) + ((cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i, r = idx >> 4, c = idx & 15;
+    *reinterpret_cast<uint4*>(&tile[r][8 * c]) = v[i];
+  }
+  __syncthreads();
+  bf16_t* dst = xt + (size_t(b) * kv_heads + kv) * D * size_t(ld) + tok0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i, d = idx >> 3, tc = idx & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = uint32_t(tile[8 * tc + 2 * e][d]) | (uint32_t(tile[8 * tc + 2 * e + 1][d]) << 16);
+    *reinterpret_cast<uint4*>(dst + size_t(d) * ld + 8 * tc) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
-__device__ __forceinline__ uint32_t ld_h(const bf16_t* p) {
-  return uint32_t(*reinterpret_cast<const uint16_t*>(p));
-}
+// ------------------------------------------------------------------- key tiles
 
-// One 16-key tile of a wave: keys key0 + r (r < 16) of rows `base + key*rs`.
-// ka: A operand of S^T = K Q^T (key c16, dims 32i + 8 r4 .. +8).
-// va: A operand of O^T = V^T P^T (dim 16n + c16; keys 4 r4 + 2m, +1).
-// Key rows are clamped to [0, kmax] so every load is in bounds; the caller masks.
-struct KeyTile {
-  uint4 ka[4];
-  uint32_t va[16];
-};
+// One 32-key tile of a wave, keys key0 .. key0+31 (key0 a multiple of 32).
+// ka[h] (KeyFrag): A operand of S^T = K Q^T for keys key0 + 16h + c16, dims 32i + 8 r4 .. +8
+//        (row-major K, rows clamped to kmax so every load is in bounds).
+// va[n] (ValFrag): A operand of O^T = V^T P^T for dim 16n + c16, from the transposed
+//        values; k-slot e < 4 holds key key0 + 4 r4 + e, e >= 4 key key0 + 16 +
+//        4 r4 + e - 4 (the same slots the S^T accumulators give P^T).
+typedef uint4 KeyFrag[2][4];
+typedef uint4 ValFrag[8];
 
-template <bool WITH_V>
-__device__ __forceinline__ void load_tile(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb,
-                                          size_t rs, int key0, int kmax, KeyTile& T) {
+__device__ __forceinline__ void load_keys(const bf16_t* __restrict__ kb, size_t rs, int key0,
+                                          int kmax, KeyFrag& ka) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
-  const bf16_t* kr = kb + size_t(min(key0 + c16, kmax)) * rs + 8 * r4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) T.ka[i] = ld16(kr + 32 * i);
-  if constexpr (WITH_V) {
-    const bf16_t* vr[4];
+  for (int h = 0; h < 2; ++h) {
+    const bf16_t* kr = kb + size_t(min(key0 + 16 * h + c16, kmax)) * rs + 8 * r4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vr[e] = vb + size_t(min(key0 + 4 * r4 + e, kmax)) * rs + c16;
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        T.va[2 * n + m] = ld_h(vr[2 * m] + 16 * n) | (ld_h(vr[2 * m + 1] + 16 * n) << 16);
+    for (int i = 0; i < 4; ++i) ka[h][i] = ld16(kr + 32 * i);
   }
 }
 
-__device__ __forceinline__ f32x4_t tile_scores(const KeyTile& T, const uint4 (&qb)[4]) {
+__device__ __forceinline__ void load_vals(const bf16_t* __restrict__ vt, int ldv, int key0,
+                                          ValFrag& va) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
+  const bf16_t* vr = vt + size_t(c16) * ldv + key0 + 4 * r4;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(vr + size_t(16 * n) * ldv);
+    const uint2 hi = *reinterpret_cast<const uint2*>(vr + size_t(16 * n) * ldv + 16);
+    va[n] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// Tile loop: keys first .. last in 32-key tiles from `first` (a multiple of 32).
+// The next tile's keys are double-buffered; its values are loaded into the one
+// value buffer right after this tile's P.V has consumed it, so they arrive
+// during the next tile's scores.
+// PREFETCH_KEYS = false keeps a single key buffer (the next tile's keys are then
+// loaded after this tile's scores), for kernels short of registers.
+template <bool WITH_V, bool PREFETCH_KEYS = true, typename F>
+__device__ __forceinline__ void tile_loop(const bf16_t* __restrict__ kb, size_t rs,
+                                          const bf16_t* __restrict__ vt, int ldv, int first,
+                                          int last, int kmax, F&& process) {
+  if (first > last) return;
+  ValFrag va;
+  if constexpr (!PREFETCH_KEYS) {
+    KeyFrag ka;
+    load_keys(kb, rs, first, kmax, ka);
+    if constexpr (WITH_V) load_vals(vt, ldv, first, va);
+    for (int key0 = first; key0 <= last; key0 += 32) {
+      process(key0, ka, va);
+      if (key0 + 32 <= last) {
+        load_keys(kb, rs, key0 + 32, kmax, ka);
+        if constexpr (WITH_V) load_vals(vt, ldv, key0 + 32, va);
+      }
+    }
+    return;
+  }
+  KeyFrag kA, kB;
+  load_keys(kb, rs, first, kmax, kA);
+  if constexpr (WITH_V) load_vals(vt, ldv, first, va);
+  for (int key0 = first;; key0 += 64) {
+    const bool has1 = key0 + 32 <= last;
+    if (has1) load_keys(kb, rs, key0 + 32, kmax, kB);
+    process(key0, kA, va);
+    if (!has1) break;
+    if constexpr (WITH_V) load_vals(vt, ldv, key0 + 32, va);
+    const bool has2 = key0 + 64 <= last;
+    if (has2) load_keys(kb, rs, key0 + 64, kmax, kA);
+    process(key0 + 32, kB, va);
+    if (!has2) break;
+    if constexpr (WITH_V) load_vals(vt, ldv, key0 + 64, va);
+  }
+}
+
+// S^T of half h: lane (c16, r4) element e = score of key key0 + 16h + 4 r4 + e
+// against head c16.
+__device__ __forceinline__ f32x4_t tile_scores(const uint4 (&ka)[2][4], int h, const uint4 (&qb)[4]) {
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.ka[i]),
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[h][i]),
                                                 __builtin_bit_cast(bf16x8_t, qb[i]), s, 0, 0, 0);
   return s;
 }
 
-__device__ __forceinline__ void tile_pv(const KeyTile& T, const float (&p)[4], f32x4_t (&acc)[8]) {
-  const bf16x2_t p01 = {(__bf16)p[0], (__bf16)p[1]};
-  const bf16x2_t p23 = {(__bf16)p[2], (__bf16)p[3]};
-  const s16x4_t pb = __builtin_bit_cast(
-      s16x4_t, make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)));
+// O^T += V^T P^T over the tile's 32 keys; p[e] in the k-slot order of va.
+__device__ __forceinline__ void tile_pv(const uint4 (&va)[8], const float (&p)[8], f32x4_t (&acc)[8]) {
+  const bf16x8_t pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                       (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(T.va[2 * n], T.va[2 * n + 1]));
-    acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[n], 0, 0, 0);
-  }
+  for (int n = 0; n < 8; ++n)
+    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va[n]), pb,
+                                                     acc[n], 0, 0, 0);
+}
+
+// Group scores of one 16-window half tile: p[e] is the lane's probability of
+// window 4 r4 + e for head c16.  Returns in lane (c16, r4) the sum over the 16
+// head columns of window 4 r4 + 2 (c16 & 1) + ((c16 >> 1) & 1); lane 15 of a
+// row (c16 & 3 == 3) therefore holds the row's last window.  Pairwise DPP
+// exchanges split the four windows over the quad, then two rotations finish
+// the sum over the row.
+__device__ __forceinline__ float head_sums(const float (&p)[4]) {
+  const bool odd = threadIdx.x & 1, hi = (threadIdx.x >> 1) & 1;
+  float s0 = odd ? p[2] : p[0], s1 = odd ? p[3] : p[1];
+  s0 += dpp<kDppQuadXor1>(odd ? p[0] : p[2]);
+  s1 += dpp<kDppQuadXor1>(odd ? p[1] : p[3]);
+  float k = hi ? s1 : s0;
+  k += dpp<kDppQuadXor2>(hi ? s0 : s1);
+  k += dpp<kDppRowRor4>(k);
+  return k + dpp<kDppRowRor8>(k);
+}
+
+// Value of lane 15 of the previous row (rows 1..3); row 0 gets `first`.
+__device__ __forceinline__ float prev_row_last(float x, float first) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(x),
+                                                    0x142 /* row_bcast:15 */, 0xE, 0xF, false));
 }
 
 // Column (head) reductions over the 4 lane rows of a wave.
@@ -137,95 +234,165 @@ __device__ __forceinline__ void store_rows(void* __restrict__ out, int out_f32, 
 
 // ------------------------------------------------------------- compressed branch
 
+// Query tokens per wave: every key tile loaded by a wave serves this many tokens.
+constexpr int kTpw = 4;
+
+// The tokens of one wave: query positions tq0 .. tq0 + n - 1 of sequence b
+// (grid z), packed rows row0 .. row0 + n - 1, key positions t0 .. t0 + n - 1.
+struct WaveRows {
+  int n, row0, t0;
+};
+
+__device__ __forceinline__ WaveRows wave_rows(const int* __restrict__ cu_q,
+                                              const int* __restrict__ cu_k, int b, int tile) {
+  const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
+  const int lk = cu_k[b + 1] - cu_k[b];
+  const int tq = tile * kTpw;
+  WaveRows r;
+  r.n = max(0, min(kTpw, lq - tq));
+  r.row0 = q0 + tq;
+  r.t0 = tq + (lk - lq);
+  return r;
+}
+
 // PROBS = false: per (row, head) log2 normaliser lse2 = max + log2(sum exp2).
 // PROBS = true:  o_cmp, natural-log lse, and the group's block scores.
+// vct: the compressed values transposed ([batch][kv][128][ldv]).
 template <int G, bool PROBS>
 __global__ __launch_bounds__(256) void compressed_prefill_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
-    const int* __restrict__ cu_q, const int* __restrict__ cu_k, const int* __restrict__ cu_c,
-    int batch, int rows_total, int kv_heads, float scale_log2, float* __restrict__ lse2,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vct,
+    int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    const int* __restrict__ cu_c, int kv_heads, float scale_log2, float* __restrict__ lse2,
     void* __restrict__ o_cmp, int out_f32, float* __restrict__ lse_nat,
     float* __restrict__ block_scores, int nb_max) {
   constexpr int D = kHeadDim;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
-  const int row = blockIdx.x * 4 + wave;
-  const int kv = blockIdx.y;
-  if (row >= rows_total) return;  // whole wave; the kernel has no barriers
-  int b, t;
-  prefill_row_position(row, cu_q, cu_k, batch, b, t);
+  const int kv = blockIdx.y, b = blockIdx.z;
+  const WaveRows R = wave_rows(cu_q, cu_k, b, blockIdx.x * 4 + wave);
+  if (R.n == 0) return;  // whole wave; the kernel has no barriers
   const int len = cu_k[b + 1] - cu_k[b];
   const int cbase = cu_c[b];
   const int nc = cu_c[b + 1] - cbase;
-  const int nvis = t >= kKernel - 1 ? min(nc, (t - (kKernel - 1)) / kStride + 1) : 0;
-  const size_t head0 = (size_t(row) * kv_heads + kv) * G;  // first head of the group
-  uint4 qb[4];
-  load_q<G>(q + head0 * D, qb);
+  int nvis[kTpw];
+  size_t head0[kTpw];  // first head of the group, per token (clamped to a valid row)
+  uint4 qb[kTpw][4];
+#pragma unroll
+  for (int j = 0; j < kTpw; ++j) {
+    const int t = R.t0 + j;
+    nvis[j] = (j < R.n && t >= kKernel - 1) ? min(nc, (t - (kKernel - 1)) / kStride + 1) : 0;
+    head0[j] = (size_t(R.row0 + min(j, R.n - 1)) * kv_heads + kv) * G;
+    load_q<G>(q + head0[j] * D, qb[j]);
+  }
+  int nv_max = 0;
+#pragma unroll
+  for (int j = 0; j < kTpw; ++j) nv_max = max(nv_max, nvis[j]);
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kb = kc + size_t(cbase) * rs + size_t(kv) * D;
-  const bf16_t* vb = vc + size_t(cbase) * rs + size_t(kv) * D;
-  const int cmax = max(nvis - 1, 0);
+  const bf16_t* vt = vct + (size_t(b) * kv_heads + kv) * D * size_t(ldv);
+  const int cmax = max(nv_max - 1, 0);
 
   if constexpr (!PROBS) {
-    float m_run = -INFINITY, l_run = 0.f;
-    for (int w0 = 0; w0 < nvis; w0 += 16) {
-      KeyTile T;
-      load_tile<false>(kb, vb, rs, w0, cmax, T);
-      const f32x4_t s = tile_scores(T, qb);
-      float sv[4], mx = -INFINITY;
+    float m_run[kTpw], l_run[kTpw];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sv[e] = w0 + 4 * r4 + e < nvis ? s[e] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[e]);
-      }
-      mx = rows_max(mx);
-      if (mx > m_run) {
-        l_run *= fast_exp2(m_run - mx);
-        m_run = mx;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) l_run += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run);
+    for (int j = 0; j < kTpw; ++j) {
+      m_run[j] = -INFINITY;
+      l_run[j] = 0.f;
     }
-    l_run = rows_sum(l_run);
-    if (r4 == 0 && c16 < G) lse2[head0 + c16] = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
+    auto process = [&](int w0, const KeyFrag& ka, const ValFrag& va) {
+      // every token runs every tile (windows past its own count are masked), so
+      // the four tokens' chains interleave
+#pragma unroll
+      for (int j = 0; j < kTpw; ++j) {
+        float sv[8], mx = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t s = tile_scores(ka, h, qb[j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[4 * h + e] = w0 + 16 * h + 4 * r4 + e < nvis[j] ? s[e] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[4 * h + e]);
+          }
+        }
+        mx = rows_max(mx);
+        if (mx > m_run[j]) {
+          l_run[j] *= fast_exp2(m_run[j] - mx);
+          m_run[j] = mx;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l_run[j] += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run[j]);
+      }
+    };
+    tile_loop<false>(kb, rs, vt, ldv, 0, nv_max - 1, cmax, process);
+#pragma unroll
+    for (int j = 0; j < kTpw; ++j) {
+      const float l = rows_sum(l_run[j]);
+      if (j < R.n && r4 == 0 && c16 < G)
+        lse2[head0[j] + c16] = l > 0.f ? m_run[j] + __log2f(l) : -INFINITY;
+    }
   } else {
-    const float lh = lse2[head0 + min(c16, G - 1)];
-    f32x4_t acc[8];
+    float lh[kTpw], carry[kTpw];
+    f32x4_t acc[kTpw][8];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int nb = (len + kBlock - 1) / kBlock;
-    float* bs_row = block_scores != nullptr ? block_scores + (size_t(row) * kv_heads + kv) * nb_max : nullptr;
-    float carry = 0.f;  // group score of window 16u - 1 (the previous tile's last)
-    for (int w0 = 0; w0 < nvis; w0 += 16) {
-      KeyTile T;
-      load_tile<true>(kb, vb, rs, w0, cmax, T);
-      const f32x4_t s = tile_scores(T, qb);
-      float p[4];
+    for (int j = 0; j < kTpw; ++j) {
+      lh[j] = lse2[head0[j] + min(c16, G - 1)];
+      carry[j] = 0.f;  // group score of window w0 - 1 (the previous tile's last)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p[e] = (c16 < G && w0 + 4 * r4 + e < nvis) ? fast_exp2(s[e] * scale_log2 - lh) : 0.f;
-      tile_pv(T, p, acc);
-      if (bs_row != nullptr) {
-        // group scores of windows w0 + 4 r4 + e, then block w0/4 + r4 over its
-        // windows 4i-1 .. 4i+3 (the first one ends the previous lane row)
-        float pg[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pg[e] = row_reduce(p[e], OpSum());
-        const float up = __shfl(pg[3], (lane + 48) & 63);  // row r4 - 1
-        const float first = r4 == 0 ? carry : up;
-        const float sc = fmaxf(fmaxf(first, pg[0]), fmaxf(fmaxf(pg[1], pg[2]), pg[3]));
-        const int blk = w0 / 4 + r4;
-        if (c16 == 0 && blk < nb) bs_row[blk] = sc;
-        carry = __shfl(pg[3], 48);
-      }
+      for (int n = 0; n < 8; ++n) acc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    store_rows<G>(o_cmp, out_f32, head0, acc, 1.f);
-    if (lse_nat != nullptr && r4 == 0 && c16 < G) lse_nat[head0 + c16] = lh * kLn2;
-    if (bs_row != nullptr) {
-      // blocks past the last tile: the first still sees window 16U - 1
-      const int first_blk = nvis > 0 ? ((nvis + 15) / 16) * 4 : 0;
-      for (int i = first_blk + lane; i < nb_max; i += kWave)
-        bs_row[i] = (i == first_blk && nvis > 0 && i < nb) ? carry : 0.f;
+    const int nb = (len + kBlock - 1) / kBlock;
+    auto process = [&](int w0, const KeyFrag& ka, const ValFrag& va) {
+      // every token runs every tile (windows past its own count are masked), so
+      // the four tokens' chains interleave
+#pragma unroll
+      for (int j = 0; j < kTpw; ++j) {
+        float p[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t s = tile_scores(ka, h, qb[j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[4 * h + e] = (c16 < G && w0 + 16 * h + 4 * r4 + e < nvis[j])
+                               ? fast_exp2(s[e] * scale_log2 - lh[j]) : 0.f;
+        }
+        tile_pv(va, p, acc[j]);
+        if (block_scores != nullptr) {
+          // block w0/4 + 4h + r4 covers windows 4i-1 .. 4i+3: the lane row's four
+          // windows and the previous row's last (the previous half's last for row 0)
+          const float pgA = head_sums({p[0], p[1], p[2], p[3]});
+          const float pgB = head_sums({p[4], p[5], p[6], p[7]});
+          const float lastA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pgA), 63));
+          const float lastB = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pgB), 63));
+          float mA = fmaxf(pgA, dpp<kDppQuadXor1>(pgA));
+          mA = fmaxf(mA, dpp<kDppQuadXor2>(mA));
+          float mB = fmaxf(pgB, dpp<kDppQuadXor1>(pgB));
+          mB = fmaxf(mB, dpp<kDppQuadXor2>(mB));
+          const float scA = fmaxf(mA, prev_row_last(pgA, carry[j]));
+          const float scB = fmaxf(mB, prev_row_last(pgB, lastA));
+          float* bs_row = block_scores + (size_t(R.row0 + j) * kv_heads + kv) * nb_max;
+          const int blkA = w0 / 4 + r4, blkB = blkA + 4;
+          if (w0 < nvis[j] && c16 == 0) {
+            if (blkA < nb) bs_row[blkA] = scA;
+            if (blkB < nb) bs_row[blkB] = scB;
+          }
+          if (w0 < nvis[j]) carry[j] = lastB;                   // window w0 + 31
+        }
+      }
+    };
+    tile_loop<true, false>(kb, rs, vt, ldv, 0, nv_max - 1, cmax, process);
+#pragma unroll
+    for (int j = 0; j < kTpw; ++j) {
+      if (j >= R.n) continue;
+      store_rows<G>(o_cmp, out_f32, head0[j], acc[j], 1.f);
+      if (lse_nat != nullptr && r4 == 0 && c16 < G) lse_nat[head0[j] + c16] = lh[j] * kLn2;
+      if (block_scores != nullptr) {
+        // blocks past the token's last tile: the first still sees the tile's last
+        // window; blocks past the sequence are 0
+        float* bs_row = block_scores + (size_t(R.row0 + j) * kv_heads + kv) * nb_max;
+        const int first_blk = nvis[j] > 0 ? ((nvis[j] + 31) / 32) * 8 : 0;
+        for (int i = min(first_blk, nb) + lane; i < nb_max; i += kWave)
+          bs_row[i] = (i == first_blk && nvis[j] > 0 && i < nb) ? carry[j] : 0.f;
+      }
     }
   }
 }
@@ -234,108 +401,144 @@ __global__ __launch_bounds__(256) void compressed_prefill_kernel(
 
 // Sliding-window attention over keys max(0, t-W+1) .. t; with GATED the output
 // is g0 * o_cmp + g1 * o_sel + g2 * o_win (the branch outputs are fp32 rows).
+// The wave's tokens share the key tiles of the union of their windows.
+// vtr: the values transposed ([batch][kv][128][ldv]).
 template <int G, bool GATED>
 __global__ __launch_bounds__(256) void window_prefill_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int rows_total,
-    int kv_heads, int window, float scale_log2, void* __restrict__ out, int out_f32,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vtr,
+    int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads,
+    int window, float scale_log2, void* __restrict__ out, int out_f32,
     float* __restrict__ lse_nat, const float* __restrict__ gates,
     const float* __restrict__ o_cmp, const float* __restrict__ o_sel) {
   constexpr int D = kHeadDim;
   constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
-  const int row = blockIdx.x * 4 + wave;
-  const int kv = blockIdx.y;
-  if (row >= rows_total) return;  // whole wave; the kernel has no barriers
-  int b, t;
-  prefill_row_position(row, cu_q, cu_k, batch, b, t);
-  const size_t head0 = (size_t(row) * kv_heads + kv) * G;
-  uint4 qb[4];
-  load_q<G>(q + head0 * D, qb);
+  const int kv = blockIdx.y, b = blockIdx.z;
+  const WaveRows R = wave_rows(cu_q, cu_k, b, blockIdx.x * 4 + wave);
+  if (R.n == 0) return;  // whole wave; the kernel has no barriers
+  size_t head0[kTpw];
+  uint4 qb[kTpw][4];
+#pragma unroll
+  for (int j = 0; j < kTpw; ++j) {
+    head0[j] = (size_t(R.row0 + min(j, R.n - 1)) * kv_heads + kv) * G;
+    load_q<G>(q + head0[j] * D, qb[j]);
+  }
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kb = k + size_t(cu_k[b]) * rs + size_t(kv) * D;
-  const bf16_t* vb = v + size_t(cu_k[b]) * rs + size_t(kv) * D;
-  const int j_lo = max(0, t - window + 1);
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t acc[8];
+  const bf16_t* vt = vtr + (size_t(b) * kv_heads + kv) * D * size_t(ldv);
+  const int t_last = R.t0 + R.n - 1;
+  const int j_lo = max(0, R.t0 - window + 1) & ~31;  // tiles start 32-aligned
+  float m_run[kTpw], l_run[kTpw];
+  f32x4_t acc[kTpw][8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  KeyTile A, B;
-  auto step = [&](int key0, const KeyTile& T) {
-    const f32x4_t s = tile_scores(T, qb);
-    float sv[4], mx = -INFINITY;
+  for (int j = 0; j < kTpw; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = key0 + 4 * r4 + e <= t ? s[e] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[e]);
-    }
-    mx = rows_max(mx);
-    if (mx > m_run + kLazy) {  // also true for the first tile with a key
-      const float alpha = fast_exp2(m_run - mx);
-      m_run = mx;
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-    }
-    float p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[e] = sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run);
-      l_run += p[e];
-    }
-    tile_pv(T, p, acc);
-  };
-  // double-buffered: the next tile's loads are in flight during this tile's math
-  if (t >= 0) load_tile<true>(kb, vb, rs, j_lo, t, A);
-  for (int key0 = j_lo; key0 <= t; key0 += 32) {
-    const bool has1 = key0 + 16 <= t;
-    if (has1) load_tile<true>(kb, vb, rs, key0 + 16, t, B);
-    step(key0, A);
-    if (has1) {
-      if (key0 + 32 <= t) load_tile<true>(kb, vb, rs, key0 + 32, t, A);
-      step(key0 + 16, B);
-    }
+    for (int n = 0; n < 8; ++n) acc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  l_run = rows_sum(l_run);
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  if constexpr (GATED) {
-    if (c16 < G) {
-      const size_t h = head0 + c16;
-      const float g0 = gates[h * 3 + 0], g1 = gates[h * 3 + 1], g2 = gates[h * 3 + 2];
-      const float* pc = o_cmp + h * D + 4 * r4;
-      const float* ps = o_sel + h * D + 4 * r4;
+  auto process = [&](int key0, const KeyFrag& ka, const ValFrag& va) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const float4 a = *reinterpret_cast<const float4*>(pc + 16 * n);
-        const float4 s = *reinterpret_cast<const float4*>(ps + 16 * n);
-        acc[n][0] = g0 * a.x + g1 * s.x + g2 * acc[n][0] * inv;
-        acc[n][1] = g0 * a.y + g1 * s.y + g2 * acc[n][1] * inv;
-        acc[n][2] = g0 * a.z + g1 * s.z + g2 * acc[n][2] * inv;
-        acc[n][3] = g0 * a.w + g1 * s.w + g2 * acc[n][3] * inv;
+    for (int j = 0; j < kTpw; ++j) {
+      // every token runs every tile of the union (keys outside its own window
+      // are masked), so the four tokens' chains interleave
+      const int t = R.t0 + j;
+      const int lo = max(0, t - window + 1);
+      float sv[8], mx = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4_t s = tile_scores(ka, h, qb[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = key0 + 16 * h + 4 * r4 + e;
+          sv[4 * h + e] = (key <= t && key >= lo) ? s[e] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sv[4 * h + e]);
+        }
       }
+      mx = rows_max(mx);
+      if (mx > m_run[j] + kLazy) {  // also true for the first tile with a key
+        const float alpha = fast_exp2(m_run[j] - mx);
+        m_run[j] = mx;
+        l_run[j] *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[j][n] *= alpha;
+      }
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run[j]);
+        l_run[j] += p[e];
+      }
+      tile_pv(va, p, acc[j]);
     }
-    store_rows<G>(out, out_f32, head0, acc, 1.f);
-  } else {
-    store_rows<G>(out, out_f32, head0, acc, inv);
+  };
+  tile_loop<true>(kb, rs, vt, ldv, j_lo, t_last, t_last, process);
+#pragma unroll
+  for (int j = 0; j < kTpw; ++j) {
+    const float l = rows_sum(l_run[j]);
+    if (j >= R.n) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if constexpr (GATED) {
+      if (c16 < G) {
+        const size_t h = head0[j] + c16;
+        const float g0 = gates[h * 3 + 0], g1 = gates[h * 3 + 1], g2 = gates[h * 3 + 2];
+        const float* pc = o_cmp + h * D + 4 * r4;
+        const float* ps = o_sel + h * D + 4 * r4;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const float4 a = *reinterpret_cast<const float4*>(pc + 16 * n);
+          const float4 s = *reinterpret_cast<const float4*>(ps + 16 * n);
+          acc[j][n][0] = g0 * a.x + g1 * s.x + g2 * acc[j][n][0] * inv;
+          acc[j][n][1] = g0 * a.y + g1 * s.y + g2 * acc[j][n][1] * inv;
+          acc[j][n][2] = g0 * a.z + g1 * s.z + g2 * acc[j][n][2] * inv;
+          acc[j][n][3] = g0 * a.w + g1 * s.w + g2 * acc[j][n][3] * inv;
+        }
+      }
+      store_rows<G>(out, out_f32, head0[j], acc[j], 1.f);
+    } else {
+      store_rows<G>(out, out_f32, head0[j], acc[j], inv);
+    }
+    if (lse_nat != nullptr && r4 == 0 && c16 < G)
+      lse_nat[head0[j] + c16] = l > 0.f ? (m_run[j] + __log2f(l)) * kLn2 : -INFINITY;
   }
-  if (lse_nat != nullptr && r4 == 0 && c16 < G)
-    lse_nat[head0 + c16] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
 }
 
 // --------------------------------------------------------------------------- host
 
+// Grid: (groups of 4 waves x kTpw tokens, kv head, sequence).
+static dim3 prefill_grid(int max_seqlen_q, int kv_heads, int batch) {
+  return dim3((max_seqlen_q + 4 * kTpw - 1) / (4 * kTpw), kv_heads, batch);
+}
+
+int transposed_ld(int max_len) { return (max_len + 63) / 64 * 64; }
+
+size_t transposed_bytes(int batch, int kv_heads, int max_len) {
+  return size_t(batch) * kv_heads * kHeadDim * size_t(transposed_ld(max_len)) * sizeof(bf16_t);
+}
+
+static hipError_t launch_transpose(const bf16_t* x, const int* cu, int batch, int kv_heads,
+                                   int max_len, bf16_t* xt, hipStream_t s) {
+  const int ld = transposed_ld(max_len);
+  if (ld == 0 || batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_values_kernel, dim3(ld / 64, kv_heads, batch), dim3(256), 0, s, x,
+                     cu, kv_heads, ld, xt);
+  return hipGetLastError();
+}
+
 template <int G>
 static hipError_t launch_cmp_g(const CompressedPrefillArgs& a, hipStream_t s) {
-  const dim3 grid((a.rows_total + 3) / 4, a.kv_heads);
-  hipError_t e = launch_kernel(
-      kKindCmpLse, compressed_prefill_kernel<G, false>, grid, dim3(256), s, a.q, a.kc, a.vc,
-      a.cu_q, a.cu_k, a.cu_c, a.batch, a.rows_total, a.kv_heads, a.scale_log2, a.lse2,
-      static_cast<void*>(nullptr), 0, static_cast<float*>(nullptr), static_cast<float*>(nullptr),
-      0);
+  const dim3 grid = prefill_grid(a.max_seqlen_q, a.kv_heads, a.batch);
+  const int ldv = transposed_ld(a.max_windows);
+  hipError_t e = launch_transpose(a.vc, a.cu_c, a.batch, a.kv_heads, a.max_windows, a.vct, s);
+  if (e != hipSuccess) return e;
+  e = launch_kernel(kKindCmpLse, compressed_prefill_kernel<G, false>, grid, dim3(256), s, a.q,
+                    a.kc, static_cast<const bf16_t*>(a.vct), ldv, a.cu_q, a.cu_k, a.cu_c,
+                    a.kv_heads, a.scale_log2, a.lse2, static_cast<void*>(nullptr), 0,
+                    static_cast<float*>(nullptr), static_cast<float*>(nullptr), 0);
   if (e != hipSuccess) return e;
   return launch_kernel(kKindCmpProbs, compressed_prefill_kernel<G, true>, grid, dim3(256), s,
-                       a.q, a.kc, a.vc, a.cu_q, a.cu_k, a.cu_c, a.batch, a.rows_total,
+                       a.q, a.kc, static_cast<const bf16_t*>(a.vct), ldv, a.cu_q, a.cu_k, a.cu_c,
                        a.kv_heads, a.scale_log2, a.lse2, a.o_cmp, a.out_f32, a.lse_nat,
                        a.block_scores, a.nb_max);
 }
@@ -354,16 +557,19 @@ hipError_t launch_compressed_prefill(const CompressedPrefillArgs& a, hipStream_t
 
 template <int G>
 static hipError_t launch_win_g(const WindowPrefillArgs& a, hipStream_t s) {
-  const dim3 grid((a.rows_total + 3) / 4, a.kv_heads);
+  const dim3 grid = prefill_grid(a.max_seqlen_q, a.kv_heads, a.batch);
+  const int ldv = transposed_ld(a.max_seqlen_k);
+  hipError_t e = launch_transpose(a.v, a.cu_k, a.batch, a.kv_heads, a.max_seqlen_k, a.vt, s);
+  if (e != hipSuccess) return e;
+  const bf16_t* vt = a.vt;
   if (a.gates != nullptr)
     return launch_kernel(kKindWindow, window_prefill_kernel<G, true>, grid, dim3(256), s, a.q,
-                         a.k, a.v, a.cu_q, a.cu_k, a.batch, a.rows_total, a.kv_heads, a.window,
-                         a.scale_log2, a.out, a.out_f32, a.lse_nat, a.gates, a.o_cmp, a.o_sel);
+                         a.k, vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
+                         a.out_f32, a.lse_nat, a.gates, a.o_cmp, a.o_sel);
   return launch_kernel(kKindWindow, window_prefill_kernel<G, false>, grid, dim3(256), s, a.q, a.k,
-                       a.v, a.cu_q, a.cu_k, a.batch, a.rows_total, a.kv_heads, a.window,
-                       a.scale_log2, a.out, a.out_f32, a.lse_nat,
-                       static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
-                       static_cast<const float*>(nullptr));
+                       vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
+                       a.out_f32, a.lse_nat, static_cast<const float*>(nullptr),
+                       static_cast<const float*>(nullptr), static_cast<const float*>(nullptr));
 }
 
 hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s) {

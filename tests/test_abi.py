@@ -121,8 +121,8 @@ def test_decode_step_checks():
 
 def test_prefill_branch_checks():
     L = nsa.lib()
-    need = L.nsa_compressed_attn_workspace_size(100, 64)
-    assert need >= 100 * 64 * 4
+    need = L.nsa_compressed_attn_workspace_size(1, 100, 100, 64, 4, 32, 16)
+    assert need >= 100 * 64 * 4 + 4 * 128 * 64 * 2
     args = [FAKE, FAKE, FAKE, nsa.NSA_BF16, FAKE, nsa.NSA_F32, None, None, 0, FAKE, FAKE, FAKE,
             1, 100, 100, 64, 4, 128, 32, 16, 64, 0.0, FAKE, need, None]
     bad = list(args)
@@ -140,8 +140,13 @@ def test_prefill_branch_checks():
     bad = list(args)
     bad[15] = 3                   # 64 heads / 3 kv heads
     assert L.nsa_compressed_attn_fwd(*bad) == 2
+    wneed = L.nsa_window_attn_workspace_size(1, 100, 4)
+    assert wneed >= 4 * 128 * 128 * 2
     wargs = [FAKE, FAKE, FAKE, nsa.NSA_BF16, FAKE, nsa.NSA_BF16, None, FAKE, FAKE, 1, 100, 100, 64,
-             4, 128, 512, 0.0, None]
+             4, 128, 512, 0.0, FAKE, wneed, None]
+    bad = list(wargs)
+    bad[18] = wneed - 1           # workspace too small
+    assert L.nsa_window_attn_fwd(*bad) == 3
     bad = list(wargs)
     bad[15] = 0                   # empty window
     assert L.nsa_window_attn_fwd(*bad) == 1

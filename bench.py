@@ -61,7 +61,8 @@ COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "selected_attn_decode_nosa1b_counters.md")
 ATTN_SOURCES = ["sparse_attention_compress_amd/csrc/attn.hip",
-                "sparse_attention_compress_amd/csrc/common.h"]
+                "sparse_attention_compress_amd/csrc/common.h",
+                "sparse_attention_compress_amd/csrc/select_core.h"]
 
 
 def attn_source_hash() -> str:
@@ -200,8 +201,17 @@ def main():
           file=sys.stderr, flush=True)
 
     # per-kernel durations, from events recorded at each kernel's own start and end
-    kinds = {"logits_and_refresh": nsa.KERNEL_LOGITS, "block_scores_topk": nsa.KERNEL_BLOCK_SCORES,
-             "selected_attn": nsa.KERNEL_SELECTED_ATTN, "combine": nsa.KERNEL_COMBINE}
+    # bf16 decode with up to 1024 blocks and 256 selected blocks per sequence runs the
+    # selection inside the attention kernel (one launch per step fewer)
+    fused = (w.dtype == torch.bfloat16 and -(-max_len // 64) <= 1024 and w.topk <= 256)
+    if fused:
+        kinds = {"logits_and_refresh": nsa.KERNEL_LOGITS,
+                 "select_and_attn": nsa.KERNEL_SELECTED_ATTN, "combine": nsa.KERNEL_COMBINE}
+        attn_key = "select_and_attn"
+    else:
+        kinds = {"logits_and_refresh": nsa.KERNEL_LOGITS, "block_scores_topk": nsa.KERNEL_BLOCK_SCORES,
+                 "selected_attn": nsa.KERNEL_SELECTED_ATTN, "combine": nsa.KERNEL_COMBINE}
+        attn_key = "selected_attn"
     n_prof = max(1, args.profile_steps)
     evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(n_prof)] for name in kinds}
@@ -228,16 +238,23 @@ def main():
                 if blk >= 0:
                     sel_tokens += min(64, L - 64 * int(blk))
     elt = 2  # bf16
+    G = H // Hkv
+    if fused:
+        # the selection's inputs: logits, chunk (max, sum) pairs, block CIS maxima
+        sel_in = sum(Hkv * (G * c * 4 + -(-c // 64) * G * 8 + -(-L // 64) * 4)
+                     for L, c in zip(lengths, nc))
+    else:
+        sel_in = B * Hkv * w.topk * 4                 # block ids
     attn_bytes = (sel_tokens * D * elt * 2            # selected K and V rows
                   + 2 * B * H * D * elt               # queries in, outputs out
-                  + B * Hkv * w.topk * 4)             # block ids
+                  + sel_in)
     kc_elt = 4 if kc_dt == torch.float32 else 2
     score_bytes = (sum(nc) * Hkv * D * kc_elt         # compressed keys
                    + sum(nc) * Hkv * 4                # pooled CIS
                    + B * H * D * elt)                 # queries
     refresh_bytes = B * (32 * Hkv * D * elt + 32 * Hkv * 4 + Hkv * D * kc_elt + Hkv * 4)
     step_bytes = attn_bytes + score_bytes + refresh_bytes
-    attn_gbs = attn_bytes / (kern_us["selected_attn"] * 1e-6) / 1e9
+    attn_gbs = attn_bytes / (kern_us[attn_key] * 1e-6) / 1e9
 
     result = {
         "metric": METRIC,
@@ -261,7 +278,9 @@ def main():
             "layer_buffers_rotated": nl, "step": "one layer, whole batch, HIP-graph replay",
         },
         "roofline": {
-            "kernel": "selected_attn_kernel (decode, split over selected blocks)",
+            "kernel": ("select_attn_kernel (decode: block scores, top-k and attention over "
+                       "the selected blocks, split over blocks)" if fused else
+                       "selected_attn_kernel (decode, split over selected blocks)"),
             "bound": "hbm",
             "achieved": round(attn_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -269,7 +288,7 @@ def main():
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
             "traffic": counter_traffic(),
             "algorithmic_bytes_per_launch": attn_bytes,
-            "mean_kernel_us": round(kern_us["selected_attn"], 3),
+            "mean_kernel_us": round(kern_us[attn_key], 3),
             "source_hash": attn_source_hash(),
         },
         "kernel_us": {k_: round(v_, 3) for k_, v_ in kern_us.items()},

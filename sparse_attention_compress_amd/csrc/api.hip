@@ -330,9 +330,20 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
     a.refresh_k = p->k;
     a.refresh_cis = p->cis_pooled ? p->cis : nullptr;
   }
+  const nsa::AttnWs aws = nsa::attn_ws_carve(base + lay.attn, p->batch, p->kv_heads, G, p->topk, 1);
+  const int nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
+  if (p->dtype == NSA_BF16 && nb_max <= nsa::kFusedMaxBlocks && p->topk <= nsa::kFusedMaxSel) {
+    // logits, then selection and attention in one launch, then the merge
+    a.logits_only = 1;
+    a.indices = p->indices;  // debug output only: the ids stay in LDS
+    hipError_t e = nsa::launch_decode_scores(a, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+    e = nsa::launch_select_attn(a, p->k, p->v, p->cis_values ? p->cis : nullptr, p->out, aws,
+                                stream);
+    return hip_status(e, fn);
+  }
   hipError_t e = nsa::launch_decode_scores(a, stream);
   if (e != hipSuccess) return hip_status(e, fn);
-  const nsa::AttnWs aws = nsa::attn_ws_carve(base + lay.attn, p->batch, p->kv_heads, G, p->topk, 1);
   e = nsa::launch_selected_attn(p->q, p->k, p->v, p->dtype == NSA_BF16, idx, p->topk,
                                 p->cis_values ? p->cis : nullptr, p->out, nullptr, nullptr,
                                 p->cu_seqlens_k, p->batch, p->batch, p->heads, p->kv_heads, sl2,

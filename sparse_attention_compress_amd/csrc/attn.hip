@@ -22,6 +22,7 @@
 // use one workgroup per (row, kv head) and write the output directly.
 #include "common.h"
 #include "launch.h"
+#include "select_core.h"
 
 namespace nsa {
 
@@ -322,53 +323,65 @@ __device__ __forceinline__ uint32_t ld_u16(const bf16_t* p) {
   return uint32_t(*reinterpret_cast<const uint16_t*>(p));
 }
 
+// LDS of the wave merge at the end of attend_staged_blocks.
+struct MfmaAttnSmem {
+  float m_s[4][16], l_s[4][16];
+  float accx_s[4][32][kWave];  // [wave][tile element 4n + e][lane]
+};
+
+// Stage ids[s_begin, s_end) of one row that are valid for position t (id >= 0,
+// block start <= t) into ids_s, in order; returns the count through nv_s (set
+// by wave 0, read after the caller's barrier).
+__device__ __forceinline__ void stage_ids(const int* ids, int s_begin, int s_end, int t,
+                                          int* ids_s, int* nv_s) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) != 0) return;
+  int base = 0;
+  for (int s0 = s_begin; s0 < s_end; s0 += kWave) {
+    const int sl = s0 + lane;
+    const int id = sl < s_end ? ids[sl] : -1;
+    const bool ok = id >= 0 && id * kBlock <= t;
+    const unsigned long long mask = __ballot(ok);
+    const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+    if (ok && pos < kMaxWgSlots) ids_s[pos] = id;
+    base += __popcll(mask);
+  }
+  if (lane == 0) *nv_s = min(base, kMaxWgSlots);
+}
+
+// B operand of S^T = K Q^T: Q^T[dims 32i + 8 r4 .. +8][head c16] (zero past G).
+template <int G>
+__device__ __forceinline__ void load_q_operand(const bf16_t* __restrict__ q, size_t unit,
+                                               uint4 (&qb)[4]) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
+  const bf16_t* qp = q + (unit * G + min(c16, G - 1)) * kHeadDim + 8 * r4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qb[i] = ld16(qp + 32 * i);
+  if (c16 >= G) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// The G heads of `unit` (query position t of the sequence starting at kstart)
+// attend to the nv staged block ids; the result is written as split `split` of
+// n_split partial states (SPLIT) or as the output rows.
 template <int G, bool CIS, bool SPLIT>
-__global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
-    bf16_t* __restrict__ out, float* __restrict__ lse, const int* __restrict__ cu_q,
-    const int* __restrict__ cu_k, int batch, int kv_heads, float scale_log2, int bpw,
+__device__ __forceinline__ void attend_staged_blocks(
+    MfmaAttnSmem& sm, const int* ids_s, int nv, const uint4 (&qb)[4],
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ cis,
+    int kstart, int t, size_t unit, int kv, int kv_heads, float scale_log2, int split,
+    int n_split, bf16_t* __restrict__ out, float* __restrict__ lse,
     float2* __restrict__ part_ml, float* __restrict__ part_acc) {
   static_assert(G <= 16, "one MFMA column per query head");
   constexpr int D = kHeadDim;
   constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
-  __shared__ float m_s[4][16], l_s[4][16];
-  __shared__ float accx_s[4][32][kWave];  // [wave][tile element 4n + e][lane]
-  __shared__ int ids_s[kMaxWgSlots];
-  __shared__ int nv_s;
-
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
-  const int kv = blockIdx.y;
-  const int row = SPLIT ? int(blockIdx.z) : int(blockIdx.x);
-  const int split = SPLIT ? int(blockIdx.x) : 0;
-  int b, t;
-  attn_row_position(row, cu_q, cu_k, batch, b, t);
-  const int kstart = cu_k[b];
-  const size_t unit = size_t(row) * kv_heads + kv;
-  const int s_begin = split * bpw;
-  const int s_end = SPLIT ? min(k_sel, s_begin + bpw) : k_sel;
-
-  if (wave == 0) {
-    int base = 0;
-    for (int s0 = s_begin; s0 < s_end; s0 += kWave) {
-      const int sl = s0 + lane;
-      const int id = sl < s_end ? indices[unit * k_sel + sl] : -1;
-      const bool ok = id >= 0 && id * kBlock <= t;
-      const unsigned long long mask = __ballot(ok);
-      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
-      if (ok && pos < kMaxWgSlots) ids_s[pos] = id;
-      base += __popcll(mask);
-    }
-    if (lane == 0) nv_s = min(base, kMaxWgSlots);
-  }
-  // B operand of S^T = K Q^T: Q^T[dims 32i + 8 r4 .. +8][head c16] (zero past G)
-  uint4 qb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    qb[i] = c16 < G ? ld16(q + (unit * G + c16) * D + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
-  __syncthreads();
-  const int nv = nv_s;
+  float (&m_s)[4][16] = sm.m_s;
+  float (&l_s)[4][16] = sm.l_s;
+  float (&accx_s)[4][32][kWave] = sm.accx_s;
+  (void)tid;
 
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kbase = k + size_t(kstart) * rs + size_t(kv) * D;
@@ -494,7 +507,6 @@ __global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
     f[w] = (M == -INFINITY || f[w] == -INFINITY) ? 0.f : fast_exp2(f[w] - M);
     L += f[w] * l_s[w][c16];
   }
-  const int n_split = SPLIT ? int(gridDim.x) : 1;
   const size_t ps = unit * n_split + split;
 #pragma unroll
   for (int nn = 0; nn < 2; ++nn) {
@@ -529,6 +541,84 @@ __global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
       lse[unit * G + c16] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
   }
+}
+
+template <int G, bool CIS, bool SPLIT>
+__global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
+    bf16_t* __restrict__ out, float* __restrict__ lse, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int batch, int kv_heads, float scale_log2, int bpw,
+    float2* __restrict__ part_ml, float* __restrict__ part_acc) {
+  __shared__ MfmaAttnSmem sm;
+  __shared__ int ids_s[kMaxWgSlots];
+  __shared__ int nv_s;
+  const int kv = blockIdx.y;
+  const int row = SPLIT ? int(blockIdx.z) : int(blockIdx.x);
+  const int split = SPLIT ? int(blockIdx.x) : 0;
+  int b, t;
+  attn_row_position(row, cu_q, cu_k, batch, b, t);
+  const size_t unit = size_t(row) * kv_heads + kv;
+  const int s_begin = split * bpw;
+  const int s_end = SPLIT ? min(k_sel, s_begin + bpw) : k_sel;
+  stage_ids(indices + unit * k_sel, s_begin, s_end, t, ids_s, &nv_s);
+  uint4 qb[4];
+  load_q_operand<G>(q, unit, qb);
+  __syncthreads();
+  attend_staged_blocks<G, CIS, SPLIT>(sm, ids_s, nv_s, qb, k, v, cis, cu_k[b], t, unit, kv,
+                                      kv_heads, scale_log2, split, SPLIT ? int(gridDim.x) : 1,
+                                      out, lse, part_ml, part_acc);
+}
+
+// Decode: score the blocks, select and attend in one launch.  Every workgroup
+// of a (sequence, kv head) runs the same selection (identical inputs, so
+// identical ids), then attends to its own run of `bpw` selected blocks and
+// writes a partial state; split 0 also writes the debug outputs.  Grid
+// (splits, kv heads, sequences).
+template <int G, bool CIS>
+__global__ __launch_bounds__(256) void select_attn_kernel(
+    const float* __restrict__ logits, const float2* __restrict__ part,
+    const float* __restrict__ cisb, float cis_weight, const int* __restrict__ cu_k,
+    const int* __restrict__ cu_c, int kv_heads, int nc_max, int ldc, int nb_max,
+    int n_chunk_max, int ldb, int topk, int n_init, int n_local,
+    float* __restrict__ block_scores, int* __restrict__ indices, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ cis,
+    float scale_log2, int bpw, float2* __restrict__ part_ml, float* __restrict__ part_acc) {
+  using Sel = SelCfg<256, kFusedMaxBlocks>;
+  __shared__ union {
+    SelShared<256, kFusedMaxBlocks> sel;
+    MfmaAttnSmem att;
+  } U;
+  __shared__ int ids_all[kFusedMaxSel];
+  __shared__ int ids_s[kMaxWgSlots];
+  __shared__ int nv_s;
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int kstart = cu_k[b];
+  const int len = cu_k[b + 1] - kstart;
+  const int t = len - 1;
+  const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
+  const int nvis = min(cu_c[b + 1] - cu_c[b], full_windows_dev(len));
+  const size_t unit = size_t(b) * kv_heads + kv;
+  const bool lead = split == 0;
+  uint4 qb[4];
+  load_q_operand<G>(q, unit, qb);  // in flight during the selection
+  float sc[Sel::kPer];
+  block_scores_from_logits<G, 256, kFusedMaxBlocks>(U.sel, sc, logits, part, cisb, cis_weight,
+                                                    unit, nvis, nb, n_chunk_max, ldc, ldb, nb_max,
+                                                    nc_max, lead ? block_scores : nullptr, nullptr);
+  __syncthreads();
+  topk_select<256, kFusedMaxBlocks>(U.sel, sc, sel_geometry(t, nb, topk, n_init, n_local), topk,
+                                    ids_all);
+  __syncthreads();
+  if (lead && indices != nullptr)
+    for (int i = tid; i < topk; i += 256) indices[unit * topk + i] = ids_all[i];
+  const int s_begin = split * bpw;
+  stage_ids(ids_all, s_begin, min(topk, s_begin + bpw), t, ids_s, &nv_s);
+  __syncthreads();
+  attend_staged_blocks<G, CIS, true>(U.att, ids_s, nv_s, qb, k, v, cis, kstart, t, unit, kv,
+                                     kv_heads, scale_log2, split, int(gridDim.x), nullptr,
+                                     nullptr, part_ml, part_acc);
 }
 
 // Merge the per-split partial states of one (row, kv head, query head): grid
@@ -676,6 +766,50 @@ hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int
   }
   if (cis) return launch_attn_t<float, true>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s, out_f32);
   return launch_attn_t<float, false>(G, q, k, v, indices, k_sel, cis, out, lse, cu_q, cu_k, batch, rows_total, kv_heads, scale_log2, ws, s, out_f32);
+}
+
+template <int G, bool CIS>
+static hipError_t launch_select_attn_g(const DecodeScoresArgs& a, const void* k, const void* v,
+                                       const float* cis_values, void* out, const AttnWs& ws,
+                                       hipStream_t s) {
+  const ScoreDims d = score_dims(a.max_seqlen_k);
+  const int bpw = attn_split_blocks(a.batch, a.kv_heads, a.topk);
+  const int n_split = (a.topk + bpw - 1) / bpw;
+  const float* cisb = a.cis_pooled != nullptr ? a.ws.cisb : nullptr;
+  hipError_t e = launch_kernel(
+      kKindAttn, select_attn_kernel<G, CIS>, dim3(n_split, a.kv_heads, a.batch), dim3(256), s,
+      static_cast<const float*>(a.ws.logits), static_cast<const float2*>(a.ws.part), cisb,
+      a.cis_weight, a.cu_k, a.cu_c, a.kv_heads, d.nc_max, d.ldc, d.nb_max, d.n_chunk_max, d.ldb,
+      a.topk, a.n_init, a.n_local, a.block_scores, a.indices, static_cast<const bf16_t*>(a.q),
+      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), cis_values, a.scale_log2, bpw,
+      ws.part_ml, ws.part_acc);
+  if (e != hipSuccess) return e;
+  return launch_kernel(kKindCombine, combine_kernel<bf16_t>, dim3(a.batch * a.kv_heads, G),
+                       dim3(kHeadDim), s, static_cast<const float2*>(ws.part_ml),
+                       static_cast<const float*>(ws.part_acc), static_cast<bf16_t*>(out),
+                       static_cast<float*>(nullptr), n_split, G);
+}
+
+template <bool CIS>
+static hipError_t launch_select_attn_c(int G, const DecodeScoresArgs& a, const void* k,
+                                       const void* v, const float* cis_values, void* out,
+                                       const AttnWs& ws, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_select_attn_g<1, CIS>(a, k, v, cis_values, out, ws, s);
+    case 2: return launch_select_attn_g<2, CIS>(a, k, v, cis_values, out, ws, s);
+    case 4: return launch_select_attn_g<4, CIS>(a, k, v, cis_values, out, ws, s);
+    case 8: return launch_select_attn_g<8, CIS>(a, k, v, cis_values, out, ws, s);
+    case 16: return launch_select_attn_g<16, CIS>(a, k, v, cis_values, out, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_select_attn(const DecodeScoresArgs& a, const void* k, const void* v,
+                              const float* cis_values, void* out, const AttnWs& ws,
+                              hipStream_t s) {
+  const int G = a.heads / a.kv_heads;
+  if (cis_values != nullptr) return launch_select_attn_c<true>(G, a, k, v, cis_values, out, ws, s);
+  return launch_select_attn_c<false>(G, a, k, v, cis_values, out, ws, s);
 }
 
 }  // namespace nsa

@@ -146,6 +146,37 @@ __device__ __forceinline__ float wave_reduce(float x, Op op) {
   return cross32(x, op);
 }
 __device__ __forceinline__ float wave_max(float x) { return wave_reduce(x, OpMax()); }
+// Unsigned minimum / maximum over the whole wave (result in all 64 lanes).
+struct OpUMin {
+  __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct OpUMax {
+  __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
+  x = op(x, uint32_t(dpp<kDppQuadXor1>(int(x))));
+  x = op(x, uint32_t(dpp<kDppQuadXor2>(int(x))));
+  x = op(x, uint32_t(dpp<kDppRowHalfMirror>(int(x))));
+  x = op(x, uint32_t(dpp<kDppRowMirror>(int(x))));
+  auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(r16[0], r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(r32[0], r32[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return wave_reduce_u32(x, OpUMin()); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) { return wave_reduce_u32(x, OpUMax()); }
+
+// Integer sum over the whole wave (result in all 64 lanes).
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  x = cross16i(x, OpSumI());
+  return cross32i(x, OpSumI());
+}
+
 // Integer minimum over the whole wave (result in all 64 lanes).
 __device__ __forceinline__ int wave_min_i(int x) {
   const OpMinI op;

@@ -25,6 +25,10 @@ constexpr int kBlocksPerWG = 256;
 constexpr int kMaxSortBlocks = 4096;
 // Partial states one decode (row, kv head) may be split into.
 constexpr int kMaxSplits = 64;
+// The decode kernel that selects and attends in one launch handles sequences of
+// up to this many blocks and up to this many selected blocks.
+constexpr int kFusedMaxBlocks = 1024;
+constexpr int kFusedMaxSel = 256;
 
 // Kernel kinds that a profiling request can target.
 enum KernelKind {
@@ -69,11 +73,16 @@ hipError_t launch_mean_pool(const void* x, int x_bf16, void* y, int y_bf16, cons
 
 // Scoring workspace carve-up (decode rows).
 struct ScoresWs {
-  float* logits;  // [batch, kv_heads, G, n_chunk_max*64] scaled log2-domain logits
+  float* logits;  // [batch, kv_heads, G, n_chunk_max*64] exp2(logit - chunk max), log2 domain
   float2* part;   // [batch, kv_heads, n_chunk_max, G] chunk (max, sum of exp2)
   float* cisb;    // [batch, kv_heads, n_chunk_max*16+1] per-block CIS maxima
 };
 size_t scores_ws_bytes(int batch, int kv_heads, int group, int max_seqlen_k);
+// Layout of the scoring workspace for sequences of up to max_seqlen_k tokens.
+struct ScoreDims {
+  int nc_max, nb_max, n_chunk_max, ldc, ldb;
+};
+ScoreDims score_dims(int max_seqlen_k);
 ScoresWs scores_ws_carve(void* base, int batch, int kv_heads, int group, int max_seqlen_k);
 
 struct DecodeScoresArgs {
@@ -94,6 +103,7 @@ struct DecodeScoresArgs {
   int topk, n_init, n_local;
   const void* refresh_k;       // nullable: recompute the newest window from these keys
   const float* refresh_cis;    // nullable: and the newest pooled CIS from these scores
+  int logits_only;             // launch the logits kernel only (the selection runs elsewhere)
 };
 hipError_t launch_decode_scores(const DecodeScoresArgs& a, hipStream_t s);
 
@@ -116,6 +126,12 @@ hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int
                                 float* lse, const int* cu_q, const int* cu_k, int batch,
                                 int rows_total, int heads, int kv_heads, float scale_log2,
                                 const AttnWs& ws, hipStream_t s, float* out_f32 = nullptr);
+
+// Decode: selection and attention in one launch (bf16; nb_max <= kFusedMaxBlocks,
+// topk <= kFusedMaxSel), after the logits kernel, then the merge of the splits.
+hipError_t launch_select_attn(const DecodeScoresArgs& a, const void* k, const void* v,
+                              const float* cis_values, void* out, const AttnWs& ws,
+                              hipStream_t s);
 
 // Prefill branches (bf16, prefill rows).
 struct CompressedPrefillArgs {

@@ -14,7 +14,8 @@
 //   (four v_mfma_f32_16x16x32_bf16 per wave when both are bf16, else thirty-two
 //   v_mfma_f32_16x16x4_f32 in full fp32).  Each compressed key is read from HBM
 //   once for the whole GQA group.
-//   Outputs: log2-domain logits, a per-chunk (max, sum of exp2) per head, and the
+//   Outputs: per window and head exp2(logit - chunk max) (log2-domain logits), the
+//   per-chunk (max, sum of exp2) per head, and the
 //   CIS maximum of the blocks the chunk owns (blocks 16j..16j+15, the last chunk
 //   also block 16*n_chunks).  The workgroup owning the newest window can first
 //   recompute that window of the K_c and pooled-CIS caches (decode refresh).
@@ -33,15 +34,12 @@
 // workgroup: each hand-off is a kernel boundary.
 #include "common.h"
 #include "launch.h"
+#include "select_core.h"
 
 namespace nsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int full_windows_dev(int len) {
-  return len >= kKernel ? (len - kKernel) / kStride + 1 : 0;
-}
 
 __device__ __forceinline__ void row_position(int row, const int* __restrict__ cu_q,
                                              const int* __restrict__ cu_k, int batch, int& b,
@@ -223,16 +221,20 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
     sv[e] = cw0 + e < nvis ? sacc[e] * scale_log2 : -INFINITY;
     mx = fmaxf(mx, sv[e]);
   }
-  if (c16 < G)
-    *reinterpret_cast<float4*>(lrow + size_t(c16) * ldc + cw0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
   mx = cross32(cross16(mx, OpMax()), OpMax());
   if (r4 == 0) red_s[0][wave][c16] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(red_s[0][0][c16], red_s[0][1][c16]),
                         fmaxf(red_s[0][2][c16], red_s[0][3][c16]));
-  float l = 0.f;
+  // stored per window: exp2(logit - chunk max), 0 for windows not visible
+  float ev[4], l = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) l += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - M);
+  for (int e = 0; e < 4; ++e) {
+    ev[e] = sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - M);
+    l += ev[e];
+  }
+  if (c16 < G)
+    *reinterpret_cast<float4*>(lrow + size_t(c16) * ldc + cw0) = make_float4(ev[0], ev[1], ev[2], ev[3]);
   l = cross32(cross16(l, OpSum()), OpSum());
   if (r4 == 0) red_s[1][wave][c16] = l;
   __syncthreads();
@@ -244,230 +246,7 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
 // ------------------------------------------------------------ kernel 2: select
 
 constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kBins = 1024;
-constexpr int kCandMax = kSelThreads;  // candidates ranked exactly, one per thread
-constexpr int kWinLds = 4 * kMaxSortBlocks;  // every window of the longest sequence
-constexpr int kBlkPer = kMaxSortBlocks / kSelThreads;  // slabs: thread tid owns ids tid + 512u
-static_assert(kBlkPer * kSelWaves == kWave, "one lane per (slab, wave) count");
-
-struct SelShared {
-  float pg[kWinLds];                  // group probabilities of the windows
-  float sc[kMaxSortBlocks];           // scores and states, staged only for the
-  unsigned char st[kMaxSortBlocks];   //   exact fallback ranking
-  int hist[kBins];
-  float cand_sc[kCandMax];            // candidates of the exact ranking, id order
-  unsigned char cand_keep[kCandMax];
-  int cnt[2][kWave];                  // per (slab, wave) counts of the ordered scans
-  float wred[2][kSelWaves][16];
-  int misc[4];
-};
-
-// Positions, in ascending id order, of the flagged ids (thread tid, slab u owns id
-// tid + 512u); returns the number flagged, in every thread.  One barrier; `cnt`
-// must not be written again before another barrier.
-__device__ __forceinline__ int ordered_positions(const bool (&flag)[kBlkPer], int (&pos)[kBlkPer],
-                                                 int* cnt) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) {
-    const unsigned long long m = __ballot(flag[u]);
-    pos[u] = __popcll(m & below);
-    if (lane == 0) cnt[u * kSelWaves + wave] = __popcll(m);
-  }
-  __syncthreads();
-  const int c = cnt[lane];  // lane = slab * waves + wave: the id order of the runs
-  const int incl = wave_inclusive_scan(c);
-  const int excl = incl - c;
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) pos[u] += __builtin_amdgcn_readlane(excl, u * kSelWaves + wave);
-  return __builtin_amdgcn_readlane(incl, kWave - 1);
-}
-
-__device__ __forceinline__ void block_minmax(float lo, float hi, SelShared& S, float& vmin,
-                                             float& vmax) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  lo = -wave_max(-lo);
-  hi = wave_max(hi);
-  if (lane == 0) {
-    S.wred[0][wave][0] = lo;
-    S.wred[1][wave][0] = hi;
-  }
-  __syncthreads();
-  vmin = INFINITY;
-  vmax = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    vmin = fminf(vmin, S.wred[0][w][0]);
-    vmax = fmaxf(vmax, S.wred[1][w][0]);
-  }
-}
-
-__device__ __forceinline__ int bin_of(float v, float base, float scale) {
-  return min(kBins - 1, max(0, int((v - base) * scale)));
-}
-
-// Top-k over the eligible ids with scores sc and states st held in registers
-// (0 out, 1 chosen, 2 free candidate); kf free places to fill among n_free
-// candidates whose scores lie in [lo, hi] per thread.  Writes topk ascending ids
-// (-1 padded) to out.
-__device__ __forceinline__ void topk_select(SelShared& S, const float (&sc)[kBlkPer],
-                                            int (&st)[kBlkPer], int n_elig, int kf, int n_free,
-                                            float lo, float hi, int topk,
-                                            int* __restrict__ out) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  float vmin, vmax;
-  block_minmax(lo, hi, S, vmin, vmax);
-  int need = kf;
-  bool take_rest = false;  // every remaining candidate is chosen
-  bool by_index = false;   // all remaining scores equal: the lowest ids are chosen
-  bool by_rank = false;    // few candidates: exact rank among them
-  bool by_scan = false;    // otherwise: exact rank against every candidate
-  if (kf > 0 && kf < n_free) {
-    float base = vmin, width = vmax - vmin;
-    for (int level = 0; level < 12; ++level) {
-      const float scale = float(kBins) / width;
-      if (width == 0.f) {
-        by_index = true;
-        break;
-      }
-      if (!isfinite(width) || !isfinite(scale) || !(width > 0.f)) {
-        by_scan = true;
-        break;
-      }
-      // histogram of the candidates over [base, base + width)
-#pragma unroll
-      for (int u = 0; u < kBlkPer; ++u)
-        if (st[u] == 2) atomicAdd(&S.hist[bin_of(sc[u], base, scale)], 1);
-      __syncthreads();
-      if (tid < kWave) {
-        if (tid == 0) {  // found below; defaults keep every later step in range
-          S.misc[0] = 0;
-          S.misc[1] = 0;
-          S.misc[2] = need;
-        }
-        // lane l owns bins 1023-16l .. 1008-16l (descending scores)
-        int cnt[16], tot = 0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          cnt[e] = S.hist[kBins - 1 - 16 * lane - e];
-          tot += cnt[e];
-        }
-        const int incl = wave_inclusive_scan(tot);
-        int above = incl - tot;  // candidates in higher bins
-        if (above < need && need <= incl) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            if (above < need && need <= above + cnt[e]) {
-              S.misc[0] = kBins - 1 - 16 * lane - e;
-              S.misc[1] = above;
-              S.misc[2] = cnt[e];
-            }
-            above += cnt[e];
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) S.hist[kBins - 1 - 16 * lane - e] = 0;
-      }
-      __syncthreads();
-      const int bstar = S.misc[0], above = S.misc[1], m = S.misc[2];
-#pragma unroll
-      for (int u = 0; u < kBlkPer; ++u) {
-        if (st[u] == 2) {
-          const int bin = bin_of(sc[u], base, scale);
-          if (bin != bstar) st[u] = bin > bstar ? 1 : 0;
-        }
-      }
-      need -= above;
-      if (m == need) {
-        take_rest = true;
-        break;
-      }
-      if (m <= kCandMax) {
-        by_rank = true;
-        break;
-      }
-      base = base + float(bstar) / scale;
-      width = 1.f / scale;
-    }
-    if (!take_rest && !by_rank && !by_index) by_scan = true;  // refinement did not settle
-  }
-  if (by_scan) {
-    // each remaining candidate counts the candidates that beat it
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u) {
-      const int i = tid + kSelThreads * u;
-      if (i < n_elig) {
-        S.sc[i] = sc[u];
-        S.st[i] = static_cast<unsigned char>(st[u]);
-      }
-    }
-    __syncthreads();
-    int keep[kBlkPer];
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u) {
-      const int i = tid + kSelThreads * u;
-      keep[u] = 0;
-      if (st[u] == 2) {
-        const float v = sc[u];
-        int rank = 0;
-        for (int o = 0; o < n_elig; ++o) {
-          if (S.st[o] != 2) continue;
-          const float w = S.sc[o];
-          rank += (w > v || (w == v && o < i)) ? 1 : 0;
-        }
-        keep[u] = rank < need ? 1 : 0;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u)
-      if (st[u] == 2) st[u] = keep[u];
-  }
-  if (by_rank || by_index) {
-    bool f[kBlkPer];
-    int pos[kBlkPer];
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u) f[u] = st[u] == 2;
-    const int m = min(ordered_positions(f, pos, S.cnt[0]), kCandMax);
-    if (by_index) {
-#pragma unroll
-      for (int u = 0; u < kBlkPer; ++u)
-        if (f[u]) st[u] = pos[u] < need ? 1 : 0;
-    } else {
-#pragma unroll
-      for (int u = 0; u < kBlkPer; ++u)
-        if (f[u] && pos[u] < kCandMax) S.cand_sc[pos[u]] = sc[u];
-      __syncthreads();
-      if (tid < m) {
-        // candidates sit in id order, so the lower id of a tie is the lower slot
-        const float v = S.cand_sc[tid];
-        int rank = 0;
-        for (int c = 0; c < m; ++c) {
-          const float w = S.cand_sc[c];
-          rank += (w > v || (w == v && c < tid)) ? 1 : 0;
-        }
-        S.cand_keep[tid] = rank < need ? 1 : 0;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < kBlkPer; ++u)
-        if (f[u]) st[u] = (pos[u] < m && S.cand_keep[pos[u]]) ? 1 : 0;
-    }
-  }
-  // ordered compaction of the chosen ids
-  bool f[kBlkPer];
-  int pos[kBlkPer];
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) f[u] = st[u] == 1 || (take_rest && st[u] == 2);
-  const int total = ordered_positions(f, pos, S.cnt[1]);
-  // writes stay inside the row's topk slots even if the count were wrong
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u)
-    if (f[u] && pos[u] < topk) out[pos[u]] = tid + kSelThreads * u;
-  for (int i = max(0, total) + tid; i < topk; i += kSelThreads) out[i] = -1;
-  (void)lane;
-}
+using BigSel = SelCfg<kSelThreads, kMaxSortBlocks>;
 
 template <int G, bool FROM_LOGITS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
@@ -477,156 +256,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     float* __restrict__ block_scores, float* __restrict__ window_probs, int kv_heads,
     int nc_max, int ldc, int nb_max, int n_chunk_max, int ldb, int* __restrict__ indices,
     int topk, int n_init, int n_local) {
-  __shared__ SelShared S;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ SelShared<kSelThreads, kMaxSortBlocks> S;
+  const int tid = threadIdx.x;
   const int row = blockIdx.x, kv = blockIdx.y;
   int b, t;
   row_position(row, cu_q, cu_k, batch, b, t);
   const int len = cu_k[b + 1] - cu_k[b];
   const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
-  const int n_slab = (nb + kSelThreads - 1) / kSelThreads;  // uniform
   const size_t unit = size_t(row) * kv_heads + kv;
-  // selection geometry
-  const int n_elig = t >= 0 ? min(nb, t / kBlock + 1) : 0;
-  const int f_init = min(n_init, n_elig);
-  const int f_loc = max(max(0, n_elig - n_local), f_init);  // forced local: [f_loc, n_elig)
-  const int n_forced = f_init + (n_elig - f_loc);
-  const int n_free = n_elig - n_forced;
-  const int kf = max(0, min(topk - n_forced, n_free));
-  const int free_mark = kf == n_free ? 1 : (kf == 0 ? 0 : 2);
-  for (int i = tid; i < kBins; i += kSelThreads) S.hist[i] = 0;
-
-  float sc[kBlkPer];
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) sc[u] = 0.f;
+  float sc[BigSel::kPer];
   if constexpr (FROM_LOGITS) {
     const int nc = cu_c[b + 1] - cu_c[b];
     const int nvis = min(nc, full_windows_dev(len));
-    const int n_chunk = (nvis + kChunkWindows - 1) / kChunkWindows;
-    // ---- every load at once: the chunk (max, sum) pairs, the first round of
-    // logits and the block CIS maxima.  Counts of load rounds are uniform;
-    // indices inside a round are clamped into range and the values masked.
-    constexpr int kPairs = 4096 / kSelThreads;
-    const int n_pairs = n_chunk * G;
-    const int n_pu = (n_pairs + kSelThreads - 1) / kSelThreads;
-    const float2* prow = part + unit * n_chunk_max * G;
-    float2 ml[kPairs];
-#pragma unroll
-    for (int u = 0; u < kPairs; ++u)
-      ml[u] = u < n_pu ? prow[min(tid + kSelThreads * u, n_pairs - 1)] : make_float2(-INFINITY, 0.f);
-    const float* lrow = logits + unit * G * ldc;
-    const int cmax = max(nvis - 1, 0);
-    const int n_wu = min(4, (nvis + kSelThreads - 1) / kSelThreads);  // first round only
-    float lg[4][G];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = min(tid + kSelThreads * u, cmax);
-#pragma unroll
-      for (int h = 0; h < G; ++h) lg[u][h] = u < n_wu ? lrow[size_t(h) * ldc + c] : 0.f;
-    }
-    float cv[kBlkPer];
-    const bool with_cis = cisb != nullptr && n_chunk > 0;
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u)
-      cv[u] = (with_cis && u < n_slab) ? cisb[unit * ldb + min(tid + kSelThreads * u, ldb - 1)] : 0.f;
-
-    // per-head softmax normaliser from the chunk pairs; pair i of this thread
-    // belongs to head i % G == tid % G
-    float m = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kPairs; ++u)
-      m = fmaxf(m, tid + kSelThreads * u < n_pairs ? ml[u].x : -INFINITY);
-    m = column_reduce<G>(m, OpMax());
-    if (lane < G) S.wred[0][wave][lane] = m;
-    __syncthreads();
-    float Mh = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) Mh = fmaxf(Mh, S.wred[0][w][tid % G]);
-    float l = 0.f;
-#pragma unroll
-    for (int u = 0; u < kPairs; ++u)
-      l += (tid + kSelThreads * u < n_pairs && ml[u].x != -INFINITY)
-               ? ml[u].y * fast_exp2(ml[u].x - Mh) : 0.f;
-    l = column_reduce<G>(l, OpSum());
-    if (lane < G) S.wred[1][wave][lane] = l;
-    __syncthreads();
-    float M[G], invL[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mm = -INFINITY, ll = 0.f;
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) {
-        mm = fmaxf(mm, S.wred[0][w][h]);
-        ll += S.wred[1][w][h];
-      }
-      M[h] = mm;
-      invL[h] = 1.f / ll;
-    }
-    // group probabilities of every visible window into LDS, 4 windows per thread
-    // per round; rounds after the first load their logits here
-    for (int r0 = 0; r0 < nvis; r0 += 4 * kSelThreads) {
-      if (r0 > 0) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = min(r0 + tid + kSelThreads * u, cmax);
-#pragma unroll
-          for (int h = 0; h < G; ++h) lg[u][h] = lrow[size_t(h) * ldc + c];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = r0 + tid + kSelThreads * u;
-        float pg = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) pg += fast_exp2(lg[u][h] - M[h]) * invL[h];
-        if (c < nvis) S.pg[c] = pg;
-      }
-    }
-    __syncthreads();
-    // blocks up to 16 * n_chunk carry a CIS maximum from the logits kernel
-    const int owned = with_cis ? min(nb, 16 * n_chunk + 1) : 0;
-#pragma unroll
-    for (int u = 0; u < kBlkPer; ++u) {
-      const int i = tid + kSelThreads * u;
-      if (u < n_slab) {
-        float pm = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 5; ++e) {
-          const int c = 4 * i - 1 + e;
-          const float pg = S.pg[min(max(c, 0), kWinLds - 1)];
-          if (c >= 0 && c < nvis) pm = fmaxf(pm, pg);
-        }
-        float s = pm == -INFINITY ? 0.f : pm;
-        if (cisb != nullptr) s += cis_weight * (i < owned ? cv[u] : 0.f);
-        sc[u] = s;
-        if (block_scores != nullptr && i < nb) block_scores[unit * nb_max + i] = s;
-      }
-    }
-    if (block_scores != nullptr)
-      for (int i = nb + tid; i < nb_max; i += kSelThreads) block_scores[unit * nb_max + i] = 0.f;
-    if (window_probs != nullptr)
-      for (int c = tid; c < nc_max; c += kSelThreads)
-        window_probs[unit * nc_max + c] = c < nvis ? S.pg[c] : 0.f;
+    block_scores_from_logits<G, kSelThreads, kMaxSortBlocks>(
+        S, sc, logits, part, cisb, cis_weight, unit, nvis, nb, n_chunk_max, ldc, ldb, nb_max,
+        nc_max, block_scores, window_probs);
   } else {
+    const int n_slab = (nb + kSelThreads - 1) / kSelThreads;  // uniform
 #pragma unroll
-    for (int u = 0; u < kBlkPer; ++u)
-      if (u < n_slab) sc[u] = block_scores[unit * nb_max + min(tid + kSelThreads * u, nb - 1)];
+    for (int u = 0; u < BigSel::kPer; ++u)
+      sc[u] = u < n_slab ? block_scores[unit * nb_max + min(tid + kSelThreads * u, nb - 1)] : 0.f;
   }
   if (indices == nullptr) return;
-
-  int st[kBlkPer];
-  float lo = INFINITY, hi = -INFINITY;  // free-score range seen by this thread
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) {
-    const int i = tid + kSelThreads * u;
-    const bool forced = i < f_init || (i >= f_loc && i < n_elig);
-    st[u] = i >= n_elig ? 0 : (forced ? 1 : free_mark);
-    if (i < n_elig && !forced) {
-      lo = fminf(lo, sc[u]);
-      hi = fmaxf(hi, sc[u]);
-    }
-  }
-  topk_select(S, sc, st, n_elig, kf, n_free, lo, hi, topk, indices + unit * topk);
+  __syncthreads();
+  topk_select<kSelThreads, kMaxSortBlocks>(S, sc, sel_geometry(t, nb, topk, n_init, n_local), topk,
+                                            indices + unit * topk);
 }
 
 // ------------------------------------------------- kernel 3: select, one wave per row
@@ -710,10 +364,7 @@ static int n_windows_max(int max_seqlen_k) {
   return max_seqlen_k >= kKernel ? (max_seqlen_k - kKernel) / kStride + 1 : 0;
 }
 
-struct ScoreDims {
-  int nc_max, nb_max, n_chunk_max, ldc, ldb;
-};
-static ScoreDims score_dims(int max_seqlen_k) {
+ScoreDims score_dims(int max_seqlen_k) {
   ScoreDims d;
   d.nc_max = n_windows_max(max_seqlen_k);
   d.nb_max = (max_seqlen_k + kBlock - 1) / kBlock;
@@ -758,6 +409,7 @@ static hipError_t launch_scores_g(const DecodeScoresArgs& a, hipStream_t s) {
         a.scale_log2, static_cast<const TQ*>(a.refresh_k), a.refresh_cis);
     if (e != hipSuccess) return e;
   }
+  if (a.logits_only) return hipSuccess;
   return launch_kernel(kKindBlockScores, select_kernel<G, true>, dim3(a.batch, a.kv_heads),
                        dim3(kSelThreads), s, static_cast<const float*>(a.ws.logits),
                        static_cast<const float2*>(a.ws.part), static_cast<const float*>(cisb),

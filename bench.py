@@ -59,7 +59,7 @@ def parse():
 
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "selected_attn_decode_nosa1b_counters.md")
+                            "select_attn_decode_nosa1b_counters.md")
 ATTN_SOURCES = ["sparse_attention_compress_amd/csrc/attn.hip",
                 "sparse_attention_compress_amd/csrc/common.h",
                 "sparse_attention_compress_amd/csrc/select_core.h"]

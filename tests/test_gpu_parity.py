@@ -403,3 +403,73 @@ def test_decode_step_append_refreshes_last_window():
     assert torch.equal(d["kc"][last], good_kc)
     assert torch.equal(d["cp"][last], good_cp)
     _check_decode("append", d, out, bs, idx, 16, 1, 2, True, False, atol=2e-2)
+
+
+# ----------------------------------------------------------------------------- full sizes
+
+def _workload_decode_inputs(w, kc_dtype):
+    q = W.decode_query(w, DEV)
+    k, v = W.keys_values(w, DEV)
+    cis = W.cis_scores(w, DEV)
+    nc = [oracle.n_windows(L, 32, 16) for L in w.lengths]
+    cu_k, cu_c = cu(w.lengths), cu(nc)
+    kc = torch.zeros((sum(nc), w.kv_heads, 128), dtype=kc_dtype, device=DEV)
+    cp = torch.zeros((sum(nc), w.kv_heads), dtype=F32, device=DEV)
+    nsa.nsa_compress_k(k, kc, cu_k, cu_c, max(nc))
+    nsa.nsa_cis_mean_pool_varlen(cis, cp, cu_k, cu_c, max(nc))
+    return dict(q=q, k=k, v=v, cis=cis, kc=kc, cp=cp, cu_k=cu_k, cu_c=cu_c, nc=nc,
+                lengths=list(w.lengths), H=w.heads, H_kv=w.kv_heads)
+
+
+@pytest.mark.parametrize("kc_dtype", [F32, BF16])
+def test_decode_step_nosa1b_full_size(kc_dtype):
+    """The batched decode workload at full size (8 sequences of 8K-32K tokens, CIS
+    fused into the block scores, top-64 with 1 init and 16 local blocks), through
+    the same single-kernel select-and-attend path the throughput run times; every
+    (sequence, kv head) is checked."""
+    w = W.nosa1b_decode()
+    d = _workload_decode_inputs(w, kc_dtype)
+    log(f"decode step full size {w.name} kc={kc_dtype}")
+    out, bs, idx = _run_decode_step(d, w.topk, w.n_init, w.n_local, True, False, append=True)
+    _check_decode("nosa1b_full", d, out, bs, idx, w.topk, w.n_init, w.n_local, True, False,
+                  atol=2e-2)
+
+
+def test_decode_step_cis_values_full_size():
+    """The long-context CIS-valued decode at full size: 4 sequences of 131072 tokens
+    (2048 blocks each, beyond the single-kernel path's block limit, so the
+    separate select and attention kernels run)."""
+    w = W.cis_decode()
+    d = _workload_decode_inputs(w, F32)
+    log(f"decode step full size {w.name}")
+    out, bs, idx = _run_decode_step(d, w.topk, w.n_init, w.n_local, True, True, append=True)
+    _check_decode("cis_full", d, out, bs, idx, w.topk, w.n_init, w.n_local, True, True,
+                  atol=2e-2)
+
+
+def test_selected_attn_prefill_full_size_sampled_rows():
+    """Given-index selected attention at full size (8 x 16384 rows), sampled rows."""
+    w = W.selected_prefill()
+    q = W.prefill_query(w, DEV)
+    k, v = W.keys_values(w, DEV)
+    idx = W.given_block_indices(w, DEV)
+    cu_k = cu(w.lengths)
+    out = torch.full_like(q, float("nan"))
+    log(f"prefill selected attn full size {w.name}")
+    nsa.nsa_selected_attn_fwd(q, k, v, idx, cu_k, max(w.lengths), out, cu_seqlens_q=cu_k)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    cu_np = _cu_np(cu_k)
+    picks = [(0, 0), (0, 63), (0, 64), (1, 1000), (3, 8191), (5, 16320), (7, 16383)]
+    picks += [(b, int(t)) for b in range(8) for t in np.linspace(100, 16380, 5).round()]
+    rows = [(int(cu_np[b]) + t, t) for b, t in picks]
+    ref = np.zeros((len(rows), w.heads, 128))
+    got = np.zeros_like(ref)
+    idxn = idx.cpu().numpy()
+    for i, (r, t) in enumerate(rows):
+        b = int(np.searchsorted(cu_np, r, side="right") - 1)
+        s0, L = cu_np[b], cu_np[b + 1] - cu_np[b]
+        ref[i] = oracle.selected_attention_row(np64(q[r]), np64(k[s0:s0 + L]), np64(v[s0:s0 + L]),
+                                               idxn[r], t, 64, 1 / math.sqrt(128))
+        got[i] = np64(out[r])
+    assert_close("prefill_selected_full", got, ref, atol=2e-2)

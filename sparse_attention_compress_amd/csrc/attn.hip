@@ -571,10 +571,12 @@ __global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
 }
 
 // Decode: score the blocks, select and attend in one launch.  Every workgroup
-// of a (sequence, kv head) runs the same selection (identical inputs, so
-// identical ids), then attends to its own run of `bpw` selected blocks and
-// writes a partial state; split 0 also writes the debug outputs.  Grid
-// (splits, kv heads, sequences).
+// of a (sequence, kv head) whose run of `bpw` places holds a free pick runs the
+// same selection (identical inputs, so identical ids); a run of forced places
+// only (the local window, or everything when all eligible blocks are chosen)
+// takes its ids from the geometry and starts on its K/V at once.  Each split
+// then attends to its run and writes a partial state; split 0 always selects
+// and also writes the debug outputs.  Grid (splits, kv heads, sequences).
 template <int G, bool CIS>
 __global__ __launch_bounds__(256) void select_attn_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
@@ -589,7 +591,6 @@ __global__ __launch_bounds__(256) void select_attn_kernel(
     SelShared<256, kFusedMaxBlocks> sel;
     MfmaAttnSmem att;
   } U;
-  __shared__ int ids_all[kFusedMaxSel];
   __shared__ int ids_s[kMaxWgSlots];
   __shared__ int nv_s;
   const int tid = threadIdx.x;
@@ -601,20 +602,38 @@ __global__ __launch_bounds__(256) void select_attn_kernel(
   const int nvis = min(cu_c[b + 1] - cu_c[b], full_windows_dev(len));
   const size_t unit = size_t(b) * kv_heads + kv;
   const bool lead = split == 0;
+  const SelGeom g = sel_geometry(t, nb, topk, n_init, n_local);
+  const int s_begin = split * bpw, s_end = min(topk, s_begin + bpw);
   uint4 qb[4];
   load_q_operand<G>(q, unit, qb);  // in flight during the selection
-  float sc[Sel::kPer];
-  block_scores_from_logits<G, 256, kFusedMaxBlocks>(U.sel, sc, logits, part, cisb, cis_weight,
-                                                    unit, nvis, nb, n_chunk_max, ldc, ldb, nb_max,
-                                                    nc_max, lead ? block_scores : nullptr, nullptr);
-  __syncthreads();
-  topk_select<256, kFusedMaxBlocks>(U.sel, sc, sel_geometry(t, nb, topk, n_init, n_local), topk,
-                                    ids_all);
-  __syncthreads();
-  if (lead && indices != nullptr)
-    for (int i = tid; i < topk; i += 256) indices[unit * topk + i] = ids_all[i];
-  const int s_begin = split * bpw;
-  stage_ids(ids_all, s_begin, min(topk, s_begin + bpw), t, ids_s, &nv_s);
+  // A split whose places hold no free pick knows its ids from the geometry
+  // alone and skips the selection; the lead split always selects, since it
+  // writes the row's indices and block scores.  (Uniform per workgroup.)
+  const bool known = !lead && (g.free_mark != 2 || s_end <= g.f_init || s_begin >= g.f_init + g.kf);
+  if (known) {
+    if (tid < kWave) {
+      const int p = s_begin + tid;
+      const int id = p < s_end ? forced_id_at(g, p) : -1;
+      if (id >= 0) ids_s[tid] = id;  // ids are ascending, so the valid ones are a prefix
+      const int n = __popcll(__ballot(id >= 0));
+      if (tid == 0) nv_s = n;
+    }
+  } else {
+    float sc[Sel::kPer];
+    block_scores_from_logits<G, 256, kFusedMaxBlocks>(U.sel, sc, logits, part, cisb, cis_weight,
+                                                      unit, nvis, nb, n_chunk_max, ldc, ldb, nb_max,
+                                                      nc_max, lead ? block_scores : nullptr, nullptr);
+    int* irow = indices != nullptr && lead ? indices + unit * topk : nullptr;
+    // every chosen id is eligible (start <= t): the split's ids go straight to
+    // its slots, the lead's also to the row's indices
+    const int total = topk_select<256, kFusedMaxBlocks>(U.sel, sc, g, topk, [&](int pos, int id) {
+      if (pos >= s_begin && pos < s_end) ids_s[pos - s_begin] = id;
+      if (irow != nullptr) irow[pos] = id;
+    });
+    if (irow != nullptr)
+      for (int i = total + tid; i < topk; i += 256) irow[i] = -1;
+    if (tid == 0) nv_s = max(0, min(total, s_end) - s_begin);
+  }
   __syncthreads();
   attend_staged_blocks<G, CIS, true>(U.att, ids_s, nv_s, qb, k, v, cis, kstart, t, unit, kv,
                                      kv_heads, scale_log2, split, int(gridDim.x), nullptr,

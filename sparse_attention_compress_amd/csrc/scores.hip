@@ -278,9 +278,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       sc[u] = u < n_slab ? block_scores[unit * nb_max + min(tid + kSelThreads * u, nb - 1)] : 0.f;
   }
   if (indices == nullptr) return;
-  __syncthreads();
-  topk_select<kSelThreads, kMaxSortBlocks>(S, sc, sel_geometry(t, nb, topk, n_init, n_local), topk,
-                                            indices + unit * topk);
+  int* out = indices + unit * topk;
+  const int total = topk_select<kSelThreads, kMaxSortBlocks>(
+      S, sc, sel_geometry(t, nb, topk, n_init, n_local), topk,
+      [&](int pos, int id) { out[pos] = id; });
+  for (int i = total + tid; i < topk; i += kSelThreads) out[i] = -1;
 }
 
 // ------------------------------------------------- kernel 3: select, one wave per row

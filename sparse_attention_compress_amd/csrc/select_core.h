@@ -98,8 +98,11 @@ __device__ __forceinline__ SelGeom sel_geometry(int t, int nb, int topk, int n_i
   return g;
 }
 
-// Top-k over the eligible ids with scores sc (registers); writes topk ascending
-// ids (-1 padded) to out, which may point to global memory or LDS.
+// Top-k over the eligible ids with scores sc (registers).  Calls emit(pos, id)
+// for every chosen id, pos being its place in ascending id order (pos < topk),
+// and returns the number chosen (in every thread); places from that count to
+// topk are the caller's to pad.  Needs no barrier before it as long as the
+// caller's preceding LDS use is of other fields of S.
 // The free candidates' scores become order-preserving 32-bit keys.  A 256-bin
 // histogram of the keys over their range (a shift of the key offset from the
 // minimum, so binning is exact integer arithmetic) locates the bin holding the
@@ -107,10 +110,10 @@ __device__ __forceinline__ SelGeom sel_geometry(int t, int nb, int topk, int n_i
 // candidates share that bin they are gathered and one wave ranks them exactly by
 // (key desc, id asc); otherwise the bin is refined with the next lower bits.
 // Chosen ids are then written in ascending order.
-template <int THREADS, int MAXB>
-__device__ __forceinline__ void topk_select(SelShared<THREADS, MAXB>& S,
-                                            const float (&sc)[SelCfg<THREADS, MAXB>::kPer],
-                                            const SelGeom& g, int topk, int* out) {
+template <int THREADS, int MAXB, typename Emit>
+__device__ __forceinline__ int topk_select(SelShared<THREADS, MAXB>& S,
+                                           const float (&sc)[SelCfg<THREADS, MAXB>::kPer],
+                                           const SelGeom& g, int topk, Emit&& emit) {
   using C = SelCfg<THREADS, MAXB>;
   constexpr int P = C::kPer;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -257,11 +260,24 @@ __device__ __forceinline__ void topk_select(SelShared<THREADS, MAXB>& S,
 #pragma unroll
   for (int u = 0; u < P; ++u) f[u] = st[u] == 1;
   const int total = ordered_positions<THREADS, MAXB>(f, pos, S.cnt[1]);
-  // writes stay inside the row's topk slots even if the count were wrong
+  // emitted places stay inside the row's topk slots even if the count were wrong
 #pragma unroll
   for (int u = 0; u < P; ++u)
-    if (f[u] && pos[u] < topk) out[pos[u]] = tid + THREADS * u;
-  for (int i = max(0, total) + tid; i < topk; i += THREADS) out[i] = -1;
+    if (f[u] && pos[u] < topk) emit(pos[u], tid + THREADS * u);
+  return min(total, topk);
+}
+
+// The id at place p of the ascending selection when p is not one of the free
+// picks: the forced init blocks come first and the forced local blocks last
+// (they are the highest eligible ids); with every eligible block chosen, place p
+// holds id p.  Returns -2 for a free pick's place and -1 past the chosen count.
+__device__ __forceinline__ int forced_id_at(const SelGeom& g, int p) {
+  const int n_loc = g.n_elig - g.f_loc;
+  const int kf = g.free_mark == 0 ? 0 : g.kf;
+  if (p >= g.f_init + kf + n_loc) return -1;
+  if (p < g.f_init) return p;
+  if (p < g.f_init + kf) return g.free_mark == 1 ? p : -2;
+  return g.f_loc + (p - g.f_init - kf);
 }
 
 // (max, sum of exp2) of the union of two sets of log2-domain logits.

@@ -313,20 +313,23 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <bool CIS>
+// Output dims are permuted across the eight O^T tiles: row c of tile n is dim
+// 8c + n.  The A operand of tile n then needs, in lane (c16, r4), element n of
+// dims 8 c16 .. 8 c16 + 7 of tokens 4 r4 .. 4 r4 + 3: four 16-byte loads of V
+// rows per block instead of 32 two-byte gathers.
 struct MfmaBlockRegs {
-  uint4 k[4];      // A operand of S^T = K Q^T: token c16, dims 32i + 8 r4 .. +8
-  uint32_t v[16];  // A operand of O^T = V^T P^T: dim 16n + c16, tokens 4 r4 + 2m, +1
-  float cw[4];     // CIS of tokens 4 r4 + e
+  uint4 k[4];   // A operand of S^T = K Q^T: token c16, dims 32i + 8 r4 .. +8
+  uint4 v[4];   // V rows: token 4 r4 + e, dims 8 c16 .. 8 c16 + 7
+  float cw[4];  // CIS of tokens 4 r4 + e
 };
 
-__device__ __forceinline__ uint32_t ld_u16(const bf16_t* p) {
-  return uint32_t(*reinterpret_cast<const uint16_t*>(p));
-}
-
-// LDS of the wave merge at the end of attend_staged_blocks.
+// LDS of the wave merge at the end of attend_staged_blocks.  Staged rows are
+// padded to 80 floats: the merge reads lane c16 + 16w of rows 4n + r4, which
+// then fall in distinct banks.
+constexpr int kAccRow = kWave + 16;
 struct MfmaAttnSmem {
   float m_s[4][16], l_s[4][16];
-  float accx_s[4][32][kWave];  // [wave][tile element 4n + e][lane]
+  float accx_s[4][32][kAccRow];  // [wave][tile element 4n + e][lane]
 };
 
 // Stage ids[s_begin, s_end) of one row that are valid for position t (id >= 0,
@@ -380,7 +383,7 @@ __device__ __forceinline__ void attend_staged_blocks(
   const int c16 = lane & 15, r4 = lane >> 4;
   float (&m_s)[4][16] = sm.m_s;
   float (&l_s)[4][16] = sm.l_s;
-  float (&accx_s)[4][32][kWave] = sm.accx_s;
+  float (&accx_s)[4][32][kAccRow] = sm.accx_s;
   (void)tid;
 
   const size_t rs = size_t(kv_heads) * D;
@@ -394,14 +397,9 @@ __device__ __forceinline__ void attend_staged_blocks(
     const bf16_t* kr = kbase + size_t(min(j0 + c16, t)) * rs + 8 * r4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) R.k[i] = ld16(kr + 32 * i);
-    const bf16_t* vr[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vr[e] = vbase + size_t(min(j0 + 4 * r4 + e, t)) * rs + c16;
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2)
-        R.v[2 * n + e2] = ld_u16(vr[2 * e2] + 16 * n) | (ld_u16(vr[2 * e2 + 1] + 16 * n) << 16);
+    for (int e = 0; e < 4; ++e)
+      R.v[e] = ld16(vbase + size_t(min(j0 + 4 * r4 + e, t)) * rs + 8 * c16);
     if (CIS) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -411,7 +409,7 @@ __device__ __forceinline__ void attend_staged_blocks(
 
   float m_run = -INFINITY;  // running max of head c16 (same in the wave's 4 rows)
   float l_run = 0.f;        // this lane's share of the normaliser (its row's tokens)
-  f32x4_t acc[8];           // O^T[dims 16n + 4 r4 + e][head c16]
+  f32x4_t acc[8];           // O^T[dim 8 (4 r4 + e) + n][head c16]
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -457,7 +455,12 @@ __device__ __forceinline__ void attend_staged_blocks(
                                                               __builtin_bit_cast(uint32_t, p23)));
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(R.v[2 * n], R.v[2 * n + 1]));
+      // element n of the four token rows: tokens 4 r4 .. 4 r4 + 3 of dim 8 c16 + n
+      const uint32_t w0 = (&R.v[0].x)[n >> 1], w1 = (&R.v[1].x)[n >> 1];
+      const uint32_t w2 = (&R.v[2].x)[n >> 1], w3 = (&R.v[3].x)[n >> 1];
+      const uint32_t lo = (n & 1) ? (w0 >> 16) | (w1 & 0xFFFF0000u) : (w0 & 0xFFFFu) | (w1 << 16);
+      const uint32_t hi = (n & 1) ? (w2 >> 16) | (w3 & 0xFFFF0000u) : (w2 & 0xFFFFu) | (w3 << 16);
+      const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[n], 0, 0, 0);
     }
   };
@@ -494,8 +497,9 @@ __device__ __forceinline__ void attend_staged_blocks(
     for (int e = 0; e < 4; ++e) accx_s[wave][4 * n + e][lane] = acc[n][e];
   __syncthreads();
 
-  // wave w merges tiles n = 2w, 2w+1 of the four waves for its lane's entries
-  // (head c16, dims 16n + 4 r4 .. +3) and writes them as one 16-byte run each
+  // thread (wave w, r4, c16) merges head c16, dims 32w + 8 r4 .. +8 of the four
+  // waves: in every wave's staged tiles these are rows 4n + r4 (n = 0..7) of
+  // lane c16 + 16w; it writes them as one run
   float f[4], M = -INFINITY, L = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -508,30 +512,31 @@ __device__ __forceinline__ void attend_staged_blocks(
     L += f[w] * l_s[w][c16];
   }
   const size_t ps = unit * n_split + split;
+  float o[8];
 #pragma unroll
-  for (int nn = 0; nn < 2; ++nn) {
-    const int n = 2 * wave + nn;
-    float o[4];
+  for (int n = 0; n < 8; ++n) {
+    o[n] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[e] = 0.f;
+    for (int w = 0; w < 4; ++w) o[n] += f[w] * accx_s[w][4 * n + r4][c16 + 16 * wave];
+  }
+  const int d0 = 32 * wave + 8 * r4;
+  if (c16 < G) {
+    if constexpr (SPLIT) {
+      float* dst = part_acc + (ps * G + c16) * D + d0;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    } else if (part_acc != nullptr) {
+      // unsplit rows may ask for float32 output rows (passed in part_acc)
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      float* dst = part_acc + (unit * G + c16) * D + d0;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+    } else {
+      uint32_t w[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) o[e] += f[w] * accx_s[w][4 * n + e][lane];
-    }
-    if (c16 < G) {
-      if constexpr (SPLIT) {
-        *reinterpret_cast<float4*>(part_acc + (ps * G + c16) * D + 16 * n + 4 * r4) =
-            make_float4(o[0], o[1], o[2], o[3]);
-      } else if (part_acc != nullptr) {
-        // unsplit rows may ask for float32 output rows (passed in part_acc)
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<float4*>(part_acc + (unit * G + c16) * D + 16 * n + 4 * r4) =
-            make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-      } else {
-        bf16_t* dst = out + (unit * G + c16) * D + 16 * n + 4 * r4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) store_f32(dst + e, L > 0.f ? o[e] / L : 0.f);
-      }
+      for (int i = 0; i < 4; ++i)
+        w[i] = pack_bf16x2(L > 0.f ? o[2 * i] / L : 0.f, L > 0.f ? o[2 * i + 1] / L : 0.f);
+      *reinterpret_cast<uint4*>(out + (unit * G + c16) * D + d0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
   if (wave == 0 && r4 == 0 && c16 < G) {

@@ -15,16 +15,18 @@
 // Design (gfx950): one wave per 4 consecutive query tokens of one sequence and
 // KV group; for each token the group's G <= 16 query heads are the 16 columns
 // of the MFMA tiles, keys (or windows) go 16 at a time as the rows:
-// S^T = K Q^T with four v_mfma_f32_16x16x32_bf16 (key rows loaded straight into
-// the A operand, Q^T kept in registers), then O^T += V^T P^T with eight
-// v_mfma_f32_16x16x16_bf16 (P^T is already in the operand layout).  Each key
-// tile a wave loads serves its 4 tokens, and the next tile is in flight while
-// the current one is computed.  A workgroup holds 4 waves = 16 consecutive
-// tokens, so the tiles they share come from L1/L2.  No LDS, no workgroup
-// barriers.  The compressed branch runs in two passes: the first finds each
-// head's log2 normaliser, the second forms normalised probabilities, which give
-// o_cmp directly and, summed over the 16 head columns with DPP, the window
-// scores of the group.
+// S^T = K Q^T with four v_mfma_f32_16x16x32_bf16 (Q^T kept in registers), then
+// O^T += V^T P^T with eight v_mfma_f32_16x16x32_bf16 (P^T is already in the
+// operand layout).  A workgroup holds 4 waves = 16 consecutive tokens; it
+// stages each 32-key tile (keys and transposed values, 16 KB) in LDS once, all
+// 256 threads loading it, double-buffered so the next tile is in flight while
+// the current one is computed, and every wave reads its MFMA operands from
+// there.  A tile is thus fetched once per 16 tokens instead of once per wave,
+// which is what bounded these kernels (they are limited by operand fetch, not
+// by the matrix cores).  The compressed branch runs in two passes: the first
+// finds each head's log2 normaliser, the second forms normalised
+// probabilities, which give o_cmp directly and, summed over the 16 head
+// columns with DPP, the window scores of the group.
 #include "common.h"
 #include "launch.h"
 
@@ -76,77 +78,115 @@ __global__ __launch_bounds__(256) void transpose_values_kernel(const bf16_t* __r
 
 // ------------------------------------------------------------------- key tiles
 
-// One 32-key tile of a wave, keys key0 .. key0+31 (key0 a multiple of 32).
-// ka[h] (KeyFrag): A operand of S^T = K Q^T for keys key0 + 16h + c16, dims 32i + 8 r4 .. +8
-//        (row-major K, rows clamped to kmax so every load is in bounds).
-// va[n] (ValFrag): A operand of O^T = V^T P^T for dim 16n + c16, from the transposed
-//        values; k-slot e < 4 holds key key0 + 4 r4 + e, e >= 4 key key0 + 16 +
-//        4 r4 + e - 4 (the same slots the S^T accumulators give P^T).
+// One 32-key tile (keys key0 .. key0+31, key0 a multiple of 32) as MFMA operands:
+// ka[h] (KeyFrag): A operand of S^T = K Q^T for keys key0 + 16h + c16, dims 32i + 8 r4 .. +8.
+// va[n] (ValFrag): A operand of O^T = V^T P^T for dim 16n + c16; k-slot e < 4
+//        holds key key0 + 4 r4 + e, e >= 4 key key0 + 16 + 4 r4 + e - 4 (the same
+//        slots the S^T accumulators give P^T).
 typedef uint4 KeyFrag[2][4];
 typedef uint4 ValFrag[8];
 
-__device__ __forceinline__ void load_keys(const bf16_t* __restrict__ kb, size_t rs, int key0,
-                                          int kmax, KeyFrag& ka) {
-  const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
+// LDS staging of one workgroup's tiles, double-buffered.  Key rows are padded to
+// 272 B and value rows to 80 B so that the 16 rows one A operand reads start in
+// distinct banks.  Value rows hold the tile's 32 keys in k-slot order (keys
+// 4r..4r+3 then 16+4r..16+4r+3 at places 8r .. 8r+7), so each ValFrag entry is
+// one 16-byte read.
+constexpr int kKRow = kHeadDim + 8;  // bf16 per staged key row
+constexpr int kVRow = 32 + 8;        // bf16 per staged value row (one dim, 32 keys)
+struct TileLds {
+  bf16_t k[2][32 * kKRow];
+  bf16_t v[2][kHeadDim * kVRow];
+};
+
+// A tile in flight: with THREADS threads, thread tid holds key chunks
+// c = tid + THREADS u (row c / 16, dims 8 (c % 16) .. +8) and value chunks
+// c = tid + THREADS u (dim c / 4, keys 8 (c % 4) .. +8) of the 512 16-byte
+// chunks of each.
+template <int THREADS>
+struct TileRegs {
+  static constexpr int kPer = 512 / THREADS;
+  uint4 k[kPer], v[kPer];
+};
+
+// Key rows are clamped to kmax so every load is in bounds (the scores of such
+// rows are masked).  Value rows come from the transposed copy, which holds
+// zeros past the sequence up to its padded length ldv (a multiple of 64).
+template <bool WITH_V, int THREADS>
+__device__ __forceinline__ void fetch_tile(const bf16_t* __restrict__ kb, size_t rs,
+                                           const bf16_t* __restrict__ vt, int ldv, int key0,
+                                           int kmax, TileRegs<THREADS>& r) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const bf16_t* kr = kb + size_t(min(key0 + 16 * h + c16, kmax)) * rs + 8 * r4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ka[h][i] = ld16(kr + 32 * i);
+  for (int u = 0; u < TileRegs<THREADS>::kPer; ++u) {
+    const int c = tid + THREADS * u;
+    r.k[u] = ld16(kb + size_t(min(key0 + (c >> 4), kmax)) * rs + 8 * (c & 15));
+    if constexpr (WITH_V) r.v[u] = ld16(vt + size_t(c >> 2) * ldv + key0 + 8 * (c & 3));
   }
 }
 
-__device__ __forceinline__ void load_vals(const bf16_t* __restrict__ vt, int ldv, int key0,
-                                          ValFrag& va) {
-  const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
-  const bf16_t* vr = vt + size_t(c16) * ldv + key0 + 4 * r4;
+template <bool WITH_V, int THREADS>
+__device__ __forceinline__ void stash_tile(TileLds& T, int buf, const TileRegs<THREADS>& r) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(vr + size_t(16 * n) * ldv);
-    const uint2 hi = *reinterpret_cast<const uint2*>(vr + size_t(16 * n) * ldv + 16);
-    va[n] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
-}
-
-// Tile loop: keys first .. last in 32-key tiles from `first` (a multiple of 32).
-// The next tile's keys are double-buffered; its values are loaded into the one
-// value buffer right after this tile's P.V has consumed it, so they arrive
-// during the next tile's scores.
-// PREFETCH_KEYS = false keeps a single key buffer (the next tile's keys are then
-// loaded after this tile's scores), for kernels short of registers.
-template <bool WITH_V, bool PREFETCH_KEYS = true, typename F>
-__device__ __forceinline__ void tile_loop(const bf16_t* __restrict__ kb, size_t rs,
-                                          const bf16_t* __restrict__ vt, int ldv, int first,
-                                          int last, int kmax, F&& process) {
-  if (first > last) return;
-  ValFrag va;
-  if constexpr (!PREFETCH_KEYS) {
-    KeyFrag ka;
-    load_keys(kb, rs, first, kmax, ka);
-    if constexpr (WITH_V) load_vals(vt, ldv, first, va);
-    for (int key0 = first; key0 <= last; key0 += 32) {
-      process(key0, ka, va);
-      if (key0 + 32 <= last) {
-        load_keys(kb, rs, key0 + 32, kmax, ka);
-        if constexpr (WITH_V) load_vals(vt, ldv, key0 + 32, va);
-      }
+  for (int u = 0; u < TileRegs<THREADS>::kPer; ++u) {
+    const int c = tid + THREADS * u;
+    *reinterpret_cast<uint4*>(&T.k[buf][(c >> 4) * kKRow + 8 * (c & 15)]) = r.k[u];
+    if constexpr (WITH_V) {
+      // keys 8kc .. 8kc+3 go to places p, keys 8kc+4 .. 8kc+7 to p + 8
+      const int kc = c & 3;
+      const int p = kc < 2 ? 16 * kc : 16 * (kc - 2) + 4;
+      bf16_t* row = &T.v[buf][(c >> 2) * kVRow];
+      *reinterpret_cast<uint2*>(row + p) = make_uint2(r.v[u].x, r.v[u].y);
+      *reinterpret_cast<uint2*>(row + p + 8) = make_uint2(r.v[u].z, r.v[u].w);
     }
-    return;
   }
-  KeyFrag kA, kB;
-  load_keys(kb, rs, first, kmax, kA);
-  if constexpr (WITH_V) load_vals(vt, ldv, first, va);
-  for (int key0 = first;; key0 += 64) {
-    const bool has1 = key0 + 32 <= last;
-    if (has1) load_keys(kb, rs, key0 + 32, kmax, kB);
-    process(key0, kA, va);
-    if (!has1) break;
-    if constexpr (WITH_V) load_vals(vt, ldv, key0 + 32, va);
-    const bool has2 = key0 + 64 <= last;
-    if (has2) load_keys(kb, rs, key0 + 64, kmax, kA);
-    process(key0 + 32, kB, va);
-    if (!has2) break;
-    if constexpr (WITH_V) load_vals(vt, ldv, key0 + 64, va);
+}
+
+__device__ __forceinline__ void read_keys(const TileLds& T, int buf, KeyFrag& ka) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ka[h][i] = *reinterpret_cast<const uint4*>(&T.k[buf][(16 * h + c16) * kKRow + 32 * i + 8 * r4]);
+}
+
+__device__ __forceinline__ void read_vals(const TileLds& T, int buf, ValFrag& va) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    va[n] = *reinterpret_cast<const uint4*>(&T.v[buf][(16 * n + c16) * kVRow + 8 * r4]);
+}
+
+// Tile loop of a workgroup over keys first .. last (first a multiple of 32;
+// both the same in every thread).  Every thread takes part in the loads and
+// barriers; waves with `active` false (no tokens) skip the compute.  The next
+// tile's loads are issued before the current tile is computed and written to
+// the other buffer after it; one barrier per tile.
+template <bool WITH_V, int THREADS, typename F>
+__device__ __forceinline__ void lds_tile_loop(TileLds& T, const bf16_t* __restrict__ kb,
+                                              size_t rs, const bf16_t* __restrict__ vt, int ldv,
+                                              int first, int last, int kmax, bool active,
+                                              F&& process) {
+  if (first > last) return;
+  TileRegs<THREADS> r;
+  fetch_tile<WITH_V>(kb, rs, vt, ldv, first, kmax, r);
+  stash_tile<WITH_V>(T, 0, r);
+  __syncthreads();
+  int buf = 0;
+  for (int key0 = first; key0 <= last; key0 += 32) {
+    const bool more = key0 + 32 <= last;
+    if (more) fetch_tile<WITH_V>(kb, rs, vt, ldv, key0 + 32, kmax, r);
+    if (active) {
+      KeyFrag ka;
+      ValFrag va;
+      read_keys(T, buf, ka);
+      if constexpr (WITH_V) read_vals(T, buf, va);
+      process(key0, ka, va);
+    }
+    if (more) stash_tile<WITH_V>(T, buf ^ 1, r);
+    __syncthreads();
+    buf ^= 1;
   }
 }
 
@@ -234,8 +274,11 @@ __device__ __forceinline__ void store_rows(void* __restrict__ out, int out_f32, 
 
 // ------------------------------------------------------------- compressed branch
 
-// Query tokens per wave: every key tile loaded by a wave serves this many tokens.
-constexpr int kTpw = 4;
+// Query tokens per workgroup (a multiple of 16 consecutive tokens of one
+// sequence and KV group); a wave holds TPW of them and a workgroup
+// kGroupTokens / TPW waves.  Fewer tokens per wave means fewer registers and
+// more waves per SIMD; the tiles are shared through LDS either way.
+constexpr int kGroupTokens = 16;
 
 // The tokens of one wave: query positions tq0 .. tq0 + n - 1 of sequence b
 // (grid z), packed rows row0 .. row0 + n - 1, key positions t0 .. t0 + n - 1.
@@ -243,13 +286,28 @@ struct WaveRows {
   int n, row0, t0;
 };
 
+// Key positions of the first and last query tokens of workgroup `grp` of
+// sequence b; returns false when the workgroup has none.
+__device__ __forceinline__ bool group_span(const int* __restrict__ cu_q,
+                                           const int* __restrict__ cu_k, int b, int grp,
+                                           int& t_first, int& t_last) {
+  const int lq = cu_q[b + 1] - cu_q[b];
+  const int lk = cu_k[b + 1] - cu_k[b];
+  const int tq = grp * kGroupTokens;
+  if (tq >= lq) return false;
+  t_first = tq + (lk - lq);
+  t_last = min(tq + kGroupTokens, lq) - 1 + (lk - lq);
+  return true;
+}
+
+template <int TPW>
 __device__ __forceinline__ WaveRows wave_rows(const int* __restrict__ cu_q,
                                               const int* __restrict__ cu_k, int b, int tile) {
   const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
   const int lk = cu_k[b + 1] - cu_k[b];
-  const int tq = tile * kTpw;
+  const int tq = tile * TPW;
   WaveRows r;
-  r.n = max(0, min(kTpw, lq - tq));
+  r.n = max(0, min(TPW, lq - tq));
   r.row0 = q0 + tq;
   r.t0 = tq + (lk - lq);
   return r;
@@ -258,19 +316,23 @@ __device__ __forceinline__ WaveRows wave_rows(const int* __restrict__ cu_q,
 // PROBS = false: per (row, head) log2 normaliser lse2 = max + log2(sum exp2).
 // PROBS = true:  o_cmp, natural-log lse, and the group's block scores.
 // vct: the compressed values transposed ([batch][kv][128][ldv]).
-template <int G, bool PROBS>
-__global__ __launch_bounds__(256) void compressed_prefill_kernel(
+template <int G, bool PROBS, int TPW>
+__global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vct,
     int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
     const int* __restrict__ cu_c, int kv_heads, float scale_log2, float* __restrict__ lse2,
     void* __restrict__ o_cmp, int out_f32, float* __restrict__ lse_nat,
     float* __restrict__ block_scores, int nb_max) {
   constexpr int D = kHeadDim;
+  __shared__ TileLds T;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
   const int kv = blockIdx.y, b = blockIdx.z;
-  const WaveRows R = wave_rows(cu_q, cu_k, b, blockIdx.x * 4 + wave);
-  if (R.n == 0) return;  // whole wave; the kernel has no barriers
+  int t_first, t_last;
+  if (!group_span(cu_q, cu_k, b, blockIdx.x, t_first, t_last)) return;  // whole workgroup
+  constexpr int kTpw = TPW, kThreads = kGroupTokens / TPW * kWave;
+  const WaveRows R = wave_rows<TPW>(cu_q, cu_k, b, blockIdx.x * (kGroupTokens / TPW) + wave);
+  const bool active = R.n > 0;  // waves past the sequence only help with the tiles
   const int len = cu_k[b + 1] - cu_k[b];
   const int cbase = cu_c[b];
   const int nc = cu_c[b + 1] - cbase;
@@ -281,16 +343,15 @@ __global__ __launch_bounds__(256) void compressed_prefill_kernel(
   for (int j = 0; j < kTpw; ++j) {
     const int t = R.t0 + j;
     nvis[j] = (j < R.n && t >= kKernel - 1) ? min(nc, (t - (kKernel - 1)) / kStride + 1) : 0;
-    head0[j] = (size_t(R.row0 + min(j, R.n - 1)) * kv_heads + kv) * G;
+    head0[j] = (size_t(active ? R.row0 + min(j, R.n - 1) : cu_q[b]) * kv_heads + kv) * G;
     load_q<G>(q + head0[j] * D, qb[j]);
   }
-  int nv_max = 0;
-#pragma unroll
-  for (int j = 0; j < kTpw; ++j) nv_max = max(nv_max, nvis[j]);
+  // windows of the workgroup: those of its last token
+  const int nv_wg = t_last >= kKernel - 1 ? min(nc, (t_last - (kKernel - 1)) / kStride + 1) : 0;
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kb = kc + size_t(cbase) * rs + size_t(kv) * D;
   const bf16_t* vt = vct + (size_t(b) * kv_heads + kv) * D * size_t(ldv);
-  const int cmax = max(nv_max - 1, 0);
+  const int cmax = max(nv_wg - 1, 0);
 
   if constexpr (!PROBS) {
     float m_run[kTpw], l_run[kTpw];
@@ -323,7 +384,7 @@ __global__ __launch_bounds__(256) void compressed_prefill_kernel(
         for (int e = 0; e < 8; ++e) l_run[j] += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run[j]);
       }
     };
-    tile_loop<false>(kb, rs, vt, ldv, 0, nv_max - 1, cmax, process);
+    lds_tile_loop<false, kThreads>(T, kb, rs, vt, ldv, 0, nv_wg - 1, cmax, active, process);
 #pragma unroll
     for (int j = 0; j < kTpw; ++j) {
       const float l = rows_sum(l_run[j]);
@@ -379,7 +440,7 @@ __global__ __launch_bounds__(256) void compressed_prefill_kernel(
         }
       }
     };
-    tile_loop<true, false>(kb, rs, vt, ldv, 0, nv_max - 1, cmax, process);
+    lds_tile_loop<true, kThreads>(T, kb, rs, vt, ldv, 0, nv_wg - 1, cmax, active, process);
 #pragma unroll
     for (int j = 0; j < kTpw; ++j) {
       if (j >= R.n) continue;
@@ -403,8 +464,8 @@ __global__ __launch_bounds__(256) void compressed_prefill_kernel(
 // is g0 * o_cmp + g1 * o_sel + g2 * o_win (the branch outputs are fp32 rows).
 // The wave's tokens share the key tiles of the union of their windows.
 // vtr: the values transposed ([batch][kv][128][ldv]).
-template <int G, bool GATED>
-__global__ __launch_bounds__(256) void window_prefill_kernel(
+template <int G, bool GATED, int TPW>
+__global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vtr,
     int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads,
     int window, float scale_log2, void* __restrict__ out, int out_f32,
@@ -412,23 +473,27 @@ __global__ __launch_bounds__(256) void window_prefill_kernel(
     const float* __restrict__ o_cmp, const float* __restrict__ o_sel) {
   constexpr int D = kHeadDim;
   constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
+  __shared__ TileLds T;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
   const int kv = blockIdx.y, b = blockIdx.z;
-  const WaveRows R = wave_rows(cu_q, cu_k, b, blockIdx.x * 4 + wave);
-  if (R.n == 0) return;  // whole wave; the kernel has no barriers
+  int t_first, t_last;
+  if (!group_span(cu_q, cu_k, b, blockIdx.x, t_first, t_last)) return;  // whole workgroup
+  constexpr int kTpw = TPW, kThreads = kGroupTokens / TPW * kWave;
+  const WaveRows R = wave_rows<TPW>(cu_q, cu_k, b, blockIdx.x * (kGroupTokens / TPW) + wave);
+  const bool active = R.n > 0;  // waves past the sequence only help with the tiles
   size_t head0[kTpw];
   uint4 qb[kTpw][4];
 #pragma unroll
   for (int j = 0; j < kTpw; ++j) {
-    head0[j] = (size_t(R.row0 + min(j, R.n - 1)) * kv_heads + kv) * G;
+    head0[j] = (size_t(active ? R.row0 + min(j, R.n - 1) : cu_q[b]) * kv_heads + kv) * G;
     load_q<G>(q + head0[j] * D, qb[j]);
   }
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kb = k + size_t(cu_k[b]) * rs + size_t(kv) * D;
   const bf16_t* vt = vtr + (size_t(b) * kv_heads + kv) * D * size_t(ldv);
-  const int t_last = R.t0 + R.n - 1;
-  const int j_lo = max(0, R.t0 - window + 1) & ~31;  // tiles start 32-aligned
+  // keys of the workgroup: the union of its tokens' windows, tiles 32-aligned
+  const int j_lo = max(0, t_first - window + 1) & ~31;
   float m_run[kTpw], l_run[kTpw];
   f32x4_t acc[kTpw][8];
 #pragma unroll
@@ -473,7 +538,7 @@ __global__ __launch_bounds__(256) void window_prefill_kernel(
       tile_pv(va, p, acc[j]);
     }
   };
-  tile_loop<true>(kb, rs, vt, ldv, j_lo, t_last, t_last, process);
+  lds_tile_loop<true, kThreads>(T, kb, rs, vt, ldv, j_lo, t_last, t_last, active, process);
 #pragma unroll
   for (int j = 0; j < kTpw; ++j) {
     const float l = rows_sum(l_run[j]);
@@ -506,10 +571,16 @@ __global__ __launch_bounds__(256) void window_prefill_kernel(
 
 // --------------------------------------------------------------------------- host
 
-// Grid: (groups of 4 waves x kTpw tokens, kv head, sequence).
+// Tokens per wave of each kernel: the normaliser pass keeps no output
+// accumulators and holds 4; the passes with P.V hold 2 (8 waves a workgroup).
+constexpr int kTpwLse = 4, kTpwOut = 2;
+
+// Grid: (groups of kGroupTokens tokens, kv head, sequence).
 static dim3 prefill_grid(int max_seqlen_q, int kv_heads, int batch) {
-  return dim3((max_seqlen_q + 4 * kTpw - 1) / (4 * kTpw), kv_heads, batch);
+  return dim3((max_seqlen_q + kGroupTokens - 1) / kGroupTokens, kv_heads, batch);
 }
+
+static dim3 prefill_block(int tpw) { return dim3(kGroupTokens / tpw * kWave); }
 
 int transposed_ld(int max_len) { return (max_len + 63) / 64 * 64; }
 
@@ -532,12 +603,14 @@ static hipError_t launch_cmp_g(const CompressedPrefillArgs& a, hipStream_t s) {
   const int ldv = transposed_ld(a.max_windows);
   hipError_t e = launch_transpose(a.vc, a.cu_c, a.batch, a.kv_heads, a.max_windows, a.vct, s);
   if (e != hipSuccess) return e;
-  e = launch_kernel(kKindCmpLse, compressed_prefill_kernel<G, false>, grid, dim3(256), s, a.q,
+  e = launch_kernel(kKindCmpLse, compressed_prefill_kernel<G, false, kTpwLse>, grid,
+                    prefill_block(kTpwLse), s, a.q,
                     a.kc, static_cast<const bf16_t*>(a.vct), ldv, a.cu_q, a.cu_k, a.cu_c,
                     a.kv_heads, a.scale_log2, a.lse2, static_cast<void*>(nullptr), 0,
                     static_cast<float*>(nullptr), static_cast<float*>(nullptr), 0);
   if (e != hipSuccess) return e;
-  return launch_kernel(kKindCmpProbs, compressed_prefill_kernel<G, true>, grid, dim3(256), s,
+  return launch_kernel(kKindCmpProbs, compressed_prefill_kernel<G, true, kTpwOut>, grid,
+                       prefill_block(kTpwOut), s,
                        a.q, a.kc, static_cast<const bf16_t*>(a.vct), ldv, a.cu_q, a.cu_k, a.cu_c,
                        a.kv_heads, a.scale_log2, a.lse2, a.o_cmp, a.out_f32, a.lse_nat,
                        a.block_scores, a.nb_max);
@@ -563,10 +636,12 @@ static hipError_t launch_win_g(const WindowPrefillArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const bf16_t* vt = a.vt;
   if (a.gates != nullptr)
-    return launch_kernel(kKindWindow, window_prefill_kernel<G, true>, grid, dim3(256), s, a.q,
+    return launch_kernel(kKindWindow, window_prefill_kernel<G, true, kTpwOut>, grid,
+                         prefill_block(kTpwOut), s, a.q,
                          a.k, vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
                          a.out_f32, a.lse_nat, a.gates, a.o_cmp, a.o_sel);
-  return launch_kernel(kKindWindow, window_prefill_kernel<G, false>, grid, dim3(256), s, a.q, a.k,
+  return launch_kernel(kKindWindow, window_prefill_kernel<G, false, kTpwOut>, grid,
+                       prefill_block(kTpwOut), s, a.q, a.k,
                        vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
                        a.out_f32, a.lse_nat, static_cast<const float*>(nullptr),
                        static_cast<const float*>(nullptr), static_cast<const float*>(nullptr));

@@ -549,7 +549,7 @@ __device__ __forceinline__ void attend_staged_blocks(
 }
 
 template <int G, bool CIS, bool SPLIT>
-__global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void selected_attn_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
     bf16_t* __restrict__ out, float* __restrict__ lse, const int* __restrict__ cu_q,
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(256) void selected_attn_mfma_kernel(
 // then attends to its run and writes a partial state; split 0 always selects
 // and also writes the debug outputs.  Grid (splits, kv heads, sequences).
 template <int G, bool CIS>
-__global__ __launch_bounds__(256) void select_attn_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void select_attn_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
     const float* __restrict__ cisb, float cis_weight, const int* __restrict__ cu_k,
     const int* __restrict__ cu_c, int kv_heads, int nc_max, int ldc, int nb_max,

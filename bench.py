@@ -430,9 +430,11 @@ def prefill_main(args, dev):
                  "selected_attn": 4.0 * D * G * float(sel),
                  "window_attn": 4.0 * D * H * float(win.sum())}
         gathered = float(sel) * D * 2 * 2
-        dominant = "compressed_attn"
+        dominant = None
     wall_s, gpu_ms = _timed(fn, steps, warmup, stream)
     kern = _kernel_us(nsa, fn, kinds, 3, stream)
+    if dominant is None:  # the longest of the kernels that carry the branches' flops
+        dominant = max(flops, key=lambda n: kern[n])
     tokens = w.total_tokens
     ms_per_step = wall_s * 1e3 / steps
     tflops = {n: flops[n] / (kern[n] * 1e-6) / 1e12 for n in flops}

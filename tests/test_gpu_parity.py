@@ -361,6 +361,29 @@ def test_decode_step_cis_values_small():
     _check_decode("cis_small", d, out, bs, idx, 64, 1, 16, True, True, atol=2e-2)
 
 
+@pytest.mark.parametrize("topk,n_local", [(16, 2), (64, 16)])
+def test_decode_step_edge_lengths(topk, n_local):
+    """Degenerate sequences in one decode batch: empty, shorter than one window,
+    exactly one window, one and two blocks, and a ragged tail; with the newest
+    window refreshed.  The empty sequence's output is 0."""
+    lengths = [0, 1, 31, 32, 33, 64, 65, 1000, 4097]
+    d = _decode_inputs(lengths, SEED + 12)
+    log(f"decode step edge lengths {lengths} topk={topk} n_local={n_local}")
+    out, bs, idx = _run_decode_step(d, topk, 1, n_local, True, False, append=True)
+    assert torch.equal(out[0].float(), torch.zeros_like(out[0].float()))
+    assert (idx[0] == -1).all()
+    _check_decode("edge", d, out, bs, idx, topk, 1, n_local, True, False, atol=2e-2)
+
+
+@pytest.mark.parametrize("H,H_kv", [(32, 2), (8, 2), (4, 4)])
+def test_decode_step_group_sizes(H, H_kv):
+    """GQA groups of 16, 4 and 1 query heads through the single-kernel decode path."""
+    d = _decode_inputs([3000, 7000, 12345], SEED + 13, H=H, H_kv=H_kv)
+    log(f"decode step H={H} H_kv={H_kv}")
+    out, bs, idx = _run_decode_step(d, 64, 1, 16, True, False)
+    _check_decode(f"groups{H}_{H_kv}", d, out, bs, idx, 64, 1, 16, True, False, atol=2e-2)
+
+
 def test_decode_step_planted_blocks_select_exactly():
     """Keys of blocks 5, 9, 17 and 30 equal half the sum of their group's query
     heads (logits ~ 5.7 against ~ 0 elsewhere), so their windows, and at a lower

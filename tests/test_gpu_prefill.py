@@ -186,3 +186,63 @@ def test_prefill_step_full_size_sampled_rows():
     rows_sample = [0, 31, 32, 511, 512, 1023, 1024, 4095, 4096, 20000, 32767, 32768, 50001,
                    65472, 65534, 65535] + [int(x) for x in np.linspace(100, 65000, 8)]
     _check_step(w, d, sorted(set(rows_sample)), out, idx, None, 0.3)
+
+
+def test_prefill_step_ragged_batch_query_tails():
+    """A ragged batch whose queries are only the last tokens of each sequence
+    (chunked prefill: query t sits at key position L_k - L_q + i), including a
+    sequence shorter than one window and an empty one, through the whole
+    three-branch step."""
+    lk = [20, 33, 0, 700, 1500]
+    lq = [20, 10, 0, 300, 1500]
+    w = W.scaled(W.nsa_prefill(), lk)
+    qfull = W.prefill_query(w, DEV)
+    k, v = W.keys_values(w, DEV)
+    gfull = W.gates(w, DEV)
+    starts = np.cumsum([0] + lk)
+    tail = np.concatenate([np.arange(s + L - n, s + L) for s, L, n in zip(starts, lk, lq)]).astype(np.int64)
+    sel = torch.tensor(tail, device=DEV)
+    q, g = qfull[sel].contiguous(), gfull[sel].contiguous()
+    nc = [oracle.n_windows(L, 32, 16) for L in lk]
+    cu_q, cu_k, cu_c = cu(lq), cu(lk), cu(nc)
+    kc = torch.empty((max(1, sum(nc)), w.kv_heads, 128), dtype=BF16, device=DEV)
+    vc = torch.empty_like(kc)
+    nsa.nsa_compress_k(k, kc, cu_k, cu_c, max(nc))
+    nsa.nsa_compress_k(v, vc, cu_k, cu_c, max(nc))
+    rows = sum(lq)
+    nb_max = -(-max(lk) // 64)
+    out = torch.full((rows, w.heads, 128), float("nan"), dtype=BF16, device=DEV)
+    idx = torch.full((rows, w.kv_heads, w.topk), -7, dtype=torch.int32, device=DEV)
+    bs = torch.full((rows, w.kv_heads, nb_max), float("nan"), device=DEV)
+    p = nsa.prefill_params(q, k, v, kc, vc, g, cu_q, cu_k, cu_c, max(lk), out, topk=w.topk,
+                           window=w.window, block_scores=bs, indices=idx)
+    log(f"prefill step, query tails lq={lq} of lk={lk}")
+    nsa.nsa_prefill_step(p)
+    torch.cuda.synchronize()
+    qn, kn, vn, gn = np64(qfull), np64(k), np64(v), np64(gfull)
+    outn, idxn, bsn = np64(out), idx.cpu().numpy(), np64(bs)
+    row0, identical, checked = 0, 0, 0
+    for b, (L, n) in enumerate(zip(lk, lq)):
+        if n == 0:
+            continue
+        s0 = starts[b]
+        ts = sorted({L - n, L - n + 1, L - 1, L - 2, (2 * L - n) // 2} & set(range(L - n, L)))
+        ref = oracle.nsa_prefill_rows(qn[s0:s0 + L], kn[s0:s0 + L], vn[s0:s0 + L], gn[s0:s0 + L],
+                                      ts, topk=w.topk, window=w.window)
+        nb = -(-L // 64)
+        for i, t in enumerate(ts):
+            r = row0 + t - (L - n)
+            assert_close(f"block_scores[b={b},t={t}]", bsn[r][:, :nb], ref["block_scores"][i],
+                         atol=1e-5, rtol=1e-2)
+            same = True
+            for kv in range(w.kv_heads):
+                ok, _ = check_index_sets(f"b={b} t={t} kv={kv}", idxn[r, kv], ref["indices"][i, kv],
+                                         ref["block_scores"][i, kv], t, nb, w.topk, 0, 0)
+                same &= ok
+            checked += 1
+            if same:
+                identical += 1
+                assert_close(f"out[b={b},t={t}]", outn[r], ref["out"][i], atol=2e-2)
+        row0 += n
+    log(f"index sets identical on {identical}/{checked} rows")
+    assert identical >= 0.3 * checked

@@ -499,10 +499,10 @@ PrefillLayout prefill_layout(const nsa_prefill_params* p) {
   off += up(nsa::transposed_bytes(p->batch, p->kv_heads, L.max_windows));
   L.vt = off;
   off += up(nsa::transposed_bytes(p->batch, p->kv_heads, p->max_seqlen_k));
-  L.o_cmp = off;
-  off += up(rows * H * p->head_dim * sizeof(float));
+  L.o_cmp = off;  // branch outputs kept in bf16 until the gated sum
+  off += up(rows * H * p->head_dim * sizeof(uint16_t));
   L.o_sel = off;
-  off += up(rows * H * p->head_dim * sizeof(float));
+  off += up(rows * H * p->head_dim * sizeof(uint16_t));
   L.scores = off;
   if (p->block_scores == nullptr) off += up(rows * p->kv_heads * size_t(L.nb_max) * sizeof(float));
   L.indices = off;
@@ -553,8 +553,8 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
   NSA_REQUIRE(workspace_bytes >= lay.total, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, lay.total);
   char* base = static_cast<char*>(workspace);
-  float* o_cmp = reinterpret_cast<float*>(base + lay.o_cmp);
-  float* o_sel = reinterpret_cast<float*>(base + lay.o_sel);
+  nsa::bf16_t* o_cmp = reinterpret_cast<nsa::bf16_t*>(base + lay.o_cmp);
+  nsa::bf16_t* o_sel = reinterpret_cast<nsa::bf16_t*>(base + lay.o_sel);
   float* bs = p->block_scores ? p->block_scores : reinterpret_cast<float*>(base + lay.scores);
   int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.indices);
   const float sl2 = scale_log2_of(p->softmax_scale, p->head_dim);
@@ -587,7 +587,7 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   c.lse2 = reinterpret_cast<float*>(base + lay.lse2);
   c.vct = reinterpret_cast<nsa::bf16_t*>(base + lay.vct);
   c.o_cmp = o_cmp;
-  c.out_f32 = 1;
+  c.out_f32 = 0;
   c.lse_nat = nullptr;
   c.block_scores = bs;
   c.nb_max = lay.nb_max;
@@ -597,11 +597,10 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   e = nsa::launch_select_topk(bs, idx, p->cu_seqlens_q, p->cu_seqlens_k, p->batch, p->rows_total,
                               p->kv_heads, lay.nb_max, p->topk, p->n_init, p->n_local, stream);
   if (e != hipSuccess) return hip_status(e, fn);
-  // 4. selected branch (float32 rows)
-  e = nsa::launch_selected_attn(p->q, p->k, p->v, 1, idx, p->topk, nullptr, p->out, nullptr,
+  // 4. selected branch (bf16 rows)
+  e = nsa::launch_selected_attn(p->q, p->k, p->v, 1, idx, p->topk, nullptr, o_sel, nullptr,
                                 p->cu_seqlens_q, p->cu_seqlens_k, p->batch, p->rows_total,
-                                p->heads, p->kv_heads, sl2, nsa::AttnWs{nullptr, nullptr}, stream,
-                                o_sel);
+                                p->heads, p->kv_heads, sl2, nsa::AttnWs{nullptr, nullptr}, stream);
   if (e != hipSuccess) return hip_status(e, fn);
   // 5. window branch and the gated sum
   nsa::WindowPrefillArgs w{};

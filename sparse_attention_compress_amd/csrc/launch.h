@@ -166,8 +166,8 @@ struct WindowPrefillArgs {
   int out_f32;
   float* lse_nat;        // nullable
   const float* gates;    // nullable [rows, heads, 3]: gated sum with o_cmp and o_sel
-  const float* o_cmp;    // [rows, heads, 128] float32 (with gates)
-  const float* o_sel;    // [rows, heads, 128] float32 (with gates)
+  const bf16_t* o_cmp;   // [rows, heads, 128] (with gates)
+  const bf16_t* o_sel;   // [rows, heads, 128] (with gates)
 };
 hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s);
 

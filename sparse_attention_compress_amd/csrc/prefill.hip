@@ -234,6 +234,12 @@ __device__ __forceinline__ float prev_row_last(float x, float first) {
                                                     0x142 /* row_bcast:15 */, 0xE, 0xF, false));
 }
 
+// Four bf16 values (two packed words) as floats.
+__device__ __forceinline__ float4 bf16x4_to_float4(uint2 w) {
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+}
+
 // Column (head) reductions over the 4 lane rows of a wave.
 __device__ __forceinline__ float rows_max(float x) { return cross32(cross16(x, OpMax()), OpMax()); }
 __device__ __forceinline__ float rows_sum(float x) { return cross32(cross16(x, OpSum()), OpSum()); }
@@ -461,7 +467,7 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
 // --------------------------------------------------------------- window branch
 
 // Sliding-window attention over keys max(0, t-W+1) .. t; with GATED the output
-// is g0 * o_cmp + g1 * o_sel + g2 * o_win (the branch outputs are fp32 rows).
+// is g0 * o_cmp + g1 * o_sel + g2 * o_win (the other branches' outputs are bf16 rows).
 // The wave's tokens share the key tiles of the union of their windows.
 // vtr: the values transposed ([batch][kv][128][ldv]).
 template <int G, bool GATED, int TPW>
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
     int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads,
     int window, float scale_log2, void* __restrict__ out, int out_f32,
     float* __restrict__ lse_nat, const float* __restrict__ gates,
-    const float* __restrict__ o_cmp, const float* __restrict__ o_sel) {
+    const bf16_t* __restrict__ o_cmp, const bf16_t* __restrict__ o_sel) {
   constexpr int D = kHeadDim;
   constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
   __shared__ TileLds T;
@@ -548,12 +554,12 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
       if (c16 < G) {
         const size_t h = head0[j] + c16;
         const float g0 = gates[h * 3 + 0], g1 = gates[h * 3 + 1], g2 = gates[h * 3 + 2];
-        const float* pc = o_cmp + h * D + 4 * r4;
-        const float* ps = o_sel + h * D + 4 * r4;
+        const bf16_t* pc = o_cmp + h * D + 4 * r4;
+        const bf16_t* ps = o_sel + h * D + 4 * r4;
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const float4 a = *reinterpret_cast<const float4*>(pc + 16 * n);
-          const float4 s = *reinterpret_cast<const float4*>(ps + 16 * n);
+          const float4 a = bf16x4_to_float4(*reinterpret_cast<const uint2*>(pc + 16 * n));
+          const float4 s = bf16x4_to_float4(*reinterpret_cast<const uint2*>(ps + 16 * n));
           acc[j][n][0] = g0 * a.x + g1 * s.x + g2 * acc[j][n][0] * inv;
           acc[j][n][1] = g0 * a.y + g1 * s.y + g2 * acc[j][n][1] * inv;
           acc[j][n][2] = g0 * a.z + g1 * s.z + g2 * acc[j][n][2] * inv;
@@ -644,7 +650,7 @@ static hipError_t launch_win_g(const WindowPrefillArgs& a, hipStream_t s) {
                        prefill_block(kTpwOut), s, a.q, a.k,
                        vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
                        a.out_f32, a.lse_nat, static_cast<const float*>(nullptr),
-                       static_cast<const float*>(nullptr), static_cast<const float*>(nullptr));
+                       static_cast<const bf16_t*>(nullptr), static_cast<const bf16_t*>(nullptr));
 }
 
 hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s) {

@@ -354,6 +354,8 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
   }
   // windows of the workgroup: those of its last token
   const int nv_wg = t_last >= kKernel - 1 ? min(nc, (t_last - (kKernel - 1)) / kStride + 1) : 0;
+  // windows every token of the wave sees (its first token's)
+  const int nv_lo = active ? nvis[0] : 0;
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kb = kc + size_t(cbase) * rs + size_t(kv) * D;
   const bf16_t* vt = vct + (size_t(b) * kv_heads + kv) * D * size_t(ldv);
@@ -368,26 +370,34 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
     }
     auto process = [&](int w0, const KeyFrag& ka, const ValFrag& va) {
       // every token runs every tile (windows past its own count are masked), so
-      // the four tokens' chains interleave
+      // the tokens' chains interleave; a tile every token sees whole needs no mask
+      const bool inside = w0 + 32 <= nv_lo;
 #pragma unroll
       for (int j = 0; j < kTpw; ++j) {
-        float sv[8], mx = -INFINITY;
+        float sv[8];  // raw scores; the scale goes into the max and the exponent's fma
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const f32x4_t s = tile_scores(ka, h, qb[j]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[4 * h + e] = w0 + 16 * h + 4 * r4 + e < nvis[j] ? s[e] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[4 * h + e]);
-          }
+          for (int e = 0; e < 4; ++e) sv[4 * h + e] = s[e];
         }
-        mx = rows_max(mx);
+        if (!inside) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (w0 + 16 * (e >> 2) + 4 * r4 + (e & 3) >= nvis[j]) sv[e] = -INFINITY;
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+        mx = rows_max(mx) * scale_log2;
         if (mx > m_run[j]) {
           l_run[j] *= fast_exp2(m_run[j] - mx);
           m_run[j] = mx;
         }
+        if (m_run[j] != -INFINITY) {  // the same in every lane: all heads see the same windows
 #pragma unroll
-        for (int e = 0; e < 8; ++e) l_run[j] += sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run[j]);
+          for (int e = 0; e < 8; ++e) l_run[j] += fast_exp2(fmaf(sv[e], scale_log2, -m_run[j]));
+        }
       }
     };
     lds_tile_loop<false, kThreads>(T, kb, rs, vt, ldv, 0, nv_wg - 1, cmax, active, process);
@@ -402,7 +412,8 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
     f32x4_t acc[kTpw][8];
 #pragma unroll
     for (int j = 0; j < kTpw; ++j) {
-      lh[j] = lse2[head0[j] + min(c16, G - 1)];
+        // columns past the group get +inf, so their probabilities are exactly 0
+      lh[j] = c16 < G ? lse2[head0[j] + c16] : INFINITY;
       carry[j] = 0.f;  // group score of window w0 - 1 (the previous tile's last)
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -410,7 +421,8 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
     const int nb = (len + kBlock - 1) / kBlock;
     auto process = [&](int w0, const KeyFrag& ka, const ValFrag& va) {
       // every token runs every tile (windows past its own count are masked), so
-      // the four tokens' chains interleave
+      // the tokens' chains interleave; a tile every token sees whole needs no mask
+      const bool inside = w0 + 32 <= nv_lo;
 #pragma unroll
       for (int j = 0; j < kTpw; ++j) {
         float p[8];
@@ -418,9 +430,10 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
         for (int h = 0; h < 2; ++h) {
           const f32x4_t s = tile_scores(ka, h, qb[j]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            p[4 * h + e] = (c16 < G && w0 + 16 * h + 4 * r4 + e < nvis[j])
-                               ? fast_exp2(s[e] * scale_log2 - lh[j]) : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const float x = fast_exp2(fmaf(s[e], scale_log2, -lh[j]));
+            p[4 * h + e] = (inside || w0 + 16 * h + 4 * r4 + e < nvis[j]) ? x : 0.f;
+          }
         }
         tile_pv(va, p, acc[j]);
         if (block_scores != nullptr) {

@@ -522,25 +522,36 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  // keys every token of the wave sees: from its last token's window start to
+  // its first token
+  const int in_lo = R.t0 + R.n - 1 - window + 1, in_hi = R.t0;
   auto process = [&](int key0, const KeyFrag& ka, const ValFrag& va) {
+    // every token runs every tile of the union (keys outside its own window
+    // are masked), so the tokens' chains interleave; a tile every token sees
+    // whole needs no mask
+    const bool inside = key0 >= in_lo && key0 + 31 <= in_hi;
 #pragma unroll
     for (int j = 0; j < kTpw; ++j) {
-      // every token runs every tile of the union (keys outside its own window
-      // are masked), so the four tokens' chains interleave
       const int t = R.t0 + j;
       const int lo = max(0, t - window + 1);
-      float sv[8], mx = -INFINITY;
+      float sv[8];  // raw scores; the scale goes into the max and the exponent's fma
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const f32x4_t s = tile_scores(ka, h, qb[j]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = key0 + 16 * h + 4 * r4 + e;
-          sv[4 * h + e] = (key <= t && key >= lo) ? s[e] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sv[4 * h + e]);
+        for (int e = 0; e < 4; ++e) sv[4 * h + e] = s[e];
+      }
+      if (!inside) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = key0 + 16 * (e >> 2) + 4 * r4 + (e & 3);
+          if (key > t || key < lo) sv[e] = -INFINITY;
         }
       }
-      mx = rows_max(mx);
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = rows_max(mx) * scale_log2;
       if (mx > m_run[j] + kLazy) {  // also true for the first tile with a key
         const float alpha = fast_exp2(m_run[j] - mx);
         m_run[j] = mx;
@@ -548,10 +559,11 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[j][n] *= alpha;
       }
+      if (m_run[j] == -INFINITY) continue;  // no key of this token yet (same in every lane)
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run[j]);
+        p[e] = fast_exp2(fmaf(sv[e], scale_log2, -m_run[j]));
         l_run[j] += p[e];
       }
       tile_pv(va, p, acc[j]);

@@ -86,12 +86,14 @@ __global__ __launch_bounds__(256) void transpose_values_kernel(const bf16_t* __r
 typedef uint4 KeyFrag[2][4];
 typedef uint4 ValFrag[8];
 
-// LDS staging of one workgroup's tiles, double-buffered.  Key rows are padded to
-// 272 B and value rows to 80 B so that the 16 rows one A operand reads start in
-// distinct banks.  Value rows hold the tile's 32 keys in k-slot order (keys
-// 4r..4r+3 then 16+4r..16+4r+3 at places 8r .. 8r+7), so each ValFrag entry is
-// one 16-byte read.
-constexpr int kKRow = kHeadDim + 8;  // bf16 per staged key row
+// LDS staging of one workgroup's tiles, double-buffered.  Key rows are 256 B
+// with their sixteen 16-byte chunks XOR-swizzled by the row's low four bits,
+// so the 16 rows one A operand reads hit distinct banks (padding the rows
+// instead measured bank conflicts on these reads).  Value rows are padded to
+// 80 B and hold the tile's 32 keys in k-slot order (keys 4r..4r+3 then
+// 16+4r..16+4r+3 at places 8r .. 8r+7), so each ValFrag entry is one 16-byte
+// read.
+constexpr int kKRow = kHeadDim;  // bf16 per staged key row (16-byte chunks XOR-swizzled by row)
 constexpr int kVRow = 32 + 8;        // bf16 per staged value row (one dim, 32 keys)
 struct TileLds {
   bf16_t k[2][32 * kKRow];
@@ -130,7 +132,7 @@ __device__ __forceinline__ void stash_tile(TileLds& T, int buf, const TileRegs<T
 #pragma unroll
   for (int u = 0; u < TileRegs<THREADS>::kPer; ++u) {
     const int c = tid + THREADS * u;
-    *reinterpret_cast<uint4*>(&T.k[buf][(c >> 4) * kKRow + 8 * (c & 15)]) = r.k[u];
+    *reinterpret_cast<uint4*>(&T.k[buf][(c >> 4) * kKRow + 8 * ((c & 15) ^ ((c >> 4) & 15))]) = r.k[u];
     if constexpr (WITH_V) {
       // keys 8kc .. 8kc+3 go to places p, keys 8kc+4 .. 8kc+7 to p + 8
       const int kc = c & 3;
@@ -148,7 +150,7 @@ __device__ __forceinline__ void read_keys(const TileLds& T, int buf, KeyFrag& ka
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ka[h][i] = *reinterpret_cast<const uint4*>(&T.k[buf][(16 * h + c16) * kKRow + 32 * i + 8 * r4]);
+      ka[h][i] = *reinterpret_cast<const uint4*>(&T.k[buf][(16 * h + c16) * kKRow + 8 * ((4 * i + r4) ^ c16)]);
 }
 
 __device__ __forceinline__ void read_vals(const TileLds& T, int buf, ValFrag& va) {

@@ -327,8 +327,10 @@ nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_
  * Steps: mean-pool K and V into k_c, v_c (written); compressed attention with
  * block scores; top-`topk` blocks per (row, kv head) with n_init / n_local forced
  * blocks (0 and 0 for the pages' configuration); attention over the selected
- * blocks; sliding-window attention; the gated sum into out.  Branch outputs
- * stay float32 in the workspace until the sum.  bfloat16 only.
+ * blocks; sliding-window attention; the gated sum into out.  The compressed and
+ * selected branch outputs wait in the workspace as bfloat16 rows (fp32
+ * accumulation inside each branch); the gated sum is formed in fp32 and
+ * rounded once.  bfloat16 only.
  */
 typedef struct nsa_prefill_params {
   const void* q;               /* [rows, heads, head_dim] bf16 */

@@ -503,7 +503,7 @@ def cpu_baseline(w, layer, lengths, args):
                                      cis_weight=w.cis_weight)
             t_total += time.perf_counter() - t0
             reps += 1
-            if reps >= 20:
+            if reps >= 200:  # bounds the leg if the host is much faster than expected
                 break
     finally:
         if ctx:

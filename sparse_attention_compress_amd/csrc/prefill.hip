@@ -432,10 +432,12 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
         for (int h = 0; h < 2; ++h) {
           const f32x4_t s = tile_scores(ka, h, qb[j]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = fast_exp2(fmaf(s[e], scale_log2, -lh[j]));
-            p[4 * h + e] = (inside || w0 + 16 * h + 4 * r4 + e < nvis[j]) ? x : 0.f;
-          }
+          for (int e = 0; e < 4; ++e) p[4 * h + e] = fast_exp2(fmaf(s[e], scale_log2, -lh[j]));
+        }
+        if (!inside) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (w0 + 16 * (e >> 2) + 4 * r4 + (e & 3) >= nvis[j]) p[e] = 0.f;
         }
         tile_pv(va, p, acc[j]);
         if (block_scores != nullptr) {

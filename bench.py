@@ -66,12 +66,19 @@ ATTN_SOURCES = ["sparse_attention_compress_amd/csrc/attn.hip",
 
 
 def attn_source_hash() -> str:
+    """sha256 (first 16 hex digits) of the select-and-attend kernel's sources with
+    comments and whitespace removed, so that only a change of code invalidates
+    the stored counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
     for rel in ATTN_SOURCES:
-        with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,16 +10,20 @@
 // Design (gfx950; decode is HBM-bound): one workgroup of 4 waves serves one
 // (row, kv head) and a run of selected blocks.  Wave w owns tokens 16w..16w+15
 // of every block and keeps its own online-softmax state, so the block loop has
-// no workgroup barrier.  For q.k a quad of lanes shares a key row (each lane a
-// 32-dim slice via 16-byte loads; the G query heads come from LDS; bf16 products
-// use v_dot2_f32_bf16); for p.v each lane owns 8 dims of 4 tokens, so V rows
-// are read as whole 256-byte lines.  The K/V of the next block are loaded into a
-// second register buffer while the current block is computed.  Every selected
-// K/V byte is fetched from HBM once for the whole query group.  Softmax runs in
-// the exp2 domain (log2 e folded into the scale).
+// no workgroup barrier.  The K/V of the next block are loaded into a second
+// register buffer while the current block is computed, and every selected K/V
+// byte is fetched from HBM once for the whole query group.  Softmax runs in the
+// exp2 domain (log2 e folded into the scale).  Two variants:
+//   * bf16 (decode and prefill rows): both products on the matrix cores (see
+//     selected_attn_mfma_kernel);
+//   * float32 (the fp32 decode configuration): on the vector ALUs; for q.k a
+//     quad of lanes shares a key row (each lane a 32-dim slice via 16-byte
+//     loads, the G query heads from LDS); for p.v each lane owns 8 dims of 4
+//     tokens, so V rows are read as whole 256-byte lines.
 // Decode splits the selected blocks of a (row, kv head) over several workgroups
-// that write partial (max, sum, acc); combine_kernel merges them.  Prefill rows
-// use one workgroup per (row, kv head) and write the output directly.
+// that write partial (max, sum, acc); combine_kernel merges them.  The decode
+// step runs the selection inside that kernel (select_attn_kernel).  Prefill
+// rows use one workgroup per (row, kv head) and write the output directly.
 #include "common.h"
 #include "launch.h"
 #include "select_core.h"
@@ -305,9 +309,10 @@ __global__ __launch_bounds__(256) void selected_attn_valu_kernel(
 // Q^T held in registers); lane (row r, column c) then holds the scores of tokens
 // 4r..4r+3 for head c, so the softmax needs only in-lane work plus two lane
 // swaps for the wave maximum; O^T += V^T P^T with eight v_mfma_f32_16x16x16_bf16
-// takes P^T in exactly that layout (two packed conversions) and V^T from 2-byte
-// loads.  No LDS and no shuffles inside the block loop.  The running maximum is
-// only raised when a block exceeds it by more than 2^8, so rescaling is rare.
+// takes P^T in exactly that layout (two packed conversions) and V^T from the
+// V rows (below).  No LDS and no shuffles inside the block loop.  The running
+// maximum is only raised when a block exceeds it by more than 2^8, so rescaling
+// is rare.  Three waves per SIMD.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

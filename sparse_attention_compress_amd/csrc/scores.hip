@@ -19,16 +19,18 @@
 //   CIS maximum of the blocks the chunk owns (blocks 16j..16j+15, the last chunk
 //   also block 16*n_chunks).  The workgroup owning the newest window can first
 //   recompute that window of the K_c and pooled-CIS caches (decode refresh).
-// select_kernel -- one workgroup of 512 threads per (row, kv head).  Derives the
-//   block scores (group probabilities of all windows staged in LDS) or reads
-//   given scores, then selects: forced blocks, and among the others a 1024-bin
-//   histogram of the scores over [min, max] locates the bin holding the k-th
-//   best; blocks above it are taken, blocks below dropped, and the bin is
-//   refined the same way until at most 512 candidates remain, which are ranked
-//   exactly by (score desc, id asc); exactly equal scores go to the lower ids.
-//   Thread tid keeps the scores and states of ids tid + 512u in registers; the
-//   chosen ids are written in ascending order from wave ballots and one scan of
-//   the per-(slab, wave) counts.
+// select_kernel -- one workgroup of 512 threads per (row, kv head), for rows
+//   with more blocks than the single-kernel decode path takes (up to 4096).
+//   Derives the block scores (group probabilities of the windows, from the
+//   logits kernel's per-chunk normalisers) or reads given scores, then selects
+//   with the histogram top-k of select_core.h: forced blocks, and among the
+//   others a 256-bin histogram of order-preserving keys over their range locates
+//   the bin holding the k-th best; higher bins are taken, lower bins dropped;
+//   a boundary bin of at most 64 candidates is ranked exactly by (score desc,
+//   id asc), a larger one refined on the next 8 bits.  Chosen ids are written in
+//   ascending order from wave ballots and one scan of the per-(slab, wave)
+//   counts.
+// select_wave_kernel -- one wave per (row, kv head) for many short rows (prefill).
 // Every load phase is branch-free (indices clamped into range, values masked)
 // so all of a thread's loads are in flight together.  No kernel waits on another
 // workgroup: each hand-off is a kernel boundary.

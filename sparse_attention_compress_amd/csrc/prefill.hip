@@ -80,18 +80,17 @@ __global__ __launch_bounds__(256) void transpose_values_kernel(const bf16_t* __r
 
 // One 32-key tile (keys key0 .. key0+31, key0 a multiple of 32) as MFMA operands:
 // ka[h] (KeyFrag): A operand of S^T = K Q^T for keys key0 + 16h + c16, dims 32i + 8 r4 .. +8.
-// va[n] (ValFrag): A operand of O^T = V^T P^T for dim 16n + c16; k-slot e < 4
+// read_val(n): A operand of O^T = V^T P^T for dim 16n + c16; k-slot e < 4
 //        holds key key0 + 4 r4 + e, e >= 4 key key0 + 16 + 4 r4 + e - 4 (the same
 //        slots the S^T accumulators give P^T).
 typedef uint4 KeyFrag[2][4];
-typedef uint4 ValFrag[8];
 
 // LDS staging of one workgroup's tiles, double-buffered.  Key rows are 256 B
 // with their sixteen 16-byte chunks XOR-swizzled by the row's low four bits,
 // so the 16 rows one A operand reads hit distinct banks (padding the rows
 // instead measured bank conflicts on these reads).  Value rows are padded to
 // 80 B and hold the tile's 32 keys in k-slot order (keys 4r..4r+3 then
-// 16+4r..16+4r+3 at places 8r .. 8r+7), so each ValFrag entry is one 16-byte
+// 16+4r..16+4r+3 at places 8r .. 8r+7), so each value operand is one 16-byte
 // read.
 constexpr int kKRow = kHeadDim;  // bf16 per staged key row (16-byte chunks XOR-swizzled by row)
 constexpr int kVRow = 32 + 8;        // bf16 per staged value row (one dim, 32 keys)
@@ -153,11 +152,10 @@ __device__ __forceinline__ void read_keys(const TileLds& T, int buf, KeyFrag& ka
       ka[h][i] = *reinterpret_cast<const uint4*>(&T.k[buf][(16 * h + c16) * kKRow + 8 * ((4 * i + r4) ^ c16)]);
 }
 
-__device__ __forceinline__ void read_vals(const TileLds& T, int buf, ValFrag& va) {
+// ValFrag entry n of a staged value tile (vs: one buffer of TileLds::v).
+__device__ __forceinline__ uint4 read_val(const bf16_t* vs, int n) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
-#pragma unroll
-  for (int n = 0; n < 8; ++n)
-    va[n] = *reinterpret_cast<const uint4*>(&T.v[buf][(16 * n + c16) * kVRow + 8 * r4]);
+  return *reinterpret_cast<const uint4*>(&vs[(16 * n + c16) * kVRow + 8 * r4]);
 }
 
 // Tile loop of a workgroup over keys first .. last (first a multiple of 32;
@@ -181,10 +179,8 @@ __device__ __forceinline__ void lds_tile_loop(TileLds& T, const bf16_t* __restri
     if (more) fetch_tile<WITH_V>(kb, rs, vt, ldv, key0 + 32, kmax, r);
     if (active) {
       KeyFrag ka;
-      ValFrag va;
       read_keys(T, buf, ka);
-      if constexpr (WITH_V) read_vals(T, buf, va);
-      process(key0, ka, va);
+      process(key0, ka, static_cast<const bf16_t*>(T.v[buf]));  // values: read_val per fragment
     }
     if (more) stash_tile<WITH_V>(T, buf ^ 1, r);
     __syncthreads();
@@ -203,14 +199,24 @@ __device__ __forceinline__ f32x4_t tile_scores(const uint4 (&ka)[2][4], int h, c
   return s;
 }
 
-// O^T += V^T P^T over the tile's 32 keys; p[e] in the k-slot order of va.
-__device__ __forceinline__ void tile_pv(const uint4 (&va)[8], const float (&p)[8], f32x4_t (&acc)[8]) {
-  const bf16x8_t pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                       (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+// P^T of one token as the B operand: p[e] in the k-slot order of the value tiles.
+__device__ __forceinline__ bf16x8_t pack_p(const float (&p)[8]) {
+  return bf16x8_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                  (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+}
+
+// O^T += V^T P^T over the tile's 32 keys for every token of the wave: each value
+// fragment is read from LDS once and used by all the tokens.
+template <int TPW>
+__device__ __forceinline__ void tile_pv(const bf16_t* vs, const bf16x8_t (&pb)[TPW],
+                                        f32x4_t (&acc)[TPW][8]) {
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
-    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va[n]), pb,
-                                                     acc[n], 0, 0, 0);
+  for (int n = 0; n < 8; ++n) {
+    const bf16x8_t va = __builtin_bit_cast(bf16x8_t, read_val(vs, n));
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+      acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[j], acc[j][n], 0, 0, 0);
+  }
 }
 
 // Group scores of one 16-window half tile: p[e] is the lane's probability of
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
       m_run[j] = -INFINITY;
       l_run[j] = 0.f;
     }
-    auto process = [&](int w0, const KeyFrag& ka, const ValFrag& va) {
+    auto process = [&](int w0, const KeyFrag& ka, const bf16_t*) {
       // every token runs every tile (windows past its own count are masked), so
       // the tokens' chains interleave; a tile every token sees whole needs no mask
       const bool inside = w0 + 32 <= nv_lo;
@@ -421,10 +427,11 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
       for (int n = 0; n < 8; ++n) acc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const int nb = (len + kBlock - 1) / kBlock;
-    auto process = [&](int w0, const KeyFrag& ka, const ValFrag& va) {
+    auto process = [&](int w0, const KeyFrag& ka, const bf16_t* vs) {
       // every token runs every tile (windows past its own count are masked), so
       // the tokens' chains interleave; a tile every token sees whole needs no mask
       const bool inside = w0 + 32 <= nv_lo;
+      bf16x8_t pb[kTpw];
 #pragma unroll
       for (int j = 0; j < kTpw; ++j) {
         float p[8];
@@ -439,7 +446,7 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
           for (int e = 0; e < 8; ++e)
             if (w0 + 16 * (e >> 2) + 4 * r4 + (e & 3) >= nvis[j]) p[e] = 0.f;
         }
-        tile_pv(va, p, acc[j]);
+        pb[j] = pack_p(p);
         if (block_scores != nullptr) {
           // block w0/4 + 4h + r4 covers windows 4i-1 .. 4i+3: the lane row's four
           // windows and the previous row's last (the previous half's last for row 0)
@@ -462,6 +469,7 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
           if (w0 < nvis[j]) carry[j] = lastB;                   // window w0 + 31
         }
       }
+      tile_pv<kTpw>(vs, pb, acc);
     };
     lds_tile_loop<true, kThreads>(T, kb, rs, vt, ldv, 0, nv_wg - 1, cmax, active, process);
 #pragma unroll
@@ -529,11 +537,12 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
   // keys every token of the wave sees: from its last token's window start to
   // its first token
   const int in_lo = R.t0 + R.n - 1 - window + 1, in_hi = R.t0;
-  auto process = [&](int key0, const KeyFrag& ka, const ValFrag& va) {
+  auto process = [&](int key0, const KeyFrag& ka, const bf16_t* vs) {
     // every token runs every tile of the union (keys outside its own window
     // are masked), so the tokens' chains interleave; a tile every token sees
     // whole needs no mask
     const bool inside = key0 >= in_lo && key0 + 31 <= in_hi;
+    bf16x8_t pb[kTpw];
 #pragma unroll
     for (int j = 0; j < kTpw; ++j) {
       const int t = R.t0 + j;
@@ -563,15 +572,20 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[j][n] *= alpha;
       }
-      if (m_run[j] == -INFINITY) continue;  // no key of this token yet (same in every lane)
       float p[8];
+      if (m_run[j] == -INFINITY) {  // no key of this token yet (same in every lane)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(fmaf(sv[e], scale_log2, -m_run[j]));
-        l_run[j] += p[e];
+        for (int e = 0; e < 8; ++e) p[e] = 0.f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(sv[e], scale_log2, -m_run[j]));
+          l_run[j] += p[e];
+        }
       }
-      tile_pv(va, p, acc[j]);
+      pb[j] = pack_p(p);
     }
+    tile_pv<kTpw>(vs, pb, acc);
   };
   lds_tile_loop<true, kThreads>(T, kb, rs, vt, ldv, j_lo, t_last, t_last, active, process);
 #pragma unroll

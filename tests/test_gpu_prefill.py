@@ -246,3 +246,19 @@ def test_prefill_step_ragged_batch_query_tails():
         row0 += n
     log(f"index sets identical on {identical}/{checked} rows")
     assert identical >= 0.3 * checked
+
+
+@pytest.mark.parametrize("heads,kv_heads", [(32, 4), (16, 4)])
+def test_prefill_step_group_sizes(heads, kv_heads):
+    """The whole three-branch step with GQA groups of 8 and 4 query heads."""
+    w = dataclasses.replace(W.scaled(W.nsa_prefill(), [1500]), heads=heads, kv_heads=kv_heads)
+    d = _inputs(w, 4.0)
+    L = w.lengths[0]
+    out = torch.full((L, w.heads, 128), float("nan"), dtype=BF16, device=DEV)
+    idx = torch.full((L, w.kv_heads, w.topk), -7, dtype=torch.int32, device=DEV)
+    p = nsa.prefill_params(d["q"], d["k"], d["v"], d["kc"], d["vc"], d["g"], d["cu_k"], d["cu_k"],
+                           d["cu_c"], L, out, topk=w.topk, window=w.window, indices=idx)
+    log(f"prefill step L={L} heads={heads} kv_heads={kv_heads}")
+    nsa.nsa_prefill_step(p)
+    torch.cuda.synchronize()
+    _check_step(w, d, _rows_of(L, 24, None), out, idx, None, 0.3)

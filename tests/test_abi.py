@@ -178,3 +178,34 @@ def test_prefill_step_checks():
     p.topk = 16
     p.dtype = nsa.NSA_F32
     assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 2
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libnsa.so the binding raises ImportError on first use: there is no
+    fallback path of any kind."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "sparse_attention_compress_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(nsa.__file__), "__init__.py"), pkg / "__init__.py")
+    code = (
+        "import sys\n"
+        f"sys.path.insert(0, {str(tmp_path)!r})\n"
+        "import torch\n"
+        "import sparse_attention_compress_amd as m\n"
+        "assert m.__file__.startswith(sys.path[0])\n"
+        "try:\n"
+        "    m.lib()\n"
+        "except ImportError as e:\n"
+        "    print('IMPORT_ERROR', e)\n"
+        "try:\n"
+        "    x = torch.zeros(64, 2, 128, dtype=torch.bfloat16)\n"
+        "    xc = torch.zeros(3, 2, 128, dtype=torch.float32)\n"
+        "    cu = torch.tensor([0, 64], dtype=torch.int32)\n"
+        "    m.nsa_compress_k(x, xc, cu, torch.tensor([0, 3], dtype=torch.int32), 3)\n"
+        "except ImportError as e:\n"
+        "    print('ENTRY_IMPORT_ERROR', e)\n")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert "IMPORT_ERROR" in res.stdout, res.stdout + res.stderr
+    assert "ENTRY_IMPORT_ERROR" in res.stdout, res.stdout + res.stderr

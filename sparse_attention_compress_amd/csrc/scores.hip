@@ -132,10 +132,14 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
 #pragma unroll
       for (int j = 0; j < kKernel; ++j)
         xv[j] = to_f32(k_src[(size_t(j0 + j) * kv_heads + kv) * D + tid]);
-      // same summation order as the pooling kernel: token by token
+      // same summation order as the pooling kernel: each half of the window
+      // token by token, then the two halves
+      float h0 = 0.f, h1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < kKernel; ++j) racc += xv[j];
-      racc = racc / float(kKernel);
+      for (int j = 0; j < kStride; ++j) h0 += xv[j];
+#pragma unroll
+      for (int j = kStride; j < kKernel; ++j) h1 += xv[j];
+      racc = (h0 + h1) / float(kKernel);
     } else if (cis_src != nullptr && tid >= 128 && tid < 128 + kKernel) {
       rcis = cis_src[size_t(j0 + tid - 128) * kv_heads + kv];
     }
@@ -151,12 +155,16 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
       kc[(size_t(cbase + rw) * kv_heads + kv) * D + tid] = st;
     }
     if (wave == 2) {
-      // lanes 0..31 of wave 2 hold the window's 32 scores; summed in token order
-      float acc = 0.f;
+      // lanes 0..31 of wave 2 hold the window's 32 scores; summed as the
+      // pooling kernel does: each half in token order, then the two halves
+      float h0 = 0.f, h1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < kKernel; ++j)
-        acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rcis), j));
-      const float pooled = acc / float(kKernel);
+      for (int j = 0; j < kStride; ++j)
+        h0 += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rcis), j));
+#pragma unroll
+      for (int j = kStride; j < kKernel; ++j)
+        h1 += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rcis), j));
+      const float pooled = (h0 + h1) / float(kKernel);
       if (lane == 0 && cis_pooled != nullptr) {
         if (cis_src != nullptr) cis_pooled[size_t(cbase + rw) * kv_heads + kv] = pooled;
         cisw_s[rw - c0 + 1] =

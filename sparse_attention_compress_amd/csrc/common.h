@@ -118,9 +118,6 @@ struct OpMax {
 struct OpSum {
   __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
 };
-struct OpSumI {
-  __device__ __forceinline__ int operator()(int a, int b) const { return a + b; }
-};
 struct OpMinI {
   __device__ __forceinline__ int operator()(int a, int b) const { return min(a, b); }
 };
@@ -167,16 +164,6 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return wave_reduce_u32(x, OpUMin()); }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) { return wave_reduce_u32(x, OpUMax()); }
 
-// Integer sum over the whole wave (result in all 64 lanes).
-__device__ __forceinline__ int wave_sum_i(int x) {
-  x += dpp<kDppQuadXor1>(x);
-  x += dpp<kDppQuadXor2>(x);
-  x += dpp<kDppRowHalfMirror>(x);
-  x += dpp<kDppRowMirror>(x);
-  x = cross16i(x, OpSumI());
-  return cross32i(x, OpSumI());
-}
-
 // Integer minimum over the whole wave (result in all 64 lanes).
 __device__ __forceinline__ int wave_min_i(int x) {
   const OpMinI op;
@@ -188,23 +175,6 @@ __device__ __forceinline__ int wave_min_i(int x) {
   return cross32i(x, op);
 }
 __device__ __forceinline__ float wave_sum(float x) { return wave_reduce(x, OpSum()); }
-
-// Reduction over the lanes that share lane % G (G a power of two <= 64): the
-// result for column (lane % G) lands in every lane of that column.
-template <int G, typename Op>
-__device__ __forceinline__ float column_reduce(float x, Op op) {
-  if constexpr (G == 1) {
-    return wave_reduce(x, op);
-  } else {
-    // rotations by 2, 4, 8 inside a row accumulate every lane of the column
-    if constexpr (G <= 2) x = op(x, dpp<kDppRowRor2>(x));
-    if constexpr (G <= 4) x = op(x, dpp<kDppRowRor4>(x));
-    if constexpr (G <= 8) x = op(x, dpp<kDppRowRor8>(x));
-    if constexpr (G <= 16) x = cross16(x, op);
-    if constexpr (G <= 32) x = cross32(x, op);
-    return x;
-  }
-}
 
 // Inclusive prefix sum over the wave (lane order), 6 DPP / swap steps.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {

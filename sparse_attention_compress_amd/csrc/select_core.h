@@ -287,8 +287,9 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
   m = M;
 }
 
-// ml_merge over the lanes that share lane % G (G a power of two <= 16), the
-// schedule of column_reduce: the result for column lane % G lands in all of them.
+// ml_merge over the lanes that share lane % G (G a power of two <= 16): rotations
+// by 2, 4, 8 inside a row (for G = 1 the four quad / mirror steps), then the two
+// row-pair swaps; the result for column lane % G lands in all of them.
 template <int G>
 __device__ __forceinline__ void column_merge_ml(float& m, float& l) {
   auto dpp_step = [&](auto ctrl) {

@@ -357,7 +357,10 @@ __device__ __forceinline__ void stage_ids(const int* ids, int s_begin, int s_end
   if (lane == 0) *nv_s = min(base, kMaxWgSlots);
 }
 
-// B operand of S^T = K Q^T: Q^T[dims 32i + 8 r4 .. +8][head c16] (zero past G).
+// B operand of S^T = K Q^T: Q^T[dims 32i + 8 r4 .. +8][head c16].  Columns past
+// G repeat head G-1: every step of the attention keeps the columns apart and
+// none of theirs is written, so they need no zeroing (which would have to wait
+// for the loads to land).
 template <int G>
 __device__ __forceinline__ void load_q_operand(const bf16_t* __restrict__ q, size_t unit,
                                                uint4 (&qb)[4]) {
@@ -365,10 +368,6 @@ __device__ __forceinline__ void load_q_operand(const bf16_t* __restrict__ q, siz
   const bf16_t* qp = q + (unit * G + min(c16, G - 1)) * kHeadDim + 8 * r4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) qb[i] = ld16(qp + 32 * i);
-  if (c16 >= G) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qb[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
 }
 
 // The G heads of `unit` (query position t of the sequence starting at kstart)
@@ -605,17 +604,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   __shared__ int nv_s;
   const int tid = threadIdx.x;
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const size_t unit = size_t(b) * kv_heads + kv;
+  // the selection's inputs and the queries are in flight while the sequence
+  // offsets arrive
+  ScoreInputs<G, 256, kFusedMaxBlocks> sin;
+  load_score_inputs(sin, logits, part, cisb, unit, n_chunk_max, ldc, ldb);
+  uint4 qb[4];
+  load_q_operand<G>(q, unit, qb);
   const int kstart = cu_k[b];
   const int len = cu_k[b + 1] - kstart;
   const int t = len - 1;
   const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
   const int nvis = min(cu_c[b + 1] - cu_c[b], full_windows_dev(len));
-  const size_t unit = size_t(b) * kv_heads + kv;
   const bool lead = split == 0;
   const SelGeom g = sel_geometry(t, nb, topk, n_init, n_local);
   const int s_begin = split * bpw, s_end = min(topk, s_begin + bpw);
-  uint4 qb[4];
-  load_q_operand<G>(q, unit, qb);  // in flight during the selection
   // A split whose places hold no free pick knows its ids from the geometry
   // alone and skips the selection; the lead split always selects, since it
   // writes the row's indices and block scores.  (Uniform per workgroup.)
@@ -630,9 +633,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     }
   } else {
     float sc[Sel::kPer];
-    block_scores_from_logits<G, 256, kFusedMaxBlocks>(U.sel, sc, logits, part, cisb, cis_weight,
-                                                      unit, nvis, nb, n_chunk_max, ldc, ldb, nb_max,
-                                                      nc_max, lead ? block_scores : nullptr, nullptr);
+    block_scores_from_logits<G, 256, kFusedMaxBlocks>(U.sel, sc, sin, logits, cisb, cis_weight,
+                                                      unit, nvis, nb, ldc, nb_max, nc_max,
+                                                      lead ? block_scores : nullptr, nullptr);
     int* irow = indices != nullptr && lead ? indices + unit * topk : nullptr;
     // every chosen id is eligible (start <= t): the split's ids go straight to
     // its slots, the lead's also to the row's indices
@@ -695,10 +698,13 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float2* __restr
 // --------------------------------------------------------------------------- host
 
 int attn_split_blocks(int batch, int kv_heads, int k_sel) {
-  // enough workgroups to give every CU two, at most 8 blocks each, <= kMaxSplits splits
+  // enough workgroups to give every CU one, at most 8 blocks each, <= kMaxSplits
+  // splits.  More splits spread the block loads wider but every split of a
+  // fused decode row repeats the row's selection (one workgroup per CU measured
+  // fastest: 16 units of 64 blocks at 4 blocks per split)
   const int units = batch * kv_heads;
   int bpw = 8;
-  while (bpw > 1 && units * ((k_sel + bpw - 1) / bpw) < 512) bpw >>= 1;
+  while (bpw > 1 && units * ((k_sel + bpw - 1) / bpw) < 256) bpw >>= 1;
   while ((k_sel + bpw - 1) / bpw > kMaxSplits) bpw <<= 1;
   return bpw;
 }

@@ -269,18 +269,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ SelShared<kSelThreads, kMaxSortBlocks> S;
   const int tid = threadIdx.x;
   const int row = blockIdx.x, kv = blockIdx.y;
+  const size_t unit = size_t(row) * kv_heads + kv;
+  ScoreInputs<G, kSelThreads, kMaxSortBlocks> sin;
+  if constexpr (FROM_LOGITS)  // in flight while the row's position is found
+    load_score_inputs(sin, logits, part, cisb, unit, n_chunk_max, ldc, ldb);
   int b, t;
   row_position(row, cu_q, cu_k, batch, b, t);
   const int len = cu_k[b + 1] - cu_k[b];
   const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
-  const size_t unit = size_t(row) * kv_heads + kv;
   float sc[BigSel::kPer];
   if constexpr (FROM_LOGITS) {
     const int nc = cu_c[b + 1] - cu_c[b];
     const int nvis = min(nc, full_windows_dev(len));
     block_scores_from_logits<G, kSelThreads, kMaxSortBlocks>(
-        S, sc, logits, part, cisb, cis_weight, unit, nvis, nb, n_chunk_max, ldc, ldb, nb_max,
-        nc_max, block_scores, window_probs);
+        S, sc, sin, logits, cisb, cis_weight, unit, nvis, nb, ldc, nb_max, nc_max, block_scores,
+        window_probs);
   } else {
     const int n_slab = (nb + kSelThreads - 1) / kSelThreads;  // uniform
 #pragma unroll

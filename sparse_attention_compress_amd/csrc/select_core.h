@@ -323,9 +323,76 @@ __device__ __forceinline__ void column_merge_ml(float& m, float& l) {
   }
 }
 
+// Inputs of block_scores_from_logits held in registers: the chunk (max, sum)
+// pairs, the windows 4i-1 .. 4i+3 of every head for the first kPre id slabs
+// (later slabs are loaded after the normaliser), and the block CIS maxima.
+template <int G, int THREADS, int MAXB>
+struct ScoreInputs {
+  static constexpr int kPer = SelCfg<THREADS, MAXB>::kPer;
+  static constexpr int kPairs = (MAXB + THREADS - 1) / THREADS;  // n_chunk * G <= MAXB pairs
+  static constexpr int kPre = kPer < 2 ? kPer : (G > 8 ? 1 : 2);
+  float2 ml[kPairs];
+  float4 lg4[kPre][G];
+  float lgp[kPre][G];
+  float cv[kPer];
+};
+
+// Window logits of id slab u (blocks tid + THREADS*u) of one unit's rows: the
+// float4 of windows 4i .. 4i+3 and window 4i-1 for every head, the column
+// clamped into the row (ldc is a multiple of 64 and at least 64).
+template <int G, int THREADS>
+__device__ __forceinline__ void load_window_slab(const float* __restrict__ lrow, int ldc, int u,
+                                                 float4 (&w4)[G], float (&wp)[G]) {
+  const int c0 = min(4 * (int(threadIdx.x) + THREADS * u), ldc - 4);
+  const int cp = max(c0 - 1, 0);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    w4[h] = *reinterpret_cast<const float4*>(lrow + size_t(h) * ldc + c0);
+    wp[h] = lrow[size_t(h) * ldc + cp];
+  }
+}
+
+// Issues the loads of ScoreInputs.  Their addresses depend only on the unit and
+// the buffer geometry (n_chunk_max, ldc, ldb), not on the sequence's length, so
+// a kernel calls this first and the loads overlap its wait for the sequence
+// offsets; every index is clamped into the unit's rows and block_scores_from_logits
+// ignores the values past the sequence's windows and blocks.  With no window
+// buffer at all (n_chunk_max == 0) nothing is loaded.
+template <int G, int THREADS, int MAXB>
+__device__ __forceinline__ void load_score_inputs(ScoreInputs<G, THREADS, MAXB>& in,
+                                                  const float* __restrict__ logits,
+                                                  const float2* __restrict__ part,
+                                                  const float* __restrict__ cisb, size_t unit,
+                                                  int n_chunk_max, int ldc, int ldb) {
+  using In = ScoreInputs<G, THREADS, MAXB>;
+  const int tid = threadIdx.x;
+  const bool any = n_chunk_max > 0;  // uniform
+  const float2* prow = part + unit * n_chunk_max * G;
+#pragma unroll
+  for (int u = 0; u < In::kPairs; ++u)
+    in.ml[u] = any ? prow[min(tid + THREADS * u, n_chunk_max * G - 1)] : make_float2(-INFINITY, 0.f);
+  const float* lrow = logits + unit * G * ldc;
+#pragma unroll
+  for (int u = 0; u < In::kPre; ++u) {
+    if (any) {
+      load_window_slab<G, THREADS>(lrow, ldc, u, in.lg4[u], in.lgp[u]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        in.lg4[u][h] = make_float4(0.f, 0.f, 0.f, 0.f);
+        in.lgp[u][h] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < In::kPer; ++u)
+    in.cv[u] = cisb != nullptr ? cisb[unit * ldb + min(tid + THREADS * u, ldb - 1)] : 0.f;
+}
+
 // Block scores of one decode (sequence, kv head) from the compressed-key logits
 // kernel's outputs (per window and head e = exp2(logit - chunk max) [unit][G][ldc],
-// chunk (max, sum) pairs [unit][n_chunk_max][G], block CIS maxima [unit][ldb]):
+// chunk (max, sum) pairs [unit][n_chunk_max][G], block CIS maxima [unit][ldb]),
+// given the inputs load_score_inputs fetched for the same unit:
 // sc[u] for block i = tid + THREADS*u (u < slabs holding ids < nb; 0 elsewhere).
 // P_h(c) = e_h(c) * exp2(m_h(chunk) - M_h) / L_h, the per-(chunk, head) factor
 // computed once per workgroup into LDS.  The thread owning block i reads the
@@ -335,60 +402,28 @@ __device__ __forceinline__ void column_merge_ml(float& m, float& l) {
 template <int G, int THREADS, int MAXB>
 __device__ __forceinline__ void block_scores_from_logits(
     SelShared<THREADS, MAXB>& S, float (&sc)[SelCfg<THREADS, MAXB>::kPer],
-    const float* __restrict__ logits, const float2* __restrict__ part,
+    const ScoreInputs<G, THREADS, MAXB>& in, const float* __restrict__ logits,
     const float* __restrict__ cisb, float cis_weight, size_t unit, int nvis, int nb,
-    int n_chunk_max, int ldc, int ldb, int nb_max, int nc_max, float* __restrict__ block_scores,
+    int ldc, int nb_max, int nc_max, float* __restrict__ block_scores,
     float* __restrict__ window_probs) {
   using C = SelCfg<THREADS, MAXB>;
+  using In = ScoreInputs<G, THREADS, MAXB>;
   constexpr int P = C::kPer;
+  constexpr int kPairs = In::kPairs;
+  constexpr int kPre = In::kPre;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_slab = (nb + THREADS - 1) / THREADS;  // uniform
   const int n_chunk = (nvis + kChunkWindows - 1) / kChunkWindows;
-  // ---- every load at once: the chunk (max, sum) pairs, each owned block's
-  // five windows for every head, and the block CIS maxima.  Counts of load
-  // rounds are uniform; indices are clamped into range and the values masked.
-  constexpr int kPairs = (MAXB + THREADS - 1) / THREADS;  // n_chunk * G <= MAXB pairs
   const int n_pairs = n_chunk * G;
-  const int n_pu = (n_pairs + THREADS - 1) / THREADS;
-  const float2* prow = part + unit * n_chunk_max * G;
-  float2 ml[kPairs];
-#pragma unroll
-  for (int u = 0; u < kPairs; ++u)
-    ml[u] = u < n_pu ? prow[min(tid + THREADS * u, n_pairs - 1)] : make_float2(-INFINITY, 0.f);
   const float* lrow = logits + unit * G * ldc;
-  const bool any_win = nvis > 0;  // uniform; ldc >= 64 whenever a window exists
-  // the first kPre slabs' windows are loaded here, later slabs after the barriers
-  constexpr int kPre = P < 2 ? P : (G > 8 ? 1 : 2);
-  float4 lg4[kPre][G];
-  float lgp[kPre][G];
-  auto load_slab = [&](int u, float4 (&w4)[G], float (&wp)[G]) {
-    const int c0 = min(4 * (tid + THREADS * u), max(ldc - 4, 0));
-    const int cp = max(c0 - 1, 0);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (u < n_slab && any_win) {
-        w4[h] = *reinterpret_cast<const float4*>(lrow + size_t(h) * ldc + c0);
-        wp[h] = lrow[size_t(h) * ldc + cp];
-      } else {
-        w4[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-        wp[h] = 0.f;
-      }
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < kPre; ++u) load_slab(u, lg4[u], lgp[u]);
-  float cv[P];
   const bool with_cis = cisb != nullptr && n_chunk > 0;
-#pragma unroll
-  for (int u = 0; u < P; ++u)
-    cv[u] = (with_cis && u < n_slab) ? cisb[unit * ldb + min(tid + THREADS * u, ldb - 1)] : 0.f;
 
   // per-head softmax normaliser: merge of the chunk pairs; pair i of this
   // thread belongs to head i % G == tid % G
   float m = -INFINITY, l = 0.f;
 #pragma unroll
   for (int u = 0; u < kPairs; ++u)
-    if (tid + THREADS * u < n_pairs) ml_merge(m, l, ml[u].x, ml[u].y);
+    if (tid + THREADS * u < n_pairs) ml_merge(m, l, in.ml[u].x, in.ml[u].y);
   column_merge_ml<G>(m, l);
   if (lane < G) {
     S.wred[0][wave][lane] = m;
@@ -405,7 +440,7 @@ __device__ __forceinline__ void block_scores_from_logits(
 #pragma unroll
     for (int u = 0; u < kPairs; ++u) {
       const int p = tid + THREADS * u;
-      if (p < n_pairs) S.fac[p] = ml[u].x == -INFINITY ? 0.f : fast_exp2(ml[u].x - Mh) * invL;
+      if (p < n_pairs) S.fac[p] = in.ml[u].x == -INFINITY ? 0.f : fast_exp2(in.ml[u].x - Mh) * invL;
     }
   }
   __syncthreads();
@@ -433,7 +468,7 @@ __device__ __forceinline__ void block_scores_from_logits(
       if (c >= 0 && c < nvis) pm = fmaxf(pm, pg[e]);
     }
     float s = pm == -INFINITY ? 0.f : pm;
-    if (cisb != nullptr) s += cis_weight * (i < owned ? cv[u] : 0.f);
+    if (cisb != nullptr) s += cis_weight * (i < owned ? in.cv[u] : 0.f);
     if (block_scores != nullptr && i < nb) block_scores[unit * nb_max + i] = s;
     if (window_probs != nullptr) {
 #pragma unroll
@@ -449,11 +484,19 @@ __device__ __forceinline__ void block_scores_from_logits(
     sc[u] = 0.f;
     if (u < n_slab) {
       if (u < kPre) {
-        sc[u] = score_slab(u, lg4[u < kPre ? u : 0], lgp[u < kPre ? u : 0]);
+        sc[u] = score_slab(u, in.lg4[u < kPre ? u : 0], in.lgp[u < kPre ? u : 0]);
       } else {
         float4 w4[G];
         float wp[G];
-        load_slab(u, w4, wp);
+        if (ldc > 0) {
+          load_window_slab<G, THREADS>(lrow, ldc, u, w4, wp);
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            w4[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+            wp[h] = 0.f;
+          }
+        }
         sc[u] = score_slab(u, w4, wp);
       }
     }

@@ -218,16 +218,21 @@ __device__ __forceinline__ int topk_select(SelShared<THREADS, MAXB>& S,
         break;
       }
       if (m <= kWave) {
-        // gather the bin's candidates (any order) and rank them exactly in one
-        // wave by (key desc, id asc)
+        // gather the bin's candidates (any order: one LDS atomic per wave and
+        // slab reserves their places) and rank them exactly in one wave by
+        // (key desc, id asc), lane c2's candidate read back with readlane
+        const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
         for (int u = 0; u < P; ++u) {
-          if (st[u] == 2) {
-            const int slot = atomicAdd(&S.n_cand, 1);
-            if (slot < kWave) {
-              S.cand_key[slot] = key[u];
-              S.cand_id[slot] = tid + THREADS * u;
-            }
+          const unsigned long long bm = __ballot(st[u] == 2);
+          if (bm == 0ull) continue;  // uniform in the wave
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&S.n_cand, __popcll(bm));
+          base = __builtin_amdgcn_readlane(base, 0);
+          const int slot = base + __popcll(bm & below);
+          if (st[u] == 2 && slot < kWave) {
+            S.cand_key[slot] = key[u];
+            S.cand_id[slot] = tid + THREADS * u;
           }
         }
         __syncthreads();
@@ -237,8 +242,8 @@ __device__ __forceinline__ int topk_select(SelShared<THREADS, MAXB>& S,
           const int id = lane < mm ? S.cand_id[lane] : 0x7fffffff;
           int rank = 0;
           for (int c2 = 0; c2 < mm; ++c2) {
-            const uint32_t k2 = S.cand_key[c2];
-            const int id2 = S.cand_id[c2];
+            const uint32_t k2 = uint32_t(__builtin_amdgcn_readlane(int(kk), c2));
+            const int id2 = __builtin_amdgcn_readlane(id, c2);
             rank += (k2 > kk || (k2 == kk && id2 < id)) ? 1 : 0;
           }
           if (lane < mm) S.keep[id] = rank < need ? 1 : 0;

@@ -586,7 +586,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 // takes its ids from the geometry and starts on its K/V at once.  Each split
 // then attends to its run and writes a partial state; split 0 always selects
 // and also writes the debug outputs.  Grid (splits, kv heads, sequences).
-template <int G, bool CIS>
+// MAXB bounds the blocks of a sequence: each thread keeps MAXB / 256 of them,
+// so a smaller bound means less work in every step of the selection.
+template <int G, bool CIS, int MAXB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void select_attn_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
     const float* __restrict__ cisb, float cis_weight, const int* __restrict__ cu_k,
@@ -595,9 +597,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     float* __restrict__ block_scores, int* __restrict__ indices, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ cis,
     float scale_log2, int bpw, float2* __restrict__ part_ml, float* __restrict__ part_acc) {
-  using Sel = SelCfg<256, kFusedMaxBlocks>;
+  using Sel = SelCfg<256, MAXB>;
   __shared__ union {
-    SelShared<256, kFusedMaxBlocks> sel;
+    SelShared<256, MAXB> sel;
     MfmaAttnSmem att;
   } U;
   __shared__ int ids_s[kMaxWgSlots];
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   const size_t unit = size_t(b) * kv_heads + kv;
   // the selection's inputs and the queries are in flight while the sequence
   // offsets arrive
-  ScoreInputs<G, 256, kFusedMaxBlocks> sin;
+  ScoreInputs<G, 256, MAXB> sin;
   load_score_inputs(sin, logits, part, cisb, unit, n_chunk_max, ldc, ldb);
   uint4 qb[4];
   load_q_operand<G>(q, unit, qb);
@@ -633,13 +635,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     }
   } else {
     float sc[Sel::kPer];
-    block_scores_from_logits<G, 256, kFusedMaxBlocks>(U.sel, sc, sin, logits, cisb, cis_weight,
+    block_scores_from_logits<G, 256, MAXB>(U.sel, sc, sin, logits, cisb, cis_weight,
                                                       unit, nvis, nb, ldc, nb_max, nc_max,
                                                       lead ? block_scores : nullptr, nullptr);
     int* irow = indices != nullptr && lead ? indices + unit * topk : nullptr;
     // every chosen id is eligible (start <= t): the split's ids go straight to
     // its slots, the lead's also to the row's indices
-    const int total = topk_select<256, kFusedMaxBlocks>(U.sel, sc, g, topk, [&](int pos, int id) {
+    const int total = topk_select<256, MAXB>(U.sel, sc, g, topk, [&](int pos, int id) {
       if (pos >= s_begin && pos < s_end) ids_s[pos - s_begin] = id;
       if (irow != nullptr) irow[pos] = id;
     });
@@ -811,8 +813,10 @@ static hipError_t launch_select_attn_g(const DecodeScoresArgs& a, const void* k,
   const int bpw = attn_split_blocks(a.batch, a.kv_heads, a.topk);
   const int n_split = (a.topk + bpw - 1) / bpw;
   const float* cisb = a.cis_pooled != nullptr ? a.ws.cisb : nullptr;
+  auto kern = d.nb_max <= kFusedSmallBlocks ? select_attn_kernel<G, CIS, kFusedSmallBlocks>
+                                            : select_attn_kernel<G, CIS, kFusedMaxBlocks>;
   hipError_t e = launch_kernel(
-      kKindAttn, select_attn_kernel<G, CIS>, dim3(n_split, a.kv_heads, a.batch), dim3(256), s,
+      kKindAttn, kern, dim3(n_split, a.kv_heads, a.batch), dim3(256), s,
       static_cast<const float*>(a.ws.logits), static_cast<const float2*>(a.ws.part), cisb,
       a.cis_weight, a.cu_k, a.cu_c, a.kv_heads, d.nc_max, d.ldc, d.nb_max, d.n_chunk_max, d.ldb,
       a.topk, a.n_init, a.n_local, a.block_scores, a.indices, static_cast<const bf16_t*>(a.q),

@@ -26,8 +26,10 @@ constexpr int kMaxSortBlocks = 4096;
 // Partial states one decode (row, kv head) may be split into.
 constexpr int kMaxSplits = 64;
 // The decode kernel that selects and attends in one launch handles sequences of
-// up to this many blocks and up to this many selected blocks.
+// up to this many blocks and up to this many selected blocks; batches whose
+// longest sequence has at most kFusedSmallBlocks blocks use a lighter variant.
 constexpr int kFusedMaxBlocks = 1024;
+constexpr int kFusedSmallBlocks = 512;
 constexpr int kFusedMaxSel = 256;
 
 // Kernel kinds that a profiling request can target.

@@ -375,6 +375,17 @@ def test_decode_step_edge_lengths(topk, n_local):
     _check_decode("edge", d, out, bs, idx, topk, 1, n_local, True, False, atol=2e-2)
 
 
+@pytest.mark.parametrize("lengths", [[1000, 60000, 33000], [513 * 64, 200]])
+def test_decode_step_long_rows(lengths):
+    """Rows of more than 512 blocks (up to 1024) in the single-kernel decode
+    path, which then keeps four id slabs per thread instead of two; the second
+    batch sits one block past the lighter variant's bound."""
+    d = _decode_inputs(lengths, SEED + 14)
+    log(f"decode step long rows {lengths}")
+    out, bs, idx = _run_decode_step(d, 64, 1, 16, True, False)
+    _check_decode("long_rows", d, out, bs, idx, 64, 1, 16, True, False, atol=2e-2)
+
+
 @pytest.mark.parametrize("H,H_kv", [(32, 2), (8, 2), (4, 4)])
 def test_decode_step_group_sizes(H, H_kv):
     """GQA groups of 16, 4 and 1 query heads through the single-kernel decode path."""

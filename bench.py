@@ -36,7 +36,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2800)
     ap.add_argument("--warmup", type=int, default=280)
-    ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="distinct layer buffers the decode steps rotate over (default 28 for "
+                         "decode, 12 for decode-long: enough that the selected K/V of the "
+                         "rotation exceeds the 256 MB Infinity Cache)")
     ap.add_argument("--pinned-32k", action="store_true", help="all contexts 32768")
     ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--profile-steps", type=int, default=280)
@@ -45,9 +48,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of from a HIP graph "
                          "(for counter-collection runs, which serialise dispatches)")
-    ap.add_argument("--workload", choices=["decode", "prefill-selected", "prefill-nsa"],
+    ap.add_argument("--workload", choices=["decode", "decode-long", "prefill-selected", "prefill-nsa"],
                     default="decode",
-                    help="decode: the headline NOSA-1B-shaped decode (default); prefill-selected: "
+                    help="decode: the headline NOSA-1B-shaped decode (default); decode-long: "
+                         "CIS-weighted decode of 4 x 131072 tokens; prefill-selected: "
                          "selected-block attention prefill with given indices (batch 8 x 16384); "
                          "prefill-nsa: the three-branch prefill (65536 tokens, 64 heads)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -124,10 +128,15 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    if args.workload != "decode":
+    if args.workload not in ("decode", "decode-long"):
         prefill_main(args, dev)
         return
-    w = W.nosa1b_decode(pinned_32k=args.pinned_32k)
+    if args.workload == "decode-long":
+        w = W.cis_decode()
+        n_layers = args.layers or 12
+    else:
+        w = W.nosa1b_decode(pinned_32k=args.pinned_32k)
+        n_layers = args.layers or 28
     B, H, Hkv, D = w.batch, w.heads, w.kv_heads, w.head_dim
     lengths = list(w.lengths)
     nc = [nsa.full_windows(L) for L in lengths]
@@ -135,10 +144,10 @@ def main():
     cu_c = nsa.cu_seqlens_of(nc, dev)
     max_len = max(lengths)
     kc_dt = torch.float32 if args.kc_dtype == "f32" else torch.bfloat16
-    print(f"[bench] workload {w.name} lengths={lengths} layers={args.layers}", file=sys.stderr, flush=True)
+    print(f"[bench] workload {w.name} lengths={lengths} layers={n_layers}", file=sys.stderr, flush=True)
 
     layers = []
-    for li in range(args.layers):
+    for li in range(n_layers):
         q = W.decode_query(w, dev, layer=li)
         k, v = W.keys_values(w, dev, layer=li)
         cis = W.cis_scores(w, dev, layer=li)
@@ -208,9 +217,9 @@ def main():
           file=sys.stderr, flush=True)
 
     # per-kernel durations, from events recorded at each kernel's own start and end
-    # bf16 decode with up to 1024 blocks and 256 selected blocks per sequence runs the
+    # bf16 decode with up to 2048 blocks and 256 selected blocks per sequence runs the
     # selection inside the attention kernel (one launch per step fewer)
-    fused = (w.dtype == torch.bfloat16 and -(-max_len // 64) <= 1024 and w.topk <= 256)
+    fused = (w.dtype == torch.bfloat16 and -(-max_len // 64) <= 2048 and w.topk <= 256)
     if fused:
         kinds = {"logits_and_refresh": nsa.KERNEL_LOGITS,
                  "select_and_attn": nsa.KERNEL_SELECTED_ATTN, "combine": nsa.KERNEL_COMBINE}
@@ -252,9 +261,10 @@ def main():
                      for L, c in zip(lengths, nc))
     else:
         sel_in = B * Hkv * w.topk * 4                 # block ids
+    cis_sel = sel_tokens * 4 if w.cis_values else 0  # CIS of the selected tokens
     attn_bytes = (sel_tokens * D * elt * 2            # selected K and V rows
                   + 2 * B * H * D * elt               # queries in, outputs out
-                  + sel_in)
+                  + sel_in + cis_sel)
     kc_elt = 4 if kc_dt == torch.float32 else 2
     score_bytes = (sum(nc) * Hkv * D * kc_elt         # compressed keys
                    + sum(nc) * Hkv * 4                # pooled CIS
@@ -262,6 +272,34 @@ def main():
     refresh_bytes = B * (32 * Hkv * D * elt + 32 * Hkv * 4 + Hkv * D * kc_elt + Hkv * 4)
     step_bytes = attn_bytes + score_bytes + refresh_bytes
     attn_gbs = attn_bytes / (kern_us[attn_key] * 1e-6) / 1e9
+
+    # The selected-block attention kernel alone (nsa_selected_attn_fwd over the ids
+    # each layer's step chose), rotating over the layers like the step: the part of
+    # the step that streams the selected K/V, without the selection's latency.
+    sa_out = torch.empty_like(layers[0]["out"])
+    sa_ws = torch.zeros(max(1, nsa.selected_attn_workspace_size(B, H, Hkv, D, w.topk, True)),
+                        dtype=torch.uint8, device=dev)
+    sa_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_prof)]
+
+    def sa_call(i):
+        L_ = layers[i % nl]
+        nsa.nsa_selected_attn_fwd(L_["q"], L_["k"], L_["v"], L_["idx"], cu_k, max_len, sa_out,
+                                  cis=L_["cis"] if w.cis_values else None, workspace=sa_ws)
+
+    with torch.cuda.stream(stream):
+        for i in range(nl):
+            sa_call(i)
+        for a, b in sa_evs:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(n_prof):
+            nsa.nsa_profile_next_launch(nsa.KERNEL_SELECTED_ATTN, *sa_evs[i])
+            sa_call(i)
+    torch.cuda.synchronize()
+    sa_us = float(np.mean([a.elapsed_time(b) for a, b in sa_evs])) * 1e3
+    sa_bytes = sel_tokens * D * elt * 2 + 2 * B * H * D * elt + B * Hkv * w.topk * 4 + cis_sel
 
     result = {
         "metric": METRIC,
@@ -281,7 +319,7 @@ def main():
             "batch": B, "context_lengths": lengths, "heads": H, "kv_heads": Hkv, "head_dim": D,
             "compress_kernel": w.kernel, "compress_stride": w.stride, "block": w.block,
             "topk": w.topk, "forced_init_blocks": w.n_init, "forced_local_blocks": w.n_local,
-            "cis_fused": True, "compressed_key_dtype": args.kc_dtype,
+            "cis_fused": True, "cis_values": bool(w.cis_values), "compressed_key_dtype": args.kc_dtype,
             "layer_buffers_rotated": nl, "step": "one layer, whole batch, HIP-graph replay",
         },
         "roofline": {
@@ -293,12 +331,19 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic(),
+            # the stored counters belong to the fused kernel on the 8K-32K batch
+            "traffic": counter_traffic() if fused and w.name.startswith("nosa1b_decode_b8_L8k") else None,
             "algorithmic_bytes_per_launch": attn_bytes,
             "mean_kernel_us": round(kern_us[attn_key], 3),
             "source_hash": attn_source_hash(),
         },
         "kernel_us": {k_: round(v_, 3) for k_, v_ in kern_us.items()},
+        "selected_attn_alone": {
+            "kernel": "selected_attn_mfma_kernel (nsa_selected_attn_fwd on the step's ids)",
+            "mean_kernel_us": round(sa_us, 3), "algorithmic_bytes_per_launch": sa_bytes,
+            "achieved": round(sa_bytes / (sa_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+            "frac": round(sa_bytes / (sa_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        },
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "tokens_per_s_28_layers": round(tokens_per_s / 28.0, 1),

@@ -814,6 +814,7 @@ static hipError_t launch_select_attn_g(const DecodeScoresArgs& a, const void* k,
   const int n_split = (a.topk + bpw - 1) / bpw;
   const float* cisb = a.cis_pooled != nullptr ? a.ws.cisb : nullptr;
   auto kern = d.nb_max <= kFusedSmallBlocks ? select_attn_kernel<G, CIS, kFusedSmallBlocks>
+             : d.nb_max <= kFusedMidBlocks  ? select_attn_kernel<G, CIS, kFusedMidBlocks>
                                             : select_attn_kernel<G, CIS, kFusedMaxBlocks>;
   hipError_t e = launch_kernel(
       kKindAttn, kern, dim3(n_split, a.kv_heads, a.batch), dim3(256), s,

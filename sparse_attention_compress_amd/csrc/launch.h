@@ -28,7 +28,8 @@ constexpr int kMaxSplits = 64;
 // The decode kernel that selects and attends in one launch handles sequences of
 // up to this many blocks and up to this many selected blocks; batches whose
 // longest sequence has at most kFusedSmallBlocks blocks use a lighter variant.
-constexpr int kFusedMaxBlocks = 1024;
+constexpr int kFusedMaxBlocks = 2048;
+constexpr int kFusedMidBlocks = 1024;
 constexpr int kFusedSmallBlocks = 512;
 constexpr int kFusedMaxSel = 256;
 

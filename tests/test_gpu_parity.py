@@ -375,15 +375,27 @@ def test_decode_step_edge_lengths(topk, n_local):
     _check_decode("edge", d, out, bs, idx, topk, 1, n_local, True, False, atol=2e-2)
 
 
-@pytest.mark.parametrize("lengths", [[1000, 60000, 33000], [513 * 64, 200]])
+@pytest.mark.parametrize("lengths", [[1000, 60000, 33000], [513 * 64, 200], [1025 * 64 - 5, 3000],
+                                     [100000, 2048 * 64]])
 def test_decode_step_long_rows(lengths):
-    """Rows of more than 512 blocks (up to 1024) in the single-kernel decode
-    path, which then keeps four id slabs per thread instead of two; the second
-    batch sits one block past the lighter variant's bound."""
+    """Rows of more than 512 blocks in the single-kernel decode path, which then
+    keeps four (up to 1024 blocks) or eight (up to 2048) id slabs per thread
+    instead of two; the second and third batches sit just past the lighter
+    variants' bounds, the last one at the 2048-block limit."""
     d = _decode_inputs(lengths, SEED + 14)
     log(f"decode step long rows {lengths}")
     out, bs, idx = _run_decode_step(d, 64, 1, 16, True, False)
     _check_decode("long_rows", d, out, bs, idx, 64, 1, 16, True, False, atol=2e-2)
+
+
+@pytest.mark.parametrize("cis_values", [False, True])
+def test_decode_step_beyond_fused_limit(cis_values):
+    """A row of more than 2048 blocks sends the bf16 decode step through the
+    separate selection kernel and the split attention kernel instead."""
+    d = _decode_inputs([2049 * 64 + 17, 5000], SEED + 15)
+    log(f"decode step beyond the single-kernel limit cis_values={cis_values}")
+    out, bs, idx = _run_decode_step(d, 64, 1, 16, True, cis_values, append=True)
+    _check_decode("beyond_fused", d, out, bs, idx, 64, 1, 16, True, cis_values, atol=2e-2)
 
 
 @pytest.mark.parametrize("H,H_kv", [(32, 2), (8, 2), (4, 4)])
@@ -471,8 +483,7 @@ def test_decode_step_nosa1b_full_size(kc_dtype):
 
 def test_decode_step_cis_values_full_size():
     """The long-context CIS-valued decode at full size: 4 sequences of 131072 tokens
-    (2048 blocks each, beyond the single-kernel path's block limit, so the
-    separate select and attention kernels run)."""
+    (2048 blocks each, the single-kernel path's largest variant)."""
     w = W.cis_decode()
     d = _workload_decode_inputs(w, F32)
     log(f"decode step full size {w.name}")

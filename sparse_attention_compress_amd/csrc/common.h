@@ -58,6 +58,16 @@ __device__ __forceinline__ void load8f(const bf16_t* p, float* o) {
   o[4] = bf16lo(a.z); o[5] = bf16hi(a.z); o[6] = bf16lo(a.w); o[7] = bf16hi(a.w);
 }
 
+// 4 consecutive elements as floats.
+__device__ __forceinline__ void load4f(const float* p, float* o) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
+__device__ __forceinline__ void load4f(const bf16_t* p, float* o) {
+  uint2 a = *reinterpret_cast<const uint2*>(p);
+  o[0] = bf16lo(a.x); o[1] = bf16hi(a.x); o[2] = bf16lo(a.y); o[3] = bf16hi(a.y);
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
 __device__ __forceinline__ void store_f32(float* p, float x) { *p = x; }

@@ -65,7 +65,7 @@ __device__ __forceinline__ void row_position(int row, const int* __restrict__ cu
 constexpr int kCisSpan = kChunkWindows + 5;  // windows c0-1 .. c0+67 (17 owned blocks)
 
 template <int G, typename TQ, typename TKC>
-__global__ __launch_bounds__(256) void window_logits_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void window_logits_kernel(
     const TQ* __restrict__ q, TKC* __restrict__ kc, const int* __restrict__ cu_k,
     const int* __restrict__ cu_c, float* __restrict__ logits, float2* __restrict__ part,
     float* __restrict__ cisb, float* __restrict__ cis_pooled, int kv_heads, int ldc,
@@ -98,8 +98,9 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
   // ---- every global load of the workgroup, before the first use.  Lane (c16, r4)
   // holds row c16 of the A operand (window ca) and column c16 of the B operand
   // (query head c16; zero past G).  bf16 tiles: dims 32i + 8 r4 .. +8 form the k
-  // range of tile i.  fp32 tiles: dims 32 r4 .. 32 r4 + 31, dim 32 r4 + j being
-  // the k index r4 of tile j, so the 32 tiles cover every dim once.
+  // range of tile i.  fp32 tiles: tile 4i + e takes dim 16i + 4 r4 + e as its k
+  // index r4, so the 32 tiles cover every dim once and each load instruction
+  // reads 64 contiguous bytes of a row (the four lanes r4 side by side).
   const int ca = c0 + 16 * wave + c16;
   const TKC* krow = kc + (size_t(cbase + min(ca, nvis - 1)) * kv_heads + kv) * D;
   const TQ* qrow = q + (unit * G + min(c16, G - 1)) * D;
@@ -113,9 +114,9 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      load8f(krow + 32 * r4 + 8 * i, &kf[8 * i]);
-      load8f(qrow + 32 * r4 + 8 * i, &qf[8 * i]);
+    for (int i = 0; i < 8; ++i) {
+      load4f(krow + 16 * i + 4 * r4, &kf[4 * i]);
+      load4f(qrow + 16 * i + 4 * r4, &qf[4 * i]);
     }
   }
   float cisv = -INFINITY;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void window_logits_kernel(
   } else {
     if (ca == rw) {
 #pragma unroll
-      for (int j = 0; j < 32; ++j) kf[j] = newf_s[32 * r4 + j];
+      for (int j = 0; j < 32; ++j) kf[j] = newf_s[16 * (j >> 2) + 4 * r4 + (j & 3)];
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j) qf[j] = c16 < G ? qf[j] : 0.f;

@@ -44,6 +44,10 @@ R7 token-level causality inside the diagonal block (keys j <= t).
 R8 CIS mode: o = sum p*cis*v / sum p*cis (the ones-value pass carries the same
    CIS scaling).
 R9 sliding window: keys max(0, t-W+1) .. t (W keys including the query's own).
+R5b two-stage selection (optional): the n_cand best free blocks by the
+   compressed-attention block score are the candidates; the k - |forced| best
+   candidates by the pooled-CIS block score are chosen (ties to the lower index
+   in both stages).  The pages leave n_cand open; callers pass it.
 """
 from __future__ import annotations
 
@@ -190,6 +194,33 @@ def select_blocks(score, t: int, n_blk: int, k: int, n_init: int, n_local: int,
     return out
 
 
+def select_blocks_two_stage(score_qk, score_cis, t: int, n_blk: int, k: int, n_init: int,
+                            n_local: int, block: int, n_cand: int) -> np.ndarray:
+    """R5b: two-stage top-k for one (query position, KV head) (NOSA-1B core
+    components, component 3: a coarse pick of candidate blocks by the
+    compressed-attention block score, then a re-rank by the block score of the
+    pooled CIS down to the top-k).
+
+    Eligible and forced blocks as in select_blocks.  Stage 1: the n_cand best
+    other eligible blocks by score_qk are the candidates.  Stage 2: the
+    k - |forced| best candidates by score_cis are chosen.  Ties go to the lower
+    index in both stages.  Returns k int32 ids, ascending, -1 padded."""
+    score_qk = np.asarray(score_qk, dtype=np.float64)
+    score_cis = np.asarray(score_cis, dtype=np.float64)
+    n_elig = min(n_blk, t // block + 1) if t >= 0 else 0
+    forced = set(range(min(n_init, n_elig)))
+    forced |= set(range(max(0, n_elig - n_local), n_elig))
+    assert len(forced) <= k, "forced blocks must fit in k"
+    rest = [b for b in range(n_elig) if b not in forced]
+    rest.sort(key=lambda b: (-score_qk[b], b))
+    cand = rest[:max(0, n_cand)]
+    cand.sort(key=lambda b: (-score_cis[b], b))
+    chosen = sorted(forced | set(cand[:k - len(forced)]))
+    out = np.full(k, -1, dtype=np.int32)
+    out[:len(chosen)] = chosen
+    return out
+
+
 # ----------------------------------------------------------------------------- attention
 
 
@@ -287,14 +318,17 @@ def decode_block_scores(q, kc_seq, t: int, n_blk: int, kernel: int, stride: int,
 
 def decode_step(q, k, v, cu_seqlens, *, kernel=32, stride=16, block=64, topk=64, n_init=1,
                 n_local=16, scale=None, cis=None, cis_select=False, cis_values=False,
-                cis_weight=1.0, seqs=None):
+                cis_weight=1.0, seqs=None, n_cand=0):
     """One decode step over a packed batch: the newest token (t = L_b - 1) of each
     sequence attends to its selected blocks.
 
     q: [B, H, D]; k, v: [N, H_kv, D]; cis: [N, H_kv] or None.  Returns a dict with
     kc, cis_pooled (all full windows), block_scores [B, H_kv, n_blk_max] (0 beyond a
     sequence's blocks), indices [B, H_kv, topk] and out [B, H, D].  ``seqs`` limits
-    the work to some sequences (others stay zero / -1)."""
+    the work to some sequences (others stay zero / -1).  With n_cand > 0 (and
+    cis_select) the selection is the two-stage one (R5b): block_scores then holds
+    the compressed-attention scores alone and cis_block_scores the pooled-CIS
+    block scores."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -311,6 +345,10 @@ def decode_step(q, k, v, cu_seqlens, *, kernel=32, stride=16, block=64, topk=64,
     kc = np.zeros((int(cuc[-1]), H_kv, D))
     cp = np.zeros((int(cuc[-1]), H_kv)) if cis is not None else None
     scores = np.zeros((B, H_kv, nb_max))
+    cis_scores = np.zeros((B, H_kv, nb_max))
+    two_stage = n_cand > 0
+    if two_stage:
+        assert cis is not None and cis_select, "the two-stage selection needs the pooled CIS"
     idx = np.full((B, H_kv, topk), -1, dtype=np.int32)
     out = np.zeros((B, H, D))
     for b in seqs:
@@ -326,16 +364,24 @@ def decode_step(q, k, v, cu_seqlens, *, kernel=32, stride=16, block=64, topk=64,
             cp[cuc[b]:cuc[b + 1]] = cp_b
         t = L - 1
         nb = n_blocks(L, block)
-        sc = decode_block_scores(q[b], kc_b, t, nb, kernel, stride, block, scale,
-                                 cp_b if cis_select else None, cis_weight)
+        if two_stage:
+            sc = decode_block_scores(q[b], kc_b, t, nb, kernel, stride, block, scale)
+            scc = block_max(np.asarray(cp_b, dtype=np.float64).T, nb, kernel, stride, block)
+            cis_scores[b, :, :nb] = scc
+            for g in range(H_kv):
+                idx[b, g] = select_blocks_two_stage(sc[g], scc[g], t, nb, topk, n_init, n_local,
+                                                    block, n_cand)
+        else:
+            sc = decode_block_scores(q[b], kc_b, t, nb, kernel, stride, block, scale,
+                                     cp_b if cis_select else None, cis_weight)
+            for g in range(H_kv):
+                idx[b, g] = select_blocks(sc[g], t, nb, topk, n_init, n_local, block)
         scores[b, :, :nb] = sc
-        for g in range(H_kv):
-            idx[b, g] = select_blocks(sc[g], t, nb, topk, n_init, n_local, block)
         cis_seq = np.asarray(cis, dtype=np.float64)[s0:s0 + L] if cis_values else None
         out[b] = selected_attention_row(q[b], k[s0:s0 + L], v[s0:s0 + L], idx[b], t, block,
                                         scale, cis_seq)
-    return dict(kc=kc, cis_pooled=cp, block_scores=scores, indices=idx, out=out,
-                cu_seqlens_c=cuc, lengths=lengths)
+    return dict(kc=kc, cis_pooled=cp, block_scores=scores, cis_block_scores=cis_scores,
+                indices=idx, out=out, cu_seqlens_c=cuc, lengths=lengths)
 
 
 def nsa_prefill_rows(q_seq, k_seq, v_seq, gates_seq, rows, *, kernel=32, stride=16, block=64,

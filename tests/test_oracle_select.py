@@ -153,3 +153,97 @@ def test_decode_fusion_with_planted_cis():
     np.testing.assert_allclose(sc[7] - sc[6], 0.4, rtol=1e-12)
     np.testing.assert_allclose(sc[6] - sc[3], 0.4, rtol=1e-12)
     np.testing.assert_allclose(sc[3], 4.0 / n_c + 0.1, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- two-stage selection
+
+def _brute_two_stage(s_qk, s_cis, t, n_blk, k, n_init, n_local, n_cand):
+    """The two-stage rule by counting instead of sorting: a free block is a
+    candidate when fewer than n_cand free blocks beat it on (score_qk desc, id
+    asc), and it is chosen when fewer than k - |forced| candidates beat it on
+    (score_cis desc, id asc)."""
+    n_elig = min(n_blk, t // 64 + 1)
+    forced = set(range(min(n_init, n_elig))) | set(range(max(0, n_elig - n_local), n_elig))
+    free = [b for b in range(n_elig) if b not in forced]
+
+    def beats(s, a, b):  # a ranks above b
+        return s[a] > s[b] or (s[a] == s[b] and a < b)
+
+    cand = [b for b in free if sum(beats(s_qk, a, b) for a in free if a != b) < n_cand]
+    chosen = [b for b in cand
+              if sum(beats(s_cis, a, b) for a in cand if a != b) < k - len(forced)]
+    return sorted(forced | set(chosen))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_two_stage_equals_counting_definition(seed):
+    rng = np.random.default_rng(300 + seed)
+    n_blk = int(rng.integers(3, 14))
+    k = int(rng.integers(2, 9))
+    n_init = int(rng.integers(0, 2))
+    n_local = int(rng.integers(0, 3))
+    if n_init + n_local > k:
+        n_local = k - n_init
+    n_cand = int(rng.integers(0, n_blk + 2))
+    t = int(rng.integers(0, 64 * n_blk))
+    # few distinct values, so ties occur in both stages
+    s_qk = rng.integers(0, 4, n_blk).astype(float)
+    s_cis = rng.integers(0, 3, n_blk).astype(float)
+    got = oracle.select_blocks_two_stage(s_qk, s_cis, t, n_blk, k, n_init, n_local, 64, n_cand)
+    want = _brute_two_stage(s_qk, s_cis, t, n_blk, k, n_init, n_local, n_cand)
+    assert got[:len(want)].tolist() == want
+    assert np.all(got[len(want):] == -1)
+
+
+def test_two_stage_special_cases_reduce_to_one_stage():
+    rng = np.random.default_rng(31)
+    n_blk, k, t = 40, 12, 40 * 64 - 1
+    s_qk, s_cis = rng.random(n_blk), rng.random(n_blk)
+    n_free = n_blk - 1 - 3
+    # every free block a candidate: the CIS scores alone rank them
+    for n_cand in (n_free, n_free + 5):
+        got = oracle.select_blocks_two_stage(s_qk, s_cis, t, n_blk, k, 1, 3, 64, n_cand)
+        assert got.tolist() == oracle.select_blocks(s_cis, t, n_blk, k, 1, 3, 64).tolist()
+    # as many candidates as free places: stage 2 keeps them all
+    got = oracle.select_blocks_two_stage(s_qk, s_cis, t, n_blk, k, 1, 3, 64, k - 4)
+    assert got.tolist() == oracle.select_blocks(s_qk, t, n_blk, k, 1, 3, 64).tolist()
+    # fewer candidates than free places: only forced + candidates, -1 padded
+    got = oracle.select_blocks_two_stage(s_qk, s_cis, t, n_blk, k, 1, 3, 64, 2)
+    best2 = sorted(range(1, n_blk - 3), key=lambda b: (-s_qk[b], b))[:2]
+    assert got.tolist() == sorted([0, 37, 38, 39] + best2) + [-1] * (k - 6)
+
+
+def test_two_stage_planted():
+    # blocks 5, 9 lead on the attention score but have the lowest CIS; block 30
+    # has the best CIS but misses the candidate cut; among the candidates
+    # {5, 9, 12, 20} the CIS keeps 12 and 20.
+    n_blk = 40
+    s_qk = np.zeros(n_blk)
+    s_qk[[5, 9, 12, 20]] = [4.0, 3.0, 2.0, 1.0]
+    s_cis = np.full(n_blk, 0.5)
+    s_cis[[5, 9]] = 0.1
+    s_cis[[12, 20]] = [0.8, 0.7]
+    s_cis[30] = 0.99
+    got = oracle.select_blocks_two_stage(s_qk, s_cis, 64 * n_blk - 1, n_blk, 3, 1, 0, 64, 4)
+    assert got.tolist() == [0, 12, 20]
+
+
+def test_two_stage_decode_with_uniform_attention_and_planted_cis():
+    # q = 0: every block has the same compressed-attention score, so stage 1 takes
+    # the lowest free ids; with CIS 0.9 on block 7 (0.5 on blocks 6 and 8 through
+    # their half-covered windows, 0.1 elsewhere) stage 2 then decides.
+    L, H, H_kv, D = 1024, 8, 2, 16
+    rng = np.random.default_rng(16)
+    k = rng.standard_normal((L, H_kv, D))
+    cis = np.full((L, H_kv), 0.1)
+    cis[448:512] = 0.9
+    q = np.zeros((1, H, D))
+    cu = np.array([0, L])
+    kw = dict(topk=5, n_init=1, n_local=2, cis=cis, cis_select=True)
+    res = oracle.decode_step(q, k, k, cu, n_cand=5, **kw)
+    assert res["indices"][0, 0].tolist() == [0, 1, 2, 14, 15]
+    res = oracle.decode_step(q, k, k, cu, n_cand=13, **kw)
+    assert res["indices"][0, 1].tolist() == [0, 6, 7, 14, 15]
+    np.testing.assert_allclose(res["cis_block_scores"][0, 0, [5, 6, 7, 8]], [0.1, 0.5, 0.9, 0.5],
+                               rtol=1e-12)
+    assert np.ptp(res["block_scores"][0, 0, :16]) == 0.0

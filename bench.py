@@ -42,6 +42,9 @@ def parse():
                          "rotation exceeds the 256 MB Infinity Cache)")
     ap.add_argument("--pinned-32k", action="store_true", help="all contexts 32768")
     ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--n-cand", type=int, default=0,
+                    help="decode: > 0 selects in two stages (the n_cand best blocks by the "
+                         "compressed-attention score, re-ranked by the pooled CIS)")
     ap.add_argument("--profile-steps", type=int, default=280)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,7 +162,8 @@ def main():
         idx = torch.empty((B, Hkv, w.topk), dtype=torch.int32, device=dev)
         p = nsa.decode_params(q, k, v, kc, cu_k, cu_c, max_len, out, topk=w.topk, n_init=w.n_init,
                               n_local=w.n_local, cis=cis, cis_pooled=cp, cis_weight=w.cis_weight,
-                              cis_values=w.cis_values, append_window=True, indices=idx)
+                              cis_values=w.cis_values, append_window=True, indices=idx,
+                              n_cand=args.n_cand)
         layers.append(dict(q=q, k=k, v=v, cis=cis, kc=kc, cp=cp, out=out, idx=idx, p=p))
     torch.cuda.synchronize()
     ws = torch.zeros(nsa.decode_workspace_size(layers[0]["p"]), dtype=torch.uint8, device=dev)
@@ -342,6 +346,8 @@ def main():
             "compress_kernel": w.kernel, "compress_stride": w.stride, "block": w.block,
             "topk": w.topk, "forced_init_blocks": w.n_init, "forced_local_blocks": w.n_local,
             "cis_fused": True, "cis_values": bool(w.cis_values), "compressed_key_dtype": args.kc_dtype,
+            "selection": (f"two-stage, {args.n_cand} candidates" if args.n_cand > 0 else
+                          "one fused score"),
             "layer_buffers_rotated": nl, "step": "one layer, whole batch, HIP-graph replay",
         },
         "roofline": {
@@ -354,7 +360,8 @@ def main():
             "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
             # the stored counters belong to the fused kernel on the 8K-32K batch
-            "traffic": counter_traffic() if fused and w.name.startswith("nosa1b_decode_b8_L8k") else None,
+            "traffic": (counter_traffic() if fused and args.n_cand == 0
+                        and w.name.startswith("nosa1b_decode_b8_L8k") else None),
             "algorithmic_bytes_per_launch": attn_bytes,
             "mean_kernel_us": round(kern_us[attn_key], 3),
             "source_hash": attn_source_hash(),
@@ -580,7 +587,7 @@ def cpu_baseline(w, layer, lengths, args):
             res = oracle.decode_step(q, k, v, cu, kernel=w.kernel, stride=w.stride, block=w.block,
                                      topk=w.topk, n_init=w.n_init, n_local=w.n_local, cis=cis,
                                      cis_select=w.cis_select, cis_values=w.cis_values,
-                                     cis_weight=w.cis_weight)
+                                     cis_weight=w.cis_weight, n_cand=args.n_cand)
             t_total += time.perf_counter() - t0
             reps += 1
             if reps >= 200:  # bounds the leg if the host is much faster than expected

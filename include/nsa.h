@@ -237,6 +237,14 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
  * With append_window != 0 the step first (re)computes the newest full window
  * (index n_c-1) of the K_c and pooled-CIS caches from the K and CIS caches, so a
  * caller that appended tokens completing a window gets an up-to-date cache.
+ * Block choice: with n_cand == 0 one score per block, the compressed-attention
+ * block score plus cis_weight times the block's pooled-CIS maximum (NOSA-1B
+ * source analysis part 3, "beyond the kernel").  With n_cand > 0 the two-stage
+ * choice of NOSA-1B core components, component 3: the n_cand best free blocks
+ * by the compressed-attention score alone are the candidates, and the best
+ * topk - |forced| of them by the pooled-CIS block maximum are kept (ties to the
+ * lower id in both stages); needs cis_pooled; block_scores then receives the
+ * compressed-attention scores alone.  The pages do not give n_cand.
  */
 typedef struct nsa_decode_params {
   const void* q;            /* [batch, heads, head_dim], dtype */
@@ -259,6 +267,7 @@ typedef struct nsa_decode_params {
   int32_t cis_values;       /* != 0: CIS-scaled values with the ones normaliser (needs cis) */
   int32_t append_window;    /* != 0: refresh window n_c-1 of k_c / cis_pooled first */
   float softmax_scale;
+  int32_t n_cand;           /* 0: one fused score; > 0: two-stage choice (needs cis_pooled) */
 } nsa_decode_params;
 
 size_t nsa_decode_workspace_size(const nsa_decode_params* p);

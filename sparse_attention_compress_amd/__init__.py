@@ -49,6 +49,7 @@ class DecodeParams(ctypes.Structure):
         ("head_dim", c_i32), ("kernel", c_i32), ("stride", c_i32), ("block_size", c_i32),
         ("topk", c_i32), ("n_init", c_i32), ("n_local", c_i32), ("cis_weight", c_f32),
         ("cis_values", c_i32), ("append_window", c_i32), ("softmax_scale", c_f32),
+        ("n_cand", c_i32),
     ]
 
 
@@ -251,7 +252,7 @@ def nsa_selected_attn_fwd(q, k, v, indices, cu_seqlens_k, max_seqlen_k, out, cis
 def decode_params(q, k, v, k_c, cu_seqlens_k, cu_seqlens_c, max_seqlen_k, out, topk=64, n_init=1,
                   n_local=16, cis=None, cis_pooled=None, cis_weight=1.0, cis_values=False,
                   append_window=False, block_scores=None, indices=None, softmax_scale=0.0,
-                  kernel=32, stride=16, block_size=64) -> DecodeParams:
+                  kernel=32, stride=16, block_size=64, n_cand=0) -> DecodeParams:
     B, H, D = q.shape
     p = DecodeParams()
     p.q, p.k, p.v, p.k_c = q.data_ptr(), k.data_ptr(), v.data_ptr(), k_c.data_ptr()
@@ -269,6 +270,7 @@ def decode_params(q, k, v, k_c, cu_seqlens_k, cu_seqlens_c, max_seqlen_k, out, t
     p.cis_values = int(bool(cis_values))
     p.append_window = int(bool(append_window))
     p.softmax_scale = float(softmax_scale)
+    p.n_cand = int(n_cand)
     return p
 
 
@@ -349,6 +351,7 @@ def prefill_params(q, k, v, k_c, v_c, gates, cu_seqlens_q, cu_seqlens_k, cu_seql
     p.kernel, p.stride, p.block_size = kernel, stride, block_size
     p.topk, p.n_init, p.n_local, p.window = int(topk), int(n_init), int(n_local), int(window)
     p.softmax_scale = float(softmax_scale)
+    p.n_cand = int(n_cand)
     return p
 
 

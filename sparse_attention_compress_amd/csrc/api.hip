@@ -87,7 +87,7 @@ nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEve
   return ok();
 }
 
-int32_t nsa_version(void) { return 100; }
+int32_t nsa_version(void) { return 200; }
 
 nsa_status nsa_compress_k(const void* x, nsa_dtype x_dtype, void* x_c, nsa_dtype xc_dtype,
                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_c, int32_t batch,
@@ -274,7 +274,10 @@ nsa_status check_decode(const nsa_decode_params* p) {
   const int nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
   NSA_REQUIRE(nb_max <= nsa::kMaxSortBlocks, NSA_ERR_UNSUPPORTED, "%s: %d blocks per sequence exceed the supported %d", fn, nb_max, nsa::kMaxSortBlocks);
   NSA_REQUIRE(std::isfinite(p->cis_weight), NSA_ERR_INVALID_ARG, "%s: cis_weight must be finite", fn);
+  NSA_REQUIRE(p->n_cand >= 0, NSA_ERR_INVALID_ARG, "%s: n_cand must be >= 0", fn);
   if (p->batch == 0) return NSA_OK;
+  NSA_REQUIRE(p->n_cand == 0 || p->cis_pooled != nullptr, NSA_ERR_INVALID_ARG,
+              "%s: the two-stage choice (n_cand > 0) needs cis_pooled", fn);
   NSA_REQUIRE(p->q && p->k && p->v && p->k_c && p->cu_seqlens_k && p->cu_seqlens_c && p->out,
               NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
   NSA_REQUIRE(aligned16(p->q) && aligned16(p->k) && aligned16(p->v) && aligned16(p->k_c) && aligned16(p->out),
@@ -326,6 +329,7 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
   a.topk = p->topk;
   a.n_init = p->n_init;
   a.n_local = p->n_local;
+  a.n_cand = p->n_cand;
   if (p->append_window) {
     a.refresh_k = p->k;
     a.refresh_cis = p->cis_pooled ? p->cis : nullptr;

@@ -593,7 +593,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     const float* __restrict__ logits, const float2* __restrict__ part,
     const float* __restrict__ cisb, float cis_weight, const int* __restrict__ cu_k,
     const int* __restrict__ cu_c, int kv_heads, int nc_max, int ldc, int nb_max,
-    int n_chunk_max, int ldb, int topk, int n_init, int n_local,
+    int n_chunk_max, int ldb, int topk, int n_init, int n_local, int n_cand,
     float* __restrict__ block_scores, int* __restrict__ indices, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ cis,
     float scale_log2, int bpw, float2* __restrict__ part_ml, float* __restrict__ part_acc) {
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
   const int nvis = min(cu_c[b + 1] - cu_c[b], full_windows_dev(len));
   const bool lead = split == 0;
-  const SelGeom g = sel_geometry(t, nb, topk, n_init, n_local);
+  const SelGeom g = sel_geometry(t, nb, topk, n_init, n_local, n_cand);
   const int s_begin = split * bpw, s_end = min(topk, s_begin + bpw);
   // A split whose places hold no free pick knows its ids from the geometry
   // alone and skips the selection; the lead split always selects, since it
@@ -634,14 +634,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
       if (tid == 0) nv_s = n;
     }
   } else {
-    float sc[Sel::kPer];
-    block_scores_from_logits<G, 256, MAXB>(U.sel, sc, sin, logits, cisb, cis_weight,
-                                                      unit, nvis, nb, ldc, nb_max, nc_max,
-                                                      lead ? block_scores : nullptr, nullptr);
+    float sc[Sel::kPer], scc[Sel::kPer];
+    block_scores_from_logits<G, 256, MAXB>(U.sel, sc, scc, n_cand > 0, sin, logits, cisb,
+                                           cis_weight, unit, nvis, nb, ldc, nb_max, nc_max,
+                                           lead ? block_scores : nullptr, nullptr);
     int* irow = indices != nullptr && lead ? indices + unit * topk : nullptr;
     // every chosen id is eligible (start <= t): the split's ids go straight to
     // its slots, the lead's also to the row's indices
-    const int total = topk_select<256, MAXB>(U.sel, sc, g, topk, [&](int pos, int id) {
+    const int total = topk_select<256, MAXB>(U.sel, sc, scc, n_cand, g, topk, [&](int pos, int id) {
       if (pos >= s_begin && pos < s_end) ids_s[pos - s_begin] = id;
       if (irow != nullptr) irow[pos] = id;
     });
@@ -820,7 +820,7 @@ static hipError_t launch_select_attn_g(const DecodeScoresArgs& a, const void* k,
       kKindAttn, kern, dim3(n_split, a.kv_heads, a.batch), dim3(256), s,
       static_cast<const float*>(a.ws.logits), static_cast<const float2*>(a.ws.part), cisb,
       a.cis_weight, a.cu_k, a.cu_c, a.kv_heads, d.nc_max, d.ldc, d.nb_max, d.n_chunk_max, d.ldb,
-      a.topk, a.n_init, a.n_local, a.block_scores, a.indices, static_cast<const bf16_t*>(a.q),
+      a.topk, a.n_init, a.n_local, a.n_cand, a.block_scores, a.indices, static_cast<const bf16_t*>(a.q),
       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), cis_values, a.scale_log2, bpw,
       ws.part_ml, ws.part_acc);
   if (e != hipSuccess) return e;

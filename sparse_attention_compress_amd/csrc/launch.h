@@ -104,6 +104,7 @@ struct DecodeScoresArgs {
   ScoresWs ws;
   int* indices;  // nullable: no selection
   int topk, n_init, n_local;
+  int n_cand;                  // > 0: two-stage selection (candidates, then CIS re-rank)
   const void* refresh_k;       // nullable: recompute the newest window from these keys
   const float* refresh_cis;    // nullable: and the newest pooled CIS from these scores
   int logits_only;             // launch the logits kernel only (the selection runs elsewhere)

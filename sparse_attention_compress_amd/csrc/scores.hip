@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int* __restrict__ cu_k, const int* __restrict__ cu_c, int batch,
     float* __restrict__ block_scores, float* __restrict__ window_probs, int kv_heads,
     int nc_max, int ldc, int nb_max, int n_chunk_max, int ldb, int* __restrict__ indices,
-    int topk, int n_init, int n_local) {
+    int topk, int n_init, int n_local, int n_cand) {
   __shared__ SelShared<kSelThreads, kMaxSortBlocks> S;
   const int tid = threadIdx.x;
   const int row = blockIdx.x, kv = blockIdx.y;
@@ -278,23 +278,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   row_position(row, cu_q, cu_k, batch, b, t);
   const int len = cu_k[b + 1] - cu_k[b];
   const int nb = min(nb_max, (len + kBlock - 1) / kBlock);
-  float sc[BigSel::kPer];
+  float sc[BigSel::kPer], scc[BigSel::kPer];
   if constexpr (FROM_LOGITS) {
     const int nc = cu_c[b + 1] - cu_c[b];
     const int nvis = min(nc, full_windows_dev(len));
     block_scores_from_logits<G, kSelThreads, kMaxSortBlocks>(
-        S, sc, sin, logits, cisb, cis_weight, unit, nvis, nb, ldc, nb_max, nc_max, block_scores,
-        window_probs);
+        S, sc, scc, n_cand > 0, sin, logits, cisb, cis_weight, unit, nvis, nb, ldc, nb_max,
+        nc_max, block_scores, window_probs);
   } else {
     const int n_slab = (nb + kSelThreads - 1) / kSelThreads;  // uniform
 #pragma unroll
-    for (int u = 0; u < BigSel::kPer; ++u)
+    for (int u = 0; u < BigSel::kPer; ++u) {
       sc[u] = u < n_slab ? block_scores[unit * nb_max + min(tid + kSelThreads * u, nb - 1)] : 0.f;
+      scc[u] = 0.f;
+    }
   }
   if (indices == nullptr) return;
   int* out = indices + unit * topk;
   const int total = topk_select<kSelThreads, kMaxSortBlocks>(
-      S, sc, sel_geometry(t, nb, topk, n_init, n_local), topk,
+      S, sc, scc, n_cand, sel_geometry(t, nb, topk, n_init, n_local, n_cand), topk,
       [&](int pos, int id) { out[pos] = id; });
   for (int i = total + tid; i < topk; i += kSelThreads) out[i] = -1;
 }
@@ -431,7 +433,7 @@ static hipError_t launch_scores_g(const DecodeScoresArgs& a, hipStream_t s) {
                        static_cast<const float2*>(a.ws.part), static_cast<const float*>(cisb),
                        a.cis_weight, static_cast<const int*>(nullptr), a.cu_k, a.cu_c, a.batch,
                        a.block_scores, a.window_probs, a.kv_heads, d.nc_max, d.ldc, d.nb_max,
-                       d.n_chunk_max, d.ldb, a.indices, a.topk, a.n_init, a.n_local);
+                       d.n_chunk_max, d.ldb, a.indices, a.topk, a.n_init, a.n_local, a.n_cand);
 }
 
 template <typename TQ, typename TKC>
@@ -486,7 +488,7 @@ hipError_t launch_select_topk(const float* block_scores, int* indices, const int
                        static_cast<const float2*>(nullptr), static_cast<const float*>(nullptr),
                        0.f, cu_q, cu_k, static_cast<const int*>(nullptr), batch,
                        const_cast<float*>(block_scores), static_cast<float*>(nullptr), kv_heads,
-                       0, 0, nb_max, 0, 0, indices, topk, n_init, n_local);
+                       0, 0, nb_max, 0, 0, indices, topk, n_init, n_local, 0);
 }
 
 }  // namespace nsa

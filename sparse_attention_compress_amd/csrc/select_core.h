@@ -86,7 +86,9 @@ struct SelGeom {
   int n_elig, f_init, f_loc, n_free, kf, free_mark;
 };
 
-__device__ __forceinline__ SelGeom sel_geometry(int t, int nb, int topk, int n_init, int n_local) {
+// With n_cand > 0 (two-stage selection) at most n_cand free blocks can be chosen.
+__device__ __forceinline__ SelGeom sel_geometry(int t, int nb, int topk, int n_init, int n_local,
+                                                int n_cand = 0) {
   SelGeom g;
   g.n_elig = t >= 0 ? min(nb, t / kBlock + 1) : 0;
   g.f_init = min(n_init, g.n_elig);
@@ -94,8 +96,160 @@ __device__ __forceinline__ SelGeom sel_geometry(int t, int nb, int topk, int n_i
   const int n_forced = g.f_init + (g.n_elig - g.f_loc);
   g.n_free = g.n_elig - n_forced;
   g.kf = max(0, min(topk - n_forced, g.n_free));
+  if (n_cand > 0) g.kf = min(g.kf, n_cand);
   g.free_mark = g.kf == g.n_free ? 1 : (g.kf == 0 ? 0 : 2);
   return g;
+}
+
+// Resolves every free candidate (st == 2) to chosen (1) or dropped (0): the kf
+// best by (key desc, id asc) are chosen.  Needs 0 < kf < the number of
+// candidates (uniform).  A 256-bin histogram of the keys over their range (a
+// shift of the key offset from the minimum, so binning is exact integer
+// arithmetic) locates the bin holding the kf-th best: keys in higher bins are
+// chosen, lower bins dropped.  If at most 64 candidates share that bin they are
+// gathered and one wave ranks them exactly by (key desc, id asc); otherwise the
+// bin is refined with the next lower bits.
+template <int THREADS, int MAXB>
+__device__ __forceinline__ void resolve_free(SelShared<THREADS, MAXB>& S,
+                                             const uint32_t (&key)[SelCfg<THREADS, MAXB>::kPer],
+                                             int (&st)[SelCfg<THREADS, MAXB>::kPer], int kf) {
+  using C = SelCfg<THREADS, MAXB>;
+  constexpr int P = C::kPer;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    if (st[u] == 2) {
+      kmin = min(kmin, key[u]);
+      kmax = max(kmax, key[u]);
+    }
+  }
+  // ---- key range over the workgroup
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    S.kred[0][wave] = kmin;
+    S.kred[1][wave] = kmax;
+  }
+  for (int i = tid; i < kBins; i += THREADS) S.hist[0][i] = 0;
+  if (tid == 0) S.n_cand = 0;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < C::kWaves; ++w) {
+    kmin = min(kmin, S.kred[0][w]);
+    kmax = max(kmax, S.kred[1][w]);
+  }
+  // offsets from kmin; the bin is the offset's top 8 significant bits
+  const uint32_t span = kmax - kmin;
+  int shift = span == 0u ? 0 : max(0, 24 - __clz(static_cast<int>(span)));  // span >> shift < 256
+  uint32_t lo = 0u;                 // offsets of the current range: [lo, lo + (256 << shift))
+  int need = kf;
+  for (int level = 0; level < 5; ++level) {
+    int* hist = S.hist[level & 1];
+    // the other buffer was last read before the previous level's second
+    // barrier and is next filled after this level's second barrier
+    for (int i = tid; i < kBins; i += THREADS) S.hist[(level + 1) & 1][i] = 0;
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+      if (st[u] == 2) atomicAdd(&hist[((key[u] - kmin - lo) >> shift) & (kBins - 1)], 1);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns bins 255-4l .. 252-4l (descending keys)
+      int c[4], tot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = hist[kBins - 1 - 4 * lane - e];
+        tot += c[e];
+      }
+      const int incl = wave_inclusive_scan(tot);
+      const int above = incl - tot;
+      const int r = need - above;
+      int run = 0, e_star = 0, before = 0, m_star = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        run += c[e];
+        const bool below = run < r;
+        e_star += below ? 1 : 0;
+        before += below ? c[e] : 0;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m_star += e == e_star ? c[e] : 0;
+      if (above < need && need <= incl) {
+        S.misc[0] = kBins - 1 - 4 * lane - e_star;
+        S.misc[1] = above + before;
+        S.misc[2] = m_star;
+      }
+    }
+    __syncthreads();
+    const int bstar = S.misc[0], above = S.misc[1], m = S.misc[2];
+    // decide every candidate outside the boundary bin
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      if (st[u] == 2) {
+        const int bin = int(((key[u] - kmin - lo) >> shift) & (kBins - 1));
+        if (bin != bstar) st[u] = bin > bstar ? 1 : 0;
+      }
+    }
+    need -= above;
+    if (m == need) {  // the whole bin is chosen
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (st[u] == 2) st[u] = 1;
+      break;
+    }
+    if (m > kWave && shift == 0) {
+      // more than 64 candidates share one key value: the lowest ids win
+      bool f[P];
+      int pos[P];
+#pragma unroll
+      for (int u = 0; u < P; ++u) f[u] = st[u] == 2;
+      ordered_positions<THREADS, MAXB>(f, pos, S.cnt[0]);
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (f[u]) st[u] = pos[u] < need ? 1 : 0;
+      break;
+    }
+    if (m <= kWave) {
+      // gather the bin's candidates (any order: one LDS atomic per wave and
+      // slab reserves their places) and rank them exactly in one wave by
+      // (key desc, id asc), lane c2's candidate read back with readlane
+      const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const unsigned long long bm = __ballot(st[u] == 2);
+        if (bm == 0ull) continue;  // uniform in the wave
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&S.n_cand, __popcll(bm));
+        base = __builtin_amdgcn_readlane(base, 0);
+        const int slot = base + __popcll(bm & below);
+        if (st[u] == 2 && slot < kWave) {
+          S.cand_key[slot] = key[u];
+          S.cand_id[slot] = tid + THREADS * u;
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int mm = min(S.n_cand, kWave);
+        const uint32_t kk = lane < mm ? S.cand_key[lane] : 0u;
+        const int id = lane < mm ? S.cand_id[lane] : 0x7fffffff;
+        int rank = 0;
+        for (int c2 = 0; c2 < mm; ++c2) {
+          const uint32_t k2 = uint32_t(__builtin_amdgcn_readlane(int(kk), c2));
+          const int id2 = __builtin_amdgcn_readlane(id, c2);
+          rank += (k2 > kk || (k2 == kk && id2 < id)) ? 1 : 0;
+        }
+        if (lane < mm) S.keep[id] = rank < need ? 1 : 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (st[u] == 2) st[u] = S.keep[tid + THREADS * u];
+      break;
+    }
+    // refine inside the boundary bin
+    lo += uint32_t(bstar) << shift;
+    shift = max(0, shift - 8);
+  }
 }
 
 // Top-k over the eligible ids with scores sc (registers).  Calls emit(pos, id)
@@ -103,160 +257,53 @@ __device__ __forceinline__ SelGeom sel_geometry(int t, int nb, int topk, int n_i
 // and returns the number chosen (in every thread); places from that count to
 // topk are the caller's to pad.  Needs no barrier before it as long as the
 // caller's preceding LDS use is of other fields of S.
-// The free candidates' scores become order-preserving 32-bit keys.  A 256-bin
-// histogram of the keys over their range (a shift of the key offset from the
-// minimum, so binning is exact integer arithmetic) locates the bin holding the
-// kf-th best: keys in higher bins are chosen, lower bins dropped.  If at most 64
-// candidates share that bin they are gathered and one wave ranks them exactly by
-// (key desc, id asc); otherwise the bin is refined with the next lower bits.
-// Chosen ids are then written in ascending order.
+// One stage (n_cand <= 0): the forced ids plus the g.kf best free ids by sc.
+// Two stages (n_cand > 0; g from sel_geometry with the same n_cand): the
+// n_cand best free ids by sc are the candidates, and the g.kf best candidates
+// by scc are chosen; ties go to the lower id in both stages.  The free scores
+// become order-preserving 32-bit keys (resolve_free).  Chosen ids are then
+// written in ascending order from wave ballots and one scan of the per-(slab,
+// wave) counts.
 template <int THREADS, int MAXB, typename Emit>
 __device__ __forceinline__ int topk_select(SelShared<THREADS, MAXB>& S,
                                            const float (&sc)[SelCfg<THREADS, MAXB>::kPer],
-                                           const SelGeom& g, int topk, Emit&& emit) {
+                                           const float (&scc)[SelCfg<THREADS, MAXB>::kPer],
+                                           int n_cand, const SelGeom& g, int topk, Emit&& emit) {
   using C = SelCfg<THREADS, MAXB>;
   constexpr int P = C::kPer;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   int st[P];  // 0 out, 1 chosen, 2 free candidate
   uint32_t key[P];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (n_cand <= 0) {  // uniform
 #pragma unroll
-  for (int u = 0; u < P; ++u) {
-    const int i = tid + THREADS * u;
-    const bool forced = i < g.f_init || (i >= g.f_loc && i < g.n_elig);
-    st[u] = i >= g.n_elig ? 0 : (forced ? 1 : g.free_mark);
-    key[u] = float_key(sc[u] + 0.f);  // + 0 folds -0 into +0 (they compare equal)
-    if (st[u] == 2) {
-      kmin = min(kmin, key[u]);
-      kmax = max(kmax, key[u]);
+    for (int u = 0; u < P; ++u) {
+      const int i = tid + THREADS * u;
+      const bool forced = i < g.f_init || (i >= g.f_loc && i < g.n_elig);
+      st[u] = i >= g.n_elig ? 0 : (forced ? 1 : g.free_mark);
+      key[u] = float_key(sc[u] + 0.f);  // + 0 folds -0 into +0 (they compare equal)
     }
-  }
-  if (g.kf > 0 && g.kf < g.n_free) {  // uniform
-    // ---- key range over the workgroup
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    if (lane == 0) {
-      S.kred[0][wave] = kmin;
-      S.kred[1][wave] = kmax;
+    if (g.kf > 0 && g.kf < g.n_free) resolve_free<THREADS, MAXB>(S, key, st, g.kf);  // uniform
+  } else {
+    bool fz[P];
+    const int c1 = min(n_cand, g.n_free);  // candidates
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int i = tid + THREADS * u;
+      fz[u] = i < g.f_init || (i >= g.f_loc && i < g.n_elig);
+      st[u] = i >= g.n_elig ? 0 : (fz[u] ? 1 : 2);
+      key[u] = float_key(sc[u] + 0.f);
     }
-    for (int i = tid; i < kBins; i += THREADS) S.hist[0][i] = 0;
-    if (tid == 0) S.n_cand = 0;
-    __syncthreads();
+    if (c1 < g.n_free) resolve_free<THREADS, MAXB>(S, key, st, c1);  // c1 > 0: n_free > 0
+    // stage 2 over the candidates (free ids still in)
+    const int kf2 = min(g.kf, c1);
 #pragma unroll
-    for (int w = 0; w < C::kWaves; ++w) {
-      kmin = min(kmin, S.kred[0][w]);
-      kmax = max(kmax, S.kred[1][w]);
+    for (int u = 0; u < P; ++u) {
+      st[u] = fz[u] ? 1 : (st[u] != 0 ? (kf2 == c1 ? 1 : (kf2 == 0 ? 0 : 2)) : 0);
+      key[u] = float_key(scc[u] + 0.f);
     }
-    // offsets from kmin; the bin is the offset's top 8 significant bits
-    const uint32_t span = kmax - kmin;
-    int shift = span == 0u ? 0 : max(0, 24 - __clz(static_cast<int>(span)));  // span >> shift < 256
-    uint32_t lo = 0u;                 // offsets of the current range: [lo, lo + (256 << shift))
-    int need = g.kf;
-    for (int level = 0; level < 5; ++level) {
-      int* hist = S.hist[level & 1];
-      // the other buffer was last read before the previous level's second
-      // barrier and is next filled after this level's second barrier
-      for (int i = tid; i < kBins; i += THREADS) S.hist[(level + 1) & 1][i] = 0;
-#pragma unroll
-      for (int u = 0; u < P; ++u)
-        if (st[u] == 2) atomicAdd(&hist[((key[u] - kmin - lo) >> shift) & (kBins - 1)], 1);
-      __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 255-4l .. 252-4l (descending keys)
-        int c[4], tot = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c[e] = hist[kBins - 1 - 4 * lane - e];
-          tot += c[e];
-        }
-        const int incl = wave_inclusive_scan(tot);
-        const int above = incl - tot;
-        const int r = need - above;
-        int run = 0, e_star = 0, before = 0, m_star = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          run += c[e];
-          const bool below = run < r;
-          e_star += below ? 1 : 0;
-          before += below ? c[e] : 0;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m_star += e == e_star ? c[e] : 0;
-        if (above < need && need <= incl) {
-          S.misc[0] = kBins - 1 - 4 * lane - e_star;
-          S.misc[1] = above + before;
-          S.misc[2] = m_star;
-        }
-      }
-      __syncthreads();
-      const int bstar = S.misc[0], above = S.misc[1], m = S.misc[2];
-      // decide every candidate outside the boundary bin
-#pragma unroll
-      for (int u = 0; u < P; ++u) {
-        if (st[u] == 2) {
-          const int bin = int(((key[u] - kmin - lo) >> shift) & (kBins - 1));
-          if (bin != bstar) st[u] = bin > bstar ? 1 : 0;
-        }
-      }
-      need -= above;
-      if (m == need) {  // the whole bin is chosen
-#pragma unroll
-        for (int u = 0; u < P; ++u)
-          if (st[u] == 2) st[u] = 1;
-        break;
-      }
-      if (m > kWave && shift == 0) {
-        // more than 64 candidates share one key value: the lowest ids win
-        bool f[P];
-        int pos[P];
-#pragma unroll
-        for (int u = 0; u < P; ++u) f[u] = st[u] == 2;
-        ordered_positions<THREADS, MAXB>(f, pos, S.cnt[0]);
-#pragma unroll
-        for (int u = 0; u < P; ++u)
-          if (f[u]) st[u] = pos[u] < need ? 1 : 0;
-        break;
-      }
-      if (m <= kWave) {
-        // gather the bin's candidates (any order: one LDS atomic per wave and
-        // slab reserves their places) and rank them exactly in one wave by
-        // (key desc, id asc), lane c2's candidate read back with readlane
-        const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-        for (int u = 0; u < P; ++u) {
-          const unsigned long long bm = __ballot(st[u] == 2);
-          if (bm == 0ull) continue;  // uniform in the wave
-          int base = 0;
-          if (lane == 0) base = atomicAdd(&S.n_cand, __popcll(bm));
-          base = __builtin_amdgcn_readlane(base, 0);
-          const int slot = base + __popcll(bm & below);
-          if (st[u] == 2 && slot < kWave) {
-            S.cand_key[slot] = key[u];
-            S.cand_id[slot] = tid + THREADS * u;
-          }
-        }
-        __syncthreads();
-        if (wave == 0) {
-          const int mm = min(S.n_cand, kWave);
-          const uint32_t kk = lane < mm ? S.cand_key[lane] : 0u;
-          const int id = lane < mm ? S.cand_id[lane] : 0x7fffffff;
-          int rank = 0;
-          for (int c2 = 0; c2 < mm; ++c2) {
-            const uint32_t k2 = uint32_t(__builtin_amdgcn_readlane(int(kk), c2));
-            const int id2 = __builtin_amdgcn_readlane(id, c2);
-            rank += (k2 > kk || (k2 == kk && id2 < id)) ? 1 : 0;
-          }
-          if (lane < mm) S.keep[id] = rank < need ? 1 : 0;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < P; ++u)
-          if (st[u] == 2) st[u] = S.keep[tid + THREADS * u];
-        break;
-      }
-      // refine inside the boundary bin
-      lo += uint32_t(bstar) << shift;
-      shift = max(0, shift - 8);
+    if (kf2 > 0 && kf2 < c1) {  // uniform
+      __syncthreads();  // stage 1's last LDS reads are behind every thread
+      resolve_free<THREADS, MAXB>(S, key, st, kf2);
     }
   }
   // ordered compaction of the chosen ids
@@ -402,11 +449,14 @@ __device__ __forceinline__ void load_score_inputs(ScoreInputs<G, THREADS, MAXB>&
 // P_h(c) = e_h(c) * exp2(m_h(chunk) - M_h) / L_h, the per-(chunk, head) factor
 // computed once per workgroup into LDS.  The thread owning block i reads the
 // values of its windows 4i-1 .. 4i+3 itself, so no window value crosses threads.
-// Optional debug outputs: block_scores [unit][nb_max] (0 past nb) and
-// window_probs [unit][nc_max].  Two workgroup barriers.
+// With split_cis (two-stage selection) sc holds the attention part alone and
+// scc the block CIS maxima; otherwise sc = attention part + cis_weight * CIS
+// maximum and scc is 0.  Optional debug outputs: block_scores [unit][nb_max]
+// (sc; 0 past nb) and window_probs [unit][nc_max].  Two workgroup barriers.
 template <int G, int THREADS, int MAXB>
 __device__ __forceinline__ void block_scores_from_logits(
     SelShared<THREADS, MAXB>& S, float (&sc)[SelCfg<THREADS, MAXB>::kPer],
+    float (&scc)[SelCfg<THREADS, MAXB>::kPer], bool split_cis,
     const ScoreInputs<G, THREADS, MAXB>& in, const float* __restrict__ logits,
     const float* __restrict__ cisb, float cis_weight, size_t unit, int nvis, int nb,
     int ldc, int nb_max, int nc_max, float* __restrict__ block_scores,
@@ -473,7 +523,13 @@ __device__ __forceinline__ void block_scores_from_logits(
       if (c >= 0 && c < nvis) pm = fmaxf(pm, pg[e]);
     }
     float s = pm == -INFINITY ? 0.f : pm;
-    if (cisb != nullptr) s += cis_weight * (i < owned ? in.cv[u] : 0.f);
+    if (cisb != nullptr) {
+      const float cv = i < owned ? in.cv[u] : 0.f;
+      if (split_cis)
+        scc[u] = cv;
+      else
+        s += cis_weight * cv;
+    }
     if (block_scores != nullptr && i < nb) block_scores[unit * nb_max + i] = s;
     if (window_probs != nullptr) {
 #pragma unroll
@@ -487,6 +543,7 @@ __device__ __forceinline__ void block_scores_from_logits(
 #pragma unroll
   for (int u = 0; u < P; ++u) {
     sc[u] = 0.f;
+    scc[u] = 0.f;
     if (u < n_slab) {
       if (u < kPre) {
         sc[u] = score_slab(u, in.lg4[u < kPre ? u : 0], in.lgp[u < kPre ? u : 0]);

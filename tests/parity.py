@@ -86,3 +86,30 @@ def check_index_sets(name, gpu_idx, ref_idx, ref_scores, t, nb, k, n_init, n_loc
     for b in set(g) ^ set(r):
         assert abs(float(ref_scores[b]) - kth) <= BAND, f"{name}: block {b} outside the tie band"
     return False, band_pop
+
+
+def check_two_stage_sets(name, gpu_idx, ref_idx, s_qk, s_cis, t, nb, k, n_init, n_local, n_cand,
+                         block=64):
+    """The agreement rule for the two-stage choice on one (row, kv head): the
+    sets must be equal unless the oracle's stage-1 boundary (n_cand-th against
+    (n_cand+1)-th free attention score) or its stage-2 boundary (the last kept
+    against the first dropped candidate CIS score) lies within the band; the
+    GPU set must be well formed in any case.  Returns whether they are equal."""
+    g = sorted(int(x) for x in gpu_idx if x >= 0)
+    r = sorted(int(x) for x in ref_idx if x >= 0)
+    assert list(gpu_idx[len(g):]) == [-1] * (len(gpu_idx) - len(g)), f"{name}: bad padding {gpu_idx}"
+    assert list(gpu_idx[:len(g)]) == g, f"{name}: not ascending {gpu_idx}"
+    if g == r:
+        return True
+    free, forced = free_scores_sorted(s_qk, t, nb, n_init, n_local, block)
+    assert len(g) == len(r), f"{name}: {len(g)} ids vs {len(r)}"
+    assert forced <= set(g), f"{name}: forced blocks missing"
+    c1 = min(n_cand, len(free))
+    near1 = 0 < c1 < len(free) and free[c1 - 1][0] - free[c1][0] <= BAND
+    cand = sorted((float(s_cis[b]), b) for _, b in free[:c1])
+    cand.sort(key=lambda x: (-x[0], x[1]))
+    kf = min(k - len(forced), c1)
+    near2 = 0 < kf < c1 and cand[kf - 1][0] - cand[kf][0] <= BAND
+    assert near1 or near2, (f"{name}: index sets differ with both stage boundaries outside the "
+                            f"band: {g} vs {r}")
+    return False

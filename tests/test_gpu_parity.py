@@ -11,7 +11,7 @@ import gen
 import oracle
 import sparse_attention_compress_amd as nsa
 from gen import workloads as W
-from parity import assert_close, check_index_sets, cu, log, np64
+from parity import assert_close, check_index_sets, check_two_stage_sets, cu, log, np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -396,6 +396,79 @@ def test_decode_step_beyond_fused_limit(cis_values):
     log(f"decode step beyond the single-kernel limit cis_values={cis_values}")
     out, bs, idx = _run_decode_step(d, 64, 1, 16, True, cis_values, append=True)
     _check_decode("beyond_fused", d, out, bs, idx, 64, 1, 16, True, cis_values, atol=2e-2)
+
+
+def _run_two_stage(d, topk, n_init, n_local, n_cand, append=False):
+    B, H = len(d["lengths"]), d["H"]
+    max_len = max(d["lengths"])
+    nb_max = -(-max_len // 64)
+    out = torch.full((B, H, 128), float("nan"), dtype=d["q"].dtype, device=DEV)
+    bs = torch.full((B, d["H_kv"], nb_max), float("nan"), device=DEV)
+    idx = torch.full((B, d["H_kv"], topk), -7, dtype=torch.int32, device=DEV)
+    p = nsa.decode_params(d["q"], d["k"], d["v"], d["kc"], d["cu_k"], d["cu_c"], max_len, out,
+                          topk=topk, n_init=n_init, n_local=n_local, cis=d["cis"],
+                          cis_pooled=d["cp"], append_window=append, block_scores=bs, indices=idx,
+                          n_cand=n_cand)
+    nsa.nsa_decode_step(p, device=DEV)
+    torch.cuda.synchronize()
+    return out, bs, idx
+
+
+@pytest.mark.parametrize("dtype,lengths", [
+    (BF16, [0, 40, 1000, 4097, 20000, 33000]),       # single-kernel path
+    (F32, [40, 3000, 9000]),                         # separate selection kernel
+    (BF16, [2049 * 64 + 17, 700]),                   # beyond the single-kernel bound
+])
+def test_decode_step_two_stage_uniform_attention(dtype, lengths):
+    """Two-stage choice with zero queries: every attention block score is exactly
+    tied on both sides, so stage 1 keeps the lowest free ids and stage 2 ranks
+    them by the pooled CIS alone; index sets must be identical."""
+    d = _decode_inputs(lengths, SEED + 16, dtype=dtype)
+    d["q"].zero_()
+    topk, n_init, n_local, n_cand = 32, 1, 8, 48
+    log(f"decode step two-stage uniform attention {lengths} dtype={dtype}")
+    out, bs, idx = _run_two_stage(d, topk, n_init, n_local, n_cand, append=True)
+    q, k, v, cis = np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["cis"])
+    res = oracle.decode_step(q, k, v, _cu_np(d["cu_k"]), topk=topk, n_init=n_init,
+                             n_local=n_local, cis=cis, cis_select=True, n_cand=n_cand)
+    idx_g = idx.cpu().numpy()
+    assert (idx_g == res["indices"]).all(), "two-stage index sets differ"
+    assert_close("two_stage_uniform.block_scores", np64(bs), res["block_scores"][:, :, :bs.shape[2]],
+                 atol=1e-9, rtol=1e-4)
+    atol = 1e-4 if dtype == F32 else 2e-2
+    assert_close("two_stage_uniform.out", np64(out), res["out"], atol=atol)
+
+
+@pytest.mark.parametrize("n_cand", [16, 64, 100, 5000])
+def test_decode_step_two_stage(n_cand):
+    """Two-stage choice on N(0,1) queries through the single-kernel path: the
+    sets agree unless one of the oracle's stage boundaries is inside the band;
+    outputs are compared where they agree.  n_cand 16 keeps fewer than the free
+    places; 5000 makes every free block a candidate."""
+    lengths = [3000, 9000, 20000, 31000]
+    d = _decode_inputs(lengths, SEED + 17)
+    topk, n_init, n_local = 64, 1, 16
+    log(f"decode step two-stage n_cand={n_cand}")
+    out, bs, idx = _run_two_stage(d, topk, n_init, n_local, n_cand)
+    q, k, v, cis = np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["cis"])
+    res = oracle.decode_step(q, k, v, _cu_np(d["cu_k"]), topk=topk, n_init=n_init,
+                             n_local=n_local, cis=cis, cis_select=True, n_cand=n_cand)
+    assert_close("two_stage.block_scores", np64(bs), res["block_scores"][:, :, :bs.shape[2]],
+                 atol=1e-9, rtol=1e-4)
+    idx_g, out_g = idx.cpu().numpy(), np64(out)
+    exact = 0
+    for b, L in enumerate(lengths):
+        nb = -(-L // 64)
+        for g in range(2):
+            ok = check_two_stage_sets(f"two_stage[{b},{g}]", idx_g[b, g], res["indices"][b, g],
+                                      res["block_scores"][b, g], res["cis_block_scores"][b, g],
+                                      L - 1, nb, topk, n_init, n_local, n_cand)
+            if ok:
+                exact += 1
+                assert_close(f"two_stage.out[{b},{g}]", out_g[b, g * 8:(g + 1) * 8],
+                             res["out"][b, g * 8:(g + 1) * 8], atol=2e-2)
+    log(f"[two_stage n_cand={n_cand}] identical index sets for {exact}/{2 * len(lengths)}")
+    assert exact >= 1
 
 
 @pytest.mark.parametrize("H,H_kv", [(32, 2), (8, 2), (4, 4)])

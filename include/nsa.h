@@ -105,7 +105,8 @@ int32_t nsa_version(void);
  * selection, 3 selected attention, 4 merge of split partial states (decode),
  * 5 compressed-attention normaliser pass (prefill), 6 compressed-attention
  * output and block-score pass (prefill), 7 sliding-window attention (prefill,
- * with the gated sum in nsa_prefill_step).  The events are owned by the caller
+ * with the gated sum in nsa_prefill_step), 8 block copies from host memory
+ * (nsa_decode_step_offload).  The events are owned by the caller
  * and must have timing enabled; a launch made during stream capture must not
  * be armed.
  */
@@ -117,7 +118,8 @@ typedef enum nsa_kernel_kind {
   NSA_KERNEL_COMBINE = 4,
   NSA_KERNEL_COMPRESSED_LSE = 5,
   NSA_KERNEL_COMPRESSED_ATTN = 6,
-  NSA_KERNEL_WINDOW_ATTN = 7
+  NSA_KERNEL_WINDOW_ATTN = 7,
+  NSA_KERNEL_FETCH = 8
 } nsa_kernel_kind;
 nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
 
@@ -273,6 +275,60 @@ typedef struct nsa_decode_params {
 size_t nsa_decode_workspace_size(const nsa_decode_params* p);
 nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * KV offload for decode: the K/V cache stays in host memory and each step moves
+ * to the GPU only the selected blocks it does not already hold.
+ * [NOSA-1B core components: the core idea (the whole KV cache offloaded to CPU
+ *  memory, only the few important blocks brought back for each step's
+ *  attention) and the decode stage.]
+ * The caller owns the state, all of it in device memory:
+ *   k_pool, v_pool  [batch*kv_heads, pool_slots, 64, head_dim] of the decode
+ *                   dtype (nsa_offload_pool_bytes each): the K/V rows of the
+ *                   blocks each (sequence, KV head) holds
+ *   slot_of         int32 [batch*kv_heads, nb_cap]: the pool slot holding a
+ *                   block, -1 if none
+ *   block_of        int32 [batch*kv_heads, pool_slots]: the block a slot holds,
+ *                   -1 if empty
+ *   fetched         nullable int32 [batch*kv_heads], written by every step: the
+ *                   blocks it copied from host memory
+ * nsa_offload_reset marks every slot empty; call it before the first step and
+ * whenever a (sequence, KV head) place of the batch changes owner.  Steps that
+ * share a state must not overlap.  Limits: pool_slots <= 1024, nb_cap <= 4096.
+ */
+typedef struct nsa_offload_state {
+  void* k_pool;
+  void* v_pool;
+  int32_t* slot_of;
+  int32_t* block_of;
+  int32_t* fetched;
+  int32_t pool_slots;
+  int32_t nb_cap;
+} nsa_offload_state;
+size_t nsa_offload_pool_bytes(int32_t batch, int32_t kv_heads, int32_t pool_slots,
+                              int32_t head_dim, nsa_dtype dtype);
+nsa_status nsa_offload_reset(const nsa_offload_state* o, int32_t batch, int32_t kv_heads,
+                             hipStream_t stream);
+
+/*
+ * nsa_decode_step_offload -- nsa_decode_step with p->k and p->v in host memory
+ * (pinned, hipHostMalloc), read by the GPU over the host link.  The step scores
+ * and selects as nsa_decode_step does (compressed keys, CIS and every other
+ * array stay in device memory; with append_window the newest window's 32 key
+ * rows are read from host memory), then, per (sequence, KV head): listed
+ * blocks already in a slot are kept; every other listed block takes the next
+ * free slot (empty slots first, then slots holding a block this step does not
+ * list, each in ascending order; misses in list order) and its 64 K and V rows
+ * of that KV head are copied from host memory;
+ * then attention runs over the pool.  The outputs equal nsa_decode_step's on
+ * the same inputs.  bfloat16 only; topk <= 256 and topk <= pool_slots; blocks per
+ * sequence <= nb_cap.  Errors as nsa_decode_step, plus NSA_ERR_INVALID_ARG /
+ * NSA_ERR_UNSUPPORTED for a state outside these limits.
+ *   workspace: nsa_decode_offload_workspace_size(p, o) bytes.
+ */
+size_t nsa_decode_offload_workspace_size(const nsa_decode_params* p, const nsa_offload_state* o);
+nsa_status nsa_decode_step_offload(const nsa_decode_params* p, const nsa_offload_state* o,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nsa_compressed_attn_fwd -- compressed-branch attention of prefill rows, and

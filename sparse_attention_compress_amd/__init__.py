@@ -53,6 +53,14 @@ class DecodeParams(ctypes.Structure):
     ]
 
 
+class OffloadState(ctypes.Structure):
+    """Mirror of ``nsa_offload_state``."""
+    _fields_ = [
+        ("k_pool", c_vp), ("v_pool", c_vp), ("slot_of", c_vp), ("block_of", c_vp),
+        ("fetched", c_vp), ("pool_slots", c_i32), ("nb_cap", c_i32),
+    ]
+
+
 class PrefillParams(ctypes.Structure):
     """Mirror of ``nsa_prefill_params``."""
     _fields_ = [
@@ -86,6 +94,12 @@ _SIGS = {
                                              c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
     "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
+    "nsa_offload_pool_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, ctypes.c_int]),
+    "nsa_offload_reset": (ctypes.c_int, [ctypes.POINTER(OffloadState), c_i32, c_i32, c_vp]),
+    "nsa_decode_offload_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams),
+                                                 ctypes.POINTER(OffloadState)]),
+    "nsa_decode_step_offload": (ctypes.c_int, [ctypes.POINTER(DecodeParams),
+                                               ctypes.POINTER(OffloadState), c_vp, c_sz, c_vp]),
     "nsa_compressed_attn_workspace_size": (c_sz, [c_i32] * 7),
     "nsa_window_attn_workspace_size": (c_sz, [c_i32] * 3),
     "nsa_compressed_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_int,
@@ -285,8 +299,45 @@ def nsa_decode_step(params: DecodeParams, workspace=None, device=None, stream=No
     _check(lib().nsa_decode_step(ctypes.byref(params), _ptr(ws), nbytes, _stream(stream)))
 
 
+def offload_state(batch, kv_heads, pool_slots, nb_cap, device, head_dim=128, dtype=torch.bfloat16,
+                  with_fetched=True):
+    """Allocate (with torch) the device pools and tables of ``nsa_offload_state`` and
+    reset them; returns (state, tensors) where tensors keeps the allocations alive."""
+    units = batch * kv_heads
+    t = dict(k_pool=torch.empty((units, pool_slots, 64, head_dim), dtype=dtype, device=device),
+             v_pool=torch.empty((units, pool_slots, 64, head_dim), dtype=dtype, device=device),
+             slot_of=torch.empty((units, nb_cap), dtype=torch.int32, device=device),
+             block_of=torch.empty((units, pool_slots), dtype=torch.int32, device=device))
+    if with_fetched:
+        t["fetched"] = torch.zeros(units, dtype=torch.int32, device=device)
+    st = OffloadState()
+    st.k_pool, st.v_pool = t["k_pool"].data_ptr(), t["v_pool"].data_ptr()
+    st.slot_of, st.block_of = t["slot_of"].data_ptr(), t["block_of"].data_ptr()
+    st.fetched = t["fetched"].data_ptr() if with_fetched else None
+    st.pool_slots, st.nb_cap = int(pool_slots), int(nb_cap)
+    nsa_offload_reset(st, batch, kv_heads)
+    return st, t
+
+
+def nsa_offload_reset(state: OffloadState, batch, kv_heads, stream=None):
+    _check(lib().nsa_offload_reset(ctypes.byref(state), int(batch), int(kv_heads), _stream(stream)))
+
+
+def decode_offload_workspace_size(params: DecodeParams, state: OffloadState) -> int:
+    return lib().nsa_decode_offload_workspace_size(ctypes.byref(params), ctypes.byref(state))
+
+
+def nsa_decode_step_offload(params: DecodeParams, state: OffloadState, workspace=None, device=None,
+                            stream=None):
+    """Enqueue one decode step whose K/V (params.k, params.v) live in pinned host memory."""
+    need = decode_offload_workspace_size(params, state)
+    ws, nbytes = _workspace(need, device or torch.device("cuda"), workspace)
+    _check(lib().nsa_decode_step_offload(ctypes.byref(params), ctypes.byref(state), _ptr(ws),
+                                         nbytes, _stream(stream)))
+
+
 KERNEL_POOL, KERNEL_LOGITS, KERNEL_BLOCK_SCORES, KERNEL_SELECTED_ATTN, KERNEL_COMBINE = 0, 1, 2, 3, 4
-KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN = 5, 6, 7
+KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN, KERNEL_FETCH = 5, 6, 7, 8
 
 
 def compressed_attn_workspace_size(batch, rows, max_seqlen_k, heads, kv_heads, kernel=32, stride=16):

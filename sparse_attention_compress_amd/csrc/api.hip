@@ -288,7 +288,150 @@ nsa_status check_decode(const nsa_decode_params* p) {
   return NSA_OK;
 }
 
+// Arguments of the compressed-key logits and selection launches of one decode step.
+nsa::DecodeScoresArgs decode_scores_args(const nsa_decode_params* p, char* base,
+                                         const DecodeLayout& lay, int32_t* idx) {
+  const int G = p->heads / p->kv_heads;
+  nsa::DecodeScoresArgs a{};
+  a.q = p->q;
+  a.q_bf16 = p->dtype == NSA_BF16;
+  a.kc = p->k_c;
+  a.kc_bf16 = p->kc_dtype == NSA_BF16;
+  a.cis_pooled = p->cis_pooled;
+  a.cis_weight = p->cis_weight;
+  a.block_scores = p->block_scores;
+  a.window_probs = nullptr;
+  a.cu_k = p->cu_seqlens_k;
+  a.cu_c = p->cu_seqlens_c;
+  a.batch = p->batch;
+  a.max_seqlen_k = p->max_seqlen_k;
+  a.heads = p->heads;
+  a.kv_heads = p->kv_heads;
+  a.scale_log2 = scale_log2_of(p->softmax_scale, p->head_dim);
+  a.ws = nsa::scores_ws_carve(base + lay.scores, p->batch, p->kv_heads, G, p->max_seqlen_k);
+  a.indices = idx;
+  a.topk = p->topk;
+  a.n_init = p->n_init;
+  a.n_local = p->n_local;
+  a.n_cand = p->n_cand;
+  if (p->append_window) {
+    a.refresh_k = p->k;
+    a.refresh_cis = p->cis_pooled ? p->cis : nullptr;
+  }
+  return a;
+}
+
+// Offloaded decode: the decode step's workspace, then the plan's slot ids, copy
+// list and copy counts.
+struct OffloadLayout {
+  DecodeLayout dec;
+  size_t slot_ids, copies, n_copy, total;
+};
+
+OffloadLayout offload_layout(const nsa_decode_params* p) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  OffloadLayout L{};
+  L.dec = decode_layout(p);
+  const size_t places = size_t(p->batch) * p->kv_heads * p->topk;
+  L.slot_ids = L.dec.total;
+  L.copies = L.slot_ids + up(places * sizeof(int32_t));
+  L.n_copy = L.copies + up(places * 2 * sizeof(int32_t));
+  L.total = L.n_copy + up(size_t(p->batch) * p->kv_heads * sizeof(int32_t));
+  return L;
+}
+
+nsa_status check_offload_state(const char* fn, const nsa_offload_state* o) {
+  NSA_REQUIRE(o != nullptr, NSA_ERR_INVALID_ARG, "%s: offload state is null", fn);
+  NSA_REQUIRE(o->pool_slots >= 1 && o->pool_slots <= nsa::kMaxPoolSlots, NSA_ERR_UNSUPPORTED,
+              "%s: pool_slots %d outside 1..%d", fn, o->pool_slots, nsa::kMaxPoolSlots);
+  NSA_REQUIRE(o->nb_cap >= 1 && o->nb_cap <= nsa::kMaxSortBlocks, NSA_ERR_UNSUPPORTED,
+              "%s: nb_cap %d outside 1..%d", fn, o->nb_cap, nsa::kMaxSortBlocks);
+  NSA_REQUIRE(o->k_pool && o->v_pool && o->slot_of && o->block_of, NSA_ERR_INVALID_ARG,
+              "%s: null pool or table pointer", fn);
+  NSA_REQUIRE(aligned16(o->k_pool) && aligned16(o->v_pool), NSA_ERR_INVALID_ARG,
+              "%s: pools must be 16-byte aligned", fn);
+  return NSA_OK;
+}
+
+nsa_status check_decode_offload(const nsa_decode_params* p, const nsa_offload_state* o) {
+  const char* fn = "nsa_decode_step_offload";
+  nsa_status st = check_decode(p);
+  if (st != NSA_OK) return st;
+  st = check_offload_state(fn, o);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(p->dtype == NSA_BF16, NSA_ERR_UNSUPPORTED, "%s: bfloat16 K/V only", fn);
+  NSA_REQUIRE(p->topk <= nsa::kMaxOffloadSel, NSA_ERR_UNSUPPORTED, "%s: topk %d above the supported %d", fn, p->topk, nsa::kMaxOffloadSel);
+  NSA_REQUIRE(p->topk <= o->pool_slots, NSA_ERR_INVALID_ARG, "%s: pool_slots %d below topk %d", fn, o->pool_slots, p->topk);
+  const int nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
+  NSA_REQUIRE(nb_max <= o->nb_cap, NSA_ERR_INVALID_ARG, "%s: %d blocks per sequence above nb_cap %d", fn, nb_max, o->nb_cap);
+  return NSA_OK;
+}
+
 }  // namespace
+
+size_t nsa_offload_pool_bytes(int32_t batch, int32_t kv_heads, int32_t pool_slots,
+                              int32_t head_dim, nsa_dtype dtype) {
+  if (batch < 0 || kv_heads <= 0 || pool_slots <= 0 || head_dim <= 0 || !dtype_ok(dtype)) return 0;
+  return size_t(batch) * kv_heads * pool_slots * 64 * head_dim * (dtype == NSA_BF16 ? 2 : 4);
+}
+
+nsa_status nsa_offload_reset(const nsa_offload_state* o, int32_t batch, int32_t kv_heads,
+                             hipStream_t stream) {
+  const char* fn = "nsa_offload_reset";
+  nsa_status st = check_offload_state(fn, o);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(batch >= 0 && kv_heads >= 1, NSA_ERR_INVALID_ARG, "%s: bad batch or kv_heads", fn);
+  const size_t units = size_t(batch) * kv_heads;
+  return hip_status(nsa::launch_offload_reset(o->slot_of, units * o->nb_cap, o->block_of,
+                                              units * o->pool_slots, stream), fn);
+}
+
+size_t nsa_decode_offload_workspace_size(const nsa_decode_params* p, const nsa_offload_state* o) {
+  if (check_decode_offload(p, o) != NSA_OK || p->batch == 0) return 0;
+  return offload_layout(p).total;
+}
+
+nsa_status nsa_decode_step_offload(const nsa_decode_params* p, const nsa_offload_state* o,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_decode_step_offload";
+  nsa_status st = check_decode_offload(p, o);
+  if (st != NSA_OK) return st;
+  if (p->batch == 0) return ok();
+  const OffloadLayout lay = offload_layout(p);
+  NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= lay.total, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, lay.total);
+  char* base = static_cast<char*>(workspace);
+  const int G = p->heads / p->kv_heads;
+  int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.dec.indices);
+  // logits and the stand-alone selection (the ids are needed before any K/V moves)
+  nsa::DecodeScoresArgs a = decode_scores_args(p, base, lay.dec, idx);
+  hipError_t e = nsa::launch_decode_scores(a, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  nsa::OffloadArgs oa{};
+  oa.indices = idx;
+  oa.k_sel = p->topk;
+  oa.units = p->batch * p->kv_heads;
+  oa.kv_heads = p->kv_heads;
+  oa.nb_cap = o->nb_cap;
+  oa.pool_slots = o->pool_slots;
+  oa.slot_of = o->slot_of;
+  oa.block_of = o->block_of;
+  oa.slot_ids = reinterpret_cast<int*>(base + lay.slot_ids);
+  oa.copies = reinterpret_cast<int2*>(base + lay.copies);
+  oa.n_copy = reinterpret_cast<int*>(base + lay.n_copy);
+  oa.fetched = o->fetched;
+  oa.k_src = static_cast<const nsa::bf16_t*>(p->k);
+  oa.v_src = static_cast<const nsa::bf16_t*>(p->v);
+  oa.cu_k = p->cu_seqlens_k;
+  oa.kpool = static_cast<nsa::bf16_t*>(o->k_pool);
+  oa.vpool = static_cast<nsa::bf16_t*>(o->v_pool);
+  e = nsa::launch_offload_fetch(oa, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  const nsa::AttnWs aws = nsa::attn_ws_carve(base + lay.dec.attn, p->batch, p->kv_heads, G, p->topk, 1);
+  e = nsa::launch_pool_attn(p->q, oa, p->cis_values ? p->cis : nullptr, p->out, p->heads,
+                            a.scale_log2, aws, stream);
+  return hip_status(e, fn);
+}
 
 size_t nsa_decode_workspace_size(const nsa_decode_params* p) {
   if (check_decode(p) != NSA_OK || p->batch == 0) return 0;
@@ -308,32 +451,7 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
   const int G = p->heads / p->kv_heads;
   int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.indices);
   const float sl2 = scale_log2_of(p->softmax_scale, p->head_dim);
-  nsa::DecodeScoresArgs a{};
-  a.q = p->q;
-  a.q_bf16 = p->dtype == NSA_BF16;
-  a.kc = p->k_c;
-  a.kc_bf16 = p->kc_dtype == NSA_BF16;
-  a.cis_pooled = p->cis_pooled;
-  a.cis_weight = p->cis_weight;
-  a.block_scores = p->block_scores;
-  a.window_probs = nullptr;
-  a.cu_k = p->cu_seqlens_k;
-  a.cu_c = p->cu_seqlens_c;
-  a.batch = p->batch;
-  a.max_seqlen_k = p->max_seqlen_k;
-  a.heads = p->heads;
-  a.kv_heads = p->kv_heads;
-  a.scale_log2 = sl2;
-  a.ws = nsa::scores_ws_carve(base + lay.scores, p->batch, p->kv_heads, G, p->max_seqlen_k);
-  a.indices = idx;
-  a.topk = p->topk;
-  a.n_init = p->n_init;
-  a.n_local = p->n_local;
-  a.n_cand = p->n_cand;
-  if (p->append_window) {
-    a.refresh_k = p->k;
-    a.refresh_cis = p->cis_pooled ? p->cis : nullptr;
-  }
+  nsa::DecodeScoresArgs a = decode_scores_args(p, base, lay, idx);
   const nsa::AttnWs aws = nsa::attn_ws_carve(base + lay.attn, p->batch, p->kv_heads, G, p->topk, 1);
   const int nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
   if (p->dtype == NSA_BF16 && nb_max <= nsa::kFusedMaxBlocks && p->topk <= nsa::kFusedMaxSel) {

@@ -372,14 +372,17 @@ __device__ __forceinline__ void load_q_operand(const bf16_t* __restrict__ q, siz
 
 // The G heads of `unit` (query position t of the sequence starting at kstart)
 // attend to the nv staged block ids; the result is written as split `split` of
-// n_split partial states (SPLIT) or as the output rows.
-template <int G, bool CIS, bool SPLIT>
+// n_split partial states (SPLIT) or as the output rows.  POOL: k and v are a
+// block pool [units][pool_slots][64][128] and block ids_s[i] sits in slot
+// slots_s[i] (the CIS values, when given, stay indexed by token).
+template <int G, bool CIS, bool SPLIT, bool POOL = false>
 __device__ __forceinline__ void attend_staged_blocks(
     MfmaAttnSmem& sm, const int* ids_s, int nv, const uint4 (&qb)[4],
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ cis,
     int kstart, int t, size_t unit, int kv, int kv_heads, float scale_log2, int split,
     int n_split, bf16_t* __restrict__ out, float* __restrict__ lse,
-    float2* __restrict__ part_ml, float* __restrict__ part_acc) {
+    float2* __restrict__ part_ml, float* __restrict__ part_acc,
+    const int* slots_s = nullptr, int pool_slots = 0) {
   static_assert(G <= 16, "one MFMA column per query head");
   constexpr int D = kHeadDim;
   constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
@@ -390,20 +393,26 @@ __device__ __forceinline__ void attend_staged_blocks(
   float (&accx_s)[4][32][kAccRow] = sm.accx_s;
   (void)tid;
 
-  const size_t rs = size_t(kv_heads) * D;
-  const bf16_t* kbase = k + size_t(kstart) * rs + size_t(kv) * D;
-  const bf16_t* vbase = v + size_t(kstart) * rs + size_t(kv) * D;
+  const size_t rs = POOL ? size_t(D) : size_t(kv_heads) * D;
+  const bf16_t* kbase = POOL ? k + unit * size_t(pool_slots) * kBlock * D
+                             : k + size_t(kstart) * rs + size_t(kv) * D;
+  const bf16_t* vbase = POOL ? v + unit * size_t(pool_slots) * kBlock * D
+                             : v + size_t(kstart) * rs + size_t(kv) * D;
 
   // Token rows past t are clamped to t: they lie inside the sequence (finite
   // data) and their probabilities are 0, so no per-load branches are needed.
-  auto load_block = [&](int id, MfmaBlockRegs<CIS>& R) {
+  // Staged place i holds block ids_s[i]; in a pool, token j of that block is
+  // row slots_s[i] * 64 + j - ids_s[i] * 64.
+  auto load_block = [&](int i_st, MfmaBlockRegs<CIS>& R) {
+    const int id = ids_s[i_st];
     const int j0 = id * kBlock + wave * 16;
-    const bf16_t* kr = kbase + size_t(min(j0 + c16, t)) * rs + 8 * r4;
+    const int rb = POOL ? (slots_s[i_st] - id) * kBlock : 0;  // pool row of token j: j + rb
+    const bf16_t* kr = kbase + size_t(min(j0 + c16, t) + rb) * rs + 8 * r4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) R.k[i] = ld16(kr + 32 * i);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      R.v[e] = ld16(vbase + size_t(min(j0 + 4 * r4 + e, t)) * rs + 8 * c16);
+      R.v[e] = ld16(vbase + size_t(min(j0 + 4 * r4 + e, t) + rb) * rs + 8 * c16);
     if (CIS) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -470,15 +479,15 @@ __device__ __forceinline__ void attend_staged_blocks(
   };
 
   MfmaBlockRegs<CIS> A, B;
-  if (nv > 0) load_block(ids_s[0], A);
+  if (nv > 0) load_block(0, A);
   for (int i = 0; i < nv; i += 2) {
     const int id0 = ids_s[i];
     const bool has1 = i + 1 < nv;
     const int id1 = has1 ? ids_s[i + 1] : 0;
-    if (has1) load_block(id1, B);
+    if (has1) load_block(i + 1, B);
     compute_block(id0, A);
     if (has1) {
-      if (i + 2 < nv) load_block(ids_s[i + 2], A);
+      if (i + 2 < nv) load_block(i + 2, A);
       compute_block(id1, B);
     }
   }
@@ -577,6 +586,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   attend_staged_blocks<G, CIS, SPLIT>(sm, ids_s, nv_s, qb, k, v, cis, cu_k[b], t, unit, kv,
                                       kv_heads, scale_log2, split, SPLIT ? int(gridDim.x) : 1,
                                       out, lse, part_ml, part_acc);
+}
+
+// Decode over a block pool (KV offload): like selected_attn_mfma_kernel with
+// SPLIT, but the K/V rows of listed block indices[unit][p] come from pool slot
+// slot_ids[unit][p] (nsa_offload_plan); grid (splits, kv heads, sequences).
+template <int G, bool CIS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pool_attn_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kpool,
+    const bf16_t* __restrict__ vpool, const int* __restrict__ indices,
+    const int* __restrict__ slot_ids, int k_sel, int pool_slots, const float* __restrict__ cis,
+    const int* __restrict__ cu_k, int kv_heads, float scale_log2, int bpw,
+    float2* __restrict__ part_ml, float* __restrict__ part_acc) {
+  __shared__ MfmaAttnSmem sm;
+  __shared__ int ids_s[kMaxWgSlots];
+  __shared__ int slots_s[kMaxWgSlots];
+  __shared__ int nv_s;
+  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const size_t unit = size_t(b) * kv_heads + kv;
+  uint4 qb[4];
+  load_q_operand<G>(q, unit, qb);
+  const int kstart = cu_k[b];
+  const int t = cu_k[b + 1] - kstart - 1;
+  const int s_begin = split * bpw, s_end = min(k_sel, s_begin + bpw);
+  if (threadIdx.x < kWave) {
+    const int p = s_begin + int(threadIdx.x);
+    const int id = p < s_end ? indices[unit * k_sel + p] : -1;
+    const int sl = p < s_end ? slot_ids[unit * k_sel + p] : -1;
+    const bool ok = id >= 0 && id * kBlock <= t && sl >= 0 && sl < pool_slots;
+    const unsigned long long m = __ballot(ok);
+    const int pos = __popcll(m & ((1ull << threadIdx.x) - 1ull));
+    if (ok) {
+      ids_s[pos] = id;
+      slots_s[pos] = sl;
+    }
+    if (threadIdx.x == 0) nv_s = __popcll(m);
+  }
+  __syncthreads();
+  attend_staged_blocks<G, CIS, true, true>(sm, ids_s, nv_s, qb, kpool, vpool, cis, kstart, t,
+                                           unit, kv, kv_heads, scale_log2, split,
+                                           int(gridDim.x), nullptr, nullptr, part_ml, part_acc,
+                                           slots_s, pool_slots);
 }
 
 // Decode: score the blocks, select and attend in one launch.  Every workgroup
@@ -828,6 +878,49 @@ static hipError_t launch_select_attn_g(const DecodeScoresArgs& a, const void* k,
                        dim3(kHeadDim), s, static_cast<const float2*>(ws.part_ml),
                        static_cast<const float*>(ws.part_acc), static_cast<bf16_t*>(out),
                        static_cast<float*>(nullptr), n_split, G);
+}
+
+template <int G, bool CIS>
+static hipError_t launch_pool_attn_g(const void* q, const OffloadArgs& a, const float* cis_values,
+                                     void* out, float scale_log2, const AttnWs& ws,
+                                     hipStream_t s) {
+  const int batch = a.units / a.kv_heads;
+  const int bpw = attn_split_blocks(batch, a.kv_heads, a.k_sel);
+  const int n_split = (a.k_sel + bpw - 1) / bpw;
+  hipError_t e = launch_kernel(
+      kKindAttn, pool_attn_kernel<G, CIS>, dim3(n_split, a.kv_heads, batch), dim3(256), s,
+      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(a.kpool),
+      static_cast<const bf16_t*>(a.vpool), a.indices, static_cast<const int*>(a.slot_ids),
+      a.k_sel, a.pool_slots, cis_values, a.cu_k, a.kv_heads, scale_log2, bpw, ws.part_ml,
+      ws.part_acc);
+  if (e != hipSuccess) return e;
+  return launch_kernel(kKindCombine, combine_kernel<bf16_t>, dim3(a.units, G), dim3(kHeadDim), s,
+                       static_cast<const float2*>(ws.part_ml),
+                       static_cast<const float*>(ws.part_acc), static_cast<bf16_t*>(out),
+                       static_cast<float*>(nullptr), n_split, G);
+}
+
+template <bool CIS>
+static hipError_t launch_pool_attn_c(int G, const void* q, const OffloadArgs& a,
+                                     const float* cis_values, void* out, float scale_log2,
+                                     const AttnWs& ws, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_pool_attn_g<1, CIS>(q, a, cis_values, out, scale_log2, ws, s);
+    case 2: return launch_pool_attn_g<2, CIS>(q, a, cis_values, out, scale_log2, ws, s);
+    case 4: return launch_pool_attn_g<4, CIS>(q, a, cis_values, out, scale_log2, ws, s);
+    case 8: return launch_pool_attn_g<8, CIS>(q, a, cis_values, out, scale_log2, ws, s);
+    case 16: return launch_pool_attn_g<16, CIS>(q, a, cis_values, out, scale_log2, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_pool_attn(const void* q, const OffloadArgs& a, const float* cis_values,
+                            void* out, int heads, float scale_log2, const AttnWs& ws,
+                            hipStream_t s) {
+  const int G = heads / a.kv_heads;
+  if (cis_values != nullptr)
+    return launch_pool_attn_c<true>(G, q, a, cis_values, out, scale_log2, ws, s);
+  return launch_pool_attn_c<false>(G, q, a, cis_values, out, scale_log2, ws, s);
 }
 
 template <bool CIS>

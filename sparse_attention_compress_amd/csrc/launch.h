@@ -32,6 +32,10 @@ constexpr int kFusedMaxBlocks = 2048;
 constexpr int kFusedMidBlocks = 1024;
 constexpr int kFusedSmallBlocks = 512;
 constexpr int kFusedMaxSel = 256;
+// KV offload: block slots per (sequence, KV head) in the device pool, and the
+// largest top-k the offloaded decode step handles (one plan thread per place).
+constexpr int kMaxPoolSlots = 1024;
+constexpr int kMaxOffloadSel = 256;
 
 // Kernel kinds that a profiling request can target.
 enum KernelKind {
@@ -43,7 +47,8 @@ enum KernelKind {
   kKindCmpLse = 5,
   kKindCmpProbs = 6,
   kKindWindow = 7,
-  kKindCount = 8
+  kKindFetch = 8,
+  kKindCount = 9
 };
 
 // One armed (start, stop) event pair per kernel kind, per host thread.
@@ -136,6 +141,30 @@ hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int
 hipError_t launch_select_attn(const DecodeScoresArgs& a, const void* k, const void* v,
                               const float* cis_values, void* out, const AttnWs& ws,
                               hipStream_t s);
+
+// KV offload (decode): plan the fetches of the listed blocks that are not in the
+// pool, copy them from the caller's K/V (host memory), attend over the pool.
+struct OffloadArgs {
+  const int* indices;    // [units, k_sel] listed blocks, ascending, -1 padded
+  int k_sel, units, kv_heads, nb_cap, pool_slots;
+  int* slot_of;          // [units, nb_cap]: slot of a resident block, else -1
+  int* block_of;         // [units, pool_slots]: block held by a slot, else -1
+  int* slot_ids;         // [units, k_sel] workspace: slot of each listed block
+  int2* copies;          // [units, k_sel] workspace: (block, slot) of each miss
+  int* n_copy;           // [units] workspace: misses
+  int* fetched;          // nullable [units]: misses, for the caller
+  const bf16_t* k_src;   // [N_k, kv_heads, 128] (host memory)
+  const bf16_t* v_src;
+  const int* cu_k;
+  bf16_t* kpool;         // [units, pool_slots, 64, 128]
+  bf16_t* vpool;
+};
+hipError_t launch_offload_reset(int* slot_of, size_t n_slot_of, int* block_of, size_t n_block_of,
+                                hipStream_t s);
+hipError_t launch_offload_fetch(const OffloadArgs& a, hipStream_t s);
+hipError_t launch_pool_attn(const void* q, const OffloadArgs& a, const float* cis_values,
+                            void* out, int heads, float scale_log2, const AttnWs& ws,
+                            hipStream_t s);
 
 // Prefill branches (bf16, prefill rows).
 struct CompressedPrefillArgs {

@@ -209,3 +209,41 @@ def test_missing_library_fails_loudly(tmp_path):
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert "IMPORT_ERROR" in res.stdout, res.stdout + res.stderr
     assert "ENTRY_IMPORT_ERROR" in res.stdout, res.stdout + res.stderr
+
+
+def test_two_stage_and_offload_checks():
+    p = nsa.DecodeParams()
+    p.batch, p.max_seqlen_k, p.heads, p.kv_heads, p.head_dim = 2, 4096, 16, 2, 128
+    p.kernel, p.stride, p.block_size = 32, 16, 64
+    p.topk, p.n_init, p.n_local = 16, 1, 2
+    p.dtype, p.kc_dtype = nsa.NSA_BF16, nsa.NSA_F32
+    for f in ("q", "k", "v", "k_c", "cu_seqlens_k", "cu_seqlens_c", "out"):
+        setattr(p, f, 0x1000)
+    need = nsa.decode_workspace_size(p)
+    ws = ctypes.c_void_p(0x1000)
+    p.n_cand = 32      # two stages need the pooled CIS
+    assert nsa.lib().nsa_decode_step(ctypes.byref(p), ws, need, None) == 1
+    p.n_cand = -1
+    assert nsa.lib().nsa_decode_step(ctypes.byref(p), ws, need, None) == 1
+    p.n_cand = 0
+    o = nsa.OffloadState()
+    o.k_pool = o.v_pool = o.slot_of = o.block_of = 0x1000
+    o.pool_slots, o.nb_cap = 64, 64
+    need_o = nsa.decode_offload_workspace_size(p, o)
+    assert need_o > need
+    step = nsa.lib().nsa_decode_step_offload
+    assert step(ctypes.byref(p), ctypes.byref(o), ws, need_o - 1, None) == 3   # workspace
+    o.pool_slots = 8   # fewer slots than topk
+    assert step(ctypes.byref(p), ctypes.byref(o), ws, need_o, None) == 1
+    o.pool_slots = 2048  # above the pool limit
+    assert step(ctypes.byref(p), ctypes.byref(o), ws, need_o, None) == 2
+    o.pool_slots, o.nb_cap = 64, 32  # 64 blocks per sequence above nb_cap
+    assert step(ctypes.byref(p), ctypes.byref(o), ws, need_o, None) == 1
+    o.nb_cap = 64
+    p.dtype = nsa.NSA_F32  # bfloat16 K/V only
+    assert step(ctypes.byref(p), ctypes.byref(o), ws, need_o, None) == 2
+    p.dtype = nsa.NSA_BF16
+    o.k_pool = 0
+    assert step(ctypes.byref(p), ctypes.byref(o), ws, need_o, None) == 1
+    assert nsa.lib().nsa_offload_reset(ctypes.byref(o), 2, 2, None) == 1
+    assert nsa.lib().nsa_offload_pool_bytes(2, 2, 64, 128, nsa.NSA_BF16) == 2 * 2 * 64 * 64 * 128 * 2

@@ -51,7 +51,16 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of from a HIP graph "
                          "(for counter-collection runs, which serialise dispatches)")
-    ap.add_argument("--workload", choices=["decode", "decode-long", "prefill-selected", "prefill-nsa"],
+    ap.add_argument("--cis-weight", type=float, default=None,
+                    help="decode: weight of the pooled CIS in the block score (default: the "
+                         "workload's, 1.0)")
+    ap.add_argument("--pool-slots", type=int, default=128,
+                    help="decode-offload: device block slots per (sequence, KV head)")
+    ap.add_argument("--queries", type=int, default=16,
+                    help="decode-offload: distinct queries the steps cycle through (1: every "
+                         "step repeats one selection, so the pool holds it after the first)")
+    ap.add_argument("--workload", choices=["decode", "decode-long", "decode-offload",
+                                           "prefill-selected", "prefill-nsa"],
                     default="decode",
                     help="decode: the headline NOSA-1B-shaped decode (default); decode-long: "
                          "CIS-weighted decode of 4 x 131072 tokens; prefill-selected: "
@@ -131,6 +140,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.workload == "decode-offload":
+        offload_main(args, dev)
+        return
     if args.workload not in ("decode", "decode-long"):
         prefill_main(args, dev)
         return
@@ -441,6 +453,133 @@ def _kernel_us(nsa, fn, kinds, reps, stream):
             fn()
     torch.cuda.synchronize()
     return {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) * 1e3 for n in kinds}
+
+
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def offload_main(args, dev):
+    """The batched decode with its K/V cache in pinned host memory: every step
+    scores and selects on the device and copies only the selected blocks that the
+    device pool does not hold.  The steps cycle through `--queries` distinct query
+    sets (fresh selections each step: the least reuse); the pool starts empty."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_compress_amd as nsa
+    from gen import workloads as W
+
+    w = W.nosa1b_decode()
+    B, H, Hkv, D = w.batch, w.heads, w.kv_heads, w.head_dim
+    lengths = list(w.lengths)
+    nc = [nsa.full_windows(L) for L in lengths]
+    cu_k, cu_c = nsa.cu_seqlens_of(lengths, dev), nsa.cu_seqlens_of(nc, dev)
+    max_len = max(lengths)
+    nb_max = -(-max_len // 64)
+    print(f"[bench] workload {w.name} (K/V in host memory) pool_slots={args.pool_slots} "
+          f"queries={args.queries}", file=sys.stderr, flush=True)
+    k, v = W.keys_values(w, dev)
+    cis = W.cis_scores(w, dev)
+    kc = torch.empty((sum(nc), Hkv, D), dtype=torch.float32, device=dev)
+    cp = torch.empty((sum(nc), Hkv), dtype=torch.float32, device=dev)
+    nsa.nsa_compress_k(k, kc, cu_k, cu_c, max(nc))
+    nsa.nsa_cis_mean_pool_varlen(cis, cp, cu_k, cu_c, max(nc))
+    k_host = torch.empty(k.shape, dtype=k.dtype, pin_memory=True)
+    v_host = torch.empty(v.shape, dtype=v.dtype, pin_memory=True)
+    k_host.copy_(k)
+    v_host.copy_(v)
+    torch.cuda.synchronize()
+    del k, v
+    torch.cuda.empty_cache()
+    st, keep = nsa.offload_state(B, Hkv, args.pool_slots, nb_max, dev)
+    out = torch.empty((B, H, D), dtype=w.dtype, device=dev)
+    cis_w = w.cis_weight if args.cis_weight is None else args.cis_weight
+    qs = [W.decode_query(w, dev, layer=i) for i in range(args.queries)]  # kept alive: params hold pointers
+    ps = [nsa.decode_params(q_, k_host, v_host, kc, cu_k, cu_c, max_len, out, topk=w.topk,
+                            n_init=w.n_init, n_local=w.n_local, cis=cis, cis_pooled=cp,
+                            cis_weight=cis_w, append_window=True, n_cand=args.n_cand)
+          for q_ in qs]
+    ws = torch.zeros(nsa.decode_offload_workspace_size(ps[0], st), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    n_all = args.warmup + args.steps
+
+    def step(i):
+        nsa.nsa_decode_step_offload(ps[i % len(ps)], st, workspace=ws)
+
+    # pass 1, eager: blocks fetched by every step of the sequence the timed run replays
+    fetched = []
+    with torch.cuda.stream(stream):
+        nsa.nsa_offload_reset(st, B, Hkv)
+        for i in range(n_all):
+            step(i)
+            torch.cuda.synchronize()
+            fetched.append(int(keep["fetched"].sum().item()))
+    f_timed = fetched[args.warmup:]
+    blk_bytes = 64 * D * 2 * 2  # K and V rows of one block of one KV head
+    # pass 2: the same sequence from an empty pool, warm-up then timed, from HIP graphs
+    with torch.cuda.stream(stream):
+        nsa.nsa_offload_reset(st, B, Hkv)
+    torch.cuda.synchronize()
+
+    def capture(lo, hi):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(lo, hi):
+                step(i)
+        return g
+
+    g_warm, g_timed = capture(0, args.warmup), capture(args.warmup, n_all)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        nsa.nsa_offload_reset(st, B, Hkv)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g_warm.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        g_timed.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel durations over a few more eager steps (continuing the sequence)
+    kinds = {"logits_and_refresh": nsa.KERNEL_LOGITS, "select": nsa.KERNEL_BLOCK_SCORES,
+             "fetch": nsa.KERNEL_FETCH, "pool_attn": nsa.KERNEL_SELECTED_ATTN,
+             "combine": nsa.KERNEL_COMBINE}
+    nxt = [n_all]
+
+    def step_next():
+        step(nxt[0])
+        nxt[0] += 1
+    kern = _kernel_us(nsa, step_next, kinds, min(56, max(8, args.profile_steps)), stream)
+    mean_fetch = float(np.mean(f_timed)) if f_timed else 0.0
+    fetch_gbs = mean_fetch * blk_bytes / (kern["fetch"] * 1e-6) / 1e9 if kern["fetch"] > 0 else 0.0
+    result = {
+        "metric": METRIC + " (KV offloaded to host memory)",
+        "value": round(B * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, sigmoid(N(0,1)) CIS; no dataset)",
+        "config": {"workload": w.name + "_kv_offload", "batch": B, "context_lengths": lengths,
+                   "heads": H, "kv_heads": Hkv, "head_dim": D, "topk": w.topk,
+                   "pool_slots": args.pool_slots, "distinct_queries": args.queries,
+                   "cis_weight": cis_w,
+                   "kv_location": "pinned host memory", "step": "one layer, whole batch, HIP-graph replay"},
+        "roofline": {"kernel": "offload_fetch_kernel (selected blocks copied from host memory)",
+                     "bound": "host-link", "achieved": round(fetch_gbs, 2), "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(fetch_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None},
+        "fetched_blocks_per_step": round(mean_fetch, 2),
+        "fetched_bytes_per_step": round(mean_fetch * blk_bytes, 1),
+        "selected_blocks_per_step": B * Hkv * w.topk,
+        "kernel_us": {k_: round(v_, 3) for k_, v_ in kern.items()},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def prefill_main(args, dev):

@@ -59,8 +59,11 @@ def parse():
     ap.add_argument("--queries", type=int, default=16,
                     help="decode-offload: distinct queries the steps cycle through (1: every "
                          "step repeats one selection, so the pool holds it after the first)")
+    ap.add_argument("--seq", type=int, default=16384,
+                    help="prefill-blockmask: tokens per sequence (the pages' table: 1024, 4096, 16384)")
+    ap.add_argument("--causal", action="store_true", help="prefill-blockmask: lower triangle only")
     ap.add_argument("--workload", choices=["decode", "decode-long", "decode-offload",
-                                           "prefill-selected", "prefill-nsa"],
+                                           "prefill-selected", "prefill-nsa", "prefill-blockmask"],
                     default="decode",
                     help="decode: the headline NOSA-1B-shaped decode (default); decode-long: "
                          "CIS-weighted decode of 4 x 131072 tokens; prefill-selected: "
@@ -142,6 +145,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "decode-offload":
         offload_main(args, dev)
+        return
+    if args.workload == "prefill-blockmask":
+        blockmask_main(args, dev)
         return
     if args.workload not in ("decode", "decode-long"):
         prefill_main(args, dev)
@@ -578,6 +584,81 @@ def offload_main(args, dev):
         "fetched_bytes_per_step": round(mean_fetch * blk_bytes, 1),
         "selected_blocks_per_step": B * Hkv * w.topk,
         "kernel_us": {k_: round(v_, 3) for k_, v_ in kern.items()},
+    }
+    print(json.dumps(result), flush=True)
+
+
+# The pages' TileLang block-sparse timings on H100-80GB (batch 8, 16 heads, dim
+# 128, 50% of 64 x 64 blocks, fp16 storage): ms per call at 1024 / 4096 / 16384.
+PAGES_BLOCKMASK_H100_MS = {1024: 3.2, 4096: 42.3, 16384: 318.6}
+
+
+def blockmask_main(args, dev):
+    """Block-mask attention at the pages' benchmark shape: one step = one call over
+    the batch; value = query tokens/s; roofline = algorithmic bf16 MFMA flops
+    (4 * 128 per (query, head, attended key))."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_compress_amd as nsa
+    from gen import workloads as W
+
+    w = W.blockmask_prefill(args.seq, args.causal)
+    print(f"[bench] workload {w.name}", file=sys.stderr, flush=True)
+    D, seq = w.head_dim, args.seq
+    q = W.prefill_query(w, dev)
+    k, v = W.keys_values(w, dev)
+    mask = W.block_mask(w, dev)
+    cu = nsa.cu_seqlens_of(w.lengths, dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(nsa.blockmask_attn_workspace_size(w.batch, seq, w.heads), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def fn():
+        nsa.nsa_blockmask_attn_fwd(q, k, v, mask, cu, seq, out, causal=args.causal, workspace=ws)
+    steps = args.steps if args.steps != 2800 else (200 if seq <= 4096 else 10)
+    warmup = args.warmup if args.warmup != 280 else 3
+    wall_s, gpu_ms = _timed(fn, steps, warmup, stream)
+    kern = _kernel_us(nsa, fn, {"blockmask_attn": nsa.KERNEL_BLOCKMASK_ATTN}, 3, stream)
+    # attended (query, key) pairs per head, from the mask
+    m = mask.cpu().numpy().astype(np.int64)        # [B, H, nb, nb]
+    nb = m.shape[-1]
+    full = 64 * 64
+    if args.causal:
+        tri = np.tril(np.ones((nb, nb), dtype=np.int64), -1)
+        pairs = float((m * tri).sum() * full + np.trace(m, axis1=2, axis2=3).sum() * (64 * 65 // 2))
+    else:
+        pairs = float(m.sum() * full)
+    flops = 4.0 * D * pairs
+    tfl = flops / (kern["blockmask_attn"] * 1e-6) / 1e12
+    ms = wall_s * 1e3 / steps
+    value = w.total_tokens * steps / wall_s
+    pages_ms = PAGES_BLOCKMASK_H100_MS.get(seq) if not args.causal else None
+    result = {
+        "metric": f"prefill tokens/s ({w.name})",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(pages_ms / ms, 3) if pages_ms else None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded 50% block mask; no dataset)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": seq, "heads": w.heads,
+                   "head_dim": D, "block": 64, "density": 0.5, "causal": bool(args.causal),
+                   "active_blocks": int(m.sum())},
+        "roofline": {"kernel": "blockmask_attn_kernel", "bound": "mfma", "achieved": round(tfl, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops,
+                     "mean_kernel_us": round(kern["blockmask_attn"], 1)},
+        "pages_context": ({"h100_tilelang_ms": pages_ms, "note": "H100-80GB, fp16 storage; "
+                           "vs_baseline = their ms / ours"} if pages_ms else None),
+        "timed_gpu_ms": round(gpu_ms, 3),
     }
     print(json.dumps(result), flush=True)
 

@@ -18,9 +18,9 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import _lsr, normal, sigmoid_normal, u64_at, uniform_ints
+from . import _lsr, normal, random_keys, sigmoid_normal, u64_at, uniform_ints
 
-S_Q, S_K, S_V, S_CIS, S_GATE, S_LEN, S_IDX = 1, 2, 3, 4, 5, 6, 7
+S_Q, S_K, S_V, S_CIS, S_GATE, S_LEN, S_IDX, S_MASK = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclass
@@ -88,6 +88,25 @@ def cis_decode() -> Workload:
     return Workload("cis_decode_b4_L131072", 0x5EED0005, "decode", 4, [131072] * 4, 16, 2, 128,
                     torch.bfloat16, topk=64, n_init=1, n_local=1024 // 64,
                     cis_select=True, cis_values=True)
+
+
+def blockmask_prefill(seq: int = 16384, causal: bool = False) -> Workload:
+    """The pages' block-sparse benchmark shape (TileLang NSA, performance table):
+    batch 8, 16 heads, head_dim 128, 64 x 64 blocks at 50% density."""
+    return Workload(f"blockmask_b8_h16_T{seq}" + ("_causal" if causal else ""), 0x5EED0006,
+                    "prefill_blockmask", 8, [seq] * 8, 16, 16, 128, torch.bfloat16,
+                    extra={"density": 0.5, "causal": causal})
+
+
+def block_mask(w: Workload, device="cpu", density: float = None) -> torch.Tensor:
+    """uint8 [B, H, nb, nb] (nb = ceil(max length / 64)): block (b, h, i, j) is on
+    when the top 63 bits of its counter's splitmix64 output fall below
+    density * 2**63 (an integer comparison)."""
+    if density is None:
+        density = w.extra.get("density", 0.5)
+    nb = (max(w.lengths) + w.block - 1) // w.block
+    keys = random_keys(w.seed, S_MASK, (w.batch, w.heads, nb, nb), device)
+    return (keys < int(density * 2 ** 63)).to(torch.uint8)
 
 
 ALL = {

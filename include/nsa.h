@@ -106,7 +106,7 @@ int32_t nsa_version(void);
  * 5 compressed-attention normaliser pass (prefill), 6 compressed-attention
  * output and block-score pass (prefill), 7 sliding-window attention (prefill,
  * with the gated sum in nsa_prefill_step), 8 block copies from host memory
- * (nsa_decode_step_offload).  The events are owned by the caller
+ * (nsa_decode_step_offload), 9 block-mask attention.  The events are owned by the caller
  * and must have timing enabled; a launch made during stream capture must not
  * be armed.
  */
@@ -119,7 +119,8 @@ typedef enum nsa_kernel_kind {
   NSA_KERNEL_COMPRESSED_LSE = 5,
   NSA_KERNEL_COMPRESSED_ATTN = 6,
   NSA_KERNEL_WINDOW_ATTN = 7,
-  NSA_KERNEL_FETCH = 8
+  NSA_KERNEL_FETCH = 8,
+  NSA_KERNEL_BLOCKMASK_ATTN = 9
 } nsa_kernel_kind;
 nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
 
@@ -364,6 +365,31 @@ nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v
                                    int32_t head_dim, int32_t kernel, int32_t stride,
                                    int32_t block_size, float softmax_scale, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nsa_blockmask_attn_fwd -- block-sparse attention driven by a block mask.
+ * [TileLang NSA, section 1 (block-sparse attention): the attention matrix is
+ *  cut into 64 x 64 blocks and a boolean block mask marks the ones computed;
+ *  with is_causal the lower triangle only.]
+ *   q, k, v  [N, heads, head_dim] bfloat16, packed by cu_seqlens [batch+1]
+ *            (self-attention: query t of a sequence is its token t)
+ *   mask     [batch, heads, nb, nb] uint8 (device), nb = ceil(max_seqlen / 64):
+ *            nonzero at [b, h, i, j] = the queries of block i attend to the keys
+ *            of block j
+ *   causal   != 0: in addition, keys after the query's own position are ignored
+ *            (blocks above the diagonal are skipped)
+ *   out      [N, heads, head_dim] bfloat16 (written): softmax over the query's
+ *            keys of scale * q.k, times v; 0 for a query with no key
+ *   workspace: nsa_blockmask_attn_workspace_size(...) bytes (values transposed).
+ *   bfloat16, head_dim 128, max_seqlen <= 32768; errors are reported before
+ *   anything is launched.
+ */
+size_t nsa_blockmask_attn_workspace_size(int32_t batch, int32_t max_seqlen, int32_t heads);
+nsa_status nsa_blockmask_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
+                                  const uint8_t* mask, int32_t causal, void* out,
+                                  const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                                  int32_t heads, int32_t head_dim, float softmax_scale,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nsa_window_attn_fwd -- sliding-window attention of prefill rows.

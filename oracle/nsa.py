@@ -273,6 +273,31 @@ def selected_attention_row(q, k_seq, v_seq, idx, t: int, block: int, scale: floa
     return out
 
 
+def blockmask_attention_row(q, k_seq, v_seq, mask_rows, t: int, block: int, scale: float,
+                            causal: bool = False) -> np.ndarray:
+    """Block-mask attention of query position t of one sequence (TileLang NSA,
+    section 1: the attention matrix in block x block tiles, a block mask marking
+    the computed ones, the lower triangle only when causal).
+
+    q: [H, D] (the query's heads); k_seq, v_seq: [L, H, D] (multi-head, one K/V
+    head per query head); mask_rows: [H, nb, nb].  Head h attends to the keys j
+    with mask_rows[h, t // block, j // block] != 0 (and j <= t when causal);
+    a query with no key gets 0."""
+    q = np.asarray(q, dtype=np.float64)
+    k_seq = np.asarray(k_seq, dtype=np.float64)
+    v_seq = np.asarray(v_seq, dtype=np.float64)
+    H, D = q.shape
+    L = k_seq.shape[0]
+    j = np.arange(L)
+    out = np.zeros((H, D))
+    for h in range(H):
+        on = np.asarray(mask_rows[h, t // block])[j // block] != 0
+        if causal:
+            on &= j <= t
+        out[h] = attend(q[h], k_seq[on, h], v_seq[on, h], scale)
+    return out
+
+
 def window_attention_row(q, k_seq, v_seq, t: int, window: int, scale: float) -> np.ndarray:
     """Sliding-window branch (R9): keys max(0, t-window+1) .. t.  (NSA section 1.1.)"""
     q = np.asarray(q, dtype=np.float64)

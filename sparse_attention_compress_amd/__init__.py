@@ -102,6 +102,10 @@ _SIGS = {
                                                ctypes.POINTER(OffloadState), c_vp, c_sz, c_vp]),
     "nsa_compressed_attn_workspace_size": (c_sz, [c_i32] * 7),
     "nsa_window_attn_workspace_size": (c_sz, [c_i32] * 3),
+    "nsa_blockmask_attn_workspace_size": (c_sz, [c_i32] * 3),
+    "nsa_blockmask_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i32, c_vp,
+                                              c_vp, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_sz,
+                                              c_vp]),
     "nsa_compressed_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_int,
                                                c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32,
                                                c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -338,6 +342,25 @@ def nsa_decode_step_offload(params: DecodeParams, state: OffloadState, workspace
 
 KERNEL_POOL, KERNEL_LOGITS, KERNEL_BLOCK_SCORES, KERNEL_SELECTED_ATTN, KERNEL_COMBINE = 0, 1, 2, 3, 4
 KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN, KERNEL_FETCH = 5, 6, 7, 8
+KERNEL_BLOCKMASK_ATTN = 9
+
+
+def blockmask_attn_workspace_size(batch, max_seqlen, heads):
+    return lib().nsa_blockmask_attn_workspace_size(int(batch), int(max_seqlen), int(heads))
+
+
+def nsa_blockmask_attn_fwd(q, k, v, mask, cu_seqlens, max_seqlen, out, causal=False,
+                           softmax_scale=0.0, workspace=None, stream=None):
+    """q, k, v, out [N, H, 128] bf16; mask [B, H, nb, nb] uint8, nb = ceil(max_seqlen / 64)."""
+    N, H, D = q.shape
+    batch = cu_seqlens.numel() - 1
+    need = blockmask_attn_workspace_size(batch, max_seqlen, H)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check(lib().nsa_blockmask_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(mask),
+                                        int(bool(causal)), _ptr(out), _ptr(cu_seqlens), batch,
+                                        int(max_seqlen), H, D, float(softmax_scale), _ptr(ws),
+                                        nbytes, _stream(stream)))
+    return out
 
 
 def compressed_attn_workspace_size(batch, rows, max_seqlen_k, heads, kv_heads, kernel=32, stride=16):

@@ -558,6 +558,38 @@ nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v
   return hip_status(nsa::launch_compressed_prefill(a, stream), fn);
 }
 
+size_t nsa_blockmask_attn_workspace_size(int32_t batch, int32_t max_seqlen, int32_t heads) {
+  if (batch <= 0 || max_seqlen <= 0 || heads <= 0) return 0;
+  return (nsa::transposed_bytes(batch, heads, max_seqlen) + 255) & ~size_t(255);
+}
+
+nsa_status nsa_blockmask_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
+                                  const uint8_t* mask, int32_t causal, void* out,
+                                  const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                                  int32_t heads, int32_t head_dim, float softmax_scale,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_blockmask_attn_fwd";
+  NSA_REQUIRE(batch >= 0 && max_seqlen >= 0 && heads >= 1, NSA_ERR_INVALID_ARG, "%s: bad batch, max_seqlen or heads", fn);
+  NSA_REQUIRE(dtype == NSA_BF16, NSA_ERR_UNSUPPORTED, "%s: bfloat16 inputs only", fn);
+  NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
+  NSA_REQUIRE(max_seqlen <= nsa::kBlockMaskMaxLen, NSA_ERR_UNSUPPORTED, "%s: max_seqlen %d above %d", fn, max_seqlen, nsa::kBlockMaskMaxLen);
+  NSA_REQUIRE(heads <= 65535 && batch <= 65535, NSA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  if (batch == 0 || max_seqlen == 0) return ok();
+  NSA_REQUIRE(q && k && v && mask && out && cu_seqlens, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), NSA_ERR_INVALID_ARG,
+              "%s: q, k, v, out must be 16-byte aligned", fn);
+  const size_t need = nsa_blockmask_attn_workspace_size(batch, max_seqlen, heads);
+  NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  return hip_status(nsa::launch_blockmask_attn(
+                        static_cast<const nsa::bf16_t*>(q), static_cast<const nsa::bf16_t*>(k),
+                        static_cast<const nsa::bf16_t*>(v), mask, causal != 0,
+                        static_cast<nsa::bf16_t*>(out), cu_seqlens, batch, max_seqlen, heads,
+                        scale_log2_of(softmax_scale, head_dim), static_cast<nsa::bf16_t*>(workspace),
+                        stream),
+                    fn);
+}
+
 nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_dtype dtype,
                                void* out, nsa_dtype out_dtype, float* lse,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -48,7 +48,8 @@ enum KernelKind {
   kKindCmpProbs = 6,
   kKindWindow = 7,
   kKindFetch = 8,
-  kKindCount = 9
+  kKindMask = 9,
+  kKindCount = 10
 };
 
 // One armed (start, stop) event pair per kernel kind, per host thread.
@@ -203,6 +204,13 @@ struct WindowPrefillArgs {
   const bf16_t* o_sel;   // [rows, heads, 128] (with gates)
 };
 hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s);
+
+// Block-mask attention (multi-head, bf16): longest sequence it takes.
+constexpr int kBlockMaskMaxLen = 32768;
+hipError_t launch_blockmask_attn(const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                 const unsigned char* mask, int causal, bf16_t* out,
+                                 const int* cu, int batch, int max_seqlen, int heads,
+                                 float scale_log2, bf16_t* vt, hipStream_t s);
 
 // Values transposed per (sequence, KV head, dim) for the prefill branches.
 int transposed_ld(int max_len);

@@ -618,6 +618,155 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
   }
 }
 
+// ------------------------------------------------------ block-mask attention
+
+// Block-sparse attention with a block mask (TileLang NSA, section 1): query
+// block i of sequence b and head h attends to the keys of every key block j
+// with mask[b][h][i][j] != 0 (and, when causal, to keys <= its own position).
+// Multi-head: Q, K, V [N, heads, 128] packed by cu_seqlens (queries are the
+// sequence's own tokens).  One workgroup per (query block of 64 tokens, head,
+// sequence); its 2 waves hold 2 column tiles of 16 tokens each (the MFMA
+// columns are tokens of one head here).  The active 32-key tiles are listed in
+// LDS from the mask row, then staged and consumed as in the window branch.
+constexpr int kMaskWaves = 2, kMaskTpw = 2, kMaskThreads = kMaskWaves * kWave;
+constexpr int kMaskMaxBlocks = kBlockMaskMaxLen / 64;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kMaskThreads) __attribute__((amdgpu_waves_per_eu(2))) void blockmask_attn_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vtr,
+    int ldv, const unsigned char* __restrict__ mask, int nb_max, const int* __restrict__ cu,
+    int heads, float scale_log2, bf16_t* __restrict__ out) {
+  constexpr int D = kHeadDim;
+  constexpr float kLazy = 8.f;
+  __shared__ TileLds T;
+  __shared__ int tiles_s[2 * kMaskMaxBlocks];
+  __shared__ int n_tiles_s;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s0 = cu[b], L = cu[b + 1] - s0;
+  if (64 * qb >= L) return;  // whole workgroup
+  const int nkb = min((L + 63) / 64, nb_max);  // a max_seqlen below L reads no mask past nb_max
+  // active key tiles of this query block, ascending (wave 0 scans the mask row)
+  if (wave == 0) {
+    const unsigned char* mrow = mask + ((size_t(b) * heads + h) * nb_max + qb) * nb_max;
+    int base = 0;
+    for (int j0 = 0; j0 < nkb; j0 += kWave) {
+      const int j = j0 + lane;
+      const bool on = j < nkb && mrow[j] != 0 && (!CAUSAL || j <= qb);
+      const unsigned long long m = __ballot(on);
+      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (on) {
+        tiles_s[2 * pos] = 64 * j;
+        tiles_s[2 * pos + 1] = 64 * j + 32;
+      }
+      base += __popcll(m);
+    }
+    if (lane == 0) n_tiles_s = 2 * base;
+  }
+  // the wave's tokens: 64 qb + 32 wave + 16 jt + c16 (jt < kMaskTpw)
+  int tok[kMaskTpw];
+  uint4 qbop[kMaskTpw][4];
+#pragma unroll
+  for (int jt = 0; jt < kMaskTpw; ++jt) {
+    tok[jt] = 64 * qb + 32 * wave + 16 * jt + c16;
+    const bf16_t* qp = q + (size_t(s0 + min(tok[jt], L - 1)) * heads + h) * D + 8 * r4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qbop[jt][i] = ld16(qp + 32 * i);
+  }
+  float m_run[kMaskTpw], l_run[kMaskTpw];
+  f32x4_t acc[kMaskTpw][8];
+#pragma unroll
+  for (int jt = 0; jt < kMaskTpw; ++jt) {
+    m_run[jt] = -INFINITY;
+    l_run[jt] = 0.f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[jt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  const int n_tiles = n_tiles_s;
+  const size_t rs = size_t(heads) * D;
+  const bf16_t* kb = k + size_t(s0) * rs + size_t(h) * D;
+  const bf16_t* vt = vtr + (size_t(b) * heads + h) * D * size_t(ldv);
+  auto process = [&](int key0, const KeyFrag& ka, const bf16_t* vs) {
+    // keys past the sequence, and (causal) keys after a token, are masked; a
+    // tile wholly before the query block and inside the sequence needs no mask
+    const bool inside = key0 + 31 < L && (!CAUSAL || key0 + 31 < 64 * qb);
+    bf16x8_t pb[kMaskTpw];
+#pragma unroll
+    for (int jt = 0; jt < kMaskTpw; ++jt) {
+      float sv[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4_t sc = tile_scores(ka, hh, qbop[jt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * hh + e] = sc[e];
+      }
+      if (!inside) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = key0 + 16 * (e >> 2) + 4 * r4 + (e & 3);
+          if (key >= L || (CAUSAL && key > tok[jt])) sv[e] = -INFINITY;
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = rows_max(mx) * scale_log2;
+      if (mx > m_run[jt] + kLazy) {
+        const float alpha = fast_exp2(m_run[jt] - mx);
+        m_run[jt] = mx;
+        l_run[jt] *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[jt][n] *= alpha;
+      }
+      float p[8];
+      if (m_run[jt] == -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = 0.f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(sv[e], scale_log2, -m_run[jt]));
+          l_run[jt] += p[e];
+        }
+      }
+      pb[jt] = pack_p(p);
+    }
+    tile_pv<kMaskTpw>(vs, pb, acc);
+  };
+  // the listed tiles, double-buffered through LDS as in lds_tile_loop
+  if (n_tiles > 0) {
+    TileRegs<kMaskThreads> r;
+    fetch_tile<true>(kb, rs, vt, ldv, tiles_s[0], L - 1, r);
+    stash_tile<true>(T, 0, r);
+    __syncthreads();
+    int buf = 0;
+    for (int it = 0; it < n_tiles; ++it) {
+      const bool more = it + 1 < n_tiles;
+      if (more) fetch_tile<true>(kb, rs, vt, ldv, tiles_s[it + 1], L - 1, r);
+      KeyFrag ka;
+      read_keys(T, buf, ka);
+      process(tiles_s[it], ka, static_cast<const bf16_t*>(T.v[buf]));
+      if (more) stash_tile<true>(T, buf ^ 1, r);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < kMaskTpw; ++jt) {
+    const float l = rows_sum(l_run[jt]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (tok[jt] >= L) continue;
+    bf16_t* dst = out + (size_t(s0 + tok[jt]) * heads + h) * D + 4 * r4;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<uint2*>(dst + 16 * n) =
+          make_uint2(pack_bf16x2(acc[jt][n][0] * inv, acc[jt][n][1] * inv),
+                     pack_bf16x2(acc[jt][n][2] * inv, acc[jt][n][3] * inv));
+  }
+}
+
 // --------------------------------------------------------------------------- host
 
 // Tokens per wave of each kernel: the normaliser pass keeps no output
@@ -706,6 +855,20 @@ hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s) {
     case 16: return launch_win_g<16>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_blockmask_attn(const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                 const unsigned char* mask, int causal, bf16_t* out,
+                                 const int* cu, int batch, int max_seqlen, int heads,
+                                 float scale_log2, bf16_t* vt, hipStream_t s) {
+  if (batch == 0 || max_seqlen == 0) return hipSuccess;
+  hipError_t e = launch_transpose(v, cu, batch, heads, max_seqlen, vt, s);
+  if (e != hipSuccess) return e;
+  const int nb = (max_seqlen + 63) / 64;
+  const int ldv = transposed_ld(max_seqlen);
+  auto kern = causal ? blockmask_attn_kernel<true> : blockmask_attn_kernel<false>;
+  return launch_kernel(kKindMask, kern, dim3(nb, heads, batch), dim3(kMaskThreads), s, q, k,
+                       static_cast<const bf16_t*>(vt), ldv, mask, nb, cu, heads, scale_log2, out);
 }
 
 }  // namespace nsa

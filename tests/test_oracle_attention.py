@@ -204,3 +204,51 @@ def test_three_branch_gates_and_dense_equivalence():
             res["out"][i],
             g[t][:, 0:1] * res["o_cmp"][i] + g[t][:, 1:2] * res["o_sel"][i] + g[t][:, 2:3] * res["o_win"][i],
             rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------- block-mask attention
+
+def _sdpa_masked(q, k, v, allowed):
+    """torch's SDPA in float64 with a boolean [T, L] mask per head; rows with no
+    allowed key are set to 0 (SDPA would give NaN)."""
+    import torch
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]      # [1, H, T, D]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None]
+    m = torch.from_numpy(allowed)[None]                  # [1, H, T, L]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m)
+    o = torch.nan_to_num(o, nan=0.0)
+    o = torch.where(m.any(-1, keepdim=True), o, torch.zeros_like(o))
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("density", [1.0, 0.5, 0.0])
+def test_blockmask_attention_matches_masked_sdpa(causal, density):
+    rng = np.random.default_rng(41)
+    L, H, D, blk = 200, 3, 16, 64
+    nb = -(-L // blk)
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, H, D))
+    v = rng.standard_normal((L, H, D))
+    mask = (rng.random((H, nb, nb)) < density).astype(np.uint8)
+    scale = 1 / math.sqrt(D)
+    # the token-level mask written out from the blocks, independently of the oracle
+    allowed = np.zeros((H, L, L), dtype=bool)
+    for h in range(H):
+        for t in range(L):
+            for j in range(L):
+                allowed[h, t, j] = bool(mask[h, t // blk, j // blk]) and (not causal or j <= t)
+    ref = _sdpa_masked(q, k, v, allowed)
+    got = np.stack([oracle.blockmask_attention_row(q[t], k, v, mask, t, blk, scale, causal)
+                    for t in range(L)])
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+    if density == 1.0 and not causal:
+        # every block on: plain dense attention
+        import torch
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q).permute(1, 0, 2), torch.from_numpy(k).permute(1, 0, 2),
+            torch.from_numpy(v).permute(1, 0, 2)).permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(got, dense, atol=1e-12)
+    if density == 0.0:
+        assert np.all(got == 0.0)

@@ -425,7 +425,6 @@ def prefill_params(q, k, v, k_c, v_c, gates, cu_seqlens_q, cu_seqlens_k, cu_seql
     p.kernel, p.stride, p.block_size = kernel, stride, block_size
     p.topk, p.n_init, p.n_local, p.window = int(topk), int(n_init), int(n_local), int(window)
     p.softmax_scale = float(softmax_scale)
-    p.n_cand = int(n_cand)
     return p
 
 

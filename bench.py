@@ -41,6 +41,9 @@ def parse():
                          "decode, 12 for decode-long: enough that the selected K/V of the "
                          "rotation exceeds the 256 MB Infinity Cache)")
     ap.add_argument("--pinned-32k", action="store_true", help="all contexts 32768")
+    ap.add_argument("--batch", type=int, default=8,
+                    help="decode: sequences per step (the metric's configuration is 8; larger "
+                         "batches show the kernels at larger launch sizes)")
     ap.add_argument("--kc-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--n-cand", type=int, default=0,
                     help="decode: > 0 selects in two stages (the n_cand best blocks by the "
@@ -156,8 +159,10 @@ def main():
         w = W.cis_decode()
         n_layers = args.layers or 12
     else:
-        w = W.nosa1b_decode(pinned_32k=args.pinned_32k)
-        n_layers = args.layers or 28
+        w = W.nosa1b_decode(pinned_32k=args.pinned_32k, batch=args.batch)
+        # enough layer buffers that a rotation's selected K/V (4 MiB per sequence)
+        # exceeds the 256 MB Infinity Cache: 28 (the model's layers) at batch 8
+        n_layers = args.layers or max(2, -(-28 * 8 // args.batch))
     B, H, Hkv, D = w.batch, w.heads, w.kv_heads, w.head_dim
     lengths = list(w.lengths)
     nc = [nsa.full_windows(L) for L in lengths]

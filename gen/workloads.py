@@ -66,11 +66,14 @@ def tiny_decode() -> Workload:
                     torch.float32, topk=16, n_init=1, n_local=2)
 
 
-def nosa1b_decode(pinned_32k: bool = False) -> Workload:
+def nosa1b_decode(pinned_32k: bool = False, batch: int = 8) -> Workload:
+    """Batched decode; other batch sizes draw more lengths from the same stream
+    (the first 8 are the batch-8 lengths)."""
     seed = 0x5EED0002
-    lengths = [32768] * 8 if pinned_32k else uniform_ints(seed, S_LEN, 8, 8192, 32768)
-    name = "nosa1b_decode_b8_L32768" if pinned_32k else "nosa1b_decode_b8_L8k-32k"
-    return Workload(name, seed, "decode", 8, lengths, 16, 2, 128, torch.bfloat16,
+    lengths = [32768] * batch if pinned_32k else uniform_ints(seed, S_LEN, batch, 8192, 32768)
+    span = "L32768" if pinned_32k else "L8k-32k"
+    name = f"nosa1b_decode_b{batch}_{span}"
+    return Workload(name, seed, "decode", batch, lengths, 16, 2, 128, torch.bfloat16,
                     topk=64, n_init=1, n_local=1024 // 64, cis_select=True)
 
 

@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -665,7 +666,62 @@ def blockmask_main(args, dev):
                            "vs_baseline = their ms / ours"} if pages_ms else None),
         "timed_gpu_ms": round(gpu_ms, 3),
     }
+    if not args.no_cpu_baseline:
+        import oracle
+        qn = q.float().cpu().numpy().astype(np.float64)
+        kn, vn = k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+        scale = 1.0 / math.sqrt(D)
+
+        def rows_fn(rows):
+            for r in rows:
+                b_, t_ = divmod(r, seq)
+                s0 = b_ * seq
+                oracle.blockmask_attention_row(qn[r], kn[s0:s0 + seq], vn[s0:s0 + seq], m[b_], t_,
+                                               64, scale, args.causal)
+        result["cpu_baseline"] = sampled_oracle_baseline(rows_fn, w.total_tokens, w.total_tokens,
+                                                         args.cpu_seconds, "query rows")
     print(json.dumps(result), flush=True)
+
+
+def sampled_oracle_baseline(rows_fn, n_rows_total, tokens_total, seconds, what, chunk=1,
+                            fixed_fn=None):
+    """CPU baseline of a prefill workload: the float64 oracle on one host thread
+    over evenly strided sample rows (calls of `chunk` rows) until `seconds` are
+    spent, extrapolated to every row of the step.  `fixed_fn`, if given, is the
+    per-call work done once for the whole step (pooling the sequence): it is timed
+    once, taken out of every call and counted once."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    order = np.linspace(0, n_rows_total - 1, num=min(n_rows_total, 8192)).round().astype(np.int64)
+    done, spent, calls, fixed = 0, 0.0, 0, 0.0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        if fixed_fn is not None:
+            t0 = time.perf_counter()
+            fixed_fn()
+            fixed = time.perf_counter() - t0
+        for i in range(0, len(order), chunk):
+            rows = [int(r) for r in order[i:i + chunk]]
+            t0 = time.perf_counter()
+            rows_fn(rows)
+            spent += time.perf_counter() - t0
+            done += len(rows)
+            calls += 1
+            if spent >= seconds:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    per_row = max(spent - calls * fixed, 1e-9) / done
+    step_s = fixed + per_row * n_rows_total
+    return {"value": round(tokens_total / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {n_rows_total} {what} (evenly strided), {spent:.1f} s on one host "
+                      f"thread, extrapolated to the whole step ({step_s:.4g} s)"}
 
 
 def prefill_main(args, dev):
@@ -784,6 +840,37 @@ def prefill_main(args, dev):
         "selected_gathered_gbs": round(gathered / (kern["selected_attn"] * 1e-6) / 1e9, 1),
         "timed_gpu_ms": round(gpu_ms, 3),
     }
+    if not args.no_cpu_baseline:
+        import oracle
+        scale = 1.0 / math.sqrt(D)
+        kn, vn = k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+        qn = q.float().cpu().numpy().astype(np.float64)
+        if args.workload == "prefill-selected":
+            idn = idx.cpu().numpy()
+            L0 = w.lengths[0]
+
+            def rows_fn(rows):  # rows of equal-length sequences, packed
+                for r in rows:
+                    b_, t_ = divmod(r, L0)
+                    s0 = b_ * L0
+                    oracle.selected_attention_row(qn[r], kn[s0:s0 + L0], vn[s0:s0 + L0], idn[r], t_,
+                                                  64, scale)
+            result["cpu_baseline"] = sampled_oracle_baseline(rows_fn, w.total_tokens, w.total_tokens,
+                                                             args.cpu_seconds, "query rows")
+        else:
+            gn = g.float().cpu().numpy().astype(np.float64)
+            one = np.array([0, w.lengths[0]])
+            onec = np.array([0, nc])
+
+            def pool():  # what every oracle call redoes once: K and V pooled
+                oracle.mean_pool_varlen(kn, one, onec, 32, 16)
+                oracle.mean_pool_varlen(vn, one, onec, 32, 16)
+
+            def rows_fn(rows):
+                oracle.nsa_prefill_rows(qn, kn, vn, gn, rows, topk=w.topk, window=w.window)
+            result["cpu_baseline"] = sampled_oracle_baseline(rows_fn, w.total_tokens, w.total_tokens,
+                                                             args.cpu_seconds, "query rows",
+                                                             chunk=32, fixed_fn=pool)
     print(json.dumps(result), flush=True)
 
 

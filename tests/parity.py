@@ -18,7 +18,6 @@ import sys
 import numpy as np
 import torch
 
-import oracle
 
 BAND = 1e-3
 

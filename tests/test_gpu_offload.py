@@ -9,7 +9,6 @@ blocks already held are kept; every other listed block takes the next free slot
 (empty slots first, then slots holding a block the step does not list, each in
 ascending order), misses in list order.
 """
-import numpy as np
 import pytest
 import torch
 

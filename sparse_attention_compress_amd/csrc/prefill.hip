@@ -288,11 +288,10 @@ __device__ __forceinline__ void store_rows(void* __restrict__ out, int out_f32, 
 
 // ------------------------------------------------------------- compressed branch
 
-// Query tokens per workgroup (a multiple of 16 consecutive tokens of one
-// sequence and KV group); a wave holds TPW of them and a workgroup
-// kGroupTokens / TPW waves.  Fewer tokens per wave means fewer registers and
+// Query tokens per workgroup (GT consecutive tokens of one sequence and KV
+// group; a template parameter of each kernel); a wave holds TPW of them and a
+// workgroup GT / TPW waves.  Fewer tokens per wave means fewer registers and
 // more waves per SIMD; the tiles are shared through LDS either way.
-constexpr int kGroupTokens = 16;
 
 // The tokens of one wave: query positions tq0 .. tq0 + n - 1 of sequence b
 // (grid z), packed rows row0 .. row0 + n - 1, key positions t0 .. t0 + n - 1.
@@ -300,17 +299,18 @@ struct WaveRows {
   int n, row0, t0;
 };
 
-// Key positions of the first and last query tokens of workgroup `grp` of
-// sequence b; returns false when the workgroup has none.
+// Key positions of the first and last query tokens of workgroup `grp` (GT
+// tokens a workgroup) of sequence b; returns false when the workgroup has none.
+template <int GT>
 __device__ __forceinline__ bool group_span(const int* __restrict__ cu_q,
                                            const int* __restrict__ cu_k, int b, int grp,
                                            int& t_first, int& t_last) {
   const int lq = cu_q[b + 1] - cu_q[b];
   const int lk = cu_k[b + 1] - cu_k[b];
-  const int tq = grp * kGroupTokens;
+  const int tq = grp * GT;
   if (tq >= lq) return false;
   t_first = tq + (lk - lq);
-  t_last = min(tq + kGroupTokens, lq) - 1 + (lk - lq);
+  t_last = min(tq + GT, lq) - 1 + (lk - lq);
   return true;
 }
 
@@ -330,8 +330,8 @@ __device__ __forceinline__ WaveRows wave_rows(const int* __restrict__ cu_q,
 // PROBS = false: per (row, head) log2 normaliser lse2 = max + log2(sum exp2).
 // PROBS = true:  o_cmp, natural-log lse, and the group's block scores.
 // vct: the compressed values transposed ([batch][kv][128][ldv]).
-template <int G, bool PROBS, int TPW>
-__global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill_kernel(
+template <int G, bool PROBS, int TPW, int GT>
+__global__ __launch_bounds__(GT / TPW * kWave) void compressed_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vct,
     int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
     const int* __restrict__ cu_c, int kv_heads, float scale_log2, float* __restrict__ lse2,
@@ -343,9 +343,9 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
   const int c16 = lane & 15, r4 = lane >> 4;
   const int kv = blockIdx.y, b = blockIdx.z;
   int t_first, t_last;
-  if (!group_span(cu_q, cu_k, b, blockIdx.x, t_first, t_last)) return;  // whole workgroup
-  constexpr int kTpw = TPW, kThreads = kGroupTokens / TPW * kWave;
-  const WaveRows R = wave_rows<TPW>(cu_q, cu_k, b, blockIdx.x * (kGroupTokens / TPW) + wave);
+  if (!group_span<GT>(cu_q, cu_k, b, blockIdx.x, t_first, t_last)) return;  // whole workgroup
+  constexpr int kTpw = TPW, kThreads = GT / TPW * kWave;
+  const WaveRows R = wave_rows<TPW>(cu_q, cu_k, b, blockIdx.x * (GT / TPW) + wave);
   const bool active = R.n > 0;  // waves past the sequence only help with the tiles
   const int len = cu_k[b + 1] - cu_k[b];
   const int cbase = cu_c[b];
@@ -495,8 +495,8 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void compressed_prefill
 // is g0 * o_cmp + g1 * o_sel + g2 * o_win (the other branches' outputs are bf16 rows).
 // The wave's tokens share the key tiles of the union of their windows.
 // vtr: the values transposed ([batch][kv][128][ldv]).
-template <int G, bool GATED, int TPW>
-__global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_kernel(
+template <int G, bool GATED, int TPW, int GT>
+__global__ __launch_bounds__(GT / TPW * kWave) void window_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vtr,
     int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads,
     int window, float scale_log2, void* __restrict__ out, int out_f32,
@@ -509,9 +509,9 @@ __global__ __launch_bounds__(kGroupTokens / TPW * kWave) void window_prefill_ker
   const int c16 = lane & 15, r4 = lane >> 4;
   const int kv = blockIdx.y, b = blockIdx.z;
   int t_first, t_last;
-  if (!group_span(cu_q, cu_k, b, blockIdx.x, t_first, t_last)) return;  // whole workgroup
-  constexpr int kTpw = TPW, kThreads = kGroupTokens / TPW * kWave;
-  const WaveRows R = wave_rows<TPW>(cu_q, cu_k, b, blockIdx.x * (kGroupTokens / TPW) + wave);
+  if (!group_span<GT>(cu_q, cu_k, b, blockIdx.x, t_first, t_last)) return;  // whole workgroup
+  constexpr int kTpw = TPW, kThreads = GT / TPW * kWave;
+  const WaveRows R = wave_rows<TPW>(cu_q, cu_k, b, blockIdx.x * (GT / TPW) + wave);
   const bool active = R.n > 0;  // waves past the sequence only help with the tiles
   size_t head0[kTpw];
   uint4 qb[kTpw][4];
@@ -770,16 +770,19 @@ __global__ __launch_bounds__(kMaskThreads) __attribute__((amdgpu_waves_per_eu(2)
 
 // --------------------------------------------------------------------------- host
 
-// Tokens per wave of each kernel: the normaliser pass keeps no output
-// accumulators and holds 4; the passes with P.V hold 2 (8 waves a workgroup).
-constexpr int kTpwLse = 4, kTpwOut = 2;
+// Tokens per wave and per workgroup of each kernel: the normaliser pass keeps
+// no output accumulators and holds 4 tokens a wave, 16 a workgroup; the passes
+// with P.V hold 1 a wave, 8 a workgroup (about 100 VGPRs, four waves per SIMD:
+// 6% faster than 2 a wave and 16 a workgroup at 190 VGPRs, while the normaliser
+// pass measured 23% slower at 8 a workgroup).
+constexpr int kTpwLse = 4, kGtLse = 16, kTpwOut = 1, kGtOut = 8;
 
-// Grid: (groups of kGroupTokens tokens, kv head, sequence).
-static dim3 prefill_grid(int max_seqlen_q, int kv_heads, int batch) {
-  return dim3((max_seqlen_q + kGroupTokens - 1) / kGroupTokens, kv_heads, batch);
+// Grid: (groups of gt tokens, kv head, sequence).
+static dim3 prefill_grid(int max_seqlen_q, int kv_heads, int batch, int gt) {
+  return dim3((max_seqlen_q + gt - 1) / gt, kv_heads, batch);
 }
 
-static dim3 prefill_block(int tpw) { return dim3(kGroupTokens / tpw * kWave); }
+static dim3 prefill_block(int tpw, int gt) { return dim3(gt / tpw * kWave); }
 
 int transposed_ld(int max_len) { return (max_len + 63) / 64 * 64; }
 
@@ -798,18 +801,19 @@ static hipError_t launch_transpose(const bf16_t* x, const int* cu, int batch, in
 
 template <int G>
 static hipError_t launch_cmp_g(const CompressedPrefillArgs& a, hipStream_t s) {
-  const dim3 grid = prefill_grid(a.max_seqlen_q, a.kv_heads, a.batch);
   const int ldv = transposed_ld(a.max_windows);
   hipError_t e = launch_transpose(a.vc, a.cu_c, a.batch, a.kv_heads, a.max_windows, a.vct, s);
   if (e != hipSuccess) return e;
-  e = launch_kernel(kKindCmpLse, compressed_prefill_kernel<G, false, kTpwLse>, grid,
-                    prefill_block(kTpwLse), s, a.q,
+  e = launch_kernel(kKindCmpLse, compressed_prefill_kernel<G, false, kTpwLse, kGtLse>,
+                    prefill_grid(a.max_seqlen_q, a.kv_heads, a.batch, kGtLse),
+                    prefill_block(kTpwLse, kGtLse), s, a.q,
                     a.kc, static_cast<const bf16_t*>(a.vct), ldv, a.cu_q, a.cu_k, a.cu_c,
                     a.kv_heads, a.scale_log2, a.lse2, static_cast<void*>(nullptr), 0,
                     static_cast<float*>(nullptr), static_cast<float*>(nullptr), 0);
   if (e != hipSuccess) return e;
-  return launch_kernel(kKindCmpProbs, compressed_prefill_kernel<G, true, kTpwOut>, grid,
-                       prefill_block(kTpwOut), s,
+  return launch_kernel(kKindCmpProbs, compressed_prefill_kernel<G, true, kTpwOut, kGtOut>,
+                       prefill_grid(a.max_seqlen_q, a.kv_heads, a.batch, kGtOut),
+                       prefill_block(kTpwOut, kGtOut), s,
                        a.q, a.kc, static_cast<const bf16_t*>(a.vct), ldv, a.cu_q, a.cu_k, a.cu_c,
                        a.kv_heads, a.scale_log2, a.lse2, a.o_cmp, a.out_f32, a.lse_nat,
                        a.block_scores, a.nb_max);
@@ -829,18 +833,18 @@ hipError_t launch_compressed_prefill(const CompressedPrefillArgs& a, hipStream_t
 
 template <int G>
 static hipError_t launch_win_g(const WindowPrefillArgs& a, hipStream_t s) {
-  const dim3 grid = prefill_grid(a.max_seqlen_q, a.kv_heads, a.batch);
+  const dim3 grid = prefill_grid(a.max_seqlen_q, a.kv_heads, a.batch, kGtOut);
   const int ldv = transposed_ld(a.max_seqlen_k);
   hipError_t e = launch_transpose(a.v, a.cu_k, a.batch, a.kv_heads, a.max_seqlen_k, a.vt, s);
   if (e != hipSuccess) return e;
   const bf16_t* vt = a.vt;
   if (a.gates != nullptr)
-    return launch_kernel(kKindWindow, window_prefill_kernel<G, true, kTpwOut>, grid,
-                         prefill_block(kTpwOut), s, a.q,
+    return launch_kernel(kKindWindow, window_prefill_kernel<G, true, kTpwOut, kGtOut>, grid,
+                         prefill_block(kTpwOut, kGtOut), s, a.q,
                          a.k, vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
                          a.out_f32, a.lse_nat, a.gates, a.o_cmp, a.o_sel);
-  return launch_kernel(kKindWindow, window_prefill_kernel<G, false, kTpwOut>, grid,
-                       prefill_block(kTpwOut), s, a.q, a.k,
+  return launch_kernel(kKindWindow, window_prefill_kernel<G, false, kTpwOut, kGtOut>, grid,
+                       prefill_block(kTpwOut, kGtOut), s, a.q, a.k,
                        vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
                        a.out_f32, a.lse_nat, static_cast<const float*>(nullptr),
                        static_cast<const bf16_t*>(nullptr), static_cast<const bf16_t*>(nullptr));

@@ -457,7 +457,7 @@ template <int G, int THREADS, int MAXB>
 __device__ __forceinline__ void block_scores_from_logits(
     SelShared<THREADS, MAXB>& S, float (&sc)[SelCfg<THREADS, MAXB>::kPer],
     float (&scc)[SelCfg<THREADS, MAXB>::kPer], bool split_cis,
-    const ScoreInputs<G, THREADS, MAXB>& in, const float* __restrict__ logits,
+    ScoreInputs<G, THREADS, MAXB>& in, const float* __restrict__ logits,
     const float* __restrict__ cisb, float cis_weight, size_t unit, int nvis, int nb,
     int ldc, int nb_max, int nc_max, float* __restrict__ block_scores,
     float* __restrict__ window_probs) {
@@ -540,28 +540,18 @@ __device__ __forceinline__ void block_scores_from_logits(
     }
     return s;
   };
+  // Slab u is scored from preload set u % kPre, which then takes the loads of
+  // slab u + kPre: kPre slabs stay in flight.  Those loads are issued whether or
+  // not the slab holds blocks of this row (addresses clamped into the unit's
+  // rows), so no branch makes the wait counts conservative.
 #pragma unroll
   for (int u = 0; u < P; ++u) {
     sc[u] = 0.f;
     scc[u] = 0.f;
-    if (u < n_slab) {
-      if (u < kPre) {
-        sc[u] = score_slab(u, in.lg4[u < kPre ? u : 0], in.lgp[u < kPre ? u : 0]);
-      } else {
-        float4 w4[G];
-        float wp[G];
-        if (ldc > 0) {
-          load_window_slab<G, THREADS>(lrow, ldc, u, w4, wp);
-        } else {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            w4[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-            wp[h] = 0.f;
-          }
-        }
-        sc[u] = score_slab(u, w4, wp);
-      }
-    }
+    constexpr int kSets = kPre > 0 ? kPre : 1;
+    if (u < n_slab) sc[u] = score_slab(u, in.lg4[u % kSets], in.lgp[u % kSets]);
+    if (u + kPre < P && ldc > 0)
+      load_window_slab<G, THREADS>(lrow, ldc, u + kPre, in.lg4[u % kSets], in.lgp[u % kSets]);
   }
   if (block_scores != nullptr)
     for (int i = nb + tid; i < nb_max; i += THREADS) block_scores[unit * nb_max + i] = 0.f;

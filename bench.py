@@ -133,7 +133,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build runs on one GPU only "
-              "(no multi-GPU path exists; DESIGN.md describes how the path would shard).",
+              "(no multi-GPU path exists; the decode would shard over (sequence, KV head) "
+              "with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -132,7 +132,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: --gpus {args.gpus} requested, but this build runs on one GPU only "
+        print(f"bench.py: --gpus {args.gpus} requested, but the library runs on one GPU only "
               "(no multi-GPU path exists; the decode would shard over (sequence, KV head) "
               "with no exchange between GPUs).",
               file=sys.stderr)

@@ -1,7 +1,7 @@
 """Shared helpers of the GPU parity tests: host copies, tolerance checks and the
 index-set agreement rule.
 
-Gates (fixed by the benchmark's tolerances and derived where it gives none):
+Gates (the stated tolerances of the method's outputs, and derived ones where none is stated):
 * pooled means in float32: |gpu - ref| <= 1e-5 * max(|ref|, mean |x| of the
   window), i.e. 1e-5 relative to the magnitude of the summands;
 * attention outputs: 2e-2 absolute for bf16 inputs (fp32 accumulation); 1e-4

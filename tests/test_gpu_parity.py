@@ -471,6 +471,17 @@ def test_decode_step_two_stage(n_cand):
     assert exact >= 1
 
 
+def test_decode_step_large_batch():
+    """Twenty sequences with two KV heads: 40 (sequence, KV head) units already
+    fill 256 workgroups at 8 selected blocks per workgroup, so each split of the
+    single-kernel decode attends to 8 blocks, not the 4 of smaller batches."""
+    lengths = gen.uniform_ints(SEED + 18, 1, 20, 1000, 9000)
+    d = _decode_inputs(lengths, SEED + 18)
+    log(f"decode step large batch {lengths}")
+    out, bs, idx = _run_decode_step(d, 64, 1, 16, True, False, append=True)
+    _check_decode("large_batch", d, out, bs, idx, 64, 1, 16, True, False, atol=2e-2)
+
+
 @pytest.mark.parametrize("H,H_kv", [(32, 2), (8, 2), (4, 4)])
 def test_decode_step_group_sizes(H, H_kv):
     """GQA groups of 16, 4 and 1 query heads through the single-kernel decode path."""

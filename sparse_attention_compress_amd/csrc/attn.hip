@@ -590,7 +590,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 
 // Decode over a block pool (KV offload): like selected_attn_mfma_kernel with
 // SPLIT, but the K/V rows of listed block indices[unit][p] come from pool slot
-// slot_ids[unit][p] (nsa_offload_plan); grid (splits, kv heads, sequences).
+// slot_ids[unit][p] (the offload plan); a one-dimensional grid over (sequence,
+// kv head, split).
 template <int G, bool CIS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pool_attn_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kpool,
@@ -602,8 +603,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   __shared__ int ids_s[kMaxWgSlots];
   __shared__ int slots_s[kMaxWgSlots];
   __shared__ int nv_s;
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const size_t unit = size_t(b) * kv_heads + kv;
+  // one-dimensional grid over (sequence, kv head, split), XCD-grouped as in the
+  // resident decode step
+  const int n_split = (k_sel + bpw - 1) / bpw;
+  const int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
+  const int unit_i = m / n_split;
+  const int split = m - unit_i * n_split, kv = unit_i % kv_heads, b = unit_i / kv_heads;
+  const size_t unit = size_t(unit_i);
   uint4 qb[4];
   load_q_operand<G>(q, unit, qb);
   const int kstart = cu_k[b];
@@ -624,9 +630,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   }
   __syncthreads();
   attend_staged_blocks<G, CIS, true, true>(sm, ids_s, nv_s, qb, kpool, vpool, cis, kstart, t,
-                                           unit, kv, kv_heads, scale_log2, split,
-                                           int(gridDim.x), nullptr, nullptr, part_ml, part_acc,
-                                           slots_s, pool_slots);
+                                           unit, kv, kv_heads, scale_log2, split, n_split,
+                                           nullptr, nullptr, part_ml, part_acc, slots_s,
+                                           pool_slots);
 }
 
 // Decode: score the blocks, select and attend in one launch.  Every workgroup
@@ -635,7 +641,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 // only (the local window, or everything when all eligible blocks are chosen)
 // takes its ids from the geometry and starts on its K/V at once.  Each split
 // then attends to its run and writes a partial state; split 0 always selects
-// and also writes the debug outputs.  Grid (splits, kv heads, sequences).
+// and also writes the debug outputs.  One-dimensional grid over (sequence, kv
+// head, split), in XCD-grouped order.
 // MAXB bounds the blocks of a sequence: each thread keeps MAXB / 256 of them,
 // so a smaller bound means less work in every step of the selection.
 template <int G, bool CIS, int MAXB>
@@ -655,8 +662,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   __shared__ int ids_s[kMaxWgSlots];
   __shared__ int nv_s;
   const int tid = threadIdx.x;
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const size_t unit = size_t(b) * kv_heads + kv;
+  // one-dimensional grid: the splits of one (sequence, kv head) run on one XCD,
+  // which then reads the selection inputs of that unit into its L2 once
+  const int n_split = (topk + bpw - 1) / bpw;
+  const int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
+  const int unit_i = m / n_split;
+  const int split = m - unit_i * n_split, kv = unit_i % kv_heads, b = unit_i / kv_heads;
+  const size_t unit = size_t(unit_i);
   // the selection's inputs and the queries are in flight while the sequence
   // offsets arrive
   ScoreInputs<G, 256, MAXB> sin;
@@ -701,12 +713,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   }
   __syncthreads();
   attend_staged_blocks<G, CIS, true>(U.att, ids_s, nv_s, qb, k, v, cis, kstart, t, unit, kv,
-                                     kv_heads, scale_log2, split, int(gridDim.x), nullptr,
+                                     kv_heads, scale_log2, split, n_split, nullptr,
                                      nullptr, part_ml, part_acc);
 }
 
-// Merge the per-split partial states of one (row, kv head, query head): grid
-// (units, G), one thread per output dim.
+// Merge the per-split partial states of one (row, kv head, query head): a
+// one-dimensional grid over (unit, query head) in XCD-grouped order, like the
+// decode splits that wrote them; one thread per output dim.
 template <typename T>
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float2* __restrict__ part_ml,
                                                            const float* __restrict__ part_acc,
@@ -716,8 +729,9 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float2* __restr
   constexpr int D = kHeadDim;
   __shared__ float f_s[kMaxSplits];
   __shared__ float ML_s[2];
-  const size_t unit = blockIdx.x;
-  const int h = blockIdx.y, d = threadIdx.x;
+  const int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
+  const size_t unit = size_t(m / G);
+  const int h = m - int(unit) * G, d = threadIdx.x;
   // every load first: the (max, sum) pair of split d and this dim of every split
   const float2 ml0 = part_ml[(unit * n_split + min(d, n_split - 1)) * G + h];
   const float* src = part_acc + (unit * n_split * G + h) * D + d;
@@ -812,7 +826,7 @@ static hipError_t launch_attn_g(const void* q, const void* k, const void* v, con
         indices, k_sel, cis, static_cast<T*>(out), lse, cu_q, cu_k, batch, kv_heads, scale_log2,
         bpw, ws.part_ml, ws.part_acc);
     if (e != hipSuccess) return e;
-    return launch_kernel(kKindCombine, combine_kernel<T>, dim3(rows_total * kv_heads, G),
+    return launch_kernel(kKindCombine, combine_kernel<T>, dim3(rows_total * kv_heads * G),
                          dim3(kHeadDim), s, static_cast<const float2*>(ws.part_ml),
                          static_cast<const float*>(ws.part_acc), static_cast<T*>(out), lse,
                          n_split, G);
@@ -867,14 +881,14 @@ static hipError_t launch_select_attn_g(const DecodeScoresArgs& a, const void* k,
              : d.nb_max <= kFusedMidBlocks  ? select_attn_kernel<G, CIS, kFusedMidBlocks>
                                             : select_attn_kernel<G, CIS, kFusedMaxBlocks>;
   hipError_t e = launch_kernel(
-      kKindAttn, kern, dim3(n_split, a.kv_heads, a.batch), dim3(256), s,
+      kKindAttn, kern, dim3(n_split * a.kv_heads * a.batch), dim3(256), s,
       static_cast<const float*>(a.ws.logits), static_cast<const float2*>(a.ws.part), cisb,
       a.cis_weight, a.cu_k, a.cu_c, a.kv_heads, d.nc_max, d.ldc, d.nb_max, d.n_chunk_max, d.ldb,
       a.topk, a.n_init, a.n_local, a.n_cand, a.block_scores, a.indices, static_cast<const bf16_t*>(a.q),
       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), cis_values, a.scale_log2, bpw,
       ws.part_ml, ws.part_acc);
   if (e != hipSuccess) return e;
-  return launch_kernel(kKindCombine, combine_kernel<bf16_t>, dim3(a.batch * a.kv_heads, G),
+  return launch_kernel(kKindCombine, combine_kernel<bf16_t>, dim3(a.batch * a.kv_heads * G),
                        dim3(kHeadDim), s, static_cast<const float2*>(ws.part_ml),
                        static_cast<const float*>(ws.part_acc), static_cast<bf16_t*>(out),
                        static_cast<float*>(nullptr), n_split, G);
@@ -888,13 +902,13 @@ static hipError_t launch_pool_attn_g(const void* q, const OffloadArgs& a, const 
   const int bpw = attn_split_blocks(batch, a.kv_heads, a.k_sel);
   const int n_split = (a.k_sel + bpw - 1) / bpw;
   hipError_t e = launch_kernel(
-      kKindAttn, pool_attn_kernel<G, CIS>, dim3(n_split, a.kv_heads, batch), dim3(256), s,
+      kKindAttn, pool_attn_kernel<G, CIS>, dim3(n_split * a.units), dim3(256), s,
       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(a.kpool),
       static_cast<const bf16_t*>(a.vpool), a.indices, static_cast<const int*>(a.slot_ids),
       a.k_sel, a.pool_slots, cis_values, a.cu_k, a.kv_heads, scale_log2, bpw, ws.part_ml,
       ws.part_acc);
   if (e != hipSuccess) return e;
-  return launch_kernel(kKindCombine, combine_kernel<bf16_t>, dim3(a.units, G), dim3(kHeadDim), s,
+  return launch_kernel(kKindCombine, combine_kernel<bf16_t>, dim3(a.units * G), dim3(kHeadDim), s,
                        static_cast<const float2*>(ws.part_ml),
                        static_cast<const float*>(ws.part_acc), static_cast<bf16_t*>(out),
                        static_cast<float*>(nullptr), n_split, G);

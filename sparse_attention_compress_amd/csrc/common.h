@@ -207,6 +207,17 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
+// The workgroups of a launch are handed to the 8 XCDs in turn (launch-order id
+// modulo 8), and each XCD has its own L2.  This maps a launch-order id of a
+// one-dimensional grid of `total` workgroups to a logical index such that every
+// XCD takes one contiguous range of logical indices: workgroups with
+// neighbouring logical indices (the splits or chunks of one sequence and KV
+// head) then share one XCD and its L2.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_grouped_index(int id, int total) {
+  const int x = id & 7, j = id >> 3, q = total >> 3, r = total & 7;
+  return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
 // exp2 on the hardware unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

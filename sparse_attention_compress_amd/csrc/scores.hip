@@ -8,9 +8,10 @@
 // with stride 16); plus w * the same max of the pooled CIS; then the init and
 // local blocks forced in and the best other blocks picked, ids ascending.
 //
-// window_logits_kernel -- grid (chunk of 64 windows, kv head, sequence), 4 waves
-//   of 16 windows, on the matrix cores: S^T = Kc Q^T with the compressed-key rows
-//   loaded straight into the A operand and the group's queries as the B operand
+// window_logits_kernel -- one-dimensional grid over (sequence, kv head, chunk of
+//   64 windows) in XCD-grouped order, 4 waves of 16 windows, on the matrix
+//   cores: S^T = Kc Q^T with the compressed-key rows loaded straight into the A
+//   operand and the group's queries as the B operand
 //   (four v_mfma_f32_16x16x32_bf16 per wave when both are bf16, else thirty-two
 //   v_mfma_f32_16x16x4_f32 in full fp32).  Each compressed key is read from HBM
 //   once for the whole GQA group.
@@ -78,7 +79,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w
   __shared__ float newf_s[D];        // refreshed compressed key as the cache holds it
   __shared__ float cisw_s[kCisSpan];
   __shared__ float red_s[2][4][16];
-  const int b = blockIdx.z, kv = blockIdx.y, chunk = blockIdx.x;
+  // one-dimensional grid over (sequence, kv head, chunk): the chunks of one
+  // (sequence, kv head) run on one XCD, the one its decode splits run on
+  const int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
+  const int unit_i = m / n_chunk_max;
+  const int chunk = m - unit_i * n_chunk_max, kv = unit_i % kv_heads, b = unit_i / kv_heads;
   const int start = cu_k[b];
   const int len = cu_k[b + 1] - start;
   const int cbase = cu_c[b];
@@ -269,8 +274,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int topk, int n_init, int n_local, int n_cand) {
   __shared__ SelShared<kSelThreads, kMaxSortBlocks> S;
   const int tid = threadIdx.x;
-  const int row = blockIdx.x, kv = blockIdx.y;
-  const size_t unit = size_t(row) * kv_heads + kv;
+  // one-dimensional grid over (row, kv head) in XCD-grouped order: a decode row
+  // is selected on the XCD that wrote its window logits
+  const int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
+  const int row = m / kv_heads, kv = m - row * kv_heads;
+  const size_t unit = size_t(m);
   ScoreInputs<G, kSelThreads, kMaxSortBlocks> sin;
   if constexpr (FROM_LOGITS)  // in flight while the row's position is found
     load_score_inputs(sin, logits, part, cisb, unit, n_chunk_max, ldc, ldb);
@@ -421,14 +429,14 @@ static hipError_t launch_scores_g(const DecodeScoresArgs& a, hipStream_t s) {
   float* cisb = a.cis_pooled != nullptr ? a.ws.cisb : nullptr;
   if (d.n_chunk_max > 0) {
     hipError_t e = launch_kernel(
-        kKindLogits, window_logits_kernel<G, TQ, TKC>, dim3(d.n_chunk_max, a.kv_heads, a.batch),
+        kKindLogits, window_logits_kernel<G, TQ, TKC>, dim3(d.n_chunk_max * a.kv_heads * a.batch),
         dim3(256), s, static_cast<const TQ*>(a.q), static_cast<TKC*>(a.kc), a.cu_k, a.cu_c,
         a.ws.logits, a.ws.part, cisb, a.cis_pooled, a.kv_heads, d.ldc, d.n_chunk_max, d.ldb,
         a.scale_log2, static_cast<const TQ*>(a.refresh_k), a.refresh_cis);
     if (e != hipSuccess) return e;
   }
   if (a.logits_only) return hipSuccess;
-  return launch_kernel(kKindBlockScores, select_kernel<G, true>, dim3(a.batch, a.kv_heads),
+  return launch_kernel(kKindBlockScores, select_kernel<G, true>, dim3(a.batch * a.kv_heads),
                        dim3(kSelThreads), s, static_cast<const float*>(a.ws.logits),
                        static_cast<const float2*>(a.ws.part), static_cast<const float*>(cisb),
                        a.cis_weight, static_cast<const int*>(nullptr), a.cu_k, a.cu_c, a.batch,
@@ -483,7 +491,7 @@ hipError_t launch_select_topk(const float* block_scores, int* indices, const int
     if (per <= 32) return launch_select_wave<32>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
     return launch_select_wave<64>(block_scores, indices, cu_q, cu_k, batch, units, kv_heads, nb_max, topk, n_init, n_local, s);
   }
-  return launch_kernel(kKindBlockScores, select_kernel<1, false>, dim3(rows_total, kv_heads),
+  return launch_kernel(kKindBlockScores, select_kernel<1, false>, dim3(rows_total * kv_heads),
                        dim3(kSelThreads), s, static_cast<const float*>(nullptr),
                        static_cast<const float2*>(nullptr), static_cast<const float*>(nullptr),
                        0.f, cu_q, cu_k, static_cast<const int*>(nullptr), batch,

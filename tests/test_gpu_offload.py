@@ -153,3 +153,32 @@ def test_offload_pool_exactly_topk_and_degenerate_rows():
         want = [m.step(idx_np[u]) for u, m in enumerate(models)]
         assert keep["fetched"].cpu().numpy().tolist() == want
         assert keep["block_of"].cpu().numpy().tolist() == [m.block_of for m in models]
+
+
+def test_offload_ragged_grid():
+    """Three sequences, one KV head, top-20: the pool attention runs 60
+    workgroups, not a multiple of the XCD count, in XCD-grouped order."""
+    lengths = [9000, 700, 5000]
+    d = _inputs(lengths, SEED + 3, H=8, H_kv=1)
+    B, H, H_kv, topk, slots = len(lengths), d["H"], d["H_kv"], 20, 40
+    nb_cap = -(-max(lengths) // 64)
+    st, keep = nsa.offload_state(B, H_kv, slots, nb_cap, DEV)
+    models = [PoolModel(slots, nb_cap) for _ in range(B * H_kv)]
+    log("offload ragged grid")
+    for step in range(2):
+        q = gen.normal(SEED + 3, 30 + step, (B, H, 128), DEV, BF16)
+        out_r = torch.full((B, H, 128), float("nan"), dtype=BF16, device=DEV)
+        out_o = torch.full_like(out_r, float("nan"))
+        idx_r = torch.full((B, H_kv, topk), -7, dtype=torch.int32, device=DEV)
+        idx_o = torch.full_like(idx_r, -7)
+        nsa.nsa_decode_step(_params(d, q, out_r, idx_r, d["k"], d["v"], topk, 1, 4, False, 0),
+                            device=DEV)
+        nsa.nsa_decode_step_offload(_params(d, q, out_o, idx_o, d["k_host"], d["v_host"], topk, 1,
+                                            4, False, 0), st, device=DEV)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_o, idx_r)
+        assert torch.equal(out_o, out_r)
+        assert not torch.isnan(out_o.float()).any()
+        idx_np = idx_o.cpu().numpy().reshape(B * H_kv, topk)
+        want = [m.step(idx_np[u]) for u, m in enumerate(models)]
+        assert keep["fetched"].cpu().numpy().tolist() == want

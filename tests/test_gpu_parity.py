@@ -482,6 +482,18 @@ def test_decode_step_large_batch():
     _check_decode("large_batch", d, out, bs, idx, 64, 1, 16, True, False, atol=2e-2)
 
 
+def test_decode_step_grids_not_multiple_of_eight():
+    """Three sequences, one KV head, top-20: 60 select-and-attend workgroups (one
+    block each) and 27 logits workgroups, so the XCD-grouped order of both grids
+    has a ragged last round; a workgroup the mapping skipped or repeated would
+    leave a partial state or a chunk of window logits unwritten."""
+    lengths = [9000, 700, 5000]
+    d = _decode_inputs(lengths, SEED + 19, H=8, H_kv=1)
+    log(f"decode step ragged grids {lengths}")
+    out, bs, idx = _run_decode_step(d, 20, 1, 4, True, False)
+    _check_decode("ragged_grids", d, out, bs, idx, 20, 1, 4, True, False, atol=2e-2)
+
+
 @pytest.mark.parametrize("H,H_kv", [(32, 2), (8, 2), (4, 4)])
 def test_decode_step_group_sizes(H, H_kv):
     """GQA groups of 16, 4 and 1 query heads through the single-kernel decode path."""

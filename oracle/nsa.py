@@ -44,6 +44,12 @@ R7 token-level causality inside the diagonal block (keys j <= t).
 R8 CIS mode: o = sum p*cis*v / sum p*cis (the ones-value pass carries the same
    CIS scaling).
 R9 sliding window: keys max(0, t-W+1) .. t (W keys including the query's own).
+R16 backward of the selected attention (no CIS): the exact gradient of the
+   forward above with respect to q, k and v for a given upstream gradient of the
+   output; the pages describe the method as trainable end to end (DeepSeek NSA
+   with Triton, introduction and section 2.3, the kernels wrapped as a
+   trainable module) but print no backward, so the gradient is the plain one.
+   Keys reached through no row get zero gradient.
 R5b two-stage selection (optional): the n_cand best free blocks by the
    compressed-attention block score are the candidates; the k - |forced| best
    candidates by the pooled-CIS block score are chosen (ties to the lower index
@@ -271,6 +277,60 @@ def selected_attention_row(q, k_seq, v_seq, idx, t: int, block: int, scale: floa
         w = None if cis_seq is None else np.asarray(cis_seq, dtype=np.float64)[J, g]
         out[h] = attend(q[h], np.asarray(k_seq)[J, g], np.asarray(v_seq)[J, g], scale, w)
     return out
+
+
+def selected_attention_row_grad(q, k_seq, v_seq, idx, t: int, block: int, scale: float,
+                                d_out, dk, dv) -> np.ndarray:
+    """Gradient of selected_attention_row (no CIS, R16) for query position t.
+
+    d_out: [H, D] upstream gradient of the row's output.  Adds the row's
+    contributions to dk, dv ([L, H_kv, D] float64, in place) and returns dq
+    [H, D].  Per head, over the selected keys J: p = softmax(scale * K_J q),
+    o = p V_J; dV_J += p d_out^T; dp = V_J d_out; ds = p * (dp - d_out . o);
+    dq = scale * ds K_J; dK_J += scale * ds q^T."""
+    q = np.asarray(q, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    k_seq = np.asarray(k_seq, dtype=np.float64)
+    v_seq = np.asarray(v_seq, dtype=np.float64)
+    H, D = q.shape
+    L, H_kv = k_seq.shape[0], k_seq.shape[1]
+    G = H // H_kv
+    dq = np.zeros((H, D))
+    for h in range(H):
+        g = h // G
+        J = selected_keys(idx[g], t, L, block)
+        if not J:
+            continue
+        K, V = k_seq[J, g], v_seq[J, g]
+        p = softmax(K @ q[h] * scale)
+        o = p @ V
+        ds = p * (V @ d_out[h] - d_out[h] @ o)
+        dq[h] = scale * (ds @ K)
+        dk[J, g] += scale * np.outer(ds, q[h])
+        dv[J, g] += np.outer(p, d_out[h])
+    return dq
+
+
+def selected_attention_bwd(q, k, v, idx, d_out, cu_q, cu_k, block: int, scale: float):
+    """Gradients of the selected attention over packed prefill rows (R16).
+
+    q, d_out: [rows, H, D]; k, v: [N_k, H_kv, D]; idx: [rows, H_kv, k];
+    cu_q, cu_k: sequence offsets.  Row r of sequence b sits at position
+    t = (r - cu_q[b]) + (L_b - Lq_b).  Returns dq [rows, H, D], dk and dv
+    [N_k, H_kv, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        shift = (k1 - k0) - (q1 - q0)
+        for r in range(q0, q1):
+            dq[r] = selected_attention_row_grad(q[r], k[k0:k1], v[k0:k1], idx[r], r - q0 + shift,
+                                                block, scale, d_out[r], dk[k0:k1], dv[k0:k1])
+    return dq, dk, dv
 
 
 def blockmask_attention_row(q, k_seq, v_seq, mask_rows, t: int, block: int, scale: float,

@@ -20,7 +20,7 @@ import torch
 
 from . import _lsr, normal, random_keys, sigmoid_normal, u64_at, uniform_ints
 
-S_Q, S_K, S_V, S_CIS, S_GATE, S_LEN, S_IDX, S_MASK = 1, 2, 3, 4, 5, 6, 7, 8
+S_Q, S_K, S_V, S_CIS, S_GATE, S_LEN, S_IDX, S_MASK, S_DOUT = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 @dataclass
@@ -137,6 +137,11 @@ def decode_query(w: Workload, device="cpu", layer: int = 0) -> torch.Tensor:
 def prefill_query(w: Workload, device="cpu") -> torch.Tensor:
     """[N, H, D] packed queries, one per token."""
     return normal(w.seed, S_Q, (w.total_tokens, w.heads, w.head_dim), device, w.dtype)
+
+
+def prefill_out_grad(w: Workload, device="cpu") -> torch.Tensor:
+    """[N, H, D] upstream gradient of the attention output, N(0,1), one per token."""
+    return normal(w.seed, S_DOUT, (w.total_tokens, w.heads, w.head_dim), device, w.dtype)
 
 
 def keys_values(w: Workload, device="cpu", layer: int = 0):

@@ -106,7 +106,9 @@ int32_t nsa_version(void);
  * 5 compressed-attention normaliser pass (prefill), 6 compressed-attention
  * output and block-score pass (prefill), 7 sliding-window attention (prefill,
  * with the gated sum in nsa_prefill_step), 8 block copies from host memory
- * (nsa_decode_step_offload), 9 block-mask attention.  The events are owned by the caller
+ * (nsa_decode_step_offload), 9 block-mask attention, 10 selected-attention
+ * backward dq, 11 its dk and dv, 12 its delta and per-block row lists (the
+ * first of those four launches).  The events are owned by the caller
  * and must have timing enabled; a launch made during stream capture must not
  * be armed.
  */
@@ -120,7 +122,10 @@ typedef enum nsa_kernel_kind {
   NSA_KERNEL_COMPRESSED_ATTN = 6,
   NSA_KERNEL_WINDOW_ATTN = 7,
   NSA_KERNEL_FETCH = 8,
-  NSA_KERNEL_BLOCKMASK_ATTN = 9
+  NSA_KERNEL_BLOCKMASK_ATTN = 9,
+  NSA_KERNEL_SELECTED_BWD_DQ = 10,
+  NSA_KERNEL_SELECTED_BWD_DKDV = 11,
+  NSA_KERNEL_SELECTED_BWD_LISTS = 12
 } nsa_kernel_kind;
 nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
 
@@ -231,6 +236,44 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
                                  int32_t max_seqlen_k, int32_t heads, int32_t kv_heads,
                                  int32_t head_dim, int32_t block_size, float softmax_scale,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nsa_selected_attn_bwd -- gradient of nsa_selected_attn_fwd (plain softmax,
+ * no CIS) over prefill rows.
+ * [DeepSeek NSA with Triton, introduction and section 2.3: the method is
+ *  trained end to end, its kernels wrapped as a trainable module; the pages
+ *  print no backward, so this is the exact gradient of the forward above.]
+ *   q, out, d_out [rows, heads, 128] bf16: the forward's queries, its output
+ *                 and the upstream gradient of that output
+ *   k, v          [N_k, kv_heads, 128] bf16
+ *   lse           [rows, heads] float32: the forward's natural-log normaliser
+ *   indices       [rows, kv_heads, k_sel] int32, the forward's (ids of one row
+ *                 unique; -1 and ids with 64*id > t are skipped)
+ *   cu_seqlens_q, cu_seqlens_k (required): row r of sequence b sits at
+ *                 t = (r - cu_q[b]) + (L_b - Lq_b); every L_b <= max_seqlen_k.
+ *   dq            [rows, heads, 128] float32, written
+ *   dk, dv        [N_k, kv_heads, 128] float32, written in full (0 for keys no
+ *                 row attends to)
+ *   Per head over the row's keys J: dV_J += p dO^T; ds = p*(V_J dO - dO.O);
+ *   dq = scale ds K_J; dK_J += scale ds q^T.  dk and dv are gathered per
+ *   (sequence, KV head, block) over the rows that list the block (no atomics on
+ *   the gradients); their summation order follows the row lists, which atomics
+ *   build, so it may change between calls (fp32 rounding only).
+ *   workspace: nsa_selected_attn_bwd_workspace_size(...) bytes, device memory.
+ *   Returns NSA_ERR_UNSUPPORTED for non-bf16 inputs or k_sel > 64.
+ */
+size_t nsa_selected_attn_bwd_workspace_size(int32_t batch, int32_t rows_total,
+                                            int32_t max_seqlen_k, int32_t heads,
+                                            int32_t kv_heads, int32_t k_sel);
+nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                 const void* d_out, const float* lse, nsa_dtype dtype,
+                                 const int32_t* indices, int32_t k_sel,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                                 int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                 int32_t block_size, float softmax_scale, float* dq, float* dk,
+                                 float* dv, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * nsa_decode_step -- one decode step of the whole path for a packed batch: the

@@ -92,6 +92,11 @@ _SIGS = {
     "nsa_selected_attn_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i32, c_vp,
                                              c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                              c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
+    "nsa_selected_attn_bwd_workspace_size": (c_sz, [c_i32] * 6),
+    "nsa_selected_attn_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int,
+                                             c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                             c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp,
+                                             c_sz, c_vp]),
     "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
     "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
     "nsa_offload_pool_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, ctypes.c_int]),
@@ -267,6 +272,32 @@ def nsa_selected_attn_fwd(q, k, v, indices, cu_seqlens_k, max_seqlen_k, out, cis
     return out
 
 
+def selected_attn_bwd_workspace_size(batch, rows, max_seqlen_k, heads, kv_heads, k_sel):
+    return lib().nsa_selected_attn_bwd_workspace_size(int(batch), int(rows), int(max_seqlen_k),
+                                                      int(heads), int(kv_heads), int(k_sel))
+
+
+def nsa_selected_attn_bwd(q, k, v, out, d_out, lse, indices, cu_seqlens_q, cu_seqlens_k,
+                          max_seqlen_k, dq, dk, dv, softmax_scale=0.0, block_size=64,
+                          workspace=None, stream=None):
+    """Gradient of nsa_selected_attn_fwd (no CIS) over prefill rows: q, out, d_out
+    [rows, H, D] bf16, k, v [N_k, H_kv, D] bf16, lse [rows, H] float32 from the
+    forward -> dq [rows, H, D], dk, dv [N_k, H_kv, D] float32."""
+    rows, H, D = q.shape
+    H_kv = k.shape[1]
+    k_sel = indices.shape[2]
+    batch = cu_seqlens_k.numel() - 1
+    need = selected_attn_bwd_workspace_size(batch, rows, max_seqlen_k, H, H_kv, k_sel)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check(lib().nsa_selected_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(d_out),
+                                       _ptr(lse), _dt(q), _ptr(indices), k_sel,
+                                       _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, rows,
+                                       int(max_seqlen_k), H, H_kv, D, block_size,
+                                       float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv
+
+
 def decode_params(q, k, v, k_c, cu_seqlens_k, cu_seqlens_c, max_seqlen_k, out, topk=64, n_init=1,
                   n_local=16, cis=None, cis_pooled=None, cis_weight=1.0, cis_values=False,
                   append_window=False, block_scores=None, indices=None, softmax_scale=0.0,
@@ -343,6 +374,7 @@ def nsa_decode_step_offload(params: DecodeParams, state: OffloadState, workspace
 KERNEL_POOL, KERNEL_LOGITS, KERNEL_BLOCK_SCORES, KERNEL_SELECTED_ATTN, KERNEL_COMBINE = 0, 1, 2, 3, 4
 KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN, KERNEL_FETCH = 5, 6, 7, 8
 KERNEL_BLOCKMASK_ATTN = 9
+KERNEL_SELECTED_BWD_DQ, KERNEL_SELECTED_BWD_DKDV, KERNEL_SELECTED_BWD_LISTS = 10, 11, 12
 
 
 def blockmask_attn_workspace_size(batch, max_seqlen, heads):

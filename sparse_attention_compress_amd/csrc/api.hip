@@ -237,6 +237,72 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
                     fn);
 }
 
+size_t nsa_selected_attn_bwd_workspace_size(int32_t batch, int32_t rows_total,
+                                            int32_t max_seqlen_k, int32_t heads,
+                                            int32_t kv_heads, int32_t k_sel) {
+  if (batch <= 0 || rows_total <= 0 || max_seqlen_k <= 0 || heads <= 0 || kv_heads <= 0 ||
+      k_sel <= 0)
+    return 0;
+  const int nb_max = (max_seqlen_k + nsa::kBlock - 1) / nsa::kBlock;
+  return nsa::selected_bwd_ws_bytes(rows_total, heads, kv_heads, k_sel, batch, nb_max);
+}
+
+nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                 const void* d_out, const float* lse, nsa_dtype dtype,
+                                 const int32_t* indices, int32_t k_sel,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                                 int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                 int32_t block_size, float softmax_scale, float* dq, float* dk,
+                                 float* dv, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  const char* fn = "nsa_selected_attn_bwd";
+  NSA_REQUIRE(batch >= 0 && rows_total >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(dtype == NSA_BF16, NSA_ERR_UNSUPPORTED, "%s: bfloat16 inputs only", fn);
+  NSA_REQUIRE(group_ok(heads, kv_heads), NSA_ERR_UNSUPPORTED, "%s: heads %d / kv_heads %d unsupported", fn, heads, kv_heads);
+  NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
+  NSA_REQUIRE(block_size == nsa::kBlock, NSA_ERR_UNSUPPORTED, "%s: block_size %d unsupported (64 only)", fn, block_size);
+  NSA_REQUIRE(k_sel >= 1 && k_sel <= kMaxPrefillSel, NSA_ERR_UNSUPPORTED, "%s: k_sel %d outside 1..%d", fn, k_sel, kMaxPrefillSel);
+  NSA_REQUIRE(cu_seqlens_q != nullptr, NSA_ERR_INVALID_ARG, "%s: cu_seqlens_q is required (prefill rows)", fn);
+  if (rows_total == 0 || batch == 0) return ok();
+  NSA_REQUIRE(max_seqlen_k >= 1, NSA_ERR_INVALID_ARG, "%s: rows without keys (max_seqlen_k 0)", fn);
+  const int nb_max = (max_seqlen_k + nsa::kBlock - 1) / nsa::kBlock;
+  NSA_REQUIRE(size_t(batch) * kv_heads * nb_max <= size_t(INT32_MAX) &&
+                  size_t(rows_total) * kv_heads * k_sel <= size_t(INT32_MAX) &&
+                  size_t(rows_total) * kv_heads <= size_t(UINT32_MAX),
+              NSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  NSA_REQUIRE(q && k && v && out && d_out && lse && indices && cu_seqlens_k && dq && dk && dv,
+              NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(d_out),
+              NSA_ERR_INVALID_ARG, "%s: q, k, v, out, d_out must be 16-byte aligned", fn);
+  const size_t need = nsa_selected_attn_bwd_workspace_size(batch, rows_total, max_seqlen_k, heads, kv_heads, k_sel);
+  NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt(float(head_dim));
+  nsa::SelectedBwdArgs a{};
+  a.q = static_cast<const nsa::bf16_t*>(q);
+  a.k = static_cast<const nsa::bf16_t*>(k);
+  a.v = static_cast<const nsa::bf16_t*>(v);
+  a.out = static_cast<const nsa::bf16_t*>(out);
+  a.dout = static_cast<const nsa::bf16_t*>(d_out);
+  a.lse = lse;
+  a.indices = indices;
+  a.k_sel = k_sel;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.rows_total = rows_total;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.nb_max = nb_max;
+  a.scale = scale;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  nsa::selected_bwd_ws_carve(workspace, a);
+  return hip_status(nsa::launch_selected_bwd(a, stream), fn);
+}
+
 // ------------------------------------------------------------------ decode step
 
 namespace {

@@ -1,0 +1,392 @@
+// Backward of the selected attention (plain softmax, no CIS), prefill rows.
+//
+// What is computed: the gradient of the selected attention with respect to q,
+// k and v for an upstream gradient dO of its output (the method is trained end
+// to end: DeepSeek NSA with Triton, introduction and section 2.3, where the
+// kernels are wrapped as a trainable module; the pages print no backward, so
+// this is the plain gradient).  Per (row, query head h of KV group g), over the
+// row's selected keys J, with p = softmax(scale K_J q) from the forward's
+// log-normaliser:
+//   dV_J += p dO^T,  ds = p * (V_J dO - delta),  delta = dO . O,
+//   dq = scale ds K_J,  dK_J += scale ds q^T.
+// dq is a gather (each row reads its own blocks).  dK and dV are sums over the
+// rows that list a block; instead of scattering them with atomics, the row
+// lists are transposed into one list of rows per (sequence, KV head, block)
+// (count, scan, fill), and each block gathers its rows, so every gradient
+// element is written once by one workgroup.
+//
+// Launches: prep (delta, list counts cleared), count, scan, fill, dq, dk/dv.
+// Order within a block's row list depends on atomics, so dK and dV are summed
+// in an order that can change from call to call (fp32 rounding only).
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace nsa {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ void bwd_row_position(int row, const int* __restrict__ cu_q,
+                                                 const int* __restrict__ cu_k, int batch, int& b,
+                                                 int& t) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  b = lo;
+  t = (row - cu_q[b]) + ((cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]));
+}
+
+// delta[row, h] = dO . O (one wave per (row, head), two dims a lane); the
+// per-block row counts are cleared by the same launch.
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
+    const bf16_t* __restrict__ out, const bf16_t* __restrict__ dout, size_t n_rh,
+    float* __restrict__ delta, int* __restrict__ cnt, int n_slots) {
+  const int lane = threadIdx.x & 63;
+  const size_t rh = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  for (size_t i = size_t(blockIdx.x) * kBwdThreads + threadIdx.x; i < size_t(n_slots);
+       i += size_t(gridDim.x) * kBwdThreads)
+    cnt[i] = 0;
+  if (rh >= n_rh) return;
+  const uint32_t o = *reinterpret_cast<const uint32_t*>(out + rh * kHeadDim + 2 * lane);
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(dout + rh * kHeadDim + 2 * lane);
+  float s = bf16lo(o) * bf16lo(d) + bf16hi(o) * bf16hi(d);
+  s = wave_reduce(s, OpSum());
+  if (lane == 0) delta[rh] = s;
+}
+
+// One thread per (row, kv head, place): whether the place lists a block the
+// row attends to, and its (sequence, kv head, block) slot.
+__device__ __forceinline__ int bwd_slot_of(size_t i, const int* __restrict__ indices, int k_sel,
+                                           int kv_heads, const int* __restrict__ cu_q,
+                                           const int* __restrict__ cu_k, int batch, int nb_max,
+                                           int& row) {
+  const size_t unit = i / size_t(k_sel);
+  row = int(unit / size_t(kv_heads));
+  const int g = int(unit % size_t(kv_heads));
+  const int id = indices[i];
+  if (id < 0 || id >= nb_max) return -1;
+  int b, t;
+  bwd_row_position(row, cu_q, cu_k, batch, b, t);
+  const int len = cu_k[b + 1] - cu_k[b];
+  if (t < 0 || t >= len || kBlock * id > t) return -1;
+  return (b * kv_heads + g) * nb_max + id;
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_count_kernel(
+    const int* __restrict__ indices, size_t n, int k_sel, int kv_heads,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int nb_max,
+    int* __restrict__ cnt) {
+  const size_t i = size_t(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (i >= n) return;
+  int row;
+  const int slot = bwd_slot_of(i, indices, k_sel, kv_heads, cu_q, cu_k, batch, nb_max, row);
+  if (slot >= 0) atomicAdd(cnt + slot, 1);
+}
+
+// Exclusive scan of the counts into the list offsets (and the fill cursors),
+// one workgroup walking the slots 1024 at a time.
+__global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const int* __restrict__ cnt,
+                                                                int n_slots, int* __restrict__ off,
+                                                                int* __restrict__ cursor) {
+  __shared__ int wsum[kScanThreads / kWave];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < n_slots; base += kScanThreads) {
+    const int i = base + tid;
+    const int c = i < n_slots ? cnt[i] : 0;
+    const int incl = wave_inclusive_scan(c);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = carry_s;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int excl = before + incl - c;
+    if (i < n_slots) {
+      off[i] = excl;
+      cursor[i] = excl;
+    }
+    __syncthreads();
+    if (tid == kScanThreads - 1) carry_s = excl + c;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_fill_kernel(
+    const int* __restrict__ indices, size_t n, int k_sel, int kv_heads,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int nb_max,
+    int* __restrict__ cursor, int* __restrict__ list) {
+  const size_t i = size_t(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (i >= n) return;
+  int row;
+  const int slot = bwd_slot_of(i, indices, k_sel, kv_heads, cu_q, cu_k, batch, nb_max, row);
+  if (slot >= 0) list[atomicAdd(cursor + slot, 1)] = row;
+}
+
+// Thread (j, part) of a 64-token block: token j, dims 32*part .. +31.
+struct KeySlice {
+  float k[32];
+  float v[32];
+};
+
+__device__ __forceinline__ void load_key_slice(const bf16_t* __restrict__ k,
+                                               const bf16_t* __restrict__ v, size_t off,
+                                               bool ok, KeySlice& s) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (ok) {
+      load8f(k + off + 8 * i, &s.k[8 * i]);
+      load8f(v + off + 8 * i, &s.v[8 * i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s.k[8 * i + e] = 0.f;
+        s.v[8 * i + e] = 0.f;
+      }
+    }
+  }
+}
+
+// The G heads' q and dO rows of one query row in LDS (fp32), with the
+// log2-domain normaliser and delta.
+template <int G>
+struct RowLds {
+  float q[G][kHeadDim];
+  float d[G][kHeadDim];
+  float lse2[G];
+  float delta[G];
+};
+
+template <int G>
+__device__ __forceinline__ void stage_row(RowLds<G>& R, const bf16_t* __restrict__ q,
+                                          const bf16_t* __restrict__ dout,
+                                          const float* __restrict__ lse,
+                                          const float* __restrict__ delta, size_t head0) {
+  for (int c = threadIdx.x; c < G * 16; c += kBwdThreads) {
+    const int h = c >> 4, d0 = (c & 15) * 8;
+    load8f(q + (head0 + h) * kHeadDim + d0, &R.q[h][d0]);
+    load8f(dout + (head0 + h) * kHeadDim + d0, &R.d[h][d0]);
+  }
+  if (threadIdx.x < G) {
+    R.lse2[threadIdx.x] = lse[head0 + threadIdx.x] * kLog2e;
+    R.delta[threadIdx.x] = delta[head0 + threadIdx.x];
+  }
+}
+
+// p and ds of head h for this thread's token (all four lanes of the token get
+// the sums over the 128 dims).
+template <int G>
+__device__ __forceinline__ void probs(const RowLds<G>& R, const KeySlice& s, int h, int part,
+                                      bool valid, float scale_log2, float& p, float& ds) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    a = fmaf(R.q[h][32 * part + e], s.k[e], a);
+    b = fmaf(R.d[h][32 * part + e], s.v[e], b);
+  }
+  a = quad_reduce(a, OpSum());
+  b = quad_reduce(b, OpSum());
+  p = valid ? fast_exp2(a * scale_log2 - R.lse2[h]) : 0.f;
+  ds = p * (b - R.delta[h]);
+}
+
+// dq of one (row, kv head): the row's selected blocks one at a time.
+template <int G>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int* __restrict__ indices, int k_sel,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int heads,
+    int kv_heads, float scale_log2, float scale, float* __restrict__ dq) {
+  constexpr int kOut = (G * kHeadDim + kBwdThreads - 1) / kBwdThreads;
+  __shared__ RowLds<G> R;
+  __shared__ float k_s[kBlock][kHeadDim + 1];
+  __shared__ float ds_s[G][kBlock];
+  const int tid = threadIdx.x, j = tid >> 2, part = tid & 3;
+  const int row = int(blockIdx.x / unsigned(kv_heads)), g = int(blockIdx.x % unsigned(kv_heads));
+  int b, t;
+  bwd_row_position(row, cu_q, cu_k, batch, b, t);
+  const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
+  const size_t head0 = size_t(row) * heads + size_t(g) * G;
+  stage_row<G>(R, q, dout, lse, delta, head0);
+  float acc[kOut];
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) acc[i] = 0.f;
+  __syncthreads();
+  const int* irow = indices + (size_t(row) * kv_heads + g) * k_sel;
+  for (int pl = 0; pl < k_sel; ++pl) {
+    const int id = irow[pl];
+    if (t < 0 || t >= len || id < 0 || id > t / kBlock) continue;  // uniform
+    const int tok = kBlock * id + j;
+    const bool valid = tok <= t;
+    KeySlice s;
+    load_key_slice(k, v, (size_t(kstart + min(tok, t)) * kv_heads + g) * kHeadDim + 32 * part,
+                   valid, s);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) k_s[j][32 * part + e] = s.k[e];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float p, ds;
+      probs<G>(R, s, h, part, valid, scale_log2, p, ds);
+      if (part == 0) ds_s[h][j] = ds;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int o = tid + kBwdThreads * i;
+      if (o < G * kHeadDim) {
+        const int h = o / kHeadDim, d = o % kHeadDim;
+        float a = acc[i];
+#pragma unroll 8
+        for (int jj = 0; jj < kBlock; ++jj) a = fmaf(ds_s[h][jj], k_s[jj][d], a);
+        acc[i] = a;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int o = tid + kBwdThreads * i;
+    if (o < G * kHeadDim) dq[head0 * kHeadDim + o] = scale * acc[i];
+  }
+}
+
+// dK and dV of one (sequence, kv head, block): the rows that list it, one at a
+// time.  Every token of the block is written (zeros when no row lists it).
+template <int G>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int* __restrict__ cnt, const int* __restrict__ off,
+    const int* __restrict__ list, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    int batch, int heads, int kv_heads, int nb_max, float scale_log2, float scale,
+    float* __restrict__ dk, float* __restrict__ dv) {
+  __shared__ RowLds<G> R;
+  const int tid = threadIdx.x, j = tid >> 2, part = tid & 3;
+  const int slot = blockIdx.x;
+  const int id = slot % nb_max;
+  const int g = (slot / nb_max) % kv_heads;
+  const int b = slot / (nb_max * kv_heads);
+  const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
+  if (kBlock * id >= len) return;  // uniform: no token of this sequence here
+  const int tok = kBlock * id + j;
+  const bool tok_ok = tok < len;
+  const size_t kv_off = (size_t(kstart + min(tok, len - 1)) * kv_heads + g) * kHeadDim + 32 * part;
+  KeySlice s;
+  load_key_slice(k, v, kv_off, tok_ok, s);
+  float ak[32], av[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    ak[e] = 0.f;
+    av[e] = 0.f;
+  }
+  const int n = cnt[slot], first = off[slot];
+  for (int e0 = 0; e0 < n; ++e0) {
+    const int row = list[first + e0];
+    int bb, t;
+    bwd_row_position(row, cu_q, cu_k, batch, bb, t);
+    __syncthreads();  // the previous row's LDS is no longer read
+    stage_row<G>(R, q, dout, lse, delta, size_t(row) * heads + size_t(g) * G);
+    __syncthreads();
+    const bool valid = tok_ok && tok <= t;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float p, ds;
+      probs<G>(R, s, h, part, valid, scale_log2, p, ds);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        av[e] = fmaf(p, R.d[h][32 * part + e], av[e]);
+        ak[e] = fmaf(ds, R.q[h][32 * part + e], ak[e]);
+      }
+    }
+  }
+  if (!tok_ok) return;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    dk[kv_off + e] = scale * ak[e];
+    dv[kv_off + e] = av[e];
+  }
+}
+
+template <int G>
+hipError_t launch_bwd_g(const SelectedBwdArgs& a, hipStream_t s) {
+  const size_t n_rh = size_t(a.rows_total) * a.heads;
+  const int n_slots = a.batch * a.kv_heads * a.nb_max;
+  const size_t n_place = size_t(a.rows_total) * a.kv_heads * a.k_sel;
+  const unsigned prep_grid = unsigned(std::max<size_t>((n_rh + 3) / 4, 1));
+  hipError_t e = launch_kernel(kKindBwdLists, bwd_prep_kernel, dim3(prep_grid), dim3(kBwdThreads), s,
+                               a.out, a.dout, n_rh, a.delta, a.cnt, n_slots);
+  if (e != hipSuccess) return e;
+  const unsigned place_grid = unsigned((n_place + kBwdThreads - 1) / kBwdThreads);
+  if (place_grid > 0) {
+    e = launch_kernel(kKindBwdLists, bwd_count_kernel, dim3(place_grid), dim3(kBwdThreads), s,
+                      a.indices, n_place, a.k_sel, a.kv_heads, a.cu_q, a.cu_k, a.batch, a.nb_max,
+                      a.cnt);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_kernel(kKindBwdLists, bwd_scan_kernel, dim3(1), dim3(kScanThreads), s,
+                    static_cast<const int*>(a.cnt), n_slots, a.off, a.cursor);
+  if (e != hipSuccess) return e;
+  if (place_grid > 0) {
+    e = launch_kernel(kKindBwdLists, bwd_fill_kernel, dim3(place_grid), dim3(kBwdThreads), s,
+                      a.indices, n_place, a.k_sel, a.kv_heads, a.cu_q, a.cu_k, a.batch, a.nb_max,
+                      a.cursor, a.list);
+    if (e != hipSuccess) return e;
+  }
+  const float scale_log2 = a.scale * kLog2eHost;
+  e = launch_kernel(kKindBwdQ, bwd_dq_kernel<G>, dim3(unsigned(a.rows_total) * a.kv_heads),
+                    dim3(kBwdThreads), s, a.q, a.k, a.v, a.dout, a.lse,
+                    static_cast<const float*>(a.delta), a.indices, a.k_sel, a.cu_q, a.cu_k,
+                    a.batch, a.heads, a.kv_heads, scale_log2, a.scale, a.dq);
+  if (e != hipSuccess) return e;
+  return launch_kernel(kKindBwdKV, bwd_dkdv_kernel<G>, dim3(unsigned(n_slots)),
+                       dim3(kBwdThreads), s, a.q, a.k, a.v, a.dout, a.lse,
+                       static_cast<const float*>(a.delta), static_cast<const int*>(a.cnt),
+                       static_cast<const int*>(a.off), static_cast<const int*>(a.list), a.cu_q,
+                       a.cu_k, a.batch, a.heads, a.kv_heads, a.nb_max, scale_log2, a.scale,
+                       a.dk, a.dv);
+}
+
+}  // namespace
+
+size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel, int batch,
+                             int nb_max) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t n_slots = size_t(batch) * kv_heads * nb_max;
+  return up(size_t(rows_total) * heads * sizeof(float)) + 3 * up(n_slots * sizeof(int)) +
+         up(size_t(rows_total) * kv_heads * k_sel * sizeof(int));
+}
+
+void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t n_slots = size_t(a.batch) * a.kv_heads * a.nb_max;
+  char* p = static_cast<char*>(base);
+  a.delta = reinterpret_cast<float*>(p);
+  p += up(size_t(a.rows_total) * a.heads * sizeof(float));
+  a.cnt = reinterpret_cast<int*>(p);
+  p += up(n_slots * sizeof(int));
+  a.off = reinterpret_cast<int*>(p);
+  p += up(n_slots * sizeof(int));
+  a.cursor = reinterpret_cast<int*>(p);
+  p += up(n_slots * sizeof(int));
+  a.list = reinterpret_cast<int*>(p);
+}
+
+hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s) {
+  switch (a.heads / a.kv_heads) {
+    case 1: return launch_bwd_g<1>(a, s);
+    case 2: return launch_bwd_g<2>(a, s);
+    case 4: return launch_bwd_g<4>(a, s);
+    case 8: return launch_bwd_g<8>(a, s);
+    case 16: return launch_bwd_g<16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace nsa

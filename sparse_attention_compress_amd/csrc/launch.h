@@ -49,7 +49,10 @@ enum KernelKind {
   kKindWindow = 7,
   kKindFetch = 8,
   kKindMask = 9,
-  kKindCount = 10
+  kKindBwdQ = 10,     // selected-attention backward: dq
+  kKindBwdKV = 11,    // selected-attention backward: dk and dv
+  kKindBwdLists = 12, // selected-attention backward: delta and the per-block row lists
+  kKindCount = 13
 };
 
 // One armed (start, stop) event pair per kernel kind, per host thread.
@@ -211,6 +214,35 @@ hipError_t launch_blockmask_attn(const bf16_t* q, const bf16_t* k, const bf16_t*
                                  const unsigned char* mask, int causal, bf16_t* out,
                                  const int* cu, int batch, int max_seqlen, int heads,
                                  float scale_log2, bf16_t* vt, hipStream_t s);
+
+// Backward of the selected attention (bf16 inputs, fp32 gradients, prefill rows).
+struct SelectedBwdArgs {
+  const bf16_t* q;     // [rows, heads, 128]
+  const bf16_t* k;     // [N_k, kv_heads, 128]
+  const bf16_t* v;
+  const bf16_t* out;   // [rows, heads, 128] forward output
+  const bf16_t* dout;  // [rows, heads, 128] its upstream gradient
+  const float* lse;    // [rows, heads] forward natural-log normaliser
+  const int* indices;  // [rows, kv_heads, k_sel]
+  int k_sel;
+  const int* cu_q;
+  const int* cu_k;
+  int batch, rows_total, heads, kv_heads, nb_max;
+  float scale;         // softmax scale (natural domain)
+  float* dq;           // [rows, heads, 128]
+  float* dk;           // [N_k, kv_heads, 128]
+  float* dv;
+  // workspace (selected_bwd_ws_carve)
+  float* delta;        // [rows, heads]
+  int* cnt;            // [batch, kv_heads, nb_max] rows listing each block
+  int* off;            // list offsets
+  int* cursor;         // fill cursors
+  int* list;           // [rows * kv_heads * k_sel] rows, grouped by block
+};
+size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel, int batch,
+                             int nb_max);
+void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a);
+hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s);
 
 // Values transposed per (sequence, KV head, dim) for the prefill branches.
 int transposed_ld(int max_len);

@@ -67,12 +67,15 @@ def parse():
                     help="prefill-blockmask: tokens per sequence (the pages' table: 1024, 4096, 16384)")
     ap.add_argument("--causal", action="store_true", help="prefill-blockmask: lower triangle only")
     ap.add_argument("--workload", choices=["decode", "decode-long", "decode-offload",
-                                           "prefill-selected", "prefill-nsa", "prefill-blockmask"],
+                                           "prefill-selected", "prefill-nsa", "prefill-blockmask",
+                                           "prefill-selected-bwd"],
                     default="decode",
                     help="decode: the headline NOSA-1B-shaped decode (default); decode-long: "
                          "CIS-weighted decode of 4 x 131072 tokens; prefill-selected: "
                          "selected-block attention prefill with given indices (batch 8 x 16384); "
-                         "prefill-nsa: the three-branch prefill (65536 tokens, 64 heads)")
+                         "prefill-nsa: the three-branch prefill (65536 tokens, 64 heads); "
+                         "prefill-selected-bwd: the gradient of the selected-block attention "
+                         "for the prefill-selected batch")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with three streaming kernels (fp32 negation) that read and "
                          "write 256 MiB each, the reference dispatch that scales the HBM "
@@ -153,6 +156,9 @@ def main():
         return
     if args.workload == "prefill-blockmask":
         blockmask_main(args, dev)
+        return
+    if args.workload == "prefill-selected-bwd":
+        selected_bwd_main(args, dev)
         return
     if args.workload not in ("decode", "decode-long"):
         prefill_main(args, dev)
@@ -427,6 +433,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -872,6 +879,112 @@ def prefill_main(args, dev):
             result["cpu_baseline"] = sampled_oracle_baseline(rows_fn, w.total_tokens, w.total_tokens,
                                                              args.cpu_seconds, "query rows",
                                                              chunk=32, fixed_fn=pool)
+    print(json.dumps(result), flush=True)
+
+
+def selected_bwd_main(args, dev):
+    """Backward of the selected attention over the prefill-selected batch: one
+    step = the gradient (dq, dk, dv) of the whole batch from the forward's
+    output, log-normaliser and a given upstream gradient; value = prefill tokens/s
+    of the backward.  The kernels run on the vector ALUs in fp32, so the roofline
+    is the algorithmic fp32 flops of the longer of the dq and dk/dv kernels."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_compress_amd as nsa
+    from gen import workloads as W
+
+    stream = torch.cuda.Stream(device=dev)
+    steps = args.steps if args.steps != 2800 else 5
+    warmup = args.warmup if args.warmup != 280 else 1
+    D = 128
+    w = W.selected_prefill()
+    print(f"[bench] workload {w.name} (backward)", file=sys.stderr, flush=True)
+    q = W.prefill_query(w, dev)
+    k, v = W.keys_values(w, dev)
+    idx = W.given_block_indices(w, dev)
+    d_out = W.prefill_out_grad(w, dev)
+    cu = nsa.cu_seqlens_of(w.lengths, dev)
+    L_max = max(w.lengths)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    nsa.nsa_selected_attn_fwd(q, k, v, idx, cu, L_max, out, lse=lse, cu_seqlens_q=cu)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(nsa.selected_attn_bwd_workspace_size(w.batch, w.total_tokens, L_max, w.heads,
+                                                          w.kv_heads, w.topk),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def fn():
+        nsa.nsa_selected_attn_bwd(q, k, v, out, d_out, lse, idx, cu, cu, L_max, dq, dk, dv,
+                                  workspace=ws)
+    kinds = {"lists": nsa.KERNEL_SELECTED_BWD_LISTS, "dq": nsa.KERNEL_SELECTED_BWD_DQ,
+             "dkdv": nsa.KERNEL_SELECTED_BWD_DKDV}
+    ids = idx.cpu().numpy().astype(np.int64).reshape(-1, w.topk)
+    pos = np.concatenate([np.arange(L) for L in w.lengths])
+    t = np.repeat(pos, w.kv_heads).reshape(-1, 1)
+    keys = float(np.where(ids >= 0, np.clip(t - 64 * ids + 1, 0, 64), 0).sum())
+    G = w.heads // w.kv_heads
+    # per attended (row, head, key): q.k, dO.v and ds.k for dq (3 dot products of
+    # D); q.k, dO.v and the dk, dv updates for dk/dv (4)
+    flops = {"dq": 6.0 * D * G * keys, "dkdv": 8.0 * D * G * keys}
+    wall_s, gpu_ms = _timed(fn, steps, warmup, stream)
+    kern = _kernel_us(nsa, fn, kinds, 3, stream)
+    dominant = max(flops, key=lambda n: kern[n])
+    tflops = {n: flops[n] / (kern[n] * 1e-6) / 1e12 for n in flops}
+    ms_per_step = wall_s * 1e3 / steps
+    result = {
+        "metric": f"prefill backward tokens/s ({w.name})",
+        "value": round(w.total_tokens * steps / wall_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V and upstream gradient, uniform causal block "
+                "indices; no dataset)",
+        "config": {"workload": w.name + "_bwd", "batch": w.batch, "seq_len": L_max,
+                   "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": D, "topk": w.topk},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "alu",
+            "achieved": round(tflops[dominant], 2),
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops[dominant] / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops[dominant],
+            "mean_kernel_us": round(kern[dominant], 1),
+        },
+        "kernel_us": {n: round(x, 1) for n, x in kern.items()},
+        "kernel_tflops": {n: round(x, 2) for n, x in tflops.items()},
+        "timed_gpu_ms": round(gpu_ms, 3),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        scale = 1.0 / math.sqrt(D)
+        kn, vn = k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+        qn = q.float().cpu().numpy().astype(np.float64)
+        don = d_out.float().cpu().numpy().astype(np.float64)
+        idn = idx.cpu().numpy()
+        L0 = w.lengths[0]
+        dk_s = np.zeros((L0,) + kn.shape[1:])
+        dv_s = np.zeros((L0,) + vn.shape[1:])
+
+        def rows_fn(rows):  # rows of equal-length sequences, packed
+            for r in rows:
+                b_, t_ = divmod(r, L0)
+                s0 = b_ * L0
+                oracle.selected_attention_row_grad(qn[r], kn[s0:s0 + L0], vn[s0:s0 + L0], idn[r],
+                                                   t_, 64, scale, don[r], dk_s, dv_s)
+        result["cpu_baseline"] = sampled_oracle_baseline(rows_fn, w.total_tokens, w.total_tokens,
+                                                         args.cpu_seconds, "query rows")
     print(json.dumps(result), flush=True)
 
 

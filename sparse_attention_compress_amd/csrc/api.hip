@@ -273,8 +273,9 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
               NSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
   NSA_REQUIRE(q && k && v && out && d_out && lse && indices && cu_seqlens_k && dq && dk && dv,
               NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
-  NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(d_out),
-              NSA_ERR_INVALID_ARG, "%s: q, k, v, out, d_out must be 16-byte aligned", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(d_out) &&
+                  aligned16(dk) && aligned16(dv),
+              NSA_ERR_INVALID_ARG, "%s: q, k, v, out, d_out, dk, dv must be 16-byte aligned", fn);
   const size_t need = nsa_selected_attn_bwd_workspace_size(batch, rows_total, max_seqlen_k, heads, kv_heads, k_sel);
   NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
   NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
@@ -295,6 +296,7 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.nb_max = nb_max;
+  a.max_seqlen_k = max_seqlen_k;
   a.scale = scale;
   a.dq = dq;
   a.dk = dk;

@@ -10,14 +10,17 @@
 //   dV_J += p dO^T,  ds = p * (V_J dO - delta),  delta = dO . O,
 //   dq = scale ds K_J,  dK_J += scale ds q^T.
 // dq is a gather (each row reads its own blocks).  dK and dV are sums over the
-// rows that list a block; instead of scattering them with atomics, the row
-// lists are transposed into one list of rows per (sequence, KV head, block)
-// (count, scan, fill), and each block gathers its rows, so every gradient
-// element is written once by one workgroup.
+// rows that list a block; instead of scattering every (row, key) term with
+// atomics, the row lists are transposed into one list of rows per (sequence,
+// KV head, block) (count, scan, fill), and each block gathers its rows, in
+// chunks of up to 256 rows per workgroup (the chunks of one block add their
+// sums with fp32 atomics, one per gradient element and chunk).
 //
-// Launches: prep (delta, list counts cleared), count, scan, fill, dq, dk/dv.
-// Order within a block's row list depends on atomics, so dK and dV are summed
-// in an order that can change from call to call (fp32 rounding only).
+// Launches: prep (delta, list counts cleared), count, scan, fill, zero (the
+// blocks with long row lists), dq, dk/dv.
+// The order within a block's row list, and of the chunk sums, depends on
+// atomics, so dK and dV are summed in an order that can change from call to
+// call (fp32 rounding only).
 #include <algorithm>
 
 #include "common.h"
@@ -29,6 +32,7 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 constexpr int kScanThreads = 1024;
+constexpr int kRowsPerChunk = 256;  // rows of a block's list one dk/dv workgroup takes
 
 __device__ __forceinline__ void bwd_row_position(int row, const int* __restrict__ cu_q,
                                                  const int* __restrict__ cu_k, int batch, int& b,
@@ -129,10 +133,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fill_kernel(
   if (slot >= 0) list[atomicAdd(cursor + slot, 1)] = row;
 }
 
-// Thread (j, part) of a 64-token block: token j, dims 32*part .. +31.
+// dk and dv of the blocks whose row list spans several chunks start at 0 (the
+// chunks add to them); one workgroup per (sequence, kv head, block).
+__global__ __launch_bounds__(kBwdThreads) void bwd_zero_kernel(const int* __restrict__ cnt,
+                                                               const int* __restrict__ cu_k,
+                                                               int kv_heads, int nb_max,
+                                                               float* __restrict__ dk,
+                                                               float* __restrict__ dv) {
+  const int slot = blockIdx.x;
+  if (cnt[slot] <= kRowsPerChunk) return;
+  const int id = slot % nb_max;
+  const int g = (slot / nb_max) % kv_heads;
+  const int b = slot / (nb_max * kv_heads);
+  const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
+  const int tok = kBlock * id + (threadIdx.x >> 2);
+  if (tok >= len) return;
+  const size_t o = (size_t(kstart + tok) * kv_heads + g) * kHeadDim + 32 * (threadIdx.x & 3);
+#pragma unroll
+  for (int e = 0; e < 32; e += 4) {
+    *reinterpret_cast<float4*>(dk + o + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dv + o + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// Thread (j, part) of a 64-token block: token j, dims 32*part .. +31, kept as
+// bf16 pairs (16 registers each).
 struct KeySlice {
-  float k[32];
-  float v[32];
+  uint32_t k[16];
+  uint32_t v[16];
 };
 
 __device__ __forceinline__ void load_key_slice(const bf16_t* __restrict__ k,
@@ -140,16 +168,10 @@ __device__ __forceinline__ void load_key_slice(const bf16_t* __restrict__ k,
                                                bool ok, KeySlice& s) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (ok) {
-      load8f(k + off + 8 * i, &s.k[8 * i]);
-      load8f(v + off + 8 * i, &s.v[8 * i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s.k[8 * i + e] = 0.f;
-        s.v[8 * i + e] = 0.f;
-      }
-    }
+    const uint4 a = ok ? ld16(k + off + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 b = ok ? ld16(v + off + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+    s.k[4 * i] = a.x; s.k[4 * i + 1] = a.y; s.k[4 * i + 2] = a.z; s.k[4 * i + 3] = a.w;
+    s.v[4 * i] = b.x; s.v[4 * i + 1] = b.y; s.v[4 * i + 2] = b.z; s.v[4 * i + 3] = b.w;
   }
 }
 
@@ -185,10 +207,14 @@ template <int G>
 __device__ __forceinline__ void probs(const RowLds<G>& R, const KeySlice& s, int h, int part,
                                       bool valid, float scale_log2, float& p, float& ds) {
   float a = 0.f, b = 0.f;
+  const float* qh = &R.q[h][32 * part];
+  const float* dh = &R.d[h][32 * part];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    a = fmaf(R.q[h][32 * part + e], s.k[e], a);
-    b = fmaf(R.d[h][32 * part + e], s.v[e], b);
+  for (int e = 0; e < 16; ++e) {
+    a = fmaf(qh[2 * e], bf16lo(s.k[e]), a);
+    a = fmaf(qh[2 * e + 1], bf16hi(s.k[e]), a);
+    b = fmaf(dh[2 * e], bf16lo(s.v[e]), b);
+    b = fmaf(dh[2 * e + 1], bf16hi(s.v[e]), b);
   }
   a = quad_reduce(a, OpSum());
   b = quad_reduce(b, OpSum());
@@ -229,8 +255,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     load_key_slice(k, v, (size_t(kstart + min(tok, t)) * kv_heads + g) * kHeadDim + 32 * part,
                    valid, s);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) k_s[j][32 * part + e] = s.k[e];
-#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      k_s[j][32 * part + 2 * e] = bf16lo(s.k[e]);
+      k_s[j][32 * part + 2 * e + 1] = bf16hi(s.k[e]);
+    }
+#pragma unroll 1
     for (int h = 0; h < G; ++h) {
       float p, ds;
       probs<G>(R, s, h, part, valid, scale_log2, p, ds);
@@ -257,8 +286,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   }
 }
 
-// dK and dV of one (sequence, kv head, block): the rows that list it, one at a
-// time.  Every token of the block is written (zeros when no row lists it).
+// dK and dV of one (sequence, kv head, block) over one chunk of up to
+// kRowsPerChunk of the rows that list it (grid: slot x chunk).  A block listed
+// by at most one chunk's rows stores its gradients (zeros when no row lists
+// it); the chunks of a longer list add theirs to the zeroed gradients with
+// fp32 atomics, so the earliest blocks, which most rows list, are spread over
+// several workgroups instead of one.
 template <int G>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -269,7 +302,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     float* __restrict__ dk, float* __restrict__ dv) {
   __shared__ RowLds<G> R;
   const int tid = threadIdx.x, j = tid >> 2, part = tid & 3;
-  const int slot = blockIdx.x;
+  const int slot = blockIdx.x, chunk = blockIdx.y;
+  const int n = cnt[slot];
+  const int e_begin = chunk * kRowsPerChunk;
+  if (chunk > 0 && e_begin >= n) return;  // uniform: no rows left for this chunk
+  const int e_end = min(n, e_begin + kRowsPerChunk);
   const int id = slot % nb_max;
   const int g = (slot / nb_max) % kv_heads;
   const int b = slot / (nb_max * kv_heads);
@@ -286,8 +323,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     ak[e] = 0.f;
     av[e] = 0.f;
   }
-  const int n = cnt[slot], first = off[slot];
-  for (int e0 = 0; e0 < n; ++e0) {
+  const int first = off[slot];
+  for (int e0 = e_begin; e0 < e_end; ++e0) {
     const int row = list[first + e0];
     int bb, t;
     bwd_row_position(row, cu_q, cu_k, batch, bb, t);
@@ -295,22 +332,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     stage_row<G>(R, q, dout, lse, delta, size_t(row) * heads + size_t(g) * G);
     __syncthreads();
     const bool valid = tok_ok && tok <= t;
-#pragma unroll
+#pragma unroll 1
     for (int h = 0; h < G; ++h) {
       float p, ds;
       probs<G>(R, s, h, part, valid, scale_log2, p, ds);
+      const float* qh = &R.q[h][32 * part];
+      const float* dh = &R.d[h][32 * part];
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        av[e] = fmaf(p, R.d[h][32 * part + e], av[e]);
-        ak[e] = fmaf(ds, R.q[h][32 * part + e], ak[e]);
+        av[e] = fmaf(p, dh[e], av[e]);
+        ak[e] = fmaf(ds, qh[e], ak[e]);
       }
     }
   }
   if (!tok_ok) return;
+  if (n <= kRowsPerChunk) {
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    dk[kv_off + e] = scale * ak[e];
-    dv[kv_off + e] = av[e];
+    for (int e = 0; e < 32; ++e) {
+      dk[kv_off + e] = scale * ak[e];
+      dv[kv_off + e] = av[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      atomicAdd(dk + kv_off + e, scale * ak[e]);
+      atomicAdd(dv + kv_off + e, av[e]);
+    }
   }
 }
 
@@ -339,13 +386,17 @@ hipError_t launch_bwd_g(const SelectedBwdArgs& a, hipStream_t s) {
                       a.cursor, a.list);
     if (e != hipSuccess) return e;
   }
+  e = launch_kernel(kKindBwdLists, bwd_zero_kernel, dim3(unsigned(n_slots)), dim3(kBwdThreads), s,
+                    static_cast<const int*>(a.cnt), a.cu_k, a.kv_heads, a.nb_max, a.dk, a.dv);
+  if (e != hipSuccess) return e;
   const float scale_log2 = a.scale * kLog2eHost;
   e = launch_kernel(kKindBwdQ, bwd_dq_kernel<G>, dim3(unsigned(a.rows_total) * a.kv_heads),
                     dim3(kBwdThreads), s, a.q, a.k, a.v, a.dout, a.lse,
                     static_cast<const float*>(a.delta), a.indices, a.k_sel, a.cu_q, a.cu_k,
                     a.batch, a.heads, a.kv_heads, scale_log2, a.scale, a.dq);
   if (e != hipSuccess) return e;
-  return launch_kernel(kKindBwdKV, bwd_dkdv_kernel<G>, dim3(unsigned(n_slots)),
+  const unsigned n_chunk = unsigned((a.max_seqlen_k + kRowsPerChunk - 1) / kRowsPerChunk);
+  return launch_kernel(kKindBwdKV, bwd_dkdv_kernel<G>, dim3(unsigned(n_slots), std::max(1u, n_chunk)),
                        dim3(kBwdThreads), s, a.q, a.k, a.v, a.dout, a.lse,
                        static_cast<const float*>(a.delta), static_cast<const int*>(a.cnt),
                        static_cast<const int*>(a.off), static_cast<const int*>(a.list), a.cu_q,

@@ -227,7 +227,7 @@ struct SelectedBwdArgs {
   int k_sel;
   const int* cu_q;
   const int* cu_k;
-  int batch, rows_total, heads, kv_heads, nb_max;
+  int batch, rows_total, heads, kv_heads, nb_max, max_seqlen_k;
   float scale;         // softmax scale (natural domain)
   float* dq;           // [rows, heads, 128]
   float* dk;           // [N_k, kv_heads, 128]

@@ -256,9 +256,10 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
  *                 row attends to)
  *   Per head over the row's keys J: dV_J += p dO^T; ds = p*(V_J dO - dO.O);
  *   dq = scale ds K_J; dK_J += scale ds q^T.  dk and dv are gathered per
- *   (sequence, KV head, block) over the rows that list the block (no atomics on
- *   the gradients); their summation order follows the row lists, which atomics
- *   build, so it may change between calls (fp32 rounding only).
+ *   (sequence, KV head, block) over the rows that list the block, up to 256
+ *   rows per workgroup; a block listed by more rows has its chunk sums added
+ *   with fp32 atomics.  The row lists are built with atomics too, so the
+ *   summation order of dk and dv may change between calls (fp32 rounding only).
  *   workspace: nsa_selected_attn_bwd_workspace_size(...) bytes, device memory.
  *   Returns NSA_ERR_UNSUPPORTED for non-bf16 inputs or k_sel > 64.
  */

@@ -156,29 +156,36 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_zero_kernel(const int* __rest
   }
 }
 
-// Thread (j, part) of a 64-token block: token j, dims 32*part .. +31, kept as
-// bf16 pairs (16 registers each).
-struct KeySlice {
-  uint32_t k[16];
-  uint32_t v[16];
+// Thread (tg, dp) of a 64-token block: tokens 4*tg .. 4*tg+3, dims 8*dp .. +7,
+// kept as bf16 (one 16-byte run per token).  The 16 lanes of a DPP row hold the
+// 16 dim slices of the same four tokens, so a dot product over the 128 dims is
+// a row reduction, and each q or dO value read from LDS serves four keys.
+struct KeyTile {
+  uint4 k[4];
+  uint4 v[4];
 };
 
-__device__ __forceinline__ void load_key_slice(const bf16_t* __restrict__ k,
-                                               const bf16_t* __restrict__ v, size_t off,
-                                               bool ok, KeySlice& s) {
+__device__ __forceinline__ float bf16_at(const uint4& w, int e) {
+  const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+  return (e & 1) ? bf16hi(x) : bf16lo(x);
+}
+
+// K and V of tokens tok0 .. tok0+3 (row offsets given by the caller); a token
+// with ok[i] false reads nothing and holds zeros.
+__device__ __forceinline__ void load_tile(const bf16_t* __restrict__ k,
+                                          const bf16_t* __restrict__ v, const size_t off[4],
+                                          const bool ok[4], KeyTile& s) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 a = ok ? ld16(k + off + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
-    const uint4 b = ok ? ld16(v + off + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
-    s.k[4 * i] = a.x; s.k[4 * i + 1] = a.y; s.k[4 * i + 2] = a.z; s.k[4 * i + 3] = a.w;
-    s.v[4 * i] = b.x; s.v[4 * i + 1] = b.y; s.v[4 * i + 2] = b.z; s.v[4 * i + 3] = b.w;
+    s.k[i] = ok[i] ? ld16(k + off[i]) : make_uint4(0u, 0u, 0u, 0u);
+    s.v[i] = ok[i] ? ld16(v + off[i]) : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
 // The G heads' q and dO rows of one query row in LDS (fp32), with the
 // log2-domain normaliser and delta.
 template <int G>
-struct RowLds {
+struct alignas(16) RowLds {
   float q[G][kHeadDim];
   float d[G][kHeadDim];
   float lse2[G];
@@ -201,25 +208,39 @@ __device__ __forceinline__ void stage_row(RowLds<G>& R, const bf16_t* __restrict
   }
 }
 
-// p and ds of head h for this thread's token (all four lanes of the token get
-// the sums over the 128 dims).
+// This thread's 8 dims of head h's q and dO.
 template <int G>
-__device__ __forceinline__ void probs(const RowLds<G>& R, const KeySlice& s, int h, int part,
-                                      bool valid, float scale_log2, float& p, float& ds) {
-  float a = 0.f, b = 0.f;
-  const float* qh = &R.q[h][32 * part];
-  const float* dh = &R.d[h][32 * part];
+__device__ __forceinline__ void head_slice(const RowLds<G>& R, int h, int dp, float q8[8],
+                                           float d8[8]) {
+  const float4 qa = *reinterpret_cast<const float4*>(&R.q[h][8 * dp]);
+  const float4 qb = *reinterpret_cast<const float4*>(&R.q[h][8 * dp + 4]);
+  const float4 da = *reinterpret_cast<const float4*>(&R.d[h][8 * dp]);
+  const float4 db = *reinterpret_cast<const float4*>(&R.d[h][8 * dp + 4]);
+  q8[0] = qa.x; q8[1] = qa.y; q8[2] = qa.z; q8[3] = qa.w;
+  q8[4] = qb.x; q8[5] = qb.y; q8[6] = qb.z; q8[7] = qb.w;
+  d8[0] = da.x; d8[1] = da.y; d8[2] = da.z; d8[3] = da.w;
+  d8[4] = db.x; d8[5] = db.y; d8[6] = db.z; d8[7] = db.w;
+}
+
+// p and ds of head h for the thread's four tokens (every lane of the DPP row
+// gets the sums over the 128 dims).
+template <int G>
+__device__ __forceinline__ void probs4(const RowLds<G>& R, const KeyTile& s, int h,
+                                       const float q8[8], const float d8[8], const bool valid[4],
+                                       float scale_log2, float p[4], float ds[4]) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    a = fmaf(qh[2 * e], bf16lo(s.k[e]), a);
-    a = fmaf(qh[2 * e + 1], bf16hi(s.k[e]), a);
-    b = fmaf(dh[2 * e], bf16lo(s.v[e]), b);
-    b = fmaf(dh[2 * e + 1], bf16hi(s.v[e]), b);
+  for (int i = 0; i < 4; ++i) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a = fmaf(q8[e], bf16_at(s.k[i], e), a);
+      b = fmaf(d8[e], bf16_at(s.v[i], e), b);
+    }
+    a = row_reduce(a, OpSum());
+    b = row_reduce(b, OpSum());
+    p[i] = valid[i] ? fast_exp2(a * scale_log2 - R.lse2[h]) : 0.f;
+    ds[i] = p[i] * (b - R.delta[h]);
   }
-  a = quad_reduce(a, OpSum());
-  b = quad_reduce(b, OpSum());
-  p = valid ? fast_exp2(a * scale_log2 - R.lse2[h]) : 0.f;
-  ds = p * (b - R.delta[h]);
 }
 
 // dq of one (row, kv head): the row's selected blocks one at a time.
@@ -232,9 +253,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     int kv_heads, float scale_log2, float scale, float* __restrict__ dq) {
   constexpr int kOut = (G * kHeadDim + kBwdThreads - 1) / kBwdThreads;
   __shared__ RowLds<G> R;
-  __shared__ float k_s[kBlock][kHeadDim + 1];
+  __shared__ float k_s[kBlock][kHeadDim + 4];
   __shared__ float ds_s[G][kBlock];
-  const int tid = threadIdx.x, j = tid >> 2, part = tid & 3;
+  const int tid = threadIdx.x, tg = tid >> 4, dp = tid & 15;
   const int row = int(blockIdx.x / unsigned(kv_heads)), g = int(blockIdx.x % unsigned(kv_heads));
   int b, t;
   bwd_row_position(row, cu_q, cu_k, batch, b, t);
@@ -249,21 +270,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   for (int pl = 0; pl < k_sel; ++pl) {
     const int id = irow[pl];
     if (t < 0 || t >= len || id < 0 || id > t / kBlock) continue;  // uniform
-    const int tok = kBlock * id + j;
-    const bool valid = tok <= t;
-    KeySlice s;
-    load_key_slice(k, v, (size_t(kstart + min(tok, t)) * kv_heads + g) * kHeadDim + 32 * part,
-                   valid, s);
+    bool valid[4];
+    size_t off[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      k_s[j][32 * part + 2 * e] = bf16lo(s.k[e]);
-      k_s[j][32 * part + 2 * e + 1] = bf16hi(s.k[e]);
+    for (int i = 0; i < 4; ++i) {
+      const int tok = kBlock * id + 4 * tg + i;
+      valid[i] = tok <= t;
+      off[i] = (size_t(kstart + min(tok, t)) * kv_heads + g) * kHeadDim + 8 * dp;
     }
+    KeyTile s;
+    load_tile(k, v, off, valid, s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) k_s[4 * tg + i][8 * dp + e] = bf16_at(s.k[i], e);
 #pragma unroll 1
     for (int h = 0; h < G; ++h) {
-      float p, ds;
-      probs<G>(R, s, h, part, valid, scale_log2, p, ds);
-      if (part == 0) ds_s[h][j] = ds;
+      float q8[8], d8[8], p[4], ds[4];
+      head_slice<G>(R, h, dp, q8, d8);
+      probs4<G>(R, s, h, q8, d8, valid, scale_log2, p, ds);
+      if (dp == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds_s[h][4 * tg + i] = ds[i];
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -301,7 +330,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     int batch, int heads, int kv_heads, int nb_max, float scale_log2, float scale,
     float* __restrict__ dk, float* __restrict__ dv) {
   __shared__ RowLds<G> R;
-  const int tid = threadIdx.x, j = tid >> 2, part = tid & 3;
+  const int tid = threadIdx.x, tg = tid >> 4, dp = tid & 15;
   const int slot = blockIdx.x, chunk = blockIdx.y;
   const int n = cnt[slot];
   const int e_begin = chunk * kRowsPerChunk;
@@ -312,17 +341,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   const int b = slot / (nb_max * kv_heads);
   const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
   if (kBlock * id >= len) return;  // uniform: no token of this sequence here
-  const int tok = kBlock * id + j;
-  const bool tok_ok = tok < len;
-  const size_t kv_off = (size_t(kstart + min(tok, len - 1)) * kv_heads + g) * kHeadDim + 32 * part;
-  KeySlice s;
-  load_key_slice(k, v, kv_off, tok_ok, s);
-  float ak[32], av[32];
+  int tok[4];
+  bool tok_ok[4];
+  size_t kv_off[4];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    ak[e] = 0.f;
-    av[e] = 0.f;
+  for (int i = 0; i < 4; ++i) {
+    tok[i] = kBlock * id + 4 * tg + i;
+    tok_ok[i] = tok[i] < len;
+    kv_off[i] = (size_t(kstart + min(tok[i], len - 1)) * kv_heads + g) * kHeadDim + 8 * dp;
   }
+  KeyTile s;
+  load_tile(k, v, kv_off, tok_ok, s);
+  float ak[4][8], av[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ak[i][e] = 0.f;
+      av[i][e] = 0.f;
+    }
   const int first = off[slot];
   for (int e0 = e_begin; e0 < e_end; ++e0) {
     const int row = list[first + e0];
@@ -331,32 +368,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     __syncthreads();  // the previous row's LDS is no longer read
     stage_row<G>(R, q, dout, lse, delta, size_t(row) * heads + size_t(g) * G);
     __syncthreads();
-    const bool valid = tok_ok && tok <= t;
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) valid[i] = tok_ok[i] && tok[i] <= t;
 #pragma unroll 1
     for (int h = 0; h < G; ++h) {
-      float p, ds;
-      probs<G>(R, s, h, part, valid, scale_log2, p, ds);
-      const float* qh = &R.q[h][32 * part];
-      const float* dh = &R.d[h][32 * part];
+      float q8[8], d8[8], p[4], ds[4];
+      head_slice<G>(R, h, dp, q8, d8);
+      probs4<G>(R, s, h, q8, d8, valid, scale_log2, p, ds);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        av[e] = fmaf(p, dh[e], av[e]);
-        ak[e] = fmaf(ds, qh[e], ak[e]);
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          av[i][e] = fmaf(p[i], d8[e], av[i][e]);
+          ak[i][e] = fmaf(ds[i], q8[e], ak[i][e]);
+        }
     }
   }
-  if (!tok_ok) return;
-  if (n <= kRowsPerChunk) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      dk[kv_off + e] = scale * ak[e];
-      dv[kv_off + e] = av[e];
-    }
-  } else {
+  for (int i = 0; i < 4; ++i) {
+    if (!tok_ok[i]) continue;
+    if (n <= kRowsPerChunk) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      atomicAdd(dk + kv_off + e, scale * ak[e]);
-      atomicAdd(dv + kv_off + e, av[e]);
+      for (int e = 0; e < 8; e += 4) {
+        *reinterpret_cast<float4*>(dk + kv_off[i] + e) =
+            make_float4(scale * ak[i][e], scale * ak[i][e + 1], scale * ak[i][e + 2], scale * ak[i][e + 3]);
+        *reinterpret_cast<float4*>(dv + kv_off[i] + e) =
+            make_float4(av[i][e], av[i][e + 1], av[i][e + 2], av[i][e + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        atomicAdd(dk + kv_off[i] + e, scale * ak[i][e]);
+        atomicAdd(dv + kv_off[i] + e, av[i][e]);
+      }
     }
   }
 }

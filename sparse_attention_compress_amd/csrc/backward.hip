@@ -243,7 +243,10 @@ __device__ __forceinline__ void probs4(const RowLds<G>& R, const KeyTile& s, int
   }
 }
 
-// dq of one (row, kv head): the row's selected blocks one at a time.
+// dq of one (row, kv head): the row's selected blocks one at a time.  Each
+// thread adds ds * k of its four tokens to its 8 dims of every head's dq in
+// registers; the 16 token groups are summed once at the end (the four groups
+// of a wave by lane swaps across its DPP rows, the four waves through LDS).
 template <int G>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -253,18 +256,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     int kv_heads, float scale_log2, float scale, float* __restrict__ dq) {
   constexpr int kOut = (G * kHeadDim + kBwdThreads - 1) / kBwdThreads;
   __shared__ RowLds<G> R;
-  __shared__ float k_s[kBlock][kHeadDim + 4];
-  __shared__ float ds_s[G][kBlock];
-  const int tid = threadIdx.x, tg = tid >> 4, dp = tid & 15;
+  __shared__ float red_s[4][G][kHeadDim];
+  const int tid = threadIdx.x, tg = tid >> 4, dp = tid & 15, wave = tid >> 6;
   const int row = int(blockIdx.x / unsigned(kv_heads)), g = int(blockIdx.x % unsigned(kv_heads));
   int b, t;
   bwd_row_position(row, cu_q, cu_k, batch, b, t);
   const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
   const size_t head0 = size_t(row) * heads + size_t(g) * G;
   stage_row<G>(R, q, dout, lse, delta, head0);
-  float acc[kOut];
+  float acc[G][8];
 #pragma unroll
-  for (int i = 0; i < kOut; ++i) acc[i] = 0.f;
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   __syncthreads();
   const int* irow = indices + (size_t(row) * kv_heads + g) * k_sel;
   for (int pl = 0; pl < k_sel; ++pl) {
@@ -281,37 +285,38 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     KeyTile s;
     load_tile(k, v, off, valid, s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) k_s[4 * tg + i][8 * dp + e] = bf16_at(s.k[i], e);
-#pragma unroll 1
     for (int h = 0; h < G; ++h) {
       float q8[8], d8[8], p[4], ds[4];
       head_slice<G>(R, h, dp, q8, d8);
       probs4<G>(R, s, h, q8, d8, valid, scale_log2, p, ds);
-      if (dp == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ds_s[h][4 * tg + i] = ds[i];
-      }
-    }
-    __syncthreads();
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < kOut; ++i) {
-      const int o = tid + kBwdThreads * i;
-      if (o < G * kHeadDim) {
-        const int h = o / kHeadDim, d = o % kHeadDim;
-        float a = acc[i];
-#pragma unroll 8
-        for (int jj = 0; jj < kBlock; ++jj) a = fmaf(ds_s[h][jj], k_s[jj][d], a);
-        acc[i] = a;
-      }
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ds[i], bf16_at(s.k[i], e), acc[h][e]);
     }
-    __syncthreads();
   }
+  // sum over the token groups: the 4 DPP rows of the wave, then the 4 waves
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = cross16(acc[h][e], OpSum());
+      acc[h][e] = cross32(x, OpSum());
+    }
+  if ((tid & 63) < 16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_s[wave][h][8 * dp + e] = acc[h][e];
+  }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < kOut; ++i) {
     const int o = tid + kBwdThreads * i;
-    if (o < G * kHeadDim) dq[head0 * kHeadDim + o] = scale * acc[i];
+    if (o < G * kHeadDim) {
+      const int h = o / kHeadDim, d = o % kHeadDim;
+      dq[head0 * kHeadDim + o] = scale * (red_s[0][h][d] + red_s[1][h][d] + red_s[2][h][d] + red_s[3][h][d]);
+    }
   }
 }
 

@@ -65,17 +65,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
 }
 
 // One thread per (row, kv head, place): whether the place lists a block the
-// row attends to, and its (sequence, kv head, block) slot.
+// row attends to, its (sequence, kv head, block) slot, and the row's position.
 __device__ __forceinline__ int bwd_slot_of(size_t i, const int* __restrict__ indices, int k_sel,
                                            int kv_heads, const int* __restrict__ cu_q,
                                            const int* __restrict__ cu_k, int batch, int nb_max,
-                                           int& row) {
+                                           int& row, int& t) {
   const size_t unit = i / size_t(k_sel);
   row = int(unit / size_t(kv_heads));
   const int g = int(unit % size_t(kv_heads));
   const int id = indices[i];
+  t = -1;
   if (id < 0 || id >= nb_max) return -1;
-  int b, t;
+  int b;
   bwd_row_position(row, cu_q, cu_k, batch, b, t);
   const int len = cu_k[b + 1] - cu_k[b];
   if (t < 0 || t >= len || kBlock * id > t) return -1;
@@ -88,8 +89,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_count_kernel(
     int* __restrict__ cnt) {
   const size_t i = size_t(blockIdx.x) * kBwdThreads + threadIdx.x;
   if (i >= n) return;
-  int row;
-  const int slot = bwd_slot_of(i, indices, k_sel, kv_heads, cu_q, cu_k, batch, nb_max, row);
+  int row, t;
+  const int slot = bwd_slot_of(i, indices, k_sel, kv_heads, cu_q, cu_k, batch, nb_max, row, t);
   if (slot >= 0) atomicAdd(cnt + slot, 1);
 }
 
@@ -125,12 +126,12 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const int* __res
 __global__ __launch_bounds__(kBwdThreads) void bwd_fill_kernel(
     const int* __restrict__ indices, size_t n, int k_sel, int kv_heads,
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int nb_max,
-    int* __restrict__ cursor, int* __restrict__ list) {
+    int* __restrict__ cursor, int2* __restrict__ list) {
   const size_t i = size_t(blockIdx.x) * kBwdThreads + threadIdx.x;
   if (i >= n) return;
-  int row;
-  const int slot = bwd_slot_of(i, indices, k_sel, kv_heads, cu_q, cu_k, batch, nb_max, row);
-  if (slot >= 0) list[atomicAdd(cursor + slot, 1)] = row;
+  int row, t;
+  const int slot = bwd_slot_of(i, indices, k_sel, kv_heads, cu_q, cu_k, batch, nb_max, row, t);
+  if (slot >= 0) list[atomicAdd(cursor + slot, 1)] = make_int2(row, t);
 }
 
 // dk and dv of the blocks whose row list spans several chunks start at 0 (the
@@ -331,10 +332,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, const int* __restrict__ cnt, const int* __restrict__ off,
-    const int* __restrict__ list, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
-    int batch, int heads, int kv_heads, int nb_max, float scale_log2, float scale,
-    float* __restrict__ dk, float* __restrict__ dv) {
-  __shared__ RowLds<G> R;
+    const int2* __restrict__ list, const int* __restrict__ cu_k, int heads, int kv_heads,
+    int nb_max, float scale_log2, float scale, float* __restrict__ dk, float* __restrict__ dv) {
+  __shared__ RowLds<G> R[2];
   const int tid = threadIdx.x, tg = tid >> 4, dp = tid & 15;
   const int slot = blockIdx.x, chunk = blockIdx.y;
   const int n = cnt[slot];
@@ -366,28 +366,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       av[i][e] = 0.f;
     }
   const int first = off[slot];
-  for (int e0 = e_begin; e0 < e_end; ++e0) {
-    const int row = list[first + e0];
-    int bb, t;
-    bwd_row_position(row, cu_q, cu_k, batch, bb, t);
-    __syncthreads();  // the previous row's LDS is no longer read
-    stage_row<G>(R, q, dout, lse, delta, size_t(row) * heads + size_t(g) * G);
+  // two listed rows (with their positions) per pair of barriers
+  for (int e0 = e_begin; e0 < e_end; e0 += 2) {
+    const bool two = e0 + 1 < e_end;  // uniform
+    const int2 r0 = list[first + e0];
+    const int2 r1 = two ? list[first + e0 + 1] : r0;
+    __syncthreads();  // the previous rows' LDS is no longer read
+    stage_row<G>(R[0], q, dout, lse, delta, size_t(r0.x) * heads + size_t(g) * G);
+    if (two) stage_row<G>(R[1], q, dout, lse, delta, size_t(r1.x) * heads + size_t(g) * G);
     __syncthreads();
-    bool valid[4];
+    for (int rr = 0; rr < (two ? 2 : 1); ++rr) {
+      const RowLds<G>& Rr = R[rr];
+      const int t = rr ? r1.y : r0.y;
+      bool valid[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) valid[i] = tok_ok[i] && tok[i] <= t;
+      for (int i = 0; i < 4; ++i) valid[i] = tok_ok[i] && tok[i] <= t;
 #pragma unroll 1
-    for (int h = 0; h < G; ++h) {
-      float q8[8], d8[8], p[4], ds[4];
-      head_slice<G>(R, h, dp, q8, d8);
-      probs4<G>(R, s, h, q8, d8, valid, scale_log2, p, ds);
+      for (int h = 0; h < G; ++h) {
+        float q8[8], d8[8], p[4], ds[4];
+        head_slice<G>(Rr, h, dp, q8, d8);
+        probs4<G>(Rr, s, h, q8, d8, valid, scale_log2, p, ds);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          av[i][e] = fmaf(p[i], d8[e], av[i][e]);
-          ak[i][e] = fmaf(ds[i], q8[e], ak[i][e]);
-        }
+          for (int e = 0; e < 8; ++e) {
+            av[i][e] = fmaf(p[i], d8[e], av[i][e]);
+            ak[i][e] = fmaf(ds[i], q8[e], ak[i][e]);
+          }
+      }
     }
   }
 #pragma unroll
@@ -449,9 +455,8 @@ hipError_t launch_bwd_g(const SelectedBwdArgs& a, hipStream_t s) {
   return launch_kernel(kKindBwdKV, bwd_dkdv_kernel<G>, dim3(unsigned(n_slots), std::max(1u, n_chunk)),
                        dim3(kBwdThreads), s, a.q, a.k, a.v, a.dout, a.lse,
                        static_cast<const float*>(a.delta), static_cast<const int*>(a.cnt),
-                       static_cast<const int*>(a.off), static_cast<const int*>(a.list), a.cu_q,
-                       a.cu_k, a.batch, a.heads, a.kv_heads, a.nb_max, scale_log2, a.scale,
-                       a.dk, a.dv);
+                       static_cast<const int*>(a.off), static_cast<const int2*>(a.list), a.cu_k,
+                       a.heads, a.kv_heads, a.nb_max, scale_log2, a.scale, a.dk, a.dv);
 }
 
 }  // namespace
@@ -461,7 +466,7 @@ size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel,
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t n_slots = size_t(batch) * kv_heads * nb_max;
   return up(size_t(rows_total) * heads * sizeof(float)) + 3 * up(n_slots * sizeof(int)) +
-         up(size_t(rows_total) * kv_heads * k_sel * sizeof(int));
+         up(size_t(rows_total) * kv_heads * k_sel * sizeof(int2));
 }
 
 void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a) {
@@ -476,7 +481,7 @@ void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a) {
   p += up(n_slots * sizeof(int));
   a.cursor = reinterpret_cast<int*>(p);
   p += up(n_slots * sizeof(int));
-  a.list = reinterpret_cast<int*>(p);
+  a.list = reinterpret_cast<int2*>(p);
 }
 
 hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s) {

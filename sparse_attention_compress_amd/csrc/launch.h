@@ -237,7 +237,7 @@ struct SelectedBwdArgs {
   int* cnt;            // [batch, kv_heads, nb_max] rows listing each block
   int* off;            // list offsets
   int* cursor;         // fill cursors
-  int* list;           // [rows * kv_heads * k_sel] rows, grouped by block
+  int2* list;          // [rows * kv_heads * k_sel] (row, position), grouped by block
 };
 size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel, int batch,
                              int nb_max);

@@ -247,3 +247,29 @@ def test_two_stage_and_offload_checks():
     assert step(ctypes.byref(p), ctypes.byref(o), ws, need_o, None) == 1
     assert nsa.lib().nsa_offload_reset(ctypes.byref(o), 2, 2, None) == 1
     assert nsa.lib().nsa_offload_pool_bytes(2, 2, 64, 128, nsa.NSA_BF16) == 2 * 2 * 64 * 64 * 128 * 2
+
+
+def test_selected_bwd_checks():
+    """Argument checks of the selected-attention backward, all taken on the host
+    before any launch (fake device addresses are never dereferenced)."""
+    f = nsa.lib().nsa_selected_attn_bwd
+    P = 0x1000
+    need = nsa.selected_attn_bwd_workspace_size(2, 100, 4096, 16, 2, 16)
+    assert need > 0
+    assert nsa.selected_attn_bwd_workspace_size(0, 100, 4096, 16, 2, 16) == 0
+
+    def call(dtype=nsa.NSA_BF16, k_sel=16, cu_q=P, heads=16, kv=2, hd=128, block=64, ws=P,
+             nbytes=None, dk=P):
+        return f(P, P, P, P, P, P, dtype, P, k_sel, cu_q, P, 2, 100, 4096, heads, kv, hd, block,
+                 0.0, P, dk, P, ws, need if nbytes is None else nbytes, None)
+    assert call(dtype=nsa.NSA_F32) == 2          # bfloat16 only
+    assert call(k_sel=65) == 2                   # above the prefill top-k limit
+    assert call(k_sel=0) == 2
+    assert call(cu_q=None) == 1                  # prefill rows only
+    assert call(heads=12, kv=5) == 2             # group size
+    assert call(hd=64) == 2
+    assert call(block=32) == 2
+    assert call(nbytes=need - 1) == 3            # workspace too small
+    assert call(ws=None) == 3
+    assert call(dk=P + 4) == 1                   # gradients must be 16-byte aligned
+    assert call(dk=None) == 1

@@ -366,15 +366,62 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       av[i][e] = 0.f;
     }
   const int first = off[slot];
-  // two listed rows (with their positions) per pair of barriers
+  // Two listed rows (with their positions) per pair of barriers; the next
+  // pair's q and dO chunks, normalisers and deltas are loaded into registers
+  // while the current pair is computed.  Chunk c of a pair: row c / (16 G),
+  // head (c % (16 G)) / 16, dims 8 (c % 16) .. +7.
+  constexpr int kPer = (2 * G * 16 + kBwdThreads - 1) / kBwdThreads;
+  uint4 pq[kPer], pd[kPer];
+  float plse = 0.f, pdel = 0.f;
+  int2 n0 = make_int2(0, -1), n1 = make_int2(0, -1);
+  auto prefetch = [&](int e) {
+    n0 = list[first + e];
+    n1 = e + 1 < e_end ? list[first + e + 1] : n0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + kBwdThreads * i;
+      if (c < 2 * G * 16) {
+        const int rr = c / (G * 16), cc = c % (G * 16);
+        const size_t hrow = (size_t(rr ? n1.x : n0.x) * heads + size_t(g) * G + (cc >> 4)) * kHeadDim + 8 * (cc & 15);
+        pq[i] = ld16(q + hrow);
+        pd[i] = ld16(dout + hrow);
+      }
+    }
+    if (tid < 2 * G) {
+      const size_t hh = size_t(tid < G ? n0.x : n1.x) * heads + size_t(g) * G + (tid % G);
+      plse = lse[hh];
+      pdel = delta[hh];
+    }
+  };
+  if (e_begin < e_end) prefetch(e_begin);
   for (int e0 = e_begin; e0 < e_end; e0 += 2) {
     const bool two = e0 + 1 < e_end;  // uniform
-    const int2 r0 = list[first + e0];
-    const int2 r1 = two ? list[first + e0 + 1] : r0;
+    const int2 r0 = n0, r1 = n1;
     __syncthreads();  // the previous rows' LDS is no longer read
-    stage_row<G>(R[0], q, dout, lse, delta, size_t(r0.x) * heads + size_t(g) * G);
-    if (two) stage_row<G>(R[1], q, dout, lse, delta, size_t(r1.x) * heads + size_t(g) * G);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + kBwdThreads * i;
+      if (c < 2 * G * 16) {
+        const int rr = c / (G * 16), cc = c % (G * 16);
+        float* qd = &R[rr].q[cc >> 4][8 * (cc & 15)];
+        float* dd = &R[rr].d[cc >> 4][8 * (cc & 15)];
+        const uint32_t qw[4] = {pq[i].x, pq[i].y, pq[i].z, pq[i].w};
+        const uint32_t dw[4] = {pd[i].x, pd[i].y, pd[i].z, pd[i].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          qd[2 * w] = bf16lo(qw[w]);
+          qd[2 * w + 1] = bf16hi(qw[w]);
+          dd[2 * w] = bf16lo(dw[w]);
+          dd[2 * w + 1] = bf16hi(dw[w]);
+        }
+      }
+    }
+    if (tid < 2 * G) {
+      R[tid / G].lse2[tid % G] = plse * kLog2e;
+      R[tid / G].delta[tid % G] = pdel;
+    }
     __syncthreads();
+    if (e0 + 2 < e_end) prefetch(e0 + 2);
     for (int rr = 0; rr < (two ? 2 : 1); ++rr) {
       const RowLds<G>& Rr = R[rr];
       const int t = rr ? r1.y : r0.y;

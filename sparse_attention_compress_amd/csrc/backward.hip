@@ -423,6 +423,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     __syncthreads();
     if (e0 + 2 < e_end) prefetch(e0 + 2);
     for (int rr = 0; rr < (two ? 2 : 1); ++rr) {
+      // An empty register barrier on the packed key tile: its bf16 -> fp32
+      // conversions then stay next to their uses instead of being hoisted out
+      // of the row loop as 64 more live registers (167 instead of 189 VGPRs,
+      // three waves per SIMD instead of two).  It emits no instruction.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        asm volatile("" : "+v"(s.k[i].x), "+v"(s.k[i].y), "+v"(s.k[i].z), "+v"(s.k[i].w));
+        asm volatile("" : "+v"(s.v[i].x), "+v"(s.v[i].y), "+v"(s.v[i].z), "+v"(s.v[i].w));
+      }
       const RowLds<G>& Rr = R[rr];
       const int t = rr ? r1.y : r0.y;
       bool valid[4];

@@ -265,50 +265,56 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
   const size_t head0 = size_t(row) * heads + size_t(g) * G;
   stage_row<G>(R, q, dout, lse, delta, head0);
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   __syncthreads();
   const int* irow = indices + (size_t(row) * kv_heads + g) * k_sel;
-  for (int pl = 0; pl < k_sel; ++pl) {
-    const int id = irow[pl];
-    if (t < 0 || t >= len || id < 0 || id > t / kBlock) continue;  // uniform
-    bool valid[4];
-    size_t off[4];
+  // at most 8 heads' accumulators at a time: a 16-head group takes two passes
+  // over the blocks (the second mostly from L2) instead of one wave per SIMD
+  constexpr int HG = G > 8 ? 8 : G;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = kBlock * id + 4 * tg + i;
-      valid[i] = tok <= t;
-      off[i] = (size_t(kstart + min(tok, t)) * kv_heads + g) * kHeadDim + 8 * dp;
+  for (int h0 = 0; h0 < G; h0 += HG) {
+    float acc[HG][8];
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int pl = 0; pl < k_sel; ++pl) {
+      const int id = irow[pl];
+      if (t < 0 || t >= len || id < 0 || id > t / kBlock) continue;  // uniform
+      bool valid[4];
+      size_t off[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = kBlock * id + 4 * tg + i;
+        valid[i] = tok <= t;
+        off[i] = (size_t(kstart + min(tok, t)) * kv_heads + g) * kHeadDim + 8 * dp;
+      }
+      KeyTile s;
+      load_tile(k, v, off, valid, s);
+#pragma unroll
+      for (int h = 0; h < HG; ++h) {
+        float q8[8], d8[8], p[4], ds[4];
+        head_slice<G>(R, h0 + h, dp, q8, d8);
+        probs4<G>(R, s, h0 + h, q8, d8, valid, scale_log2, p, ds);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ds[i], bf16_at(s.k[i], e), acc[h][e]);
+      }
     }
-    KeyTile s;
-    load_tile(k, v, off, valid, s);
+    // sum over the token groups: the 4 DPP rows of the wave, then the 4 waves
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float q8[8], d8[8], p[4], ds[4];
-      head_slice<G>(R, h, dp, q8, d8);
-      probs4<G>(R, s, h, q8, d8, valid, scale_log2, p, ds);
+    for (int h = 0; h < HG; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int e = 0; e < 8; ++e) {
+        const float x = cross16(acc[h][e], OpSum());
+        acc[h][e] = cross32(x, OpSum());
+      }
+    if ((tid & 63) < 16) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ds[i], bf16_at(s.k[i], e), acc[h][e]);
+      for (int h = 0; h < HG; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red_s[wave][h0 + h][8 * dp + e] = acc[h][e];
     }
-  }
-  // sum over the token groups: the 4 DPP rows of the wave, then the 4 waves
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = cross16(acc[h][e], OpSum());
-      acc[h][e] = cross32(x, OpSum());
-    }
-  if ((tid & 63) < 16) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red_s[wave][h][8 * dp + e] = acc[h][e];
   }
   __syncthreads();
 #pragma unroll

@@ -273,8 +273,9 @@ __global__ __launch_bounds__(256) void selected_attn_valu_kernel(
 
   const int n_split = SPLIT ? int(gridDim.x) : 1;
 #pragma unroll
-  for (int it = 0; it < G * D / 256; ++it) {
+  for (int it = 0; it < (G * D + 255) / 256; ++it) {
     const int i = tid + 256 * it;
+    if (i >= G * D) break;  // G = 1: 128 merge items for 256 threads
     const int h = i / D, d = i % D;
     float mw[4], M = -INFINITY;
 #pragma unroll

@@ -252,3 +252,92 @@ def test_blockmask_attention_matches_masked_sdpa(causal, density):
         np.testing.assert_allclose(got, dense, atol=1e-12)
     if density == 0.0:
         assert np.all(got == 0.0)
+
+
+# ----------------------------------------------------------------------------- three-branch selection, planted
+
+def _planted_three_branch_case():
+    """Rows t >= 1024 of a sequence in which, for each KV group g, a run of 16
+    consecutive blocks (the past run) holds keys with a large component along
+    the group's own axis e_g, and every query head of the group has a large
+    component along e_g too.  The compressed windows inside the run then take
+    almost all of the group's compressed-attention mass (logit gap about 11
+    against noise of about 0.3), the half-overlapping windows at the run's two
+    ends lie about e^-5.6 below them, and the rest sit at noise level, so the
+    top-16 blocks of the group are exactly the run.  A second, stronger run lies
+    after the query rows (in the future): it is invisible to every checked row,
+    and a selection that scored invisible windows would pick it instead."""
+    rng = np.random.default_rng(20260)
+    L, H, H_kv, D = 3000, 8, 2, 32
+    G = H // H_kv
+    a = b = 8.0
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, H_kv, D))
+    v = rng.standard_normal((L, H_kv, D))
+    runs = {0: 2, 1: 0}              # first block of each group's past run (ends by token 1151)
+    future = {0: 39, 1: 39}          # first block of the future run (tokens 2496 ..)
+    for g in range(H_kv):
+        q[:, g * G:(g + 1) * G, g] += a
+        p0 = 64 * runs[g]
+        k[p0:p0 + 16 * 64, g, g] += b
+        f0 = 64 * future[g]
+        k[f0:f0 + 6 * 64, g, g] += 2 * b
+    rows = [1151, 1500, 2047, 2367, 2368, 2400, 2495]   # every past-run window visible
+    expect = {g: list(range(runs[g], runs[g] + 16)) for g in range(H_kv)}
+    return q, k, v, rows, expect, G
+
+
+def _planted_pin_holds(prefill_rows):
+    q, k, v, rows, expect, G = _planted_three_branch_case()
+    L, H, D = q.shape
+    g1 = np.zeros((L, H, 3))
+    g1[:, :, 1] = 1.0
+    res = prefill_rows(q, k, v, g1, rows, topk=16, window=512)
+    scale = 1 / math.sqrt(D)
+    for i, t in enumerate(rows):
+        for g in expect:
+            if res["indices"][i, g].tolist() != expect[g]:
+                return False
+        # o_sel against torch SDPA with the token mask written out from the runs
+        mask = np.zeros((H, L), dtype=bool)
+        for h in range(H):
+            for blk in expect[h // G]:
+                lo, hi = 64 * blk, min(64 * blk + 64, t + 1)
+                mask[h, lo:hi] = True
+        dense = _sdpa(q[t], _expand(k, G), _expand(v, G), mask, scale)
+        if not np.allclose(res["o_sel"][i], dense, rtol=1e-12, atol=1e-12):
+            return False
+        if not np.array_equal(res["out"][i], res["o_sel"][i]):
+            return False
+    return True
+
+
+def test_three_branch_selection_planted_rows_past_1024():
+    """Rows t >= 1024, where 16 blocks no longer cover every causal block: the
+    selection inside the three-branch oracle must return exactly the planted run
+    of each KV group, and the selected branch must equal SDPA over those blocks
+    (DeepSeek NSA with Triton, section 1.1: the selected branch ranks blocks by
+    the group's compressed-attention probabilities; no forced blocks)."""
+    assert _planted_pin_holds(oracle.nsa_prefill_rows)
+
+
+@pytest.mark.parametrize("mutation", ["n_local_16", "n_init_1", "topk_15", "invisible_windows"])
+def test_three_branch_planted_pin_catches_mutations(mutation, monkeypatch):
+    """Plausible mistakes planted in a patched copy of the oracle's selection or
+    scoring must make the planted pin fail."""
+    import oracle.nsa as onsa
+    real_select = onsa.select_blocks
+    if mutation == "n_local_16":
+        monkeypatch.setattr(onsa, "select_blocks",
+                            lambda s, t, nb, k, ni, nl, blk: real_select(s, t, nb, k, ni, 16, blk))
+    elif mutation == "n_init_1":
+        monkeypatch.setattr(onsa, "select_blocks",
+                            lambda s, t, nb, k, ni, nl, blk: real_select(s, t, nb, k, 1, nl, blk))
+    elif mutation == "topk_15":
+        def sel15(s, t, nb, k, ni, nl, blk):
+            out = real_select(s, t, nb, k - 1, ni, nl, blk)
+            return np.concatenate([out, [-1]]).astype(np.int32)
+        monkeypatch.setattr(onsa, "select_blocks", sel15)
+    else:  # invisible windows scored
+        monkeypatch.setattr(onsa, "window_visible", lambda c, t, kernel, stride: True)
+    assert not _planted_pin_holds(onsa.nsa_prefill_rows)

@@ -66,16 +66,20 @@ def parse():
     ap.add_argument("--seq", type=int, default=16384,
                     help="prefill-blockmask: tokens per sequence (the pages' table: 1024, 4096, 16384)")
     ap.add_argument("--causal", action="store_true", help="prefill-blockmask: lower triangle only")
-    ap.add_argument("--workload", choices=["decode", "decode-long", "decode-offload",
+    ap.add_argument("--workload", choices=["decode", "decode-long", "decode-tiny", "decode-offload",
                                            "prefill-selected", "prefill-nsa", "prefill-blockmask",
                                            "prefill-selected-bwd"],
                     default="decode",
                     help="decode: the headline NOSA-1B-shaped decode (default); decode-long: "
-                         "CIS-weighted decode of 4 x 131072 tokens; prefill-selected: "
+                         "CIS-weighted decode of 4 x 131072 tokens; decode-tiny: the float32 "
+                         "decode of one 4096-token sequence; prefill-selected: "
                          "selected-block attention prefill with given indices (batch 8 x 16384); "
                          "prefill-nsa: the three-branch prefill (65536 tokens, 64 heads); "
                          "prefill-selected-bwd: the gradient of the selected-block attention "
                          "for the prefill-selected batch")
+    ap.add_argument("--trace-stats", metavar="CSV", default=None,
+                    help="print per-kernel duration statistics (count, mean, median, p10, p90, "
+                         "min, max in microseconds) of a rocprofv3 kernel-trace CSV and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with three streaming kernels (fp32 negation) that read and "
                          "write 256 MiB each, the reference dispatch that scales the HBM "
@@ -84,8 +88,11 @@ def parse():
 
 
 COPY_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "select_attn_decode_nosa1b_counters.md")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+TRAFFIC_FILES = {  # counter summaries of the select-and-attend kernel, per decode workload
+    "nosa1b_decode_b8_L8k-32k": os.path.join(PROFILES, "select_attn_decode_nosa1b_counters.md"),
+    "cis_decode_b4_L131072": os.path.join(PROFILES, "select_attn_decode_cis_b4_L131072_counters.md"),
+}
 ATTN_SOURCES = ["sparse_attention_compress_amd/csrc/attn.hip",
                 "sparse_attention_compress_amd/csrc/common.h",
                 "sparse_attention_compress_amd/csrc/select_core.h"]
@@ -108,15 +115,17 @@ def attn_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per selected-attention launch from the committed counter summary.
+def counter_traffic(path):
+    """HBM bytes per selected-attention launch from a committed counter summary.
 
     The summary holds FETCH_SIZE and WRITE_SIZE of the kernel, each scaled by what
     the same counter reads for a plain copy of known size, and the hash of the
     kernel sources it was taken with.  None when it is missing or the sources
     have changed since."""
+    if path is None:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             text = f.read()
     except OSError:
         return None
@@ -131,8 +140,61 @@ def counter_traffic():
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
+def trace_stats(path):
+    """Per-kernel duration statistics of a rocprofv3 kernel-trace CSV (the
+    `*_kernel_trace.csv` that `rocprofv3 --kernel-trace` writes)."""
+    import csv
+
+    import numpy as np
+    durs = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            durs.setdefault(name, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    out = []
+    for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        a = np.asarray(d)
+        out.append({"kernel": name[:120], "count": int(a.size), "mean_us": round(float(a.mean()), 3),
+                    "median_us": round(float(np.median(a)), 3),
+                    "p10_us": round(float(np.percentile(a, 10)), 3),
+                    "p90_us": round(float(np.percentile(a, 90)), 3),
+                    "min_us": round(float(a.min()), 3), "max_us": round(float(a.max()), 3)})
+    for r in out:
+        print(json.dumps(r))
+
+
+def host_cpu():
+    """Host facts the CPU baseline is reported with: the CPU model, the logical
+    CPUs of the machine and those this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def kernel_stats_us(pairs):
+    """mean, median, p10 and p90 (microseconds) of a list of (start, stop) events."""
+    import numpy as np
+    a = np.asarray([s.elapsed_time(e) for s, e in pairs]) * 1e3
+    return {"mean": round(float(a.mean()), 3), "median": round(float(np.median(a)), 3),
+            "p10": round(float(np.percentile(a, 10)), 3), "p90": round(float(np.percentile(a, 90)), 3)}
+
+
 def main():
     args = parse()
+    if args.trace_stats:
+        trace_stats(args.trace_stats)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but the library runs on one GPU only "
@@ -160,12 +222,16 @@ def main():
     if args.workload == "prefill-selected-bwd":
         selected_bwd_main(args, dev)
         return
-    if args.workload not in ("decode", "decode-long"):
+    if args.workload not in ("decode", "decode-long", "decode-tiny"):
         prefill_main(args, dev)
         return
     if args.workload == "decode-long":
         w = W.cis_decode()
         n_layers = args.layers or 12
+    elif args.workload == "decode-tiny":
+        w = W.tiny_decode()
+        # 2.1 MB of selected fp32 K/V per step: 128 buffers exceed the Infinity Cache
+        n_layers = args.layers or 128
     else:
         w = W.nosa1b_decode(pinned_32k=args.pinned_32k, batch=args.batch)
         # enough layer buffers that a rotation's selected K/V (4 MiB per sequence)
@@ -173,11 +239,12 @@ def main():
         n_layers = args.layers or max(2, -(-28 * 8 // args.batch))
     B, H, Hkv, D = w.batch, w.heads, w.kv_heads, w.head_dim
     lengths = list(w.lengths)
-    nc = [nsa.full_windows(L) for L in lengths]
+    nc = [nsa.window_count(L) for L in lengths]
     cu_k = nsa.cu_seqlens_of(lengths, dev)
     cu_c = nsa.cu_seqlens_of(nc, dev)
     max_len = max(lengths)
     kc_dt = torch.float32 if args.kc_dtype == "f32" else torch.bfloat16
+    dt_name = "f32" if w.dtype == torch.float32 else "bf16"
     print(f"[bench] workload {w.name} lengths={lengths} layers={n_layers}", file=sys.stderr, flush=True)
 
     layers = []
@@ -192,9 +259,9 @@ def main():
         out = torch.empty((B, H, D), dtype=w.dtype, device=dev)
         idx = torch.empty((B, Hkv, w.topk), dtype=torch.int32, device=dev)
         p = nsa.decode_params(q, k, v, kc, cu_k, cu_c, max_len, out, topk=w.topk, n_init=w.n_init,
-                              n_local=w.n_local, cis=cis, cis_pooled=cp, cis_weight=w.cis_weight,
-                              cis_values=w.cis_values, append_window=True, indices=idx,
-                              n_cand=args.n_cand)
+                              n_local=w.n_local, cis=cis, cis_pooled=cp if w.cis_select else None,
+                              cis_weight=w.cis_weight, cis_values=w.cis_values, append_window=True,
+                              indices=idx, n_cand=args.n_cand)
         layers.append(dict(q=q, k=k, v=v, cis=cis, kc=kc, cp=cp, out=out, idx=idx, p=p))
     torch.cuda.synchronize()
     ws = torch.zeros(nsa.decode_workspace_size(layers[0]["p"]), dtype=torch.uint8, device=dev)
@@ -210,25 +277,28 @@ def main():
     torch.cuda.synchronize()
     print("[bench] eager steps done; capturing graphs", file=sys.stderr, flush=True)
 
-    def capture(n):
+    # the timed steps continue the warm-up's rotation over the layer buffers, so
+    # the first timed step does not re-read what the last warm-up steps touched
+    def capture(n, start):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for i in range(n):
+            for i in range(start, start + n):
                 step(i)
         return g
 
+    n_warm = max(1, args.warmup)
     if args.eager:
-        def run(n):
+        def run(n, start):
             with torch.cuda.stream(stream):
-                for i in range(n):
+                for i in range(start, start + n):
                     step(i)
     else:
-        g_warm = capture(max(1, args.warmup))
-        g_timed = capture(args.steps)
+        g_warm = capture(n_warm, 0)
+        g_timed = capture(args.steps, n_warm)
         run = None
     torch.cuda.synchronize()
     if args.eager:
-        run(args.warmup)
+        run(n_warm, 0)
     else:
         g_warm.replay()
     torch.cuda.synchronize()
@@ -237,7 +307,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     if args.eager:
-        run(args.steps)
+        run(args.steps, n_warm)
     else:
         with torch.cuda.stream(stream):
             g_timed.replay()
@@ -279,6 +349,7 @@ def main():
             step(i)
     torch.cuda.synchronize()
     kern_us = {name: float(np.mean([a.elapsed_time(b) for a, b in evs[name]])) * 1e3 for name in kinds}
+    kern_stats = {name: kernel_stats_us(evs[name]) for name in kinds}
 
     # algorithmic bytes of one selected-attention launch (identical for every layer)
     idx0 = layers[0]["idx"].cpu().numpy()
@@ -288,7 +359,7 @@ def main():
             for blk in idx0[b_, g]:
                 if blk >= 0:
                     sel_tokens += min(64, L - 64 * int(blk))
-    elt = 2  # bf16
+    elt = 2 if w.dtype == torch.bfloat16 else 4
     G = H // Hkv
     if fused:
         # the selection's inputs: logits, chunk (max, sum) pairs, block CIS maxima
@@ -369,14 +440,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dt_name,
         "data": "synthetic (seeded N(0,1) Q/K/V, sigmoid(N(0,1)) CIS; no dataset)",
         "config": {
             "workload": w.name,
             "batch": B, "context_lengths": lengths, "heads": H, "kv_heads": Hkv, "head_dim": D,
             "compress_kernel": w.kernel, "compress_stride": w.stride, "block": w.block,
             "topk": w.topk, "forced_init_blocks": w.n_init, "forced_local_blocks": w.n_local,
-            "cis_fused": True, "cis_values": bool(w.cis_values), "compressed_key_dtype": args.kc_dtype,
+            "cis_fused": bool(w.cis_select), "cis_values": bool(w.cis_values),
+            "compressed_key_dtype": args.kc_dtype,
             "selection": (f"two-stage, {args.n_cand} candidates" if args.n_cand > 0 else
                           "one fused score"),
             "layer_buffers_rotated": nl, "step": "one layer, whole batch, HIP-graph replay",
@@ -384,22 +456,26 @@ def main():
         "roofline": {
             "kernel": ("select_attn_kernel (decode: block scores, top-k and attention over "
                        "the selected blocks, split over blocks)" if fused else
-                       "selected_attn_kernel (decode, split over selected blocks)"),
+                       "selected_attn_valu_kernel (decode, float32, split over selected blocks)"
+                       if w.dtype == torch.float32 else
+                       "selected_attn_mfma_kernel (decode, split over selected blocks)"),
             "bound": "hbm",
             "achieved": round(attn_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
             # the stored counters belong to the fused kernel on the 8K-32K batch
-            "traffic": (counter_traffic() if fused and args.n_cand == 0
-                        and w.name.startswith("nosa1b_decode_b8_L8k") else None),
+            "traffic": (counter_traffic(TRAFFIC_FILES.get(w.name)) if fused and args.n_cand == 0
+                        and args.kc_dtype == "f32" else None),
             "algorithmic_bytes_per_launch": attn_bytes,
             "mean_kernel_us": round(kern_us[attn_key], 3),
             "source_hash": attn_source_hash(),
         },
         "kernel_us": {k_: round(v_, 3) for k_, v_ in kern_us.items()},
+        "kernel_us_stats": kern_stats,
         "selected_attn_alone": {
-            "kernel": "selected_attn_mfma_kernel (nsa_selected_attn_fwd on the step's ids)",
+            "kernel": ("selected_attn_mfma_kernel" if w.dtype == torch.bfloat16 else
+                       "selected_attn_valu_kernel") + " (nsa_selected_attn_fwd on the step's ids)",
             "mean_kernel_us": round(sa_us, 3), "algorithmic_bytes_per_launch": sa_bytes,
             "achieved": round(sa_bytes / (sa_us * 1e-6) / 1e9, 1), "unit": "GB/s",
             "frac": round(sa_bytes / (sa_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -433,7 +509,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (with packed fp32 instructions)
+# The library is built without packed fp32 instructions, so one fp32 FMA per lane
+# per cycle: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s.
+FP32_VECTOR_UNPACKED_TFLOPS = 78.6
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -492,7 +571,7 @@ def offload_main(args, dev):
     w = W.nosa1b_decode()
     B, H, Hkv, D = w.batch, w.heads, w.kv_heads, w.head_dim
     lengths = list(w.lengths)
-    nc = [nsa.full_windows(L) for L in lengths]
+    nc = [nsa.window_count(L) for L in lengths]
     cu_k, cu_c = nsa.cu_seqlens_of(lengths, dev), nsa.cu_seqlens_of(nc, dev)
     max_len = max(lengths)
     nb_max = -(-max_len // 64)
@@ -729,7 +808,8 @@ def sampled_oracle_baseline(rows_fn, n_rows_total, tokens_total, seconds, what, 
     step_s = fixed + per_row * n_rows_total
     return {"value": round(tokens_total / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {n_rows_total} {what} (evenly strided), {spent:.1f} s on one host "
-                      f"thread, extrapolated to the whole step ({step_s:.4g} s)"}
+                      f"thread, extrapolated to the whole step ({step_s:.4g} s)",
+            **host_cpu()}
 
 
 def prefill_main(args, dev):
@@ -774,7 +854,7 @@ def prefill_main(args, dev):
         k, v = W.keys_values(w, dev)
         g = W.gates(w, dev)
         L = w.lengths[0]
-        nc = nsa.full_windows(L)
+        nc = nsa.window_count(L)
         cu = nsa.cu_seqlens_of(w.lengths, dev)
         cuc = nsa.cu_seqlens_of([nc], dev)
         kc = torch.empty((nc, w.kv_heads, D), dtype=torch.bfloat16, device=dev)
@@ -886,8 +966,11 @@ def selected_bwd_main(args, dev):
     """Backward of the selected attention over the prefill-selected batch: one
     step = the gradient (dq, dk, dv) of the whole batch from the forward's
     output, log-normaliser and a given upstream gradient; value = prefill tokens/s
-    of the backward.  The kernels run on the vector ALUs in fp32, so the roofline
-    is the algorithmic fp32 flops of the longer of the dq and dk/dv kernels."""
+    of the backward.  The kernels run on the vector ALUs in fp32 without packed
+    instructions, so the roofline is the algorithmic flops of the longer of the dq
+    and dk/dv kernels against the unpacked fp32 vector peak; the fraction of the
+    bf16 matrix-core peak (the ceiling of these bf16-input contractions) is
+    reported beside it."""
     import numpy as np
     import torch
 
@@ -955,9 +1038,10 @@ def selected_bwd_main(args, dev):
             "kernel": dominant,
             "bound": "alu",
             "achieved": round(tflops[dominant], 2),
-            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "peak": FP32_VECTOR_UNPACKED_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops[dominant] / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "frac": round(tflops[dominant] / FP32_VECTOR_UNPACKED_TFLOPS, 4),
+            "frac_of_bf16_mfma_peak": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(kern[dominant], 1),
@@ -1027,7 +1111,10 @@ def cpu_baseline(w, layer, lengths, args):
         "cores": 1,
         "kind": "oracle",
         "sample": f"layer 0 of the same workload, full batch of {w.batch} sequences, "
-                  f"{reps} decode step(s), {t_total:.1f} s on one host thread",
+                  f"{reps} decode step(s), {t_total:.1f} s on one host thread; every oracle "
+                  f"step pools the whole K (and CIS) cache into windows, where the GPU step "
+                  f"refreshes only the newest window",
+        **host_cpu(),
     }
     got_idx = layer["idx"].cpu().numpy()
     got = f64(layer["out"])

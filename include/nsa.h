@@ -130,6 +130,24 @@ typedef enum nsa_kernel_kind {
 nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
 
 /*
+ * nsa_window_count -- number of compressed windows of one sequence, the count a
+ * caller puts into cu_seqlens_c.
+ * [NOSA-1B source analysis part 3: the avg_pool1d consistency check (windows
+ *  that lie wholly inside the sequence) and the masked block load (a window
+ *  reaching past the end keeps only its valid tokens, divided by their count).]
+ *   tail_mode 0: full windows only, floor((length - kernel) / stride) + 1, and 0
+ *                when length < kernel (the default of every scoring path);
+ *   tail_mode 1: windows until every token is covered, the smallest n with
+ *                stride * (n - 1) + kernel >= length (1 when 0 < length <=
+ *                kernel, 0 when length == 0); the last ones are partial.
+ * The pooling entry points take the window count of each sequence from
+ * cu_seqlens_c, so the tail mode is chosen by building cu_seqlens_c from this
+ * function.  Returns -1 when length < 0, kernel < 1, stride < 1 or tail_mode is
+ * neither 0 nor 1.  Host function; touches no device state.
+ */
+int32_t nsa_window_count(int32_t length, int32_t kernel, int32_t stride, int32_t tail_mode);
+
+/*
  * nsa_compress_k -- mean-pool keys (or values) into compressed windows.
  * [NOSA-1B core components, component 1: CompressK, 32-token windows, stride 16,
  *  one mean per window.]

@@ -77,6 +77,7 @@ class PrefillParams(ctypes.Structure):
 _SIGS = {
     "nsa_last_error": (ctypes.c_char_p, []),
     "nsa_version": (c_i32, []),
+    "nsa_window_count": (c_i32, [c_i32, c_i32, c_i32, c_i32]),
     "nsa_profile_next_launch": (ctypes.c_int, [c_i32, c_vp, c_vp]),
     "nsa_compress_k": (ctypes.c_int, [c_vp, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_i32,
                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
@@ -184,8 +185,13 @@ def _workspace(nbytes: int, device, workspace=None):
 # ----------------------------------------------------------------------------- host helpers
 
 
-def full_windows(length: int, kernel: int = 32, stride: int = 16) -> int:
-    return 0 if length < kernel else (length - kernel) // stride + 1
+def window_count(length: int, kernel: int = 32, stride: int = 16, tail: bool = False) -> int:
+    """Window count of one sequence (nsa_window_count): full windows, or with
+    ``tail`` the windows that cover every token."""
+    n = lib().nsa_window_count(int(length), int(kernel), int(stride), int(bool(tail)))
+    if n < 0:
+        raise NsaError(1, f"nsa_window_count: invalid arguments ({length}, {kernel}, {stride})")
+    return n
 
 
 def cu_seqlens_of(lengths, device) -> torch.Tensor:

@@ -46,9 +46,6 @@ bool group_ok(int heads, int kv_heads) {
 constexpr int kMaxPrefillSel = 64;
 constexpr int kMaxDecodeSel = 64 * nsa::kMaxSplits;
 
-int full_windows(int len, int kernel, int stride) {
-  return len >= kernel ? (len - kernel) / stride + 1 : 0;
-}
 float scale_log2_of(float softmax_scale, int head_dim) {
   const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   return sc * nsa::kLog2eHost;
@@ -88,6 +85,14 @@ nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEve
 }
 
 int32_t nsa_version(void) { return 200; }
+
+int32_t nsa_window_count(int32_t length, int32_t kernel, int32_t stride, int32_t tail_mode) {
+  if (length < 0 || kernel < 1 || stride < 1 || (tail_mode != 0 && tail_mode != 1)) return -1;
+  if (length == 0) return 0;
+  if (tail_mode == 0) return length >= kernel ? (length - kernel) / stride + 1 : 0;
+  if (length <= kernel) return 1;
+  return (length - kernel + stride - 1) / stride + 1;
+}
 
 nsa_status nsa_compress_k(const void* x, nsa_dtype x_dtype, void* x_c, nsa_dtype xc_dtype,
                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_c, int32_t batch,
@@ -547,7 +552,7 @@ size_t nsa_compressed_attn_workspace_size(int32_t batch, int32_t rows_total, int
                                           int32_t heads, int32_t kv_heads, int32_t kernel,
                                           int32_t stride) {
   if (batch <= 0 || rows_total <= 0 || heads <= 0 || kv_heads <= 0 || kernel < 1 || stride < 1) return 0;
-  const int max_windows = full_windows(max_seqlen_k, kernel, stride);
+  const int max_windows = nsa_window_count(max_seqlen_k, kernel, stride, 0);
   return ((size_t(rows_total) * heads * sizeof(float) + 255) & ~size_t(255)) +
          ((nsa::transposed_bytes(batch, kv_heads, max_windows) + 255) & ~size_t(255));
 }
@@ -614,7 +619,7 @@ nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
-  a.max_windows = full_windows(max_seqlen_k, kernel, stride);
+  a.max_windows = nsa_window_count(max_seqlen_k, kernel, stride, 0);
   a.lse2 = static_cast<float*>(workspace);
   a.vct = reinterpret_cast<nsa::bf16_t*>(static_cast<char*>(workspace) +
                                          ((size_t(rows_total) * heads * sizeof(float) + 255) & ~size_t(255)));
@@ -713,7 +718,7 @@ PrefillLayout prefill_layout(const nsa_prefill_params* p) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t rows = size_t(p->rows_total), H = size_t(p->heads);
   L.nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
-  L.max_windows = full_windows(p->max_seqlen_k, p->kernel, p->stride);
+  L.max_windows = nsa_window_count(p->max_seqlen_k, p->kernel, p->stride, 0);
   size_t off = 0;
   L.lse2 = off;
   off += up(rows * H * sizeof(float));

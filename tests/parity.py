@@ -13,6 +13,7 @@ Gates (the stated tolerances of the method's outputs, and derived ones where non
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -25,6 +26,18 @@ BAND = 1e-3
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def report(*a):
+    """A line that must survive pytest's output capture (agreement rates, band
+    populations): written to the process's real stderr, and appended to the file
+    named by NSA_PARITY_REPORT when that variable is set."""
+    line = " ".join(str(x) for x in a)
+    print(line, file=sys.__stderr__, flush=True)
+    path = os.environ.get("NSA_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
 
 
 def np64(t: torch.Tensor) -> np.ndarray:

@@ -273,3 +273,26 @@ def test_selected_bwd_checks():
     assert call(ws=None) == 3
     assert call(dk=P + 4) == 1                   # gradients must be 16-byte aligned
     assert call(dk=None) == 1
+
+
+def test_window_count_export():
+    """nsa_window_count against the hand-derived window counts of the geometry
+    fixture, and against the oracle's count over a sweep of lengths and window
+    shapes, in both tail modes; invalid arguments give -1."""
+    import json
+
+    import oracle
+    L = nsa.lib()
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "window_geometry.json")))
+    for length, full, tail in fx["window_counts"]:
+        assert L.nsa_window_count(length, 32, 16, 0) == full, length
+        assert L.nsa_window_count(length, 32, 16, 1) == tail, length
+        assert nsa.window_count(length) == full
+        assert nsa.window_count(length, tail=True) == tail
+    for kernel, stride in ((32, 16), (8, 8), (5, 3), (1, 1), (64, 1)):
+        for length in list(range(0, 200)) + [4095, 4096, 4097, 65536, 131072]:
+            for tail in (0, 1):
+                assert L.nsa_window_count(length, kernel, stride, tail) == \
+                    oracle.n_windows(length, kernel, stride, bool(tail)), (length, kernel, stride, tail)
+    for args in ((-1, 32, 16, 0), (10, 0, 16, 0), (10, 32, 0, 0), (10, 32, 16, 2)):
+        assert L.nsa_window_count(*args) == -1

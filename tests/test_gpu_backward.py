@@ -82,11 +82,13 @@ def _compare(d, dq, dk, dv, tag):
 
 
 @pytest.mark.parametrize("H,H_kv,lengths", [(16, 2, [500, 900]), (16, 1, [300, 420]),
-                                            (4, 4, [700, 90])])
+                                            (4, 4, [700, 90]), (8, 4, [500, 900]),
+                                            (8, 2, [300, 420])])
 def test_selected_bwd_matches_oracle(H, H_kv, lengths):
     """Every row of a ragged batch (several 64-token blocks and a ragged tail;
-    rows early in a sequence list fewer than k blocks), GQA groups of 8, 16 and
-    1 query heads."""
+    rows early in a sequence list fewer than k blocks), GQA groups of 8, 16, 1,
+    2 and 4 query heads (the last two: chunks of 2*G*16 rows that are not a
+    multiple of 256, and head counts below one 8-head pass)."""
     w = dataclasses.replace(W.scaled(W.selected_prefill(), lengths), heads=H, kv_heads=H_kv)
     d = _inputs(w)
     log(f"selected bwd H={H} H_kv={H_kv} lengths={lengths}")

@@ -77,3 +77,31 @@ def test_blockmask_benchmark_shape_sampled_rows(seq):
             ref = oracle.blockmask_attention_row(np64(q[s0 + t]), kn, vn, mn[b], t, 64,
                                                  1 / math.sqrt(128))
             assert_close(f"blockmask[{b},{t}]", np64(out[s0 + t]), ref, atol=2e-2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blockmask_benchmark_shape_16k_sampled_rows(causal):
+    """The pages' largest benchmark shape, 8 x 16384 tokens (256 blocks per mask
+    row, so the mask-row scan runs over four 64-block chunks), on sampled rows
+    of every sequence, including rows at the chunk edges."""
+    seq = 16384
+    w = W.blockmask_prefill(seq)
+    q = W.prefill_query(w, DEV)
+    k, v = W.keys_values(w, DEV)
+    mask = W.block_mask(w, DEV)
+    cu_k = cu(w.lengths)
+    out = torch.full_like(q, float("nan"))
+    log(f"blockmask {w.name} causal={causal}")
+    nsa.nsa_blockmask_attn_fwd(q, k, v, mask, cu_k, seq, out, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    mn = mask.cpu().numpy()
+    ts = [0, 63, 64, 4095, 4096, 4097, 8191, 8192, 8209, 12345, 16320, 16383]
+    for b in range(w.batch):
+        s0 = b * seq
+        kn, vn = np64(k[s0:s0 + seq]), np64(v[s0:s0 + seq])
+        for t in ts[b % 3::3] + [ts[(5 * b) % len(ts)]]:
+            ref = oracle.blockmask_attention_row(np64(q[s0 + t]), kn, vn, mn[b], t, 64,
+                                                 1 / math.sqrt(128), causal)
+            assert_close(f"blockmask16k[{b},{t},c={int(causal)}]", np64(out[s0 + t]), ref,
+                         atol=2e-2)

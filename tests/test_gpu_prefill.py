@@ -14,7 +14,7 @@ import torch
 import oracle
 import sparse_attention_compress_amd as nsa
 from gen import workloads as W
-from parity import assert_close, check_index_sets, cu, log, np64
+from parity import assert_close, check_index_sets, cu, log, np64, report
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -121,9 +121,12 @@ def test_window_branch(window):
         s0 += L
 
 
-def _check_step(w, d, rows_sample, out, idx, bs, min_identical):
+def _check_step(name, w, d, rows_sample, out, idx, bs, min_identical):
     """Oracle rows vs the GPU step: index sets by the tie-band rule, outputs on
-    rows whose index sets all agree."""
+    rows whose index sets all agree.  On N(0,1) inputs many rows carry blocks
+    within the 1e-3 band of their 16th score, so a few rows may legitimately
+    differ; measured agreement is 0.875-1.0 of the sampled rows, and the floor
+    is 0.8.  The planted-run test below requires every row to agree."""
     q, k, v, g = np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"])
     out, idx = np64(out), idx.cpu().numpy()
     L = w.lengths[0]
@@ -141,7 +144,8 @@ def _check_step(w, d, rows_sample, out, idx, bs, min_identical):
         if all_same:
             identical_rows += 1
             same_rows.append(i)
-    log(f"index sets identical on {identical_rows}/{len(rows_sample)} rows (max tie-band population {band})")
+    report(f"[{name}] index sets identical on {identical_rows}/{len(rows_sample)} rows "
+           f"(max tie-band population {band})")
     assert identical_rows >= min_identical * len(rows_sample)
     sel = np.array(same_rows)
     got = out[[rows_sample[i] for i in sel]]
@@ -166,7 +170,7 @@ def test_prefill_step_small(q_scale):
     nsa.nsa_prefill_step(p)
     torch.cuda.synchronize()
     rows_sample = _rows_of(L, 40, None)
-    _check_step(w, d, rows_sample, out, idx, bs, 0.3)
+    _check_step(f"prefill_small[q_scale={q_scale}]", w, d, rows_sample, out, idx, bs, 0.8)
 
 
 def test_prefill_step_full_size_sampled_rows():
@@ -185,7 +189,7 @@ def test_prefill_step_full_size_sampled_rows():
     assert torch.isfinite(out.float()).all()
     rows_sample = [0, 31, 32, 511, 512, 1023, 1024, 4095, 4096, 20000, 32767, 32768, 50001,
                    65472, 65534, 65535] + [int(x) for x in np.linspace(100, 65000, 8)]
-    _check_step(w, d, sorted(set(rows_sample)), out, idx, None, 0.3)
+    _check_step("prefill_full", w, d, sorted(set(rows_sample)), out, idx, None, 0.8)
 
 
 def test_prefill_step_ragged_batch_query_tails():
@@ -244,8 +248,8 @@ def test_prefill_step_ragged_batch_query_tails():
                 identical += 1
                 assert_close(f"out[b={b},t={t}]", outn[r], ref["out"][i], atol=2e-2)
         row0 += n
-    log(f"index sets identical on {identical}/{checked} rows")
-    assert identical >= 0.3 * checked
+    report(f"[prefill_query_tails] index sets identical on {identical}/{checked} rows")
+    assert identical >= 0.8 * checked
 
 
 @pytest.mark.parametrize("heads,kv_heads", [(32, 4), (16, 4)])
@@ -261,4 +265,58 @@ def test_prefill_step_group_sizes(heads, kv_heads):
     log(f"prefill step L={L} heads={heads} kv_heads={kv_heads}")
     nsa.nsa_prefill_step(p)
     torch.cuda.synchronize()
-    _check_step(w, d, _rows_of(L, 24, None), out, idx, None, 0.3)
+    _check_step(f"prefill_groups[{heads},{kv_heads}]", w, d, _rows_of(L, 24, None), out, idx, None,
+                0.8)
+
+
+def _plant_runs(d, w, runs, a=11.5, b=11.5):
+    """Give every query head of KV group g a component `a` along axis g and the
+    keys of blocks runs[g] .. runs[g]+15 of group g a component `b` along the same
+    axis, then re-pool K_c.  The windows inside a run then lead the group's
+    compressed attention by a logit gap of a*b/sqrt(128), about 11.7, the two
+    half-overlapping windows at its ends lie e^-5.8 below them, and everything
+    else sits at noise level (logit spread about 0.3): for every row that sees
+    the whole run, the top-16 blocks of the group are exactly the run, with a
+    margin of about 0.25 in block score against the 1e-3 tie band."""
+    G = w.heads // w.kv_heads
+    q = d["q"].float()
+    k = d["k"].float()
+    for g, r0 in runs.items():
+        q[:, g * G:(g + 1) * G, g] += a
+        k[64 * r0:64 * (r0 + 16), g, g] += b
+    d["q"], d["k"] = q.to(BF16).contiguous(), k.to(BF16).contiguous()
+    nsa.nsa_compress_k(d["k"], d["kc"], d["cu_k"], d["cu_c"], max(d["nc"]))
+
+
+@pytest.mark.parametrize("L", [8192, 65536])
+def test_prefill_step_planted_runs_select_exactly(L):
+    """The three-branch recipe with a planted 16-block run per KV group: on every
+    sampled row that sees its whole run, the GPU's index set of every group must
+    equal the run and the oracle's set exactly, and the outputs must agree."""
+    w = W.nsa_prefill() if L == 65536 else W.scaled(W.nsa_prefill(), [L])
+    d = _inputs(w)
+    runs = {g: 2 + 20 * g for g in range(w.kv_heads)}
+    _plant_runs(d, w, runs)
+    out = torch.full((L, w.heads, 128), float("nan"), dtype=BF16, device=DEV)
+    idx = torch.full((L, w.kv_heads, w.topk), -7, dtype=torch.int32, device=DEV)
+    p = nsa.prefill_params(d["q"], d["k"], d["v"], d["kc"], d["vc"], d["g"], d["cu_k"], d["cu_k"],
+                           d["cu_c"], L, out, topk=w.topk, window=w.window, indices=idx)
+    log(f"prefill step with planted runs L={L}")
+    nsa.nsa_prefill_step(p)
+    torch.cuda.synchronize()
+    # the last window of a run ending at block r0+15 covers tokens up to 64*(r0+16)-1
+    t0 = 64 * (max(runs.values()) + 16) - 1
+    rows = sorted({t0, t0 + 1, 8191, L - 1, L - 64, L - 65} |
+                  {int(x) for x in np.linspace(t0, L - 1, 14).round()})
+    rows = [t for t in rows if t0 <= t < L]
+    got_idx = idx.cpu().numpy()
+    q, k, v, g = np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"])
+    ref = oracle.nsa_prefill_rows(q, k, v, g, rows, topk=w.topk, window=w.window)
+    for i, t in enumerate(rows):
+        for kv, r0 in runs.items():
+            want = list(range(r0, r0 + 16))
+            assert ref["indices"][i, kv].tolist() == want, ("oracle", t, kv)
+            assert got_idx[t, kv].tolist() == want, ("gpu", t, kv, got_idx[t, kv].tolist())
+    report(f"[prefill_planted L={L}] index sets identical on {len(rows)}/{len(rows)} rows "
+           f"(every KV group equal to its planted run)")
+    assert_close(f"prefill_planted.out[L={L}]", np64(out)[rows], ref["out"], atol=2e-2)

@@ -340,6 +340,24 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
                            hipStream_t stream);
 
 /*
+ * nsa_decode_step_noalloc -- nsa_decode_step for callers that cannot allocate
+ * device memory (code under stream capture, serving loops and harnesses that
+ * forbid allocation).  Same parameters, kernels and outputs as nsa_decode_step;
+ * the workspace is a fixed device array inside the library instead of a caller
+ * buffer: nsa_decode_noalloc_scratch_bytes() bytes (32 MiB) per GPU, held from
+ * the library's load until the process ends.  Its device address is looked up
+ * once per device on the first call there (the device of `stream`, or the
+ * current one for the NULL stream).  The call allocates nothing.  Steps whose
+ * workspace (nsa_decode_workspace_size) exceeds the scratch return
+ * NSA_ERR_WORKSPACE before launching.  Every call on one GPU uses the same
+ * scratch: calls that can overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  No part of the scratch
+ * needs clearing between calls (the step writes every byte it reads).
+ */
+size_t nsa_decode_noalloc_scratch_bytes(void);
+nsa_status nsa_decode_step_noalloc(const nsa_decode_params* p, hipStream_t stream);
+
+/*
  * KV offload for decode: the K/V cache stays in host memory and each step moves
  * to the GPU only the selected blocks it does not already hold.
  * [NOSA-1B core components: the core idea (the whole KV cache offloaded to CPU

@@ -100,6 +100,8 @@ _SIGS = {
                                              c_sz, c_vp]),
     "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
     "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
+    "nsa_decode_noalloc_scratch_bytes": (c_sz, []),
+    "nsa_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp]),
     "nsa_offload_pool_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, ctypes.c_int]),
     "nsa_offload_reset": (ctypes.c_int, [ctypes.POINTER(OffloadState), c_i32, c_i32, c_vp]),
     "nsa_decode_offload_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams),
@@ -338,6 +340,16 @@ def nsa_decode_step(params: DecodeParams, workspace=None, device=None, stream=No
     need = decode_workspace_size(params)
     ws, nbytes = _workspace(need, device or torch.device("cuda"), workspace)
     _check(lib().nsa_decode_step(ctypes.byref(params), _ptr(ws), nbytes, _stream(stream)))
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    return lib().nsa_decode_noalloc_scratch_bytes()
+
+
+def nsa_decode_step_noalloc(params: DecodeParams, stream=None):
+    """Enqueue one decode step whose workspace is the library's fixed per-GPU
+    scratch (no allocation by the library or by this binding)."""
+    _check(lib().nsa_decode_step_noalloc(ctypes.byref(params), _stream(stream)))
 
 
 def offload_state(batch, kv_heads, pool_slots, nb_cap, device, head_dim=128, dtype=torch.bfloat16,

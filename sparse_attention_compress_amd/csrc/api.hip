@@ -68,6 +68,11 @@ nsa_status check_geometry(const char* fn, int head_dim, int kernel, int stride, 
 
 nsa::ProfSlot& nsa::prof_slot(int kind) { return g_prof[kind]; }
 
+namespace nsa {
+// The nsa_last_error text for entry points defined in other sources.
+nsa_status set_error(nsa_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace nsa
+
 extern "C" {
 
 const char* nsa_last_error(void) { return g_err.c_str(); }

@@ -50,6 +50,12 @@ R16 backward of the selected attention (no CIS): the exact gradient of the
    with Triton, introduction and section 2.3, the kernels wrapped as a
    trainable module) but print no backward, so the gradient is the plain one.
    Keys reached through no row get zero gradient.
+R17 backward of the compressed and sliding-window branches: the exact gradient
+   of each branch's output for a given upstream gradient; the compressed
+   branch's key and value gradients reach K and V through the transpose of the
+   window mean (each window's gradient spread over its valid tokens divided by
+   their count).  The selection is a discrete choice and passes no gradient; the
+   gates receive dO . o_branch.
 R5b two-stage selection (optional): the n_cand best free blocks by the
    compressed-attention block score are the candidates; the k - |forced| best
    candidates by the pooled-CIS block score are chosen (ties to the lower index
@@ -333,6 +339,78 @@ def selected_attention_bwd(q, k, v, idx, d_out, cu_q, cu_k, block: int, scale: f
     return dq, dk, dv
 
 
+def _attend_grad(q_h, K, V, scale: float, d_out_h):
+    """Gradient of softmax(scale K q) V with respect to q, K and V for the upstream
+    gradient d_out_h: returns (dq, dK, dV); empty key sets give zeros."""
+    if K.shape[0] == 0:
+        return np.zeros_like(q_h), np.zeros_like(K), np.zeros_like(V)
+    p = softmax(K @ q_h * scale)
+    o = p @ V
+    ds = p * (V @ d_out_h - d_out_h @ o)
+    return scale * (ds @ K), scale * np.outer(ds, q_h), np.outer(p, d_out_h)
+
+
+def compressed_attention_row_grad(q, kc_seq, vc_seq, t: int, kernel: int, stride: int,
+                                  scale: float, d_out, dkc, dvc) -> np.ndarray:
+    """Gradient of compressed_attention_row (R17) for query position t: adds the
+    row's contributions to dkc, dvc ([n_c, H_kv, D] float64, in place) and
+    returns dq [H, D].  The keys are the windows visible to t (R2)."""
+    q = np.asarray(q, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    kc_seq = np.asarray(kc_seq, dtype=np.float64)
+    vc_seq = np.asarray(vc_seq, dtype=np.float64)
+    H = q.shape[0]
+    n_c, H_kv = kc_seq.shape[0], kc_seq.shape[1]
+    G = H // H_kv
+    vis = [c for c in range(n_c) if window_visible(c, t, kernel, stride)]
+    dq = np.zeros(q.shape)
+    for h in range(H):
+        g = h // G
+        dq[h], dk_, dv_ = _attend_grad(q[h], kc_seq[vis, g], vc_seq[vis, g], scale, d_out[h])
+        dkc[vis, g] += dk_
+        dvc[vis, g] += dv_
+    return dq
+
+
+def window_attention_row_grad(q, k_seq, v_seq, t: int, window: int, scale: float, d_out, dk,
+                              dv) -> np.ndarray:
+    """Gradient of window_attention_row (R9, R17) for query position t: keys
+    max(0, t-window+1) .. t; adds to dk, dv in place and returns dq [H, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    k_seq = np.asarray(k_seq, dtype=np.float64)
+    v_seq = np.asarray(v_seq, dtype=np.float64)
+    H = q.shape[0]
+    G = H // k_seq.shape[1]
+    J = list(range(max(0, t - window + 1), t + 1))
+    dq = np.zeros(q.shape)
+    for h in range(H):
+        g = h // G
+        dq[h], dk_, dv_ = _attend_grad(q[h], k_seq[J, g], v_seq[J, g], scale, d_out[h])
+        dk[J, g] += dk_
+        dv[J, g] += dv_
+    return dq
+
+
+def mean_pool_varlen_bwd(dxc, cu_seqlens, cu_seqlens_c, kernel: int, stride: int,
+                         n_tokens: int) -> np.ndarray:
+    """Transpose of mean_pool_varlen (R17): window c's gradient, divided by its
+    count of valid tokens, added to each of those tokens.  dxc [N_c, ...] ->
+    [n_tokens, ...]."""
+    dxc = np.asarray(dxc, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cuc = np.asarray(cu_seqlens_c, dtype=np.int64)
+    dx = np.zeros((n_tokens,) + dxc.shape[1:])
+    for b in range(len(cu) - 1):
+        start, length = int(cu[b]), int(cu[b + 1] - cu[b])
+        for c in range(int(cuc[b + 1] - cuc[b])):
+            lo = stride * c
+            hi = min(lo + kernel, length)
+            if hi > lo:
+                dx[start + lo:start + hi] += dxc[cuc[b] + c] / (hi - lo)
+    return dx
+
+
 def blockmask_attention_row(q, k_seq, v_seq, mask_rows, t: int, block: int, scale: float,
                             causal: bool = False) -> np.ndarray:
     """Block-mask attention of query position t of one sequence (TileLang NSA,
@@ -503,3 +581,47 @@ def nsa_prefill_rows(q_seq, k_seq, v_seq, gates_seq, rows, *, kernel=32, stride=
                          ("indices", idx), ("block_scores", sc)):
             res[key].append(val)
     return {key: np.stack(val) for key, val in res.items()}
+
+
+def nsa_prefill_rows_grad(q_seq, k_seq, v_seq, gates_seq, d_out_seq, rows, *, kernel=32,
+                          stride=16, block=64, topk=16, window=512, scale=None):
+    """Gradient of the three-branch output of some query positions of one
+    sequence (R17), for the upstream gradient d_out_seq [L, H, D] of those rows
+    (other rows contribute nothing).  The block choice of each row is the
+    forward's (nsa_prefill_rows) and passes no gradient.  Per branch b the
+    output gradient is gate_b * dO; the gate gradient is dO . o_b.  Returns a
+    dict: dq [len(rows), H, D], dk, dv [L, H_kv, D] and dgates [len(rows), H, 3],
+    plus the forward's indices."""
+    q_seq = np.asarray(q_seq, dtype=np.float64)
+    k_seq = np.asarray(k_seq, dtype=np.float64)
+    v_seq = np.asarray(v_seq, dtype=np.float64)
+    d_out_seq = np.asarray(d_out_seq, dtype=np.float64)
+    L, H, D = q_seq.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    fwd = nsa_prefill_rows(q_seq, k_seq, v_seq, gates_seq, rows, kernel=kernel, stride=stride,
+                           block=block, topk=topk, window=window, scale=scale)
+    nc = n_windows(L, kernel, stride)
+    one, onec = np.array([0, L]), np.array([0, nc])
+    kc = mean_pool_varlen(k_seq, one, onec, kernel, stride)
+    vc = mean_pool_varlen(v_seq, one, onec, kernel, stride)
+    dk = np.zeros(k_seq.shape)
+    dv = np.zeros(v_seq.shape)
+    dkc = np.zeros(kc.shape)
+    dvc = np.zeros(vc.shape)
+    dq = np.zeros((len(rows), H, D))
+    dg = np.zeros((len(rows), H, 3))
+    for i, t in enumerate(rows):
+        g = np.asarray(gates_seq[t], dtype=np.float64)
+        do = d_out_seq[t]
+        for j, key in enumerate(("o_cmp", "o_sel", "o_win")):
+            dg[i, :, j] = (do * fwd[key][i]).sum(axis=1)
+        dq[i] += compressed_attention_row_grad(q_seq[t], kc, vc, t, kernel, stride, scale,
+                                               g[:, 0:1] * do, dkc, dvc)
+        dq[i] += selected_attention_row_grad(q_seq[t], k_seq, v_seq, fwd["indices"][i], t, block,
+                                             scale, g[:, 1:2] * do, dk, dv)
+        dq[i] += window_attention_row_grad(q_seq[t], k_seq, v_seq, t, window, scale,
+                                           g[:, 2:3] * do, dk, dv)
+    dk += mean_pool_varlen_bwd(dkc, one, onec, kernel, stride, L)
+    dv += mean_pool_varlen_bwd(dvc, one, onec, kernel, stride, L)
+    return {"dq": dq, "dk": dk, "dv": dv, "dgates": dg, "indices": fwd["indices"]}

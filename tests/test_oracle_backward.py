@@ -120,3 +120,143 @@ def test_backward_single_key_and_unreached_keys():
                                                cu_q, cu_k, block, scale)
     assert np.all(dk[:4] == 0) and np.all(dk[8:] == 0) and np.all(dv[8:] == 0)
     assert np.abs(dv[4:8]).sum() > 0
+
+
+# ----------------------------------------------------------------- compressed and window branches (R17)
+
+def test_pool_bwd_is_the_adjoint_of_the_pooling():
+    """<pool(x), y> = <x, pool_bwd(y)> for every window geometry, with tail
+    windows (fewer valid tokens, and one with none) and varlen packing; and the
+    full-window case equals torch autograd of avg_pool1d."""
+    rng = np.random.default_rng(21)
+    lengths = [0, 5, 31, 32, 33, 100, 257]
+    for kernel, stride, tail in ((32, 16, False), (32, 16, True), (5, 3, True), (4, 4, False)):
+        nc = [oracle.n_windows(L, kernel, stride, tail) + (1 if tail else 0) for L in lengths]
+        cu, cuc = oracle.cu_from_lengths(lengths), oracle.cu_from_lengths(nc)
+        x = rng.standard_normal((int(cu[-1]), 3))
+        y = rng.standard_normal((int(cuc[-1]), 3))
+        lhs = (oracle.mean_pool_varlen(x, cu, cuc, kernel, stride) * y).sum()
+        rhs = (x * oracle.mean_pool_varlen_bwd(y, cu, cuc, kernel, stride, int(cu[-1]))).sum()
+        assert abs(lhs - rhs) < 1e-12 * max(1.0, abs(lhs)), (kernel, stride, tail)
+    L = 300
+    x = torch.tensor(rng.standard_normal((1, 4, L)), requires_grad=True)
+    pooled = F.avg_pool1d(x, 32, 16)
+    gy = rng.standard_normal(tuple(pooled.shape))
+    pooled.backward(torch.tensor(gy))
+    nc = oracle.n_windows(L, 32, 16)
+    got = oracle.mean_pool_varlen_bwd(gy[0].T, [0, L], [0, nc], 32, 16, L)
+    np.testing.assert_allclose(got, x.grad[0].numpy().T, atol=1e-13)
+
+
+def _sdpa_grads(q, kk, vv, mask, d_out, scale, G):
+    """torch autograd of masked SDPA in float64: q [T, H, D], kk, vv [L, H_kv, D]
+    tensors that may carry grad (already leaves or functions of leaves), mask
+    [T, L] bool (rows with no key are excluded by the caller)."""
+    qt = torch.tensor(q.transpose(1, 0, 2), requires_grad=True)
+    ke = kk.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    ve = vv.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    out = F.scaled_dot_product_attention(qt, ke, ve, attn_mask=torch.from_numpy(mask)[None],
+                                         scale=scale)
+    out.backward(torch.tensor(d_out.transpose(1, 0, 2)))
+    return qt.grad.numpy().transpose(1, 0, 2)
+
+
+def test_compressed_branch_grad_equals_autograd_of_pooled_sdpa():
+    """The compressed branch is SDPA over avg_pool1d(32, 16)-pooled K and V with
+    the window-visibility mask; torch autograd of that composition gives dq and,
+    through the pooling, dK and dV."""
+    rng = np.random.default_rng(22)
+    L, H, H_kv, D = 260, 4, 2, 8
+    G, scale = H // H_kv, 0.3
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, H_kv, D))
+    v = rng.standard_normal((L, H_kv, D))
+    d_out = rng.standard_normal((L, H, D))
+    nc = oracle.n_windows(L, 32, 16)
+    rows = [t for t in range(L) if t >= 31]            # rows that see a window
+    kl = torch.tensor(k, requires_grad=True)
+    vl = torch.tensor(v, requires_grad=True)
+    kc_t = F.avg_pool1d(kl.permute(1, 2, 0).reshape(1, H_kv * D, L), 32, 16)
+    kc_t = kc_t.reshape(H_kv, D, nc).permute(2, 0, 1)                 # [nc, H_kv, D]
+    vc_t = F.avg_pool1d(vl.permute(1, 2, 0).reshape(1, H_kv * D, L), 32, 16)
+    vc_t = vc_t.reshape(H_kv, D, nc).permute(2, 0, 1)
+    mask = np.array([[oracle.window_visible(c, t, 32, 16) for c in range(nc)] for t in rows])
+    dq_ref = _sdpa_grads(q[rows], kc_t, vc_t, mask, d_out[rows], scale, G)
+    kc = oracle.mean_pool_varlen(k, [0, L], [0, nc], 32, 16)
+    vc = oracle.mean_pool_varlen(v, [0, L], [0, nc], 32, 16)
+    dkc, dvc = np.zeros(kc.shape), np.zeros(vc.shape)
+    dq = np.stack([oracle.compressed_attention_row_grad(q[t], kc, vc, t, 32, 16, scale, d_out[t],
+                                                        dkc, dvc) for t in rows])
+    np.testing.assert_allclose(dq, dq_ref, atol=1e-11)
+    dk = oracle.mean_pool_varlen_bwd(dkc, [0, L], [0, nc], 32, 16, L)
+    dv = oracle.mean_pool_varlen_bwd(dvc, [0, L], [0, nc], 32, 16, L)
+    np.testing.assert_allclose(dk, kl.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, vl.grad.numpy(), atol=1e-11)
+    # a row that sees no window contributes nothing
+    dkc0 = np.zeros(kc.shape)
+    assert np.all(oracle.compressed_attention_row_grad(q[30], kc, vc, 30, 32, 16, scale, d_out[30],
+                                                       dkc0, dkc0.copy()) == 0)
+    assert np.all(dkc0 == 0)
+
+
+def test_window_branch_grad_equals_autograd_of_banded_sdpa():
+    rng = np.random.default_rng(23)
+    L, H, H_kv, D, W = 150, 4, 1, 8, 40
+    G, scale = H // H_kv, 0.25
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, H_kv, D))
+    v = rng.standard_normal((L, H_kv, D))
+    d_out = rng.standard_normal((L, H, D))
+    kl = torch.tensor(k, requires_grad=True)
+    vl = torch.tensor(v, requires_grad=True)
+    t = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    mask = (j <= t) & (j > t - W)
+    dq_ref = _sdpa_grads(q, kl, vl, mask, d_out, scale, G)
+    dk, dv = np.zeros(k.shape), np.zeros(v.shape)
+    dq = np.stack([oracle.window_attention_row_grad(q[r], k, v, r, W, scale, d_out[r], dk, dv)
+                   for r in range(L)])
+    np.testing.assert_allclose(dq, dq_ref, atol=1e-11)
+    np.testing.assert_allclose(dk, kl.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, vl.grad.numpy(), atol=1e-11)
+
+
+def test_three_branch_grad_matches_finite_differences():
+    """The whole three-branch gradient (dq, dk, dv and the gates) against central
+    differences of the forward oracle, on rows past 1024 where the selection
+    matters; the block choice is checked to stay put under the perturbations."""
+    rng = np.random.default_rng(24)
+    L, H, H_kv, D = 1300, 4, 2, 8
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, H_kv, D))
+    v = rng.standard_normal((L, H_kv, D))
+    gates = 1 / (1 + np.exp(-rng.standard_normal((L, H, 3))))
+    d_out = rng.standard_normal((L, H, D))
+    rows = [40, 700, 1100, 1299]
+    kw = dict(topk=16, window=64)
+    res = oracle.nsa_prefill_rows_grad(q, k, v, gates, d_out, rows, **kw)
+
+    def loss():
+        f = oracle.nsa_prefill_rows(q, k, v, gates, rows, **kw)
+        assert np.array_equal(f["indices"], res["indices"])
+        return float((f["out"] * d_out[rows]).sum())
+
+    eps = 1e-6
+    checks = [("q", q, None), ("k", k, res["dk"]), ("v", v, res["dv"]), ("gates", gates, None)]
+    for name, x, g in checks:
+        for _ in range(12):
+            if name in ("q", "gates"):
+                i = int(rng.integers(len(rows)))
+                idx = (rows[i], int(rng.integers(H)), int(rng.integers(x.shape[2])))
+                want = (res["dq"] if name == "q" else res["dgates"])[(i,) + idx[1:]]
+            else:
+                idx = (int(rng.integers(L)), int(rng.integers(H_kv)), int(rng.integers(D)))
+                want = g[idx]
+            old = x[idx]
+            x[idx] = old + eps
+            lp = loss()
+            x[idx] = old - eps
+            lm = loss()
+            x[idx] = old
+            num = (lp - lm) / (2 * eps)
+            assert abs(num - want) < 1e-6 * max(1.0, abs(num)), (name, idx, num, want)

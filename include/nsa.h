@@ -295,6 +295,61 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
                                  hipStream_t stream);
 
 /*
+ * Backward of the other two prefill branches and of the window mean.
+ * [DeepSeek NSA with Triton, introduction and section 2.3 (the method is trained
+ *  end to end, its kernels wrapped as a trainable module) and section 1.1 (the
+ *  compressed branch over mean-pooled keys and values, the sliding-window
+ *  branch).  The pages print no backward: these are the exact gradients of
+ *  nsa_compressed_attn_fwd's output, nsa_window_attn_fwd's output and
+ *  nsa_compress_k's means.]
+ * Shared conventions: bf16 inputs, fp32 gradients, prefill rows (cu_seqlens_q
+ * required; row r of sequence b at t = (r - cu_q[b]) + (L_b - Lq_b)).  `out` and
+ * `lse` are the branch forward's output and natural-log normaliser, `d_out` the
+ * upstream gradient of that output (for a gated sum, the gate times the
+ * gradient of the sum).  accumulate 0: dq and the key/value gradients are
+ * written in full (0 for keys no row attends to); 1: they are added to what the
+ * arrays hold, so the branches of one step can share dq, dk and dv.  Per head
+ * over the row's keys J: dV_J += p dO^T; ds = p * (V_J dO - dO . out);
+ * dq += scale ds K_J; dK_J += scale ds q^T.  Key gradients of a block seen by
+ * more than 256 rows are summed with fp32 atomics (order may change between
+ * calls: fp32 rounding only).  workspace: nsa_branch_attn_bwd_workspace_size
+ * bytes (delta = dO . out per row and head).
+ *
+ * nsa_compressed_attn_bwd: keys are the compressed windows visible to t
+ *   (stride*c + kernel - 1 <= t); k_c, v_c [N_c, kv_heads, 128] with
+ *   cu_seqlens_c holding full-window counts; writes dq [rows, heads, 128] and
+ *   dk_c, dv_c [N_c, kv_heads, 128].  Kernel 32, stride 16.
+ * nsa_window_attn_bwd: keys max(0, t - window + 1) .. t; writes dq, dk, dv
+ *   [N_k, kv_heads, 128].
+ * nsa_compress_bwd: the transpose of nsa_compress_k for fp32 gradients: dx[j]
+ *   (+)= sum over the windows c holding token j of dx_c[c] / (valid tokens of
+ *   window c); dx_c [N_c, heads, head_dim], dx [N, heads, head_dim], windows
+ *   as in nsa_compress_k; tokens in no window get 0 (accumulate 0).
+ */
+size_t nsa_branch_attn_bwd_workspace_size(int32_t rows_total, int32_t heads);
+nsa_status nsa_compressed_attn_bwd(const void* q, const void* k_c, const void* v_c,
+                                   const void* o_cmp, const void* d_out, const float* lse,
+                                   nsa_dtype dtype, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_c,
+                                   int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                                   int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                   int32_t kernel, int32_t stride, float softmax_scale,
+                                   int32_t accumulate, float* dq, float* dk_c, float* dv_c,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+nsa_status nsa_window_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                               const void* d_out, const float* lse, nsa_dtype dtype,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                               int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t window,
+                               float softmax_scale, int32_t accumulate, float* dq, float* dk,
+                               float* dv, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+nsa_status nsa_compress_bwd(const float* dx_c, float* dx, const int32_t* cu_seqlens,
+                            const int32_t* cu_seqlens_c, int32_t batch, int32_t max_seqlen,
+                            int32_t heads, int32_t head_dim, int32_t kernel, int32_t stride,
+                            int32_t accumulate, hipStream_t stream);
+
+/*
  * nsa_decode_step -- one decode step of the whole path for a packed batch: the
  * newest token of every sequence (t = L_b - 1) scores the compressed keys,
  * selects k blocks and attends to them.

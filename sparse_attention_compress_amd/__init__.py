@@ -98,6 +98,16 @@ _SIGS = {
                                              c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                              c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp,
                                              c_sz, c_vp]),
+    "nsa_branch_attn_bwd_workspace_size": (c_sz, [c_i32, c_i32]),
+    "nsa_compressed_attn_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int,
+                                               c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                               c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_vp, c_vp,
+                                               c_vp, c_sz, c_vp]),
+    "nsa_window_attn_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp,
+                                           c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                           c_f32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "nsa_compress_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                        c_i32, c_i32, c_vp]),
     "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
     "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
     "nsa_decode_noalloc_scratch_bytes": (c_sz, []),
@@ -304,6 +314,55 @@ def nsa_selected_attn_bwd(q, k, v, out, d_out, lse, indices, cu_seqlens_q, cu_se
                                        float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
                                        _ptr(ws), nbytes, _stream(stream)))
     return dq, dk, dv
+
+
+def branch_attn_bwd_workspace_size(rows, heads):
+    return lib().nsa_branch_attn_bwd_workspace_size(int(rows), int(heads))
+
+
+def nsa_compressed_attn_bwd(q, k_c, v_c, o_cmp, d_out, lse, cu_seqlens_q, cu_seqlens_k,
+                            cu_seqlens_c, max_seqlen_k, dq, dk_c, dv_c, accumulate=False,
+                            softmax_scale=0.0, kernel=32, stride=16, workspace=None, stream=None):
+    """Gradient of nsa_compressed_attn_fwd: q, o_cmp, d_out [rows, H, D] bf16, k_c,
+    v_c [N_c, H_kv, D] bf16, lse [rows, H] -> dq [rows, H, D], dk_c, dv_c
+    [N_c, H_kv, D] float32 (written, or added to with accumulate)."""
+    rows, H, D = q.shape
+    H_kv = k_c.shape[1]
+    batch = cu_seqlens_k.numel() - 1
+    ws, nbytes = _workspace(branch_attn_bwd_workspace_size(rows, H), q.device, workspace)
+    _check(lib().nsa_compressed_attn_bwd(_ptr(q), _ptr(k_c), _ptr(v_c), _ptr(o_cmp), _ptr(d_out),
+                                         _ptr(lse), _dt(q), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                         _ptr(cu_seqlens_c), batch, rows, int(max_seqlen_k), H,
+                                         H_kv, D, kernel, stride, float(softmax_scale),
+                                         int(bool(accumulate)), _ptr(dq), _ptr(dk_c), _ptr(dv_c),
+                                         _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk_c, dv_c
+
+
+def nsa_window_attn_bwd(q, k, v, out, d_out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_k, dq,
+                        dk, dv, window=512, accumulate=False, softmax_scale=0.0, workspace=None,
+                        stream=None):
+    """Gradient of nsa_window_attn_fwd -> dq [rows, H, D], dk, dv [N_k, H_kv, D] float32."""
+    rows, H, D = q.shape
+    H_kv = k.shape[1]
+    batch = cu_seqlens_k.numel() - 1
+    ws, nbytes = _workspace(branch_attn_bwd_workspace_size(rows, H), q.device, workspace)
+    _check(lib().nsa_window_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(d_out), _ptr(lse),
+                                     _dt(q), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, rows,
+                                     int(max_seqlen_k), H, H_kv, D, int(window),
+                                     float(softmax_scale), int(bool(accumulate)), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv
+
+
+def nsa_compress_bwd(dx_c, dx, cu_seqlens, cu_seqlens_c, max_seqlen, accumulate=False, kernel=32,
+                     stride=16, stream=None):
+    """Transpose of nsa_compress_k (float32): dx_c [N_c, heads, D] -> dx [N, heads, D]."""
+    heads, head_dim = dx.shape[1], dx.shape[2]
+    _check(lib().nsa_compress_bwd(_ptr(dx_c), _ptr(dx), _ptr(cu_seqlens), _ptr(cu_seqlens_c),
+                                  cu_seqlens.numel() - 1, int(max_seqlen), heads, head_dim, kernel,
+                                  stride, int(bool(accumulate)), _stream(stream)))
+    return dx
 
 
 def decode_params(q, k, v, k_c, cu_seqlens_k, cu_seqlens_c, max_seqlen_k, out, topk=64, n_init=1,

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/nsa.h: argument validation, grid
 // sizing, workspace carve-up and kernel launches on the caller's stream.  No
 // allocation, no synchronisation.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -311,8 +312,138 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.mode = nsa::kBwdSelected;
+  a.cu_kv = cu_seqlens_k;
   nsa::selected_bwd_ws_carve(workspace, a);
   return hip_status(nsa::launch_selected_bwd(a, stream), fn);
+}
+
+// ------------------------------------------- backward of the compressed and window branches
+
+namespace {
+
+size_t branch_bwd_ws(int32_t rows_total, int32_t heads) {
+  if (rows_total <= 0 || heads <= 0) return 0;
+  return (size_t(rows_total) * heads * sizeof(float) + 255) & ~size_t(255);
+}
+
+// Shared checks and launch of the two list-free branch gradients.
+nsa_status branch_bwd(const char* fn, int mode, const void* q, const void* k, const void* v,
+                      const void* out, const void* d_out, const float* lse, nsa_dtype dtype,
+                      const int32_t* cu_q, const int32_t* cu_k, const int32_t* cu_kv,
+                      int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                      int32_t max_keys, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                      int32_t window, float softmax_scale, int32_t accumulate, float* dq,
+                      float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  NSA_REQUIRE(batch >= 0 && rows_total >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(dtype == NSA_BF16, NSA_ERR_UNSUPPORTED, "%s: bfloat16 inputs only", fn);
+  NSA_REQUIRE(group_ok(heads, kv_heads), NSA_ERR_UNSUPPORTED, "%s: heads %d / kv_heads %d unsupported", fn, heads, kv_heads);
+  NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
+  NSA_REQUIRE(accumulate == 0 || accumulate == 1, NSA_ERR_INVALID_ARG, "%s: accumulate must be 0 or 1", fn);
+  NSA_REQUIRE(cu_q != nullptr, NSA_ERR_INVALID_ARG, "%s: cu_seqlens_q is required (prefill rows)", fn);
+  if (rows_total == 0 || batch == 0) return ok();
+  NSA_REQUIRE(max_seqlen_k >= 1, NSA_ERR_INVALID_ARG, "%s: rows without keys (max_seqlen_k 0)", fn);
+  const int nb_max = std::max(1, (max_keys + nsa::kBlock - 1) / nsa::kBlock);
+  NSA_REQUIRE(size_t(batch) * kv_heads * nb_max <= size_t(INT32_MAX) &&
+                  size_t(rows_total) * kv_heads <= size_t(UINT32_MAX),
+              NSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  NSA_REQUIRE(q && k && v && out && d_out && lse && cu_k && cu_kv && dq && dk && dv,
+              NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(d_out) &&
+                  aligned16(dk) && aligned16(dv),
+              NSA_ERR_INVALID_ARG, "%s: q, k, v, out, d_out, dk, dv must be 16-byte aligned", fn);
+  const size_t need = branch_bwd_ws(rows_total, heads);
+  NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  nsa::SelectedBwdArgs a{};
+  a.mode = mode;
+  a.window = window;
+  a.accumulate = accumulate;
+  a.cu_kv = cu_kv;
+  a.q = static_cast<const nsa::bf16_t*>(q);
+  a.k = static_cast<const nsa::bf16_t*>(k);
+  a.v = static_cast<const nsa::bf16_t*>(v);
+  a.out = static_cast<const nsa::bf16_t*>(out);
+  a.dout = static_cast<const nsa::bf16_t*>(d_out);
+  a.lse = lse;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.batch = batch;
+  a.rows_total = rows_total;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.nb_max = nb_max;
+  a.max_seqlen_k = max_seqlen_k;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt(float(head_dim));
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  return hip_status(nsa::launch_selected_bwd(a, stream), fn);
+}
+
+}  // namespace
+
+size_t nsa_branch_attn_bwd_workspace_size(int32_t rows_total, int32_t heads) {
+  return branch_bwd_ws(rows_total, heads);
+}
+
+nsa_status nsa_compressed_attn_bwd(const void* q, const void* k_c, const void* v_c,
+                                   const void* o_cmp, const void* d_out, const float* lse,
+                                   nsa_dtype dtype, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_c,
+                                   int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                                   int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                   int32_t kernel, int32_t stride, float softmax_scale,
+                                   int32_t accumulate, float* dq, float* dk_c, float* dv_c,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_compressed_attn_bwd";
+  nsa_status st = check_geometry(fn, head_dim, kernel, stride, nsa::kBlock);
+  if (st != NSA_OK) return st;
+  NSA_REQUIRE(cu_seqlens_c != nullptr || rows_total == 0 || batch == 0, NSA_ERR_INVALID_ARG,
+              "%s: cu_seqlens_c is null", fn);
+  return branch_bwd(fn, nsa::kBwdCompressed, q, k_c, v_c, o_cmp, d_out, lse, dtype, cu_seqlens_q,
+                    cu_seqlens_k, cu_seqlens_c, batch, rows_total, max_seqlen_k,
+                    nsa_window_count(max_seqlen_k, kernel, stride, 0), heads, kv_heads, head_dim,
+                    0, softmax_scale, accumulate, dq, dk_c, dv_c, workspace, workspace_bytes,
+                    stream);
+}
+
+nsa_status nsa_window_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                               const void* d_out, const float* lse, nsa_dtype dtype,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t rows_total, int32_t max_seqlen_k,
+                               int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t window,
+                               float softmax_scale, int32_t accumulate, float* dq, float* dk,
+                               float* dv, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  const char* fn = "nsa_window_attn_bwd";
+  NSA_REQUIRE(window >= 1, NSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
+  return branch_bwd(fn, nsa::kBwdWindow, q, k, v, out, d_out, lse, dtype, cu_seqlens_q,
+                    cu_seqlens_k, cu_seqlens_k, batch, rows_total, max_seqlen_k, max_seqlen_k,
+                    heads, kv_heads, head_dim, window, softmax_scale, accumulate, dq, dk, dv,
+                    workspace, workspace_bytes, stream);
+}
+
+nsa_status nsa_compress_bwd(const float* dx_c, float* dx, const int32_t* cu_seqlens,
+                            const int32_t* cu_seqlens_c, int32_t batch, int32_t max_seqlen,
+                            int32_t heads, int32_t head_dim, int32_t kernel, int32_t stride,
+                            int32_t accumulate, hipStream_t stream) {
+  const char* fn = "nsa_compress_bwd";
+  NSA_REQUIRE(batch >= 0 && max_seqlen >= 0, NSA_ERR_INVALID_ARG, "%s: negative batch or max_seqlen", fn);
+  NSA_REQUIRE(heads > 0 && head_dim > 0, NSA_ERR_INVALID_ARG, "%s: heads and head_dim must be positive", fn);
+  NSA_REQUIRE(kernel >= 1 && stride >= 1, NSA_ERR_INVALID_ARG, "%s: kernel and stride must be >= 1", fn);
+  NSA_REQUIRE((long(heads) * head_dim) % 4 == 0 && long(heads) * head_dim < (1L << 30),
+              NSA_ERR_UNSUPPORTED, "%s: heads * head_dim must be a multiple of 4", fn);
+  NSA_REQUIRE(accumulate == 0 || accumulate == 1, NSA_ERR_INVALID_ARG, "%s: accumulate must be 0 or 1", fn);
+  NSA_REQUIRE(batch <= 65535, NSA_ERR_UNSUPPORTED, "%s: batch above 65535", fn);
+  if (batch == 0 || max_seqlen == 0) return ok();
+  NSA_REQUIRE(dx_c && dx && cu_seqlens && cu_seqlens_c, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(aligned16(dx_c) && aligned16(dx), NSA_ERR_INVALID_ARG, "%s: dx_c and dx must be 16-byte aligned", fn);
+  return hip_status(nsa::launch_pool_bwd(dx_c, dx, cu_seqlens, cu_seqlens_c, batch, max_seqlen,
+                                         heads * head_dim, kernel, stride, accumulate, stream),
+                    fn);
 }
 
 // ------------------------------------------------------------------ decode step

@@ -18,6 +18,15 @@
 //
 // Launches: prep (delta, list counts cleared), count, scan, fill, zero (the
 // blocks with long row lists), dq, dk/dv.
+//
+// The same kernels give the gradients of the other two prefill branches
+// (DeepSeek NSA with Triton, section 1.1), whose key sets need no lists: the
+// sliding-window branch (keys t - window + 1 .. t) and the compressed branch
+// (the compressed windows c with 16c + 31 <= t, read from K_c and V_c).  There
+// a key block is seen by one contiguous range of query positions, so the dk/dv
+// workgroups walk that range directly.  With `accumulate` every gradient is
+// added to what the output arrays hold, so the branches of one step can share
+// dq, dk and dv.
 // The order within a block's row list, and of the chunk sums, depends on
 // atomics, so dK and dV are summed in an order that can change from call to
 // call (fp32 rounding only).
@@ -44,6 +53,40 @@ __device__ __forceinline__ void bwd_row_position(int row, const int* __restrict_
   }
   b = lo;
   t = (row - cu_q[b]) + ((cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]));
+}
+
+// Whether key j (a row of the key tensor, 0-based within its sequence, klen
+// keys) takes part in the attention of query position t.
+template <int MODE>
+__device__ __forceinline__ bool key_visible(int j, int t, int klen, int window) {
+  if constexpr (MODE == kBwdSelected) return j <= t;
+  else if constexpr (MODE == kBwdWindow) return j <= t && j > t - window;
+  else return j < klen && kStride * j + kKernel - 1 <= t;
+}
+
+// Query positions that see key block `id` of sequence b in an implicit mode:
+// t_lo .. t_lo + n - 1 (clipped to the sequence's query rows, row
+// cu_q[b] + t - shift); returns n.
+template <int MODE>
+__device__ __forceinline__ int implicit_rows(int b, int id, int klen, int window,
+                                             const int* __restrict__ cu_q,
+                                             const int* __restrict__ cu_k, int& t_lo,
+                                             int& row_lo) {
+  const int len = cu_k[b + 1] - cu_k[b];
+  const int shift = len - (cu_q[b + 1] - cu_q[b]);
+  int lo, hi;
+  if constexpr (MODE == kBwdWindow) {
+    lo = kBlock * id;
+    hi = min(kBlock * id + kBlock - 1, klen - 1) + window - 1;
+  } else {
+    lo = kStride * (kBlock * id) + kKernel - 1;
+    hi = len - 1;
+  }
+  lo = max(lo, shift);
+  hi = min(hi, len - 1);
+  t_lo = lo;
+  row_lo = cu_q[b] + lo - shift;
+  return max(0, hi - lo + 1);
 }
 
 // delta[row, h] = dO . O (one wave per (row, head), two dims a lane); the
@@ -136,17 +179,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fill_kernel(
 
 // dk and dv of the blocks whose row list spans several chunks start at 0 (the
 // chunks add to them); one workgroup per (sequence, kv head, block).
-__global__ __launch_bounds__(kBwdThreads) void bwd_zero_kernel(const int* __restrict__ cnt,
-                                                               const int* __restrict__ cu_k,
-                                                               int kv_heads, int nb_max,
-                                                               float* __restrict__ dk,
-                                                               float* __restrict__ dv) {
+template <int MODE>
+__global__ __launch_bounds__(kBwdThreads) void bwd_zero_kernel(
+    const int* __restrict__ cnt, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    const int* __restrict__ cu_kv, int window, int kv_heads, int nb_max, float* __restrict__ dk,
+    float* __restrict__ dv) {
   const int slot = blockIdx.x;
-  if (cnt[slot] <= kRowsPerChunk) return;
   const int id = slot % nb_max;
   const int g = (slot / nb_max) % kv_heads;
   const int b = slot / (nb_max * kv_heads);
-  const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
+  const int kstart = cu_kv[b], len = cu_kv[b + 1] - kstart;
+  if (kBlock * id >= len) return;
+  int n;
+  if constexpr (MODE == kBwdSelected) {
+    n = cnt[slot];
+  } else {
+    int t_lo, row_lo;
+    n = implicit_rows<MODE>(b, id, len, window, cu_q, cu_k, t_lo, row_lo);
+  }
+  if (n <= kRowsPerChunk) return;
   const int tok = kBlock * id + (threadIdx.x >> 2);
   if (tok >= len) return;
   const size_t o = (size_t(kstart + tok) * kv_heads + g) * kHeadDim + 32 * (threadIdx.x & 3);
@@ -248,13 +299,14 @@ __device__ __forceinline__ void probs4(const RowLds<G>& R, const KeyTile& s, int
 // thread adds ds * k of its four tokens to its 8 dims of every head's dq in
 // registers; the 16 token groups are summed once at the end (the four groups
 // of a wave by lane swaps across its DPP rows, the four waves through LDS).
-template <int G>
+template <int G, int MODE>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, const int* __restrict__ indices, int k_sel,
-    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int heads,
-    int kv_heads, float scale_log2, float scale, float* __restrict__ dq) {
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, const int* __restrict__ cu_kv,
+    int window, int accumulate, int batch, int heads, int kv_heads, float scale_log2, float scale,
+    float* __restrict__ dq) {
   constexpr int kOut = (G * kHeadDim + kBwdThreads - 1) / kBwdThreads;
   __shared__ RowLds<G> R;
   __shared__ float red_s[4][G][kHeadDim];
@@ -262,11 +314,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   const int row = int(blockIdx.x / unsigned(kv_heads)), g = int(blockIdx.x % unsigned(kv_heads));
   int b, t;
   bwd_row_position(row, cu_q, cu_k, batch, b, t);
-  const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
+  const int len = cu_k[b + 1] - cu_k[b];
+  const int kstart = cu_kv[b], klen = cu_kv[b + 1] - kstart;
   const size_t head0 = size_t(row) * heads + size_t(g) * G;
   stage_row<G>(R, q, dout, lse, delta, head0);
   __syncthreads();
   const int* irow = indices + (size_t(row) * kv_heads + g) * k_sel;
+  // key blocks to visit: the row's list, or the range an implicit key set covers
+  int n_pl = 0, blo = 0;
+  if (t >= 0 && t < len) {
+    if constexpr (MODE == kBwdSelected) {
+      n_pl = k_sel;
+    } else if constexpr (MODE == kBwdWindow) {
+      blo = max(0, t - window + 1) / kBlock;
+      n_pl = t / kBlock - blo + 1;
+    } else {
+      const int nvis = t >= kKernel - 1 ? min(klen, (t - (kKernel - 1)) / kStride + 1) : 0;
+      n_pl = (nvis + kBlock - 1) / kBlock;
+    }
+  }
   // at most 8 heads' accumulators at a time: a 16-head group takes two passes
   // over the blocks (the second mostly from L2) instead of one wave per SIMD
   constexpr int HG = G > 8 ? 8 : G;
@@ -277,16 +343,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     for (int h = 0; h < HG; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    for (int pl = 0; pl < k_sel; ++pl) {
-      const int id = irow[pl];
-      if (t < 0 || t >= len || id < 0 || id > t / kBlock) continue;  // uniform
+    for (int pl = 0; pl < n_pl; ++pl) {
+      int id = blo + pl;
+      if constexpr (MODE == kBwdSelected) {
+        id = irow[pl];
+        if (id < 0 || id > t / kBlock) continue;  // uniform
+      }
       bool valid[4];
       size_t off[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = kBlock * id + 4 * tg + i;
-        valid[i] = tok <= t;
-        off[i] = (size_t(kstart + min(tok, t)) * kv_heads + g) * kHeadDim + 8 * dp;
+        valid[i] = key_visible<MODE>(tok, t, klen, window);
+        off[i] = (size_t(kstart + min(tok, klen - 1)) * kv_heads + g) * kHeadDim + 8 * dp;
       }
       KeyTile s;
       load_tile(k, v, off, valid, s);
@@ -322,7 +391,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const int o = tid + kBwdThreads * i;
     if (o < G * kHeadDim) {
       const int h = o / kHeadDim, d = o % kHeadDim;
-      dq[head0 * kHeadDim + o] = scale * (red_s[0][h][d] + red_s[1][h][d] + red_s[2][h][d] + red_s[3][h][d]);
+      const float x = scale * (red_s[0][h][d] + red_s[1][h][d] + red_s[2][h][d] + red_s[3][h][d]);
+      if (accumulate) dq[head0 * kHeadDim + o] += x; else dq[head0 * kHeadDim + o] = x;
     }
   }
 }
@@ -333,25 +403,30 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
 // it); the chunks of a longer list add theirs to the zeroed gradients with
 // fp32 atomics, so the earliest blocks, which most rows list, are spread over
 // several workgroups instead of one.
-template <int G>
+template <int G, int MODE>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, const int* __restrict__ cnt, const int* __restrict__ off,
-    const int2* __restrict__ list, const int* __restrict__ cu_k, int heads, int kv_heads,
+    const int2* __restrict__ list, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    const int* __restrict__ cu_kv, int window, int accumulate, int heads, int kv_heads,
     int nb_max, float scale_log2, float scale, float* __restrict__ dk, float* __restrict__ dv) {
   __shared__ RowLds<G> R[2];
   const int tid = threadIdx.x, tg = tid >> 4, dp = tid & 15;
   const int slot = blockIdx.x, chunk = blockIdx.y;
-  const int n = cnt[slot];
-  const int e_begin = chunk * kRowsPerChunk;
-  if (chunk > 0 && e_begin >= n) return;  // uniform: no rows left for this chunk
-  const int e_end = min(n, e_begin + kRowsPerChunk);
   const int id = slot % nb_max;
   const int g = (slot / nb_max) % kv_heads;
   const int b = slot / (nb_max * kv_heads);
-  const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
-  if (kBlock * id >= len) return;  // uniform: no token of this sequence here
+  const int kstart = cu_kv[b], len = cu_kv[b + 1] - kstart;
+  if (kBlock * id >= len) return;  // uniform: no key of this sequence here
+  // the rows that see this block: a list (selected branch) or one range
+  int n, t_lo = 0, row_lo = 0;
+  if constexpr (MODE == kBwdSelected) n = cnt[slot];
+  else n = implicit_rows<MODE>(b, id, len, window, cu_q, cu_k, t_lo, row_lo);
+  const int e_begin = chunk * kRowsPerChunk;
+  if (chunk > 0 && e_begin >= n) return;  // uniform: no rows left for this chunk
+  if (n == 0 && accumulate) return;       // nothing to add
+  const int e_end = min(n, e_begin + kRowsPerChunk);
   int tok[4];
   bool tok_ok[4];
   size_t kv_off[4];
@@ -371,7 +446,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       ak[i][e] = 0.f;
       av[i][e] = 0.f;
     }
-  const int first = off[slot];
+  const int first = MODE == kBwdSelected ? off[slot] : 0;
+  auto entry = [&](int e) {
+    if constexpr (MODE == kBwdSelected) return list[first + e];
+    else return make_int2(row_lo + e, t_lo + e);
+  };
   // Two listed rows (with their positions) per pair of barriers; the next
   // pair's q and dO chunks, normalisers and deltas are loaded into registers
   // while the current pair is computed.  Chunk c of a pair: row c / (16 G),
@@ -381,8 +460,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   float plse = 0.f, pdel = 0.f;
   int2 n0 = make_int2(0, -1), n1 = make_int2(0, -1);
   auto prefetch = [&](int e) {
-    n0 = list[first + e];
-    n1 = e + 1 < e_end ? list[first + e + 1] : n0;
+    n0 = entry(e);
+    n1 = e + 1 < e_end ? entry(e + 1) : n0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = tid + kBwdThreads * i;
@@ -442,7 +521,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       const int t = rr ? r1.y : r0.y;
       bool valid[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) valid[i] = tok_ok[i] && tok[i] <= t;
+      for (int i = 0; i < 4; ++i) valid[i] = tok_ok[i] && key_visible<MODE>(tok[i], t, len, window);
 #pragma unroll 1
       for (int h = 0; h < G; ++h) {
         float q8[8], d8[8], p[4], ds[4];
@@ -461,7 +540,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (!tok_ok[i]) continue;
-    if (n <= kRowsPerChunk) {
+    if (n <= kRowsPerChunk && accumulate) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dk[kv_off[i] + e] += scale * ak[i][e];
+        dv[kv_off[i] + e] += av[i][e];
+      }
+    } else if (n <= kRowsPerChunk) {
 #pragma unroll
       for (int e = 0; e < 8; e += 4) {
         *reinterpret_cast<float4*>(dk + kv_off[i] + e) =
@@ -479,46 +564,109 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   }
 }
 
-template <int G>
+template <int G, int MODE>
 hipError_t launch_bwd_g(const SelectedBwdArgs& a, hipStream_t s) {
   const size_t n_rh = size_t(a.rows_total) * a.heads;
   const int n_slots = a.batch * a.kv_heads * a.nb_max;
-  const size_t n_place = size_t(a.rows_total) * a.kv_heads * a.k_sel;
+  const size_t n_place = MODE == kBwdSelected ? size_t(a.rows_total) * a.kv_heads * a.k_sel : 0;
   const unsigned prep_grid = unsigned(std::max<size_t>((n_rh + 3) / 4, 1));
   hipError_t e = launch_kernel(kKindBwdLists, bwd_prep_kernel, dim3(prep_grid), dim3(kBwdThreads), s,
-                               a.out, a.dout, n_rh, a.delta, a.cnt, n_slots);
+                               a.out, a.dout, n_rh, a.delta, a.cnt,
+                               MODE == kBwdSelected ? n_slots : 0);
   if (e != hipSuccess) return e;
   const unsigned place_grid = unsigned((n_place + kBwdThreads - 1) / kBwdThreads);
-  if (place_grid > 0) {
+  if (MODE == kBwdSelected && place_grid > 0) {
     e = launch_kernel(kKindBwdLists, bwd_count_kernel, dim3(place_grid), dim3(kBwdThreads), s,
                       a.indices, n_place, a.k_sel, a.kv_heads, a.cu_q, a.cu_k, a.batch, a.nb_max,
                       a.cnt);
     if (e != hipSuccess) return e;
   }
-  e = launch_kernel(kKindBwdLists, bwd_scan_kernel, dim3(1), dim3(kScanThreads), s,
-                    static_cast<const int*>(a.cnt), n_slots, a.off, a.cursor);
-  if (e != hipSuccess) return e;
-  if (place_grid > 0) {
+  if (MODE == kBwdSelected) {
+    e = launch_kernel(kKindBwdLists, bwd_scan_kernel, dim3(1), dim3(kScanThreads), s,
+                      static_cast<const int*>(a.cnt), n_slots, a.off, a.cursor);
+    if (e != hipSuccess) return e;
+  }
+  if (MODE == kBwdSelected && place_grid > 0) {
     e = launch_kernel(kKindBwdLists, bwd_fill_kernel, dim3(place_grid), dim3(kBwdThreads), s,
                       a.indices, n_place, a.k_sel, a.kv_heads, a.cu_q, a.cu_k, a.batch, a.nb_max,
                       a.cursor, a.list);
     if (e != hipSuccess) return e;
   }
-  e = launch_kernel(kKindBwdLists, bwd_zero_kernel, dim3(unsigned(n_slots)), dim3(kBwdThreads), s,
-                    static_cast<const int*>(a.cnt), a.cu_k, a.kv_heads, a.nb_max, a.dk, a.dv);
-  if (e != hipSuccess) return e;
+  if (!a.accumulate) {
+    e = launch_kernel(kKindBwdLists, bwd_zero_kernel<MODE>, dim3(unsigned(n_slots)),
+                      dim3(kBwdThreads), s, static_cast<const int*>(a.cnt), a.cu_q, a.cu_k,
+                      a.cu_kv, a.window, a.kv_heads, a.nb_max, a.dk, a.dv);
+    if (e != hipSuccess) return e;
+  }
   const float scale_log2 = a.scale * kLog2eHost;
-  e = launch_kernel(kKindBwdQ, bwd_dq_kernel<G>, dim3(unsigned(a.rows_total) * a.kv_heads),
+  e = launch_kernel(kKindBwdQ, bwd_dq_kernel<G, MODE>, dim3(unsigned(a.rows_total) * a.kv_heads),
                     dim3(kBwdThreads), s, a.q, a.k, a.v, a.dout, a.lse,
                     static_cast<const float*>(a.delta), a.indices, a.k_sel, a.cu_q, a.cu_k,
-                    a.batch, a.heads, a.kv_heads, scale_log2, a.scale, a.dq);
+                    a.cu_kv, a.window, a.accumulate, a.batch, a.heads, a.kv_heads, scale_log2,
+                    a.scale, a.dq);
   if (e != hipSuccess) return e;
-  const unsigned n_chunk = unsigned((a.max_seqlen_k + kRowsPerChunk - 1) / kRowsPerChunk);
-  return launch_kernel(kKindBwdKV, bwd_dkdv_kernel<G>, dim3(unsigned(n_slots), std::max(1u, n_chunk)),
-                       dim3(kBwdThreads), s, a.q, a.k, a.v, a.dout, a.lse,
-                       static_cast<const float*>(a.delta), static_cast<const int*>(a.cnt),
-                       static_cast<const int*>(a.off), static_cast<const int2*>(a.list), a.cu_k,
-                       a.heads, a.kv_heads, a.nb_max, scale_log2, a.scale, a.dk, a.dv);
+  // the most rows one key block can have: every row (selected, compressed) or
+  // the 64 + window - 1 positions that see a block of the window branch
+  const int max_rows = MODE == kBwdWindow ? std::min(a.max_seqlen_k, kBlock + a.window - 1)
+                                          : a.max_seqlen_k;
+  const unsigned n_chunk = unsigned((max_rows + kRowsPerChunk - 1) / kRowsPerChunk);
+  return launch_kernel(kKindBwdKV, bwd_dkdv_kernel<G, MODE>,
+                       dim3(unsigned(n_slots), std::max(1u, n_chunk)), dim3(kBwdThreads), s, a.q,
+                       a.k, a.v, a.dout, a.lse, static_cast<const float*>(a.delta),
+                       static_cast<const int*>(a.cnt), static_cast<const int*>(a.off),
+                       static_cast<const int2*>(a.list), a.cu_q, a.cu_k, a.cu_kv, a.window,
+                       a.accumulate, a.heads, a.kv_heads, a.nb_max, scale_log2, a.scale, a.dk,
+                       a.dv);
+}
+
+template <int MODE>
+hipError_t launch_bwd_mode(const SelectedBwdArgs& a, hipStream_t s) {
+  switch (a.heads / a.kv_heads) {
+    case 1: return launch_bwd_g<1, MODE>(a, s);
+    case 2: return launch_bwd_g<2, MODE>(a, s);
+    case 4: return launch_bwd_g<4, MODE>(a, s);
+    case 8: return launch_bwd_g<8, MODE>(a, s);
+    case 16: return launch_bwd_g<16, MODE>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// dx[j] (+)= sum over the windows c that hold token j of dx_c[c] / (valid tokens
+// of c): the transpose of the window mean.  One thread per 4 channels of one
+// token row; the grid's y dimension is the sequence.
+__global__ __launch_bounds__(256) void pool_bwd_kernel(const float* __restrict__ dxc,
+                                                       float* __restrict__ dx,
+                                                       const int* __restrict__ cu,
+                                                       const int* __restrict__ cu_c, int width,
+                                                       int kernel, int stride, int accumulate) {
+  const int b = blockIdx.y;
+  const int start = cu[b], len = cu[b + 1] - start;
+  const int cstart = cu_c[b], nc = cu_c[b + 1] - cstart;
+  const int w4 = width / 4;
+  const long i = long(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= long(len) * w4) return;
+  const int j = int(i / w4), ch = 4 * int(i % w4);
+  // windows c with stride*c <= j < stride*c + kernel, 0 <= c < nc
+  const int c_lo = j >= kernel ? (j - kernel) / stride + 1 : 0;
+  const int c_hi = min(nc - 1, j / stride);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = c_lo; c <= c_hi; ++c) {
+    const float inv = 1.f / float(min(kernel, len - stride * c));
+    const float4 g = *reinterpret_cast<const float4*>(dxc + size_t(cstart + c) * width + ch);
+    acc.x += g.x * inv;
+    acc.y += g.y * inv;
+    acc.z += g.z * inv;
+    acc.w += g.w * inv;
+  }
+  float4* o = reinterpret_cast<float4*>(dx + size_t(start + j) * width + ch);
+  if (accumulate) {
+    const float4 x = *o;
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  *o = acc;
 }
 
 }  // namespace
@@ -547,14 +695,22 @@ void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a) {
 }
 
 hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s) {
-  switch (a.heads / a.kv_heads) {
-    case 1: return launch_bwd_g<1>(a, s);
-    case 2: return launch_bwd_g<2>(a, s);
-    case 4: return launch_bwd_g<4>(a, s);
-    case 8: return launch_bwd_g<8>(a, s);
-    case 16: return launch_bwd_g<16>(a, s);
+  switch (a.mode) {
+    case kBwdSelected: return launch_bwd_mode<kBwdSelected>(a, s);
+    case kBwdWindow: return launch_bwd_mode<kBwdWindow>(a, s);
+    case kBwdCompressed: return launch_bwd_mode<kBwdCompressed>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_pool_bwd(const float* dxc, float* dx, const int* cu, const int* cu_c, int batch,
+                           int n_tokens_max, int width, int kernel, int stride, int accumulate,
+                           hipStream_t s) {
+  const long items = long(n_tokens_max) * (width / 4);
+  const unsigned gx = unsigned((items + 255) / 256);
+  if (gx == 0 || batch == 0) return hipSuccess;
+  return launch_kernel(kKindPool, pool_bwd_kernel, dim3(gx, unsigned(batch)), dim3(256), s, dxc,
+                       dx, cu, cu_c, width, kernel, stride, accumulate);
 }
 
 }  // namespace nsa

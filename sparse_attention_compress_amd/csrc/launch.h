@@ -215,10 +215,18 @@ hipError_t launch_blockmask_attn(const bf16_t* q, const bf16_t* k, const bf16_t*
                                  const int* cu, int batch, int max_seqlen, int heads,
                                  float scale_log2, bf16_t* vt, hipStream_t s);
 
-// Backward of the selected attention (bf16 inputs, fp32 gradients, prefill rows).
+// Backward of an attention branch over prefill rows (bf16 inputs, fp32
+// gradients).  The keys of a row are the tokens of its listed blocks (selected
+// branch), the last `window` tokens (sliding-window branch) or the compressed
+// windows visible to it (compressed branch; k, v are then K_c, V_c).
+enum BwdMode { kBwdSelected = 0, kBwdWindow = 1, kBwdCompressed = 2 };
 struct SelectedBwdArgs {
+  int mode;            // BwdMode
+  int window;          // kBwdWindow: keys t - window + 1 .. t
+  int accumulate;      // != 0: add to dq, dk, dv instead of writing them
+  const int* cu_kv;    // key rows of each sequence (cu_k, or cu_c for compressed keys)
   const bf16_t* q;     // [rows, heads, 128]
-  const bf16_t* k;     // [N_k, kv_heads, 128]
+  const bf16_t* k;     // [N_kv, kv_heads, 128]
   const bf16_t* v;
   const bf16_t* out;   // [rows, heads, 128] forward output
   const bf16_t* dout;  // [rows, heads, 128] its upstream gradient
@@ -227,7 +235,7 @@ struct SelectedBwdArgs {
   int k_sel;
   const int* cu_q;
   const int* cu_k;
-  int batch, rows_total, heads, kv_heads, nb_max, max_seqlen_k;
+  int batch, rows_total, heads, kv_heads, nb_max, max_seqlen_k;  // nb_max: key blocks
   float scale;         // softmax scale (natural domain)
   float* dq;           // [rows, heads, 128]
   float* dk;           // [N_k, kv_heads, 128]
@@ -243,6 +251,10 @@ size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel,
                              int nb_max);
 void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a);
 hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s);
+// dx[j] (+)= sum over the windows c holding token j of dx_c[c] / (valid tokens of c)
+hipError_t launch_pool_bwd(const float* dxc, float* dx, const int* cu, const int* cu_c, int batch,
+                           int n_tokens_max, int width, int kernel, int stride, int accumulate,
+                           hipStream_t s);
 
 // Values transposed per (sequence, KV head, dim) for the prefill branches.
 int transposed_ld(int max_len);

@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--causal", action="store_true", help="prefill-blockmask: lower triangle only")
     ap.add_argument("--workload", choices=["decode", "decode-long", "decode-tiny", "decode-offload",
                                            "prefill-selected", "prefill-nsa", "prefill-blockmask",
-                                           "prefill-selected-bwd"],
+                                           "prefill-selected-bwd", "prefill-nsa-bwd"],
                     default="decode",
                     help="decode: the headline NOSA-1B-shaped decode (default); decode-long: "
                          "CIS-weighted decode of 4 x 131072 tokens; decode-tiny: the float32 "
@@ -76,7 +76,8 @@ def parse():
                          "selected-block attention prefill with given indices (batch 8 x 16384); "
                          "prefill-nsa: the three-branch prefill (65536 tokens, 64 heads); "
                          "prefill-selected-bwd: the gradient of the selected-block attention "
-                         "for the prefill-selected batch")
+                         "for the prefill-selected batch; prefill-nsa-bwd: the gradient of the "
+                         "three-branch prefill (65536 tokens, 64 heads)")
     ap.add_argument("--trace-stats", metavar="CSV", default=None,
                     help="print per-kernel duration statistics (count, mean, median, p10, p90, "
                          "min, max in microseconds) of a rocprofv3 kernel-trace CSV and exit")
@@ -221,6 +222,9 @@ def main():
         return
     if args.workload == "prefill-selected-bwd":
         selected_bwd_main(args, dev)
+        return
+    if args.workload == "prefill-nsa-bwd":
+        nsa_bwd_main(args, dev)
         return
     if args.workload not in ("decode", "decode-long", "decode-tiny"):
         prefill_main(args, dev)
@@ -1069,6 +1073,155 @@ def selected_bwd_main(args, dev):
                                                    t_, 64, scale, don[r], dk_s, dv_s)
         result["cpu_baseline"] = sampled_oracle_baseline(rows_fn, w.total_tokens, w.total_tokens,
                                                          args.cpu_seconds, "query rows")
+    print(json.dumps(result), flush=True)
+
+
+def nsa_bwd_main(args, dev):
+    """Backward of the three-branch prefill (65536 tokens, 64 query heads over 4
+    KV heads, window 512, top-16): one step = the gate gradients and the
+    per-branch output gradients, the selected, window and compressed branches'
+    dq, dk, dv (sharing the output arrays) and the window-mean transpose of the
+    compressed keys' and values' gradients, from the forward's branch outputs,
+    normalisers and block choice (computed once before the timed region).  The
+    kernels run on the vector ALUs in fp32: roofline = algorithmic flops of the
+    longest branch against the unpacked fp32 vector peak."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_compress_amd as nsa
+    from gen import workloads as W
+
+    stream = torch.cuda.Stream(device=dev)
+    steps = args.steps if args.steps != 2800 else 3
+    warmup = args.warmup if args.warmup != 280 else 1
+    D = 128
+    w = W.nsa_prefill()
+    print(f"[bench] workload {w.name} (backward)", file=sys.stderr, flush=True)
+    L, H, Hkv = w.lengths[0], w.heads, w.kv_heads
+    q = W.prefill_query(w, dev)
+    k, v = W.keys_values(w, dev)
+    g = W.gates(w, dev)
+    d_out = W.prefill_out_grad(w, dev)
+    nc = nsa.window_count(L)
+    cu = nsa.cu_seqlens_of(w.lengths, dev)
+    cuc = nsa.cu_seqlens_of([nc], dev)
+    kc = torch.empty((nc, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    nsa.nsa_compress_k(k, kc, cu, cuc, nc)
+    nsa.nsa_compress_k(v, vc, cu, cuc, nc)
+    nb = -(-L // 64)
+    o_cmp, o_sel, o_win = (torch.empty_like(q) for _ in range(3))
+    lse = [torch.empty((L, H), dtype=torch.float32, device=dev) for _ in range(3)]
+    bs = torch.empty((L, Hkv, nb), dtype=torch.float32, device=dev)
+    nsa.nsa_compressed_attn_fwd(q, kc, vc, cu, cu, cuc, L, o_cmp, lse=lse[0], block_scores=bs)
+    idx = torch.empty((L, Hkv, w.topk), dtype=torch.int32, device=dev)
+    nsa.nsa_select_topk(bs, idx, cu, L, w.topk, 0, 0, cu_seqlens_q=cu)
+    nsa.nsa_selected_attn_fwd(q, k, v, idx, cu, L, o_sel, lse=lse[1], cu_seqlens_q=cu)
+    nsa.nsa_window_attn_fwd(q, k, v, cu, cu, L, o_win, window=w.window, lse=lse[2])
+    del bs
+    do_b = [torch.empty_like(q) for _ in range(3)]
+    d_gates = torch.empty((L, H, 3), dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    dkc = torch.empty(kc.shape, dtype=torch.float32, device=dev)
+    dvc = torch.empty(vc.shape, dtype=torch.float32, device=dev)
+    ws_sel = torch.empty(nsa.selected_attn_bwd_workspace_size(1, L, L, H, Hkv, w.topk),
+                         dtype=torch.uint8, device=dev)
+    ws_br = torch.empty(nsa.branch_attn_bwd_workspace_size(L, H), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    parts = {
+        "gates": lambda: nsa.nsa_gates_bwd(d_out, o_cmp, o_sel, o_win, g, *do_b, d_gates),
+        "selected": lambda: nsa.nsa_selected_attn_bwd(q, k, v, o_sel, do_b[1], lse[1], idx, cu, cu,
+                                                      L, dq, dk, dv, workspace=ws_sel),
+        "window": lambda: nsa.nsa_window_attn_bwd(q, k, v, o_win, do_b[2], lse[2], cu, cu, L, dq,
+                                                  dk, dv, window=w.window, accumulate=3,
+                                                  workspace=ws_br),
+        "compressed": lambda: nsa.nsa_compressed_attn_bwd(q, kc, vc, o_cmp, do_b[0], lse[0], cu,
+                                                          cu, cuc, L, dq, dkc, dvc, accumulate=1,
+                                                          workspace=ws_br),
+        "pool_transpose": lambda: (nsa.nsa_compress_bwd(dkc, dk, cu, cuc, L, accumulate=True),
+                                   nsa.nsa_compress_bwd(dvc, dv, cu, cuc, L, accumulate=True)),
+    }
+
+    def fn():
+        for f in parts.values():
+            f()
+    wall_s, gpu_ms = _timed(fn, steps, warmup, stream)
+    # per-part durations: stream events around each part over one more step
+    evs = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for n in parts}
+    with torch.cuda.stream(stream):
+        for n, f in parts.items():
+            evs[n][0].record(stream)
+            f()
+            evs[n][1].record(stream)
+    torch.cuda.synchronize()
+    part_ms = {n: a.elapsed_time(b) for n, (a, b) in evs.items()}
+    t = np.arange(L, dtype=np.int64)
+    nvis = np.where(t >= 31, np.minimum(nc, (t - 31) // 16 + 1), 0)
+    win = np.minimum(t + 1, w.window)
+    ids = idx.cpu().numpy().astype(np.int64)
+    sel = np.where(ids >= 0, np.clip(t[:, None, None] - 64 * ids + 1, 0, 64), 0).sum()
+    G = H // Hkv
+    # per attended (row, head, key): 6 * 128 flops in dq and 8 * 128 in dk/dv
+    per = 14.0 * D
+    flops = {"selected": per * G * float(sel), "window": per * H * float(win.sum()),
+             "compressed": per * H * float(nvis.sum())}
+    tflops = {n: flops[n] / (part_ms[n] * 1e-3) / 1e12 for n in flops}
+    dominant = max(flops, key=lambda n: part_ms[n])
+    ms_per_step = wall_s * 1e3 / steps
+    result = {
+        "metric": f"prefill backward tokens/s ({w.name})",
+        "value": round(L * steps / wall_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V and upstream gradient, sigmoid(N(0,1)) gates; "
+                "no dataset)",
+        "config": {"workload": w.name + "_bwd", "batch": 1, "seq_len": L, "heads": H,
+                   "kv_heads": Hkv, "head_dim": D, "topk": w.topk, "window": w.window},
+        "roofline": {
+            "kernel": f"{dominant} branch (dq and dk/dv kernels)",
+            "bound": "alu",
+            "achieved": round(tflops[dominant], 2),
+            "peak": FP32_VECTOR_UNPACKED_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops[dominant] / FP32_VECTOR_UNPACKED_TFLOPS, 4),
+            "frac_of_bf16_mfma_peak": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops[dominant],
+            "mean_kernel_us": round(part_ms[dominant] * 1e3, 1),
+        },
+        "part_ms": {n: round(x, 3) for n, x in part_ms.items()},
+        "part_tflops": {n: round(x, 2) for n, x in tflops.items()},
+        "timed_gpu_ms": round(gpu_ms, 3),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        f64 = lambda x: x.float().cpu().numpy().astype(np.float64)  # noqa: E731
+        qn, kn, vn, gn, don = f64(q), f64(k), f64(v), f64(g), f64(d_out)
+
+        one, onec = np.array([0, L]), np.array([0, nc])
+
+        def pool():  # what every oracle call redoes once: K and V pooled (twice) and transposed
+            for x in (kn, vn, kn, vn):
+                oracle.mean_pool_varlen(x, one, onec, 32, 16)
+            z = np.zeros((nc,) + kn.shape[1:])
+            oracle.mean_pool_varlen_bwd(z, one, onec, 32, 16, L)
+            oracle.mean_pool_varlen_bwd(z, one, onec, 32, 16, L)
+
+        def rows_fn(rows):
+            oracle.nsa_prefill_rows_grad(qn, kn, vn, gn, don, rows, topk=w.topk, window=w.window)
+        result["cpu_baseline"] = sampled_oracle_baseline(rows_fn, L, L, args.cpu_seconds,
+                                                         "query rows", chunk=32, fixed_fn=pool)
     print(json.dumps(result), flush=True)
 
 

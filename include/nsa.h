@@ -306,9 +306,10 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
  * required; row r of sequence b at t = (r - cu_q[b]) + (L_b - Lq_b)).  `out` and
  * `lse` are the branch forward's output and natural-log normaliser, `d_out` the
  * upstream gradient of that output (for a gated sum, the gate times the
- * gradient of the sum).  accumulate 0: dq and the key/value gradients are
- * written in full (0 for keys no row attends to); 1: they are added to what the
- * arrays hold, so the branches of one step can share dq, dk and dv.  Per head
+ * gradient of the sum: nsa_gates_bwd).  accumulate bit 0 clear: dq is written
+ * in full, set: added to what dq holds; bit 1 likewise for the key and value
+ * gradients (written in full means 0 for keys no row attends to).  With both
+ * bits the branches of one step share dq, dk and dv.  Per head
  * over the row's keys J: dV_J += p dO^T; ds = p * (V_J dO - dO . out);
  * dq += scale ds K_J; dK_J += scale ds q^T.  Key gradients of a block seen by
  * more than 256 rows are summed with fp32 atomics (order may change between
@@ -321,6 +322,10 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
  *   dk_c, dv_c [N_c, kv_heads, 128].  Kernel 32, stride 16.
  * nsa_window_attn_bwd: keys max(0, t - window + 1) .. t; writes dq, dk, dv
  *   [N_k, kv_heads, 128].
+ * nsa_gates_bwd: the gated sum o = g0 o_cmp + g1 o_sel + g2 o_win of
+ *   nsa_prefill_step: d_out, o_cmp, o_sel, o_win [rows, heads, 128] bf16, gates
+ *   [rows, heads, 3] float32 -> do_cmp, do_sel, do_win = g_b d_out (bf16,
+ *   rounded to nearest even) and d_gates [rows, heads, 3] = d_out . o_b (fp32).
  * nsa_compress_bwd: the transpose of nsa_compress_k for fp32 gradients: dx[j]
  *   (+)= sum over the windows c holding token j of dx_c[c] / (valid tokens of
  *   window c); dx_c [N_c, heads, head_dim], dx [N, heads, head_dim], windows
@@ -344,6 +349,10 @@ nsa_status nsa_window_attn_bwd(const void* q, const void* k, const void* v, cons
                                float softmax_scale, int32_t accumulate, float* dq, float* dk,
                                float* dv, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
+nsa_status nsa_gates_bwd(const void* d_out, const void* o_cmp, const void* o_sel,
+                         const void* o_win, nsa_dtype dtype, const float* gates, int32_t rows_total,
+                         int32_t heads, int32_t head_dim, void* do_cmp, void* do_sel,
+                         void* do_win, float* d_gates, hipStream_t stream);
 nsa_status nsa_compress_bwd(const float* dx_c, float* dx, const int32_t* cu_seqlens,
                             const int32_t* cu_seqlens_c, int32_t batch, int32_t max_seqlen,
                             int32_t heads, int32_t head_dim, int32_t kernel, int32_t stride,

@@ -108,6 +108,8 @@ _SIGS = {
                                            c_f32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "nsa_compress_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                         c_i32, c_i32, c_vp]),
+    "nsa_gates_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i32, c_i32,
+                                     c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "nsa_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeParams)]),
     "nsa_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeParams), c_vp, c_sz, c_vp]),
     "nsa_decode_noalloc_scratch_bytes": (c_sz, []),
@@ -320,6 +322,25 @@ def branch_attn_bwd_workspace_size(rows, heads):
     return lib().nsa_branch_attn_bwd_workspace_size(int(rows), int(heads))
 
 
+def _acc_bits(accumulate):
+    """accumulate: False/True (both bits), or an int (bit 0: dq, bit 1: key and
+    value gradients)."""
+    if isinstance(accumulate, bool):
+        return 3 if accumulate else 0
+    return int(accumulate)
+
+
+def nsa_gates_bwd(d_out, o_cmp, o_sel, o_win, gates, do_cmp, do_sel, do_win, d_gates,
+                  stream=None):
+    """Gradients of the gated three-branch sum: per-branch output gradients
+    g_b * d_out (bf16) and d_gates = d_out . o_b (float32 [rows, H, 3])."""
+    rows, H, D = d_out.shape
+    _check(lib().nsa_gates_bwd(_ptr(d_out), _ptr(o_cmp), _ptr(o_sel), _ptr(o_win), _dt(d_out),
+                               _ptr(gates), rows, H, D, _ptr(do_cmp), _ptr(do_sel), _ptr(do_win),
+                               _ptr(d_gates), _stream(stream)))
+    return do_cmp, do_sel, do_win, d_gates
+
+
 def nsa_compressed_attn_bwd(q, k_c, v_c, o_cmp, d_out, lse, cu_seqlens_q, cu_seqlens_k,
                             cu_seqlens_c, max_seqlen_k, dq, dk_c, dv_c, accumulate=False,
                             softmax_scale=0.0, kernel=32, stride=16, workspace=None, stream=None):
@@ -334,7 +355,7 @@ def nsa_compressed_attn_bwd(q, k_c, v_c, o_cmp, d_out, lse, cu_seqlens_q, cu_seq
                                          _ptr(lse), _dt(q), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                          _ptr(cu_seqlens_c), batch, rows, int(max_seqlen_k), H,
                                          H_kv, D, kernel, stride, float(softmax_scale),
-                                         int(bool(accumulate)), _ptr(dq), _ptr(dk_c), _ptr(dv_c),
+                                         _acc_bits(accumulate), _ptr(dq), _ptr(dk_c), _ptr(dv_c),
                                          _ptr(ws), nbytes, _stream(stream)))
     return dq, dk_c, dv_c
 
@@ -350,7 +371,7 @@ def nsa_window_attn_bwd(q, k, v, out, d_out, lse, cu_seqlens_q, cu_seqlens_k, ma
     _check(lib().nsa_window_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(d_out), _ptr(lse),
                                      _dt(q), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, rows,
                                      int(max_seqlen_k), H, H_kv, D, int(window),
-                                     float(softmax_scale), int(bool(accumulate)), _ptr(dq),
+                                     float(softmax_scale), _acc_bits(accumulate), _ptr(dq),
                                      _ptr(dk), _ptr(dv), _ptr(ws), nbytes, _stream(stream)))
     return dq, dk, dv
 

@@ -340,7 +340,7 @@ nsa_status branch_bwd(const char* fn, int mode, const void* q, const void* k, co
   NSA_REQUIRE(dtype == NSA_BF16, NSA_ERR_UNSUPPORTED, "%s: bfloat16 inputs only", fn);
   NSA_REQUIRE(group_ok(heads, kv_heads), NSA_ERR_UNSUPPORTED, "%s: heads %d / kv_heads %d unsupported", fn, heads, kv_heads);
   NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
-  NSA_REQUIRE(accumulate == 0 || accumulate == 1, NSA_ERR_INVALID_ARG, "%s: accumulate must be 0 or 1", fn);
+  NSA_REQUIRE(accumulate >= 0 && accumulate <= 3, NSA_ERR_INVALID_ARG, "%s: accumulate must be 0..3", fn);
   NSA_REQUIRE(cu_q != nullptr, NSA_ERR_INVALID_ARG, "%s: cu_seqlens_q is required (prefill rows)", fn);
   if (rows_total == 0 || batch == 0) return ok();
   NSA_REQUIRE(max_seqlen_k >= 1, NSA_ERR_INVALID_ARG, "%s: rows without keys (max_seqlen_k 0)", fn);
@@ -424,6 +424,26 @@ nsa_status nsa_window_attn_bwd(const void* q, const void* k, const void* v, cons
                     cu_seqlens_k, cu_seqlens_k, batch, rows_total, max_seqlen_k, max_seqlen_k,
                     heads, kv_heads, head_dim, window, softmax_scale, accumulate, dq, dk, dv,
                     workspace, workspace_bytes, stream);
+}
+
+nsa_status nsa_gates_bwd(const void* d_out, const void* o_cmp, const void* o_sel,
+                         const void* o_win, nsa_dtype dtype, const float* gates, int32_t rows_total,
+                         int32_t heads, int32_t head_dim, void* do_cmp, void* do_sel,
+                         void* do_win, float* d_gates, hipStream_t stream) {
+  const char* fn = "nsa_gates_bwd";
+  NSA_REQUIRE(rows_total >= 0 && heads > 0, NSA_ERR_INVALID_ARG, "%s: bad rows_total or heads", fn);
+  NSA_REQUIRE(dtype == NSA_BF16, NSA_ERR_UNSUPPORTED, "%s: bfloat16 only", fn);
+  NSA_REQUIRE(head_dim == nsa::kHeadDim, NSA_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
+  if (rows_total == 0) return ok();
+  NSA_REQUIRE(d_out && o_cmp && o_sel && o_win && gates && do_cmp && do_sel && do_win && d_gates,
+              NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  using B = nsa::bf16_t;
+  return hip_status(nsa::launch_gates_bwd(static_cast<const B*>(d_out), static_cast<const B*>(o_cmp),
+                                          static_cast<const B*>(o_sel), static_cast<const B*>(o_win),
+                                          gates, size_t(rows_total) * heads, static_cast<B*>(do_cmp),
+                                          static_cast<B*>(do_sel), static_cast<B*>(do_win), d_gates,
+                                          stream),
+                    fn);
 }
 
 nsa_status nsa_compress_bwd(const float* dx_c, float* dx, const int32_t* cu_seqlens,

@@ -24,9 +24,9 @@
 // sliding-window branch (keys t - window + 1 .. t) and the compressed branch
 // (the compressed windows c with 16c + 31 <= t, read from K_c and V_c).  There
 // a key block is seen by one contiguous range of query positions, so the dk/dv
-// workgroups walk that range directly.  With `accumulate` every gradient is
-// added to what the output arrays hold, so the branches of one step can share
-// dq, dk and dv.
+// workgroups walk that range directly.  `accumulate` bit 0 adds dq, bit 1 the
+// key and value gradients, to what the output arrays hold, so the branches of
+// one step can share dq, dk and dv.
 // The order within a block's row list, and of the chunk sums, depends on
 // atomics, so dK and dV are summed in an order that can change from call to
 // call (fp32 rounding only).
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     if (o < G * kHeadDim) {
       const int h = o / kHeadDim, d = o % kHeadDim;
       const float x = scale * (red_s[0][h][d] + red_s[1][h][d] + red_s[2][h][d] + red_s[3][h][d]);
-      if (accumulate) dq[head0 * kHeadDim + o] += x; else dq[head0 * kHeadDim + o] = x;
+      if (accumulate & 1) dq[head0 * kHeadDim + o] += x; else dq[head0 * kHeadDim + o] = x;
     }
   }
 }
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   else n = implicit_rows<MODE>(b, id, len, window, cu_q, cu_k, t_lo, row_lo);
   const int e_begin = chunk * kRowsPerChunk;
   if (chunk > 0 && e_begin >= n) return;  // uniform: no rows left for this chunk
-  if (n == 0 && accumulate) return;       // nothing to add
+  if (n == 0 && (accumulate & 2)) return;  // nothing to add
   const int e_end = min(n, e_begin + kRowsPerChunk);
   int tok[4];
   bool tok_ok[4];
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (!tok_ok[i]) continue;
-    if (n <= kRowsPerChunk && accumulate) {
+    if (n <= kRowsPerChunk && (accumulate & 2)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         dk[kv_off[i] + e] += scale * ak[i][e];
@@ -592,7 +592,7 @@ hipError_t launch_bwd_g(const SelectedBwdArgs& a, hipStream_t s) {
                       a.cursor, a.list);
     if (e != hipSuccess) return e;
   }
-  if (!a.accumulate) {
+  if (!(a.accumulate & 2)) {
     e = launch_kernel(kKindBwdLists, bwd_zero_kernel<MODE>, dim3(unsigned(n_slots)),
                       dim3(kBwdThreads), s, static_cast<const int*>(a.cnt), a.cu_q, a.cu_k,
                       a.cu_kv, a.window, a.kv_heads, a.nb_max, a.dk, a.dv);
@@ -701,6 +701,41 @@ hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s) {
     case kBwdCompressed: return launch_bwd_mode<kBwdCompressed>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Gradients of the gated sum o = g0 o_cmp + g1 o_sel + g2 o_win: each branch's
+// output gradient g_b dO (bf16) and dg_b = dO . o_b (fp32); one wave per (row,
+// head), two dims a lane.
+__global__ __launch_bounds__(256) void gates_bwd_kernel(
+    const bf16_t* __restrict__ dout, const bf16_t* __restrict__ o_cmp,
+    const bf16_t* __restrict__ o_sel, const bf16_t* __restrict__ o_win,
+    const float* __restrict__ gates, size_t n_rh, bf16_t* __restrict__ do_cmp,
+    bf16_t* __restrict__ do_sel, bf16_t* __restrict__ do_win, float* __restrict__ d_gates) {
+  const int lane = threadIdx.x & 63;
+  const size_t rh = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (rh >= n_rh) return;
+  const size_t o = rh * kHeadDim + 2 * lane;
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(dout + o);
+  const float d0 = bf16lo(d), d1 = bf16hi(d);
+  const bf16_t* ob[3] = {o_cmp, o_sel, o_win};
+  bf16_t* db[3] = {do_cmp, do_sel, do_win};
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const float g = gates[rh * 3 + j];
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(ob[j] + o);
+    float s = d0 * bf16lo(x) + d1 * bf16hi(x);
+    s = wave_reduce(s, OpSum());
+    *reinterpret_cast<uint32_t*>(db[j] + o) = pack_bf16x2(g * d0, g * d1);
+    if (lane == 0) d_gates[rh * 3 + j] = s;
+  }
+}
+
+hipError_t launch_gates_bwd(const bf16_t* dout, const bf16_t* o_cmp, const bf16_t* o_sel,
+                            const bf16_t* o_win, const float* gates, size_t n_rh, bf16_t* do_cmp,
+                            bf16_t* do_sel, bf16_t* do_win, float* d_gates, hipStream_t s) {
+  if (n_rh == 0) return hipSuccess;
+  return launch_kernel(kKindBwdLists, gates_bwd_kernel, dim3(unsigned((n_rh + 3) / 4)), dim3(256),
+                       s, dout, o_cmp, o_sel, o_win, gates, n_rh, do_cmp, do_sel, do_win, d_gates);
 }
 
 hipError_t launch_pool_bwd(const float* dxc, float* dx, const int* cu, const int* cu_c, int batch,

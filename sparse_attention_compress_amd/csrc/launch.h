@@ -223,7 +223,7 @@ enum BwdMode { kBwdSelected = 0, kBwdWindow = 1, kBwdCompressed = 2 };
 struct SelectedBwdArgs {
   int mode;            // BwdMode
   int window;          // kBwdWindow: keys t - window + 1 .. t
-  int accumulate;      // != 0: add to dq, dk, dv instead of writing them
+  int accumulate;      // bit 0: add to dq; bit 1: add to dk, dv (instead of writing)
   const int* cu_kv;    // key rows of each sequence (cu_k, or cu_c for compressed keys)
   const bf16_t* q;     // [rows, heads, 128]
   const bf16_t* k;     // [N_kv, kv_heads, 128]
@@ -251,6 +251,9 @@ size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel,
                              int nb_max);
 void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a);
 hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s);
+hipError_t launch_gates_bwd(const bf16_t* dout, const bf16_t* o_cmp, const bf16_t* o_sel,
+                            const bf16_t* o_win, const float* gates, size_t n_rh, bf16_t* do_cmp,
+                            bf16_t* do_sel, bf16_t* do_win, float* d_gates, hipStream_t s);
 // dx[j] (+)= sum over the windows c holding token j of dx_c[c] / (valid tokens of c)
 hipError_t launch_pool_bwd(const float* dxc, float* dx, const int* cu, const int* cu_c, int batch,
                            int n_tokens_max, int width, int kernel, int stride, int accumulate,

@@ -7,8 +7,8 @@ tensors the oracle widens; the GPU differs by fp32 accumulation and by
 delta = dO . O taken from the bf16-rounded branch output (2^-9 relative), so
 dq and the key gradients must agree within 1e-2 of their largest oracle
 magnitude and the value gradients within 1e-4.  The composed gradient feeds
-each branch gate * dO rounded to bf16 (2^-9 relative again), so every part of
-it is gated at 1e-2.  The window-mean transpose is plain fp32 arithmetic:
+each branch gate * dO rounded to bf16 (nsa_gates_bwd; 2^-9 relative again), so
+every part of it is gated at 1e-2.  The window-mean transpose is plain fp32 arithmetic:
 1e-6 relative.
 """
 import dataclasses
@@ -197,8 +197,17 @@ def _three_branch_grads(d, g, topk, window):
     o_win = torch.empty_like(d["q"])
     lse_w = torch.empty((rows, H), dtype=F32, device=DEV)
     nsa.nsa_window_attn_fwd(d["q"], d["k"], d["v"], cu_k, cu_k, L, o_win, window=window, lse=lse_w)
-    do = d["d_out"].float()
-    do_b = [(g[:, :, j:j + 1] * do).to(BF16).contiguous() for j in range(3)]
+    do_b = [torch.empty_like(d["d_out"]) for _ in range(3)]
+    d_gates = torch.empty((rows, H, 3), dtype=F32, device=DEV)
+    nsa.nsa_gates_bwd(d["d_out"], o_cmp, o_sel, o_win, g, do_b[0], do_b[1], do_b[2], d_gates)
+    # the gate gradient and the per-branch output gradients: exact products of
+    # the same bf16 values (the branch gradients rounded once to bf16)
+    torch.cuda.synchronize()
+    for j, o_b in enumerate((o_cmp, o_sel, o_win)):
+        want = (g[:, :, j:j + 1].float() * d["d_out"].float()).to(BF16)
+        assert torch.equal(do_b[j], want), f"gate-scaled gradient of branch {j}"
+        ref_g = (d["d_out"].double() * o_b.double()).sum(-1)
+        assert torch.allclose(d_gates[:, :, j].double(), ref_g, rtol=1e-5, atol=1e-5), j
     dq = torch.empty(d["q"].shape, dtype=F32, device=DEV)
     dk = torch.empty(d["k"].shape, dtype=F32, device=DEV)
     dv = torch.empty(d["v"].shape, dtype=F32, device=DEV)
@@ -206,11 +215,11 @@ def _three_branch_grads(d, g, topk, window):
                               dq, dk, dv)
     nsa.nsa_window_attn_bwd(d["q"], d["k"], d["v"], o_win, do_b[2], lse_w, cu_k, cu_k, L, dq, dk,
                             dv, window=window, accumulate=True)
-    # accumulate adds to every output: dq carries the other branches, dk_c and dv_c start at 0
-    dkc = torch.zeros(d["kc"].shape, dtype=F32, device=DEV)
-    dvc = torch.zeros(d["vc"].shape, dtype=F32, device=DEV)
+    # accumulate bit 0 only: dq carries the other branches, dk_c and dv_c are written
+    dkc = torch.full(d["kc"].shape, float("nan"), dtype=F32, device=DEV)
+    dvc = torch.full(d["vc"].shape, float("nan"), dtype=F32, device=DEV)
     nsa.nsa_compressed_attn_bwd(d["q"], d["kc"], d["vc"], o_cmp, do_b[0], lse_c, cu_k, cu_k, cu_c,
-                                L, dq, dkc, dvc, accumulate=True)
+                                L, dq, dkc, dvc, accumulate=1)
     nsa.nsa_compress_bwd(dkc, dk, cu_k, cu_c, L, accumulate=True)
     nsa.nsa_compress_bwd(dvc, dv, cu_k, cu_c, L, accumulate=True)
     torch.cuda.synchronize()

@@ -61,8 +61,10 @@
  *     launching and returns a non-zero nsa_status on failure; nsa_last_error()
  *     then describes it (thread-local string, valid until the next call on
  *     that thread).  NSA_ERR_HIP reports a launch error from hipGetLastError.
- *     Preconditions NOT checked (undefined behaviour if broken): cu_seqlens
- *     contents, unique block ids within one index row, finite inputs.
+ *     Preconditions NOT checked on the release path (undefined behaviour if
+ *     broken): cu_seqlens contents, unique block ids within one index row,
+ *     finite inputs; nsa_set_debug_checks(1) checks the first two (and NaN-free
+ *     block scores) on the device.
  */
 #ifndef NSA_H
 #define NSA_H
@@ -94,6 +96,22 @@ const char* nsa_last_error(void);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t nsa_version(void);
+
+/*
+ * nsa_set_debug_checks -- debug mode for the whole process (off by default);
+ * returns the previous setting.  While on, every entry point that takes
+ * sequence offsets or block lists first checks on the device the preconditions
+ * the release path takes on trust: each cu_seqlens array starts at 0 and never
+ * decreases, no sequence is longer than max_seqlen_k, no sequence has more query
+ * rows than keys or more windows than cover its tokens, the ids of one index row
+ * are distinct, block scores given to nsa_select_topk hold no NaN.  The call
+ * then waits for those checks (the only synchronisation in the library) and
+ * returns NSA_ERR_INVALID_ARG, naming the broken precondition, without
+ * launching its work.  [The varlen layout is the one NOSA-1B source analysis
+ * part 3 masks by (sequence b spans rows cu[b] .. cu[b+1]-1); distinct ids
+ * follow the block lists of TileLang NSA, section 2.]  Not for graph capture.
+ */
+int32_t nsa_set_debug_checks(int32_t on);
 
 /*
  * nsa_profile_next_launch -- measurement hook (not part of the method).  Arms

@@ -78,6 +78,7 @@ _SIGS = {
     "nsa_last_error": (ctypes.c_char_p, []),
     "nsa_version": (c_i32, []),
     "nsa_window_count": (c_i32, [c_i32, c_i32, c_i32, c_i32]),
+    "nsa_set_debug_checks": (c_i32, [c_i32]),
     "nsa_profile_next_launch": (ctypes.c_int, [c_i32, c_vp, c_vp]),
     "nsa_compress_k": (ctypes.c_int, [c_vp, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_i32,
                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
@@ -206,6 +207,12 @@ def window_count(length: int, kernel: int = 32, stride: int = 16, tail: bool = F
     if n < 0:
         raise NsaError(1, f"nsa_window_count: invalid arguments ({length}, {kernel}, {stride})")
     return n
+
+
+def set_debug_checks(on: bool) -> bool:
+    """Debug mode (nsa_set_debug_checks): device checks of the preconditions
+    before every call, which then synchronises.  Returns the previous setting."""
+    return bool(lib().nsa_set_debug_checks(int(bool(on))))
 
 
 def cu_seqlens_of(lengths, device) -> torch.Tensor:

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/nsa.h"
+#include "checks.h"
 #include "launch.h"
 
 namespace {
@@ -52,6 +53,18 @@ float scale_log2_of(float softmax_scale, int head_dim) {
   return sc * nsa::kLog2eHost;
 }
 
+// Debug mode: run the device checks `body` adds to `chk` and fail the call,
+// before any of its work is launched, when one finds a broken precondition.
+#define NSA_DEVICE_CHECKS(fn, stream, body)                                      \
+  do {                                                                           \
+    if (nsa::debug_checks_on()) {                                                \
+      nsa::DebugChecks chk(stream);                                              \
+      body;                                                                      \
+      char msg_[256];                                                            \
+      if (chk.failed(msg_, sizeof(msg_))) return fail(NSA_ERR_INVALID_ARG, "%s: %s", fn, msg_); \
+    }                                                                            \
+  } while (0)
+
 #define NSA_REQUIRE(cond, st, ...) \
   do {                             \
     if (!(cond)) return fail(st, __VA_ARGS__); \
@@ -92,6 +105,8 @@ nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEve
 
 int32_t nsa_version(void) { return 200; }
 
+int32_t nsa_set_debug_checks(int32_t on) { return nsa::set_debug_checks(on); }
+
 int32_t nsa_window_count(int32_t length, int32_t kernel, int32_t stride, int32_t tail_mode) {
   if (length < 0 || kernel < 1 || stride < 1 || (tail_mode != 0 && tail_mode != 1)) return -1;
   if (length == 0) return 0;
@@ -113,6 +128,11 @@ nsa_status nsa_compress_k(const void* x, nsa_dtype x_dtype, void* x_c, nsa_dtype
   NSA_REQUIRE(aligned16(x) && aligned16(x_c), NSA_ERR_INVALID_ARG, "nsa_compress_k: tensors must be 16-byte aligned");
   const long width = long(heads) * head_dim;
   NSA_REQUIRE(width < (1L << 30), NSA_ERR_INVALID_ARG, "nsa_compress_k: row too wide");
+  NSA_DEVICE_CHECKS("nsa_compress_k", stream, {
+    chk.cu(cu_seqlens, batch, -1, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_c, batch, max_windows, nsa::kCheckCuC);
+    chk.windows(cu_seqlens, cu_seqlens_c, batch, kernel, stride);
+  });
   return hip_status(nsa::launch_mean_pool(x, x_dtype == NSA_BF16, x_c, xc_dtype == NSA_BF16,
                                           cu_seqlens, cu_seqlens_c, batch, max_windows,
                                           int(width), kernel, stride, 0, stream),
@@ -128,6 +148,11 @@ nsa_status nsa_cis_mean_pool_varlen(const float* cis, float* cis_pooled, const i
   NSA_REQUIRE(kernel >= 1 && stride >= 1, NSA_ERR_INVALID_ARG, "nsa_cis_mean_pool_varlen: kernel and stride must be >= 1");
   if (batch == 0 || max_windows == 0) return ok();
   NSA_REQUIRE(cis && cis_pooled && cu_seqlens && cu_seqlens_c, NSA_ERR_INVALID_ARG, "nsa_cis_mean_pool_varlen: null pointer");
+  NSA_DEVICE_CHECKS("nsa_cis_mean_pool_varlen", stream, {
+    chk.cu(cu_seqlens, batch, -1, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_c, batch, max_windows, nsa::kCheckCuC);
+    chk.windows(cu_seqlens, cu_seqlens_c, batch, kernel, stride);
+  });
   return hip_status(nsa::launch_mean_pool(cis, 0, cis_pooled, 0, cu_seqlens, cu_seqlens_c, batch,
                                           max_windows, heads, kernel, stride, 0, stream),
                     "nsa_cis_mean_pool_varlen");
@@ -179,6 +204,11 @@ nsa_status nsa_compressed_scores(const void* q, nsa_dtype q_dtype, const void* k
   a.kv_heads = kv_heads;
   a.scale_log2 = scale_log2_of(softmax_scale, head_dim);
   a.ws = nsa::scores_ws_carve(workspace, batch, kv_heads, heads / kv_heads, max_seqlen_k);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_c, batch, -1, nsa::kCheckCuC);
+    chk.windows(cu_seqlens_k, cu_seqlens_c, batch, kernel, stride);
+  });
   return hip_status(nsa::launch_decode_scores(a, stream), fn);
 }
 
@@ -201,6 +231,12 @@ nsa_status nsa_select_topk(const float* block_scores, int32_t* indices, const in
     NSA_REQUIRE(rows_total == batch, NSA_ERR_INVALID_ARG, "%s: decode needs rows_total == batch", fn);
   if (rows_total == 0 || batch == 0) return ok();
   NSA_REQUIRE(block_scores && indices && cu_seqlens_k, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_q, batch, -1, nsa::kCheckCuQ);
+    chk.q_within_k(cu_seqlens_q, cu_seqlens_k, batch);
+    chk.no_nan(block_scores, long(rows_total) * kv_heads * n_blocks_max);
+  });
   return hip_status(nsa::launch_select_topk(block_scores, indices, cu_seqlens_q, cu_seqlens_k, batch,
                                             rows_total, kv_heads, n_blocks_max, k, n_init, n_local,
                                             stream),
@@ -241,6 +277,12 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
   NSA_REQUIRE(workspace != nullptr || need == 0, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
   NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
   const nsa::AttnWs ws = nsa::attn_ws_carve(workspace, rows_total, kv_heads, heads / kv_heads, k_sel, decode);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_q, batch, -1, nsa::kCheckCuQ);
+    chk.q_within_k(cu_seqlens_q, cu_seqlens_k, batch);
+    chk.unique_ids(indices, long(rows_total) * kv_heads, k_sel);
+  });
   return hip_status(nsa::launch_selected_attn(q, k, v, dtype == NSA_BF16, indices, k_sel, cis, out,
                                               lse, cu_seqlens_q, cu_seqlens_k, batch, rows_total,
                                               heads, kv_heads, scale_log2_of(softmax_scale, head_dim),
@@ -315,6 +357,12 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
   a.mode = nsa::kBwdSelected;
   a.cu_kv = cu_seqlens_k;
   nsa::selected_bwd_ws_carve(workspace, a);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_q, batch, -1, nsa::kCheckCuQ);
+    chk.q_within_k(cu_seqlens_q, cu_seqlens_k, batch);
+    chk.unique_ids(indices, long(rows_total) * kv_heads, k_sel);
+  });
   return hip_status(nsa::launch_selected_bwd(a, stream), fn);
 }
 
@@ -380,6 +428,15 @@ nsa_status branch_bwd(const char* fn, int mode, const void* q, const void* k, co
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_k, batch, max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(cu_q, batch, -1, nsa::kCheckCuQ);
+    chk.q_within_k(cu_q, cu_k, batch);
+    if (cu_kv != cu_k) {
+      chk.cu(cu_kv, batch, max_keys, nsa::kCheckCuC);
+      chk.windows(cu_k, cu_kv, batch, nsa::kKernel, nsa::kStride);
+    }
+  });
   return hip_status(nsa::launch_selected_bwd(a, stream), fn);
 }
 
@@ -461,6 +518,11 @@ nsa_status nsa_compress_bwd(const float* dx_c, float* dx, const int32_t* cu_seql
   if (batch == 0 || max_seqlen == 0) return ok();
   NSA_REQUIRE(dx_c && dx && cu_seqlens && cu_seqlens_c, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
   NSA_REQUIRE(aligned16(dx_c) && aligned16(dx), NSA_ERR_INVALID_ARG, "%s: dx_c and dx must be 16-byte aligned", fn);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_seqlens, batch, max_seqlen, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_c, batch, -1, nsa::kCheckCuC);
+    chk.windows(cu_seqlens, cu_seqlens_c, batch, kernel, stride);
+  });
   return hip_status(nsa::launch_pool_bwd(dx_c, dx, cu_seqlens, cu_seqlens_c, batch, max_seqlen,
                                          heads * head_dim, kernel, stride, accumulate, stream),
                     fn);
@@ -634,6 +696,11 @@ nsa_status nsa_decode_step_offload(const nsa_decode_params* p, const nsa_offload
   int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.dec.indices);
   // logits and the stand-alone selection (the ids are needed before any K/V moves)
   nsa::DecodeScoresArgs a = decode_scores_args(p, base, lay.dec, idx);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(p->cu_seqlens_k, p->batch, p->max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(p->cu_seqlens_c, p->batch, -1, nsa::kCheckCuC);
+    chk.windows(p->cu_seqlens_k, p->cu_seqlens_c, p->batch, p->kernel, p->stride);
+  });
   hipError_t e = nsa::launch_decode_scores(a, stream);
   if (e != hipSuccess) return hip_status(e, fn);
   nsa::OffloadArgs oa{};
@@ -682,6 +749,11 @@ nsa_status nsa_decode_step(const nsa_decode_params* p, void* workspace, size_t w
   const float sl2 = scale_log2_of(p->softmax_scale, p->head_dim);
   nsa::DecodeScoresArgs a = decode_scores_args(p, base, lay, idx);
   const nsa::AttnWs aws = nsa::attn_ws_carve(base + lay.attn, p->batch, p->kv_heads, G, p->topk, 1);
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(p->cu_seqlens_k, p->batch, p->max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(p->cu_seqlens_c, p->batch, -1, nsa::kCheckCuC);
+    chk.windows(p->cu_seqlens_k, p->cu_seqlens_c, p->batch, p->kernel, p->stride);
+  });
   const int nb_max = (p->max_seqlen_k + p->block_size - 1) / p->block_size;
   if (p->dtype == NSA_BF16 && nb_max <= nsa::kFusedMaxBlocks && p->topk <= nsa::kFusedMaxSel) {
     // logits, then selection and attention in one launch, then the merge
@@ -784,6 +856,13 @@ nsa_status nsa_compressed_attn_fwd(const void* q, const void* k_c, const void* v
   a.lse_nat = lse;
   a.block_scores = block_scores;
   a.nb_max = n_blocks_max;
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_q, batch, -1, nsa::kCheckCuQ);
+    chk.q_within_k(cu_seqlens_q, cu_seqlens_k, batch);
+    chk.cu(cu_seqlens_c, batch, -1, nsa::kCheckCuC);
+    chk.windows(cu_seqlens_k, cu_seqlens_c, batch, kernel, stride);
+  });
   return hip_status(nsa::launch_compressed_prefill(a, stream), fn);
 }
 
@@ -810,6 +889,7 @@ nsa_status nsa_blockmask_attn_fwd(const void* q, const void* k, const void* v, n
   const size_t need = nsa_blockmask_attn_workspace_size(batch, max_seqlen, heads);
   NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
   NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  NSA_DEVICE_CHECKS(fn, stream, chk.cu(cu_seqlens, batch, max_seqlen, nsa::kCheckCuK));
   return hip_status(nsa::launch_blockmask_attn(
                         static_cast<const nsa::bf16_t*>(q), static_cast<const nsa::bf16_t*>(k),
                         static_cast<const nsa::bf16_t*>(v), mask, causal != 0,
@@ -857,6 +937,11 @@ nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_
   a.out = out;
   a.out_f32 = out_dtype == NSA_F32;
   a.lse_nat = lse;
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(cu_seqlens_q, batch, -1, nsa::kCheckCuQ);
+    chk.q_within_k(cu_seqlens_q, cu_seqlens_k, batch);
+  });
   return hip_status(nsa::launch_window_prefill(a, stream), fn);
 }
 
@@ -942,6 +1027,13 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   int32_t* idx = p->indices ? p->indices : reinterpret_cast<int32_t*>(base + lay.indices);
   const float sl2 = scale_log2_of(p->softmax_scale, p->head_dim);
   const int width = p->kv_heads * p->head_dim;
+  NSA_DEVICE_CHECKS(fn, stream, {
+    chk.cu(p->cu_seqlens_k, p->batch, p->max_seqlen_k, nsa::kCheckCuK);
+    chk.cu(p->cu_seqlens_q, p->batch, -1, nsa::kCheckCuQ);
+    chk.q_within_k(p->cu_seqlens_q, p->cu_seqlens_k, p->batch);
+    chk.cu(p->cu_seqlens_c, p->batch, -1, nsa::kCheckCuC);
+    chk.windows(p->cu_seqlens_k, p->cu_seqlens_c, p->batch, p->kernel, p->stride);
+  });
   // 1. compressed keys and values
   hipError_t e = hipSuccess;
   if (lay.max_windows > 0) {

@@ -32,6 +32,7 @@
 // call (fp32 rounding only).
 #include <algorithm>
 
+#include "bwd_keys.h"
 #include "common.h"
 #include "launch.h"
 
@@ -43,51 +44,6 @@ constexpr int kBwdThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kRowsPerChunk = 256;  // rows of a block's list one dk/dv workgroup takes
 
-__device__ __forceinline__ void bwd_row_position(int row, const int* __restrict__ cu_q,
-                                                 const int* __restrict__ cu_k, int batch, int& b,
-                                                 int& t) {
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
-  }
-  b = lo;
-  t = (row - cu_q[b]) + ((cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]));
-}
-
-// Whether key j (a row of the key tensor, 0-based within its sequence, klen
-// keys) takes part in the attention of query position t.
-template <int MODE>
-__device__ __forceinline__ bool key_visible(int j, int t, int klen, int window) {
-  if constexpr (MODE == kBwdSelected) return j <= t;
-  else if constexpr (MODE == kBwdWindow) return j <= t && j > t - window;
-  else return j < klen && kStride * j + kKernel - 1 <= t;
-}
-
-// Query positions that see key block `id` of sequence b in an implicit mode:
-// t_lo .. t_lo + n - 1 (clipped to the sequence's query rows, row
-// cu_q[b] + t - shift); returns n.
-template <int MODE>
-__device__ __forceinline__ int implicit_rows(int b, int id, int klen, int window,
-                                             const int* __restrict__ cu_q,
-                                             const int* __restrict__ cu_k, int& t_lo,
-                                             int& row_lo) {
-  const int len = cu_k[b + 1] - cu_k[b];
-  const int shift = len - (cu_q[b + 1] - cu_q[b]);
-  int lo, hi;
-  if constexpr (MODE == kBwdWindow) {
-    lo = kBlock * id;
-    hi = min(kBlock * id + kBlock - 1, klen - 1) + window - 1;
-  } else {
-    lo = kStride * (kBlock * id) + kKernel - 1;
-    hi = len - 1;
-  }
-  lo = max(lo, shift);
-  hi = min(hi, len - 1);
-  t_lo = lo;
-  row_lo = cu_q[b] + lo - shift;
-  return max(0, hi - lo + 1);
-}
 
 // delta[row, h] = dO . O (one wave per (row, head), two dims a lane); the
 // per-block row counts are cleared by the same launch.
@@ -182,8 +138,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fill_kernel(
 template <int MODE>
 __global__ __launch_bounds__(kBwdThreads) void bwd_zero_kernel(
     const int* __restrict__ cnt, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
-    const int* __restrict__ cu_kv, int window, int kv_heads, int nb_max, float* __restrict__ dk,
-    float* __restrict__ dv) {
+    const int* __restrict__ cu_kv, int window, int kv_heads, int nb_max, int rows_per_chunk,
+    float* __restrict__ dk, float* __restrict__ dv) {
   const int slot = blockIdx.x;
   const int id = slot % nb_max;
   const int g = (slot / nb_max) % kv_heads;
@@ -197,7 +153,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_zero_kernel(
     int t_lo, row_lo;
     n = implicit_rows<MODE>(b, id, len, window, cu_q, cu_k, t_lo, row_lo);
   }
-  if (n <= kRowsPerChunk) return;
+  if (n <= rows_per_chunk) return;
   const int tok = kBlock * id + (threadIdx.x >> 2);
   if (tok >= len) return;
   const size_t o = (size_t(kstart + tok) * kv_heads + g) * kHeadDim + 32 * (threadIdx.x & 3);
@@ -592,11 +548,25 @@ hipError_t launch_bwd_g(const SelectedBwdArgs& a, hipStream_t s) {
                       a.cursor, a.list);
     if (e != hipSuccess) return e;
   }
+  // dk/dv on the matrix cores (bwd_mfma.hip), chunks of mfma_bwd_rows_per_chunk()
+  // rows; the vector-ALU kernels below remain for comparison (a.valu)
   if (!(a.accumulate & 2)) {
     e = launch_kernel(kKindBwdLists, bwd_zero_kernel<MODE>, dim3(unsigned(n_slots)),
                       dim3(kBwdThreads), s, static_cast<const int*>(a.cnt), a.cu_q, a.cu_k,
-                      a.cu_kv, a.window, a.kv_heads, a.nb_max, a.dk, a.dv);
+                      a.cu_kv, a.window, a.kv_heads, a.nb_max,
+                      a.valu ? kRowsPerChunk : mfma_bwd_rows_per_chunk(), a.dk, a.dv);
     if (e != hipSuccess) return e;
+  }
+  if (!a.valu) {
+    if (MODE == kBwdSelected) {  // dq from the row lists on the vector ALUs, dk/dv on MFMA
+      e = launch_kernel(kKindBwdQ, bwd_dq_kernel<G, MODE>,
+                        dim3(unsigned(a.rows_total) * a.kv_heads), dim3(kBwdThreads), s, a.q, a.k,
+                        a.v, a.dout, a.lse, static_cast<const float*>(a.delta), a.indices, a.k_sel,
+                        a.cu_q, a.cu_k, a.cu_kv, a.window, a.accumulate, a.batch, a.heads,
+                        a.kv_heads, a.scale * kLog2eHost, a.scale, a.dq);
+      if (e != hipSuccess) return e;
+    }
+    return launch_bwd_mfma(a, s);
   }
   const float scale_log2 = a.scale * kLog2eHost;
   e = launch_kernel(kKindBwdQ, bwd_dq_kernel<G, MODE>, dim3(unsigned(a.rows_total) * a.kv_heads),

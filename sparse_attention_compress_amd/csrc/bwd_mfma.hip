@@ -1,0 +1,425 @@
+// Attention backward on the matrix cores (bf16 operands, fp32 accumulation).
+//
+// What is computed is what backward.hip computes (the exact gradient of each
+// prefill branch; DeepSeek NSA with Triton, introduction and section 2.3, and
+// section 1.1 for the branches): per (row, query head h of KV group g) over the
+// row's keys J, with p = exp(scale q.k - lse) from the forward's normaliser,
+//   dV_J += p dO^T,  ds = p * (V_J dO - delta),  delta = dO . O,
+//   dq = scale ds K_J,  dK_J += scale ds q^T.
+// The contractions are dense 16 x 16 tiles once the work is arranged by tiles of
+// 16 "query vectors" (a query vector is one (row, head) pair of a group: 16/G
+// rows of G heads) against 16 keys:
+//
+// bwd_dkdv_mfma_kernel -- key-block stationary.  A workgroup holds one 64-key
+//   block of one (sequence, KV head) (wave w: keys 16w .. 16w+15, its K and V
+//   rows in registers as MFMA B operands) and walks the query tiles that see the
+//   block (a row list for the selected branch, one contiguous range of
+//   positions for the window and compressed branches).  Each tile's q and dO
+//   rows are staged in LDS once for the four waves, both as rows and transposed.
+//   Per tile and wave: S = Q K^T and dP = dO V^T on four v_mfma_f32_16x16x32_bf16
+//   each; their accumulators hold (query 4r4+e, key c16), which is exactly the B
+//   operand of the 16x16x16 tiles dV^T += dO^T P and dK^T += Q^T dS (contraction
+//   over the 16 query vectors), so P and dS go to the matrix cores as packed
+//   registers; dO^T and Q^T come from the transposed LDS copy.
+// bwd_dq_mfma_kernel -- query-tile stationary (window and compressed branches).
+//   A workgroup holds four query tiles (one per wave; consecutive rows, which
+//   see nearly the same keys) with Q and dO in registers as B operands, and
+//   walks the 64-key blocks they see, each staged in LDS once for the four
+//   waves (K rows, K transposed, V rows).  Per 16-key slice: S^T = K Q^T and
+//   dP^T = V dO^T (accumulators (key 4r4+e, query c16)), then dQ^T += K^T dS^T
+//   with dS^T packed straight into the B operand.
+// Masked keys (outside the row's key set, or past the sequence) get p = 0.
+#include <algorithm>
+
+#include "bwd_keys.h"
+#include "common.h"
+#include "launch.h"
+
+namespace nsa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kRowPad = kHeadDim + 8;  // bf16 per staged row (272 B: 16 rows on distinct banks)
+constexpr int kTPad = 16 + 4;          // bf16 per transposed row of a query tile
+constexpr int kKTPad = 64 + 8;         // bf16 per transposed row of a key block
+constexpr int kMfmaRowsPerChunk = 512; // rows of a key block's list one dk/dv workgroup takes
+
+__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint2 pack4(const float x[4]) {
+  const bf16x2_t lo = {(__bf16)x[0], (__bf16)x[1]};
+  const bf16x2_t hi = {(__bf16)x[2], (__bf16)x[3]};
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// One staged query tile: 16 query vectors' q and dO rows, both as rows and
+// transposed (dim-major), with their log2 normalisers, deltas and positions
+// (-1: no query vector in that slot).
+struct QTileLds {
+  bf16_t q[16 * kRowPad];
+  bf16_t d[16 * kRowPad];
+  bf16_t qt[kHeadDim * kTPad];
+  bf16_t dt[kHeadDim * kTPad];
+  float lse2[16];
+  float delta[16];
+  int t[16];
+};
+
+// A query tile in flight: thread tid holds 16-byte chunk (query vector tid / 16,
+// dims 8 (tid % 16) .. +7) of q and of dO; threads 0..15 its vector's scalars.
+struct QTileRegs {
+  uint4 q, d;
+  float lse2, delta;
+  int t;
+};
+
+__device__ __forceinline__ void stash_qtile(QTileLds& T, const QTileRegs& r) {
+  const int tid = threadIdx.x, v = tid >> 4, c = tid & 15;
+  *reinterpret_cast<uint4*>(&T.q[v * kRowPad + 8 * c]) = r.q;
+  *reinterpret_cast<uint4*>(&T.d[v * kRowPad + 8 * c]) = r.d;
+  const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+  const uint32_t dw[4] = {r.d.x, r.d.y, r.d.z, r.d.w};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    T.qt[(8 * c + 2 * w) * kTPad + v].bits = uint16_t(qw[w]);
+    T.qt[(8 * c + 2 * w + 1) * kTPad + v].bits = uint16_t(qw[w] >> 16);
+    T.dt[(8 * c + 2 * w) * kTPad + v].bits = uint16_t(dw[w]);
+    T.dt[(8 * c + 2 * w + 1) * kTPad + v].bits = uint16_t(dw[w] >> 16);
+  }
+  if (tid < 16) {
+    T.lse2[tid] = r.lse2;
+    T.delta[tid] = r.delta;
+    T.t[tid] = r.t;
+  }
+}
+
+// dK, dV of one (sequence, KV head, 64-key block) over one chunk of the rows
+// that see it.  Grid: (slot, chunk).
+template <int G, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int* __restrict__ cnt, const int* __restrict__ off,
+    const int2* __restrict__ list, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    const int* __restrict__ cu_kv, int window, int accumulate, int heads, int kv_heads,
+    int nb_max, float scale_log2, float scale, float* __restrict__ dk, float* __restrict__ dv) {
+  constexpr int kRowsPerTile = 16 / G;
+  __shared__ QTileLds T[2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const int slot = blockIdx.x, chunk = blockIdx.y;
+  const int id = slot % nb_max;
+  const int g = (slot / nb_max) % kv_heads;
+  const int b = slot / (nb_max * kv_heads);
+  const int kstart = cu_kv[b], len = cu_kv[b + 1] - kstart;
+  if (kBlock * id >= len) return;  // uniform: no key of this sequence here
+  int n, t_lo = 0, row_lo = 0;
+  if constexpr (MODE == kBwdSelected) n = cnt[slot];
+  else n = implicit_rows<MODE>(b, id, len, window, cu_q, cu_k, t_lo, row_lo);
+  const int e_begin = chunk * kMfmaRowsPerChunk;
+  if (chunk > 0 && e_begin >= n) return;   // uniform: no rows left for this chunk
+  if (n == 0 && (accumulate & 2)) return;  // nothing to add
+  const int e_end = min(n, e_begin + kMfmaRowsPerChunk);
+  const int first = MODE == kBwdSelected ? off[slot] : 0;
+  auto entry = [&](int e) {
+    if constexpr (MODE == kBwdSelected) return list[first + e];
+    else return make_int2(row_lo + e, t_lo + e);
+  };
+
+  // this wave's 16 keys as B operands: key c16 of the slice, dims 32i + 8 r4 .. +8
+  const size_t rs = size_t(kv_heads) * kHeadDim;
+  const int key = kBlock * id + 16 * wave + c16;
+  const bool key_ok = key < len;
+  const bf16_t* krow = k + (size_t(kstart + min(key, len - 1))) * rs + size_t(g) * kHeadDim;
+  const bf16_t* vrow = v + (size_t(kstart + min(key, len - 1))) * rs + size_t(g) * kHeadDim;
+  uint4 kb[4], vb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kb[i] = ld16(krow + 32 * i + 8 * r4);
+    vb[i] = ld16(vrow + 32 * i + 8 * r4);
+  }
+  f32x4_t acck[8], accv[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    acck[dt] = {0.f, 0.f, 0.f, 0.f};
+    accv[dt] = {0.f, 0.f, 0.f, 0.f};
+  }
+
+  // query tile `e0`: rows entry(e0) .. entry(e0 + 16/G - 1), G heads each
+  auto fetch = [&](int e0, QTileRegs& r) {
+    const int qv = tid >> 4, c = tid & 15;
+    const int e = e0 + qv / G;
+    const bool ok = e < e_end;
+    const int2 rt = entry(min(e, e_end - 1));
+    const size_t hrow = size_t(rt.x) * heads + size_t(g) * G + (qv % G);
+    r.q = ok ? ld16(q + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    r.d = ok ? ld16(dout + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    if (tid < 16) {  // the scalars of query vector tid
+      const int es = e0 + tid / G;
+      const bool oks = es < e_end;
+      const int2 rs_ = entry(min(es, e_end - 1));
+      const size_t hs = size_t(rs_.x) * heads + size_t(g) * G + (tid % G);
+      r.lse2 = oks ? lse[hs] * kLog2e : 0.f;
+      r.delta = oks ? delta[hs] : 0.f;
+      r.t = oks ? rs_.y : -1;
+    }
+  };
+
+  const int n_tiles = (e_end - e_begin + kRowsPerTile - 1) / kRowsPerTile;
+  QTileRegs R;
+  if (n_tiles > 0) {
+    fetch(e_begin, R);
+    stash_qtile(T[0], R);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) {
+    const QTileLds& Tc = T[it & 1];
+    if (it + 1 < n_tiles) fetch(e_begin + (it + 1) * kRowsPerTile, R);
+    // S = Q K^T and dP = dO V^T: (query 4 r4 + e, key c16)
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = mfma32(*reinterpret_cast<const uint4*>(&Tc.q[c16 * kRowPad + 32 * i + 8 * r4]), kb[i], s);
+      dp = mfma32(*reinterpret_cast<const uint4*>(&Tc.d[c16 * kRowPad + 32 * i + 8 * r4]), vb[i], dp);
+    }
+    float p[4], ds[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int qv = 4 * r4 + e;
+      const bool ok = key_ok && key_visible<MODE>(key, Tc.t[qv], len, window) && Tc.t[qv] >= 0;
+      p[e] = ok ? fast_exp2(s[e] * scale_log2 - Tc.lse2[qv]) : 0.f;
+      ds[e] = p[e] * (dp[e] - Tc.delta[qv]);
+    }
+    const uint2 pb = pack4(p), dsb = pack4(ds);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint2 dta = *reinterpret_cast<const uint2*>(&Tc.dt[(16 * dt + c16) * kTPad + 4 * r4]);
+      const uint2 qta = *reinterpret_cast<const uint2*>(&Tc.qt[(16 * dt + c16) * kTPad + 4 * r4]);
+      accv[dt] = mfma16(dta, pb, accv[dt]);
+      acck[dt] = mfma16(qta, dsb, acck[dt]);
+    }
+    if (it + 1 < n_tiles) stash_qtile(T[(it + 1) & 1], R);
+    __syncthreads();
+  }
+
+  // lane (c16, r4) holds dims 16 dt + 4 r4 .. +3 of key c16 of the wave's slice
+  if (!key_ok) return;
+  const size_t o = (size_t(kstart + key) * kv_heads + g) * kHeadDim + 4 * r4;
+  const bool single = n <= kMfmaRowsPerChunk;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    float4 kx = make_float4(scale * acck[dt][0], scale * acck[dt][1], scale * acck[dt][2],
+                            scale * acck[dt][3]);
+    float4 vx = make_float4(accv[dt][0], accv[dt][1], accv[dt][2], accv[dt][3]);
+    float4* pk = reinterpret_cast<float4*>(dk + o + 16 * dt);
+    float4* pv = reinterpret_cast<float4*>(dv + o + 16 * dt);
+    if (single && !(accumulate & 2)) {
+      *pk = kx;
+      *pv = vx;
+    } else if (single) {
+      const float4 a = *pk, c = *pv;
+      *pk = make_float4(a.x + kx.x, a.y + kx.y, a.z + kx.z, a.w + kx.w);
+      *pv = make_float4(c.x + vx.x, c.y + vx.y, c.z + vx.z, c.w + vx.w);
+    } else {
+      float* fk = dk + o + 16 * dt;
+      float* fv = dv + o + 16 * dt;
+      atomicAdd(fk + 0, kx.x); atomicAdd(fk + 1, kx.y); atomicAdd(fk + 2, kx.z); atomicAdd(fk + 3, kx.w);
+      atomicAdd(fv + 0, vx.x); atomicAdd(fv + 1, vx.y); atomicAdd(fv + 2, vx.z); atomicAdd(fv + 3, vx.w);
+    }
+  }
+}
+
+// One staged 64-key block for the dq kernel: K rows, K transposed, V rows.
+struct KBlockLds {
+  bf16_t k[64 * kRowPad];
+  bf16_t kt[kHeadDim * kKTPad];
+  bf16_t v[64 * kRowPad];
+};
+
+// dq of four query tiles of one (sequence, KV head): grid (row group, kv head,
+// sequence); the window and compressed key sets.
+template <int G, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    const int* __restrict__ cu_kv, int window, int accumulate, int heads, int kv_heads,
+    float scale_log2, float scale, float* __restrict__ dq) {
+  constexpr int kRowsPerTile = 16 / G;
+  constexpr int kRowsPerWg = 4 * kRowsPerTile;
+  __shared__ KBlockLds S;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
+  const int len = cu_k[b + 1] - cu_k[b];
+  const int shift = len - lq;
+  const int rbase = blockIdx.x * kRowsPerWg;
+  if (rbase >= lq) return;  // uniform
+  const int kstart = cu_kv[b], klen = cu_kv[b + 1] - kstart;
+
+  // this wave's query tile: column c16 = (row rbase + 16/G * wave + c16 / G, head c16 % G)
+  const int rr = rbase + kRowsPerTile * wave + c16 / G;
+  const bool col_ok = rr < lq;
+  const int t = col_ok ? rr + shift : -1;
+  const size_t hrow = size_t(q0 + min(rr, lq - 1)) * heads + size_t(g) * G + (c16 % G);
+  uint4 qb[4], db[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qb[i] = col_ok ? ld16(q + hrow * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+    db[i] = col_ok ? ld16(dout + hrow * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const float lse2 = col_ok ? lse[hrow] * kLog2e : 0.f;
+  const float dlt = col_ok ? delta[hrow] : 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = {0.f, 0.f, 0.f, 0.f};
+
+  // key blocks seen by the workgroup's rows
+  const int t_first = rbase + shift;
+  const int t_last = min(rbase + kRowsPerWg, lq) - 1 + shift;
+  int blo = 0, bhi = -1;
+  if constexpr (MODE == kBwdWindow) {
+    blo = max(0, t_first - window + 1) / kBlock;
+    bhi = min(t_last, klen - 1) / kBlock;
+  } else {
+    const int nvis = t_last >= kKernel - 1 ? min(klen, (t_last - (kKernel - 1)) / kStride + 1) : 0;
+    bhi = (nvis + kBlock - 1) / kBlock - 1;
+  }
+
+  // staging: thread tid moves chunks c = tid + 256 u (u < 4) of K and of V:
+  // key c / 16, dims 8 (c % 16) .. +7
+  const size_t rs = size_t(kv_heads) * kHeadDim;
+  uint4 pk[4], pv[4];
+  auto fetch = [&](int blk) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u;
+      const int kk = kBlock * blk + (c >> 4);
+      const size_t ro = size_t(kstart + min(kk, klen - 1)) * rs + size_t(g) * kHeadDim + 8 * (c & 15);
+      pk[u] = ld16(k + ro);
+      pv[u] = ld16(v + ro);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u, kr = c >> 4, ch = c & 15;
+      *reinterpret_cast<uint4*>(&S.k[kr * kRowPad + 8 * ch]) = pk[u];
+      *reinterpret_cast<uint4*>(&S.v[kr * kRowPad + 8 * ch]) = pv[u];
+      const uint32_t w4[4] = {pk[u].x, pk[u].y, pk[u].z, pk[u].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        S.kt[(8 * ch + 2 * w) * kKTPad + kr].bits = uint16_t(w4[w]);
+        S.kt[(8 * ch + 2 * w + 1) * kKTPad + kr].bits = uint16_t(w4[w] >> 16);
+      }
+    }
+  };
+
+  if (blo <= bhi) fetch(blo);
+  for (int blk = blo; blk <= bhi; ++blk) {
+    __syncthreads();  // the previous block is no longer read
+    stash();
+    __syncthreads();
+    if (blk + 1 <= bhi) fetch(blk + 1);
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      // S^T = K Q^T and dP^T = V dO^T: (key 16 sl + 4 r4 + e, query c16)
+      f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st = mfma32(*reinterpret_cast<const uint4*>(&S.k[(16 * sl + c16) * kRowPad + 32 * i + 8 * r4]), qb[i], st);
+        dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[(16 * sl + c16) * kRowPad + 32 * i + 8 * r4]), db[i], dpt);
+      }
+      float dst[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = kBlock * blk + 16 * sl + 4 * r4 + e;
+        const bool ok = t >= 0 && kk < klen && key_visible<MODE>(kk, t, klen, window);
+        const float p = ok ? fast_exp2(st[e] * scale_log2 - lse2) : 0.f;
+        dst[e] = p * (dpt[e] - dlt);
+      }
+      const uint2 dsb = pack4(dst);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint2 kta = *reinterpret_cast<const uint2*>(&S.kt[(16 * dt + c16) * kKTPad + 16 * sl + 4 * r4]);
+        acc[dt] = mfma16(kta, dsb, acc[dt]);
+      }
+    }
+  }
+  // lane (c16, r4): dims 16 dt + 4 r4 .. +3 of query vector c16
+  if (!col_ok) return;
+  float* out = dq + hrow * kHeadDim + 4 * r4;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    float4 x = make_float4(scale * acc[dt][0], scale * acc[dt][1], scale * acc[dt][2], scale * acc[dt][3]);
+    float4* po = reinterpret_cast<float4*>(out + 16 * dt);
+    if (accumulate & 1) {
+      const float4 a = *po;
+      x = make_float4(a.x + x.x, a.y + x.y, a.z + x.z, a.w + x.w);
+    }
+    *po = x;
+  }
+}
+
+template <int G, int MODE>
+hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
+  const int n_slots = a.batch * a.kv_heads * a.nb_max;
+  const float scale_log2 = a.scale * kLog2eHost;
+  const int max_rows = MODE == kBwdWindow ? std::min(a.max_seqlen_k, kBlock + a.window - 1)
+                                          : a.max_seqlen_k;
+  const unsigned n_chunk = unsigned((max_rows + kMfmaRowsPerChunk - 1) / kMfmaRowsPerChunk);
+  hipError_t e = launch_kernel(kKindBwdKV, bwd_dkdv_mfma_kernel<G, MODE>,
+                               dim3(unsigned(n_slots), std::max(1u, n_chunk)), dim3(kThreads), s,
+                               a.q, a.k, a.v, a.dout, a.lse, static_cast<const float*>(a.delta),
+                               static_cast<const int*>(a.cnt), static_cast<const int*>(a.off),
+                               static_cast<const int2*>(a.list), a.cu_q, a.cu_k, a.cu_kv,
+                               a.window, a.accumulate, a.heads, a.kv_heads, a.nb_max, scale_log2,
+                               a.scale, a.dk, a.dv);
+  if (e != hipSuccess || MODE == kBwdSelected) return e;
+  constexpr int kRowsPerWg = 4 * (16 / G);
+  const unsigned gx = unsigned((a.max_seqlen_k + kRowsPerWg - 1) / kRowsPerWg);
+  return launch_kernel(kKindBwdQ, bwd_dq_mfma_kernel<G, MODE>,
+                       dim3(std::max(1u, gx), unsigned(a.kv_heads), unsigned(a.batch)),
+                       dim3(kThreads), s, a.q, a.k, a.v, a.dout, a.lse,
+                       static_cast<const float*>(a.delta), a.cu_q, a.cu_k, a.cu_kv, a.window,
+                       a.accumulate, a.heads, a.kv_heads, scale_log2, a.scale, a.dq);
+}
+
+template <int MODE>
+hipError_t launch_mfma_mode(const SelectedBwdArgs& a, hipStream_t s) {
+  switch (a.heads / a.kv_heads) {
+    case 1: return launch_mfma_g<1, MODE>(a, s);
+    case 2: return launch_mfma_g<2, MODE>(a, s);
+    case 4: return launch_mfma_g<4, MODE>(a, s);
+    case 8: return launch_mfma_g<8, MODE>(a, s);
+    case 16: return launch_mfma_g<16, MODE>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int mfma_bwd_rows_per_chunk() { return kMfmaRowsPerChunk; }
+
+hipError_t launch_bwd_mfma(const SelectedBwdArgs& a, hipStream_t s) {
+  switch (a.mode) {
+    case kBwdSelected: return launch_mfma_mode<kBwdSelected>(a, s);
+    case kBwdWindow: return launch_mfma_mode<kBwdWindow>(a, s);
+    case kBwdCompressed: return launch_mfma_mode<kBwdCompressed>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace nsa

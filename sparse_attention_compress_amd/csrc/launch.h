@@ -224,6 +224,7 @@ struct SelectedBwdArgs {
   int mode;            // BwdMode
   int window;          // kBwdWindow: keys t - window + 1 .. t
   int accumulate;      // bit 0: add to dq; bit 1: add to dk, dv (instead of writing)
+  int valu;            // != 0: every gradient on the vector-ALU kernels (comparison path)
   const int* cu_kv;    // key rows of each sequence (cu_k, or cu_c for compressed keys)
   const bf16_t* q;     // [rows, heads, 128]
   const bf16_t* k;     // [N_kv, kv_heads, 128]
@@ -251,6 +252,10 @@ size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel,
                              int nb_max);
 void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a);
 hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s);
+// The matrix-core kernels: dk/dv of every key set, dq of the window and
+// compressed key sets (bwd_mfma.hip).
+hipError_t launch_bwd_mfma(const SelectedBwdArgs& a, hipStream_t s);
+int mfma_bwd_rows_per_chunk();
 hipError_t launch_gates_bwd(const bf16_t* dout, const bf16_t* o_cmp, const bf16_t* o_sel,
                             const bf16_t* o_win, const float* gates, size_t n_rh, bf16_t* do_cmp,
                             bf16_t* do_sel, bf16_t* do_win, float* d_gates, hipStream_t s);

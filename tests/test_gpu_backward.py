@@ -2,11 +2,12 @@
 float64 oracle's gradient.
 
 Gate: the inputs are exactly the bf16 tensors the oracle widens, so the GPU's
-differences come from fp32 accumulation, the forward's fp32 log-normaliser and
+differences come from fp32 accumulation, the forward's fp32 log-normaliser,
 delta = dO . O taken from the bf16-rounded forward output (2^-9 relative per
-element of O, about 1e-3 of the typical ds).  Each gradient must agree within
-1e-2 of its largest oracle magnitude, dV (which does not use delta) within
-1e-4.  At full size, sampled dq rows are compared with the oracle and two
+element of O, about 1e-3 of the typical ds) and, for dK and dV, p and ds
+entering the matrix-core contractions rounded to bf16 (2^-9 relative per term).
+Each gradient must agree within 1e-2 of its largest oracle magnitude, dV
+(which does not use delta) within 2^-8.  At full size, sampled dq rows are compared with the oracle and two
 identities are checked over all keys: summed over the keys of a KV head, dK is
 0 (per row and head the ds sum to 0), and dV equals the summed dO of the
 group's heads over every row that sees a key (the p sum to 1).
@@ -78,7 +79,7 @@ def _compare(d, dq, dk, dv, tag):
         d["cu_q"].cpu().numpy(), d["cu_k"].cpu().numpy(), 64, scale)
     _gate(tag + ".dq", np64(dq), rq, 1e-2)
     _gate(tag + ".dk", np64(dk), rk, 1e-2)
-    _gate(tag + ".dv", np64(dv), rv, 1e-4)
+    _gate(tag + ".dv", np64(dv), rv, 2.0 ** -8)
 
 
 @pytest.mark.parametrize("H,H_kv,lengths", [(16, 2, [500, 900]), (16, 1, [300, 420]),
@@ -140,6 +141,9 @@ def test_selected_bwd_full_size_samples_and_identities():
             want_dv = do_np[k0:k1, g * G:(g + 1) * G].sum(axis=(0, 1))
             mag_k = np.abs(dk_np[k0:k1, g]).sum(axis=0).max()
             mag_v = np.abs(want_dv).max() + np.abs(do_np[k0:k1, g * G:(g + 1) * G]).sum(axis=(0, 1)).max() * 1e-6
-            assert np.abs(s_dk).max() <= 1e-4 * mag_k, (b, g, np.abs(s_dk).max(), mag_k)
+            # ds enters the dK contraction rounded to bf16 (2^-9 relative per term),
+            # so the key sum of dK is zero only up to that share of its magnitude; a
+            # dropped or doubled row or key would leave an O(1) share
+            assert np.abs(s_dk).max() <= 2.0 ** -9 * mag_k, (b, g, np.abs(s_dk).max(), mag_k)
             assert np.abs(s_dv - want_dv).max() <= 1e-3 * mag_v + 1e-3, (b, g)
     log("full-size identities hold")

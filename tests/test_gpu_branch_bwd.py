@@ -3,10 +3,12 @@ on the GPU against the float64 oracle, and the whole three-branch gradient
 composed from the branch entry points.  Calls go through the C ABI.
 
 Gates (as for the selected-attention backward): the inputs are the exact bf16
-tensors the oracle widens; the GPU differs by fp32 accumulation and by
-delta = dO . O taken from the bf16-rounded branch output (2^-9 relative), so
-dq and the key gradients must agree within 1e-2 of their largest oracle
-magnitude and the value gradients within 1e-4.  The composed gradient feeds
+tensors the oracle widens; the GPU differs by fp32 accumulation, by
+delta = dO . O taken from the bf16-rounded branch output (2^-9 relative), and
+by p and ds entering the matrix-core contractions rounded to bf16 (2^-9
+relative per term), so dq and the key gradients must agree within 1e-2 of
+their largest oracle magnitude and the value gradients (no delta term) within
+2^-8 (twice the per-term rounding).  The composed gradient feeds
 each branch gate * dO rounded to bf16 (nsa_gates_bwd; 2^-9 relative again), so
 every part of it is gated at 1e-2.  The window-mean transpose is plain fp32 arithmetic:
 1e-6 relative.
@@ -28,6 +30,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 BF16, F32 = torch.bfloat16, torch.float32
 SEED = 0x5EED0B00
+DV_GATE = 2.0 ** -8
 
 
 def _gate(name, got, ref, rel):
@@ -110,7 +113,7 @@ def test_window_bwd_matches_oracle(H, H_kv, window):
                                                   rdk[k0:k1], rdv[k0:k1])
     _gate("window.dq", np64(dq), rdq, 1e-2)
     _gate("window.dk", np64(dk), rdk, 1e-2)
-    _gate("window.dv", np64(dv), rdv, 1e-4)
+    _gate("window.dv", np64(dv), rdv, DV_GATE)
     assert torch.count_nonzero(dk[700:1000]) == 0 and torch.count_nonzero(dv[700:1000]) == 0
 
 
@@ -165,11 +168,11 @@ def test_compressed_bwd_matches_oracle(H, H_kv, lengths):
     nct = int(cu_c[-1])
     _gate("compressed.dq", np64(dq), rdq, 1e-2)
     _gate("compressed.dk_c", np64(dkc)[:nct], rdkc[:nct], 1e-2)
-    _gate("compressed.dv_c", np64(dvc)[:nct], rdvc[:nct], 1e-4)
+    _gate("compressed.dv_c", np64(dvc)[:nct], rdvc[:nct], DV_GATE)
     rdk = oracle.mean_pool_varlen_bwd(rdkc[:nct], cu_k, cu_c, 32, 16, int(cu_k[-1]))
     rdv = oracle.mean_pool_varlen_bwd(rdvc[:nct], cu_k, cu_c, 32, 16, int(cu_k[-1]))
     _gate("compressed.dk", np64(dk), rdk, 1e-2)
-    _gate("compressed.dv", np64(dv), rdv, 1e-4)
+    _gate("compressed.dv", np64(dv), rdv, DV_GATE)
 
 
 def _three_branch_grads(d, g, topk, window):

@@ -513,10 +513,6 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (with packed fp32 instructions)
-# The library is built without packed fp32 instructions, so one fp32 FMA per lane
-# per cycle: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s.
-FP32_VECTOR_UNPACKED_TFLOPS = 78.6
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -970,11 +966,9 @@ def selected_bwd_main(args, dev):
     """Backward of the selected attention over the prefill-selected batch: one
     step = the gradient (dq, dk, dv) of the whole batch from the forward's
     output, log-normaliser and a given upstream gradient; value = prefill tokens/s
-    of the backward.  The kernels run on the vector ALUs in fp32 without packed
-    instructions, so the roofline is the algorithmic flops of the longer of the dq
-    and dk/dv kernels against the unpacked fp32 vector peak; the fraction of the
-    bf16 matrix-core peak (the ceiling of these bf16-input contractions) is
-    reported beside it."""
+    of the backward.  The dq and dk/dv contractions run on the bf16 matrix cores
+    (fp32 accumulation), so the roofline is the algorithmic flops of the longer
+    of the two kernels against the bf16 matrix-core peak."""
     import numpy as np
     import torch
 
@@ -1033,19 +1027,18 @@ def selected_bwd_main(args, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V and upstream gradient, uniform causal block "
                 "indices; no dataset)",
         "config": {"workload": w.name + "_bwd", "batch": w.batch, "seq_len": L_max,
                    "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": D, "topk": w.topk},
         "roofline": {
             "kernel": dominant,
-            "bound": "alu",
+            "bound": "mfma",
             "achieved": round(tflops[dominant], 2),
-            "peak": FP32_VECTOR_UNPACKED_TFLOPS,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops[dominant] / FP32_VECTOR_UNPACKED_TFLOPS, 4),
-            "frac_of_bf16_mfma_peak": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(kern[dominant], 1),
@@ -1083,8 +1076,8 @@ def nsa_bwd_main(args, dev):
     dq, dk, dv (sharing the output arrays) and the window-mean transpose of the
     compressed keys' and values' gradients, from the forward's branch outputs,
     normalisers and block choice (computed once before the timed region).  The
-    kernels run on the vector ALUs in fp32: roofline = algorithmic flops of the
-    longest branch against the unpacked fp32 vector peak."""
+    contractions run on the bf16 matrix cores: roofline = algorithmic flops of
+    the longest branch against the bf16 matrix-core peak."""
     import numpy as np
     import torch
 
@@ -1183,19 +1176,18 @@ def nsa_bwd_main(args, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V and upstream gradient, sigmoid(N(0,1)) gates; "
                 "no dataset)",
         "config": {"workload": w.name + "_bwd", "batch": 1, "seq_len": L, "heads": H,
                    "kv_heads": Hkv, "head_dim": D, "topk": w.topk, "window": w.window},
         "roofline": {
             "kernel": f"{dominant} branch (dq and dk/dv kernels)",
-            "bound": "alu",
+            "bound": "mfma",
             "achieved": round(tflops[dominant], 2),
-            "peak": FP32_VECTOR_UNPACKED_TFLOPS,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops[dominant] / FP32_VECTOR_UNPACKED_TFLOPS, 4),
-            "frac_of_bf16_mfma_peak": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(part_ms[dominant] * 1e3, 1),

@@ -28,6 +28,12 @@
 //   waves (K rows, K transposed, V rows).  Per 16-key slice: S^T = K Q^T and
 //   dP^T = V dO^T (accumulators (key 4r4+e, query c16)), then dQ^T += K^T dS^T
 //   with dS^T packed straight into the B operand.
+// bwd_dq_sel_mfma_kernel -- dq of the selected branch, one (row, KV head) per
+//   workgroup: the G heads are the tile's columns (columns past G masked), each
+//   listed block is staged in LDS once (K rows), wave w takes its keys
+//   16w .. 16w+15 (V rows straight into registers), and the four waves' dq^T
+//   are summed through LDS at the end.  K^T operands come from the staged rows
+//   as four 2-byte reads.
 // Masked keys (outside the row's key set, or past the sequence) get p = 0.
 #include <algorithm>
 
@@ -373,6 +379,123 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
   }
 }
 
+template <int G>
+__global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int* __restrict__ indices, int k_sel,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int accumulate,
+    int heads, int kv_heads, float scale_log2, float scale, float* __restrict__ dq) {
+  constexpr int kRedPad = kHeadDim + 4;
+  __shared__ bf16_t Ks[64 * kRowPad];
+  __shared__ float red[4][16][kRedPad];
+  __shared__ int ids_s[64];
+  __shared__ int nv_s;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const int row = int(blockIdx.x / unsigned(kv_heads)), g = int(blockIdx.x % unsigned(kv_heads));
+  int b, t;
+  bwd_row_position(row, cu_q, cu_k, batch, b, t);
+  const int kstart = cu_k[b], len = cu_k[b + 1] - kstart;
+  // usable ids of the row (id >= 0, block start <= t), in list order
+  if (wave == 0) {
+    const int* irow = indices + (size_t(row) * kv_heads + g) * k_sel;
+    int base = 0;
+    for (int s0 = 0; s0 < k_sel; s0 += kWave) {
+      const int id = s0 + lane < k_sel ? irow[s0 + lane] : -1;
+      const bool ok = t >= 0 && t < len && id >= 0 && id * kBlock <= t;
+      const unsigned long long m = __ballot(ok);
+      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (ok && pos < 64) ids_s[pos] = id;
+      base += __popcll(m);
+    }
+    if (lane == 0) nv_s = min(base, 64);
+  }
+  const bool col_ok = c16 < G;
+  const size_t hq = size_t(row) * heads + size_t(g) * G + min(c16, G - 1);
+  uint4 qb[4], db[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qb[i] = col_ok ? ld16(q + hq * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+    db[i] = col_ok ? ld16(dout + hq * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const float lse2 = col_ok ? lse[hq] * kLog2e : 0.f;
+  const float dlt = col_ok ? delta[hq] : 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  const int nv = nv_s;
+
+  // block `id`: thread tid holds K chunks c = tid + 256 u (key c / 16, dims 8 (c % 16) ..),
+  // and the V row of key 16 wave + c16 (dims 32 i + 8 r4 ..); keys past t are clamped
+  // to t (their p is 0)
+  const size_t rs = size_t(kv_heads) * kHeadDim;
+  uint4 pk[4], pv[4], vc[4];
+  auto fetch = [&](int id) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u;
+      const int kk = min(kBlock * id + (c >> 4), t);
+      pk[u] = ld16(k + size_t(kstart + kk) * rs + size_t(g) * kHeadDim + 8 * (c & 15));
+    }
+    const int kv_ = min(kBlock * id + 16 * wave + c16, t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pv[i] = ld16(v + size_t(kstart + kv_) * rs + size_t(g) * kHeadDim + 32 * i + 8 * r4);
+  };
+  if (nv > 0) fetch(ids_s[0]);
+  for (int p = 0; p < nv; ++p) {
+    const int id = ids_s[p];
+    __syncthreads();  // the previous block's rows are no longer read
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u;
+      *reinterpret_cast<uint4*>(&Ks[(c >> 4) * kRowPad + 8 * (c & 15)]) = pk[u];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vc[i] = pv[i];
+    __syncthreads();
+    if (p + 1 < nv) fetch(ids_s[p + 1]);
+    // S^T = K Q^T, dP^T = V dO^T: (key 16 wave + 4 r4 + e, head column c16)
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st = mfma32(*reinterpret_cast<const uint4*>(&Ks[(16 * wave + c16) * kRowPad + 32 * i + 8 * r4]), qb[i], st);
+      dpt = mfma32(vc[i], db[i], dpt);
+    }
+    float ds[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = kBlock * id + 16 * wave + 4 * r4 + e;
+      const float pr = col_ok && key <= t ? fast_exp2(st[e] * scale_log2 - lse2) : 0.f;
+      ds[e] = pr * (dpt[e] - dlt);
+    }
+    const uint2 dsb = pack4(ds);
+    const bf16_t* kr = &Ks[(16 * wave + 4 * r4) * kRowPad + c16];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      // K^T[dim 16 dt + c16][keys 16 wave + 4 r4 .. +3]
+      const uint32_t k0 = kr[16 * dt].bits, k1 = kr[kRowPad + 16 * dt].bits;
+      const uint32_t k2 = kr[2 * kRowPad + 16 * dt].bits, k3 = kr[3 * kRowPad + 16 * dt].bits;
+      acc[dt] = mfma16(make_uint2(k0 | (k1 << 16), k2 | (k3 << 16)), dsb, acc[dt]);
+    }
+  }
+  // dq^T of the wave: (dim 16 dt + 4 r4 + e, head column c16); summed over the waves
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<float4*>(&red[wave][c16][16 * dt + 4 * r4]) =
+        make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+  __syncthreads();
+  for (int o = tid; o < G * kHeadDim; o += kThreads) {
+    const int h = o / kHeadDim, d = o % kHeadDim;
+    float x = scale * (red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d]);
+    float* po = dq + (size_t(row) * heads + size_t(g) * G + h) * kHeadDim + d;
+    if (accumulate & 1) x += *po;
+    *po = x;
+  }
+}
+
 template <int G, int MODE>
 hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
   const int n_slots = a.batch * a.kv_heads * a.nb_max;
@@ -387,7 +510,13 @@ hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
                                static_cast<const int2*>(a.list), a.cu_q, a.cu_k, a.cu_kv,
                                a.window, a.accumulate, a.heads, a.kv_heads, a.nb_max, scale_log2,
                                a.scale, a.dk, a.dv);
-  if (e != hipSuccess || MODE == kBwdSelected) return e;
+  if (e != hipSuccess) return e;
+  if (MODE == kBwdSelected)
+    return launch_kernel(kKindBwdQ, bwd_dq_sel_mfma_kernel<G>,
+                         dim3(unsigned(a.rows_total) * a.kv_heads), dim3(kThreads), s, a.q, a.k,
+                         a.v, a.dout, a.lse, static_cast<const float*>(a.delta), a.indices,
+                         a.k_sel, a.cu_q, a.cu_k, a.batch, a.accumulate, a.heads, a.kv_heads,
+                         scale_log2, a.scale, a.dq);
   constexpr int kRowsPerWg = 4 * (16 / G);
   const unsigned gx = unsigned((a.max_seqlen_k + kRowsPerWg - 1) / kRowsPerWg);
   return launch_kernel(kKindBwdQ, bwd_dq_mfma_kernel<G, MODE>,

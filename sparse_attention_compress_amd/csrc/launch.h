@@ -224,7 +224,6 @@ struct SelectedBwdArgs {
   int mode;            // BwdMode
   int window;          // kBwdWindow: keys t - window + 1 .. t
   int accumulate;      // bit 0: add to dq; bit 1: add to dk, dv (instead of writing)
-  int valu;            // != 0: every gradient on the vector-ALU kernels (comparison path)
   const int* cu_kv;    // key rows of each sequence (cu_k, or cu_c for compressed keys)
   const bf16_t* q;     // [rows, heads, 128]
   const bf16_t* k;     // [N_kv, kv_heads, 128]

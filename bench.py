@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--seq", type=int, default=16384,
                     help="prefill-blockmask: tokens per sequence (the pages' table: 1024, 4096, 16384)")
     ap.add_argument("--causal", action="store_true", help="prefill-blockmask: lower triangle only")
+    ap.add_argument("--selected-path", choices=["blocks", "rows"], default="blocks",
+                    help="prefill-selected: key-block stationary (workspace given) or row by row")
     ap.add_argument("--workload", choices=["decode", "decode-long", "decode-tiny", "decode-offload",
                                            "prefill-selected", "prefill-nsa", "prefill-blockmask",
                                            "prefill-selected-bwd", "prefill-nsa-bwd"],
@@ -833,11 +835,17 @@ def prefill_main(args, dev):
         idx = W.given_block_indices(w, dev)
         cu = nsa.cu_seqlens_of(w.lengths, dev)
         out = torch.empty_like(q)
+        blocks = args.selected_path == "blocks"
+        need = nsa.selected_attn_workspace_size(q.shape[0], w.heads, w.kv_heads, D, w.topk, False)
+        sws = torch.empty(need if blocks else 0, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
         def fn():
-            nsa.nsa_selected_attn_fwd(q, k, v, idx, cu, max(w.lengths), out, cu_seqlens_q=cu)
+            nsa.nsa_selected_attn_fwd(q, k, v, idx, cu, max(w.lengths), out, cu_seqlens_q=cu,
+                                      workspace=sws)
         kinds = {"selected_attn": nsa.KERNEL_SELECTED_ATTN}
+        if blocks:  # the partial states' merge
+            kinds["merge"] = nsa.KERNEL_COMBINE
         # algorithmic work: every (row, head) attends to the tokens j <= t of its blocks
         ids = idx.cpu().numpy().astype(np.int64).reshape(-1, w.topk)
         pos = np.concatenate([np.arange(L) for L in w.lengths])
@@ -910,7 +918,8 @@ def prefill_main(args, dev):
         "data": "synthetic (seeded N(0,1) Q/K/V" + (", sigmoid(N(0,1)) gates" if args.workload == "prefill-nsa" else ", uniform causal block indices") + "; no dataset)",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": max(w.lengths), "heads": w.heads,
                    "kv_heads": w.kv_heads, "head_dim": D, "topk": w.topk,
-                   **({"window": w.window} if args.workload == "prefill-nsa" else {})},
+                   **({"window": w.window} if args.workload == "prefill-nsa" else {}),
+                   **({"selected_path": args.selected_path} if args.workload == "prefill-selected" else {})},
         "roofline": {
             "kernel": dominant,
             "bound": "mfma",
@@ -928,6 +937,17 @@ def prefill_main(args, dev):
         "selected_gathered_gbs": round(gathered / (kern["selected_attn"] * 1e-6) / 1e9, 1),
         "timed_gpu_ms": round(gpu_ms, 3),
     }
+    if args.workload == "prefill-selected" and args.selected_path == "blocks":
+        # the key-block path moves partial states instead of gathering K/V rows:
+        # 256 B of bf16 output + 8 B of (max, sum) per (row, head, valid place),
+        # written by the partial kernel and read back by the merge
+        pos_k = np.repeat(pos, w.kv_heads)
+        valid = ((ids >= 0) & (64 * ids <= pos_k[:, None])).sum()
+        pbytes = float(valid) * G * 264
+        result["partial_state_bytes"] = pbytes
+        result["partial_write_gbs"] = round(pbytes / (kern["selected_attn"] * 1e-6) / 1e9, 1)
+        result["merge_read_gbs"] = round(pbytes / (kern["merge"] * 1e-6) / 1e9, 1)
+        del result["selected_gathered_gbs"]
     if not args.no_cpu_baseline:
         import oracle
         scale = 1.0 / math.sqrt(D)

@@ -261,7 +261,20 @@ nsa_status nsa_select_topk(const float* block_scores, int32_t* indices,
  *            normaliser sum_j exp(s_j) (times cis_j in CIS mode); -inf when the
  *            row sees no key (its output row is then 0).
  *   cu_seqlens_q NULL: decode (rows = batch, t = L_b - 1); else prefill rows.
- *   workspace: nsa_selected_attn_workspace_size(...) bytes.
+ *   workspace: decode rows: nsa_selected_attn_workspace_size(..., decode=1)
+ *            bytes, required.  Prefill rows: optional.  NULL or 0 bytes (or
+ *            float32 inputs): one workgroup per (row, KV head) gathers the
+ *            row's blocks.  Given with at least
+ *            nsa_selected_attn_workspace_size(..., decode=0) bytes
+ *            (rows * heads * k_sel * 264 bytes, 16-byte aligned) and bf16
+ *            inputs: key-block stationary -- one workgroup per (sequence, KV
+ *            head, 64-key block, 1024 query rows) attends the rows listing
+ *            the block and writes their partial state (bf16 output, fp32 max
+ *            and sum) at the row's place; a merge kernel combines each row's
+ *            places.  This path also needs every L_b <= max_seqlen_k.  Between
+ *            0 and the queried size: NSA_ERR_WORKSPACE.  An id listed twice
+ *            in one row counts once on this path and twice on the other (ids
+ *            of a row must be unique either way).
  */
 size_t nsa_selected_attn_workspace_size(int32_t rows_total, int32_t heads, int32_t kv_heads,
                                         int32_t head_dim, int32_t k_sel, int32_t decode);
@@ -292,7 +305,7 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
  *                 row attends to)
  *   Per head over the row's keys J: dV_J += p dO^T; ds = p*(V_J dO - dO.O);
  *   dq = scale ds K_J; dK_J += scale ds q^T.  dk and dv are gathered per
- *   (sequence, KV head, block) over the rows that list the block, up to 256
+ *   (sequence, KV head, block) over the rows that list the block, up to 512
  *   rows per workgroup; a block listed by more rows has its chunk sums added
  *   with fp32 atomics.  The row lists are built with atomics too, so the
  *   summation order of dk and dv may change between calls (fp32 rounding only).

@@ -246,6 +246,7 @@ nsa_status nsa_select_topk(const float* block_scores, int32_t* indices, const in
 size_t nsa_selected_attn_workspace_size(int32_t rows_total, int32_t heads, int32_t kv_heads,
                                         int32_t head_dim, int32_t k_sel, int32_t decode) {
   if (rows_total <= 0 || kv_heads <= 0 || heads <= 0 || k_sel <= 0 || head_dim != nsa::kHeadDim) return 0;
+  if (!decode) return k_sel <= kMaxPrefillSel ? nsa::block_attn_ws_bytes(rows_total, heads, k_sel) : 0;
   return nsa::attn_ws_bytes(rows_total, kv_heads, heads / kv_heads, k_sel, decode);
 }
 
@@ -274,8 +275,18 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
   NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), NSA_ERR_INVALID_ARG,
               "%s: q, k, v, out must be 16-byte aligned", fn);
   const size_t need = nsa_selected_attn_workspace_size(rows_total, heads, kv_heads, head_dim, k_sel, decode);
-  NSA_REQUIRE(workspace != nullptr || need == 0, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
-  NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  // prefill rows: the workspace is optional (none, or float32 inputs: the
+  // row-by-row kernel)
+  const bool blocks = !decode && workspace_bytes > 0 && dtype == NSA_BF16;
+  if (decode || blocks) {
+    NSA_REQUIRE(workspace != nullptr || need == 0, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
+    NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  }
+  if (blocks) {
+    NSA_REQUIRE(aligned16(workspace), NSA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+    NSA_REQUIRE(nsa::block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k), NSA_ERR_UNSUPPORTED,
+                "%s: shape too large for the key-block path", fn);
+  }
   const nsa::AttnWs ws = nsa::attn_ws_carve(workspace, rows_total, kv_heads, heads / kv_heads, k_sel, decode);
   NSA_DEVICE_CHECKS(fn, stream, {
     chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
@@ -283,6 +294,13 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
     chk.q_within_k(cu_seqlens_q, cu_seqlens_k, batch);
     chk.unique_ids(indices, long(rows_total) * kv_heads, k_sel);
   });
+  if (blocks)
+    return hip_status(nsa::launch_block_attn(q, k, v, indices, k_sel, cis, out, nullptr, lse,
+                                             cu_seqlens_q, cu_seqlens_k, batch, rows_total, heads,
+                                             kv_heads, max_seqlen_k,
+                                             scale_log2_of(softmax_scale, head_dim), workspace,
+                                             stream),
+                      fn);
   return hip_status(nsa::launch_selected_attn(q, k, v, dtype == NSA_BF16, indices, k_sel, cis, out,
                                               lse, cu_seqlens_q, cu_seqlens_k, batch, rows_total,
                                               heads, kv_heads, scale_log2_of(softmax_scale, head_dim),

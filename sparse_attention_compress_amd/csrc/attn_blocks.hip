@@ -1,0 +1,525 @@
+// Selected attention over prefill rows, key-block stationary.
+//
+// What is computed is the selected attention of TileLang NSA, section 2: query
+// row t of a sequence attends to the 64-token blocks its index row lists (block
+// id i starts at token 64 i and counts when 0 <= 64 i <= t; keys past t are
+// masked), the G query heads of one KV group sharing the blocks; in CIS mode
+// (NOSA-1B core components, decode stage) every probability is scaled by its
+// key's CIS value and the normaliser is the same sum over all-ones values.
+//
+// The row-by-row kernel gathers 64 K and V rows per listed block for every
+// (row, KV head): with uniform block choices no two rows share a block, so its
+// bytes come from L2 and the Infinity Cache, not from the matrix cores' reuse.
+// Here the roles are swapped:
+//
+// block_partial_kernel -- one workgroup per (sequence, KV head, chunk of 1024
+//   query rows, 64-key block).  It stages the block's K and V rows in LDS once,
+//   scans the chunk's index rows for the rows that list the block (and at which
+//   place), and walks those rows in tiles of 16 query vectors (a query vector is
+//   one (row, head) pair: 16/G rows of G heads).  Each wave holds the whole
+//   block as matrix-core operands (K in the A layout of S^T = K Q^T, V^T in the
+//   A layout of O^T = V^T P^T), so a tile costs its q rows in, 32
+//   v_mfma_f32_16x16x32_bf16, and its partial state out: the block's
+//   normalised output in bf16 plus (max, sum) in fp32, at the row's place.
+// block_merge_kernel -- per (row, head): the partial states of the row's valid
+//   places combined with the usual log-sum-exp weights.
+//
+// Precision is that of the row-by-row kernel: bf16 probabilities enter the
+// matrix cores, fp32 sums; each partial output is rounded to bf16 once more
+// (2^-9 relative) before the merge.
+#include <climits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace nsa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kScanRows = 1024;       // query rows one workgroup scans for its block
+constexpr int kLdsRow = kHeadDim + 8; // bf16 per staged K/V row (272 B)
+constexpr int kMaxPlaces = 64;        // index places per row (place fits 6 bits)
+constexpr int kMergeBatch = 8;        // places whose loads the merge keeps in flight together
+
+__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const bf16x2_t x = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+// max / sum over the four lanes c16, c16 + 16, c16 + 32, c16 + 48 (one column of
+// an MFMA accumulator)
+__device__ __forceinline__ float column_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float column_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+struct PartialLds {
+  bf16_t k[kBlock * kLdsRow];
+  bf16_t v[kBlock * kLdsRow];
+  bf16_t stage[4][16 * kLdsRow];  // per wave: one tile's 16 output rows, for the stores
+  int list[kScanRows];            // (row in chunk << 6) | place
+  int n_list;
+};
+
+// Append to the list the rows that list block `blk`, each at the first place
+// holding it.  Vector form (k_sel a multiple of 4 and a 16-byte aligned array,
+// so every index row is 16-byte aligned): P lanes per index row, 4 ids per lane, all of a batch's loads in
+// flight together.
+template <int P>
+__device__ __forceinline__ void scan_rows_vec(PartialLds& sm, const int* __restrict__ indices,
+                                              int k_sel, int kv_heads, int kv, int q0, int r_lo,
+                                              int r_first, int r_hi, int blk, int wave, int lane) {
+  constexpr int RPI = 64 / P;       // rows per wave instruction
+  constexpr int kBatch = 16;        // loads in flight per lane
+  const int seg = lane % P, gbase = lane & ~(P - 1);
+  const int n_inst = (r_hi - r_first + 4 * RPI - 1) / (4 * RPI);
+  for (int j0 = 0; j0 < n_inst; j0 += kBatch) {
+    int4 idv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int r = r_first + ((j0 + j) * 4 + wave) * RPI + lane / P;
+      const bool ok = j0 + j < n_inst && r < r_hi && 4 * seg < k_sel;
+      const int* row = indices + (size_t(q0 + min(r, r_hi - 1)) * kv_heads + kv) * k_sel;
+      idv[j] = ok ? *reinterpret_cast<const int4*>(row + 4 * seg) : make_int4(-1, -1, -1, -1);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j0 + j >= n_inst) break;  // the same for the whole wave
+      const int r = r_first + ((j0 + j) * 4 + wave) * RPI + lane / P;
+      const int4 x = idv[j];
+      const int u = x.x == blk ? 0 : x.y == blk ? 1 : x.z == blk ? 2 : x.w == blk ? 3 : -1;
+      const unsigned long long hit = __ballot(u >= 0);
+      const unsigned long long grp = (hit >> gbase) & ((1ull << P) - 1ull);
+      const bool writer = u >= 0 && (grp & ((1ull << seg) - 1ull)) == 0ull;
+      const unsigned long long wmask = __ballot(writer);
+      int base = 0;
+      if (lane == 0 && wmask != 0ull) base = atomicAdd(&sm.n_list, __popcll(wmask));
+      base = __shfl(base, 0);
+      if (writer)
+        sm.list[base + __popcll(wmask & ((1ull << lane) - 1ull))] = ((r - r_lo) << 6) | (4 * seg + u);
+    }
+  }
+}
+
+// Scalar form for any k_sel: one thread per index row.
+__device__ __forceinline__ void scan_rows_scalar(PartialLds& sm, const int* __restrict__ indices,
+                                                 int k_sel, int kv_heads, int kv, int q0, int r_lo,
+                                                 int r_first, int r_hi, int blk, int tid, int lane) {
+  for (int r0 = r_first; r0 < r_hi; r0 += 256) {
+    const int r = r0 + tid;
+    int place = -1;
+    if (r < r_hi) {
+      const int* ids = indices + (size_t(q0 + r) * kv_heads + kv) * k_sel;
+      for (int p0 = 0; p0 < k_sel; p0 += 16) {
+        int idv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) idv[u] = p0 + u < k_sel ? ids[p0 + u] : -1;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (place < 0 && idv[u] == blk) place = p0 + u;
+      }
+    }
+    const unsigned long long mask = __ballot(place >= 0);
+    int base = 0;
+    if (lane == 0 && mask != 0ull) base = atomicAdd(&sm.n_list, __popcll(mask));
+    base = __shfl(base, 0);
+    if (place >= 0)
+      sm.list[base + __popcll(mask & ((1ull << lane) - 1ull))] = ((r - r_lo) << 6) | place;
+  }
+}
+
+// Grid: one dimension over (sequence, KV head, row chunk, block) in XCD-grouped
+// order, so the blocks of one row chunk run together on one XCD and share its
+// query rows and index rows in L2.  Partial states go to
+// po[((row * k_sel + place) * heads + head) * 128 ..] (bf16) and
+// pml[(row * k_sel + place) * heads + head] = (max, sum) in the log2 domain: the
+// G heads of one (row, place) are contiguous.
+template <int G, bool CIS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void block_partial_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads, int nb_max,
+    int n_chunk, float scale_log2, bf16_t* __restrict__ po, float2* __restrict__ pml) {
+  constexpr int E = 16 / G;  // rows per tile
+  constexpr int D = kHeadDim;
+  __shared__ PartialLds sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
+
+  int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
+  const int blk = m % nb_max;
+  m /= nb_max;
+  const int chunk = m % n_chunk;
+  m /= n_chunk;
+  const int kv = m % kv_heads;
+  const int b = m / kv_heads;
+  const int kstart = cu_k[b], L = cu_k[b + 1] - kstart;
+  const int q0 = cu_q[b], Lq = cu_q[b + 1] - q0;
+  const int off = L - Lq;  // query row r of the sequence sits at position off + r
+  const int r_lo = chunk * kScanRows, r_hi = min(Lq, r_lo + kScanRows);
+  const int r_first = max(r_lo, kBlock * blk - off);  // rows that can list the block
+  if (r_first >= r_hi || kBlock * blk >= L) return;  // the same for the whole workgroup
+  const int heads = kv_heads * G;
+
+  // the block's K and V rows (rows past the sequence end repeat its last row:
+  // finite data, masked below since they lie past every row's position),
+  // requested before the index scan so both are in flight together
+  if (tid == 0) sm.n_list = 0;
+  uint4 kst[4], vst[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int x = tid + 256 * it, key = x >> 4, ch = x & 15;
+    const int j = min(kBlock * blk + key, L - 1);
+    const size_t g = (size_t(kstart + j) * kv_heads + kv) * D + 8 * ch;
+    kst[it] = ld16(k + g);
+    vst[it] = ld16(v + g);
+  }
+  __syncthreads();  // n_list = 0 seen by every wave
+  if ((k_sel & 3) == 0 && (reinterpret_cast<uintptr_t>(indices) & 15) == 0) {
+    const int lanes = k_sel / 4;
+    if (lanes <= 1) scan_rows_vec<1>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else if (lanes <= 2) scan_rows_vec<2>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else if (lanes <= 4) scan_rows_vec<4>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else if (lanes <= 8) scan_rows_vec<8>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else scan_rows_vec<16>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+  } else {
+    scan_rows_scalar(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, tid, lane);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int x = tid + 256 * it, key = x >> 4, ch = x & 15;
+    *reinterpret_cast<uint4*>(&sm.k[key * kLdsRow + 8 * ch]) = kst[it];
+    *reinterpret_cast<uint4*>(&sm.v[key * kLdsRow + 8 * ch]) = vst[it];
+  }
+  __syncthreads();
+  const int n_list = sm.n_list;
+  const int n_tiles = (n_list + E - 1) / E;
+  if (wave >= n_tiles) return;  // no barrier below
+
+  // the block as matrix-core operands of this wave
+  uint4 ka[4][4];  // S^T = K Q^T, A: key 16 s + c16, dims 32 kk + 8 r4 .. +8
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      ka[s][kk] = *reinterpret_cast<const uint4*>(&sm.k[(16 * s + c16) * kLdsRow + 32 * kk + 8 * r4]);
+  // O^T += V^T P^T, A of output tile n (row c16 = dim 8 c16 + n) for the keys of
+  // half h (k index 8 r4 + u = key 32 h + 16 (u / 4) + 4 r4 + u % 4)
+  uint4 va[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 rows[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int key = 32 * h + 16 * (u >> 2) + 4 * r4 + (u & 3);
+      rows[u] = *reinterpret_cast<const uint4*>(&sm.v[key * kLdsRow + 8 * c16]);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t a = (&rows[2 * x].x)[n >> 1], c = (&rows[2 * x + 1].x)[n >> 1];
+        w[x] = (n & 1) ? (a >> 16) | (c & 0xFFFF0000u) : (a & 0xFFFFu) | (c << 16);
+      }
+      va[h][n] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  float cw[4][4];  // CIS of key 16 s + 4 r4 + e
+  if constexpr (CIS) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        cw[s][e] = cis[size_t(kstart + min(kBlock * blk + 16 * s + 4 * r4 + e, L - 1)) * kv_heads + kv];
+  }
+
+  const int ent = c16 / G, hg = c16 % G;
+  const int key0 = kBlock * blk + 4 * r4;
+  bf16_t* stg = sm.stage[wave];
+  // tile -> this lane's query vector c16: its q row, position, partial-state
+  // slot ((row, place) * heads + head) and whether it is a list entry (a slot
+  // past the list repeats the last entry and stores nothing)
+  auto entry = [&](int tile, const bf16_t*& qp, int& t, size_t& ps, bool& live) {
+    const int li = tile * E + ent;
+    live = li < n_list;
+    const int code = sm.list[live ? li : n_list - 1];
+    const int row = q0 + r_lo + (code >> 6);
+    t = off + r_lo + (code >> 6);
+    qp = q + (size_t(row) * heads + kv * G + hg) * D + 8 * r4;
+    ps = (size_t(row) * k_sel + (code & 63)) * heads + kv * G + hg;
+  };
+  const bf16_t* qp;
+  int t;
+  size_t ps;
+  bool live;
+  uint4 qb[4];
+  entry(wave, qp, t, ps, live);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qb[kk] = ld16(qp + 32 * kk);
+  for (int tile = wave; tile < n_tiles; tile += 4) {
+    // the next tile's q rows are requested before this tile's stores, so the
+    // wait for them does not include the stores
+    const bf16_t* qp_n = qp;
+    int t_n = t;
+    size_t ps_n = ps;
+    bool live_n = false;
+    uint4 qn[4] = {qb[0], qb[1], qb[2], qb[3]};
+    if (tile + 4 < n_tiles) {
+      entry(tile + 4, qp_n, t_n, ps_n, live_n);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qn[kk] = ld16(qp_n + 32 * kk);
+    }
+
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sacc[s] = mfma32(ka[s][kk], qb[kk], sacc[s]);
+    }
+    float sv[4][4], mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[s][e] = key0 + 16 * s + e <= t ? sacc[s][e] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[s][e]);
+      }
+    mx = column_max(mx);  // finite: the block's first key is at or before t
+    float p[4][4], lsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[s][e] = sv[s][e] == -INFINITY ? 0.f : fast_exp2(sv[s][e] - mx);
+        if constexpr (CIS) p[s][e] *= cw[s][e];
+        lsum += p[s][e];
+      }
+    lsum = column_sum(lsum);
+    f32x4_t acc[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 pb = make_uint4(pack2(p[2 * h][0], p[2 * h][1]), pack2(p[2 * h][2], p[2 * h][3]),
+                                  pack2(p[2 * h + 1][0], p[2 * h + 1][1]),
+                                  pack2(p[2 * h + 1][2], p[2 * h + 1][3]));
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[n] = mfma32(va[h][n], pb, acc[n]);
+    }
+    // normalised output rows -> this wave's stage (query vector c16 holds dims
+    // 8 (4 r4 + e) + n), then 16 contiguous bytes per lane to the partial slots
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<uint4*>(&stg[c16 * kLdsRow + 32 * r4 + 8 * e]) =
+          make_uint4(pack2(acc[0][e] * inv, acc[1][e] * inv), pack2(acc[2][e] * inv, acc[3][e] * inv),
+                     pack2(acc[4][e] * inv, acc[5][e] * inv), pack2(acc[6][e] * inv, acc[7][e] * inv));
+    if (live && r4 == 0) pml[ps] = make_float2(mx, lsum);
+    __builtin_amdgcn_wave_barrier();  // LDS runs a wave's accesses in order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vq = 4 * i + r4;  // query vector this lane stores: 16 bytes (dims 8 c16 ..)
+      const int live_q = __shfl(int(live), vq);
+      const unsigned lo = __shfl(unsigned(ps), vq), hi = __shfl(unsigned(ps >> 32), vq);
+      const uint4 x = *reinterpret_cast<const uint4*>(&stg[vq * kLdsRow + 8 * c16]);
+      if (live_q) *reinterpret_cast<uint4*>(po + ((size_t(hi) << 32) | lo) * D + 8 * c16) = x;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    qp = qp_n;
+    t = t_n;
+    ps = ps_n;
+    live = live_n;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[kk] = qn[kk];
+  }
+}
+
+// Grid: one dimension over groups of 16 query vectors (row * heads + head);
+// 16 threads per query vector, 8 dims each.  A place is valid when its id is
+// >= 0, its block starts at or before the row's position and no earlier place
+// of the row holds the same id (the partial kernel writes the first such
+// place only).
+__global__ __launch_bounds__(256) void block_merge_kernel(
+    const bf16_t* __restrict__ po, const float2* __restrict__ pml, const int* __restrict__ indices,
+    int k_sel, const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int heads,
+    int kv_heads, long n_qv, bf16_t* __restrict__ out, float* __restrict__ out_f32,
+    float* __restrict__ lse) {
+  const int tid = threadIdx.x, sub = tid & 15, lane = tid & 63;
+  const long qv = long(blockIdx.x) * 16 + (tid >> 4);
+  const bool in = qv < n_qv;
+  const long qc = in ? qv : n_qv - 1;
+  const int row = int(qc / heads), head = int(qc % heads);
+  const int kv = head / (heads / kv_heads);
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int t = (row - cu_q[lo]) + ((cu_k[lo + 1] - cu_k[lo]) - (cu_q[lo + 1] - cu_q[lo]));
+  const int* ids = indices + (size_t(row) * kv_heads + kv) * k_sel;
+
+  // valid places: thread `sub` holds the ids of places sub, sub + 16, ... and
+  // compares them with the earlier places through the 16 lanes of its group
+  const int grp = lane & 48;
+  const int rounds = (k_sel + 15) >> 4;
+  int myid[kMaxPlaces / 16];
+#pragma unroll
+  for (int u = 0; u < kMaxPlaces / 16; ++u) myid[u] = 16 * u + sub < k_sel ? ids[16 * u + sub] : -1;
+  unsigned long long valid = 0ull;
+#pragma unroll
+  for (int u = 0; u < kMaxPlaces / 16; ++u) {
+    if (u >= rounds) break;
+    bool ok = myid[u] >= 0 && myid[u] <= t / kBlock;
+#pragma unroll
+    for (int w = 0; w <= u; ++w)
+      for (int j = 0; j < 16; ++j) {
+        const int other = __shfl(myid[w], grp + j);
+        if (16 * w + j < 16 * u + sub && other == myid[u]) ok = false;
+      }
+    valid |= ((__ballot(ok) >> grp) & 0xFFFFull) << (16 * u);
+  }
+
+  // online merge over batches of 8 places, every load of a batch in flight
+  // together; the running maximum M only grows, the sums are rescaled with it
+  // slot of place p: (row * k_sel + p) * heads + head
+  const size_t base = size_t(row) * k_sel * heads + head;
+  float M = -INFINITY, Ls = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < k_sel; p0 += kMergeBatch) {
+    float2 ml[kMergeBatch];
+    uint4 x[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int p = p0 + u;
+      const bool ok = p < k_sel && ((valid >> p) & 1ull);
+      const size_t slot = base + size_t(p) * heads;
+      ml[u] = ok ? pml[slot] : make_float2(-INFINITY, 0.f);
+      x[u] = ok ? ld16(po + slot * kHeadDim + 8 * sub) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, ml[u].x);
+    if (mb == -INFINITY) continue;  // no valid place yet
+    if (mb > M) {
+      const float alpha = fast_exp2(M - mb);  // 0 while M is -inf (nothing summed yet)
+      Ls *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+      M = mb;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = ml[u].x == -INFINITY ? 0.f : fast_exp2(ml[u].x - M) * ml[u].y;
+      Ls += w;
+      float f[8];
+      f[0] = bf16lo(x[u].x); f[1] = bf16hi(x[u].x); f[2] = bf16lo(x[u].y); f[3] = bf16hi(x[u].y);
+      f[4] = bf16lo(x[u].z); f[5] = bf16hi(x[u].z); f[6] = bf16lo(x[u].w); f[7] = bf16hi(x[u].w);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] += w * f[d];
+    }
+  }
+  if (!in) return;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  if (out_f32 != nullptr) {
+    float* dst = out_f32 + size_t(qv) * kHeadDim + 8 * sub;
+    *reinterpret_cast<float4*>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  } else {
+    *reinterpret_cast<uint4*>(out + size_t(qv) * kHeadDim + 8 * sub) =
+        make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+  }
+  if (lse != nullptr && sub == 0) lse[qv] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+template <int G, bool CIS>
+hipError_t launch_partial_g(const void* q, const void* k, const void* v, const int* indices,
+                            int k_sel, const float* cis, const int* cu_q, const int* cu_k,
+                            int kv_heads, int nb_max, int n_chunk, unsigned n_wg, float sl2,
+                            bf16_t* po, float2* pml, hipStream_t s) {
+  return launch_kernel(kKindAttn, block_partial_kernel<G, CIS>, dim3(n_wg), dim3(256), s,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), indices, k_sel, cis, cu_q, cu_k, kv_heads,
+                       nb_max, n_chunk, sl2, po, pml);
+}
+
+template <bool CIS>
+hipError_t launch_partial_c(int G, const void* q, const void* k, const void* v, const int* idx,
+                            int k_sel, const float* cis, const int* cu_q, const int* cu_k,
+                            int kvh, int nb_max, int n_chunk, unsigned n_wg, float sl2,
+                            bf16_t* po, float2* pml, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_partial_g<1, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
+    case 2: return launch_partial_g<2, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
+    case 4: return launch_partial_g<4, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
+    case 8: return launch_partial_g<8, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
+    case 16: return launch_partial_g<16, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t po_bytes(int rows_total, int heads, int k_sel) {
+  return (size_t(rows_total) * heads * k_sel * kHeadDim * sizeof(uint16_t) + 255) & ~size_t(255);
+}
+
+}  // namespace
+
+size_t block_attn_ws_bytes(int rows_total, int heads, int k_sel) {
+  if (rows_total <= 0 || heads <= 0 || k_sel <= 0) return 0;
+  return po_bytes(rows_total, heads, k_sel) +
+         ((size_t(rows_total) * heads * k_sel * sizeof(float2) + 255) & ~size_t(255));
+}
+
+bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k) {
+  const long long nb = (max_seqlen_k + kBlock - 1) / kBlock;
+  const long long nc = (max_seqlen_k + kScanRows - 1) / kScanRows;
+  // every grid dimension holds fewer than 2^32 work-items
+  return (long long)batch * kv_heads * nb * nc * 256 <= UINT_MAX &&
+         (long long)rows_total * heads * 16 <= UINT_MAX;
+}
+
+hipError_t launch_block_attn(const void* q, const void* k, const void* v, const int* indices,
+                             int k_sel, const float* cis, void* out, float* out_f32, float* lse,
+                             const int* cu_q, const int* cu_k, int batch, int rows_total,
+                             int heads, int kv_heads, int max_seqlen_k, float scale_log2,
+                             void* ws, hipStream_t s) {
+  if (rows_total == 0 || batch == 0 || max_seqlen_k == 0) return hipSuccess;
+  if (k_sel > kMaxPlaces || !block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k))
+    return hipErrorInvalidValue;
+  const int G = heads / kv_heads;
+  const int nb_max = (max_seqlen_k + kBlock - 1) / kBlock;
+  const int n_chunk = (max_seqlen_k + kScanRows - 1) / kScanRows;
+  const unsigned n_wg = unsigned(batch) * kv_heads * n_chunk * nb_max;
+  bf16_t* po = static_cast<bf16_t*>(ws);
+  float2* pml = reinterpret_cast<float2*>(static_cast<char*>(ws) + po_bytes(rows_total, heads, k_sel));
+  hipError_t e = cis != nullptr
+                     ? launch_partial_c<true>(G, q, k, v, indices, k_sel, cis, cu_q, cu_k, kv_heads, nb_max, n_chunk, n_wg, scale_log2, po, pml, s)
+                     : launch_partial_c<false>(G, q, k, v, indices, k_sel, cis, cu_q, cu_k, kv_heads, nb_max, n_chunk, n_wg, scale_log2, po, pml, s);
+  if (e != hipSuccess) return e;
+  const long n_qv = long(rows_total) * heads;
+  return launch_kernel(kKindCombine, block_merge_kernel, dim3(unsigned((n_qv + 15) / 16)),
+                       dim3(256), s, static_cast<const bf16_t*>(po),
+                       static_cast<const float2*>(pml), indices, k_sel, cu_q, cu_k, batch, heads,
+                       kv_heads, n_qv, static_cast<bf16_t*>(out), out_f32, lse);
+}
+
+}  // namespace nsa

@@ -259,6 +259,12 @@ def test_selected_attn_block_mass_probe(dtype):
     assert_close("block_mass", np64(out), ref, atol=2e-3)
 
 
+def _path_ws(path):
+    """None: the binding allocates the queried workspace (key-block path for
+    bf16 prefill rows); an empty buffer: the row-by-row path."""
+    return None if path == "blocks" else torch.empty(0, dtype=torch.uint8, device=DEV)
+
+
 def _sample_rows(lengths, extra=40):
     rows, r0 = [], 0
     for L in lengths:
@@ -270,8 +276,9 @@ def _sample_rows(lengths, extra=40):
     return rows
 
 
+@pytest.mark.parametrize("path", ["blocks", "rows"])
 @pytest.mark.parametrize("cis_mode", [False, True])
-def test_selected_attn_prefill_given_indices(cis_mode):
+def test_selected_attn_prefill_given_indices(cis_mode, path):
     w = W.scaled(W.selected_prefill(), [1500, 2100])
     q = W.prefill_query(w, DEV)
     k, v = W.keys_values(w, DEV)
@@ -279,9 +286,10 @@ def test_selected_attn_prefill_given_indices(cis_mode):
     idx = W.given_block_indices(w, DEV)
     cu_k = cu(w.lengths)
     out = torch.full_like(q, float("nan"))
-    log(f"prefill selected attn cis={cis_mode}")
+    log(f"prefill selected attn cis={cis_mode} path={path}")
     nsa.nsa_selected_attn_fwd(q, k, v, idx, cu_k, max(w.lengths), out,
-                              cis=cis if cis_mode else None, cu_seqlens_q=cu_k)
+                              cis=cis if cis_mode else None, cu_seqlens_q=cu_k,
+                              workspace=_path_ws(path))
     torch.cuda.synchronize()
     rows = _sample_rows(w.lengths)
     qn, kn, vn, cn, idxn = np64(q), np64(k), np64(v), np64(cis), idx.cpu().numpy()
@@ -590,16 +598,19 @@ def test_decode_step_cis_values_full_size():
                   atol=2e-2)
 
 
-def test_selected_attn_prefill_full_size_sampled_rows():
-    """Given-index selected attention at full size (8 x 16384 rows), sampled rows."""
+@pytest.mark.parametrize("path", ["blocks", "rows"])
+def test_selected_attn_prefill_full_size_sampled_rows(path):
+    """Given-index selected attention at full size (8 x 16384 rows), sampled rows,
+    on the key-block path (the launch the benchmark times) and the row path."""
     w = W.selected_prefill()
     q = W.prefill_query(w, DEV)
     k, v = W.keys_values(w, DEV)
     idx = W.given_block_indices(w, DEV)
     cu_k = cu(w.lengths)
     out = torch.full_like(q, float("nan"))
-    log(f"prefill selected attn full size {w.name}")
-    nsa.nsa_selected_attn_fwd(q, k, v, idx, cu_k, max(w.lengths), out, cu_seqlens_q=cu_k)
+    log(f"prefill selected attn full size {w.name} path={path}")
+    nsa.nsa_selected_attn_fwd(q, k, v, idx, cu_k, max(w.lengths), out, cu_seqlens_q=cu_k,
+                              workspace=_path_ws(path))
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     cu_np = _cu_np(cu_k)

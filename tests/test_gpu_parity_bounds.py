@@ -196,8 +196,8 @@ def test_selected_attn_decode_pages_style_indices(dtype, cis_mode):
     assert_close("decode_pages_ids", np64(out), ref, atol=2e-2 if dtype == BF16 else 1e-4)
 
 
-@pytest.mark.parametrize("dtype", [F32, BF16])
-def test_selected_attn_prefill_pages_style_indices(dtype):
+@pytest.mark.parametrize("dtype,path", [(F32, "rows"), (BF16, "rows"), (BF16, "blocks")])
+def test_selected_attn_prefill_pages_style_indices(dtype, path):
     """Prefill rows with ids drawn uniformly over the whole sequence's blocks (the
     pages' correctness check draws them with randint; here without repeats), so
     most rows list blocks past their own position, which must be skipped; -1
@@ -213,9 +213,10 @@ def test_selected_attn_prefill_pages_style_indices(dtype):
     cu_k = cu(lengths)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((N, 16), float("nan"), device=DEV)
-    log(f"selected attn prefill, pages-style ids {dtype}")
+    log(f"selected attn prefill, pages-style ids {dtype} path={path}")
+    ws = None if path == "blocks" else torch.empty(0, dtype=torch.uint8, device=DEV)
     nsa.nsa_selected_attn_fwd(q, k, v, torch.from_numpy(idx).to(DEV), cu_k, max(lengths), out,
-                              lse=lse, cu_seqlens_q=cu_k)
+                              lse=lse, cu_seqlens_q=cu_k, workspace=ws)
     torch.cuda.synchronize()
     qn, kn, vn, got, lse_g = np64(q), np64(k), np64(v), np64(out), np64(lse)
     s0, r = 0, 0

@@ -13,21 +13,23 @@
 // Here the roles are swapped:
 //
 // block_partial_kernel -- one workgroup per (sequence, KV head, chunk of 1024
-//   query rows, 64-key block).  It stages the block's K and V rows in LDS once,
-//   scans the chunk's index rows for the rows that list the block (and at which
-//   place), and walks those rows in tiles of 16 query vectors (a query vector is
-//   one (row, head) pair: 16/G rows of G heads).  Each wave holds the whole
-//   block as matrix-core operands (K in the A layout of S^T = K Q^T, V^T in the
-//   A layout of O^T = V^T P^T), so a tile costs its q rows in, 32
+//   query rows, 64-key block).  It builds the block's matrix-core operands
+//   once, in LDS (K in the A layout of S^T = K Q^T, V^T in the A layout of
+//   O^T = V^T P^T), scans the chunk's index rows for the rows that list the
+//   block (and at which place), and walks those rows in tiles of 16 query
+//   vectors (a query vector is one (row, head) pair: 16/G rows of G heads), one
+//   tile per wave at a time, so a tile costs its q rows in, 32
 //   v_mfma_f32_16x16x32_bf16, and its partial state out: the block's
-//   normalised output in bf16 plus (max, sum) in fp32, at the row's place.
+//   unnormalised output in bf16 plus (max, sum) in fp32, at the row's place.
 // block_merge_kernel -- per (row, head): the partial states of the row's valid
 //   places combined with the usual log-sum-exp weights.
 //
 // Precision is that of the row-by-row kernel: bf16 probabilities enter the
-// matrix cores, fp32 sums; each partial output is rounded to bf16 once more
-// (2^-9 relative) before the merge.
+// matrix cores, fp32 sums (the normaliser sums the fp32 probabilities); each
+// partial output is rounded to bf16 once more (2^-9 relative) before the
+// merge.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -69,11 +71,18 @@ __device__ __forceinline__ float column_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// The block's matrix-core operands are the same for the four waves, so they are
+// built once per workgroup and kept in LDS in lane order (lane-contiguous 16-byte
+// reads, free of bank conflicts): kop[s * 4 + kk][lane] is the A operand of
+// S^T = K Q^T for key slice s and dims 32 kk .. (key 16 s + c16, dims
+// 32 kk + 8 r4 .. +8), vop[h * 8 + n][lane] the A operand of O^T += V^T P^T for
+// output tile n and key half h (row c16 = dim 8 c16 + n; k index 8 r4 + u = key
+// 32 h + 16 (u / 4) + 4 r4 + u % 4).
 struct PartialLds {
-  bf16_t k[kBlock * kLdsRow];
-  bf16_t v[kBlock * kLdsRow];
+  uint4 kop[16][64];
+  uint4 vop[16][64];
   bf16_t stage[4][16 * kLdsRow];  // per wave: one tile's 16 output rows, for the stores
-  int list[kScanRows];            // (row in chunk << 6) | place
+  uint16_t list[kScanRows];       // (row in chunk << 6) | place
   int n_list;
 };
 
@@ -112,7 +121,7 @@ __device__ __forceinline__ void scan_rows_vec(PartialLds& sm, const int* __restr
       if (lane == 0 && wmask != 0ull) base = atomicAdd(&sm.n_list, __popcll(wmask));
       base = __shfl(base, 0);
       if (writer)
-        sm.list[base + __popcll(wmask & ((1ull << lane) - 1ull))] = ((r - r_lo) << 6) | (4 * seg + u);
+        sm.list[base + __popcll(wmask & ((1ull << lane) - 1ull))] = uint16_t(((r - r_lo) << 6) | (4 * seg + u));
     }
   }
 }
@@ -140,7 +149,7 @@ __device__ __forceinline__ void scan_rows_scalar(PartialLds& sm, const int* __re
     if (lane == 0 && mask != 0ull) base = atomicAdd(&sm.n_list, __popcll(mask));
     base = __shfl(base, 0);
     if (place >= 0)
-      sm.list[base + __popcll(mask & ((1ull << lane) - 1ull))] = ((r - r_lo) << 6) | place;
+      sm.list[base + __popcll(mask & ((1ull << lane) - 1ull))] = uint16_t(((r - r_lo) << 6) | place);
   }
 }
 
@@ -151,7 +160,7 @@ __device__ __forceinline__ void scan_rows_scalar(PartialLds& sm, const int* __re
 // pml[(row * k_sel + place) * heads + head] = (max, sum) in the log2 domain: the
 // G heads of one (row, place) are contiguous.
 template <int G, bool CIS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void block_partial_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void block_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads, int nb_max,
@@ -177,18 +186,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   if (r_first >= r_hi || kBlock * blk >= L) return;  // the same for the whole workgroup
   const int heads = kv_heads * G;
 
-  // the block's K and V rows (rows past the sequence end repeat its last row:
-  // finite data, masked below since they lie past every row's position),
-  // requested before the index scan so both are in flight together
+  // The block's operands straight from K and V (rows past the sequence end
+  // repeat its last row: finite data, masked below since they lie past every
+  // row's position), requested before the index scan so both are in flight
+  // together.  Waves 0 and 1 build the K operands of slices 2w, 2w + 1; waves 2
+  // and 3 the V operands of half w - 2 (eight V rows' 16-byte pieces per lane,
+  // transposed in registers).
   if (tid == 0) sm.n_list = 0;
-  uint4 kst[4], vst[4];
+  uint4 ld[8];
+  const size_t rs = size_t(kv_heads) * D;
+  const bf16_t* kb = k + size_t(kstart) * rs + size_t(kv) * D;
+  const bf16_t* vb = v + size_t(kstart) * rs + size_t(kv) * D;
+  if (wave < 2) {
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int x = tid + 256 * it, key = x >> 4, ch = x & 15;
-    const int j = min(kBlock * blk + key, L - 1);
-    const size_t g = (size_t(kstart + j) * kv_heads + kv) * D + 8 * ch;
-    kst[it] = ld16(k + g);
-    vst[it] = ld16(v + g);
+    for (int i = 0; i < 8; ++i) {
+      const int s = 2 * wave + (i >> 2), kk = i & 3;
+      ld[i] = ld16(kb + size_t(min(kBlock * blk + 16 * s + c16, L - 1)) * rs + 32 * kk + 8 * r4);
+    }
+  } else {
+    const int h = wave - 2;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int key = 32 * h + 16 * (u >> 2) + 4 * r4 + (u & 3);
+      ld[u] = ld16(vb + size_t(min(kBlock * blk + key, L - 1)) * rs + 8 * c16);
+    }
   }
   __syncthreads();  // n_list = 0 seen by every wave
   if ((k_sel & 3) == 0 && (reinterpret_cast<uintptr_t>(indices) & 15) == 0) {
@@ -201,46 +222,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   } else {
     scan_rows_scalar(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, tid, lane);
   }
+  if (wave < 2) {
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int x = tid + 256 * it, key = x >> 4, ch = x & 15;
-    *reinterpret_cast<uint4*>(&sm.k[key * kLdsRow + 8 * ch]) = kst[it];
-    *reinterpret_cast<uint4*>(&sm.v[key * kLdsRow + 8 * ch]) = vst[it];
+    for (int i = 0; i < 8; ++i) sm.kop[8 * wave + i][lane] = ld[i];
+  } else {
+    const int h = wave - 2;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t a = (&ld[2 * x].x)[n >> 1], c = (&ld[2 * x + 1].x)[n >> 1];
+        w[x] = (n & 1) ? (a >> 16) | (c & 0xFFFF0000u) : (a & 0xFFFFu) | (c << 16);
+      }
+      sm.vop[8 * h + n][lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
   __syncthreads();
   const int n_list = sm.n_list;
   const int n_tiles = (n_list + E - 1) / E;
   if (wave >= n_tiles) return;  // no barrier below
 
-  // the block as matrix-core operands of this wave
-  uint4 ka[4][4];  // S^T = K Q^T, A: key 16 s + c16, dims 32 kk + 8 r4 .. +8
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      ka[s][kk] = *reinterpret_cast<const uint4*>(&sm.k[(16 * s + c16) * kLdsRow + 32 * kk + 8 * r4]);
-  // O^T += V^T P^T, A of output tile n (row c16 = dim 8 c16 + n) for the keys of
-  // half h (k index 8 r4 + u = key 32 h + 16 (u / 4) + 4 r4 + u % 4)
-  uint4 va[2][8];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint4 rows[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int key = 32 * h + 16 * (u >> 2) + 4 * r4 + (u & 3);
-      rows[u] = *reinterpret_cast<const uint4*>(&sm.v[key * kLdsRow + 8 * c16]);
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      uint32_t w[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const uint32_t a = (&rows[2 * x].x)[n >> 1], c = (&rows[2 * x + 1].x)[n >> 1];
-        w[x] = (n & 1) ? (a >> 16) | (c & 0xFFFF0000u) : (a & 0xFFFFu) | (c << 16);
-      }
-      va[h][n] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
   float cw[4][4];  // CIS of key 16 s + 4 r4 + e
   if constexpr (CIS) {
 #pragma unroll
@@ -252,66 +254,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   const int ent = c16 / G, hg = c16 % G;
   const int key0 = kBlock * blk + 4 * r4;
+  const int last_key = kBlock * blk + kBlock - 1;
+  // the log2-domain scale is applied inside one fma per score: p = exp2(c s - c m)
+  // with m the raw maximum (the minimum for a negative scale)
+  const float c = scale_log2;
   bf16_t* stg = sm.stage[wave];
-  // tile -> this lane's query vector c16: its q row, position, partial-state
-  // slot ((row, place) * heads + head) and whether it is a list entry (a slot
-  // past the list repeats the last entry and stores nothing)
-  auto entry = [&](int tile, const bf16_t*& qp, int& t, size_t& ps, bool& live) {
-    const int li = tile * E + ent;
-    live = li < n_list;
-    const int code = sm.list[live ? li : n_list - 1];
-    const int row = q0 + r_lo + (code >> 6);
-    t = off + r_lo + (code >> 6);
-    qp = q + (size_t(row) * heads + kv * G + hg) * D + 8 * r4;
-    ps = (size_t(row) * k_sel + (code & 63)) * heads + kv * G + hg;
-  };
-  const bf16_t* qp;
-  int t;
-  size_t ps;
-  bool live;
-  uint4 qb[4];
-  entry(wave, qp, t, ps, live);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qb[kk] = ld16(qp + 32 * kk);
-  for (int tile = wave; tile < n_tiles; tile += 4) {
-    // the next tile's q rows are requested before this tile's stores, so the
-    // wait for them does not include the stores
-    const bf16_t* qp_n = qp;
-    int t_n = t;
-    size_t ps_n = ps;
-    bool live_n = false;
-    uint4 qn[4] = {qb[0], qb[1], qb[2], qb[3]};
-    if (tile + 4 < n_tiles) {
-      entry(tile + 4, qp_n, t_n, ps_n, live_n);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qn[kk] = ld16(qp_n + 32 * kk);
-    }
 
+  // One tile: this lane's query vector c16 (entry c16 / G of the tile, head
+  // c16 % G) -- its position, its q operand, and whether it is a list entry (a
+  // slot past the list repeats the last entry and stores nothing).
+  struct Tile {
+    int t;
+    bool live;
+    uint4 q[4];
+  };
+  auto fetch = [&](int tile, Tile& T) {
+    const int li = tile * E + ent;
+    T.live = li < n_list;
+    const int code = sm.list[T.live ? li : n_list - 1];
+    T.t = off + r_lo + (code >> 6);
+    const bf16_t* qp = q + (size_t(q0 + r_lo + (code >> 6)) * heads + kv * G + hg) * D + 8 * r4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) T.q[kk] = ld16(qp + 32 * kk);
+  };
+
+  auto compute = [&](auto pos_tag, int tile, const Tile& T) {
+    constexpr bool pos = decltype(pos_tag)::value;  // scale >= 0: maximum of the raw scores
     f32x4_t sacc[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sacc[s] = mfma32(ka[s][kk], qb[kk], sacc[s]);
+      for (int kk = 0; kk < 4; ++kk) sacc[s] = mfma32(sm.kop[4 * s + kk][lane], T.q[kk], sacc[s]);
     }
-    float sv[4][4], mx = -INFINITY;
+    // keys past a row's position exist only when the block holds the row's own
+    // position: mask only then (the same branch for the whole wave)
+    const bool masked = __any(T.t < last_key);
+    if (masked) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key0 + 16 * s + e > T.t) sacc[s][e] = pos ? -INFINITY : INFINITY;
+    }
+    float mr = sacc[0][0];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mr = pos ? fmaxf(mr, sacc[s][e]) : fminf(mr, sacc[s][e]);
+    mr = pos ? column_max(mr) : -column_max(-mr);  // finite: the block's first key is visible
+    const float mc = mr * c;
+    float p[4][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sv[s][e] = key0 + 16 * s + e <= t ? sacc[s][e] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[s][e]);
-      }
-    mx = column_max(mx);  // finite: the block's first key is at or before t
-    float p[4][4], lsum = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[s][e] = sv[s][e] == -INFINITY ? 0.f : fast_exp2(sv[s][e] - mx);
+        p[s][e] = fast_exp2(fmaf(sacc[s][e], c, -mc));
         if constexpr (CIS) p[s][e] *= cw[s][e];
-        lsum += p[s][e];
       }
+    if (masked) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key0 + 16 * s + e > T.t) p[s][e] = 0.f;
+    }
+    float lsum = 0.f;  // the normaliser sums the fp32 probabilities
+#pragma unroll
+    for (int s = 0; s < 4; ++s) lsum += (p[s][0] + p[s][1]) + (p[s][2] + p[s][3]);
     lsum = column_sum(lsum);
     f32x4_t acc[8];
 #pragma unroll
@@ -322,35 +332,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                                   pack2(p[2 * h + 1][0], p[2 * h + 1][1]),
                                   pack2(p[2 * h + 1][2], p[2 * h + 1][3]));
 #pragma unroll
-      for (int n = 0; n < 8; ++n) acc[n] = mfma32(va[h][n], pb, acc[n]);
+      for (int n = 0; n < 8; ++n) acc[n] = mfma32(sm.vop[8 * h + n][lane], pb, acc[n]);
     }
-    // normalised output rows -> this wave's stage (query vector c16 holds dims
+    // unnormalised output rows -> this wave's stage (query vector c16 holds dims
     // 8 (4 r4 + e) + n), then 16 contiguous bytes per lane to the partial slots
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       *reinterpret_cast<uint4*>(&stg[c16 * kLdsRow + 32 * r4 + 8 * e]) =
-          make_uint4(pack2(acc[0][e] * inv, acc[1][e] * inv), pack2(acc[2][e] * inv, acc[3][e] * inv),
-                     pack2(acc[4][e] * inv, acc[5][e] * inv), pack2(acc[6][e] * inv, acc[7][e] * inv));
-    if (live && r4 == 0) pml[ps] = make_float2(mx, lsum);
+          make_uint4(pack2(acc[0][e], acc[1][e]), pack2(acc[2][e], acc[3][e]),
+                     pack2(acc[4][e], acc[5][e]), pack2(acc[6][e], acc[7][e]));
+    if (T.live && r4 == 0) {
+      const int code = sm.list[tile * E + ent];
+      pml[(size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + hg] =
+          make_float2(mc, lsum);
+    }
     __builtin_amdgcn_wave_barrier();  // LDS runs a wave's accesses in order
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vq = 4 * i + r4;  // query vector this lane stores: 16 bytes (dims 8 c16 ..)
-      const int live_q = __shfl(int(live), vq);
-      const unsigned lo = __shfl(unsigned(ps), vq), hi = __shfl(unsigned(ps >> 32), vq);
+      const int li = tile * E + vq / G;
       const uint4 x = *reinterpret_cast<const uint4*>(&stg[vq * kLdsRow + 8 * c16]);
-      if (live_q) *reinterpret_cast<uint4*>(po + ((size_t(hi) << 32) | lo) * D + 8 * c16) = x;
+      if (li < n_list) {
+        const int code = sm.list[li];
+        const size_t slot = (size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + vq % G;
+        *reinterpret_cast<uint4*>(po + slot * D + 8 * c16) = x;
+      }
     }
     __builtin_amdgcn_wave_barrier();
+  };
 
-    qp = qp_n;
-    t = t_n;
-    ps = ps_n;
-    live = live_n;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qb[kk] = qn[kk];
-  }
+  // Two tile buffers used in turn: the q rows of the wave's next tile are
+  // requested before the current tile's stores, so waiting for them does not
+  // include the stores.
+  auto run = [&](auto pos_tag) {
+    Tile A, B;
+    fetch(wave, A);
+    for (int tile = wave; tile < n_tiles; tile += 8) {
+      if (tile + 4 < n_tiles) fetch(tile + 4, B);
+      compute(pos_tag, tile, A);
+      if (tile + 4 >= n_tiles) break;
+      if (tile + 8 < n_tiles) fetch(tile + 8, A);
+      compute(pos_tag, tile + 4, B);
+    }
+  };
+  if (c >= 0.f) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // Grid: one dimension over groups of 16 query vectors (row * heads + head);
@@ -428,8 +454,8 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float w = ml[u].x == -INFINITY ? 0.f : fast_exp2(ml[u].x - M) * ml[u].y;
-      Ls += w;
+      const float w = ml[u].x == -INFINITY ? 0.f : fast_exp2(ml[u].x - M);
+      Ls += w * ml[u].y;
       float f[8];
       f[0] = bf16lo(x[u].x); f[1] = bf16hi(x[u].x); f[2] = bf16lo(x[u].y); f[3] = bf16hi(x[u].y);
       f[4] = bf16lo(x[u].z); f[5] = bf16hi(x[u].z); f[6] = bf16lo(x[u].w); f[7] = bf16hi(x[u].w);

@@ -67,7 +67,8 @@ def parse():
                     help="prefill-blockmask: tokens per sequence (the pages' table: 1024, 4096, 16384)")
     ap.add_argument("--causal", action="store_true", help="prefill-blockmask: lower triangle only")
     ap.add_argument("--selected-path", choices=["blocks", "rows"], default="blocks",
-                    help="prefill-selected: key-block stationary (workspace given) or row by row")
+                    help="prefill workloads: selected attention key-block stationary (its "
+                         "workspace given) or row by row")
     ap.add_argument("--workload", choices=["decode", "decode-long", "decode-tiny", "decode-offload",
                                            "prefill-selected", "prefill-nsa", "prefill-blockmask",
                                            "prefill-selected-bwd", "prefill-nsa-bwd"],
@@ -871,7 +872,9 @@ def prefill_main(args, dev):
         idx = torch.empty((L, w.kv_heads, w.topk), dtype=torch.int32, device=dev)
         p = nsa.prefill_params(q, k, v, kc, vc, g, cu, cu, cuc, L, out, topk=w.topk,
                                window=w.window, indices=idx)
-        ws = torch.empty(nsa.prefill_workspace_size(p), dtype=torch.uint8, device=dev)
+        ws_bytes = (nsa.prefill_workspace_size(p) if args.selected_path == "blocks"
+                    else nsa.prefill_workspace_size_min(p))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
         def fn():
@@ -880,6 +883,8 @@ def prefill_main(args, dev):
                  "compressed_attn": nsa.KERNEL_COMPRESSED_ATTN,
                  "select": nsa.KERNEL_BLOCK_SCORES, "selected_attn": nsa.KERNEL_SELECTED_ATTN,
                  "window_attn": nsa.KERNEL_WINDOW_ATTN}
+        if args.selected_path == "blocks":  # the selected branch's partial-state merge
+            kinds["selected_merge"] = nsa.KERNEL_COMBINE
         fn()
         torch.cuda.synchronize()
         t = np.arange(L, dtype=np.int64)
@@ -919,7 +924,7 @@ def prefill_main(args, dev):
         "config": {"workload": w.name, "batch": w.batch, "seq_len": max(w.lengths), "heads": w.heads,
                    "kv_heads": w.kv_heads, "head_dim": D, "topk": w.topk,
                    **({"window": w.window} if args.workload == "prefill-nsa" else {}),
-                   **({"selected_path": args.selected_path} if args.workload == "prefill-selected" else {})},
+                   "selected_path": args.selected_path},
         "roofline": {
             "kernel": dominant,
             "bound": "mfma",
@@ -947,6 +952,7 @@ def prefill_main(args, dev):
         result["partial_state_bytes"] = pbytes
         result["partial_write_gbs"] = round(pbytes / (kern["selected_attn"] * 1e-6) / 1e9, 1)
         result["merge_read_gbs"] = round(pbytes / (kern["merge"] * 1e-6) / 1e9, 1)
+    if args.selected_path == "blocks":  # no per-row gather on the key-block path
         del result["selected_gathered_gbs"]
     if not args.no_cpu_baseline:
         import oracle

@@ -618,7 +618,16 @@ typedef struct nsa_prefill_params {
   float softmax_scale;
 } nsa_prefill_params;
 
+/*
+ * Workspace: nsa_prefill_workspace_size(p) bytes (16-byte aligned) run the
+ * selected branch key-block stationary (as nsa_selected_attn_fwd given a
+ * workspace; the size includes its partial states, rows * heads * topk * 264
+ * bytes, and its merged rows in float32 until the gated sum, rows * heads *
+ * 512 bytes); any size from nsa_prefill_workspace_size_min(p) up to that runs
+ * it row by row.  Less: NSA_ERR_WORKSPACE.
+ */
 size_t nsa_prefill_workspace_size(const nsa_prefill_params* p);
+size_t nsa_prefill_workspace_size_min(const nsa_prefill_params* p);
 nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 

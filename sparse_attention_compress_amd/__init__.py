@@ -135,6 +135,7 @@ _SIGS = {
                                            c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                            c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "nsa_prefill_workspace_size": (c_sz, [ctypes.POINTER(PrefillParams)]),
+    "nsa_prefill_workspace_size_min": (c_sz, [ctypes.POINTER(PrefillParams)]),
     "nsa_prefill_step": (ctypes.c_int, [ctypes.POINTER(PrefillParams), c_vp, c_sz, c_vp]),
 }
 
@@ -566,7 +567,13 @@ def prefill_params(q, k, v, k_c, v_c, gates, cu_seqlens_q, cu_seqlens_k, cu_seql
 
 
 def prefill_workspace_size(params: PrefillParams) -> int:
+    """Workspace bytes of the prefill step with the key-block selected branch."""
     return lib().nsa_prefill_workspace_size(ctypes.byref(params))
+
+
+def prefill_workspace_size_min(params: PrefillParams) -> int:
+    """Smallest workspace of the prefill step (row-by-row selected branch)."""
+    return lib().nsa_prefill_workspace_size_min(ctypes.byref(params))
 
 
 def nsa_prefill_step(params: PrefillParams, workspace=None, device=None, stream=None):

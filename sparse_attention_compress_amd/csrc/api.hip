@@ -968,7 +968,7 @@ nsa_status nsa_window_attn_fwd(const void* q, const void* k, const void* v, nsa_
 namespace {
 
 struct PrefillLayout {
-  size_t lse2, vct, vt, o_cmp, o_sel, scores, indices, total;
+  size_t lse2, vct, vt, o_cmp, o_sel, scores, indices, partial, o_sel32, base, total;
   int nb_max, max_windows;
 };
 
@@ -993,6 +993,14 @@ PrefillLayout prefill_layout(const nsa_prefill_params* p) {
   if (p->block_scores == nullptr) off += up(rows * p->kv_heads * size_t(L.nb_max) * sizeof(float));
   L.indices = off;
   if (p->indices == nullptr) off += up(rows * p->kv_heads * size_t(p->topk) * sizeof(int32_t));
+  L.base = off;  // enough for the row-by-row selected branch
+  // the key-block selected branch: its partial states, and its merged rows kept
+  // in float32 until the gated sum (one bf16 rounding fewer, for the one its
+  // partial states add)
+  L.partial = off;
+  off += nsa::block_attn_ws_bytes(p->rows_total, p->heads, p->topk);
+  L.o_sel32 = off;
+  off += up(rows * H * p->head_dim * sizeof(float));
   L.total = off;
   return L;
 }
@@ -1029,6 +1037,11 @@ size_t nsa_prefill_workspace_size(const nsa_prefill_params* p) {
   return prefill_layout(p).total;
 }
 
+size_t nsa_prefill_workspace_size_min(const nsa_prefill_params* p) {
+  if (check_prefill(p) != NSA_OK || p->batch == 0 || p->rows_total == 0) return 0;
+  return prefill_layout(p).base;
+}
+
 nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   const char* fn = "nsa_prefill_step";
@@ -1037,7 +1050,11 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   if (p->batch == 0 || p->rows_total == 0) return ok();
   const PrefillLayout lay = prefill_layout(p);
   NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
-  NSA_REQUIRE(workspace_bytes >= lay.total, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, lay.total);
+  NSA_REQUIRE(workspace_bytes >= lay.base, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, lay.base);
+  NSA_REQUIRE(aligned16(workspace), NSA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  // the key-block selected branch when the workspace holds its partial states
+  const bool blocks = workspace_bytes >= lay.total &&
+                      nsa::block_attn_grid_fits(p->batch, p->rows_total, p->heads, p->kv_heads, p->max_seqlen_k);
   char* base = static_cast<char*>(workspace);
   nsa::bf16_t* o_cmp = reinterpret_cast<nsa::bf16_t*>(base + lay.o_cmp);
   nsa::bf16_t* o_sel = reinterpret_cast<nsa::bf16_t*>(base + lay.o_sel);
@@ -1091,9 +1108,16 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
                               p->kv_heads, lay.nb_max, p->topk, p->n_init, p->n_local, stream);
   if (e != hipSuccess) return hip_status(e, fn);
   // 4. selected branch (bf16 rows)
-  e = nsa::launch_selected_attn(p->q, p->k, p->v, 1, idx, p->topk, nullptr, o_sel, nullptr,
-                                p->cu_seqlens_q, p->cu_seqlens_k, p->batch, p->rows_total,
-                                p->heads, p->kv_heads, sl2, nsa::AttnWs{nullptr, nullptr}, stream);
+  float* o_sel32 = blocks ? reinterpret_cast<float*>(base + lay.o_sel32) : nullptr;
+  if (blocks)
+    e = nsa::launch_block_attn(p->q, p->k, p->v, idx, p->topk, nullptr, nullptr, o_sel32, nullptr,
+                               p->cu_seqlens_q, p->cu_seqlens_k, p->batch, p->rows_total,
+                               p->heads, p->kv_heads, p->max_seqlen_k, sl2, base + lay.partial,
+                               stream);
+  else
+    e = nsa::launch_selected_attn(p->q, p->k, p->v, 1, idx, p->topk, nullptr, o_sel, nullptr,
+                                  p->cu_seqlens_q, p->cu_seqlens_k, p->batch, p->rows_total,
+                                  p->heads, p->kv_heads, sl2, nsa::AttnWs{nullptr, nullptr}, stream);
   if (e != hipSuccess) return hip_status(e, fn);
   // 5. window branch and the gated sum
   nsa::WindowPrefillArgs w{};
@@ -1117,6 +1141,7 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   w.gates = p->gates;
   w.o_cmp = o_cmp;
   w.o_sel = o_sel;
+  w.o_sel32 = o_sel32;
   return hip_status(nsa::launch_window_prefill(w, stream), fn);
 }
 

@@ -217,6 +217,7 @@ struct WindowPrefillArgs {
   const float* gates;    // nullable [rows, heads, 3]: gated sum with o_cmp and o_sel
   const bf16_t* o_cmp;   // [rows, heads, 128] (with gates)
   const bf16_t* o_sel;   // [rows, heads, 128] (with gates)
+  const float* o_sel32;  // nullable [rows, heads, 128]: o_sel as float32 rows instead
 };
 hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s);
 

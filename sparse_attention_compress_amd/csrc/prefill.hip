@@ -492,7 +492,8 @@ __global__ __launch_bounds__(GT / TPW * kWave) void compressed_prefill_kernel(
 // --------------------------------------------------------------- window branch
 
 // Sliding-window attention over keys max(0, t-W+1) .. t; with GATED the output
-// is g0 * o_cmp + g1 * o_sel + g2 * o_win (the other branches' outputs are bf16 rows).
+// is g0 * o_cmp + g1 * o_sel + g2 * o_win (the other branches' outputs are bf16 rows;
+// o_sel32, when given, holds the selected branch as float32 rows instead).
 // The wave's tokens share the key tiles of the union of their windows.
 // vtr: the values transposed ([batch][kv][128][ldv]).
 template <int G, bool GATED, int TPW, int GT>
@@ -501,7 +502,8 @@ __global__ __launch_bounds__(GT / TPW * kWave) void window_prefill_kernel(
     int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads,
     int window, float scale_log2, void* __restrict__ out, int out_f32,
     float* __restrict__ lse_nat, const float* __restrict__ gates,
-    const bf16_t* __restrict__ o_cmp, const bf16_t* __restrict__ o_sel) {
+    const bf16_t* __restrict__ o_cmp, const bf16_t* __restrict__ o_sel,
+    const float* __restrict__ o_sel32) {
   constexpr int D = kHeadDim;
   constexpr float kLazy = 8.f;  // log2-domain slack before the running max is raised
   __shared__ TileLds T;
@@ -602,7 +604,9 @@ __global__ __launch_bounds__(GT / TPW * kWave) void window_prefill_kernel(
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           const float4 a = bf16x4_to_float4(*reinterpret_cast<const uint2*>(pc + 16 * n));
-          const float4 s = bf16x4_to_float4(*reinterpret_cast<const uint2*>(ps + 16 * n));
+          const float4 s = o_sel32 != nullptr
+                               ? *reinterpret_cast<const float4*>(o_sel32 + h * D + 4 * r4 + 16 * n)
+                               : bf16x4_to_float4(*reinterpret_cast<const uint2*>(ps + 16 * n));
           acc[j][n][0] = g0 * a.x + g1 * s.x + g2 * acc[j][n][0] * inv;
           acc[j][n][1] = g0 * a.y + g1 * s.y + g2 * acc[j][n][1] * inv;
           acc[j][n][2] = g0 * a.z + g1 * s.z + g2 * acc[j][n][2] * inv;
@@ -842,12 +846,13 @@ static hipError_t launch_win_g(const WindowPrefillArgs& a, hipStream_t s) {
     return launch_kernel(kKindWindow, window_prefill_kernel<G, true, kTpwOut, kGtOut>, grid,
                          prefill_block(kTpwOut, kGtOut), s, a.q,
                          a.k, vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
-                         a.out_f32, a.lse_nat, a.gates, a.o_cmp, a.o_sel);
+                         a.out_f32, a.lse_nat, a.gates, a.o_cmp, a.o_sel, a.o_sel32);
   return launch_kernel(kKindWindow, window_prefill_kernel<G, false, kTpwOut, kGtOut>, grid,
                        prefill_block(kTpwOut, kGtOut), s, a.q, a.k,
                        vt, ldv, a.cu_q, a.cu_k, a.kv_heads, a.window, a.scale_log2, a.out,
                        a.out_f32, a.lse_nat, static_cast<const float*>(nullptr),
-                       static_cast<const bf16_t*>(nullptr), static_cast<const bf16_t*>(nullptr));
+                       static_cast<const bf16_t*>(nullptr), static_cast<const bf16_t*>(nullptr),
+                       static_cast<const float*>(nullptr));
 }
 
 hipError_t launch_window_prefill(const WindowPrefillArgs& a, hipStream_t s) {

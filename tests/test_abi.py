@@ -169,10 +169,13 @@ def test_prefill_step_checks():
     for f in ("q", "k", "v", "k_c", "v_c", "gates", "cu_seqlens_q", "cu_seqlens_k",
               "cu_seqlens_c", "out"):
         setattr(p, f, 0x1000)
-    need = nsa.prefill_workspace_size(p)
+    need, least = nsa.prefill_workspace_size(p), nsa.prefill_workspace_size_min(p)
     # lse (fp32) + o_cmp and o_sel (bf16 rows) + block scores + indices
-    assert need >= 1000 * 64 * 4 + 2 * 1000 * 64 * 128 * 2 + 1000 * 4 * 16 * 4 + 1000 * 4 * 16 * 4
-    assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need - 1, None) == 3
+    assert least >= 1000 * 64 * 4 + 2 * 1000 * 64 * 128 * 2 + 1000 * 4 * 16 * 4 + 1000 * 4 * 16 * 4
+    # the key-block selected branch adds its partial states (256 B of bf16 output
+    # and 8 B of (max, sum) per (row, head, place)) and its float32 rows
+    assert need - least == 1000 * 64 * 16 * 264 + 1000 * 64 * 128 * 4
+    assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), least - 1, None) == 3
     p.topk = 65                                          # above the per-row staging limit
     assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 2
     p.topk = 16

@@ -152,8 +152,17 @@ def _check_step(name, w, d, rows_sample, out, idx, bs, min_identical):
     assert_close("prefill out", got, ref["out"][sel], atol=2e-2)
 
 
+def _step_ws(p, path):
+    """None: the binding allocates nsa_prefill_workspace_size (key-block selected
+    branch); "rows": the smallest workspace, which runs that branch row by row."""
+    if path == "blocks":
+        return None
+    return torch.empty(nsa.prefill_workspace_size_min(p), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("path", ["blocks", "rows"])
 @pytest.mark.parametrize("q_scale", [1.0, 4.0])
-def test_prefill_step_small(q_scale):
+def test_prefill_step_small(q_scale, path):
     # the three-branch recipe (64 heads over 4 KV heads, window 512, top-16) at 2048 tokens;
     # q_scale 4 sharpens the compressed softmax so the selection has few near-ties
     w = W.scaled(W.nsa_prefill(), [2048])
@@ -166,14 +175,15 @@ def test_prefill_step_small(q_scale):
     p = nsa.prefill_params(d["q"], d["k"], d["v"], d["kc"], d["vc"], d["g"], d["cu_k"], d["cu_k"],
                            d["cu_c"], L, out, topk=w.topk, window=w.window, block_scores=bs,
                            indices=idx)
-    log(f"prefill step L={L} q_scale={q_scale}")
-    nsa.nsa_prefill_step(p)
+    log(f"prefill step L={L} q_scale={q_scale} path={path}")
+    nsa.nsa_prefill_step(p, workspace=_step_ws(p, path))
     torch.cuda.synchronize()
     rows_sample = _rows_of(L, 40, None)
-    _check_step(f"prefill_small[q_scale={q_scale}]", w, d, rows_sample, out, idx, bs, 0.8)
+    _check_step(f"prefill_small[q_scale={q_scale},{path}]", w, d, rows_sample, out, idx, bs, 0.8)
 
 
-def test_prefill_step_full_size_sampled_rows():
+@pytest.mark.parametrize("path", ["blocks", "rows"])
+def test_prefill_step_full_size_sampled_rows(path):
     """The full three-branch case: one sequence of 65536 tokens, 64 query heads,
     4 KV heads; 24 sampled rows checked against the oracle."""
     w = W.nsa_prefill()
@@ -183,16 +193,17 @@ def test_prefill_step_full_size_sampled_rows():
     idx = torch.empty((L, w.kv_heads, w.topk), dtype=torch.int32, device=DEV)
     p = nsa.prefill_params(d["q"], d["k"], d["v"], d["kc"], d["vc"], d["g"], d["cu_k"], d["cu_k"],
                            d["cu_c"], L, out, topk=w.topk, window=w.window, indices=idx)
-    log(f"prefill step full size L={L} H={w.heads} H_kv={w.kv_heads}")
-    nsa.nsa_prefill_step(p)
+    log(f"prefill step full size L={L} H={w.heads} H_kv={w.kv_heads} path={path}")
+    nsa.nsa_prefill_step(p, workspace=_step_ws(p, path))
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     rows_sample = [0, 31, 32, 511, 512, 1023, 1024, 4095, 4096, 20000, 32767, 32768, 50001,
                    65472, 65534, 65535] + [int(x) for x in np.linspace(100, 65000, 8)]
-    _check_step("prefill_full", w, d, sorted(set(rows_sample)), out, idx, None, 0.8)
+    _check_step(f"prefill_full[{path}]", w, d, sorted(set(rows_sample)), out, idx, None, 0.8)
 
 
-def test_prefill_step_ragged_batch_query_tails():
+@pytest.mark.parametrize("path", ["blocks", "rows"])
+def test_prefill_step_ragged_batch_query_tails(path):
     """A ragged batch whose queries are only the last tokens of each sequence
     (chunked prefill: query t sits at key position L_k - L_q + i), including a
     sequence shorter than one window and an empty one, through the whole
@@ -220,8 +231,8 @@ def test_prefill_step_ragged_batch_query_tails():
     bs = torch.full((rows, w.kv_heads, nb_max), float("nan"), device=DEV)
     p = nsa.prefill_params(q, k, v, kc, vc, g, cu_q, cu_k, cu_c, max(lk), out, topk=w.topk,
                            window=w.window, block_scores=bs, indices=idx)
-    log(f"prefill step, query tails lq={lq} of lk={lk}")
-    nsa.nsa_prefill_step(p)
+    log(f"prefill step, query tails lq={lq} of lk={lk} path={path}")
+    nsa.nsa_prefill_step(p, workspace=_step_ws(p, path))
     torch.cuda.synchronize()
     qn, kn, vn, gn = np64(qfull), np64(k), np64(v), np64(gfull)
     outn, idxn, bsn = np64(out), idx.cpu().numpy(), np64(bs)

@@ -100,17 +100,24 @@ TRAFFIC_FILES = {  # counter summaries of the select-and-attend kernel, per deco
 ATTN_SOURCES = ["sparse_attention_compress_amd/csrc/attn.hip",
                 "sparse_attention_compress_amd/csrc/common.h",
                 "sparse_attention_compress_amd/csrc/select_core.h"]
+# counter summaries of the key-block selected attention (partial kernel), per
+# prefill workload, and the sources they were taken with
+BLOCK_TRAFFIC_FILES = {
+    "selected_prefill_b8_T16384": os.path.join(PROFILES, "block_attn_selected_prefill_b8_T16384_counters.md"),
+}
+BLOCK_SOURCES = ["sparse_attention_compress_amd/csrc/attn_blocks.hip",
+                 "sparse_attention_compress_amd/csrc/common.h"]
 
 
-def attn_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the select-and-attend kernel's sources with
-    comments and whitespace removed, so that only a change of code invalidates
-    the stored counters."""
+def attn_source_hash(sources=None) -> str:
+    """sha256 (first 16 hex digits) of a kernel's sources (by default the
+    select-and-attend kernel's) with comments and whitespace removed, so that
+    only a change of code invalidates the stored counters."""
     import hashlib
     import re
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
-    for rel in ATTN_SOURCES:
+    for rel in sources or ATTN_SOURCES:
         with open(os.path.join(root, rel), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -119,8 +126,8 @@ def attn_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(path):
-    """HBM bytes per selected-attention launch from a committed counter summary.
+def counter_traffic(path, sources=None):
+    """HBM bytes per launch of a kernel from a committed counter summary.
 
     The summary holds FETCH_SIZE and WRITE_SIZE of the kernel, each scaled by what
     the same counter reads for a plain copy of known size, and the hash of the
@@ -139,9 +146,24 @@ def counter_traffic(path):
         if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", "traffic_bytes_per_launch"):
             k_, v_ = line.split(":", 1)
             vals[k_.strip()] = v_.strip()
-    if vals.get("source_hash") != attn_source_hash() or "traffic_bytes_per_launch" not in vals:
+    if vals.get("source_hash") != attn_source_hash(sources) or "traffic_bytes_per_launch" not in vals:
         return None
     return int(float(vals["traffic_bytes_per_launch"]))
+
+
+def copy_calibration(dev):
+    """Three fp32 negations of COPY_BYTES: a plain elementwise kernel whose
+    FETCH_SIZE and WRITE_SIZE scale the counters of the library's kernels (a
+    device-to-device copy_ would be a DMA blit, not a kernel dispatch)."""
+    import torch
+    src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration: 3 fp32 negations reading and writing {COPY_BYTES} bytes each",
+          file=sys.stderr, flush=True)
 
 
 def trace_stats(path):
@@ -500,17 +522,7 @@ def main():
     }
 
     if args.calibrate_copy:
-        # a plain elementwise kernel (a device-to-device copy_ would be a DMA
-        # blit, not a kernel dispatch the counters see)
-        src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        print(f"[bench] calibration: 3 fp32 negations reading and writing {COPY_BYTES} bytes each",
-              file=sys.stderr, flush=True)
-        del src, dst
+        copy_calibration(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_layer0"] = cpu_baseline(w, layers[0], lengths, args)
     print(json.dumps(result), flush=True)
@@ -932,7 +944,9 @@ def prefill_main(args, dev):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (counter_traffic(BLOCK_TRAFFIC_FILES.get(w.name), BLOCK_SOURCES)
+                        if args.workload == "prefill-selected" and args.selected_path == "blocks"
+                        else None),
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(kern[dominant], 1),
         },
@@ -954,6 +968,8 @@ def prefill_main(args, dev):
         result["merge_read_gbs"] = round(pbytes / (kern["merge"] * 1e-6) / 1e9, 1)
     if args.selected_path == "blocks":  # no per-row gather on the key-block path
         del result["selected_gathered_gbs"]
+    if args.calibrate_copy:
+        copy_calibration(dev)
     if not args.no_cpu_baseline:
         import oracle
         scale = 1.0 / math.sqrt(D)
@@ -1065,7 +1081,9 @@ def selected_bwd_main(args, dev):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (counter_traffic(BLOCK_TRAFFIC_FILES.get(w.name), BLOCK_SOURCES)
+                        if args.workload == "prefill-selected" and args.selected_path == "blocks"
+                        else None),
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(kern[dominant], 1),
         },
@@ -1214,7 +1232,9 @@ def nsa_bwd_main(args, dev):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (counter_traffic(BLOCK_TRAFFIC_FILES.get(w.name), BLOCK_SOURCES)
+                        if args.workload == "prefill-selected" and args.selected_path == "blocks"
+                        else None),
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(part_ms[dominant] * 1e3, 1),
         },

@@ -40,6 +40,20 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) accesses of the partial states: written once, read
+// once, so they bypass L2 allocation and leave it to the reused rows.
+__device__ __forceinline__ void stream_store(bf16_t* p, uint4 x) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, x), reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void stream_store(float2* p, float2 x) {
+  __builtin_nontemporal_store(f32x2_t{x.x, x.y}, reinterpret_cast<f32x2_t*>(p));
+}
+__device__ __forceinline__ uint4 stream_load(const bf16_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
 
 constexpr int kScanRows = 1024;       // query rows one workgroup scans for its block
 constexpr int kLdsRow = kHeadDim + 8; // bf16 per staged K/V row (272 B)
@@ -268,7 +282,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     bool live;
     uint4 q[4];
   };
+  // tiles past the wave's last are clamped to the last one: the prefetch then
+  // needs no branch, so its loads land straight in the registers that use them
   auto fetch = [&](int tile, Tile& T) {
+    tile = min(tile, n_tiles - 1);
     const int li = tile * E + ent;
     T.live = li < n_list;
     const int code = sm.list[T.live ? li : n_list - 1];
@@ -343,8 +360,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
                      pack2(acc[4][e], acc[5][e]), pack2(acc[6][e], acc[7][e]));
     if (T.live && r4 == 0) {
       const int code = sm.list[tile * E + ent];
-      pml[(size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + hg] =
-          make_float2(mc, lsum);
+      stream_store(&pml[(size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + hg],
+                   make_float2(mc, lsum));
     }
     __builtin_amdgcn_wave_barrier();  // LDS runs a wave's accesses in order
 #pragma unroll
@@ -355,7 +372,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       if (li < n_list) {
         const int code = sm.list[li];
         const size_t slot = (size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + vq % G;
-        *reinterpret_cast<uint4*>(po + slot * D + 8 * c16) = x;
+        stream_store(po + slot * D + 8 * c16, x);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -368,10 +385,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     Tile A, B;
     fetch(wave, A);
     for (int tile = wave; tile < n_tiles; tile += 8) {
-      if (tile + 4 < n_tiles) fetch(tile + 4, B);
+      fetch(tile + 4, B);
       compute(pos_tag, tile, A);
       if (tile + 4 >= n_tiles) break;
-      if (tile + 8 < n_tiles) fetch(tile + 8, A);
+      fetch(tile + 8, A);
       compute(pos_tag, tile + 4, B);
     }
   };
@@ -439,7 +456,7 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
       const bool ok = p < k_sel && ((valid >> p) & 1ull);
       const size_t slot = base + size_t(p) * heads;
       ml[u] = ok ? pml[slot] : make_float2(-INFINITY, 0.f);
-      x[u] = ok ? ld16(po + slot * kHeadDim + 8 * sub) : make_uint4(0u, 0u, 0u, 0u);
+      x[u] = ok ? stream_load(po + slot * kHeadDim + 8 * sub) : make_uint4(0u, 0u, 0u, 0u);
     }
     float mb = M;
 #pragma unroll

@@ -441,43 +441,57 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
     valid |= ((__ballot(ok) >> grp) & 0xFFFFull) << (16 * u);
   }
 
-  // online merge over batches of 8 places, every load of a batch in flight
-  // together; the running maximum M only grows, the sums are rescaled with it
+  // weights: lane `sub` of the group takes places sub, sub + 16, ...: their
+  // (max, sum), the group's maximum M, its weight exp2(max - M) (0 for an
+  // invalid place) into LDS, and the normaliser L = sum of weight * sum
+  __shared__ float wsm[16][kMaxPlaces];
+  const int g = tid >> 4;
   // slot of place p: (row * k_sel + p) * heads + head
   const size_t base = size_t(row) * k_sel * heads + head;
-  float M = -INFINITY, Ls = 0.f;
+  float mj[kMaxPlaces / 16], lj[kMaxPlaces / 16];
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kMaxPlaces / 16; ++u) {
+    const int p = 16 * u + sub;
+    const bool ok = u < rounds && ((valid >> p) & 1ull);
+    const float2 ml = ok ? pml[base + size_t(p) * heads] : make_float2(-INFINITY, 0.f);
+    mj[u] = ml.x;
+    lj[u] = ml.y;
+    M = fmaxf(M, ml.x);
+  }
+#pragma unroll
+  for (int x = 8; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+  float Ls = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMaxPlaces / 16; ++u) {
+    if (u >= rounds) break;
+    const float w = mj[u] == -INFINITY ? 0.f : fast_exp2(mj[u] - M);
+    Ls += w * lj[u];
+    wsm[g][16 * u + sub] = w;
+  }
+#pragma unroll
+  for (int x = 8; x >= 1; x >>= 1) Ls += __shfl_xor(Ls, x);
+  __builtin_amdgcn_wave_barrier();  // the group's lanes are in one wave; LDS keeps its order
+
+  // the weighted sum of the partial outputs, every load of a batch in flight together
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < k_sel; p0 += kMergeBatch) {
-    float2 ml[kMergeBatch];
+    float w[kMergeBatch];
     uint4 x[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       const int p = p0 + u;
-      const bool ok = p < k_sel && ((valid >> p) & 1ull);
-      const size_t slot = base + size_t(p) * heads;
-      ml[u] = ok ? pml[slot] : make_float2(-INFINITY, 0.f);
-      x[u] = ok ? stream_load(po + slot * kHeadDim + 8 * sub) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    float mb = M;
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, ml[u].x);
-    if (mb == -INFINITY) continue;  // no valid place yet
-    if (mb > M) {
-      const float alpha = fast_exp2(M - mb);  // 0 while M is -inf (nothing summed yet)
-      Ls *= alpha;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[d] *= alpha;
-      M = mb;
+      w[u] = p < k_sel ? wsm[g][p] : 0.f;
+      x[u] = w[u] != 0.f ? stream_load(po + (base + size_t(p) * heads) * kHeadDim + 8 * sub)
+                         : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float w = ml[u].x == -INFINITY ? 0.f : fast_exp2(ml[u].x - M);
-      Ls += w * ml[u].y;
       float f[8];
       f[0] = bf16lo(x[u].x); f[1] = bf16hi(x[u].x); f[2] = bf16lo(x[u].y); f[3] = bf16hi(x[u].y);
       f[4] = bf16lo(x[u].z); f[5] = bf16hi(x[u].z); f[6] = bf16lo(x[u].w); f[7] = bf16hi(x[u].w);
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[d] += w * f[d];
+      for (int d = 0; d < 8; ++d) acc[d] += w[u] * f[d];
     }
   }
   if (!in) return;

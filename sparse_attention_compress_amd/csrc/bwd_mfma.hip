@@ -53,6 +53,15 @@ constexpr int kThreads = 256;
 constexpr int kRowPad = kHeadDim + 8;  // bf16 per staged row (272 B: 16 rows on distinct banks)
 constexpr int kTPad = 16 + 4;          // bf16 per transposed row of a query tile
 constexpr int kKTPad = 64 + 8;         // bf16 per transposed row of a key block
+
+// Column swizzles of the transposed copies.  Their stores are 2-byte writes in
+// which the lanes of a wave hold rows 8 apart (one 16-byte chunk of a row each),
+// which padding alone maps onto a few banks (4- to 8-way conflicts); XORing the
+// column with a function of the row spreads them over the banks.  The XOR is in
+// units of 4 columns, so the 8-byte reads of 4 consecutive columns stay
+// contiguous, and stays inside the row.
+__device__ __forceinline__ int qt_col(int row, int col) { return col ^ (4 * ((row >> 5) & 3)); }
+__device__ __forceinline__ int kt_col(int row, int col) { return col ^ (4 * ((row >> 3) & 15)); }
 constexpr int kMfmaRowsPerChunk = 512; // rows of a key block's list one dk/dv workgroup takes
 
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
@@ -98,10 +107,11 @@ __device__ __forceinline__ void stash_qtile(QTileLds& T, const QTileRegs& r) {
   const uint32_t dw[4] = {r.d.x, r.d.y, r.d.z, r.d.w};
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    T.qt[(8 * c + 2 * w) * kTPad + v].bits = uint16_t(qw[w]);
-    T.qt[(8 * c + 2 * w + 1) * kTPad + v].bits = uint16_t(qw[w] >> 16);
-    T.dt[(8 * c + 2 * w) * kTPad + v].bits = uint16_t(dw[w]);
-    T.dt[(8 * c + 2 * w + 1) * kTPad + v].bits = uint16_t(dw[w] >> 16);
+    const int r0 = 8 * c + 2 * w, r1 = r0 + 1;
+    T.qt[r0 * kTPad + qt_col(r0, v)].bits = uint16_t(qw[w]);
+    T.qt[r1 * kTPad + qt_col(r1, v)].bits = uint16_t(qw[w] >> 16);
+    T.dt[r0 * kTPad + qt_col(r0, v)].bits = uint16_t(dw[w]);
+    T.dt[r1 * kTPad + qt_col(r1, v)].bits = uint16_t(dw[w] >> 16);
   }
   if (tid < 16) {
     T.lse2[tid] = r.lse2;
@@ -210,8 +220,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
     const uint2 pb = pack4(p), dsb = pack4(ds);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint2 dta = *reinterpret_cast<const uint2*>(&Tc.dt[(16 * dt + c16) * kTPad + 4 * r4]);
-      const uint2 qta = *reinterpret_cast<const uint2*>(&Tc.qt[(16 * dt + c16) * kTPad + 4 * r4]);
+      const int tr = 16 * dt + c16, tc = qt_col(tr, 4 * r4);
+      const uint2 dta = *reinterpret_cast<const uint2*>(&Tc.dt[tr * kTPad + tc]);
+      const uint2 qta = *reinterpret_cast<const uint2*>(&Tc.qt[tr * kTPad + tc]);
       accv[dt] = mfma16(dta, pb, accv[dt]);
       acck[dt] = mfma16(qta, dsb, acck[dt]);
     }
@@ -327,8 +338,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
       const uint32_t w4[4] = {pk[u].x, pk[u].y, pk[u].z, pk[u].w};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        S.kt[(8 * ch + 2 * w) * kKTPad + kr].bits = uint16_t(w4[w]);
-        S.kt[(8 * ch + 2 * w + 1) * kKTPad + kr].bits = uint16_t(w4[w] >> 16);
+        const int r0 = 8 * ch + 2 * w, r1 = r0 + 1;
+        S.kt[r0 * kKTPad + kt_col(r0, kr)].bits = uint16_t(w4[w]);
+        S.kt[r1 * kKTPad + kt_col(r1, kr)].bits = uint16_t(w4[w] >> 16);
       }
     }
   };
@@ -359,7 +371,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
       const uint2 dsb = pack4(dst);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint2 kta = *reinterpret_cast<const uint2*>(&S.kt[(16 * dt + c16) * kKTPad + 16 * sl + 4 * r4]);
+        const int tr = 16 * dt + c16;
+        const uint2 kta = *reinterpret_cast<const uint2*>(&S.kt[tr * kKTPad + kt_col(tr, 16 * sl + 4 * r4)]);
         acc[dt] = mfma16(kta, dsb, acc[dt]);
       }
     }

@@ -1044,7 +1044,7 @@ def selected_bwd_main(args, dev):
         nsa.nsa_selected_attn_bwd(q, k, v, out, d_out, lse, idx, cu, cu, L_max, dq, dk, dv,
                                   workspace=ws)
     kinds = {"lists": nsa.KERNEL_SELECTED_BWD_LISTS, "dq": nsa.KERNEL_SELECTED_BWD_DQ,
-             "dkdv": nsa.KERNEL_SELECTED_BWD_DKDV}
+             "dkdv": nsa.KERNEL_SELECTED_BWD_DKDV, "dq_sum": nsa.KERNEL_SELECTED_BWD_DQ_SUM}
     ids = idx.cpu().numpy().astype(np.int64).reshape(-1, w.topk)
     pos = np.concatenate([np.arange(L) for L in w.lengths])
     t = np.repeat(pos, w.kv_heads).reshape(-1, 1)
@@ -1081,9 +1081,7 @@ def selected_bwd_main(args, dev):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": (counter_traffic(BLOCK_TRAFFIC_FILES.get(w.name), BLOCK_SOURCES)
-                        if args.workload == "prefill-selected" and args.selected_path == "blocks"
-                        else None),
+            "traffic": None,
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(kern[dominant], 1),
         },
@@ -1232,9 +1230,7 @@ def nsa_bwd_main(args, dev):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops[dominant] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": (counter_traffic(BLOCK_TRAFFIC_FILES.get(w.name), BLOCK_SOURCES)
-                        if args.workload == "prefill-selected" and args.selected_path == "blocks"
-                        else None),
+            "traffic": None,
             "algorithmic_flops_per_launch": flops[dominant],
             "mean_kernel_us": round(part_ms[dominant] * 1e3, 1),
         },

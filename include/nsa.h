@@ -126,7 +126,7 @@ int32_t nsa_set_debug_checks(int32_t on);
  * with the gated sum in nsa_prefill_step), 8 block copies from host memory
  * (nsa_decode_step_offload), 9 block-mask attention, 10 selected-attention
  * backward dq, 11 its dk and dv, 12 its delta and per-block row lists (the
- * first of those four launches).  The events are owned by the caller
+ * first of those four launches), 13 the sum of its key-block dq partial states.  The events are owned by the caller
  * and must have timing enabled; a launch made during stream capture must not
  * be armed.
  */
@@ -143,7 +143,8 @@ typedef enum nsa_kernel_kind {
   NSA_KERNEL_BLOCKMASK_ATTN = 9,
   NSA_KERNEL_SELECTED_BWD_DQ = 10,
   NSA_KERNEL_SELECTED_BWD_DKDV = 11,
-  NSA_KERNEL_SELECTED_BWD_LISTS = 12
+  NSA_KERNEL_SELECTED_BWD_LISTS = 12,
+  NSA_KERNEL_SELECTED_BWD_DQ_SUM = 13
 } nsa_kernel_kind;
 nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
 
@@ -309,12 +310,23 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
  *   rows per workgroup; a block listed by more rows has its chunk sums added
  *   with fp32 atomics.  The row lists are built with atomics too, so the
  *   summation order of dk and dv may change between calls (fp32 rounding only).
- *   workspace: nsa_selected_attn_bwd_workspace_size(...) bytes, device memory.
+ *   workspace: device memory, 16-byte aligned.  With
+ *   nsa_selected_attn_bwd_workspace_size(...) bytes dq is computed key-block
+ *   stationary, as the forward given a workspace: per (sequence, KV head,
+ *   64-key block, 1024 rows) the block's share of dq of every listing row is
+ *   written as bf16 at (row, place, head) (rows * heads * k_sel * 256 bytes of
+ *   the workspace), then the valid places of each (row, head) are summed in
+ *   fp32.  Any size from nsa_selected_attn_bwd_workspace_size_min(...) up to
+ *   that computes dq with one workgroup per (row, KV head).  Less:
+ *   NSA_ERR_WORKSPACE.
  *   Returns NSA_ERR_UNSUPPORTED for non-bf16 inputs or k_sel > 64.
  */
 size_t nsa_selected_attn_bwd_workspace_size(int32_t batch, int32_t rows_total,
                                             int32_t max_seqlen_k, int32_t heads,
                                             int32_t kv_heads, int32_t k_sel);
+size_t nsa_selected_attn_bwd_workspace_size_min(int32_t batch, int32_t rows_total,
+                                                int32_t max_seqlen_k, int32_t heads,
+                                                int32_t kv_heads, int32_t k_sel);
 nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                                  const void* d_out, const float* lse, nsa_dtype dtype,
                                  const int32_t* indices, int32_t k_sel,

@@ -95,6 +95,7 @@ _SIGS = {
                                              c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                              c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "nsa_selected_attn_bwd_workspace_size": (c_sz, [c_i32] * 6),
+    "nsa_selected_attn_bwd_workspace_size_min": (c_sz, [c_i32] * 6),
     "nsa_selected_attn_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int,
                                              c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                              c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp,
@@ -301,8 +302,15 @@ def nsa_selected_attn_fwd(q, k, v, indices, cu_seqlens_k, max_seqlen_k, out, cis
 
 
 def selected_attn_bwd_workspace_size(batch, rows, max_seqlen_k, heads, kv_heads, k_sel):
+    """Workspace bytes of the selected backward with the key-block dq."""
     return lib().nsa_selected_attn_bwd_workspace_size(int(batch), int(rows), int(max_seqlen_k),
                                                       int(heads), int(kv_heads), int(k_sel))
+
+
+def selected_attn_bwd_workspace_size_min(batch, rows, max_seqlen_k, heads, kv_heads, k_sel):
+    """Smallest workspace of the selected backward (dq one workgroup per (row, KV head))."""
+    return lib().nsa_selected_attn_bwd_workspace_size_min(int(batch), int(rows), int(max_seqlen_k),
+                                                          int(heads), int(kv_heads), int(k_sel))
 
 
 def nsa_selected_attn_bwd(q, k, v, out, d_out, lse, indices, cu_seqlens_q, cu_seqlens_k,
@@ -481,6 +489,7 @@ KERNEL_POOL, KERNEL_LOGITS, KERNEL_BLOCK_SCORES, KERNEL_SELECTED_ATTN, KERNEL_CO
 KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN, KERNEL_FETCH = 5, 6, 7, 8
 KERNEL_BLOCKMASK_ATTN = 9
 KERNEL_SELECTED_BWD_DQ, KERNEL_SELECTED_BWD_DKDV, KERNEL_SELECTED_BWD_LISTS = 10, 11, 12
+KERNEL_SELECTED_BWD_DQ_SUM = 13
 
 
 def blockmask_attn_workspace_size(batch, max_seqlen, heads):

@@ -315,6 +315,17 @@ size_t nsa_selected_attn_bwd_workspace_size(int32_t batch, int32_t rows_total,
       k_sel <= 0)
     return 0;
   const int nb_max = (max_seqlen_k + nsa::kBlock - 1) / nsa::kBlock;
+  return ((nsa::selected_bwd_ws_bytes(rows_total, heads, kv_heads, k_sel, batch, nb_max) + 255) & ~size_t(255)) +
+         nsa::block_dq_ws_bytes(rows_total, heads, k_sel);
+}
+
+size_t nsa_selected_attn_bwd_workspace_size_min(int32_t batch, int32_t rows_total,
+                                                int32_t max_seqlen_k, int32_t heads,
+                                                int32_t kv_heads, int32_t k_sel) {
+  if (batch <= 0 || rows_total <= 0 || max_seqlen_k <= 0 || heads <= 0 || kv_heads <= 0 ||
+      k_sel <= 0)
+    return 0;
+  const int nb_max = (max_seqlen_k + nsa::kBlock - 1) / nsa::kBlock;
   return nsa::selected_bwd_ws_bytes(rows_total, heads, kv_heads, k_sel, batch, nb_max);
 }
 
@@ -347,9 +358,14 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
   NSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(d_out) &&
                   aligned16(dk) && aligned16(dv),
               NSA_ERR_INVALID_ARG, "%s: q, k, v, out, d_out, dk, dv must be 16-byte aligned", fn);
-  const size_t need = nsa_selected_attn_bwd_workspace_size(batch, rows_total, max_seqlen_k, heads, kv_heads, k_sel);
+  const size_t need = nsa_selected_attn_bwd_workspace_size_min(batch, rows_total, max_seqlen_k, heads, kv_heads, k_sel);
+  const size_t full = nsa_selected_attn_bwd_workspace_size(batch, rows_total, max_seqlen_k, heads, kv_heads, k_sel);
   NSA_REQUIRE(workspace != nullptr, NSA_ERR_WORKSPACE, "%s: workspace is null", fn);
   NSA_REQUIRE(workspace_bytes >= need, NSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  NSA_REQUIRE(aligned16(workspace), NSA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  // dq key-block stationary when the workspace holds its partial states
+  const bool blocks = workspace_bytes >= full &&
+                      nsa::block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt(float(head_dim));
   nsa::SelectedBwdArgs a{};
   a.q = static_cast<const nsa::bf16_t*>(q);
@@ -375,6 +391,8 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
   a.mode = nsa::kBwdSelected;
   a.cu_kv = cu_seqlens_k;
   nsa::selected_bwd_ws_carve(workspace, a);
+  a.dq_part = blocks ? reinterpret_cast<nsa::bf16_t*>(static_cast<char*>(workspace) + ((need + 255) & ~size_t(255)))
+                     : nullptr;
   NSA_DEVICE_CHECKS(fn, stream, {
     chk.cu(cu_seqlens_k, batch, max_seqlen_k, nsa::kCheckCuK);
     chk.cu(cu_seqlens_q, batch, -1, nsa::kCheckCuQ);

@@ -104,8 +104,8 @@ struct PartialLds {
 // holding it.  Vector form (k_sel a multiple of 4 and a 16-byte aligned array,
 // so every index row is 16-byte aligned): P lanes per index row, 4 ids per lane, all of a batch's loads in
 // flight together.
-template <int P>
-__device__ __forceinline__ void scan_rows_vec(PartialLds& sm, const int* __restrict__ indices,
+template <int P, typename Lds>
+__device__ __forceinline__ void scan_rows_vec(Lds& sm, const int* __restrict__ indices,
                                               int k_sel, int kv_heads, int kv, int q0, int r_lo,
                                               int r_first, int r_hi, int blk, int wave, int lane) {
   constexpr int RPI = 64 / P;       // rows per wave instruction
@@ -141,7 +141,8 @@ __device__ __forceinline__ void scan_rows_vec(PartialLds& sm, const int* __restr
 }
 
 // Scalar form for any k_sel: one thread per index row.
-__device__ __forceinline__ void scan_rows_scalar(PartialLds& sm, const int* __restrict__ indices,
+template <typename Lds>
+__device__ __forceinline__ void scan_rows_scalar(Lds& sm, const int* __restrict__ indices,
                                                  int k_sel, int kv_heads, int kv, int q0, int r_lo,
                                                  int r_first, int r_hi, int blk, int tid, int lane) {
   for (int r0 = r_first; r0 < r_hi; r0 += 256) {
@@ -167,6 +168,78 @@ __device__ __forceinline__ void scan_rows_scalar(PartialLds& sm, const int* __re
   }
 }
 
+template <typename Lds>
+__device__ __forceinline__ void scan_rows(Lds& sm, const int* __restrict__ indices, int k_sel,
+                                          int kv_heads, int kv, int q0, int r_lo, int r_first,
+                                          int r_hi, int blk) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if ((k_sel & 3) == 0 && (reinterpret_cast<uintptr_t>(indices) & 15) == 0) {
+    const int lanes = k_sel / 4;
+    if (lanes <= 1) scan_rows_vec<1>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else if (lanes <= 2) scan_rows_vec<2>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else if (lanes <= 4) scan_rows_vec<4>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else if (lanes <= 8) scan_rows_vec<8>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+    else scan_rows_vec<16>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
+  } else {
+    scan_rows_scalar(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, tid, lane);
+  }
+}
+
+// The (sequence, KV head, row chunk, block) of a workgroup of a one-dimensional
+// grid in XCD-grouped order (the blocks of one row chunk run together on one
+// XCD and share its query rows and index rows in L2), and the chunk's rows.
+struct BlockUnit {
+  int blk, kv, b, kstart, L, q0, off, r_lo, r_hi, r_first;
+};
+__device__ __forceinline__ BlockUnit block_unit(const int* __restrict__ cu_q,
+                                                const int* __restrict__ cu_k, int kv_heads,
+                                                int nb_max, int n_chunk) {
+  BlockUnit u;
+  int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
+  u.blk = m % nb_max;
+  m /= nb_max;
+  const int chunk = m % n_chunk;
+  m /= n_chunk;
+  u.kv = m % kv_heads;
+  u.b = m / kv_heads;
+  u.kstart = cu_k[u.b];
+  u.L = cu_k[u.b + 1] - u.kstart;
+  u.q0 = cu_q[u.b];
+  const int Lq = cu_q[u.b + 1] - u.q0;
+  u.off = u.L - Lq;  // query row r of the sequence sits at position off + r
+  u.r_lo = chunk * kScanRows;
+  u.r_hi = min(Lq, u.r_lo + kScanRows);
+  u.r_first = max(u.r_lo, kBlock * u.blk - u.off);  // rows that can list the block
+  return u;
+}
+
+// Valid places of one index row for position t, as a bit mask: id >= 0, block
+// start <= t, and no earlier place holding the same id.  Lane `sub` of a group
+// of 16 lanes (the lanes of one query vector, `grp` its first lane) checks
+// places sub, sub + 16, ... and compares them with the earlier places through
+// the group; every lane of the group gets the whole mask.
+__device__ __forceinline__ unsigned long long valid_places(const int* __restrict__ ids, int k_sel,
+                                                          int t, int sub, int grp) {
+  const int rounds = (k_sel + 15) >> 4;
+  int myid[kMaxPlaces / 16];
+#pragma unroll
+  for (int u = 0; u < kMaxPlaces / 16; ++u) myid[u] = 16 * u + sub < k_sel ? ids[16 * u + sub] : -1;
+  unsigned long long valid = 0ull;
+#pragma unroll
+  for (int u = 0; u < kMaxPlaces / 16; ++u) {
+    if (u >= rounds) break;
+    bool ok = myid[u] >= 0 && myid[u] <= t / kBlock;
+#pragma unroll
+    for (int w = 0; w <= u; ++w)
+      for (int j = 0; j < 16; ++j) {
+        const int other = __shfl(myid[w], grp + j);
+        if (16 * w + j < 16 * u + sub && other == myid[u]) ok = false;
+      }
+    valid |= ((__ballot(ok) >> grp) & 0xFFFFull) << (16 * u);
+  }
+  return valid;
+}
+
 // Grid: one dimension over (sequence, KV head, row chunk, block) in XCD-grouped
 // order, so the blocks of one row chunk run together on one XCD and share its
 // query rows and index rows in L2.  Partial states go to
@@ -185,18 +258,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
 
-  int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
-  const int blk = m % nb_max;
-  m /= nb_max;
-  const int chunk = m % n_chunk;
-  m /= n_chunk;
-  const int kv = m % kv_heads;
-  const int b = m / kv_heads;
-  const int kstart = cu_k[b], L = cu_k[b + 1] - kstart;
-  const int q0 = cu_q[b], Lq = cu_q[b + 1] - q0;
-  const int off = L - Lq;  // query row r of the sequence sits at position off + r
-  const int r_lo = chunk * kScanRows, r_hi = min(Lq, r_lo + kScanRows);
-  const int r_first = max(r_lo, kBlock * blk - off);  // rows that can list the block
+  const BlockUnit U = block_unit(cu_q, cu_k, kv_heads, nb_max, n_chunk);
+  const int blk = U.blk, kv = U.kv, kstart = U.kstart, L = U.L, q0 = U.q0, off = U.off;
+  const int r_lo = U.r_lo, r_hi = U.r_hi, r_first = U.r_first;
   if (r_first >= r_hi || kBlock * blk >= L) return;  // the same for the whole workgroup
   const int heads = kv_heads * G;
 
@@ -226,16 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     }
   }
   __syncthreads();  // n_list = 0 seen by every wave
-  if ((k_sel & 3) == 0 && (reinterpret_cast<uintptr_t>(indices) & 15) == 0) {
-    const int lanes = k_sel / 4;
-    if (lanes <= 1) scan_rows_vec<1>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else if (lanes <= 2) scan_rows_vec<2>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else if (lanes <= 4) scan_rows_vec<4>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else if (lanes <= 8) scan_rows_vec<8>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else scan_rows_vec<16>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-  } else {
-    scan_rows_scalar(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, tid, lane);
-  }
+  scan_rows(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk);
   if (wave < 2) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) sm.kop[8 * wave + i][lane] = ld[i];
@@ -420,26 +475,9 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
   const int t = (row - cu_q[lo]) + ((cu_k[lo + 1] - cu_k[lo]) - (cu_q[lo + 1] - cu_q[lo]));
   const int* ids = indices + (size_t(row) * kv_heads + kv) * k_sel;
 
-  // valid places: thread `sub` holds the ids of places sub, sub + 16, ... and
-  // compares them with the earlier places through the 16 lanes of its group
   const int grp = lane & 48;
   const int rounds = (k_sel + 15) >> 4;
-  int myid[kMaxPlaces / 16];
-#pragma unroll
-  for (int u = 0; u < kMaxPlaces / 16; ++u) myid[u] = 16 * u + sub < k_sel ? ids[16 * u + sub] : -1;
-  unsigned long long valid = 0ull;
-#pragma unroll
-  for (int u = 0; u < kMaxPlaces / 16; ++u) {
-    if (u >= rounds) break;
-    bool ok = myid[u] >= 0 && myid[u] <= t / kBlock;
-#pragma unroll
-    for (int w = 0; w <= u; ++w)
-      for (int j = 0; j < 16; ++j) {
-        const int other = __shfl(myid[w], grp + j);
-        if (16 * w + j < 16 * u + sub && other == myid[u]) ok = false;
-      }
-    valid |= ((__ballot(ok) >> grp) & 0xFFFFull) << (16 * u);
-  }
+  const unsigned long long valid = valid_places(ids, k_sel, t, sub, grp);
 
   // weights: lane `sub` of the group takes places sub, sub + 16, ...: their
   // (max, sum), the group's maximum M, its weight exp2(max - M) (0 for an
@@ -506,6 +544,250 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
                    pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
   }
   if (lse != nullptr && sub == 0) lse[qv] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+// ------------------------------------------------ gradient dq, key-block stationary
+//
+// The dq of the selected attention (the exact gradient of the forward without
+// CIS, for a given upstream gradient dO; the forward's natural-log normaliser
+// lse and delta = dO . O given): per (row, head) over the row's keys J,
+// p = exp(scale q.k - lse), ds = p (dO.v - delta), dq = scale sum_J ds k.  As
+// in the forward, one workgroup per (sequence, KV head, 1024-row chunk, 64-key
+// block) walks the rows that list the block in tiles of 16 query vectors;
+// per tile S^T = K Q^T and dP^T = V dO^T (16 MFMAs each), then
+// dq^T += K^T dS^T (16 MFMAs, dS^T packed straight into the B operand), and the
+// block's share of dq (without the scale) goes out as bf16 at (row, place,
+// head).  block_dq_sum_kernel adds the valid places of every (row, head).
+
+struct DqLds {
+  uint4 kop[16][64];   // A of S^T = K Q^T (as PartialLds::kop)
+  uint4 vop[16][64];   // A of dP^T = V dO^T: V rows in the layout of kop
+  uint4 ktop[16][64];  // A of dq^T += K^T dS^T: K transposed in the layout of PartialLds::vop
+  bf16_t stage[4][16 * kLdsRow];
+  uint16_t list[kScanRows];
+  int n_list;
+};
+
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void block_dq_partial_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int* __restrict__ indices, int k_sel,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads, int nb_max,
+    int n_chunk, float scale_log2, bf16_t* __restrict__ pq) {
+  constexpr int E = 16 / G;
+  constexpr int D = kHeadDim;
+  __shared__ DqLds sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const BlockUnit U = block_unit(cu_q, cu_k, kv_heads, nb_max, n_chunk);
+  const int blk = U.blk, kv = U.kv, kstart = U.kstart, L = U.L, q0 = U.q0, off = U.off;
+  const int r_lo = U.r_lo, r_hi = U.r_hi, r_first = U.r_first;
+  if (r_first >= r_hi || kBlock * blk >= L) return;  // the same for the whole workgroup
+  const int heads = kv_heads * G;
+
+  // operands straight from K and V (rows past the sequence end repeat its last
+  // row; masked), requested before the index scan: wave w loads K and V slice w
+  // (kop, vop) and the eight K rows of half w / 2 for K^T outputs tiles
+  // 4 (w % 2) .. +3 (ktop)
+  if (tid == 0) sm.n_list = 0;
+  const size_t rs = size_t(kv_heads) * D;
+  const bf16_t* kb = k + size_t(kstart) * rs + size_t(kv) * D;
+  const bf16_t* vb = v + size_t(kstart) * rs + size_t(kv) * D;
+  uint4 lk[4], lv[4], lt[8];
+  {
+    const size_t kr = size_t(min(kBlock * blk + 16 * wave + c16, L - 1)) * rs;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      lk[kk] = ld16(kb + kr + 32 * kk + 8 * r4);
+      lv[kk] = ld16(vb + kr + 32 * kk + 8 * r4);
+    }
+    const int h = wave >> 1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int key = 32 * h + 16 * (u >> 2) + 4 * r4 + (u & 3);
+      lt[u] = ld16(kb + size_t(min(kBlock * blk + key, L - 1)) * rs + 8 * c16);
+    }
+  }
+  __syncthreads();  // n_list = 0 seen by every wave
+  scan_rows(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    sm.kop[4 * wave + kk][lane] = lk[kk];
+    sm.vop[4 * wave + kk][lane] = lv[kk];
+  }
+  {
+    const int h = wave >> 1, n0 = 4 * (wave & 1);
+#pragma unroll
+    for (int n = n0; n < n0 + 4; ++n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t a = (&lt[2 * x].x)[n >> 1], c = (&lt[2 * x + 1].x)[n >> 1];
+        w[x] = (n & 1) ? (a >> 16) | (c & 0xFFFF0000u) : (a & 0xFFFFu) | (c << 16);
+      }
+      sm.ktop[8 * h + n][lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  __syncthreads();
+  const int n_list = sm.n_list;
+  const int n_tiles = (n_list + E - 1) / E;
+  if (wave >= n_tiles) return;  // no barrier below
+
+  const int ent = c16 / G, hg = c16 % G;
+  const int key0 = kBlock * blk + 4 * r4;
+  const int last_key = kBlock * blk + kBlock - 1;
+  bf16_t* stg = sm.stage[wave];
+  struct Tile {
+    int t;
+    float lse2, dlt;
+    uint4 q[4], d[4];
+  };
+  // tiles past the wave's last are clamped to the last one (no branch around the
+  // prefetch); a slot past the list repeats the last entry and stores nothing
+  auto fetch = [&](int tile, Tile& T) {
+    tile = min(tile, n_tiles - 1);
+    const int li = tile * E + ent;
+    const int code = sm.list[li < n_list ? li : n_list - 1];
+    T.t = off + r_lo + (code >> 6);
+    const size_t hr = size_t(q0 + r_lo + (code >> 6)) * heads + kv * G + hg;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      T.q[kk] = ld16(q + hr * D + 32 * kk + 8 * r4);
+      T.d[kk] = ld16(dout + hr * D + 32 * kk + 8 * r4);
+    }
+    T.lse2 = lse[hr] * kLog2e;
+    T.dlt = delta[hr];
+  };
+  auto compute = [&](int tile, const Tile& T) {
+    f32x4_t sacc[4], dpacc[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      dpacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        sacc[s] = mfma32(sm.kop[4 * s + kk][lane], T.q[kk], sacc[s]);
+        dpacc[s] = mfma32(sm.vop[4 * s + kk][lane], T.d[kk], dpacc[s]);
+      }
+    }
+    const bool masked = __any(T.t < last_key);  // the row's own block: keys past t
+    float ds[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = fast_exp2(fmaf(sacc[s][e], scale_log2, -T.lse2));
+        ds[s][e] = p * (dpacc[s][e] - T.dlt);
+      }
+    if (masked) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key0 + 16 * s + e > T.t) ds[s][e] = 0.f;
+    }
+    f32x4_t acc[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 db = make_uint4(pack2(ds[2 * h][0], ds[2 * h][1]), pack2(ds[2 * h][2], ds[2 * h][3]),
+                                  pack2(ds[2 * h + 1][0], ds[2 * h + 1][1]),
+                                  pack2(ds[2 * h + 1][2], ds[2 * h + 1][3]));
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[n] = mfma32(sm.ktop[8 * h + n][lane], db, acc[n]);
+    }
+    // dq^T rows -> this wave's stage, then 16 contiguous bytes per lane out
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<uint4*>(&stg[c16 * kLdsRow + 32 * r4 + 8 * e]) =
+          make_uint4(pack2(acc[0][e], acc[1][e]), pack2(acc[2][e], acc[3][e]),
+                     pack2(acc[4][e], acc[5][e]), pack2(acc[6][e], acc[7][e]));
+    __builtin_amdgcn_wave_barrier();  // LDS runs a wave's accesses in order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vq = 4 * i + r4;
+      const int li = tile * E + vq / G;
+      const uint4 x = *reinterpret_cast<const uint4*>(&stg[vq * kLdsRow + 8 * c16]);
+      if (li < n_list) {
+        const int code = sm.list[li];
+        const size_t slot = (size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + vq % G;
+        stream_store(pq + slot * D + 8 * c16, x);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  Tile A, B;
+  fetch(wave, A);
+  for (int tile = wave; tile < n_tiles; tile += 8) {
+    fetch(tile + 4, B);
+    compute(tile, A);
+    if (tile + 4 >= n_tiles) break;
+    fetch(tile + 8, A);
+    compute(tile + 4, B);
+  }
+}
+
+// dq[row, head] (+)= scale * (sum of the partial dq of the row's valid places);
+// 16 threads per query vector (row * heads + head), 8 dims each.
+__global__ __launch_bounds__(256) void block_dq_sum_kernel(
+    const bf16_t* __restrict__ pq, const int* __restrict__ indices, int k_sel,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int heads,
+    int kv_heads, long n_qv, float scale, int accumulate, float* __restrict__ dq) {
+  const int tid = threadIdx.x, sub = tid & 15, lane = tid & 63;
+  const long qv = long(blockIdx.x) * 16 + (tid >> 4);
+  const bool in = qv < n_qv;
+  const long qc = in ? qv : n_qv - 1;
+  const int row = int(qc / heads), head = int(qc % heads);
+  const int kv = head / (heads / kv_heads);
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int t = (row - cu_q[lo]) + ((cu_k[lo + 1] - cu_k[lo]) - (cu_q[lo + 1] - cu_q[lo]));
+  const int* ids = indices + (size_t(row) * kv_heads + kv) * k_sel;
+  const unsigned long long valid = valid_places(ids, k_sel, t, sub, lane & 48);
+  const size_t base = size_t(row) * k_sel * heads + head;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < k_sel; p0 += kMergeBatch) {
+    uint4 x[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int p = p0 + u;
+      const bool ok = p < k_sel && ((valid >> p) & 1ull);
+      x[u] = ok ? stream_load(pq + (base + size_t(p) * heads) * kHeadDim + 8 * sub)
+                : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      acc[0] += bf16lo(x[u].x); acc[1] += bf16hi(x[u].x);
+      acc[2] += bf16lo(x[u].y); acc[3] += bf16hi(x[u].y);
+      acc[4] += bf16lo(x[u].z); acc[5] += bf16hi(x[u].z);
+      acc[6] += bf16lo(x[u].w); acc[7] += bf16hi(x[u].w);
+    }
+  }
+  if (!in) return;
+  float* dst = dq + size_t(qv) * kHeadDim + 8 * sub;
+  float4 a = make_float4(scale * acc[0], scale * acc[1], scale * acc[2], scale * acc[3]);
+  float4 b = make_float4(scale * acc[4], scale * acc[5], scale * acc[6], scale * acc[7]);
+  if (accumulate & 1) {
+    const float4 a0 = *reinterpret_cast<const float4*>(dst);
+    const float4 b0 = *reinterpret_cast<const float4*>(dst + 4);
+    a = make_float4(a.x + a0.x, a.y + a0.y, a.z + a0.z, a.w + a0.w);
+    b = make_float4(b.x + b0.x, b.y + b0.y, b.z + b0.z, b.w + b0.w);
+  }
+  *reinterpret_cast<float4*>(dst) = a;
+  *reinterpret_cast<float4*>(dst + 4) = b;
+}
+
+template <int G>
+hipError_t launch_dq_g(const SelectedBwdArgs& a, int n_chunk, unsigned n_wg, hipStream_t s) {
+  return launch_kernel(kKindBwdQ, block_dq_partial_kernel<G>, dim3(n_wg), dim3(256), s, a.q, a.k,
+                       a.v, a.dout, a.lse, static_cast<const float*>(a.delta), a.indices, a.k_sel,
+                       a.cu_q, a.cu_k, a.kv_heads, a.nb_max, n_chunk, a.scale * kLog2eHost,
+                       a.dq_part);
 }
 
 template <int G, bool CIS>
@@ -577,6 +859,36 @@ hipError_t launch_block_attn(const void* q, const void* k, const void* v, const 
                        dim3(256), s, static_cast<const bf16_t*>(po),
                        static_cast<const float2*>(pml), indices, k_sel, cu_q, cu_k, batch, heads,
                        kv_heads, n_qv, static_cast<bf16_t*>(out), out_f32, lse);
+}
+
+size_t block_dq_ws_bytes(int rows_total, int heads, int k_sel) {
+  if (rows_total <= 0 || heads <= 0 || k_sel <= 0) return 0;
+  return po_bytes(rows_total, heads, k_sel);
+}
+
+hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s) {
+  if (a.rows_total == 0 || a.batch == 0 || a.max_seqlen_k == 0) return hipSuccess;
+  if (a.k_sel > kMaxPlaces ||
+      !block_attn_grid_fits(a.batch, a.rows_total, a.heads, a.kv_heads, a.max_seqlen_k))
+    return hipErrorInvalidValue;
+  const int G = a.heads / a.kv_heads;
+  const int n_chunk = (a.max_seqlen_k + kScanRows - 1) / kScanRows;
+  const unsigned n_wg = unsigned(a.batch) * a.kv_heads * n_chunk * a.nb_max;
+  hipError_t e;
+  switch (G) {
+    case 1: e = launch_dq_g<1>(a, n_chunk, n_wg, s); break;
+    case 2: e = launch_dq_g<2>(a, n_chunk, n_wg, s); break;
+    case 4: e = launch_dq_g<4>(a, n_chunk, n_wg, s); break;
+    case 8: e = launch_dq_g<8>(a, n_chunk, n_wg, s); break;
+    case 16: e = launch_dq_g<16>(a, n_chunk, n_wg, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const long n_qv = long(a.rows_total) * a.heads;
+  return launch_kernel(kKindBwdQMerge, block_dq_sum_kernel, dim3(unsigned((n_qv + 15) / 16)),
+                       dim3(256), s, static_cast<const bf16_t*>(a.dq_part), a.indices, a.k_sel,
+                       a.cu_q, a.cu_k, a.batch, a.heads, a.kv_heads, n_qv, a.scale, a.accumulate,
+                       a.dq);
 }
 
 }  // namespace nsa

@@ -524,6 +524,7 @@ hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
                                a.window, a.accumulate, a.heads, a.kv_heads, a.nb_max, scale_log2,
                                a.scale, a.dk, a.dv);
   if (e != hipSuccess) return e;
+  if (MODE == kBwdSelected && a.dq_part != nullptr) return launch_block_dq(a, s);
   if (MODE == kBwdSelected)
     return launch_kernel(kKindBwdQ, bwd_dq_sel_mfma_kernel<G>,
                          dim3(unsigned(a.rows_total) * a.kv_heads), dim3(kThreads), s, a.q, a.k,

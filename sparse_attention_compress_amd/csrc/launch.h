@@ -52,7 +52,8 @@ enum KernelKind {
   kKindBwdQ = 10,     // selected-attention backward: dq
   kKindBwdKV = 11,    // selected-attention backward: dk and dv
   kKindBwdLists = 12, // selected-attention backward: delta and the per-block row lists
-  kKindCount = 13
+  kKindBwdQMerge = 13, // selected-attention backward, key-block dq: the sum of its partial states
+  kKindCount = 14
 };
 
 // One armed (start, stop) event pair per kernel kind, per host thread.
@@ -259,11 +260,17 @@ struct SelectedBwdArgs {
   int* off;            // list offsets
   int* cursor;         // fill cursors
   int2* list;          // [rows * kv_heads * k_sel] (row, position), grouped by block
+  bf16_t* dq_part;     // nullable: the key-block dq's partial states (block_dq_ws_bytes);
+                       // without it dq runs one workgroup per (row, KV head)
 };
 size_t selected_bwd_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel, int batch,
                              int nb_max);
 void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a);
 hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s);
+// Selected-attention dq, key-block stationary (attn_blocks.hip): partial dq per
+// (row, place, head) in a.dq_part, then their sum into a.dq.
+size_t block_dq_ws_bytes(int rows_total, int heads, int k_sel);
+hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s);
 // The matrix-core kernels: dk/dv of every key set, dq of the window and
 // compressed key sets (bwd_mfma.hip).
 hipError_t launch_bwd_mfma(const SelectedBwdArgs& a, hipStream_t s);

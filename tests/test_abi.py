@@ -257,9 +257,13 @@ def test_selected_bwd_checks():
     before any launch (fake device addresses are never dereferenced)."""
     f = nsa.lib().nsa_selected_attn_bwd
     P = 0x1000
-    need = nsa.selected_attn_bwd_workspace_size(2, 100, 4096, 16, 2, 16)
-    assert need > 0
+    full = nsa.selected_attn_bwd_workspace_size(2, 100, 4096, 16, 2, 16)
+    need = nsa.selected_attn_bwd_workspace_size_min(2, 100, 4096, 16, 2, 16)
+    assert 0 < need < full
+    # the key-block dq adds its partial states: 256 B of bf16 per (row, head, place)
+    assert full - ((need + 255) // 256 * 256) == 100 * 16 * 16 * 256
     assert nsa.selected_attn_bwd_workspace_size(0, 100, 4096, 16, 2, 16) == 0
+    assert nsa.selected_attn_bwd_workspace_size_min(0, 100, 4096, 16, 2, 16) == 0
 
     def call(dtype=nsa.NSA_BF16, k_sel=16, cu_q=P, heads=16, kv=2, hd=128, block=64, ws=P,
              nbytes=None, dk=P):
@@ -272,10 +276,11 @@ def test_selected_bwd_checks():
     assert call(heads=12, kv=5) == 2             # group size
     assert call(hd=64) == 2
     assert call(block=32) == 2
-    assert call(nbytes=need - 1) == 3            # workspace too small
+    assert call(nbytes=need - 1) == 3            # workspace below the smallest size
     assert call(ws=None) == 3
     assert call(dk=P + 4) == 1                   # gradients must be 16-byte aligned
     assert call(dk=None) == 1
+    assert call(ws=P + 8) == 1                   # workspace must be 16-byte aligned
 
 
 def test_window_count_export():

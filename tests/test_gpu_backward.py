@@ -49,7 +49,10 @@ def _inputs(w, q_lengths=None):
                 max_len=max(w.lengths), q_lengths=list(q_lengths))
 
 
-def _run(d):
+def _run(d, path="blocks"):
+    """Forward, then the backward with dq key-block stationary ("blocks": the
+    binding allocates the full queried workspace) or one workgroup per (row, KV
+    head) ("rows": the smallest workspace)."""
     rows, H, D = d["q"].shape
     out = torch.empty_like(d["q"])
     lse = torch.empty((rows, H), dtype=F32, device=DEV)
@@ -58,8 +61,14 @@ def _run(d):
     dq = torch.full((rows, H, D), float("nan"), dtype=F32, device=DEV)
     dk = torch.full(d["k"].shape, float("nan"), dtype=F32, device=DEV)
     dv = torch.full(d["v"].shape, float("nan"), dtype=F32, device=DEV)
+    ws = None
+    if path == "rows":
+        n = len(d["q_lengths"])
+        ws = torch.empty(nsa.selected_attn_bwd_workspace_size_min(n, rows, d["max_len"], H,
+                                                                  d["k"].shape[1], d["idx"].shape[2]),
+                         dtype=torch.uint8, device=DEV)
     nsa.nsa_selected_attn_bwd(d["q"], d["k"], d["v"], out, d["d_out"], lse, d["idx"], d["cu_q"],
-                              d["cu_k"], d["max_len"], dq, dk, dv)
+                              d["cu_k"], d["max_len"], dq, dk, dv, workspace=ws)
     torch.cuda.synchronize()
     return out, lse, dq, dk, dv
 
@@ -85,36 +94,39 @@ def _compare(d, dq, dk, dv, tag):
 @pytest.mark.parametrize("H,H_kv,lengths", [(16, 2, [500, 900]), (16, 1, [300, 420]),
                                             (4, 4, [700, 90]), (8, 4, [500, 900]),
                                             (8, 2, [300, 420])])
-def test_selected_bwd_matches_oracle(H, H_kv, lengths):
+@pytest.mark.parametrize("path", ["blocks", "rows"])
+def test_selected_bwd_matches_oracle(H, H_kv, lengths, path):
     """Every row of a ragged batch (several 64-token blocks and a ragged tail;
     rows early in a sequence list fewer than k blocks), GQA groups of 8, 16, 1,
     2 and 4 query heads (the last two: chunks of 2*G*16 rows that are not a
     multiple of 256, and head counts below one 8-head pass)."""
     w = dataclasses.replace(W.scaled(W.selected_prefill(), lengths), heads=H, kv_heads=H_kv)
     d = _inputs(w)
-    log(f"selected bwd H={H} H_kv={H_kv} lengths={lengths}")
-    _, _, dq, dk, dv = _run(d)
-    _compare(d, dq, dk, dv, f"bwd_g{H // H_kv}")
+    log(f"selected bwd H={H} H_kv={H_kv} lengths={lengths} dq path={path}")
+    _, _, dq, dk, dv = _run(d, path)
+    _compare(d, dq, dk, dv, f"bwd_g{H // H_kv}_{path}")
 
 
-def test_selected_bwd_query_tails_and_empty_sequence():
+@pytest.mark.parametrize("path", ["blocks", "rows"])
+def test_selected_bwd_query_tails_and_empty_sequence(path):
     """Query rows that are only the last positions of their sequences (t offset
     by L - Lq), and a sequence with keys but no query rows: its dk and dv are 0."""
     w = W.scaled(W.selected_prefill(), [600, 200, 333])
     d = _inputs(w, q_lengths=[100, 0, 333])
     log("selected bwd query tails and a sequence without query rows")
-    _, _, dq, dk, dv = _run(d)
-    _compare(d, dq, dk, dv, "bwd_tails")
+    _, _, dq, dk, dv = _run(d, path)
+    _compare(d, dq, dk, dv, f"bwd_tails_{path}")
     assert torch.count_nonzero(dk[600:800]) == 0 and torch.count_nonzero(dv[600:800]) == 0
 
 
-def test_selected_bwd_full_size_samples_and_identities():
+@pytest.mark.parametrize("path", ["blocks", "rows"])
+def test_selected_bwd_full_size_samples_and_identities(path):
     """The 8 x 16384-token selected-prefill recipe: sampled dq rows against the
     oracle, and the two key-sum identities over every key."""
     w = W.selected_prefill()
     d = _inputs(w)
     log("selected bwd full size 8 x 16384")
-    out, lse, dq, dk, dv = _run(d)
+    out, lse, dq, dk, dv = _run(d, path)
     scale = 1.0 / np.sqrt(128.0)
     rows = d["q"].shape[0]
     H, H_kv, G = w.heads, w.kv_heads, w.group

@@ -284,7 +284,7 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
   }
   if (blocks) {
     NSA_REQUIRE(aligned16(workspace), NSA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
-    NSA_REQUIRE(nsa::block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k), NSA_ERR_UNSUPPORTED,
+    NSA_REQUIRE(nsa::block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k, k_sel), NSA_ERR_UNSUPPORTED,
                 "%s: shape too large for the key-block path", fn);
   }
   const nsa::AttnWs ws = nsa::attn_ws_carve(workspace, rows_total, kv_heads, heads / kv_heads, k_sel, decode);
@@ -365,7 +365,7 @@ nsa_status nsa_selected_attn_bwd(const void* q, const void* k, const void* v, co
   NSA_REQUIRE(aligned16(workspace), NSA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
   // dq key-block stationary when the workspace holds its partial states
   const bool blocks = workspace_bytes >= full &&
-                      nsa::block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k);
+                      nsa::block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k, k_sel);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt(float(head_dim));
   nsa::SelectedBwdArgs a{};
   a.q = static_cast<const nsa::bf16_t*>(q);
@@ -1072,7 +1072,7 @@ nsa_status nsa_prefill_step(const nsa_prefill_params* p, void* workspace, size_t
   NSA_REQUIRE(aligned16(workspace), NSA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
   // the key-block selected branch when the workspace holds its partial states
   const bool blocks = workspace_bytes >= lay.total &&
-                      nsa::block_attn_grid_fits(p->batch, p->rows_total, p->heads, p->kv_heads, p->max_seqlen_k);
+                      nsa::block_attn_grid_fits(p->batch, p->rows_total, p->heads, p->kv_heads, p->max_seqlen_k, p->topk);
   char* base = static_cast<char*>(workspace);
   nsa::bf16_t* o_cmp = reinterpret_cast<nsa::bf16_t*>(base + lay.o_cmp);
   nsa::bf16_t* o_sel = reinterpret_cast<nsa::bf16_t*>(base + lay.o_sel);

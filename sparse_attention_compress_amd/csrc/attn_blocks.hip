@@ -29,7 +29,6 @@
 // partial output is rounded to bf16 once more (2^-9 relative) before the
 // merge.
 #include <climits>
-#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -40,7 +39,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Streaming (non-temporal) accesses of the partial states: written once, read
@@ -48,9 +47,7 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void stream_store(bf16_t* p, uint4 x) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, x), reinterpret_cast<u32x4_t*>(p));
 }
-__device__ __forceinline__ void stream_store(float2* p, float2 x) {
-  __builtin_nontemporal_store(f32x2_t{x.x, x.y}, reinterpret_cast<f32x2_t*>(p));
-}
+__device__ __forceinline__ void stream_store(float* p, float x) { __builtin_nontemporal_store(x, p); }
 __device__ __forceinline__ uint4 stream_load(const bf16_t* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
@@ -70,33 +67,44 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, x);
 }
 
-// max / sum over the four lanes c16, c16 + 16, c16 + 32, c16 + 48 (one column of
-// an MFMA accumulator)
-__device__ __forceinline__ float column_max(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+__device__ __forceinline__ f32x16_t mfma32x32(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ float column_sum(float x) {
+
+// max / sum over lanes l and l ^ 32 (one column of a 32x32 accumulator)
+__device__ __forceinline__ float pair_max(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 // The block's matrix-core operands are the same for the four waves, so they are
 // built once per workgroup and kept in LDS in lane order (lane-contiguous 16-byte
-// reads, free of bank conflicts): kop[s * 4 + kk][lane] is the A operand of
-// S^T = K Q^T for key slice s and dims 32 kk .. (key 16 s + c16, dims
-// 32 kk + 8 r4 .. +8), vop[h * 8 + n][lane] the A operand of O^T += V^T P^T for
-// output tile n and key half h (row c16 = dim 8 c16 + n; k index 8 r4 + u = key
-// 32 h + 16 (u / 4) + 4 r4 + u % 4).
+// reads, free of bank conflicts), for 32x32x16 bf16 tiles: operand lane l holds
+// row (column) l % 32 at k indices 8 (l / 32) .. +7, and accumulator j of lane l
+// is row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.  The k index of a product
+// is summed over, so any fixed assignment of dims (keys) to it serves, as long as
+// both operands use the same one:
+//   kop[x][s][lane]: A of S^T = K Q^T for keys 32 x .. +31, step s: key
+//     32 x + lane % 32, dims 64 (lane / 32) + 8 s .. +7 (the q operand of lane l
+//     holds the same dims of its query vector);
+//   vop[n][m][lane]: A of O^T += V^T P^T for output tile n, key step m: row
+//     rho = lane % 32 is dim 32 n + f(rho), f(8 a + 4 g + b) = 16 (a / 2) + 8 g +
+//     4 (a % 2) + b, and k index u of lane half g = lane / 32 is key
+//     16 m + 8 (u / 4) + 4 g + u % 4.
+// A lane's score accumulators j = 8 (m % 2) .. +7 of key half m / 2 are then
+// exactly its k indices of P^T for key step m, and its output accumulators
+// j = 8 i .. 8 i + 7 of tile n are the eight consecutive dims
+// 32 n + 16 i + 8 (lane / 32) .. +7.
 struct PartialLds {
-  uint4 kop[16][64];
-  uint4 vop[16][64];
-  bf16_t stage[4][16 * kLdsRow];  // per wave: one tile's 16 output rows, for the stores
-  uint16_t list[kScanRows];       // (row in chunk << 6) | place
+  uint4 kop[2][8][64];
+  uint4 vop[4][4][64];
+  float cisw[kBlock];        // CIS of the block's keys (CIS mode)
+  uint16_t list[kScanRows];  // (row in chunk << 6) | place
   int n_list;
 };
 
@@ -242,21 +250,25 @@ __device__ __forceinline__ unsigned long long valid_places(const int* __restrict
 
 // Grid: one dimension over (sequence, KV head, row chunk, block) in XCD-grouped
 // order, so the blocks of one row chunk run together on one XCD and share its
-// query rows and index rows in L2.  Partial states go to
-// po[((row * k_sel + place) * heads + head) * 128 ..] (bf16) and
-// pml[(row * k_sel + place) * heads + head] = (max, sum) in the log2 domain: the
-// G heads of one (row, place) are contiguous.
+// query rows and index rows in L2.
+//
+// Partial states: pml[(row * k_sel + place) * heads + head] = (max, sum) in the
+// log2 domain; the unnormalised bf16 outputs of the G heads of one (row, place,
+// KV head) share the region of G * 128 values at
+// po[((row * k_sel + place) * heads + kv * G) * 128 ..], in which dims
+// 8 p .. 8 p + 7 of head hg sit at (p / 2) * 16 G + 16 hg + 8 (p % 2): one store
+// instruction of a tile then writes 32 G contiguous bytes per list entry.
 template <int G, bool CIS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void block_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads, int nb_max,
     int n_chunk, float scale_log2, bf16_t* __restrict__ po, float2* __restrict__ pml) {
-  constexpr int E = 16 / G;  // rows per tile
+  constexpr int E = 32 / G;  // list entries per tile of 32 query vectors
   constexpr int D = kHeadDim;
   __shared__ PartialLds sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c16 = lane & 15, r4 = lane >> 4;
+  const int c32 = lane & 31, g = lane >> 5;
 
   const BlockUnit U = block_unit(cu_q, cu_k, kv_heads, nb_max, n_chunk);
   const int blk = U.blk, kv = U.kv, kstart = U.kstart, L = U.L, q0 = U.q0, off = U.off;
@@ -267,9 +279,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   // The block's operands straight from K and V (rows past the sequence end
   // repeat its last row: finite data, masked below since they lie past every
   // row's position), requested before the index scan so both are in flight
-  // together.  Waves 0 and 1 build the K operands of slices 2w, 2w + 1; waves 2
-  // and 3 the V operands of half w - 2 (eight V rows' 16-byte pieces per lane,
-  // transposed in registers).
+  // together.  Waves 0 and 1 load K (16-byte piece x = 128 i + tid is key x / 16,
+  // dims 8 (x % 16) ..); waves 2 and 3 load V, thread t = tid - 128 taking dims
+  // 8 (t % 16) .. +7 of the eight keys of step t / 32, lane half (t / 16) % 2, and
+  // transposing them in registers.
   if (tid == 0) sm.n_list = 0;
   uint4 ld[8];
   const size_t rs = size_t(kv_heads) * D;
@@ -278,33 +291,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   if (wave < 2) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int s = 2 * wave + (i >> 2), kk = i & 3;
-      ld[i] = ld16(kb + size_t(min(kBlock * blk + 16 * s + c16, L - 1)) * rs + 32 * kk + 8 * r4);
+      const int x = 128 * i + tid;
+      ld[i] = ld16(kb + size_t(min(kBlock * blk + (x >> 4), L - 1)) * rs + 8 * (x & 15));
     }
   } else {
-    const int h = wave - 2;
+    const int t = tid - 128, m = t >> 5, gh = (t >> 4) & 1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int key = 32 * h + 16 * (u >> 2) + 4 * r4 + (u & 3);
-      ld[u] = ld16(vb + size_t(min(kBlock * blk + key, L - 1)) * rs + 8 * c16);
+      const int key = 16 * m + 8 * (u >> 2) + 4 * gh + (u & 3);
+      ld[u] = ld16(vb + size_t(min(kBlock * blk + key, L - 1)) * rs + 8 * (t & 15));
     }
   }
+  if (CIS && tid < kBlock) sm.cisw[tid] = cis[size_t(kstart + min(kBlock * blk + tid, L - 1)) * kv_heads + kv];
   __syncthreads();  // n_list = 0 seen by every wave
   scan_rows(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk);
   if (wave < 2) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm.kop[8 * wave + i][lane] = ld[i];
+    for (int i = 0; i < 8; ++i) {
+      const int x = 128 * i + tid, key = x >> 4, pc = x & 15;
+      sm.kop[key >> 5][pc & 7][(key & 31) + 32 * (pc >> 3)] = ld[i];
+    }
   } else {
-    const int h = wave - 2;
+    // dims 8 (t % 16) + c = 32 n + 16 i + 8 gp + c are rows 8 (2 i + c / 4) + 4 gp + c % 4 of tile n
+    const int t = tid - 128, m = t >> 5, gh = (t >> 4) & 1, db = t & 15;
+    const int n = db >> 2, i = (db >> 1) & 1, gp = db & 1;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int c = 0; c < 8; ++c) {
       uint32_t w[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const uint32_t a = (&ld[2 * x].x)[n >> 1], c = (&ld[2 * x + 1].x)[n >> 1];
-        w[x] = (n & 1) ? (a >> 16) | (c & 0xFFFF0000u) : (a & 0xFFFFu) | (c << 16);
+        const uint32_t a = (&ld[2 * x].x)[c >> 1], b = (&ld[2 * x + 1].x)[c >> 1];
+        w[x] = (c & 1) ? (a >> 16) | (b & 0xFFFF0000u) : (a & 0xFFFFu) | (b << 16);
       }
-      sm.vop[8 * h + n][lane] = make_uint4(w[0], w[1], w[2], w[3]);
+      const int rho = 8 * (2 * i + (c >> 2)) + 4 * gp + (c & 3);
+      sm.vop[n][m][rho + 32 * gh] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
   __syncthreads();
@@ -312,143 +332,117 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const int n_tiles = (n_list + E - 1) / E;
   if (wave >= n_tiles) return;  // no barrier below
 
-  float cw[4][4];  // CIS of key 16 s + 4 r4 + e
-  if constexpr (CIS) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        cw[s][e] = cis[size_t(kstart + min(kBlock * blk + 16 * s + 4 * r4 + e, L - 1)) * kv_heads + kv];
-  }
-
-  const int ent = c16 / G, hg = c16 % G;
-  const int key0 = kBlock * blk + 4 * r4;
+  const int ent = c32 / G, hg = c32 % G;
+  const int key0 = kBlock * blk + 4 * g;  // key of score j of half x: key0 + 32 x + 8 (j / 4) + j % 4
   const int last_key = kBlock * blk + kBlock - 1;
-  // the log2-domain scale is applied inside one fma per score: p = exp2(c s - c m)
-  // with m the raw maximum (the minimum for a negative scale)
+  // the log2-domain scale (positive) is applied inside one fma per score:
+  // p = exp2(c s - c m) with m the raw maximum
   const float c = scale_log2;
-  bf16_t* stg = sm.stage[wave];
+  // chunk bases (uniform) and per-lane byte offsets below them, which fit 32 bits
+  // for every shape the host admits
+  const char* qbase = reinterpret_cast<const char*>(q + size_t(q0 + r_lo) * heads * D);
+  char* pbase = reinterpret_cast<char*>(po + size_t(q0 + r_lo) * k_sel * heads * D);
+  char* mbase = reinterpret_cast<char*>(pml + size_t(q0 + r_lo) * k_sel * heads);
+  const uint32_t q_lane = uint32_t(((kv * G + hg) * D + 64 * g) * 2);
+  const uint32_t p_lane = uint32_t((kv * G * D + 16 * hg + 8 * g) * 2);
+  const uint32_t m_lane = uint32_t((kv * G + hg) * 8 + 4 * g);
 
-  // One tile: this lane's query vector c16 (entry c16 / G of the tile, head
-  // c16 % G) -- its position, its q operand, and whether it is a list entry (a
-  // slot past the list repeats the last entry and stores nothing).
+  // One tile: this lane's query vector c32 (entry c32 / G of the tile, head
+  // c32 % G): its list code, its position and its q operand.  A slot past the
+  // list repeats the last entry: it computes that entry's values again and
+  // stores the same bytes at the same addresses, so every store below is
+  // unconditional.
   struct Tile {
-    int t;
-    bool live;
-    uint4 q[4];
+    int code, t;
+    uint4 q[8];
   };
   // tiles past the wave's last are clamped to the last one: the prefetch then
   // needs no branch, so its loads land straight in the registers that use them
   auto fetch = [&](int tile, Tile& T) {
     tile = min(tile, n_tiles - 1);
-    const int li = tile * E + ent;
-    T.live = li < n_list;
-    const int code = sm.list[T.live ? li : n_list - 1];
-    T.t = off + r_lo + (code >> 6);
-    const bf16_t* qp = q + (size_t(q0 + r_lo + (code >> 6)) * heads + kv * G + hg) * D + 8 * r4;
+    T.code = sm.list[min(tile * E + ent, n_list - 1)];
+    T.t = off + r_lo + (T.code >> 6);
+    const char* qp = qbase + (uint32_t(T.code >> 6) * uint32_t(heads * D * 2) + q_lane);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) T.q[kk] = ld16(qp + 32 * kk);
+    for (int s = 0; s < 8; ++s) T.q[s] = ld16(qp + 16 * s);
   };
 
-  auto compute = [&](auto pos_tag, int tile, const Tile& T) {
-    constexpr bool pos = decltype(pos_tag)::value;  // scale >= 0: maximum of the raw scores
-    f32x4_t sacc[4];
+  // One tile: the scores, then the next tile's q rows requested into the same
+  // registers (in flight during the softmax, the second product and the stores),
+  // then the rest.
+  auto step = [&](int tile, Tile& T) {
+    // the operands are read from LDS per tile, not held in registers across
+    // tiles (the loop writes no LDS, so nothing else stops them being hoisted)
+    asm volatile("" ::: "memory");
+    f32x16_t sacc[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < 2; ++x) {
+      sacc[x] = f32x16_t{};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sacc[s] = mfma32(sm.kop[4 * s + kk][lane], T.q[kk], sacc[s]);
+      for (int s = 0; s < 8; ++s) sacc[x] = mfma32x32(sm.kop[x][s][lane], T.q[s], sacc[x]);
     }
+    const int code = T.code, t = T.t;
+    fetch(tile + 4, T);
     // keys past a row's position exist only when the block holds the row's own
     // position: mask only then (the same branch for the whole wave)
-    const bool masked = __any(T.t < last_key);
-    if (masked) {
+    const bool masked = __any(t < last_key);
+    const int rel = t - key0;  // compared with constant key offsets
+    if (masked) {  // exp2 of -inf is 0, since c > 0
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key0 + 16 * s + e > T.t) sacc[s][e] = pos ? -INFINITY : INFINITY;
+        for (int j = 0; j < 16; ++j)
+          if (32 * x + 8 * (j >> 2) + (j & 3) > rel) sacc[x][j] = -INFINITY;
     }
     float mr = sacc[0][0];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mr = pos ? fmaxf(mr, sacc[s][e]) : fminf(mr, sacc[s][e]);
-    mr = pos ? column_max(mr) : -column_max(-mr);  // finite: the block's first key is visible
+      for (int j = 0; j < 16; ++j) mr = fmaxf(mr, sacc[x][j]);
+    mr = pair_max(mr);  // finite: the block's first key is visible
     const float mc = mr * c;
-    float p[4][4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[s][e] = fast_exp2(fmaf(sacc[s][e], c, -mc));
-        if constexpr (CIS) p[s][e] *= cw[s][e];
-      }
-    if (masked) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key0 + 16 * s + e > T.t) p[s][e] = 0.f;
-    }
     float lsum = 0.f;  // the normaliser sums the fp32 probabilities
+    uint4 pb[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) lsum += (p[s][0] + p[s][1]) + (p[s][2] + p[s][3]);
-    lsum = column_sum(lsum);
-    f32x4_t acc[8];
+    for (int m = 0; m < 4; ++m) {
+      float p[8];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 8; ++u) p[u] = fast_exp2(fmaf(sacc[m >> 1][8 * (m & 1) + u], c, -mc));
+      if constexpr (CIS) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 pb = make_uint4(pack2(p[2 * h][0], p[2 * h][1]), pack2(p[2 * h][2], p[2 * h][3]),
-                                  pack2(p[2 * h + 1][0], p[2 * h + 1][1]),
-                                  pack2(p[2 * h + 1][2], p[2 * h + 1][3]));
-#pragma unroll
-      for (int n = 0; n < 8; ++n) acc[n] = mfma32(sm.vop[8 * h + n][lane], pb, acc[n]);
-    }
-    // unnormalised output rows -> this wave's stage (query vector c16 holds dims
-    // 8 (4 r4 + e) + n), then 16 contiguous bytes per lane to the partial slots
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      *reinterpret_cast<uint4*>(&stg[c16 * kLdsRow + 32 * r4 + 8 * e]) =
-          make_uint4(pack2(acc[0][e], acc[1][e]), pack2(acc[2][e], acc[3][e]),
-                     pack2(acc[4][e], acc[5][e]), pack2(acc[6][e], acc[7][e]));
-    if (T.live && r4 == 0) {
-      const int code = sm.list[tile * E + ent];
-      stream_store(&pml[(size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + hg],
-                   make_float2(mc, lsum));
-    }
-    __builtin_amdgcn_wave_barrier();  // LDS runs a wave's accesses in order
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int vq = 4 * i + r4;  // query vector this lane stores: 16 bytes (dims 8 c16 ..)
-      const int li = tile * E + vq / G;
-      const uint4 x = *reinterpret_cast<const uint4*>(&stg[vq * kLdsRow + 8 * c16]);
-      if (li < n_list) {
-        const int code = sm.list[li];
-        const size_t slot = (size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + vq % G;
-        stream_store(po + slot * D + 8 * c16, x);
+        for (int a = 0; a < 2; ++a) {
+          const float4 w = *reinterpret_cast<const float4*>(&sm.cisw[16 * m + 8 * a + 4 * g]);
+          p[4 * a] *= w.x; p[4 * a + 1] *= w.y; p[4 * a + 2] *= w.z; p[4 * a + 3] *= w.w;
+        }
       }
+      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pb[m] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
     }
-    __builtin_amdgcn_wave_barrier();
+    lsum = pair_sum(lsum);
+    f32x16_t acc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      acc[n] = f32x16_t{};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[n] = mfma32x32(sm.vop[n][m][lane], pb[m], acc[n]);
+    }
+    const uint32_t slot = uint32_t(code >> 6) * uint32_t(k_sel) + uint32_t(code & 63);
+    char* pp = pbase + (slot * uint32_t(heads * D * 2) + p_lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x16_t& a = acc[i >> 1];
+      const int j = 8 * (i & 1);
+      stream_store(reinterpret_cast<bf16_t*>(pp + i * 32 * G),
+                   make_uint4(pack2(a[j], a[j + 1]), pack2(a[j + 2], a[j + 3]),
+                              pack2(a[j + 4], a[j + 5]), pack2(a[j + 6], a[j + 7])));
+    }
+    // lane half 0 stores the maximum, half 1 the sum
+    stream_store(reinterpret_cast<float*>(mbase + (slot * uint32_t(heads * 8) + m_lane)), g ? lsum : mc);
   };
 
-  // Two tile buffers used in turn: the q rows of the wave's next tile are
-  // requested before the current tile's stores, so waiting for them does not
-  // include the stores.
-  auto run = [&](auto pos_tag) {
-    Tile A, B;
-    fetch(wave, A);
-    for (int tile = wave; tile < n_tiles; tile += 8) {
-      fetch(tile + 4, B);
-      compute(pos_tag, tile, A);
-      if (tile + 4 >= n_tiles) break;
-      fetch(tile + 8, A);
-      compute(pos_tag, tile + 4, B);
-    }
-  };
-  if (c >= 0.f) run(std::true_type{});
-  else run(std::false_type{});
+  Tile T;
+  fetch(wave, T);
+  for (int tile = wave; tile < n_tiles; tile += 4) step(tile, T);
 }
 
 // Grid: one dimension over groups of 16 query vectors (row * heads + head);
@@ -484,8 +478,12 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
   // invalid place) into LDS, and the normaliser L = sum of weight * sum
   __shared__ float wsm[16][kMaxPlaces];
   const int g = tid >> 4;
-  // slot of place p: (row * k_sel + p) * heads + head
+  // (max, sum) of place p at (row * k_sel + p) * heads + head; its dims 8 sub ..
+  // at pbase + p * heads * 128 (the region layout of the partial kernel)
+  const int G = heads / kv_heads, hg = head % G;
   const size_t base = size_t(row) * k_sel * heads + head;
+  const size_t pbase = (size_t(row) * k_sel * heads + size_t(kv) * G) * kHeadDim +
+                       (sub >> 1) * (16 * G) + 16 * hg + 8 * (sub & 1);
   float mj[kMaxPlaces / 16], lj[kMaxPlaces / 16];
   float M = -INFINITY;
 #pragma unroll
@@ -520,7 +518,7 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
     for (int u = 0; u < kMergeBatch; ++u) {
       const int p = p0 + u;
       w[u] = p < k_sel ? wsm[g][p] : 0.f;
-      x[u] = w[u] != 0.f ? stream_load(po + (base + size_t(p) * heads) * kHeadDim + 8 * sub)
+      x[u] = w[u] != 0.f ? stream_load(po + pbase + size_t(p) * heads * kHeadDim)
                          : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
@@ -560,9 +558,11 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
 // head).  block_dq_sum_kernel adds the valid places of every (row, head).
 
 struct DqLds {
-  uint4 kop[16][64];   // A of S^T = K Q^T (as PartialLds::kop)
+  // 16x16x32 bf16 operands in lane order (A: lane l holds row l % 16 at k
+  // indices 8 (l / 16) .. +7; the accumulator: column l % 16, rows 4 (l / 16) + e)
+  uint4 kop[16][64];   // A of S^T = K Q^T: [4 s + kk][lane] = key 16 s + c16, dims 32 kk + 8 r4 ..
   uint4 vop[16][64];   // A of dP^T = V dO^T: V rows in the layout of kop
-  uint4 ktop[16][64];  // A of dq^T += K^T dS^T: K transposed in the layout of PartialLds::vop
+  uint4 ktop[16][64];  // A of dq^T += K^T dS^T: [8 h + n][lane] = dim 8 c16 + n, keys 32 h + 16 (u / 4) + 4 r4 + u % 4
   bf16_t stage[4][16 * kLdsRow];
   uint16_t list[kScanRows];
   int n_list;
@@ -828,12 +828,15 @@ size_t block_attn_ws_bytes(int rows_total, int heads, int k_sel) {
          ((size_t(rows_total) * heads * k_sel * sizeof(float2) + 255) & ~size_t(255));
 }
 
-bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k) {
+bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k,
+                          int k_sel) {
   const long long nb = (max_seqlen_k + kBlock - 1) / kBlock;
   const long long nc = (max_seqlen_k + kScanRows - 1) / kScanRows;
-  // every grid dimension holds fewer than 2^32 work-items
+  // every grid dimension holds fewer than 2^32 work-items, and the partial
+  // states of one row chunk span fewer than 2^32 bytes (32-bit offsets)
   return (long long)batch * kv_heads * nb * nc * 256 <= UINT_MAX &&
-         (long long)rows_total * heads * 16 <= UINT_MAX;
+         (long long)rows_total * heads * 16 <= UINT_MAX &&
+         (long long)kScanRows * k_sel * heads * kHeadDim * 2 <= UINT_MAX;
 }
 
 hipError_t launch_block_attn(const void* q, const void* k, const void* v, const int* indices,
@@ -842,7 +845,8 @@ hipError_t launch_block_attn(const void* q, const void* k, const void* v, const 
                              int heads, int kv_heads, int max_seqlen_k, float scale_log2,
                              void* ws, hipStream_t s) {
   if (rows_total == 0 || batch == 0 || max_seqlen_k == 0) return hipSuccess;
-  if (k_sel > kMaxPlaces || !block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k))
+  if (k_sel > kMaxPlaces || !(scale_log2 > 0.f) ||
+      !block_attn_grid_fits(batch, rows_total, heads, kv_heads, max_seqlen_k, k_sel))
     return hipErrorInvalidValue;
   const int G = heads / kv_heads;
   const int nb_max = (max_seqlen_k + kBlock - 1) / kBlock;
@@ -869,7 +873,7 @@ size_t block_dq_ws_bytes(int rows_total, int heads, int k_sel) {
 hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s) {
   if (a.rows_total == 0 || a.batch == 0 || a.max_seqlen_k == 0) return hipSuccess;
   if (a.k_sel > kMaxPlaces ||
-      !block_attn_grid_fits(a.batch, a.rows_total, a.heads, a.kv_heads, a.max_seqlen_k))
+      !block_attn_grid_fits(a.batch, a.rows_total, a.heads, a.kv_heads, a.max_seqlen_k, a.k_sel))
     return hipErrorInvalidValue;
   const int G = a.heads / a.kv_heads;
   const int n_chunk = (a.max_seqlen_k + kScanRows - 1) / kScanRows;

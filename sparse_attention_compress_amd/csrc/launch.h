@@ -144,9 +144,10 @@ hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int
 // Prefill rows, key-block stationary (bf16): partial states per (row, head,
 // place) in `ws` (block_attn_ws_bytes), then their merge.  Writes out (bf16) or
 // out_f32 when given, and lse when given.  block_attn_grid_fits: the launch
-// shapes stay within the grid limits.
+// shapes stay within the grid limits and the 32-bit offsets of the kernels.
 size_t block_attn_ws_bytes(int rows_total, int heads, int k_sel);
-bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k);
+bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k,
+                          int k_sel);
 hipError_t launch_block_attn(const void* q, const void* k, const void* v, const int* indices,
                              int k_sel, const float* cis, void* out, float* out_f32, float* lse,
                              const int* cu_q, const int* cu_k, int batch, int rows_total,

@@ -966,6 +966,13 @@ def prefill_main(args, dev):
         result["partial_state_bytes"] = pbytes
         result["partial_write_gbs"] = round(pbytes / (kern["selected_attn"] * 1e-6) / 1e9, 1)
         result["merge_read_gbs"] = round(pbytes / (kern["merge"] * 1e-6) / 1e9, 1)
+        # the partial kernel's own ceiling is HBM: its counted bytes (partial states
+        # written, query/index/K/V rows fetched) per launch over its duration
+        tr = result["roofline"]["traffic"]
+        if tr is not None:
+            gbs = tr / (kern["selected_attn"] * 1e-6) / 1e9
+            result["partial_kernel_hbm"] = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
     if args.selected_path == "blocks":  # no per-row gather on the key-block path
         del result["selected_gathered_gbs"]
     if args.calibrate_copy:

@@ -25,7 +25,9 @@
 // output arrays hold, so the branches of one step can share dq, dk and dv.
 //
 // Launches: prep (delta, list counts cleared), count, scan, fill (selected
-// branch), zero, then the matrix-core dk/dv and dq kernels.  Also here: the
+// branch; count and fill per chunk of rows with LDS tables, or per place for
+// sequences of more than 8192 blocks), zero, then the matrix-core dk/dv and dq
+// kernels.  Also here: the
 // window mean's transpose (dK_c, dV_c back onto K, V) and the gradients of the
 // gated sum of the three branches.
 #include <algorithm>
@@ -130,6 +132,64 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_fill_kernel(
   if (slot >= 0) list[atomicAdd(cursor + slot, 1)] = make_int2(row, t);
 }
 
+// The same counts and lists built per (sequence, KV head, chunk of kListRows
+// query rows): a chunk's places are first counted per block in LDS, so the
+// global counters and cursors take one atomic per (chunk, block) instead of one
+// per place (the places of a row's early blocks otherwise all hit one counter).
+// Used when a sequence's blocks fit the LDS table.
+constexpr int kListRows = 1024;
+constexpr int kListMaxBlocks = 8192;
+
+// The chunk's places (rows r0 .. r1 - 1 of sequence b, KV head kv) that list a
+// block the row attends to: f(row, t, id) for each.
+template <typename F>
+__device__ __forceinline__ void for_chunk_places(const int* __restrict__ indices, int k_sel,
+                                                 int kv_heads, int kv, int q0, int r0, int r1,
+                                                 int off, int nb_max, F f) {
+  const int n = (r1 - r0) * k_sel;
+  for (int p = threadIdx.x; p < n; p += kBwdThreads) {
+    const int dr = p / k_sel, r = r0 + dr, place = p - dr * k_sel;
+    const int id = indices[(size_t(q0 + r) * kv_heads + kv) * k_sel + place];
+    const int t = r + off;
+    if (id >= 0 && id < nb_max && kBlock * id <= t) f(q0 + r, t, id);
+  }
+}
+
+// FILL = false: add the chunk's per-block counts to cnt.  FILL = true: reserve
+// each block's range at its cursor, then write the chunk's entries (row, t)
+// into it.  Grid (chunk, KV head, sequence).
+template <bool FILL>
+__global__ __launch_bounds__(kBwdThreads) void bwd_chunk_lists_kernel(
+    const int* __restrict__ indices, int k_sel, int kv_heads, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int nb_max, int* __restrict__ counters,
+    int2* __restrict__ list) {
+  __shared__ int h[kListMaxBlocks];
+  const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
+  const int r0 = c * kListRows;
+  if (r0 >= lq) return;  // the same for the whole workgroup
+  const int r1 = min(lq, r0 + kListRows);
+  const int off = (cu_k[b + 1] - cu_k[b]) - lq;
+  // the chunk's rows list ids up to (r1 - 1 + off) / 64
+  const int nb = min(nb_max, max(0, r1 - 1 + off) / kBlock + 1);
+  for (int i = threadIdx.x; i < nb; i += kBwdThreads) h[i] = 0;
+  __syncthreads();
+  for_chunk_places(indices, k_sel, kv_heads, kv, q0, r0, r1, off, nb_max,
+                   [&](int, int, int id) { atomicAdd(&h[id], 1); });
+  __syncthreads();
+  int* g = counters + size_t(b * kv_heads + kv) * nb_max;
+  for (int i = threadIdx.x; i < nb; i += kBwdThreads) {
+    const int n = h[i];
+    if constexpr (FILL) h[i] = n ? atomicAdd(g + i, n) : 0;
+    else if (n) atomicAdd(g + i, n);
+  }
+  if constexpr (FILL) {
+    __syncthreads();
+    for_chunk_places(indices, k_sel, kv_heads, kv, q0, r0, r1, off, nb_max,
+                     [&](int row, int t, int id) { list[atomicAdd(&h[id], 1)] = make_int2(row, t); });
+  }
+}
+
 // dk and dv of the blocks whose row list spans several chunks start at 0 (the
 // chunks add to them); one workgroup per (sequence, kv head, block).
 template <int MODE>
@@ -172,10 +232,17 @@ hipError_t launch_bwd_lists(const SelectedBwdArgs& a, hipStream_t s) {
                                MODE == kBwdSelected ? n_slots : 0);
   if (e != hipSuccess) return e;
   const unsigned place_grid = unsigned((n_place + kBwdThreads - 1) / kBwdThreads);
+  // per-chunk counting (LDS first) when the blocks fit its table, else per place
+  const bool chunked = a.nb_max <= kListMaxBlocks;
+  const dim3 chunk_grid(unsigned((a.max_seqlen_k + kListRows - 1) / kListRows),
+                        unsigned(a.kv_heads), unsigned(a.batch));
   if (MODE == kBwdSelected && place_grid > 0) {
-    e = launch_kernel(kKindBwdLists, bwd_count_kernel, dim3(place_grid), dim3(kBwdThreads), s,
-                      a.indices, n_place, a.k_sel, a.kv_heads, a.cu_q, a.cu_k, a.batch, a.nb_max,
-                      a.cnt);
+    e = chunked ? launch_kernel(kKindBwdLists, bwd_chunk_lists_kernel<false>, chunk_grid,
+                                dim3(kBwdThreads), s, a.indices, a.k_sel, a.kv_heads, a.cu_q,
+                                a.cu_k, a.nb_max, a.cnt, static_cast<int2*>(nullptr))
+                : launch_kernel(kKindBwdLists, bwd_count_kernel, dim3(place_grid),
+                                dim3(kBwdThreads), s, a.indices, n_place, a.k_sel, a.kv_heads,
+                                a.cu_q, a.cu_k, a.batch, a.nb_max, a.cnt);
     if (e != hipSuccess) return e;
   }
   if (MODE == kBwdSelected) {
@@ -184,9 +251,12 @@ hipError_t launch_bwd_lists(const SelectedBwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (MODE == kBwdSelected && place_grid > 0) {
-    e = launch_kernel(kKindBwdLists, bwd_fill_kernel, dim3(place_grid), dim3(kBwdThreads), s,
-                      a.indices, n_place, a.k_sel, a.kv_heads, a.cu_q, a.cu_k, a.batch, a.nb_max,
-                      a.cursor, a.list);
+    e = chunked ? launch_kernel(kKindBwdLists, bwd_chunk_lists_kernel<true>, chunk_grid,
+                                dim3(kBwdThreads), s, a.indices, a.k_sel, a.kv_heads, a.cu_q,
+                                a.cu_k, a.nb_max, a.cursor, a.list)
+                : launch_kernel(kKindBwdLists, bwd_fill_kernel, dim3(place_grid),
+                                dim3(kBwdThreads), s, a.indices, n_place, a.k_sel, a.kv_heads,
+                                a.cu_q, a.cu_k, a.batch, a.nb_max, a.cursor, a.list);
     if (e != hipSuccess) return e;
   }
   // dk/dv and dq on the matrix cores (bwd_mfma.hip); blocks seen by more rows

@@ -107,6 +107,30 @@ def test_selected_bwd_matches_oracle(H, H_kv, lengths, path):
     _compare(d, dq, dk, dv, f"bwd_g{H // H_kv}_{path}")
 
 
+def test_selected_bwd_per_place_lists():
+    """The block lists built one place at a time (the path for sequences of more
+    than 8192 blocks; every other test builds them per chunk of rows): the same
+    ragged batch with max_seqlen_k raised to 600000 tokens (9375 blocks); the
+    forward runs row by row, the key-block grid being too large for it."""
+    w = dataclasses.replace(W.scaled(W.selected_prefill(), [500, 900]), heads=8, kv_heads=2)
+    d = _inputs(w)
+    big = 600000
+    rows, H, D = d["q"].shape
+    log(f"selected bwd, per-place lists: max_seqlen_k={big}")
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((rows, H), dtype=F32, device=DEV)
+    nsa.nsa_selected_attn_fwd(d["q"], d["k"], d["v"], d["idx"], d["cu_k"], big, out, lse=lse,
+                              cu_seqlens_q=d["cu_q"],
+                              workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    dq = torch.full((rows, H, D), float("nan"), dtype=F32, device=DEV)
+    dk = torch.full(d["k"].shape, float("nan"), dtype=F32, device=DEV)
+    dv = torch.full(d["v"].shape, float("nan"), dtype=F32, device=DEV)
+    nsa.nsa_selected_attn_bwd(d["q"], d["k"], d["v"], out, d["d_out"], lse, d["idx"], d["cu_q"],
+                              d["cu_k"], big, dq, dk, dv)
+    torch.cuda.synchronize()
+    _compare(d, dq, dk, dv, "bwd_per_place_lists")
+
+
 @pytest.mark.parametrize("path", ["blocks", "rows"])
 def test_selected_bwd_query_tails_and_empty_sequence(path):
     """Query rows that are only the last positions of their sequences (t offset

@@ -144,7 +144,8 @@ typedef enum nsa_kernel_kind {
   NSA_KERNEL_SELECTED_BWD_DQ = 10,
   NSA_KERNEL_SELECTED_BWD_DKDV = 11,
   NSA_KERNEL_SELECTED_BWD_LISTS = 12,
-  NSA_KERNEL_SELECTED_BWD_DQ_SUM = 13
+  NSA_KERNEL_SELECTED_BWD_DQ_SUM = 13,
+  NSA_KERNEL_BLOCK_LISTS = 14
 } nsa_kernel_kind;
 nsa_status nsa_profile_next_launch(int32_t kernel_kind, hipEvent_t start, hipEvent_t stop);
 

@@ -490,6 +490,7 @@ KERNEL_COMPRESSED_LSE, KERNEL_COMPRESSED_ATTN, KERNEL_WINDOW_ATTN, KERNEL_FETCH 
 KERNEL_BLOCKMASK_ATTN = 9
 KERNEL_SELECTED_BWD_DQ, KERNEL_SELECTED_BWD_DKDV, KERNEL_SELECTED_BWD_LISTS = 10, 11, 12
 KERNEL_SELECTED_BWD_DQ_SUM = 13
+KERNEL_BLOCK_LISTS = 14
 
 
 def blockmask_attn_workspace_size(batch, max_seqlen, heads):

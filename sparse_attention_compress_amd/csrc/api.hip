@@ -246,7 +246,7 @@ nsa_status nsa_select_topk(const float* block_scores, int32_t* indices, const in
 size_t nsa_selected_attn_workspace_size(int32_t rows_total, int32_t heads, int32_t kv_heads,
                                         int32_t head_dim, int32_t k_sel, int32_t decode) {
   if (rows_total <= 0 || kv_heads <= 0 || heads <= 0 || k_sel <= 0 || head_dim != nsa::kHeadDim) return 0;
-  if (!decode) return k_sel <= kMaxPrefillSel ? nsa::block_attn_ws_bytes(rows_total, heads, k_sel) : 0;
+  if (!decode) return k_sel <= kMaxPrefillSel ? nsa::block_attn_ws_bytes(rows_total, heads, kv_heads, k_sel) : 0;
   return nsa::attn_ws_bytes(rows_total, kv_heads, heads / kv_heads, k_sel, decode);
 }
 
@@ -316,7 +316,7 @@ size_t nsa_selected_attn_bwd_workspace_size(int32_t batch, int32_t rows_total,
     return 0;
   const int nb_max = (max_seqlen_k + nsa::kBlock - 1) / nsa::kBlock;
   return ((nsa::selected_bwd_ws_bytes(rows_total, heads, kv_heads, k_sel, batch, nb_max) + 255) & ~size_t(255)) +
-         nsa::block_dq_ws_bytes(rows_total, heads, k_sel);
+         nsa::block_dq_ws_bytes(rows_total, heads, kv_heads, k_sel);
 }
 
 size_t nsa_selected_attn_bwd_workspace_size_min(int32_t batch, int32_t rows_total,
@@ -1016,7 +1016,7 @@ PrefillLayout prefill_layout(const nsa_prefill_params* p) {
   // in float32 until the gated sum (one bf16 rounding fewer, for the one its
   // partial states add)
   L.partial = off;
-  off += nsa::block_attn_ws_bytes(p->rows_total, p->heads, p->topk);
+  off += nsa::block_attn_ws_bytes(p->rows_total, p->heads, p->kv_heads, p->topk);
   L.o_sel32 = off;
   off += up(rows * H * p->head_dim * sizeof(float));
   L.total = off;

@@ -29,6 +29,7 @@
 // partial output is rounded to bf16 once more (2^-9 relative) before the
 // merge.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -104,134 +105,86 @@ struct PartialLds {
   uint4 kop[2][8][64];
   uint4 vop[4][4][64];
   float cisw[kBlock];        // CIS of the block's keys (CIS mode)
-  uint16_t list[kScanRows];  // (row in chunk << 6) | place
-  int n_list;
+  uint16_t list[kScanRows];  // the block's list entries: (row in chunk << 6) | place
 };
 
-// Append to the list the rows that list block `blk`, each at the first place
-// holding it.  Vector form (k_sel a multiple of 4 and a 16-byte aligned array,
-// so every index row is 16-byte aligned): P lanes per index row, 4 ids per lane, all of a batch's loads in
-// flight together.
-template <int P, typename Lds>
-__device__ __forceinline__ void scan_rows_vec(Lds& sm, const int* __restrict__ indices,
-                                              int k_sel, int kv_heads, int kv, int q0, int r_lo,
-                                              int r_first, int r_hi, int blk, int wave, int lane) {
-  constexpr int RPI = 64 / P;       // rows per wave instruction
-  constexpr int kBatch = 16;        // loads in flight per lane
-  const int seg = lane % P, gbase = lane & ~(P - 1);
-  const int n_inst = (r_hi - r_first + 4 * RPI - 1) / (4 * RPI);
-  for (int j0 = 0; j0 < n_inst; j0 += kBatch) {
-    int4 idv[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int r = r_first + ((j0 + j) * 4 + wave) * RPI + lane / P;
-      const bool ok = j0 + j < n_inst && r < r_hi && 4 * seg < k_sel;
-      const int* row = indices + (size_t(q0 + min(r, r_hi - 1)) * kv_heads + kv) * k_sel;
-      idv[j] = ok ? *reinterpret_cast<const int4*>(row + 4 * seg) : make_int4(-1, -1, -1, -1);
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (j0 + j >= n_inst) break;  // the same for the whole wave
-      const int r = r_first + ((j0 + j) * 4 + wave) * RPI + lane / P;
-      const int4 x = idv[j];
-      const int u = x.x == blk ? 0 : x.y == blk ? 1 : x.z == blk ? 2 : x.w == blk ? 3 : -1;
-      const unsigned long long hit = __ballot(u >= 0);
-      const unsigned long long grp = (hit >> gbase) & ((1ull << P) - 1ull);
-      const bool writer = u >= 0 && (grp & ((1ull << seg) - 1ull)) == 0ull;
-      const unsigned long long wmask = __ballot(writer);
-      int base = 0;
-      if (lane == 0 && wmask != 0ull) base = atomicAdd(&sm.n_list, __popcll(wmask));
-      base = __shfl(base, 0);
-      if (writer)
-        sm.list[base + __popcll(wmask & ((1ull << lane) - 1ull))] = uint16_t(((r - r_lo) << 6) | (4 * seg + u));
-    }
-  }
+// The rows of one (sequence, KV head, chunk of kScanRows query rows) unit: its
+// first packed query row q0 of the sequence, its rows r_lo .. r_hi - 1 of the
+// sequence (at positions off + r), the number of blocks they can list (reach),
+// and its entries of the block lists, base .. base + cap - 1 (k_sel per row, in
+// KV-head-major order, so the units' entries never overlap).
+struct ChunkRows {
+  int q0, r_lo, r_hi, off, reach, cap;
+  size_t base;
+};
+__device__ __forceinline__ bool chunk_rows(const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+                                           int b, int kv, int chunk, int rows_total, int k_sel,
+                                           int nb_max, ChunkRows& u) {
+  u.q0 = cu_q[b];
+  const int lq = cu_q[b + 1] - u.q0;
+  u.off = (cu_k[b + 1] - cu_k[b]) - lq;
+  u.r_lo = chunk * kScanRows;
+  if (u.r_lo >= lq) return false;
+  u.r_hi = min(lq, u.r_lo + kScanRows);
+  const int t_max = u.r_hi - 1 + u.off;
+  u.reach = t_max >= 0 ? min(nb_max, t_max / kBlock + 1) : 0;
+  u.cap = (u.r_hi - u.r_lo) * k_sel;
+  u.base = (size_t(kv) * rows_total + u.q0 + u.r_lo) * k_sel;
+  return true;
 }
 
-// Scalar form for any k_sel: one thread per index row.
-template <typename Lds>
-__device__ __forceinline__ void scan_rows_scalar(Lds& sm, const int* __restrict__ indices,
-                                                 int k_sel, int kv_heads, int kv, int q0, int r_lo,
-                                                 int r_first, int r_hi, int blk, int tid, int lane) {
-  for (int r0 = r_first; r0 < r_hi; r0 += 256) {
-    const int r = r0 + tid;
-    int place = -1;
-    if (r < r_hi) {
-      const int* ids = indices + (size_t(q0 + r) * kv_heads + kv) * k_sel;
-      for (int p0 = 0; p0 < k_sel; p0 += 16) {
-        int idv[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) idv[u] = p0 + u < k_sel ? ids[p0 + u] : -1;
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (place < 0 && idv[u] == blk) place = p0 + u;
-      }
-    }
-    const unsigned long long mask = __ballot(place >= 0);
-    int base = 0;
-    if (lane == 0 && mask != 0ull) base = atomicAdd(&sm.n_list, __popcll(mask));
-    base = __shfl(base, 0);
-    if (place >= 0)
-      sm.list[base + __popcll(mask & ((1ull << lane) - 1ull))] = uint16_t(((r - r_lo) << 6) | place);
-  }
-}
-
-template <typename Lds>
-__device__ __forceinline__ void scan_rows(Lds& sm, const int* __restrict__ indices, int k_sel,
-                                          int kv_heads, int kv, int q0, int r_lo, int r_first,
-                                          int r_hi, int blk) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if ((k_sel & 3) == 0 && (reinterpret_cast<uintptr_t>(indices) & 15) == 0) {
-    const int lanes = k_sel / 4;
-    if (lanes <= 1) scan_rows_vec<1>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else if (lanes <= 2) scan_rows_vec<2>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else if (lanes <= 4) scan_rows_vec<4>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else if (lanes <= 8) scan_rows_vec<8>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-    else scan_rows_vec<16>(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, wave, lane);
-  } else {
-    scan_rows_scalar(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk, tid, lane);
-  }
-}
-
-// The (sequence, KV head, row chunk, block) of a workgroup of a one-dimensional
-// grid in XCD-grouped order (the blocks of one row chunk run together on one
-// XCD and share its query rows and index rows in L2), and the chunk's rows.
+// The (sequence, KV head, row chunk, j) of a workgroup of a one-dimensional grid
+// in XCD-grouped order (the blocks of one row chunk run together on one XCD and
+// share its query rows in L2): the workgroup takes the chunk's j-th listed
+// block.  False when there is no such block for certain (past the chunk's rows
+// or past the blocks they can list).
 struct BlockUnit {
-  int blk, kv, b, kstart, L, q0, off, r_lo, r_hi, r_first;
+  int j, kv, b, kstart, L;
+  ChunkRows u;
 };
-__device__ __forceinline__ BlockUnit block_unit(const int* __restrict__ cu_q,
-                                                const int* __restrict__ cu_k, int kv_heads,
-                                                int nb_max, int n_chunk) {
-  BlockUnit u;
+__device__ __forceinline__ bool block_unit(const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+                                           int kv_heads, int nb_max, int n_chunk, int rows_total,
+                                           int k_sel, BlockUnit& U) {
   int m = xcd_grouped_index(int(blockIdx.x), int(gridDim.x));
-  u.blk = m % nb_max;
+  U.j = m % nb_max;
   m /= nb_max;
   const int chunk = m % n_chunk;
   m /= n_chunk;
-  u.kv = m % kv_heads;
-  u.b = m / kv_heads;
-  u.kstart = cu_k[u.b];
-  u.L = cu_k[u.b + 1] - u.kstart;
-  u.q0 = cu_q[u.b];
-  const int Lq = cu_q[u.b + 1] - u.q0;
-  u.off = u.L - Lq;  // query row r of the sequence sits at position off + r
-  u.r_lo = chunk * kScanRows;
-  u.r_hi = min(Lq, u.r_lo + kScanRows);
-  u.r_first = max(u.r_lo, kBlock * u.blk - u.off);  // rows that can list the block
-  return u;
+  U.kv = m % kv_heads;
+  U.b = m / kv_heads;
+  if (!chunk_rows(cu_q, cu_k, U.b, U.kv, chunk, rows_total, k_sel, nb_max, U.u)) return false;
+  if (U.j >= min(U.u.cap, U.u.reach)) return false;
+  U.kstart = cu_k[U.b];
+  U.L = cu_k[U.b + 1] - U.kstart;
+  return true;
+}
+
+// The j-th listed block of a unit (from its list head) and its entries:
+// false when the unit lists fewer blocks.
+__device__ __forceinline__ bool listed_block(const int2* __restrict__ lhead, const BlockUnit& U,
+                                             int& blk, int& start, int& n) {
+  const int2 h = lhead[U.u.base + U.j];
+  if (h.x < 0) return false;
+  blk = h.x;
+  start = h.y;
+  n = (U.j + 1 < U.u.cap ? lhead[U.u.base + U.j + 1].y : U.u.cap) - start;
+  return true;
 }
 
 // Valid places of one index row for position t, as a bit mask: id >= 0, block
 // start <= t, and no earlier place holding the same id.  Lane `sub` of a group
 // of 16 lanes (the lanes of one query vector, `grp` its first lane) checks
-// places sub, sub + 16, ... and compares them with the earlier places through
-// the group; every lane of the group gets the whole mask.
-__device__ __forceinline__ unsigned long long valid_places(const int* __restrict__ ids, int k_sel,
-                                                          int t, int sub, int grp) {
-  const int rounds = (k_sel + 15) >> 4;
-  int myid[kMaxPlaces / 16];
+// places sub, sub + 16, ... (its ids, -1 past k_sel: load_place_ids) and
+// compares them with the earlier places through the group; every lane of the
+// group gets the whole mask.
+__device__ __forceinline__ void load_place_ids(const int* __restrict__ ids, int k_sel, int sub,
+                                               int (&myid)[kMaxPlaces / 16]) {
 #pragma unroll
   for (int u = 0; u < kMaxPlaces / 16; ++u) myid[u] = 16 * u + sub < k_sel ? ids[16 * u + sub] : -1;
+}
+__device__ __forceinline__ unsigned long long valid_of_ids(const int (&myid)[kMaxPlaces / 16],
+                                                           int k_sel, int t, int sub, int grp) {
+  const int rounds = (k_sel + 15) >> 4;
   unsigned long long valid = 0ull;
 #pragma unroll
   for (int u = 0; u < kMaxPlaces / 16; ++u) {
@@ -247,6 +200,104 @@ __device__ __forceinline__ unsigned long long valid_places(const int* __restrict
   }
   return valid;
 }
+__device__ __forceinline__ unsigned long long valid_places(const int* __restrict__ ids, int k_sel,
+                                                          int t, int sub, int grp) {
+  int myid[kMaxPlaces / 16];
+  load_place_ids(ids, k_sel, sub, myid);
+  return valid_of_ids(myid, k_sel, t, sub, grp);
+}
+
+// ----------------------------------------------------------------- block lists
+//
+// block_list_kernel -- one workgroup per (sequence, KV head, chunk of kScanRows
+// query rows): the chunk's valid places (those valid_places admits, the places
+// the merge combines) grouped by block, through a table of the blocks in LDS.
+// In the unit's entries (ChunkRows::base ..): code[u] = (row in chunk << 6) |
+// place, block after block in increasing block order; head[j] = (block, first
+// u) of the chunk's j-th listed block, then (-1, number of places) from the
+// last listed block up to the number of blocks the rows can list (and once
+// when there is room), which ends every workgroup that reads past the list.
+constexpr int kListMaxBlocks = 8192;  // blocks a sequence may have on this path (524288 tokens)
+
+__global__ __launch_bounds__(256) void block_list_kernel(
+    const int* __restrict__ indices, int k_sel, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int kv_heads, int nb_max, int rows_total,
+    uint16_t* __restrict__ lcode, int2* __restrict__ lhead) {
+  __shared__ int tab[kListMaxBlocks];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = tid & 15, grp = lane & 48;
+  const int kv = blockIdx.y, b = blockIdx.z;
+  ChunkRows u;
+  if (!chunk_rows(cu_q, cu_k, b, kv, int(blockIdx.x), rows_total, k_sel, nb_max, u)) return;
+  for (int i = tid; i < u.reach; i += 256) tab[i] = 0;
+  __syncthreads();
+  const int rounds = (k_sel + 15) >> 4;
+  // every row's valid places, 16 rows a round (16 lanes a row), the index rows of
+  // kRounds rounds loaded together; FILL: place them at their block's cursor,
+  // else count them
+  constexpr int kRounds = 8;
+  auto each_place = [&](auto fill_tag) {
+    constexpr bool FILL = decltype(fill_tag)::value;
+    for (int r0 = u.r_lo; r0 < u.r_hi; r0 += 16 * kRounds) {
+      int myid[kRounds][kMaxPlaces / 16];
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) {
+        // every lane of a group takes part in the shuffles: rows past the chunk
+        // repeat its last row and count nothing
+        const int r = min(r0 + 16 * i + (tid >> 4), u.r_hi - 1);
+        load_place_ids(indices + (size_t(u.q0 + r) * kv_heads + kv) * k_sel, k_sel, sub, myid[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) {
+        const int r_in = r0 + 16 * i + (tid >> 4);
+        const int r = min(r_in, u.r_hi - 1);
+        const unsigned long long valid = valid_of_ids(myid[i], k_sel, r + u.off, sub, grp);
+        if (r_in >= u.r_hi) continue;
+#pragma unroll
+        for (int x = 0; x < kMaxPlaces / 16; ++x) {
+          if (x >= rounds) break;
+          const int p = 16 * x + sub;
+          if (!((valid >> p) & 1ull) || myid[i][x] >= u.reach) continue;
+          if constexpr (FILL)
+            lcode[u.base + atomicAdd(&tab[myid[i][x]], 1)] = uint16_t(((r - u.r_lo) << 6) | p);
+          else
+            atomicAdd(&tab[myid[i][x]], 1);
+        }
+      }
+    }
+  };
+  each_place(std::false_type{});
+  __syncthreads();
+  // exclusive scan of (count, listed) over the blocks, thread tid taking `per`
+  // consecutive blocks; packed as listed << 17 | count (a unit has at most
+  // 2^16 places and kListMaxBlocks blocks)
+  const int per = (u.reach + 255) / 256;
+  int packed = 0;
+  for (int i = 0; i < per; ++i) {
+    const int x = tid * per + i;
+    if (x < u.reach) packed += (tab[x] != 0 ? 1 << 17 : 0) + tab[x];
+  }
+  const int incl = wave_inclusive_scan(packed);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = incl - packed;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int all = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const int total = all & 0x1FFFF, listed = all >> 17;
+  int c = before & 0x1FFFF, n = before >> 17;
+  for (int i = 0; i < per; ++i) {
+    const int x = tid * per + i;
+    if (x >= u.reach) break;
+    const int cnt = tab[x];
+    if (cnt != 0) lhead[u.base + n++] = make_int2(x, c);
+    tab[x] = c;  // the block's cursor
+    c += cnt;
+  }
+  const int j_end = min(u.cap, max(u.reach, listed + 1));
+  for (int j = listed + tid; j < j_end; j += 256) lhead[u.base + j] = make_int2(-1, total);
+  __syncthreads();
+  each_place(std::true_type{});
+}
 
 // Grid: one dimension over (sequence, KV head, row chunk, block) in XCD-grouped
 // order, so the blocks of one row chunk run together on one XCD and share its
@@ -261,29 +312,30 @@ __device__ __forceinline__ unsigned long long valid_places(const int* __restrict
 template <int G, bool CIS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void block_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int* __restrict__ indices, int k_sel, const float* __restrict__ cis,
-    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads, int nb_max,
-    int n_chunk, float scale_log2, bf16_t* __restrict__ po, float2* __restrict__ pml) {
+    const uint16_t* __restrict__ lcode, const int2* __restrict__ lhead, int k_sel,
+    const float* __restrict__ cis, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    int kv_heads, int nb_max, int n_chunk, int rows_total, float scale_log2,
+    bf16_t* __restrict__ po, float2* __restrict__ pml) {
   constexpr int E = 32 / G;  // list entries per tile of 32 query vectors
   constexpr int D = kHeadDim;
   __shared__ PartialLds sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c32 = lane & 31, g = lane >> 5;
 
-  const BlockUnit U = block_unit(cu_q, cu_k, kv_heads, nb_max, n_chunk);
-  const int blk = U.blk, kv = U.kv, kstart = U.kstart, L = U.L, q0 = U.q0, off = U.off;
-  const int r_lo = U.r_lo, r_hi = U.r_hi, r_first = U.r_first;
-  if (r_first >= r_hi || kBlock * blk >= L) return;  // the same for the whole workgroup
+  BlockUnit U;  // both returns below are the same for the whole workgroup
+  if (!block_unit(cu_q, cu_k, kv_heads, nb_max, n_chunk, rows_total, k_sel, U)) return;
+  int blk, start, n_list;
+  if (!listed_block(lhead, U, blk, start, n_list)) return;
+  const int kv = U.kv, kstart = U.kstart, L = U.L, q0 = U.u.q0, off = U.u.off, r_lo = U.u.r_lo;
   const int heads = kv_heads * G;
 
   // The block's operands straight from K and V (rows past the sequence end
   // repeat its last row: finite data, masked below since they lie past every
-  // row's position), requested before the index scan so both are in flight
-  // together.  Waves 0 and 1 load K (16-byte piece x = 128 i + tid is key x / 16,
-  // dims 8 (x % 16) ..); waves 2 and 3 load V, thread t = tid - 128 taking dims
+  // row's position), requested together with the block's list entries.  Waves
+  // 0 and 1 load K (16-byte piece x = 128 i + tid is key x / 16, dims
+  // 8 (x % 16) ..); waves 2 and 3 load V, thread t = tid - 128 taking dims
   // 8 (t % 16) .. +7 of the eight keys of step t / 32, lane half (t / 16) % 2, and
   // transposing them in registers.
-  if (tid == 0) sm.n_list = 0;
   uint4 ld[8];
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kb = k + size_t(kstart) * rs + size_t(kv) * D;
@@ -302,9 +354,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       ld[u] = ld16(vb + size_t(min(kBlock * blk + key, L - 1)) * rs + 8 * (t & 15));
     }
   }
+  for (int i = tid; i < n_list; i += 256) sm.list[i] = lcode[U.u.base + start + i];
   if (CIS && tid < kBlock) sm.cisw[tid] = cis[size_t(kstart + min(kBlock * blk + tid, L - 1)) * kv_heads + kv];
-  __syncthreads();  // n_list = 0 seen by every wave
-  scan_rows(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk);
   if (wave < 2) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -328,7 +379,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     }
   }
   __syncthreads();
-  const int n_list = sm.n_list;
   const int n_tiles = (n_list + E - 1) / E;
   if (wave >= n_tiles) return;  // no barrier below
 
@@ -550,187 +600,188 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
 // CIS, for a given upstream gradient dO; the forward's natural-log normaliser
 // lse and delta = dO . O given): per (row, head) over the row's keys J,
 // p = exp(scale q.k - lse), ds = p (dO.v - delta), dq = scale sum_J ds k.  As
-// in the forward, one workgroup per (sequence, KV head, 1024-row chunk, 64-key
-// block) walks the rows that list the block in tiles of 16 query vectors;
-// per tile S^T = K Q^T and dP^T = V dO^T (16 MFMAs each), then
-// dq^T += K^T dS^T (16 MFMAs, dS^T packed straight into the B operand), and the
-// block's share of dq (without the scale) goes out as bf16 at (row, place,
-// head).  block_dq_sum_kernel adds the valid places of every (row, head).
+// in the forward, one workgroup per (sequence, KV head, 1024-row chunk, listed
+// block) walks the rows that list the block in tiles of 32 query vectors on
+// 32x32x16 tiles: per tile S^T = K Q^T and dP^T = V dO^T (16 MFMAs each, the
+// operand layouts of the forward's kop for K and V), then dq^T += K^T dS^T (16
+// MFMAs, K^T in the layout of the forward's vop, dS^T packed straight from the
+// accumulators into the B operand), and the block's share of dq (without the
+// scale) goes out as bf16 at (row, place, head), in the forward's partial
+// output layout.  block_dq_sum_kernel adds the valid places of every (row,
+// head).
 
 struct DqLds {
-  // 16x16x32 bf16 operands in lane order (A: lane l holds row l % 16 at k
-  // indices 8 (l / 16) .. +7; the accumulator: column l % 16, rows 4 (l / 16) + e)
-  uint4 kop[16][64];   // A of S^T = K Q^T: [4 s + kk][lane] = key 16 s + c16, dims 32 kk + 8 r4 ..
-  uint4 vop[16][64];   // A of dP^T = V dO^T: V rows in the layout of kop
-  uint4 ktop[16][64];  // A of dq^T += K^T dS^T: [8 h + n][lane] = dim 8 c16 + n, keys 32 h + 16 (u / 4) + 4 r4 + u % 4
-  bf16_t stage[4][16 * kLdsRow];
+  uint4 kop[2][8][64];   // K: A of S^T = K Q^T (PartialLds::kop layout)
+  uint4 vop[2][8][64];   // V: A of dP^T = V dO^T (the same layout)
+  uint4 ktop[4][4][64];  // K^T: A of dq^T += K^T dS^T (PartialLds::vop layout)
   uint16_t list[kScanRows];
-  int n_list;
 };
 
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void block_dq_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, const int* __restrict__ indices, int k_sel,
-    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int kv_heads, int nb_max,
-    int n_chunk, float scale_log2, bf16_t* __restrict__ pq) {
-  constexpr int E = 16 / G;
+    const float* __restrict__ delta, const uint16_t* __restrict__ lcode,
+    const int2* __restrict__ lhead, int k_sel, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int kv_heads, int nb_max, int n_chunk, int rows_total,
+    float scale_log2, bf16_t* __restrict__ pq) {
+  constexpr int E = 32 / G;
   constexpr int D = kHeadDim;
   __shared__ DqLds sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c16 = lane & 15, r4 = lane >> 4;
-  const BlockUnit U = block_unit(cu_q, cu_k, kv_heads, nb_max, n_chunk);
-  const int blk = U.blk, kv = U.kv, kstart = U.kstart, L = U.L, q0 = U.q0, off = U.off;
-  const int r_lo = U.r_lo, r_hi = U.r_hi, r_first = U.r_first;
-  if (r_first >= r_hi || kBlock * blk >= L) return;  // the same for the whole workgroup
+  const int c32 = lane & 31, g = lane >> 5;
+  BlockUnit U;  // both returns below are the same for the whole workgroup
+  if (!block_unit(cu_q, cu_k, kv_heads, nb_max, n_chunk, rows_total, k_sel, U)) return;
+  int blk, start, n_list;
+  if (!listed_block(lhead, U, blk, start, n_list)) return;
+  const int kv = U.kv, kstart = U.kstart, L = U.L, q0 = U.u.q0, off = U.u.off, r_lo = U.u.r_lo;
   const int heads = kv_heads * G;
 
   // operands straight from K and V (rows past the sequence end repeat its last
-  // row; masked), requested before the index scan: wave w loads K and V slice w
-  // (kop, vop) and the eight K rows of half w / 2 for K^T outputs tiles
-  // 4 (w % 2) .. +3 (ktop)
-  if (tid == 0) sm.n_list = 0;
+  // row; masked): waves 0 and 1 load K pieces for kop (as the forward), waves 2
+  // and 3 V pieces for vop and, as the forward's V, the K pieces of ktop
   const size_t rs = size_t(kv_heads) * D;
   const bf16_t* kb = k + size_t(kstart) * rs + size_t(kv) * D;
   const bf16_t* vb = v + size_t(kstart) * rs + size_t(kv) * D;
-  uint4 lk[4], lv[4], lt[8];
-  {
-    const size_t kr = size_t(min(kBlock * blk + 16 * wave + c16, L - 1)) * rs;
+  const int t2 = tid & 127;
+  const bf16_t* src = wave < 2 ? kb : vb;
+  uint4 la[8], lt[8];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      lk[kk] = ld16(kb + kr + 32 * kk + 8 * r4);
-      lv[kk] = ld16(vb + kr + 32 * kk + 8 * r4);
-    }
-    const int h = wave >> 1;
+  for (int i = 0; i < 8; ++i) {
+    const int x = 128 * i + t2;
+    la[i] = ld16(src + size_t(min(kBlock * blk + (x >> 4), L - 1)) * rs + 8 * (x & 15));
+  }
+  if (wave >= 2) {
+    const int m = t2 >> 5, gh = (t2 >> 4) & 1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int key = 32 * h + 16 * (u >> 2) + 4 * r4 + (u & 3);
-      lt[u] = ld16(kb + size_t(min(kBlock * blk + key, L - 1)) * rs + 8 * c16);
+      const int key = 16 * m + 8 * (u >> 2) + 4 * gh + (u & 3);
+      lt[u] = ld16(kb + size_t(min(kBlock * blk + key, L - 1)) * rs + 8 * (t2 & 15));
     }
   }
-  __syncthreads();  // n_list = 0 seen by every wave
-  scan_rows(sm, indices, k_sel, kv_heads, kv, q0, r_lo, r_first, r_hi, blk);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    sm.kop[4 * wave + kk][lane] = lk[kk];
-    sm.vop[4 * wave + kk][lane] = lv[kk];
-  }
+  for (int i = tid; i < n_list; i += 256) sm.list[i] = lcode[U.u.base + start + i];
   {
-    const int h = wave >> 1, n0 = 4 * (wave & 1);
+    uint4(*dst)[8][64] = wave < 2 ? sm.kop : sm.vop;
 #pragma unroll
-    for (int n = n0; n < n0 + 4; ++n) {
+    for (int i = 0; i < 8; ++i) {
+      const int x = 128 * i + t2, key = x >> 4, pc = x & 15;
+      dst[key >> 5][pc & 7][(key & 31) + 32 * (pc >> 3)] = la[i];
+    }
+  }
+  if (wave >= 2) {
+    const int m = t2 >> 5, gh = (t2 >> 4) & 1, db = t2 & 15;
+    const int n = db >> 2, i2 = (db >> 1) & 1, gp = db & 1;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
       uint32_t w[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const uint32_t a = (&lt[2 * x].x)[n >> 1], c = (&lt[2 * x + 1].x)[n >> 1];
-        w[x] = (n & 1) ? (a >> 16) | (c & 0xFFFF0000u) : (a & 0xFFFFu) | (c << 16);
+        const uint32_t a = (&lt[2 * x].x)[c >> 1], b2 = (&lt[2 * x + 1].x)[c >> 1];
+        w[x] = (c & 1) ? (a >> 16) | (b2 & 0xFFFF0000u) : (a & 0xFFFFu) | (b2 << 16);
       }
-      sm.ktop[8 * h + n][lane] = make_uint4(w[0], w[1], w[2], w[3]);
+      const int rho = 8 * (2 * i2 + (c >> 2)) + 4 * gp + (c & 3);
+      sm.ktop[n][m][rho + 32 * gh] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
   __syncthreads();
-  const int n_list = sm.n_list;
   const int n_tiles = (n_list + E - 1) / E;
   if (wave >= n_tiles) return;  // no barrier below
 
-  const int ent = c16 / G, hg = c16 % G;
-  const int key0 = kBlock * blk + 4 * r4;
+  const int ent = c32 / G, hg = c32 % G;
+  const int key0 = kBlock * blk + 4 * g;  // key of score j of half x: key0 + 32 x + 8 (j / 4) + j % 4
   const int last_key = kBlock * blk + kBlock - 1;
-  bf16_t* stg = sm.stage[wave];
+  // chunk bases (uniform) and per-lane byte offsets below them (32 bits)
+  const size_t row0 = size_t(q0 + r_lo);
+  const char* qbase = reinterpret_cast<const char*>(q + row0 * heads * D);
+  const char* dbase = reinterpret_cast<const char*>(dout + row0 * heads * D);
+  const float* lbase = lse + row0 * heads + kv * G + hg;
+  const float* ebase = delta + row0 * heads + kv * G + hg;
+  char* pbase = reinterpret_cast<char*>(pq + row0 * k_sel * heads * D);
+  const uint32_t q_lane = uint32_t(((kv * G + hg) * D + 64 * g) * 2);
+  const uint32_t p_lane = uint32_t((kv * G * D + 16 * hg + 8 * g) * 2);
+
+  // a slot past the list repeats the last entry (same values, same addresses),
+  // so the stores need no condition
   struct Tile {
-    int t;
+    int code, t;
     float lse2, dlt;
-    uint4 q[4], d[4];
+    uint4 q[8], d[8];
   };
-  // tiles past the wave's last are clamped to the last one (no branch around the
-  // prefetch); a slot past the list repeats the last entry and stores nothing
   auto fetch = [&](int tile, Tile& T) {
     tile = min(tile, n_tiles - 1);
-    const int li = tile * E + ent;
-    const int code = sm.list[li < n_list ? li : n_list - 1];
-    T.t = off + r_lo + (code >> 6);
-    const size_t hr = size_t(q0 + r_lo + (code >> 6)) * heads + kv * G + hg;
+    T.code = sm.list[min(tile * E + ent, n_list - 1)];
+    const uint32_t rc = uint32_t(T.code >> 6);
+    T.t = off + r_lo + int(rc);
+    const uint32_t o = rc * uint32_t(heads * D * 2) + q_lane;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      T.q[kk] = ld16(q + hr * D + 32 * kk + 8 * r4);
-      T.d[kk] = ld16(dout + hr * D + 32 * kk + 8 * r4);
+    for (int s = 0; s < 8; ++s) {
+      T.q[s] = ld16(qbase + o + 16 * s);
+      T.d[s] = ld16(dbase + o + 16 * s);
     }
-    T.lse2 = lse[hr] * kLog2e;
-    T.dlt = delta[hr];
+    T.lse2 = lbase[rc * heads] * kLog2e;
+    T.dlt = ebase[rc * heads];
   };
-  auto compute = [&](int tile, const Tile& T) {
-    f32x4_t sacc[4], dpacc[4];
+  auto step = [&](int tile, Tile& T) {
+    asm volatile("" ::: "memory");  // the operands are read from LDS per tile
+    f32x16_t sacc[2], dacc[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      dpacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < 2; ++x) {
+      sacc[x] = f32x16_t{};
+      dacc[x] = f32x16_t{};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        sacc[s] = mfma32(sm.kop[4 * s + kk][lane], T.q[kk], sacc[s]);
-        dpacc[s] = mfma32(sm.vop[4 * s + kk][lane], T.d[kk], dpacc[s]);
+      for (int s = 0; s < 8; ++s) {
+        sacc[x] = mfma32x32(sm.kop[x][s][lane], T.q[s], sacc[x]);
+        dacc[x] = mfma32x32(sm.vop[x][s][lane], T.d[s], dacc[x]);
       }
     }
-    const bool masked = __any(T.t < last_key);  // the row's own block: keys past t
-    float ds[4][4];
+    const int code = T.code, t = T.t;
+    const float lse2 = T.lse2, dlt = T.dlt;
+    fetch(tile + 4, T);
+    const bool masked = __any(t < last_key);  // the row's own block: keys past t
+    const int rel = t - key0;
+    uint4 db[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int m = 0; m < 4; ++m) {
+      float ds[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = fast_exp2(fmaf(sacc[s][e], scale_log2, -T.lse2));
-        ds[s][e] = p * (dpacc[s][e] - T.dlt);
+      for (int u = 0; u < 8; ++u) {
+        const int j = 8 * (m & 1) + u;
+        const float p = fast_exp2(fmaf(sacc[m >> 1][j], scale_log2, -lse2));
+        ds[u] = p * (dacc[m >> 1][j] - dlt);
       }
-    if (masked) {
+      if (masked) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key0 + 16 * s + e > T.t) ds[s][e] = 0.f;
-    }
-    f32x4_t acc[8];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 db = make_uint4(pack2(ds[2 * h][0], ds[2 * h][1]), pack2(ds[2 * h][2], ds[2 * h][3]),
-                                  pack2(ds[2 * h + 1][0], ds[2 * h + 1][1]),
-                                  pack2(ds[2 * h + 1][2], ds[2 * h + 1][3]));
-#pragma unroll
-      for (int n = 0; n < 8; ++n) acc[n] = mfma32(sm.ktop[8 * h + n][lane], db, acc[n]);
-    }
-    // dq^T rows -> this wave's stage, then 16 contiguous bytes per lane out
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      *reinterpret_cast<uint4*>(&stg[c16 * kLdsRow + 32 * r4 + 8 * e]) =
-          make_uint4(pack2(acc[0][e], acc[1][e]), pack2(acc[2][e], acc[3][e]),
-                     pack2(acc[4][e], acc[5][e]), pack2(acc[6][e], acc[7][e]));
-    __builtin_amdgcn_wave_barrier();  // LDS runs a wave's accesses in order
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int vq = 4 * i + r4;
-      const int li = tile * E + vq / G;
-      const uint4 x = *reinterpret_cast<const uint4*>(&stg[vq * kLdsRow + 8 * c16]);
-      if (li < n_list) {
-        const int code = sm.list[li];
-        const size_t slot = (size_t(q0 + r_lo + (code >> 6)) * k_sel + (code & 63)) * heads + kv * G + vq % G;
-        stream_store(pq + slot * D + 8 * c16, x);
+        for (int u = 0; u < 8; ++u)
+          if (16 * m + 8 * (u >> 2) + (u & 3) > rel) ds[u] = 0.f;
       }
+      db[m] = make_uint4(pack2(ds[0], ds[1]), pack2(ds[2], ds[3]), pack2(ds[4], ds[5]), pack2(ds[6], ds[7]));
     }
-    __builtin_amdgcn_wave_barrier();
+    f32x16_t acc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      acc[n] = f32x16_t{};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[n] = mfma32x32(sm.ktop[n][m][lane], db[m], acc[n]);
+    }
+    const uint32_t slot = uint32_t(code >> 6) * uint32_t(k_sel) + uint32_t(code & 63);
+    char* pp = pbase + (slot * uint32_t(heads * D * 2) + p_lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x16_t& a = acc[i >> 1];
+      const int j = 8 * (i & 1);
+      stream_store(reinterpret_cast<bf16_t*>(pp + i * 32 * G),
+                   make_uint4(pack2(a[j], a[j + 1]), pack2(a[j + 2], a[j + 3]),
+                              pack2(a[j + 4], a[j + 5]), pack2(a[j + 6], a[j + 7])));
+    }
   };
-  Tile A, B;
-  fetch(wave, A);
-  for (int tile = wave; tile < n_tiles; tile += 8) {
-    fetch(tile + 4, B);
-    compute(tile, A);
-    if (tile + 4 >= n_tiles) break;
-    fetch(tile + 8, A);
-    compute(tile + 4, B);
-  }
+  Tile T;
+  fetch(wave, T);
+  for (int tile = wave; tile < n_tiles; tile += 4) step(tile, T);
 }
 
 // dq[row, head] (+)= scale * (sum of the partial dq of the row's valid places);
-// 16 threads per query vector (row * heads + head), 8 dims each.
+// 16 threads per query vector (row * heads + head), 8 dims each (lane sub: dims
+// 8 sub .. +7, in the partial output layout).
 __global__ __launch_bounds__(256) void block_dq_sum_kernel(
     const bf16_t* __restrict__ pq, const int* __restrict__ indices, int k_sel,
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int heads,
@@ -740,7 +791,7 @@ __global__ __launch_bounds__(256) void block_dq_sum_kernel(
   const bool in = qv < n_qv;
   const long qc = in ? qv : n_qv - 1;
   const int row = int(qc / heads), head = int(qc % heads);
-  const int kv = head / (heads / kv_heads);
+  const int G = heads / kv_heads, kv = head / G, hg = head % G;
   int lo = 0, hi = batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -749,7 +800,8 @@ __global__ __launch_bounds__(256) void block_dq_sum_kernel(
   const int t = (row - cu_q[lo]) + ((cu_k[lo + 1] - cu_k[lo]) - (cu_q[lo + 1] - cu_q[lo]));
   const int* ids = indices + (size_t(row) * kv_heads + kv) * k_sel;
   const unsigned long long valid = valid_places(ids, k_sel, t, sub, lane & 48);
-  const size_t base = size_t(row) * k_sel * heads + head;
+  const size_t pbase = (size_t(row) * k_sel * heads + size_t(kv) * G) * kHeadDim +
+                       (sub >> 1) * (16 * G) + 16 * hg + 8 * (sub & 1);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < k_sel; p0 += kMergeBatch) {
     uint4 x[kMergeBatch];
@@ -757,8 +809,7 @@ __global__ __launch_bounds__(256) void block_dq_sum_kernel(
     for (int u = 0; u < kMergeBatch; ++u) {
       const int p = p0 + u;
       const bool ok = p < k_sel && ((valid >> p) & 1ull);
-      x[u] = ok ? stream_load(pq + (base + size_t(p) * heads) * kHeadDim + 8 * sub)
-                : make_uint4(0u, 0u, 0u, 0u);
+      x[u] = ok ? stream_load(pq + pbase + size_t(p) * heads * kHeadDim) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
@@ -783,60 +834,90 @@ __global__ __launch_bounds__(256) void block_dq_sum_kernel(
 }
 
 template <int G>
-hipError_t launch_dq_g(const SelectedBwdArgs& a, int n_chunk, unsigned n_wg, hipStream_t s) {
+hipError_t launch_dq_g(const SelectedBwdArgs& a, const uint16_t* lcode, const int2* lhead,
+                       int n_chunk, unsigned n_wg, hipStream_t s) {
   return launch_kernel(kKindBwdQ, block_dq_partial_kernel<G>, dim3(n_wg), dim3(256), s, a.q, a.k,
-                       a.v, a.dout, a.lse, static_cast<const float*>(a.delta), a.indices, a.k_sel,
-                       a.cu_q, a.cu_k, a.kv_heads, a.nb_max, n_chunk, a.scale * kLog2eHost,
-                       a.dq_part);
+                       a.v, a.dout, a.lse, static_cast<const float*>(a.delta), lcode, lhead,
+                       a.k_sel, a.cu_q, a.cu_k, a.kv_heads, a.nb_max, n_chunk, a.rows_total,
+                       a.scale * kLog2eHost, a.dq_part);
 }
 
+// The launch arguments of the partial kernel.
+struct PartialArgs {
+  const bf16_t *q, *k, *v;
+  const uint16_t* lcode;
+  const int2* lhead;
+  int k_sel;
+  const float* cis;
+  const int *cu_q, *cu_k;
+  int kv_heads, nb_max, n_chunk, rows_total;
+  float scale_log2;
+  bf16_t* po;
+  float2* pml;
+};
+
 template <int G, bool CIS>
-hipError_t launch_partial_g(const void* q, const void* k, const void* v, const int* indices,
-                            int k_sel, const float* cis, const int* cu_q, const int* cu_k,
-                            int kv_heads, int nb_max, int n_chunk, unsigned n_wg, float sl2,
-                            bf16_t* po, float2* pml, hipStream_t s) {
-  return launch_kernel(kKindAttn, block_partial_kernel<G, CIS>, dim3(n_wg), dim3(256), s,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), indices, k_sel, cis, cu_q, cu_k, kv_heads,
-                       nb_max, n_chunk, sl2, po, pml);
+hipError_t launch_partial_g(const PartialArgs& a, unsigned n_wg, hipStream_t s) {
+  return launch_kernel(kKindAttn, block_partial_kernel<G, CIS>, dim3(n_wg), dim3(256), s, a.q,
+                       a.k, a.v, a.lcode, a.lhead, a.k_sel, a.cis, a.cu_q, a.cu_k, a.kv_heads,
+                       a.nb_max, a.n_chunk, a.rows_total, a.scale_log2, a.po, a.pml);
 }
 
 template <bool CIS>
-hipError_t launch_partial_c(int G, const void* q, const void* k, const void* v, const int* idx,
-                            int k_sel, const float* cis, const int* cu_q, const int* cu_k,
-                            int kvh, int nb_max, int n_chunk, unsigned n_wg, float sl2,
-                            bf16_t* po, float2* pml, hipStream_t s) {
+hipError_t launch_partial_c(int G, const PartialArgs& a, unsigned n_wg, hipStream_t s) {
   switch (G) {
-    case 1: return launch_partial_g<1, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
-    case 2: return launch_partial_g<2, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
-    case 4: return launch_partial_g<4, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
-    case 8: return launch_partial_g<8, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
-    case 16: return launch_partial_g<16, CIS>(q, k, v, idx, k_sel, cis, cu_q, cu_k, kvh, nb_max, n_chunk, n_wg, sl2, po, pml, s);
+    case 1: return launch_partial_g<1, CIS>(a, n_wg, s);
+    case 2: return launch_partial_g<2, CIS>(a, n_wg, s);
+    case 4: return launch_partial_g<4, CIS>(a, n_wg, s);
+    case 8: return launch_partial_g<8, CIS>(a, n_wg, s);
+    case 16: return launch_partial_g<16, CIS>(a, n_wg, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t po_bytes(int rows_total, int heads, int k_sel) {
-  return (size_t(rows_total) * heads * k_sel * kHeadDim * sizeof(uint16_t) + 255) & ~size_t(255);
+  return round256(size_t(rows_total) * heads * k_sel * kHeadDim * sizeof(uint16_t));
+}
+// the block lists: codes (2 bytes) and heads (8 bytes) per (row, KV head, place)
+size_t list_code_bytes(int rows_total, int kv_heads, int k_sel) {
+  return round256(size_t(rows_total) * kv_heads * k_sel * sizeof(uint16_t));
+}
+size_t list_bytes(int rows_total, int kv_heads, int k_sel) {
+  return list_code_bytes(rows_total, kv_heads, k_sel) +
+         round256(size_t(rows_total) * kv_heads * k_sel * sizeof(int2));
+}
+
+// Build the block lists of every (sequence, KV head, row chunk) into `lists`.
+hipError_t launch_lists(int kind, const int* indices, int k_sel, const int* cu_q, const int* cu_k,
+                        int batch, int kv_heads, int nb_max, int n_chunk, int rows_total,
+                        void* lists, uint16_t*& lcode, int2*& lhead, hipStream_t s) {
+  lcode = static_cast<uint16_t*>(lists);
+  lhead = reinterpret_cast<int2*>(static_cast<char*>(lists) + list_code_bytes(rows_total, kv_heads, k_sel));
+  return launch_kernel(kind, block_list_kernel, dim3(unsigned(n_chunk), unsigned(kv_heads), unsigned(batch)),
+                       dim3(256), s, indices, k_sel, cu_q, cu_k, kv_heads, nb_max, rows_total,
+                       lcode, lhead);
 }
 
 }  // namespace
 
-size_t block_attn_ws_bytes(int rows_total, int heads, int k_sel) {
-  if (rows_total <= 0 || heads <= 0 || k_sel <= 0) return 0;
+size_t block_attn_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel) {
+  if (rows_total <= 0 || heads <= 0 || kv_heads <= 0 || k_sel <= 0) return 0;
   return po_bytes(rows_total, heads, k_sel) +
-         ((size_t(rows_total) * heads * k_sel * sizeof(float2) + 255) & ~size_t(255));
+         round256(size_t(rows_total) * heads * k_sel * sizeof(float2)) +
+         list_bytes(rows_total, kv_heads, k_sel);
 }
 
 bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k,
                           int k_sel) {
   const long long nb = (max_seqlen_k + kBlock - 1) / kBlock;
   const long long nc = (max_seqlen_k + kScanRows - 1) / kScanRows;
-  // every grid dimension holds fewer than 2^32 work-items, and the partial
-  // states of one row chunk span fewer than 2^32 bytes (32-bit offsets)
+  // every grid dimension holds fewer than 2^32 work-items, the partial states of
+  // one row chunk span fewer than 2^32 bytes (32-bit offsets), and a
+  // sequence's blocks fit the list kernel's table
   return (long long)batch * kv_heads * nb * nc * 256 <= UINT_MAX &&
          (long long)rows_total * heads * 16 <= UINT_MAX &&
-         (long long)kScanRows * k_sel * heads * kHeadDim * 2 <= UINT_MAX;
+         (long long)kScanRows * k_sel * heads * kHeadDim * 2 <= UINT_MAX && nb <= kListMaxBlocks;
 }
 
 hipError_t launch_block_attn(const void* q, const void* k, const void* v, const int* indices,
@@ -852,11 +933,22 @@ hipError_t launch_block_attn(const void* q, const void* k, const void* v, const 
   const int nb_max = (max_seqlen_k + kBlock - 1) / kBlock;
   const int n_chunk = (max_seqlen_k + kScanRows - 1) / kScanRows;
   const unsigned n_wg = unsigned(batch) * kv_heads * n_chunk * nb_max;
-  bf16_t* po = static_cast<bf16_t*>(ws);
-  float2* pml = reinterpret_cast<float2*>(static_cast<char*>(ws) + po_bytes(rows_total, heads, k_sel));
-  hipError_t e = cis != nullptr
-                     ? launch_partial_c<true>(G, q, k, v, indices, k_sel, cis, cu_q, cu_k, kv_heads, nb_max, n_chunk, n_wg, scale_log2, po, pml, s)
-                     : launch_partial_c<false>(G, q, k, v, indices, k_sel, cis, cu_q, cu_k, kv_heads, nb_max, n_chunk, n_wg, scale_log2, po, pml, s);
+  char* w = static_cast<char*>(ws);
+  bf16_t* po = reinterpret_cast<bf16_t*>(w);
+  w += po_bytes(rows_total, heads, k_sel);
+  float2* pml = reinterpret_cast<float2*>(w);
+  w += round256(size_t(rows_total) * heads * k_sel * sizeof(float2));
+  PartialArgs a{static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                static_cast<const bf16_t*>(v), nullptr, nullptr, k_sel, cis, cu_q, cu_k,
+                kv_heads, nb_max, n_chunk, rows_total, scale_log2, po, pml};
+  uint16_t* lcode;
+  int2* lhead;
+  hipError_t e = launch_lists(kKindBlockLists, indices, k_sel, cu_q, cu_k, batch, kv_heads, nb_max,
+                              n_chunk, rows_total, w, lcode, lhead, s);
+  if (e != hipSuccess) return e;
+  a.lcode = lcode;
+  a.lhead = lhead;
+  e = cis != nullptr ? launch_partial_c<true>(G, a, n_wg, s) : launch_partial_c<false>(G, a, n_wg, s);
   if (e != hipSuccess) return e;
   const long n_qv = long(rows_total) * heads;
   return launch_kernel(kKindCombine, block_merge_kernel, dim3(unsigned((n_qv + 15) / 16)),
@@ -865,9 +957,9 @@ hipError_t launch_block_attn(const void* q, const void* k, const void* v, const 
                        kv_heads, n_qv, static_cast<bf16_t*>(out), out_f32, lse);
 }
 
-size_t block_dq_ws_bytes(int rows_total, int heads, int k_sel) {
-  if (rows_total <= 0 || heads <= 0 || k_sel <= 0) return 0;
-  return po_bytes(rows_total, heads, k_sel);
+size_t block_dq_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel) {
+  if (rows_total <= 0 || heads <= 0 || kv_heads <= 0 || k_sel <= 0) return 0;
+  return po_bytes(rows_total, heads, k_sel) + list_bytes(rows_total, kv_heads, k_sel);
 }
 
 hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s) {
@@ -878,13 +970,19 @@ hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s) {
   const int G = a.heads / a.kv_heads;
   const int n_chunk = (a.max_seqlen_k + kScanRows - 1) / kScanRows;
   const unsigned n_wg = unsigned(a.batch) * a.kv_heads * n_chunk * a.nb_max;
-  hipError_t e;
+  uint16_t* lcode;
+  int2* lhead;
+  hipError_t e = launch_lists(kKindBwdLists, a.indices, a.k_sel, a.cu_q, a.cu_k, a.batch,
+                              a.kv_heads, a.nb_max, n_chunk, a.rows_total,
+                              reinterpret_cast<char*>(a.dq_part) + po_bytes(a.rows_total, a.heads, a.k_sel),
+                              lcode, lhead, s);
+  if (e != hipSuccess) return e;
   switch (G) {
-    case 1: e = launch_dq_g<1>(a, n_chunk, n_wg, s); break;
-    case 2: e = launch_dq_g<2>(a, n_chunk, n_wg, s); break;
-    case 4: e = launch_dq_g<4>(a, n_chunk, n_wg, s); break;
-    case 8: e = launch_dq_g<8>(a, n_chunk, n_wg, s); break;
-    case 16: e = launch_dq_g<16>(a, n_chunk, n_wg, s); break;
+    case 1: e = launch_dq_g<1>(a, lcode, lhead, n_chunk, n_wg, s); break;
+    case 2: e = launch_dq_g<2>(a, lcode, lhead, n_chunk, n_wg, s); break;
+    case 4: e = launch_dq_g<4>(a, lcode, lhead, n_chunk, n_wg, s); break;
+    case 8: e = launch_dq_g<8>(a, lcode, lhead, n_chunk, n_wg, s); break;
+    case 16: e = launch_dq_g<16>(a, lcode, lhead, n_chunk, n_wg, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

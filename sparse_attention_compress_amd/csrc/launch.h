@@ -53,7 +53,8 @@ enum KernelKind {
   kKindBwdKV = 11,    // selected-attention backward: dk and dv
   kKindBwdLists = 12, // selected-attention backward: delta and the per-block row lists
   kKindBwdQMerge = 13, // selected-attention backward, key-block dq: the sum of its partial states
-  kKindCount = 14
+  kKindBlockLists = 14, // key-block selected attention: the per-chunk block lists
+  kKindCount = 15
 };
 
 // One armed (start, stop) event pair per kernel kind, per host thread.
@@ -145,7 +146,7 @@ hipError_t launch_selected_attn(const void* q, const void* k, const void* v, int
 // place) in `ws` (block_attn_ws_bytes), then their merge.  Writes out (bf16) or
 // out_f32 when given, and lse when given.  block_attn_grid_fits: the launch
 // shapes stay within the grid limits and the 32-bit offsets of the kernels.
-size_t block_attn_ws_bytes(int rows_total, int heads, int k_sel);
+size_t block_attn_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel);
 bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k,
                           int k_sel);
 hipError_t launch_block_attn(const void* q, const void* k, const void* v, const int* indices,
@@ -270,7 +271,7 @@ void selected_bwd_ws_carve(void* base, SelectedBwdArgs& a);
 hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s);
 // Selected-attention dq, key-block stationary (attn_blocks.hip): partial dq per
 // (row, place, head) in a.dq_part, then their sum into a.dq.
-size_t block_dq_ws_bytes(int rows_total, int heads, int k_sel);
+size_t block_dq_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel);
 hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s);
 // The matrix-core kernels: dk/dv of every key set, dq of the window and
 // compressed key sets (bwd_mfma.hip).

@@ -173,8 +173,9 @@ def test_prefill_step_checks():
     # lse (fp32) + o_cmp and o_sel (bf16 rows) + block scores + indices
     assert least >= 1000 * 64 * 4 + 2 * 1000 * 64 * 128 * 2 + 1000 * 4 * 16 * 4 + 1000 * 4 * 16 * 4
     # the key-block selected branch adds its partial states (256 B of bf16 output
-    # and 8 B of (max, sum) per (row, head, place)) and its float32 rows
-    assert need - least == 1000 * 64 * 16 * 264 + 1000 * 64 * 128 * 4
+    # and 8 B of (max, sum) per (row, head, place)), its float32 rows and its
+    # block lists (2 B of row code and 8 B of list head per (row, KV head, place))
+    assert need - least == 1000 * 64 * 16 * 264 + 1000 * 64 * 128 * 4 + 1000 * 4 * 16 * 10
     assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), least - 1, None) == 3
     p.topk = 65                                          # above the per-row staging limit
     assert nsa.lib().nsa_prefill_step(ctypes.byref(p), ctypes.c_void_p(0x1000), need, None) == 2
@@ -261,7 +262,8 @@ def test_selected_bwd_checks():
     need = nsa.selected_attn_bwd_workspace_size_min(2, 100, 4096, 16, 2, 16)
     assert 0 < need < full
     # the key-block dq adds its partial states: 256 B of bf16 per (row, head, place)
-    assert full - ((need + 255) // 256 * 256) == 100 * 16 * 16 * 256
+    # the key-block dq's partial states (bf16) and its block lists
+    assert full - ((need + 255) // 256 * 256) == 100 * 16 * 16 * 256 + 100 * 2 * 16 * 10
     assert nsa.selected_attn_bwd_workspace_size(0, 100, 4096, 16, 2, 16) == 0
     assert nsa.selected_attn_bwd_workspace_size_min(0, 100, 4096, 16, 2, 16) == 0
 

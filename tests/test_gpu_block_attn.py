@@ -159,7 +159,8 @@ def test_block_path_every_row_and_deterministic():
 def test_block_path_workspace_too_small():
     d = _inputs([200], [200], 16, 2, 16, SEED + 6)
     need = nsa.selected_attn_workspace_size(200, 16, 2, 128, 16, False)
-    assert need == 200 * 16 * 16 * (256 + 8)
+    # partial states (264 B per (row, head, place)) and block lists (10 B per (row, KV head, place))
+    assert need == 200 * 16 * 16 * (256 + 8) + 200 * 2 * 16 * 10
     ws = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
     out = torch.zeros_like(d["q"])
     with pytest.raises(nsa.NsaError) as e:

@@ -15,25 +15,27 @@
 //   rows in registers as MFMA B operands) and walks the query tiles that see the
 //   block (a row list for the selected branch, one contiguous range of
 //   positions for the window and compressed branches).  Each tile's q and dO
-//   rows are staged in LDS once for the four waves, both as rows and transposed.
+//   rows are staged in LDS once for the four waves.
 //   Per tile and wave: S = Q K^T and dP = dO V^T on four v_mfma_f32_16x16x32_bf16
 //   each; their accumulators hold (query 4r4+e, key c16), which is exactly the B
 //   operand of the 16x16x16 tiles dV^T += dO^T P and dK^T += Q^T dS (contraction
 //   over the 16 query vectors), so P and dS go to the matrix cores as packed
-//   registers; dO^T and Q^T come from the transposed LDS copy.
+//   registers; dO^T and Q^T are read from the staged rows with gfx950's
+//   transposing LDS read (ds_read_b64_tr_b16).
 // bwd_dq_mfma_kernel -- query-tile stationary (window and compressed branches).
 //   A workgroup holds four query tiles (one per wave; consecutive rows, which
 //   see nearly the same keys) with Q and dO in registers as B operands, and
 //   walks the 64-key blocks they see, each staged in LDS once for the four
-//   waves (K rows, K transposed, V rows).  Per 16-key slice: S^T = K Q^T and
+//   waves (K rows, V rows).  Per 16-key slice: S^T = K Q^T and
 //   dP^T = V dO^T (accumulators (key 4r4+e, query c16)), then dQ^T += K^T dS^T
-//   with dS^T packed straight into the B operand.
+//   with dS^T packed straight into the B operand and K^T read transposed from
+//   the K rows.
 // bwd_dq_sel_mfma_kernel -- dq of the selected branch, one (row, KV head) per
 //   workgroup: the G heads are the tile's columns (columns past G masked), each
 //   listed block is staged in LDS once (K rows), wave w takes its keys
 //   16w .. 16w+15 (V rows straight into registers), and the four waves' dq^T
 //   are summed through LDS at the end.  K^T operands come from the staged rows
-//   as four 2-byte reads.
+//   through the transposing read.
 // Masked keys (outside the row's key set, or past the sequence) get p = 0.
 #include <algorithm>
 
@@ -50,19 +52,32 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kRowPad = kHeadDim + 8;  // bf16 per staged row (272 B: 16 rows on distinct banks)
-constexpr int kTPad = 16 + 4;          // bf16 per transposed row of a query tile
-constexpr int kKTPad = 64 + 8;         // bf16 per transposed row of a key block
-
-// Column swizzles of the transposed copies.  Their stores are 2-byte writes in
-// which the lanes of a wave hold rows 8 apart (one 16-byte chunk of a row each),
-// which padding alone maps onto a few banks (4- to 8-way conflicts); XORing the
-// column with a function of the row spreads them over the banks.  The XOR is in
-// units of 4 columns, so the 8-byte reads of 4 consecutive columns stay
-// contiguous, and stays inside the row.
-__device__ __forceinline__ int qt_col(int row, int col) { return col ^ (4 * ((row >> 5) & 3)); }
-__device__ __forceinline__ int kt_col(int row, int col) { return col ^ (4 * ((row >> 3) & 15)); }
 constexpr int kMfmaRowsPerChunk = 512; // rows of a key block's list one dk/dv workgroup takes
+
+// Unpadded 256-byte rows whose sixteen 16-byte chunks are XOR-swizzled by
+// swz(row) = 2 (row % 8) + (row / 8) % 2.  The row reads of the 16x16x32 A
+// operands (16 rows, the same chunk of each) and the transposing reads below
+// (16 lanes: 4 rows x 32 contiguous bytes; 32 lanes: 8 rows) both then fall on
+// distinct banks.  tile_at: the element offset of logical chunk c of a row.
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
+__device__ __forceinline__ int tile_at(int row, int c) { return row * kHeadDim + 8 * (c ^ swz(row)); }
+
+// The 16x16x16 A operand of X^T for dims 16 n .. 16 n + 15 and rows r0 .. r0 + 15
+// of a swizzled row tile X (query vectors or keys): lane (c16, r4) gets
+// X[r0 + 4 r4 + j][16 n + c16], j = 0..3, through one ds_read_b64_tr_b16.
+// Within 16 lanes that read hands lane i, as its element j, element i % 4 of
+// the 8 bytes at the address of lane 4 j + i / 4; so lane k addresses row
+// r0 + 4 r4 + k / 4 at dims 16 n + 4 (k % 4).
+typedef short s16x4_t_ __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr(const bf16_t* tile, int r0, int n) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
+  const int row = r0 + 4 * r4 + (c16 >> 2);
+  const int d = 16 * n + 4 * (c16 & 3);
+  const bf16_t* p = tile + tile_at(row, d >> 3) + (d & 7);
+  const s16x4_t_ x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t_*)(p));
+  return __builtin_bit_cast(uint2, x);
+}
 
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -78,14 +93,12 @@ __device__ __forceinline__ uint2 pack4(const float x[4]) {
   return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
-// One staged query tile: 16 query vectors' q and dO rows, both as rows and
-// transposed (dim-major), with their log2 normalisers, deltas and positions
-// (-1: no query vector in that slot).
+// One staged query tile: 16 query vectors' q and dO rows (swizzled rows; the
+// transposed operands are read from them with read_tr), with their log2
+// normalisers, deltas and positions (-1: no query vector in that slot).
 struct QTileLds {
-  bf16_t q[16 * kRowPad];
-  bf16_t d[16 * kRowPad];
-  bf16_t qt[kHeadDim * kTPad];
-  bf16_t dt[kHeadDim * kTPad];
+  bf16_t q[16 * kHeadDim];
+  bf16_t d[16 * kHeadDim];
   float lse2[16];
   float delta[16];
   int t[16];
@@ -101,18 +114,8 @@ struct QTileRegs {
 
 __device__ __forceinline__ void stash_qtile(QTileLds& T, const QTileRegs& r) {
   const int tid = threadIdx.x, v = tid >> 4, c = tid & 15;
-  *reinterpret_cast<uint4*>(&T.q[v * kRowPad + 8 * c]) = r.q;
-  *reinterpret_cast<uint4*>(&T.d[v * kRowPad + 8 * c]) = r.d;
-  const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-  const uint32_t dw[4] = {r.d.x, r.d.y, r.d.z, r.d.w};
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int r0 = 8 * c + 2 * w, r1 = r0 + 1;
-    T.qt[r0 * kTPad + qt_col(r0, v)].bits = uint16_t(qw[w]);
-    T.qt[r1 * kTPad + qt_col(r1, v)].bits = uint16_t(qw[w] >> 16);
-    T.dt[r0 * kTPad + qt_col(r0, v)].bits = uint16_t(dw[w]);
-    T.dt[r1 * kTPad + qt_col(r1, v)].bits = uint16_t(dw[w] >> 16);
-  }
+  *reinterpret_cast<uint4*>(&T.q[tile_at(v, c)]) = r.q;
+  *reinterpret_cast<uint4*>(&T.d[tile_at(v, c)]) = r.d;
   if (tid < 16) {
     T.lse2[tid] = r.lse2;
     T.delta[tid] = r.delta;
@@ -206,8 +209,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
     f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s = mfma32(*reinterpret_cast<const uint4*>(&Tc.q[c16 * kRowPad + 32 * i + 8 * r4]), kb[i], s);
-      dp = mfma32(*reinterpret_cast<const uint4*>(&Tc.d[c16 * kRowPad + 32 * i + 8 * r4]), vb[i], dp);
+      s = mfma32(*reinterpret_cast<const uint4*>(&Tc.q[tile_at(c16, 4 * i + r4)]), kb[i], s);
+      dp = mfma32(*reinterpret_cast<const uint4*>(&Tc.d[tile_at(c16, 4 * i + r4)]), vb[i], dp);
     }
     float p[4], ds[4];
 #pragma unroll
@@ -220,9 +223,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
     const uint2 pb = pack4(p), dsb = pack4(ds);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int tr = 16 * dt + c16, tc = qt_col(tr, 4 * r4);
-      const uint2 dta = *reinterpret_cast<const uint2*>(&Tc.dt[tr * kTPad + tc]);
-      const uint2 qta = *reinterpret_cast<const uint2*>(&Tc.qt[tr * kTPad + tc]);
+      const uint2 dta = read_tr(Tc.d, 0, dt);
+      const uint2 qta = read_tr(Tc.q, 0, dt);
       accv[dt] = mfma16(dta, pb, accv[dt]);
       acck[dt] = mfma16(qta, dsb, acck[dt]);
     }
@@ -257,11 +259,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
   }
 }
 
-// One staged 64-key block for the dq kernel: K rows, K transposed, V rows.
+// One staged 64-key block for the dq kernel: K rows and V rows (swizzled rows;
+// K^T is read from the K rows with read_tr).
 struct KBlockLds {
-  bf16_t k[64 * kRowPad];
-  bf16_t kt[kHeadDim * kKTPad];
-  bf16_t v[64 * kRowPad];
+  bf16_t k[64 * kHeadDim];
+  bf16_t v[64 * kHeadDim];
 };
 
 // dq of four query tiles of one (sequence, KV head): grid (row group, kv head,
@@ -333,15 +335,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + kThreads * u, kr = c >> 4, ch = c & 15;
-      *reinterpret_cast<uint4*>(&S.k[kr * kRowPad + 8 * ch]) = pk[u];
-      *reinterpret_cast<uint4*>(&S.v[kr * kRowPad + 8 * ch]) = pv[u];
-      const uint32_t w4[4] = {pk[u].x, pk[u].y, pk[u].z, pk[u].w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int r0 = 8 * ch + 2 * w, r1 = r0 + 1;
-        S.kt[r0 * kKTPad + kt_col(r0, kr)].bits = uint16_t(w4[w]);
-        S.kt[r1 * kKTPad + kt_col(r1, kr)].bits = uint16_t(w4[w] >> 16);
-      }
+      *reinterpret_cast<uint4*>(&S.k[tile_at(kr, ch)]) = pk[u];
+      *reinterpret_cast<uint4*>(&S.v[tile_at(kr, ch)]) = pv[u];
     }
   };
 
@@ -357,8 +352,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
       f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        st = mfma32(*reinterpret_cast<const uint4*>(&S.k[(16 * sl + c16) * kRowPad + 32 * i + 8 * r4]), qb[i], st);
-        dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[(16 * sl + c16) * kRowPad + 32 * i + 8 * r4]), db[i], dpt);
+        st = mfma32(*reinterpret_cast<const uint4*>(&S.k[tile_at(16 * sl + c16, 4 * i + r4)]), qb[i], st);
+        dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[tile_at(16 * sl + c16, 4 * i + r4)]), db[i], dpt);
       }
       float dst[4];
 #pragma unroll
@@ -371,9 +366,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
       const uint2 dsb = pack4(dst);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int tr = 16 * dt + c16;
-        const uint2 kta = *reinterpret_cast<const uint2*>(&S.kt[tr * kKTPad + kt_col(tr, 16 * sl + 4 * r4)]);
-        acc[dt] = mfma16(kta, dsb, acc[dt]);
+        acc[dt] = mfma16(read_tr(S.k, 16 * sl, dt), dsb, acc[dt]);
       }
     }
   }
@@ -400,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int batch, int accumulate,
     int heads, int kv_heads, float scale_log2, float scale, float* __restrict__ dq) {
   constexpr int kRedPad = kHeadDim + 4;
-  __shared__ bf16_t Ks[64 * kRowPad];
+  __shared__ bf16_t Ks[64 * kHeadDim];  // swizzled rows
   __shared__ float red[4][16][kRedPad];
   __shared__ int ids_s[64];
   __shared__ int nv_s;
@@ -464,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + kThreads * u;
-      *reinterpret_cast<uint4*>(&Ks[(c >> 4) * kRowPad + 8 * (c & 15)]) = pk[u];
+      *reinterpret_cast<uint4*>(&Ks[tile_at(c >> 4, c & 15)]) = pk[u];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) vc[i] = pv[i];
@@ -474,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
     f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st = mfma32(*reinterpret_cast<const uint4*>(&Ks[(16 * wave + c16) * kRowPad + 32 * i + 8 * r4]), qb[i], st);
+      st = mfma32(*reinterpret_cast<const uint4*>(&Ks[tile_at(16 * wave + c16, 4 * i + r4)]), qb[i], st);
       dpt = mfma32(vc[i], db[i], dpt);
     }
     float ds[4];
@@ -485,14 +478,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
       ds[e] = pr * (dpt[e] - dlt);
     }
     const uint2 dsb = pack4(ds);
-    const bf16_t* kr = &Ks[(16 * wave + 4 * r4) * kRowPad + c16];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      // K^T[dim 16 dt + c16][keys 16 wave + 4 r4 .. +3]
-      const uint32_t k0 = kr[16 * dt].bits, k1 = kr[kRowPad + 16 * dt].bits;
-      const uint32_t k2 = kr[2 * kRowPad + 16 * dt].bits, k3 = kr[3 * kRowPad + 16 * dt].bits;
-      acc[dt] = mfma16(make_uint2(k0 | (k1 << 16), k2 | (k3 << 16)), dsb, acc[dt]);
-    }
+    for (int dt = 0; dt < 8; ++dt)  // K^T[dim 16 dt + c16][keys 16 wave + 4 r4 .. +3]
+      acc[dt] = mfma16(read_tr(Ks, 16 * wave, dt), dsb, acc[dt]);
   }
   // dq^T of the wave: (dim 16 dt + 4 r4 + e, head column c16); summed over the waves
 #pragma unroll

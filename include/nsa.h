@@ -268,12 +268,15 @@ nsa_status nsa_select_topk(const float* block_scores, int32_t* indices,
  *            float32 inputs): one workgroup per (row, KV head) gathers the
  *            row's blocks.  Given with at least
  *            nsa_selected_attn_workspace_size(..., decode=0) bytes
- *            (rows * heads * k_sel * 264 bytes, 16-byte aligned) and bf16
- *            inputs: key-block stationary -- one workgroup per (sequence, KV
- *            head, 64-key block, 1024 query rows) attends the rows listing
+ *            (rows * heads * k_sel * 264 + rows * kv_heads * k_sel * 10
+ *            bytes, 16-byte aligned) and bf16 inputs: key-block stationary --
+ *            the valid places of every (sequence, KV head, 1024 query rows)
+ *            are listed by block, then one workgroup per (sequence, KV head,
+ *            1024 query rows, listed 64-key block) attends the rows listing
  *            the block and writes their partial state (bf16 output, fp32 max
  *            and sum) at the row's place; a merge kernel combines each row's
- *            places.  This path also needs every L_b <= max_seqlen_k.  Between
+ *            places.  This path also needs every L_b <= max_seqlen_k and at
+ *            most 8192 blocks per sequence (else NSA_ERR_UNSUPPORTED).  Between
  *            0 and the queried size: NSA_ERR_WORKSPACE.  An id listed twice
  *            in one row counts once on this path and twice on the other (ids
  *            of a row must be unique either way).
@@ -314,9 +317,11 @@ nsa_status nsa_selected_attn_fwd(const void* q, const void* k, const void* v, ns
  *   workspace: device memory, 16-byte aligned.  With
  *   nsa_selected_attn_bwd_workspace_size(...) bytes dq is computed key-block
  *   stationary, as the forward given a workspace: per (sequence, KV head,
- *   64-key block, 1024 rows) the block's share of dq of every listing row is
- *   written as bf16 at (row, place, head) (rows * heads * k_sel * 256 bytes of
- *   the workspace), then the valid places of each (row, head) are summed in
+ *   listed 64-key block, 1024 rows) the block's share of dq of every listing
+ *   row is written as bf16 at (row, place, head) (rows * heads * k_sel * 256
+ *   bytes of the workspace, and rows * kv_heads * k_sel * 10 bytes for the
+ *   block lists; at most 8192 blocks per sequence, else dq runs row by row),
+ *   then the valid places of each (row, head) are summed in
  *   fp32.  Any size from nsa_selected_attn_bwd_workspace_size_min(...) up to
  *   that computes dq with one workgroup per (row, KV head).  Less:
  *   NSA_ERR_WORKSPACE.
@@ -635,9 +640,10 @@ typedef struct nsa_prefill_params {
  * Workspace: nsa_prefill_workspace_size(p) bytes (16-byte aligned) run the
  * selected branch key-block stationary (as nsa_selected_attn_fwd given a
  * workspace; the size includes its partial states, rows * heads * topk * 264
- * bytes, and its merged rows in float32 until the gated sum, rows * heads *
- * 512 bytes); any size from nsa_prefill_workspace_size_min(p) up to that runs
- * it row by row.  Less: NSA_ERR_WORKSPACE.
+ * bytes, its block lists, rows * kv_heads * topk * 10 bytes, and its merged
+ * rows in float32 until the gated sum, rows * heads * 512 bytes); any size
+ * from nsa_prefill_workspace_size_min(p) up to that, or more than 8192 blocks
+ * per sequence, runs it row by row.  Less: NSA_ERR_WORKSPACE.
  */
 size_t nsa_prefill_workspace_size(const nsa_prefill_params* p);
 size_t nsa_prefill_workspace_size_min(const nsa_prefill_params* p);

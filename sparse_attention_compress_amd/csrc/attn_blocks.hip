@@ -12,14 +12,18 @@
 // bytes come from L2 and the Infinity Cache, not from the matrix cores' reuse.
 // Here the roles are swapped:
 //
+// block_list_kernel -- one workgroup per (sequence, KV head, chunk of 1024
+//   query rows): the chunk's valid places grouped by block (a 16-bit code of
+//   row and place per place, and per listed block its first entry), counted
+//   and placed through an LDS table of the blocks.
 // block_partial_kernel -- one workgroup per (sequence, KV head, chunk of 1024
-//   query rows, 64-key block).  It builds the block's matrix-core operands
-//   once, in LDS (K in the A layout of S^T = K Q^T, V^T in the A layout of
-//   O^T = V^T P^T), scans the chunk's index rows for the rows that list the
-//   block (and at which place), and walks those rows in tiles of 16 query
-//   vectors (a query vector is one (row, head) pair: 16/G rows of G heads), one
-//   tile per wave at a time, so a tile costs its q rows in, 32
-//   v_mfma_f32_16x16x32_bf16, and its partial state out: the block's
+//   query rows, listed block of the chunk).  It builds the block's matrix-core
+//   operands once, in LDS, for 32x32x16 bf16 tiles (K in the A layout of
+//   S^T = K Q^T, V^T in the A layout of O^T = V^T P^T), takes the rows that
+//   list the block from the lists, and walks them in tiles of 32 query vectors
+//   (a query vector is one (row, head) pair: 32/G rows of G heads), one tile per
+//   wave at a time, so a tile costs its q rows in, 32
+//   v_mfma_f32_32x32x16_bf16, and its partial state out: the block's
 //   unnormalised output in bf16 plus (max, sum) in fp32, at the row's place.
 // block_merge_kernel -- per (row, head): the partial states of the row's valid
 //   places combined with the usual log-sum-exp weights.
@@ -53,8 +57,7 @@ __device__ __forceinline__ uint4 stream_load(const bf16_t* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
 
-constexpr int kScanRows = 1024;       // query rows one workgroup scans for its block
-constexpr int kLdsRow = kHeadDim + 8; // bf16 per staged K/V row (272 B)
+constexpr int kScanRows = 1024;       // query rows of one chunk (one list unit)
 constexpr int kMaxPlaces = 64;        // index places per row (place fits 6 bits)
 constexpr int kMergeBatch = 8;        // places whose loads the merge keeps in flight together
 

@@ -167,3 +167,24 @@ def test_block_path_workspace_too_small():
         nsa.nsa_selected_attn_fwd(d["q"], d["k"], d["v"], d["idx_t"], d["cu_k"], 200, out,
                                   cu_seqlens_q=d["cu_q"], workspace=ws)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("k_sel", [16, 64])
+def test_block_path_every_place_listed(k_sel):
+    """Single-row chunks whose k_sel ids are all distinct valid blocks: every
+    place of the chunk is listed under its own block, so the chunk's list has
+    no room for an end marker and the last listed block ends at the list's
+    end."""
+    lk, lq = [2048, 5000, 70], [1, 1, 1]
+    d = _inputs(lk, lq, 16, 2, k_sel, SEED + 7 + k_sel)
+    rng = np.random.default_rng(k_sel)
+    idx = np.full((3, 2, k_sel), -1, dtype=np.int32)
+    for r, t in enumerate([2047, 4999, 69]):
+        n_blk = t // 64 + 1
+        for g in range(2):
+            ids = rng.permutation(n_blk)[:k_sel]
+            idx[r, g, :len(ids)] = ids
+    d["idx"], d["idx_t"] = idx, torch.from_numpy(idx).to(DEV)
+    log(f"block path, every place listed, k_sel={k_sel}")
+    got, lse = _run(d, "blocks", False)
+    _check(f"blocks_full_list_k{k_sel}", d, [0, 1, 2], got, lse, False)

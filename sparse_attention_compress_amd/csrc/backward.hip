@@ -264,7 +264,7 @@ hipError_t launch_bwd_lists(const SelectedBwdArgs& a, hipStream_t s) {
   if (!(a.accumulate & 2)) {
     e = launch_kernel(kKindBwdLists, bwd_zero_kernel<MODE>, dim3(unsigned(n_slots)),
                       dim3(kBwdThreads), s, static_cast<const int*>(a.cnt), a.cu_q, a.cu_k,
-                      a.cu_kv, a.window, a.kv_heads, a.nb_max, mfma_bwd_rows_per_chunk(), a.dk,
+                      a.cu_kv, a.window, a.kv_heads, a.nb_max, mfma_bwd_rows_per_chunk(MODE), a.dk,
                       a.dv);
     if (e != hipSuccess) return e;
   }

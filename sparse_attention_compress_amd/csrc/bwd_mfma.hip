@@ -52,7 +52,11 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kMfmaRowsPerChunk = 512; // rows of a key block's list one dk/dv workgroup takes
+// Rows of a key block's list one dk/dv workgroup takes: the chunks of one block
+// add their sums with fp32 atomics, so the compressed branch, whose blocks are
+// seen by nearly every later row, takes longer chunks (fewer atomics); 512
+// elsewhere (2048 measured slower for the selected branch).
+constexpr int rows_per_chunk(int mode) { return mode == kBwdCompressed ? 2048 : 512; }
 
 // Unpadded 256-byte rows whose sixteen 16-byte chunks are XOR-swizzled by
 // swz(row) = 2 (row % 8) + (row / 8) % 2.  The row reads of the 16x16x32 A
@@ -146,10 +150,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
   int n, t_lo = 0, row_lo = 0;
   if constexpr (MODE == kBwdSelected) n = cnt[slot];
   else n = implicit_rows<MODE>(b, id, len, window, cu_q, cu_k, t_lo, row_lo);
-  const int e_begin = chunk * kMfmaRowsPerChunk;
+  constexpr int kRowsPerChunk = rows_per_chunk(MODE);
+  const int e_begin = chunk * kRowsPerChunk;
   if (chunk > 0 && e_begin >= n) return;   // uniform: no rows left for this chunk
   if (n == 0 && (accumulate & 2)) return;  // nothing to add
-  const int e_end = min(n, e_begin + kMfmaRowsPerChunk);
+  const int e_end = min(n, e_begin + kRowsPerChunk);
   const int first = MODE == kBwdSelected ? off[slot] : 0;
   auto entry = [&](int e) {
     if constexpr (MODE == kBwdSelected) return list[first + e];
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
   // lane (c16, r4) holds dims 16 dt + 4 r4 .. +3 of key c16 of the wave's slice
   if (!key_ok) return;
   const size_t o = (size_t(kstart + key) * kv_heads + g) * kHeadDim + 4 * r4;
-  const bool single = n <= kMfmaRowsPerChunk;
+  const bool single = n <= kRowsPerChunk;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     float4 kx = make_float4(scale * acck[dt][0], scale * acck[dt][1], scale * acck[dt][2],
@@ -503,7 +508,7 @@ hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
   const float scale_log2 = a.scale * kLog2eHost;
   const int max_rows = MODE == kBwdWindow ? std::min(a.max_seqlen_k, kBlock + a.window - 1)
                                           : a.max_seqlen_k;
-  const unsigned n_chunk = unsigned((max_rows + kMfmaRowsPerChunk - 1) / kMfmaRowsPerChunk);
+  const unsigned n_chunk = unsigned((max_rows + rows_per_chunk(MODE) - 1) / rows_per_chunk(MODE));
   hipError_t e = launch_kernel(kKindBwdKV, bwd_dkdv_mfma_kernel<G, MODE>,
                                dim3(unsigned(n_slots), std::max(1u, n_chunk)), dim3(kThreads), s,
                                a.q, a.k, a.v, a.dout, a.lse, static_cast<const float*>(a.delta),
@@ -542,7 +547,7 @@ hipError_t launch_mfma_mode(const SelectedBwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int mfma_bwd_rows_per_chunk() { return kMfmaRowsPerChunk; }
+int mfma_bwd_rows_per_chunk(int mode) { return rows_per_chunk(mode); }
 
 hipError_t launch_bwd_mfma(const SelectedBwdArgs& a, hipStream_t s) {
   switch (a.mode) {

@@ -276,7 +276,7 @@ hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s);
 // The matrix-core kernels: dk/dv of every key set, dq of the window and
 // compressed key sets (bwd_mfma.hip).
 hipError_t launch_bwd_mfma(const SelectedBwdArgs& a, hipStream_t s);
-int mfma_bwd_rows_per_chunk();
+int mfma_bwd_rows_per_chunk(int mode);  // rows of a block one dk/dv workgroup takes
 hipError_t launch_gates_bwd(const bf16_t* dout, const bf16_t* o_cmp, const bf16_t* o_sel,
                             const bf16_t* o_win, const float* gates, size_t n_rh, bf16_t* do_cmp,
                             bf16_t* do_sel, bf16_t* do_win, float* d_gates, hipStream_t s);

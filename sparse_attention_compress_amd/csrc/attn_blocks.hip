@@ -43,7 +43,6 @@ namespace nsa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -60,11 +59,6 @@ __device__ __forceinline__ uint4 stream_load(const bf16_t* p) {
 constexpr int kScanRows = 1024;       // query rows of one chunk (one list unit)
 constexpr int kMaxPlaces = 64;        // index places per row (place fits 6 bits)
 constexpr int kMergeBatch = 8;        // places whose loads the merge keeps in flight together
-
-__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   const bf16x2_t x = {(__bf16)lo, (__bf16)hi};

@@ -56,7 +56,7 @@ __device__ __forceinline__ uint4 stream_load(const bf16_t* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
 
-constexpr int kScanRows = 1024;       // query rows of one chunk (one list unit)
+constexpr int kChunkRows = 1024;       // query rows of one chunk (one list unit)
 constexpr int kMaxPlaces = 64;        // index places per row (place fits 6 bits)
 constexpr int kMergeBatch = 8;        // places whose loads the merge keeps in flight together
 
@@ -102,10 +102,10 @@ struct PartialLds {
   uint4 kop[2][8][64];
   uint4 vop[4][4][64];
   float cisw[kBlock];        // CIS of the block's keys (CIS mode)
-  uint16_t list[kScanRows];  // the block's list entries: (row in chunk << 6) | place
+  uint16_t list[kChunkRows];  // the block's list entries: (row in chunk << 6) | place
 };
 
-// The rows of one (sequence, KV head, chunk of kScanRows query rows) unit: its
+// The rows of one (sequence, KV head, chunk of kChunkRows query rows) unit: its
 // first packed query row q0 of the sequence, its rows r_lo .. r_hi - 1 of the
 // sequence (at positions off + r), the number of blocks they can list (reach),
 // and its entries of the block lists, base .. base + cap - 1 (k_sel per row, in
@@ -120,9 +120,9 @@ __device__ __forceinline__ bool chunk_rows(const int* __restrict__ cu_q, const i
   u.q0 = cu_q[b];
   const int lq = cu_q[b + 1] - u.q0;
   u.off = (cu_k[b + 1] - cu_k[b]) - lq;
-  u.r_lo = chunk * kScanRows;
+  u.r_lo = chunk * kChunkRows;
   if (u.r_lo >= lq) return false;
-  u.r_hi = min(lq, u.r_lo + kScanRows);
+  u.r_hi = min(lq, u.r_lo + kChunkRows);
   const int t_max = u.r_hi - 1 + u.off;
   u.reach = t_max >= 0 ? min(nb_max, t_max / kBlock + 1) : 0;
   u.cap = (u.r_hi - u.r_lo) * k_sel;
@@ -206,7 +206,7 @@ __device__ __forceinline__ unsigned long long valid_places(const int* __restrict
 
 // ----------------------------------------------------------------- block lists
 //
-// block_list_kernel -- one workgroup per (sequence, KV head, chunk of kScanRows
+// block_list_kernel -- one workgroup per (sequence, KV head, chunk of kChunkRows
 // query rows): the chunk's valid places (those valid_places admits, the places
 // the merge combines) grouped by block, through a table of the blocks in LDS.
 // In the unit's entries (ChunkRows::base ..): code[u] = (row in chunk << 6) |
@@ -611,7 +611,7 @@ struct DqLds {
   uint4 kop[2][8][64];   // K: A of S^T = K Q^T (PartialLds::kop layout)
   uint4 vop[2][8][64];   // V: A of dP^T = V dO^T (the same layout)
   uint4 ktop[4][4][64];  // K^T: A of dq^T += K^T dS^T (PartialLds::vop layout)
-  uint16_t list[kScanRows];
+  uint16_t list[kChunkRows];
 };
 
 template <int G>
@@ -908,13 +908,13 @@ size_t block_attn_ws_bytes(int rows_total, int heads, int kv_heads, int k_sel) {
 bool block_attn_grid_fits(int batch, int rows_total, int heads, int kv_heads, int max_seqlen_k,
                           int k_sel) {
   const long long nb = (max_seqlen_k + kBlock - 1) / kBlock;
-  const long long nc = (max_seqlen_k + kScanRows - 1) / kScanRows;
+  const long long nc = (max_seqlen_k + kChunkRows - 1) / kChunkRows;
   // every grid dimension holds fewer than 2^32 work-items, the partial states of
   // one row chunk span fewer than 2^32 bytes (32-bit offsets), and a
   // sequence's blocks fit the list kernel's table
   return (long long)batch * kv_heads * nb * nc * 256 <= UINT_MAX &&
          (long long)rows_total * heads * 16 <= UINT_MAX &&
-         (long long)kScanRows * k_sel * heads * kHeadDim * 2 <= UINT_MAX && nb <= kListMaxBlocks;
+         (long long)kChunkRows * k_sel * heads * kHeadDim * 2 <= UINT_MAX && nb <= kListMaxBlocks;
 }
 
 hipError_t launch_block_attn(const void* q, const void* k, const void* v, const int* indices,
@@ -928,7 +928,7 @@ hipError_t launch_block_attn(const void* q, const void* k, const void* v, const 
     return hipErrorInvalidValue;
   const int G = heads / kv_heads;
   const int nb_max = (max_seqlen_k + kBlock - 1) / kBlock;
-  const int n_chunk = (max_seqlen_k + kScanRows - 1) / kScanRows;
+  const int n_chunk = (max_seqlen_k + kChunkRows - 1) / kChunkRows;
   const unsigned n_wg = unsigned(batch) * kv_heads * n_chunk * nb_max;
   char* w = static_cast<char*>(ws);
   bf16_t* po = reinterpret_cast<bf16_t*>(w);
@@ -965,7 +965,7 @@ hipError_t launch_block_dq(const SelectedBwdArgs& a, hipStream_t s) {
       !block_attn_grid_fits(a.batch, a.rows_total, a.heads, a.kv_heads, a.max_seqlen_k, a.k_sel))
     return hipErrorInvalidValue;
   const int G = a.heads / a.kv_heads;
-  const int n_chunk = (a.max_seqlen_k + kScanRows - 1) / kScanRows;
+  const int n_chunk = (a.max_seqlen_k + kChunkRows - 1) / kChunkRows;
   const unsigned n_wg = unsigned(a.batch) * a.kv_heads * n_chunk * a.nb_max;
   uint16_t* lcode;
   int2* lhead;

@@ -88,12 +88,19 @@ typedef uint4 KeyFrag[2][4];
 // LDS staging of one workgroup's tiles, double-buffered.  Key rows are 256 B
 // with their sixteen 16-byte chunks XOR-swizzled by the row's low four bits,
 // so the 16 rows one A operand reads hit distinct banks (padding the rows
-// instead measured bank conflicts on these reads).  Value rows are padded to
-// 80 B and hold the tile's 32 keys in k-slot order (keys 4r..4r+3 then
-// 16+4r..16+4r+3 at places 8r .. 8r+7), so each value operand is one 16-byte
-// read.
+// instead measured bank conflicts on these reads).  Value rows are 64 B (one
+// dim, the tile's 32 keys) in k-slot order: chunk r holds keys 4r..4r+3 then
+// 16+4r..16+4r+3, so each value operand is one 16-byte read, and chunk r of
+// row d sits at place r ^ ((d >> 1) & 3).  Measured on gfx950 (bank-conflict
+// counters over each access pattern alone), that swizzle keeps both the
+// operand reads (16 rows, one chunk each) and the 8-byte staging writes
+// conflict-free; rows padded to 80 B instead made every operand read take
+// two passes.
 constexpr int kKRow = kHeadDim;  // bf16 per staged key row (16-byte chunks XOR-swizzled by row)
-constexpr int kVRow = 32 + 8;        // bf16 per staged value row (one dim, 32 keys)
+constexpr int kVRow = 32;        // bf16 per staged value row (4 chunks, swizzled by row)
+__device__ __forceinline__ int val_place(int row, int chunk) {
+  return row * kVRow + 8 * (chunk ^ ((row >> 1) & 3));
+}
 struct TileLds {
   bf16_t k[2][32 * kKRow];
   bf16_t v[2][kHeadDim * kVRow];
@@ -133,12 +140,12 @@ __device__ __forceinline__ void stash_tile(TileLds& T, int buf, const TileRegs<T
     const int c = tid + THREADS * u;
     *reinterpret_cast<uint4*>(&T.k[buf][(c >> 4) * kKRow + 8 * ((c & 15) ^ ((c >> 4) & 15))]) = r.k[u];
     if constexpr (WITH_V) {
-      // keys 8kc .. 8kc+3 go to places p, keys 8kc+4 .. 8kc+7 to p + 8
-      const int kc = c & 3;
-      const int p = kc < 2 ? 16 * kc : 16 * (kc - 2) + 4;
-      bf16_t* row = &T.v[buf][(c >> 2) * kVRow];
-      *reinterpret_cast<uint2*>(row + p) = make_uint2(r.v[u].x, r.v[u].y);
-      *reinterpret_cast<uint2*>(row + p + 8) = make_uint2(r.v[u].z, r.v[u].w);
+      // keys 8kc .. 8kc+3 go to chunk r, keys 8kc+4 .. 8kc+7 to chunk r + 1,
+      // both in the chunks' first half (kc < 2) or second half
+      const int kc = c & 3, row = c >> 2;
+      const int ch = kc < 2 ? 2 * kc : 2 * (kc - 2), half = kc < 2 ? 0 : 4;
+      *reinterpret_cast<uint2*>(&T.v[buf][val_place(row, ch) + half]) = make_uint2(r.v[u].x, r.v[u].y);
+      *reinterpret_cast<uint2*>(&T.v[buf][val_place(row, ch + 1) + half]) = make_uint2(r.v[u].z, r.v[u].w);
     }
   }
 }
@@ -155,7 +162,7 @@ __device__ __forceinline__ void read_keys(const TileLds& T, int buf, KeyFrag& ka
 // ValFrag entry n of a staged value tile (vs: one buffer of TileLds::v).
 __device__ __forceinline__ uint4 read_val(const bf16_t* vs, int n) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, r4 = lane >> 4;
-  return *reinterpret_cast<const uint4*>(&vs[(16 * n + c16) * kVRow + 8 * r4]);
+  return *reinterpret_cast<const uint4*>(&vs[val_place(16 * n + c16, r4)]);
 }
 
 // Tile loop of a workgroup over keys first .. last (first a multiple of 32;

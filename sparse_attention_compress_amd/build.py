@@ -26,6 +26,15 @@ COMMON = [
     "-Wall", "-Wno-unused-function",
 ]
 
+# Per-source additions.  The prefill kernels are bound by vector-ALU issue:
+# MFMA results go straight to VGPRs (no copies out of AGPRs), and with NaNs
+# left out of the float model (these kernels produce none from finite inputs)
+# and the IEEE mode bit off, float max needs no canonicalising instruction
+# before it.
+EXTRA = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
+
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
@@ -33,7 +42,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

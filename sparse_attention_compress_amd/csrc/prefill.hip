@@ -338,7 +338,8 @@ __device__ __forceinline__ WaveRows wave_rows(const int* __restrict__ cu_q,
 // PROBS = true:  o_cmp, natural-log lse, and the group's block scores.
 // vct: the compressed values transposed ([batch][kv][128][ldv]).
 template <int G, bool PROBS, int TPW, int GT>
-__global__ __launch_bounds__(GT / TPW * kWave) void compressed_prefill_kernel(
+__global__ __launch_bounds__(GT / TPW * kWave)
+__attribute__((amdgpu_waves_per_eu(PROBS ? 1 : 3))) void compressed_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vct,
     int ldv, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
     const int* __restrict__ cu_c, int kv_heads, float scale_log2, float* __restrict__ lse2,
@@ -377,6 +378,12 @@ __global__ __launch_bounds__(GT / TPW * kWave) void compressed_prefill_kernel(
   const int cmax = max(nv_wg - 1, 0);
 
   if constexpr (!PROBS) {
+    // Each lane keeps its own running maximum and sum over the windows it
+    // holds (no cross-lane step per tile); the four lane rows of a head are
+    // combined once at the end.  The maximum is raised only when a score
+    // passes it by kLazy (log2 domain), so the terms stay below 2^kLazy and
+    // most tiles skip the rescale (a branch the whole wave takes or skips).
+    constexpr float kLazy = 8.f;
     float m_run[kTpw], l_run[kTpw];
 #pragma unroll
     for (int j = 0; j < kTpw; ++j) {
@@ -401,26 +408,29 @@ __global__ __launch_bounds__(GT / TPW * kWave) void compressed_prefill_kernel(
           for (int e = 0; e < 8; ++e)
             if (w0 + 16 * (e >> 2) + 4 * r4 + (e & 3) >= nvis[j]) sv[e] = -INFINITY;
         }
-        float mx = sv[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-        mx = rows_max(mx) * scale_log2;
-        if (mx > m_run[j]) {
-          l_run[j] *= fast_exp2(m_run[j] - mx);
-          m_run[j] = mx;
+        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx *= scale_log2;
+        const bool raise = mx > m_run[j] + kLazy;  // also the lane's first window
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          if (raise) {
+            l_run[j] *= fast_exp2(m_run[j] - mx);
+            m_run[j] = mx;
+          }
         }
-        if (m_run[j] != -INFINITY) {  // the same in every lane: all heads see the same windows
+        // a lane with no window yet has only masked scores: its terms are 0
+        const float mref = m_run[j] == -INFINITY ? 0.f : m_run[j];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) l_run[j] += fast_exp2(fmaf(sv[e], scale_log2, -m_run[j]));
-        }
+        for (int e = 0; e < 8; ++e) l_run[j] += fast_exp2(fmaf(sv[e], scale_log2, -mref));
       }
     };
     lds_tile_loop<false, kThreads>(T, kb, rs, vt, ldv, 0, nv_wg - 1, cmax, active, process);
 #pragma unroll
     for (int j = 0; j < kTpw; ++j) {
-      const float l = rows_sum(l_run[j]);
+      const float m = rows_max(m_run[j]);
+      const float l = m == -INFINITY ? 0.f : rows_sum(l_run[j] * fast_exp2(m_run[j] - m));
       if (j < R.n && r4 == 0 && c16 < G)
-        lse2[head0[j] + c16] = l > 0.f ? m_run[j] + __log2f(l) : -INFINITY;
+        lse2[head0[j] + c16] = l > 0.f ? m + __log2f(l) : -INFINITY;
     }
   } else {
     float lh[kTpw], carry[kTpw];

@@ -59,12 +59,22 @@ constexpr int kThreads = 256;
 constexpr int rows_per_chunk(int mode) { return mode == kBwdCompressed ? 2048 : 512; }
 
 // Unpadded 256-byte rows whose sixteen 16-byte chunks are XOR-swizzled by
-// swz(row) = 2 (row % 8) + (row / 8) % 2.  The row reads of the 16x16x32 A
-// operands (16 rows, the same chunk of each) and the transposing reads below
-// (16 lanes: 4 rows x 32 contiguous bytes; 32 lanes: 8 rows) both then fall on
-// distinct banks.  tile_at: the element offset of logical chunk c of a row.
+// swz(row) = 2 (row % 8) + (row / 8) % 2.  The transposing reads below
+// (16 lanes: 4 rows x 32 contiguous bytes) and the staging writes are then
+// conflict-free, and so are the row reads of the 16x16x32 operands (16 rows,
+// one chunk each) in the chunk order kslot gives.  tile_at: the element
+// offset of logical chunk c of a row.
 __device__ __forceinline__ int swz(int row) { return 2 * (row & 7) + ((row >> 3) & 1); }
 __device__ __forceinline__ int tile_at(int row, int c) { return row * kHeadDim + 8 * (c ^ swz(row)); }
+
+// The dims a lane feeds to MFMA step i of a 128-dim contraction (16x16x32:
+// lane row r4 supplies k-slots 8 r4 .. 8 r4 + 7): the 16-byte chunk
+// 4 i + kslot(r4), the two bits of r4 swapped.  Both operands of a product
+// take the same chunk, so the sum is unchanged; with the swizzle above this
+// order keeps the staged-row reads (16 rows, one chunk each) off each other's
+// banks, which the plain order 4 i + r4 does not on gfx950 (two passes per
+// read, measured with bank-conflict counters over the access pattern alone).
+__device__ __forceinline__ int kslot(int r4) { return ((r4 & 1) << 1) | (r4 >> 1); }
 
 // The 16x16x16 A operand of X^T for dims 16 n .. 16 n + 15 and rows r0 .. r0 + 15
 // of a swizzled row tile X (query vectors or keys): lane (c16, r4) gets
@@ -170,8 +180,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
   uint4 kb[4], vb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    kb[i] = ld16(krow + 32 * i + 8 * r4);
-    vb[i] = ld16(vrow + 32 * i + 8 * r4);
+    kb[i] = ld16(krow + 32 * i + 8 * kslot(r4));
+    vb[i] = ld16(vrow + 32 * i + 8 * kslot(r4));
   }
   f32x4_t acck[8], accv[8];
 #pragma unroll
@@ -214,8 +224,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
     f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s = mfma32(*reinterpret_cast<const uint4*>(&Tc.q[tile_at(c16, 4 * i + r4)]), kb[i], s);
-      dp = mfma32(*reinterpret_cast<const uint4*>(&Tc.d[tile_at(c16, 4 * i + r4)]), vb[i], dp);
+      s = mfma32(*reinterpret_cast<const uint4*>(&Tc.q[tile_at(c16, 4 * i + kslot(r4))]), kb[i], s);
+      dp = mfma32(*reinterpret_cast<const uint4*>(&Tc.d[tile_at(c16, 4 * i + kslot(r4))]), vb[i], dp);
     }
     float p[4], ds[4];
 #pragma unroll
@@ -301,8 +311,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
   uint4 qb[4], db[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    qb[i] = col_ok ? ld16(q + hrow * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
-    db[i] = col_ok ? ld16(dout + hrow * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+    qb[i] = col_ok ? ld16(q + hrow * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
+    db[i] = col_ok ? ld16(dout + hrow * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
   }
   const float lse2 = col_ok ? lse[hrow] * kLog2e : 0.f;
   const float dlt = col_ok ? delta[hrow] : 0.f;
@@ -357,8 +367,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
       f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        st = mfma32(*reinterpret_cast<const uint4*>(&S.k[tile_at(16 * sl + c16, 4 * i + r4)]), qb[i], st);
-        dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[tile_at(16 * sl + c16, 4 * i + r4)]), db[i], dpt);
+        st = mfma32(*reinterpret_cast<const uint4*>(&S.k[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), qb[i], st);
+        dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), db[i], dpt);
       }
       float dst[4];
 #pragma unroll
@@ -427,8 +437,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
   uint4 qb[4], db[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    qb[i] = col_ok ? ld16(q + hq * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
-    db[i] = col_ok ? ld16(dout + hq * kHeadDim + 32 * i + 8 * r4) : make_uint4(0u, 0u, 0u, 0u);
+    qb[i] = col_ok ? ld16(q + hq * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
+    db[i] = col_ok ? ld16(dout + hq * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
   }
   const float lse2 = col_ok ? lse[hq] * kLog2e : 0.f;
   const float dlt = col_ok ? delta[hq] : 0.f;
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
     const int kv_ = min(kBlock * id + 16 * wave + c16, t);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      pv[i] = ld16(v + size_t(kstart + kv_) * rs + size_t(g) * kHeadDim + 32 * i + 8 * r4);
+      pv[i] = ld16(v + size_t(kstart + kv_) * rs + size_t(g) * kHeadDim + 32 * i + 8 * kslot(r4));
   };
   if (nv > 0) fetch(ids_s[0]);
   for (int p = 0; p < nv; ++p) {
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_sel_mfma_kernel(
     f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st = mfma32(*reinterpret_cast<const uint4*>(&Ks[tile_at(16 * wave + c16, 4 * i + r4)]), qb[i], st);
+      st = mfma32(*reinterpret_cast<const uint4*>(&Ks[tile_at(16 * wave + c16, 4 * i + kslot(r4))]), qb[i], st);
       dpt = mfma32(vc[i], db[i], dpt);
     }
     float ds[4];

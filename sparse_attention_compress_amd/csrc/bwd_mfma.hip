@@ -126,6 +126,44 @@ struct QTileRegs {
   int t;
 };
 
+// A query tile staged by direct-to-LDS loads (global_load_lds: lane i of a
+// wave writes its 16 (or 4) bytes at the wave's LDS base + 16 i (4 i)), for
+// the branches whose rows are consecutive: q and dO rows in the same swizzled
+// layout as QTileLds (each lane loads the logical chunk that lands at its
+// place), and the natural-log normalisers and deltas of the 16 query vectors
+// (lanes 16..63 repeat them).  A ring of kQRing slots keeps kQRing - 1 tiles
+// in flight without holding them in registers.
+struct QSlot {
+  bf16_t q[16 * kHeadDim];
+  bf16_t d[16 * kHeadDim];
+  float lse[kWave];
+  float delta[kWave];
+};
+constexpr int kQRing = 4;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void lds_load16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
+}
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, the other counters
+// left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Runs f(cur, nxt) with the two slots declared non-aliasing, so the compiler
+// does not order the reads of the current slot behind the loads into the next
+// one (the loop's explicit waits order them against earlier loads).
+template <typename T, typename F>
+__device__ __forceinline__ void with_slots(const T* __restrict__ cur, T* __restrict__ nxt, F&& f) {
+  f(cur, nxt);
+}
+
 __device__ __forceinline__ void stash_qtile(QTileLds& T, const QTileRegs& r) {
   const int tid = threadIdx.x, v = tid >> 4, c = tid & 15;
   *reinterpret_cast<uint4*>(&T.q[tile_at(v, c)]) = r.q;
@@ -148,7 +186,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
     const int* __restrict__ cu_kv, int window, int accumulate, int heads, int kv_heads,
     int nb_max, float scale_log2, float scale, float* __restrict__ dk, float* __restrict__ dv) {
   constexpr int kRowsPerTile = 16 / G;
-  __shared__ QTileLds T[2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
   const int slot = blockIdx.x, chunk = blockIdx.y;
@@ -190,61 +227,121 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
     accv[dt] = {0.f, 0.f, 0.f, 0.f};
   }
 
-  // query tile `e0`: rows entry(e0) .. entry(e0 + 16/G - 1), G heads each
-  auto fetch = [&](int e0, QTileRegs& r) {
-    const int qv = tid >> 4, c = tid & 15;
-    const int e = e0 + qv / G;
-    const bool ok = e < e_end;
-    const int2 rt = entry(min(e, e_end - 1));
-    const size_t hrow = size_t(rt.x) * heads + size_t(g) * G + (qv % G);
-    r.q = ok ? ld16(q + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-    r.d = ok ? ld16(dout + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-    if (tid < 16) {  // the scalars of query vector tid
-      const int es = e0 + tid / G;
-      const bool oks = es < e_end;
-      const int2 rs_ = entry(min(es, e_end - 1));
-      const size_t hs = size_t(rs_.x) * heads + size_t(g) * G + (tid % G);
-      r.lse2 = oks ? lse[hs] * kLog2e : 0.f;
-      r.delta = oks ? delta[hs] : 0.f;
-      r.t = oks ? rs_.y : -1;
-    }
-  };
-
-  const int n_tiles = (e_end - e_begin + kRowsPerTile - 1) / kRowsPerTile;
-  QTileRegs R;
-  if (n_tiles > 0) {
-    fetch(e_begin, R);
-    stash_qtile(T[0], R);
-  }
-  __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const QTileLds& Tc = T[it & 1];
-    if (it + 1 < n_tiles) fetch(e_begin + (it + 1) * kRowsPerTile, R);
+  // One query tile against the wave's 16 keys: tq, td the staged q and dO rows,
+  // scal(qv, t, lse2, delta) the position and scalars of query vector qv.
+  auto compute = [&](const bf16_t* tq, const bf16_t* td, auto&& scal) {
     // S = Q K^T and dP = dO V^T: (query 4 r4 + e, key c16)
     f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s = mfma32(*reinterpret_cast<const uint4*>(&Tc.q[tile_at(c16, 4 * i + kslot(r4))]), kb[i], s);
-      dp = mfma32(*reinterpret_cast<const uint4*>(&Tc.d[tile_at(c16, 4 * i + kslot(r4))]), vb[i], dp);
+      s = mfma32(*reinterpret_cast<const uint4*>(&tq[tile_at(c16, 4 * i + kslot(r4))]), kb[i], s);
+      dp = mfma32(*reinterpret_cast<const uint4*>(&td[tile_at(c16, 4 * i + kslot(r4))]), vb[i], dp);
     }
     float p[4], ds[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int qv = 4 * r4 + e;
-      const bool ok = key_ok && key_visible<MODE>(key, Tc.t[qv], len, window) && Tc.t[qv] >= 0;
-      p[e] = ok ? fast_exp2(s[e] * scale_log2 - Tc.lse2[qv]) : 0.f;
-      ds[e] = p[e] * (dp[e] - Tc.delta[qv]);
+      int tq_;
+      float lse2, dl;
+      scal(4 * r4 + e, tq_, lse2, dl);
+      const bool ok = key_ok && tq_ >= 0 && key_visible<MODE>(key, tq_, len, window);
+      p[e] = ok ? fast_exp2(s[e] * scale_log2 - lse2) : 0.f;
+      ds[e] = p[e] * (dp[e] - dl);
     }
     const uint2 pb = pack4(p), dsb = pack4(ds);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint2 dta = read_tr(Tc.d, 0, dt);
-      const uint2 qta = read_tr(Tc.q, 0, dt);
+      const uint2 dta = read_tr(td, 0, dt);
+      const uint2 qta = read_tr(tq, 0, dt);
       accv[dt] = mfma16(dta, pb, accv[dt]);
       acck[dt] = mfma16(qta, dsb, acck[dt]);
     }
-    if (it + 1 < n_tiles) stash_qtile(T[(it + 1) & 1], R);
+  };
+  const int n_tiles = (e_end - e_begin + kRowsPerTile - 1) / kRowsPerTile;
+
+  if constexpr (MODE == kBwdSelected) {
+    // rows from the block's list: register-staged tiles, one in flight
+    __shared__ QTileLds T[2];
+    // query tile `e0`: rows entry(e0) .. entry(e0 + 16/G - 1), G heads each
+    auto fetch = [&](int e0, QTileRegs& r) {
+      const int qv = tid >> 4, c = tid & 15;
+      const int e = e0 + qv / G;
+      const bool ok = e < e_end;
+      const int2 rt = entry(min(e, e_end - 1));
+      const size_t hrow = size_t(rt.x) * heads + size_t(g) * G + (qv % G);
+      r.q = ok ? ld16(q + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+      r.d = ok ? ld16(dout + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+      if (tid < 16) {  // the scalars of query vector tid
+        const int es = e0 + tid / G;
+        const bool oks = es < e_end;
+        const int2 rs_ = entry(min(es, e_end - 1));
+        const size_t hs = size_t(rs_.x) * heads + size_t(g) * G + (tid % G);
+        r.lse2 = oks ? lse[hs] * kLog2e : 0.f;
+        r.delta = oks ? delta[hs] : 0.f;
+        r.t = oks ? rs_.y : -1;
+      }
+    };
+    QTileRegs R;
+    if (n_tiles > 0) {
+      fetch(e_begin, R);
+      stash_qtile(T[0], R);
+    }
     __syncthreads();
+    for (int it = 0; it < n_tiles; ++it) {
+      const QTileLds& Tc = T[it & 1];
+      if (it + 1 < n_tiles) fetch(e_begin + (it + 1) * kRowsPerTile, R);
+      compute(Tc.q, Tc.d, [&](int qv, int& t, float& lse2, float& dl) {
+        t = Tc.t[qv];
+        lse2 = Tc.lse2[qv];
+        dl = Tc.delta[qv];
+      });
+      if (it + 1 < n_tiles) stash_qtile(T[(it + 1) & 1], R);
+      __syncthreads();
+    }
+  } else {
+    // consecutive rows (row_lo + e, position t_lo + e): tiles loaded straight
+    // into a ring of LDS slots, kQRing - 1 in flight.  Every wave issues 2
+    // loads per tile (waves 0 and 1 one more, for the scalars), also for the
+    // tiles past the last (they repeat it into a slot no one reads), so the
+    // count of loads issued after a tile's is fixed and the waits are exact.
+    __shared__ QSlot ring[kQRing];
+    auto issue = [&](int tile, QSlot* slot) {
+      const int e0 = e_begin + min(tile, n_tiles - 1) * kRowsPerTile;
+      const int v = 4 * wave + (lane >> 4);  // the query vector whose row part this lane loads
+      const int e = min(e0 + v / G, e_end - 1);
+      const size_t hrow = size_t(row_lo + e) * heads + size_t(g) * G + (v % G);
+      const size_t src = hrow * kHeadDim + 8 * ((lane & 15) ^ swz(v));
+      lds_load16(q + src, slot->q + 4 * kHeadDim * wave);
+      lds_load16(dout + src, slot->d + 4 * kHeadDim * wave);
+      if (wave < 2) {
+        const int qv = lane & 15;
+        const int es = min(e0 + qv / G, e_end - 1);
+        const size_t hs = size_t(row_lo + es) * heads + size_t(g) * G + (qv % G);
+        lds_load4(wave == 0 ? static_cast<const void*>(lse + hs) : static_cast<const void*>(delta + hs),
+                  wave == 0 ? static_cast<void*>(slot->lse) : static_cast<void*>(slot->delta));
+      }
+    };
+    if (n_tiles > 0) {
+#pragma unroll
+      for (int t = 0; t < kQRing - 1; ++t) issue(t, &ring[t]);
+    }
+    for (int it = 0; it < n_tiles; ++it) {
+      // tile it has landed once at most the later tiles' loads are outstanding
+      if (wave < 2) wait_vm<3 * (kQRing - 2)>();
+      else wait_vm<2 * (kQRing - 2)>();
+      __builtin_amdgcn_s_barrier();  // every wave's part of tile it is in; slot it - 1 is free
+      with_slots(&ring[it % kQRing], &ring[(it + kQRing - 1) % kQRing],
+                 [&](const QSlot* cur, QSlot* nxt) {
+        issue(it + kQRing - 1, nxt);
+        const int e0 = e_begin + it * kRowsPerTile;
+        compute(cur->q, cur->d, [&](int qv, int& t, float& lse2, float& dl) {
+          const int e = e0 + qv / G;
+          t = e < e_end ? t_lo + e : -1;
+          lse2 = cur->lse[qv] * kLog2e;
+          dl = cur->delta[qv];
+        });
+      });
+    }
+    wait_vm<0>();  // no load into LDS still in flight when the workgroup ends
   }
 
   // lane (c16, r4) holds dims 16 dt + 4 r4 .. +3 of key c16 of the wave's slice

@@ -107,32 +107,13 @@ __device__ __forceinline__ uint2 pack4(const float x[4]) {
   return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
-// One staged query tile: 16 query vectors' q and dO rows (swizzled rows; the
-// transposed operands are read from them with read_tr), with their log2
-// normalisers, deltas and positions (-1: no query vector in that slot).
-struct QTileLds {
-  bf16_t q[16 * kHeadDim];
-  bf16_t d[16 * kHeadDim];
-  float lse2[16];
-  float delta[16];
-  int t[16];
-};
-
-// A query tile in flight: thread tid holds 16-byte chunk (query vector tid / 16,
-// dims 8 (tid % 16) .. +7) of q and of dO; threads 0..15 its vector's scalars.
-struct QTileRegs {
-  uint4 q, d;
-  float lse2, delta;
-  int t;
-};
-
-// A query tile staged by direct-to-LDS loads (global_load_lds: lane i of a
-// wave writes its 16 (or 4) bytes at the wave's LDS base + 16 i (4 i)), for
-// the branches whose rows are consecutive: q and dO rows in the same swizzled
-// layout as QTileLds (each lane loads the logical chunk that lands at its
-// place), and the natural-log normalisers and deltas of the 16 query vectors
-// (lanes 16..63 repeat them).  A ring of kQRing slots keeps kQRing - 1 tiles
-// in flight without holding them in registers.
+// One query tile (16 query vectors) staged by direct-to-LDS loads
+// (global_load_lds: lane i of a wave writes its 16 (or 4) bytes at the wave's
+// LDS base + 16 i (4 i)): q and dO rows as swizzled rows (each lane loads the
+// logical chunk that lands at its place; the transposed operands are read
+// from them with read_tr), and the natural-log normalisers and deltas of the
+// 16 query vectors (lanes 16..63 repeat them).  A ring of kQRing slots keeps
+// kQRing - 1 tiles in flight without holding them in registers.
 struct QSlot {
   bf16_t q[16 * kHeadDim];
   bf16_t d[16 * kHeadDim];
@@ -156,24 +137,20 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-// Runs f(cur, nxt) with the two slots declared non-aliasing, so the compiler
-// does not order the reads of the current slot behind the loads into the next
-// one (the loop's explicit waits order them against earlier loads).
-template <typename T, typename F>
-__device__ __forceinline__ void with_slots(const T* __restrict__ cur, T* __restrict__ nxt, F&& f) {
-  f(cur, nxt);
+// Runs f on the given LDS regions declared non-aliasing, so the compiler does
+// not order the reads of one (the current slot, the row list) behind the loads
+// still in flight into another (the loop's explicit waits order them against
+// earlier loads).  Every LDS read in the ring's loop goes through one of these.
+template <typename A, typename B, typename F>
+__device__ __forceinline__ void with_noalias(A* __restrict__ a, B* __restrict__ b, F&& f) {
+  f(a, b);
+}
+template <typename A, typename B, typename C, typename F>
+__device__ __forceinline__ void with_noalias(A* __restrict__ a, B* __restrict__ b, C* __restrict__ c,
+                                             F&& f) {
+  f(a, b, c);
 }
 
-__device__ __forceinline__ void stash_qtile(QTileLds& T, const QTileRegs& r) {
-  const int tid = threadIdx.x, v = tid >> 4, c = tid & 15;
-  *reinterpret_cast<uint4*>(&T.q[tile_at(v, c)]) = r.q;
-  *reinterpret_cast<uint4*>(&T.d[tile_at(v, c)]) = r.d;
-  if (tid < 16) {
-    T.lse2[tid] = r.lse2;
-    T.delta[tid] = r.delta;
-    T.t[tid] = r.t;
-  }
-}
 
 // dK, dV of one (sequence, KV head, 64-key block) over one chunk of the rows
 // that see it.  Grid: (slot, chunk).
@@ -203,10 +180,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
   if (n == 0 && (accumulate & 2)) return;  // nothing to add
   const int e_end = min(n, e_begin + kRowsPerChunk);
   const int first = MODE == kBwdSelected ? off[slot] : 0;
-  auto entry = [&](int e) {
-    if constexpr (MODE == kBwdSelected) return list[first + e];
-    else return make_int2(row_lo + e, t_lo + e);
-  };
+
 
   // this wave's 16 keys as B operands: key c16 of the slice, dims 32i + 8 r4 .. +8
   const size_t rs = size_t(kv_heads) * kHeadDim;
@@ -258,91 +232,71 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
   };
   const int n_tiles = (e_end - e_begin + kRowsPerTile - 1) / kRowsPerTile;
 
+  // Query tiles go straight from memory into a ring of LDS slots, kQRing - 1
+  // in flight.  Every wave issues 2 loads per tile (waves 0 and 1 one more,
+  // for the scalars), also for the tiles past the last (they repeat it into a
+  // slot no one reads), so the count of loads issued after a tile's is fixed
+  // and the waits are exact.  The selected branch's rows come from the block's
+  // list: the chunk's entries are loaded into LDS first, so no tile's
+  // addresses wait on a load still in the ring's queue.
+  // (Plain loads and LDS writes: a load into LDS outside the ring would make
+  // the compiler order every later LDS read behind the ring's loads.)
+  constexpr int kListChunk = MODE == kBwdSelected ? kRowsPerChunk : 1;
+  __shared__ int2 ents[kListChunk];
   if constexpr (MODE == kBwdSelected) {
-    // rows from the block's list: register-staged tiles, one in flight
-    __shared__ QTileLds T[2];
-    // query tile `e0`: rows entry(e0) .. entry(e0 + 16/G - 1), G heads each
-    auto fetch = [&](int e0, QTileRegs& r) {
-      const int qv = tid >> 4, c = tid & 15;
-      const int e = e0 + qv / G;
-      const bool ok = e < e_end;
-      const int2 rt = entry(min(e, e_end - 1));
-      const size_t hrow = size_t(rt.x) * heads + size_t(g) * G + (qv % G);
-      r.q = ok ? ld16(q + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-      r.d = ok ? ld16(dout + hrow * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-      if (tid < 16) {  // the scalars of query vector tid
-        const int es = e0 + tid / G;
-        const bool oks = es < e_end;
-        const int2 rs_ = entry(min(es, e_end - 1));
-        const size_t hs = size_t(rs_.x) * heads + size_t(g) * G + (tid % G);
-        r.lse2 = oks ? lse[hs] * kLog2e : 0.f;
-        r.delta = oks ? delta[hs] : 0.f;
-        r.t = oks ? rs_.y : -1;
-      }
-    };
-    QTileRegs R;
-    if (n_tiles > 0) {
-      fetch(e_begin, R);
-      stash_qtile(T[0], R);
+#pragma unroll
+    for (int u = 0; u < kListChunk / kThreads; ++u) {
+      const int e = e_begin + kThreads * u + tid;
+      if (e < e_end) ents[kThreads * u + tid] = list[first + e];
     }
     __syncthreads();
-    for (int it = 0; it < n_tiles; ++it) {
-      const QTileLds& Tc = T[it & 1];
-      if (it + 1 < n_tiles) fetch(e_begin + (it + 1) * kRowsPerTile, R);
-      compute(Tc.q, Tc.d, [&](int qv, int& t, float& lse2, float& dl) {
-        t = Tc.t[qv];
-        lse2 = Tc.lse2[qv];
-        dl = Tc.delta[qv];
-      });
-      if (it + 1 < n_tiles) stash_qtile(T[(it + 1) & 1], R);
-      __syncthreads();
-    }
-  } else {
-    // consecutive rows (row_lo + e, position t_lo + e): tiles loaded straight
-    // into a ring of LDS slots, kQRing - 1 in flight.  Every wave issues 2
-    // loads per tile (waves 0 and 1 one more, for the scalars), also for the
-    // tiles past the last (they repeat it into a slot no one reads), so the
-    // count of loads issued after a tile's is fixed and the waits are exact.
-    __shared__ QSlot ring[kQRing];
-    auto issue = [&](int tile, QSlot* slot) {
-      const int e0 = e_begin + min(tile, n_tiles - 1) * kRowsPerTile;
-      const int v = 4 * wave + (lane >> 4);  // the query vector whose row part this lane loads
-      const int e = min(e0 + v / G, e_end - 1);
-      const size_t hrow = size_t(row_lo + e) * heads + size_t(g) * G + (v % G);
-      const size_t src = hrow * kHeadDim + 8 * ((lane & 15) ^ swz(v));
-      lds_load16(q + src, slot->q + 4 * kHeadDim * wave);
-      lds_load16(dout + src, slot->d + 4 * kHeadDim * wave);
-      if (wave < 2) {
-        const int qv = lane & 15;
-        const int es = min(e0 + qv / G, e_end - 1);
-        const size_t hs = size_t(row_lo + es) * heads + size_t(g) * G + (qv % G);
-        lds_load4(wave == 0 ? static_cast<const void*>(lse + hs) : static_cast<const void*>(delta + hs),
-                  wave == 0 ? static_cast<void*>(slot->lse) : static_cast<void*>(slot->delta));
-      }
-    };
-    if (n_tiles > 0) {
-#pragma unroll
-      for (int t = 0; t < kQRing - 1; ++t) issue(t, &ring[t]);
-    }
-    for (int it = 0; it < n_tiles; ++it) {
-      // tile it has landed once at most the later tiles' loads are outstanding
-      if (wave < 2) wait_vm<3 * (kQRing - 2)>();
-      else wait_vm<2 * (kQRing - 2)>();
-      __builtin_amdgcn_s_barrier();  // every wave's part of tile it is in; slot it - 1 is free
-      with_slots(&ring[it % kQRing], &ring[(it + kQRing - 1) % kQRing],
-                 [&](const QSlot* cur, QSlot* nxt) {
-        issue(it + kQRing - 1, nxt);
-        const int e0 = e_begin + it * kRowsPerTile;
-        compute(cur->q, cur->d, [&](int qv, int& t, float& lse2, float& dl) {
-          const int e = e0 + qv / G;
-          t = e < e_end ? t_lo + e : -1;
-          lse2 = cur->lse[qv] * kLog2e;
-          dl = cur->delta[qv];
-        });
-      });
-    }
-    wait_vm<0>();  // no load into LDS still in flight when the workgroup ends
   }
+  // row and position of entry e of the chunk (ent: the staged list)
+  auto row_at = [&](const int2* ent, int e) {
+    if constexpr (MODE == kBwdSelected) return ent[e - e_begin];
+    else return make_int2(row_lo + e, t_lo + e);
+  };
+  __shared__ QSlot ring[kQRing];
+  auto issue = [&](const int2* ent, int tile, QSlot* slot) {
+    const int e0 = e_begin + min(tile, n_tiles - 1) * kRowsPerTile;
+    const int v = 4 * wave + (lane >> 4);  // the query vector whose row part this lane loads
+    const int2 rt = row_at(ent, min(e0 + v / G, e_end - 1));
+    const size_t hrow = size_t(rt.x) * heads + size_t(g) * G + (v % G);
+    const size_t src = hrow * kHeadDim + 8 * ((lane & 15) ^ swz(v));
+    lds_load16(q + src, slot->q + 4 * kHeadDim * wave);
+    lds_load16(dout + src, slot->d + 4 * kHeadDim * wave);
+    if (wave < 2) {
+      const int qv = lane & 15;
+      const int2 rs_ = row_at(ent, min(e0 + qv / G, e_end - 1));
+      const size_t hs = size_t(rs_.x) * heads + size_t(g) * G + (qv % G);
+      lds_load4(wave == 0 ? static_cast<const void*>(lse + hs) : static_cast<const void*>(delta + hs),
+                wave == 0 ? static_cast<void*>(slot->lse) : static_cast<void*>(slot->delta));
+    }
+  };
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int t = 0; t < kQRing - 1; ++t)
+      with_noalias(static_cast<const int2*>(ents), &ring[t],
+                   [&](const int2* ent, QSlot* nxt) { issue(ent, t, nxt); });
+  }
+  for (int it = 0; it < n_tiles; ++it) {
+    // tile it has landed once at most the later tiles' loads are outstanding
+    if (wave < 2) wait_vm<3 * (kQRing - 2)>();
+    else wait_vm<2 * (kQRing - 2)>();
+    __builtin_amdgcn_s_barrier();  // every wave's part of tile it is in; slot it - 1 is free
+    with_noalias(static_cast<const QSlot*>(&ring[it % kQRing]), &ring[(it + kQRing - 1) % kQRing],
+                 static_cast<const int2*>(ents), [&](const QSlot* cur, QSlot* nxt, const int2* ent) {
+      issue(ent, it + kQRing - 1, nxt);
+      const int e0 = e_begin + it * kRowsPerTile;
+      compute(cur->q, cur->d, [&](int qv, int& t, float& lse2, float& dl) {
+        const int e = e0 + qv / G;
+        t = e < e_end ? row_at(ent, e).y : -1;
+        lse2 = cur->lse[qv] * kLog2e;
+        dl = cur->delta[qv];
+      });
+    });
+  }
+  wait_vm<0>();  // no load into LDS still in flight when the workgroup ends
 
   // lane (c16, r4) holds dims 16 dt + 4 r4 .. +3 of key c16 of the wave's slice
   if (!key_ok) return;

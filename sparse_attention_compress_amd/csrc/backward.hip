@@ -44,22 +44,36 @@ constexpr int kBwdThreads = 256;
 constexpr int kScanThreads = 1024;
 
 
-// delta[row, h] = dO . O (one wave per (row, head), two dims a lane); the
-// per-block row counts are cleared by the same launch.
+// Dot product of two rows' 8-dim pieces (bf16).
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
+  float s = bf16lo(a.x) * bf16lo(b.x);
+  s = fmaf(bf16hi(a.x), bf16hi(b.x), s);
+  s = fmaf(bf16lo(a.y), bf16lo(b.y), s);
+  s = fmaf(bf16hi(a.y), bf16hi(b.y), s);
+  s = fmaf(bf16lo(a.z), bf16lo(b.z), s);
+  s = fmaf(bf16hi(a.z), bf16hi(b.z), s);
+  s = fmaf(bf16lo(a.w), bf16lo(b.w), s);
+  return fmaf(bf16hi(a.w), bf16hi(b.w), s);
+}
+
+// (row, head) pairs per 256-thread workgroup of the row-dot kernels: 16 lanes
+// (one DPP row) a pair, 8 dims a lane, so every load is 16 bytes.
+constexpr int kRhPerWg = kBwdThreads / 16;
+
+// delta[row, h] = dO . O; the per-block row counts are cleared by the same
+// launch.
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(
     const bf16_t* __restrict__ out, const bf16_t* __restrict__ dout, size_t n_rh,
     float* __restrict__ delta, int* __restrict__ cnt, int n_slots) {
-  const int lane = threadIdx.x & 63;
-  const size_t rh = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int sub = threadIdx.x & 15;
+  const size_t rh = size_t(blockIdx.x) * kRhPerWg + (threadIdx.x >> 4);
   for (size_t i = size_t(blockIdx.x) * kBwdThreads + threadIdx.x; i < size_t(n_slots);
        i += size_t(gridDim.x) * kBwdThreads)
     cnt[i] = 0;
-  if (rh >= n_rh) return;
-  const uint32_t o = *reinterpret_cast<const uint32_t*>(out + rh * kHeadDim + 2 * lane);
-  const uint32_t d = *reinterpret_cast<const uint32_t*>(dout + rh * kHeadDim + 2 * lane);
-  float s = bf16lo(o) * bf16lo(d) + bf16hi(o) * bf16hi(d);
-  s = wave_reduce(s, OpSum());
-  if (lane == 0) delta[rh] = s;
+  if (rh >= n_rh) return;  // whole rows of 16 lanes
+  const size_t o = rh * kHeadDim + 8 * sub;
+  const float s = row_reduce(dot8_bf16(ld16(out + o), ld16(dout + o)), OpSum());
+  if (sub == 0) delta[rh] = s;
 }
 
 // One thread per (row, kv head, place): whether the place lists a block the
@@ -226,7 +240,7 @@ hipError_t launch_bwd_lists(const SelectedBwdArgs& a, hipStream_t s) {
   const size_t n_rh = size_t(a.rows_total) * a.heads;
   const int n_slots = a.batch * a.kv_heads * a.nb_max;
   const size_t n_place = MODE == kBwdSelected ? size_t(a.rows_total) * a.kv_heads * a.k_sel : 0;
-  const unsigned prep_grid = unsigned(std::max<size_t>((n_rh + 3) / 4, 1));
+  const unsigned prep_grid = unsigned(std::max<size_t>((n_rh + kRhPerWg - 1) / kRhPerWg, 1));
   hipError_t e = launch_kernel(kKindBwdLists, bwd_prep_kernel, dim3(prep_grid), dim3(kBwdThreads), s,
                                a.out, a.dout, n_rh, a.delta, a.cnt,
                                MODE == kBwdSelected ? n_slots : 0);
@@ -346,27 +360,26 @@ hipError_t launch_selected_bwd(const SelectedBwdArgs& a, hipStream_t s) {
 // Gradients of the gated sum o = g0 o_cmp + g1 o_sel + g2 o_win: each branch's
 // output gradient g_b dO (bf16) and dg_b = dO . o_b (fp32); one wave per (row,
 // head), two dims a lane.
-__global__ __launch_bounds__(256) void gates_bwd_kernel(
+__global__ __launch_bounds__(kBwdThreads) void gates_bwd_kernel(
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ o_cmp,
     const bf16_t* __restrict__ o_sel, const bf16_t* __restrict__ o_win,
     const float* __restrict__ gates, size_t n_rh, bf16_t* __restrict__ do_cmp,
     bf16_t* __restrict__ do_sel, bf16_t* __restrict__ do_win, float* __restrict__ d_gates) {
-  const int lane = threadIdx.x & 63;
-  const size_t rh = size_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (rh >= n_rh) return;
-  const size_t o = rh * kHeadDim + 2 * lane;
-  const uint32_t d = *reinterpret_cast<const uint32_t*>(dout + o);
-  const float d0 = bf16lo(d), d1 = bf16hi(d);
+  const int sub = threadIdx.x & 15;
+  const size_t rh = size_t(blockIdx.x) * kRhPerWg + (threadIdx.x >> 4);
+  if (rh >= n_rh) return;  // whole rows of 16 lanes
+  const size_t o = rh * kHeadDim + 8 * sub;
+  const uint4 d = ld16(dout + o);
   const bf16_t* ob[3] = {o_cmp, o_sel, o_win};
   bf16_t* db[3] = {do_cmp, do_sel, do_win};
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const float g = gates[rh * 3 + j];
-    const uint32_t x = *reinterpret_cast<const uint32_t*>(ob[j] + o);
-    float s = d0 * bf16lo(x) + d1 * bf16hi(x);
-    s = wave_reduce(s, OpSum());
-    *reinterpret_cast<uint32_t*>(db[j] + o) = pack_bf16x2(g * d0, g * d1);
-    if (lane == 0) d_gates[rh * 3 + j] = s;
+    const float s = row_reduce(dot8_bf16(d, ld16(ob[j] + o)), OpSum());
+    *reinterpret_cast<uint4*>(db[j] + o) =
+        make_uint4(pack_bf16x2(g * bf16lo(d.x), g * bf16hi(d.x)), pack_bf16x2(g * bf16lo(d.y), g * bf16hi(d.y)),
+                   pack_bf16x2(g * bf16lo(d.z), g * bf16hi(d.z)), pack_bf16x2(g * bf16lo(d.w), g * bf16hi(d.w)));
+    if (sub == 0) d_gates[rh * 3 + j] = s;
   }
 }
 
@@ -374,7 +387,7 @@ hipError_t launch_gates_bwd(const bf16_t* dout, const bf16_t* o_cmp, const bf16_
                             const bf16_t* o_win, const float* gates, size_t n_rh, bf16_t* do_cmp,
                             bf16_t* do_sel, bf16_t* do_win, float* d_gates, hipStream_t s) {
   if (n_rh == 0) return hipSuccess;
-  return launch_kernel(kKindBwdLists, gates_bwd_kernel, dim3(unsigned((n_rh + 3) / 4)), dim3(256),
+  return launch_kernel(kKindBwdLists, gates_bwd_kernel, dim3(unsigned((n_rh + kRhPerWg - 1) / kRhPerWg)), dim3(kBwdThreads),
                        s, dout, o_cmp, o_sel, o_win, gates, n_rh, do_cmp, do_sel, do_win, d_gates);
 }
 

@@ -26,13 +26,15 @@ COMMON = [
     "-Wall", "-Wno-unused-function",
 ]
 
-# Per-source additions.  The prefill kernels are bound by vector-ALU issue:
+# Per-source additions.  The prefill and backward kernels are bound by
+# vector-ALU issue as much as by the matrix cores:
 # MFMA results go straight to VGPRs (no copies out of AGPRs), and with NaNs
 # left out of the float model (these kernels produce none from finite inputs)
 # and the IEEE mode bit off, float max needs no canonicalising instruction
 # before it.
 EXTRA = {
     "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 
 

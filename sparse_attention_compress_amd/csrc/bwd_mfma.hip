@@ -155,7 +155,7 @@ __device__ __forceinline__ void with_noalias(A* __restrict__ a, B* __restrict__ 
 // dK, dV of one (sequence, KV head, 64-key block) over one chunk of the rows
 // that see it.  Grid: (slot, chunk).
 template <int G, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_dkdv_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, const int* __restrict__ cnt, const int* __restrict__ off,
@@ -279,22 +279,28 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_mfma_kernel(
       with_noalias(static_cast<const int2*>(ents), &ring[t],
                    [&](const int2* ent, QSlot* nxt) { issue(ent, t, nxt); });
   }
-  for (int it = 0; it < n_tiles; ++it) {
-    // tile it has landed once at most the later tiles' loads are outstanding
-    if (wave < 2) wait_vm<3 * (kQRing - 2)>();
-    else wait_vm<2 * (kQRing - 2)>();
-    __builtin_amdgcn_s_barrier();  // every wave's part of tile it is in; slot it - 1 is free
-    with_noalias(static_cast<const QSlot*>(&ring[it % kQRing]), &ring[(it + kQRing - 1) % kQRing],
-                 static_cast<const int2*>(ents), [&](const QSlot* cur, QSlot* nxt, const int2* ent) {
-      issue(ent, it + kQRing - 1, nxt);
-      const int e0 = e_begin + it * kRowsPerTile;
-      compute(cur->q, cur->d, [&](int qv, int& t, float& lse2, float& dl) {
-        const int e = e0 + qv / G;
-        t = e < e_end ? row_at(ent, e).y : -1;
-        lse2 = cur->lse[qv] * kLog2e;
-        dl = cur->delta[qv];
+  // unrolled by the ring size, so every slot's LDS offsets are constants
+  for (int it0 = 0; it0 < n_tiles; it0 += kQRing) {
+#pragma unroll
+    for (int r = 0; r < kQRing; ++r) {
+      const int it = it0 + r;
+      if (it >= n_tiles) break;
+      // tile it has landed once at most the later tiles' loads are outstanding
+      if (wave < 2) wait_vm<3 * (kQRing - 2)>();
+      else wait_vm<2 * (kQRing - 2)>();
+      __builtin_amdgcn_s_barrier();  // every wave's part of tile it is in; slot it - 1 is free
+      with_noalias(static_cast<const QSlot*>(&ring[r]), &ring[(r + kQRing - 1) % kQRing],
+                   static_cast<const int2*>(ents), [&](const QSlot* cur, QSlot* nxt, const int2* ent) {
+        issue(ent, it + kQRing - 1, nxt);
+        const int e0 = e_begin + it * kRowsPerTile;
+        compute(cur->q, cur->d, [&](int qv, int& t, float& lse2, float& dl) {
+          const int e = e0 + qv / G;
+          t = e < e_end ? row_at(ent, e).y : -1;
+          lse2 = cur->lse[qv] * kLog2e;
+          dl = cur->delta[qv];
+        });
       });
-    });
+    }
   }
   wait_vm<0>();  // no load into LDS still in flight when the workgroup ends
 

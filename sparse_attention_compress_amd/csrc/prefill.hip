@@ -27,6 +27,8 @@
 // finds each head's log2 normaliser, the second forms normalised
 // probabilities, which give o_cmp directly and, summed over the 16 head
 // columns with DPP, the window scores of the group.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -180,18 +182,23 @@ __device__ __forceinline__ void lds_tile_loop(TileLds& T, const bf16_t* __restri
   fetch_tile<WITH_V>(kb, rs, vt, ldv, first, kmax, r);
   stash_tile<WITH_V>(T, 0, r);
   __syncthreads();
-  int buf = 0;
-  for (int key0 = first; key0 <= last; key0 += 32) {
+  // one tile from buffer BUF (a constant, so its LDS offsets are immediates)
+  auto step = [&](int key0, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
     const bool more = key0 + 32 <= last;
     if (more) fetch_tile<WITH_V>(kb, rs, vt, ldv, key0 + 32, kmax, r);
     if (active) {
       KeyFrag ka;
-      read_keys(T, buf, ka);
-      process(key0, ka, static_cast<const bf16_t*>(T.v[buf]));  // values: read_val per fragment
+      read_keys(T, BUF, ka);
+      process(key0, ka, static_cast<const bf16_t*>(T.v[BUF]));  // values: read_val per fragment
     }
-    if (more) stash_tile<WITH_V>(T, buf ^ 1, r);
+    if (more) stash_tile<WITH_V>(T, BUF ^ 1, r);
     __syncthreads();
-    buf ^= 1;
+  };
+  for (int key0 = first; key0 <= last; key0 += 64) {
+    step(key0, std::integral_constant<int, 0>());
+    if (key0 + 32 > last) break;
+    step(key0 + 32, std::integral_constant<int, 1>());
   }
 }
 

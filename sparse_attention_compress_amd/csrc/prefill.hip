@@ -770,16 +770,21 @@ __global__ __launch_bounds__(kMaskThreads) __attribute__((amdgpu_waves_per_eu(2)
     fetch_tile<true>(kb, rs, vt, ldv, tile_key0(0), L - 1, r);
     stash_tile<true>(T, 0, r);
     __syncthreads();
-    int buf = 0;
-    for (int it = 0; it < n_tiles; ++it) {
+    // unrolled by the two buffers, so their LDS offsets are immediates
+    auto step = [&](int it, auto buf_c) {
+      constexpr int BUF = decltype(buf_c)::value;
       const bool more = it + 1 < n_tiles;
       if (more) fetch_tile<true>(kb, rs, vt, ldv, tile_key0(it + 1), L - 1, r);
       KeyFrag ka;
-      read_keys(T, buf, ka);
-      process(tile_key0(it), ka, static_cast<const bf16_t*>(T.v[buf]));
-      if (more) stash_tile<true>(T, buf ^ 1, r);
+      read_keys(T, BUF, ka);
+      process(tile_key0(it), ka, static_cast<const bf16_t*>(T.v[BUF]));
+      if (more) stash_tile<true>(T, BUF ^ 1, r);
       __syncthreads();
-      buf ^= 1;
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+      step(it, std::integral_constant<int, 0>());
+      if (it + 1 >= n_tiles) break;
+      step(it + 1, std::integral_constant<int, 1>());
     }
   }
 #pragma unroll

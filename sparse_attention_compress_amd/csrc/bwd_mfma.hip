@@ -202,8 +202,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 
   // One query tile against the wave's 16 keys: tq, td the staged q and dO rows,
-  // scal(qv, t, lse2, delta) the position and scalars of query vector qv.
-  auto compute = [&](const bf16_t* tq, const bf16_t* td, auto&& scal) {
+  // ls, dls the natural-log normalisers and deltas of its 16 query vectors,
+  // tpos(qv) the position of query vector qv (-1: none).
+  auto compute = [&](const bf16_t* tq, const bf16_t* td, const float* ls, const float* dls,
+                     auto&& tpos) {
     // S = Q K^T and dP = dO V^T: (query 4 r4 + e, key c16)
     f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -211,15 +213,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       s = mfma32(*reinterpret_cast<const uint4*>(&tq[tile_at(c16, 4 * i + kslot(r4))]), kb[i], s);
       dp = mfma32(*reinterpret_cast<const uint4*>(&td[tile_at(c16, 4 * i + kslot(r4))]), vb[i], dp);
     }
+    // the lane's four query vectors 4 r4 .. 4 r4 + 3: one 16-byte read each
+    const float4 l4 = *reinterpret_cast<const float4*>(ls + 4 * r4);
+    const float4 d4 = *reinterpret_cast<const float4*>(dls + 4 * r4);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
     float p[4], ds[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      int tq_;
-      float lse2, dl;
-      scal(4 * r4 + e, tq_, lse2, dl);
+      const int tq_ = tpos(4 * r4 + e);
       const bool ok = key_ok && tq_ >= 0 && key_visible<MODE>(key, tq_, len, window);
-      p[e] = ok ? fast_exp2(s[e] * scale_log2 - lse2) : 0.f;
-      ds[e] = p[e] * (dp[e] - dl);
+      // masked keys take exp2(-inf) = 0 (no branch around the exponential)
+      p[e] = fast_exp2(ok ? fmaf(s[e], scale, -lv[e]) * kLog2e : -INFINITY);
+      ds[e] = p[e] * (dp[e] - dv4[e]);
     }
     const uint2 pb = pack4(p), dsb = pack4(ds);
 #pragma unroll
@@ -293,11 +298,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                    static_cast<const int2*>(ents), [&](const QSlot* cur, QSlot* nxt, const int2* ent) {
         issue(ent, it + kQRing - 1, nxt);
         const int e0 = e_begin + it * kRowsPerTile;
-        compute(cur->q, cur->d, [&](int qv, int& t, float& lse2, float& dl) {
+        compute(cur->q, cur->d, cur->lse, cur->delta, [&](int qv) {
           const int e = e0 + qv / G;
-          t = e < e_end ? row_at(ent, e).y : -1;
-          lse2 = cur->lse[qv] * kLog2e;
-          dl = cur->delta[qv];
+          return e < e_end ? row_at(ent, e).y : -1;
         });
       });
     }

@@ -17,19 +17,21 @@
 //   positions for the window and compressed branches).  Each tile's q and dO
 //   rows are staged in LDS once for the four waves.
 //   Per tile and wave: S = Q K^T and dP = dO V^T on four v_mfma_f32_16x16x32_bf16
-//   each; their accumulators hold (query 4r4+e, key c16), which is exactly the B
-//   operand of the 16x16x16 tiles dV^T += dO^T P and dK^T += Q^T dS (contraction
-//   over the 16 query vectors), so P and dS go to the matrix cores as packed
-//   registers; dO^T and Q^T are read from the staged rows with gfx950's
-//   transposing LDS read (ds_read_b64_tr_b16).
+//   each; their accumulators hold (query 4r4+e, key c16), which is exactly half
+//   of a B operand of the tiles dV^T += dO^T P and dK^T += Q^T dS (contraction
+//   over query vectors), so P and dS go to the matrix cores as packed
+//   registers.  Tiles are taken two at a time, so those products run on
+//   16x16x32 tiles over both tiles' 32 query vectors (the 16x16x16 form does
+//   half the work per instruction); dO^T and Q^T are read from the staged rows
+//   with gfx950's transposing LDS read (ds_read_b64_tr_b16).
 // bwd_dq_mfma_kernel -- query-tile stationary (window and compressed branches).
 //   A workgroup holds four query tiles (one per wave; consecutive rows, which
 //   see nearly the same keys) with Q and dO in registers as B operands, and
 //   walks the 64-key blocks they see, each staged in LDS once for the four
 //   waves (K rows, V rows).  Per 16-key slice: S^T = K Q^T and
-//   dP^T = V dO^T (accumulators (key 4r4+e, query c16)), then dQ^T += K^T dS^T
-//   with dS^T packed straight into the B operand and K^T read transposed from
-//   the K rows.
+//   dP^T = V dO^T (accumulators (key 4r4+e, query c16)); per two slices
+//   dQ^T += K^T dS^T on 16x16x32 tiles, with dS^T packed straight into the B
+//   operand and K^T read transposed from the K rows.
 // bwd_dq_sel_mfma_kernel -- dq of the selected branch, one (row, KV head) per
 //   workgroup: the G heads are the tile's columns (columns past G masked), each
 //   listed block is staged in LDS once (K rows), wave w takes its keys
@@ -101,6 +103,9 @@ __device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
+// the 8 bf16 of a 16x16x32 operand from two 4-element halves: k slots
+// 8 r4 .. 8 r4 + 3 from a, 8 r4 + 4 .. 8 r4 + 7 from b
+__device__ __forceinline__ uint4 cat(uint2 a, uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
 __device__ __forceinline__ uint2 pack4(const float x[4]) {
   const bf16x2_t lo = {(__bf16)x[0], (__bf16)x[1]};
   const bf16x2_t hi = {(__bf16)x[2], (__bf16)x[3]};
@@ -112,15 +117,21 @@ __device__ __forceinline__ uint2 pack4(const float x[4]) {
 // LDS base + 16 i (4 i)): q and dO rows as swizzled rows (each lane loads the
 // logical chunk that lands at its place; the transposed operands are read
 // from them with read_tr), and the natural-log normalisers and deltas of the
-// 16 query vectors (lanes 16..63 repeat them).  A ring of kQRing slots keeps
-// kQRing - 1 tiles in flight without holding them in registers.
+// 16 query vectors (lanes 16..63 repeat them).  A ring of pairs of slots keeps
+// all but one pair in flight without holding them in registers.
 struct QSlot {
   bf16_t q[16 * kHeadDim];
   bf16_t d[16 * kHeadDim];
   float lse[kWave];
   float delta[kWave];
 };
-constexpr int kQRing = 4;
+// two tiles consumed per step (their dV, dK products share 16x16x32 tiles)
+struct QPair {
+  QSlot t[2];
+};
+// pairs in the ring: three (52 KB), two for the selected branch (its staged
+// row list would push three workgroups' rings past a CU's 160 KB of LDS)
+constexpr int q_pairs(int mode) { return mode == kBwdSelected ? 2 : 3; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void lds_load16(const void* src, void* lds_wave_base) {
@@ -201,21 +212,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     accv[dt] = {0.f, 0.f, 0.f, 0.f};
   }
 
-  // One query tile against the wave's 16 keys: tq, td the staged q and dO rows,
-  // ls, dls the natural-log normalisers and deltas of its 16 query vectors,
-  // tpos(qv) the position of query vector qv (-1: none).
-  auto compute = [&](const bf16_t* tq, const bf16_t* td, const float* ls, const float* dls,
-                     auto&& tpos) {
-    // S = Q K^T and dP = dO V^T: (query 4 r4 + e, key c16)
+  // One query tile against the wave's 16 keys: S = Q K^T and dP = dO V^T, and
+  // from them P and dS packed as B operands (query 4 r4 + e, key c16).  sl the
+  // staged tile (q and dO rows, the natural-log normalisers and deltas of its
+  // 16 query vectors), tpos(qv) the position of query vector qv (-1: none).
+  auto scores = [&](const QSlot* sl, auto&& tpos, uint2& pb, uint2& dsb) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s = mfma32(*reinterpret_cast<const uint4*>(&tq[tile_at(c16, 4 * i + kslot(r4))]), kb[i], s);
-      dp = mfma32(*reinterpret_cast<const uint4*>(&td[tile_at(c16, 4 * i + kslot(r4))]), vb[i], dp);
+      s = mfma32(*reinterpret_cast<const uint4*>(&sl->q[tile_at(c16, 4 * i + kslot(r4))]), kb[i], s);
+      dp = mfma32(*reinterpret_cast<const uint4*>(&sl->d[tile_at(c16, 4 * i + kslot(r4))]), vb[i], dp);
     }
     // the lane's four query vectors 4 r4 .. 4 r4 + 3: one 16-byte read each
-    const float4 l4 = *reinterpret_cast<const float4*>(ls + 4 * r4);
-    const float4 d4 = *reinterpret_cast<const float4*>(dls + 4 * r4);
+    const float4 l4 = *reinterpret_cast<const float4*>(sl->lse + 4 * r4);
+    const float4 d4 = *reinterpret_cast<const float4*>(sl->delta + 4 * r4);
     const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
     float p[4], ds[4];
 #pragma unroll
@@ -226,21 +236,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       p[e] = fast_exp2(ok ? fmaf(s[e], scale, -lv[e]) * kLog2e : -INFINITY);
       ds[e] = p[e] * (dp[e] - dv4[e]);
     }
-    const uint2 pb = pack4(p), dsb = pack4(ds);
+    pb = pack4(p);
+    dsb = pack4(ds);
+  };
+  // Two query tiles x, y: dV^T += dO^T P and dK^T += Q^T dS over their 32 query
+  // vectors on 16x16x32 tiles; k slots 8 r4 + j hold query vector 4 r4 + j of x
+  // (j < 4) and 4 r4 + j - 4 of y (j >= 4) in both operands, dO^T and Q^T read
+  // from the staged rows with the transposing read.
+  auto compute2 = [&](const QSlot* x, const QSlot* y, auto&& tpos_x, auto&& tpos_y) {
+    uint2 px, dsx, py, dsy;
+    scores(x, tpos_x, px, dsx);
+    scores(y, tpos_y, py, dsy);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint2 dta = read_tr(td, 0, dt);
-      const uint2 qta = read_tr(tq, 0, dt);
-      accv[dt] = mfma16(dta, pb, accv[dt]);
-      acck[dt] = mfma16(qta, dsb, acck[dt]);
+      accv[dt] = mfma32(cat(read_tr(x->d, 0, dt), read_tr(y->d, 0, dt)), cat(px, py), accv[dt]);
+      acck[dt] = mfma32(cat(read_tr(x->q, 0, dt), read_tr(y->q, 0, dt)), cat(dsx, dsy), acck[dt]);
     }
   };
   const int n_tiles = (e_end - e_begin + kRowsPerTile - 1) / kRowsPerTile;
 
-  // Query tiles go straight from memory into a ring of LDS slots, kQRing - 1
-  // in flight.  Every wave issues 2 loads per tile (waves 0 and 1 one more,
-  // for the scalars), also for the tiles past the last (they repeat it into a
-  // slot no one reads), so the count of loads issued after a tile's is fixed
+  const int n_pairs = (n_tiles + 1) / 2;
+  constexpr int kQPairs = q_pairs(MODE);
+
+  // Query tiles go straight from memory into a ring of LDS slots, taken two at a
+  // time (a pair), kQPairs - 1 pairs in flight.  Every wave issues 2 loads per
+  // tile (waves 0 and 1 one more, for the scalars), also for the tiles past the
+  // last (they repeat it into a slot whose query vectors are all masked, or
+  // that no one reads), so the count of loads issued after a pair's is fixed
   // and the waits are exact.  The selected branch's rows come from the block's
   // list: the chunk's entries are loaded into LDS first, so no tile's
   // addresses wait on a load still in the ring's queue.
@@ -261,7 +283,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if constexpr (MODE == kBwdSelected) return ent[e - e_begin];
     else return make_int2(row_lo + e, t_lo + e);
   };
-  __shared__ QSlot ring[kQRing];
+  __shared__ QPair ring[kQPairs];
   auto issue = [&](const int2* ent, int tile, QSlot* slot) {
     const int e0 = e_begin + min(tile, n_tiles - 1) * kRowsPerTile;
     const int v = 4 * wave + (lane >> 4);  // the query vector whose row part this lane loads
@@ -278,30 +300,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 wave == 0 ? static_cast<void*>(slot->lse) : static_cast<void*>(slot->delta));
     }
   };
-  if (n_tiles > 0) {
+  auto issue_pair = [&](const int2* ent, int pr, QPair* slot) {
+    issue(ent, 2 * pr, &slot->t[0]);
+    issue(ent, 2 * pr + 1, &slot->t[1]);
+  };
+  if (n_pairs > 0) {
 #pragma unroll
-    for (int t = 0; t < kQRing - 1; ++t)
+    for (int t = 0; t < kQPairs - 1; ++t)
       with_noalias(static_cast<const int2*>(ents), &ring[t],
-                   [&](const int2* ent, QSlot* nxt) { issue(ent, t, nxt); });
+                   [&](const int2* ent, QPair* nxt) { issue_pair(ent, t, nxt); });
   }
   // unrolled by the ring size, so every slot's LDS offsets are constants
-  for (int it0 = 0; it0 < n_tiles; it0 += kQRing) {
+  for (int p0 = 0; p0 < n_pairs; p0 += kQPairs) {
 #pragma unroll
-    for (int r = 0; r < kQRing; ++r) {
-      const int it = it0 + r;
-      if (it >= n_tiles) break;
-      // tile it has landed once at most the later tiles' loads are outstanding
-      if (wave < 2) wait_vm<3 * (kQRing - 2)>();
-      else wait_vm<2 * (kQRing - 2)>();
-      __builtin_amdgcn_s_barrier();  // every wave's part of tile it is in; slot it - 1 is free
-      with_noalias(static_cast<const QSlot*>(&ring[r]), &ring[(r + kQRing - 1) % kQRing],
-                   static_cast<const int2*>(ents), [&](const QSlot* cur, QSlot* nxt, const int2* ent) {
-        issue(ent, it + kQRing - 1, nxt);
-        const int e0 = e_begin + it * kRowsPerTile;
-        compute(cur->q, cur->d, cur->lse, cur->delta, [&](int qv) {
-          const int e = e0 + qv / G;
-          return e < e_end ? row_at(ent, e).y : -1;
-        });
+    for (int r = 0; r < kQPairs; ++r) {
+      const int pr = p0 + r;
+      if (pr >= n_pairs) break;
+      // pair pr has landed once at most the later pairs' loads are outstanding
+      if (wave < 2) wait_vm<6 * (kQPairs - 2)>();
+      else wait_vm<4 * (kQPairs - 2)>();
+      __builtin_amdgcn_s_barrier();  // every wave's part of pair pr is in; pair pr - 1's slots are free
+      with_noalias(static_cast<const QPair*>(&ring[r]), &ring[(r + kQPairs - 1) % kQPairs],
+                   static_cast<const int2*>(ents), [&](const QPair* cur, QPair* nxt, const int2* ent) {
+        issue_pair(ent, pr + kQPairs - 1, nxt);
+        const int e0 = e_begin + 2 * pr * kRowsPerTile;
+        compute2(&cur->t[0], &cur->t[1],
+                 [&](int qv) {
+                   const int e = e0 + qv / G;
+                   return e < e_end ? row_at(ent, e).y : -1;
+                 },
+                 [&](int qv) {
+                   const int e = e0 + kRowsPerTile + qv / G;
+                   return e < e_end ? row_at(ent, e).y : -1;
+                 });
       });
     }
   }
@@ -422,27 +453,35 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
     __syncthreads();
     if (blk + 1 <= bhi) fetch(blk + 1);
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      // S^T = K Q^T and dP^T = V dO^T: (key 16 sl + 4 r4 + e, query c16)
-      f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < 2; ++sp) {
+      uint2 dsb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st = mfma32(*reinterpret_cast<const uint4*>(&S.k[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), qb[i], st);
-        dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), db[i], dpt);
-      }
-      float dst[4];
+      for (int h = 0; h < 2; ++h) {
+        const int sl = 2 * sp + h;
+        // S^T = K Q^T and dP^T = V dO^T: (key 16 sl + 4 r4 + e, query c16)
+        f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = kBlock * blk + 16 * sl + 4 * r4 + e;
-        const bool ok = t >= 0 && kk < klen && key_visible<MODE>(kk, t, klen, window);
-        const float p = ok ? fast_exp2(st[e] * scale_log2 - lse2) : 0.f;
-        dst[e] = p * (dpt[e] - dlt);
-      }
-      const uint2 dsb = pack4(dst);
+        for (int i = 0; i < 4; ++i) {
+          st = mfma32(*reinterpret_cast<const uint4*>(&S.k[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), qb[i], st);
+          dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), db[i], dpt);
+        }
+        float dst[4];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        acc[dt] = mfma16(read_tr(S.k, 16 * sl, dt), dsb, acc[dt]);
+        for (int e = 0; e < 4; ++e) {
+          const int kk = kBlock * blk + 16 * sl + 4 * r4 + e;
+          const bool ok = t >= 0 && kk < klen && key_visible<MODE>(kk, t, klen, window);
+          const float p = ok ? fast_exp2(st[e] * scale_log2 - lse2) : 0.f;
+          dst[e] = p * (dpt[e] - dlt);
+        }
+        dsb[h] = pack4(dst);
       }
+      // dQ^T += K^T dS^T over the two slices' 32 keys on one 16x16x32 tile per
+      // 16 dims: k slots 8 r4 + j hold keys 32 sp + 4 r4 + j (j < 4) and
+      // 32 sp + 16 + 4 r4 + j - 4 (j >= 4) in both operands
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        acc[dt] = mfma32(cat(read_tr(S.k, 32 * sp, dt), read_tr(S.k, 32 * sp + 16, dt)),
+                         cat(dsb[0], dsb[1]), acc[dt]);
     }
   }
   // lane (c16, r4): dims 16 dt + 4 r4 .. +3 of query vector c16

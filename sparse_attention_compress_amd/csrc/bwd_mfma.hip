@@ -172,11 +172,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const float* __restrict__ delta, const int* __restrict__ cnt, const int* __restrict__ off,
     const int2* __restrict__ list, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
     const int* __restrict__ cu_kv, int window, int accumulate, int heads, int kv_heads,
-    int nb_max, float scale_log2, float scale, float* __restrict__ dk, float* __restrict__ dv) {
+    int nb_max, int n_bg, int n_chunk, float scale_log2, float scale, float* __restrict__ dk,
+    float* __restrict__ dv) {
   constexpr int kRowsPerTile = 16 / G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
-  const int slot = blockIdx.x, chunk = blockIdx.y;
+  int slot, chunk;
+  if constexpr (MODE == kBwdSelected) {
+    slot = blockIdx.x;
+    chunk = blockIdx.y;
+  } else {
+    // One-dimensional grid over groups (chunk, sequence, KV head) of nb_max key
+    // blocks.  Workgroups go to the 8 XCDs in launch order modulo 8; group q
+    // runs on XCD q % 8, which takes its groups in turn, so the key blocks that
+    // read one chunk's rows (the same rows, or overlapping ones for the window)
+    // share that XCD's L2, and the groups of later, longer chunks spread over
+    // all XCDs.  Groups past the last (the count rounded up to 8) are empty.
+    const int j = int(blockIdx.x) >> 3;
+    const int grp = (int(blockIdx.x) & 7) + 8 * (j / nb_max);
+    if (grp >= n_bg * n_chunk) return;  // uniform
+    chunk = grp / n_bg;
+    slot = j % nb_max + nb_max * (grp % n_bg);
+  }
   const int id = slot % nb_max;
   const int g = (slot / nb_max) % kv_heads;
   const int b = slot / (nb_max * kv_heads);
@@ -617,13 +634,19 @@ hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
   const float scale_log2 = a.scale * kLog2eHost;
   const int max_rows = MODE == kBwdWindow ? std::min(a.max_seqlen_k, kBlock + a.window - 1)
                                           : a.max_seqlen_k;
-  const unsigned n_chunk = unsigned((max_rows + rows_per_chunk(MODE) - 1) / rows_per_chunk(MODE));
-  hipError_t e = launch_kernel(kKindBwdKV, bwd_dkdv_mfma_kernel<G, MODE>,
-                               dim3(unsigned(n_slots), std::max(1u, n_chunk)), dim3(kThreads), s,
+  const int n_chunk = std::max(1, (max_rows + rows_per_chunk(MODE) - 1) / rows_per_chunk(MODE));
+  const int n_bg = a.batch * a.kv_heads;
+  // the window and compressed branches: groups of nb_max workgroups, their
+  // count rounded up to a multiple of 8 (one-dimensional grid)
+  const size_t n_grouped = (size_t(n_bg) * n_chunk + 7) / 8 * 8 * size_t(a.nb_max);
+  if (MODE != kBwdSelected && n_grouped > size_t(0x7fffffff)) return hipErrorInvalidValue;
+  const dim3 grid = MODE == kBwdSelected ? dim3(unsigned(n_slots), unsigned(n_chunk))
+                                         : dim3(unsigned(n_grouped));
+  hipError_t e = launch_kernel(kKindBwdKV, bwd_dkdv_mfma_kernel<G, MODE>, grid, dim3(kThreads), s,
                                a.q, a.k, a.v, a.dout, a.lse, static_cast<const float*>(a.delta),
                                static_cast<const int*>(a.cnt), static_cast<const int*>(a.off),
                                static_cast<const int2*>(a.list), a.cu_q, a.cu_k, a.cu_kv,
-                               a.window, a.accumulate, a.heads, a.kv_heads, a.nb_max, scale_log2,
+                               a.window, a.accumulate, a.heads, a.kv_heads, a.nb_max, n_bg, n_chunk, scale_log2,
                                a.scale, a.dk, a.dv);
   if (e != hipSuccess) return e;
   if (MODE == kBwdSelected && a.dq_part != nullptr) return launch_block_dq(a, s);

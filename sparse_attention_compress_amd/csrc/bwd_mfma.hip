@@ -178,16 +178,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
   int slot, chunk;
-  if constexpr (MODE == kBwdSelected) {
+  if constexpr (MODE != kBwdCompressed) {
     slot = blockIdx.x;
     chunk = blockIdx.y;
   } else {
     // One-dimensional grid over groups (chunk, sequence, KV head) of nb_max key
     // blocks.  Workgroups go to the 8 XCDs in launch order modulo 8; group q
     // runs on XCD q % 8, which takes its groups in turn, so the key blocks that
-    // read one chunk's rows (the same rows, or overlapping ones for the window)
-    // share that XCD's L2, and the groups of later, longer chunks spread over
-    // all XCDs.  Groups past the last (the count rounded up to 8) are empty.
+    // read one chunk's rows share that XCD's L2, and the groups of later,
+    // longer chunks spread over all XCDs.  Groups past the last (the count
+    // rounded up to 8) are empty.  (The window branch has too few groups, two
+    // chunks of very different lengths per sequence and KV head, to balance
+    // the XCDs this way.)
     const int j = int(blockIdx.x) >> 3;
     const int grp = (int(blockIdx.x) & 7) + 8 * (j / nb_max);
     if (grp >= n_bg * n_chunk) return;  // uniform
@@ -636,12 +638,12 @@ hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
                                           : a.max_seqlen_k;
   const int n_chunk = std::max(1, (max_rows + rows_per_chunk(MODE) - 1) / rows_per_chunk(MODE));
   const int n_bg = a.batch * a.kv_heads;
-  // the window and compressed branches: groups of nb_max workgroups, their
-  // count rounded up to a multiple of 8 (one-dimensional grid)
+  // the compressed branch: groups of nb_max workgroups, their count rounded up
+  // to a multiple of 8 (one-dimensional grid)
   const size_t n_grouped = (size_t(n_bg) * n_chunk + 7) / 8 * 8 * size_t(a.nb_max);
-  if (MODE != kBwdSelected && n_grouped > size_t(0x7fffffff)) return hipErrorInvalidValue;
-  const dim3 grid = MODE == kBwdSelected ? dim3(unsigned(n_slots), unsigned(n_chunk))
-                                         : dim3(unsigned(n_grouped));
+  if (MODE == kBwdCompressed && n_grouped > size_t(0x7fffffff)) return hipErrorInvalidValue;
+  const dim3 grid = MODE != kBwdCompressed ? dim3(unsigned(n_slots), unsigned(n_chunk))
+                                           : dim3(unsigned(n_grouped));
   hipError_t e = launch_kernel(kKindBwdKV, bwd_dkdv_mfma_kernel<G, MODE>, grid, dim3(kThreads), s,
                                a.q, a.k, a.v, a.dout, a.lse, static_cast<const float*>(a.delta),
                                static_cast<const int*>(a.cnt), static_cast<const int*>(a.off),

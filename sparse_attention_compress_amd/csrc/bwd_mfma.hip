@@ -25,8 +25,9 @@
 //   half the work per instruction); dO^T and Q^T are read from the staged rows
 //   with gfx950's transposing LDS read (ds_read_b64_tr_b16).
 // bwd_dq_mfma_kernel -- query-tile stationary (window and compressed branches).
-//   A workgroup holds four query tiles (one per wave; consecutive rows, which
-//   see nearly the same keys) with Q and dO in registers as B operands, and
+//   A workgroup holds eight query tiles (two per wave, so each operand read
+//   from LDS feeds two products; consecutive rows, which see nearly the same
+//   keys) with Q and dO in registers as B operands, and
 //   walks the 64-key blocks they see, each staged in LDS once for the four
 //   waves (K rows, V rows).  Per 16-key slice: S^T = K Q^T and
 //   dP^T = V dO^T (accumulators (key 4r4+e, query c16)); per two slices
@@ -391,8 +392,9 @@ struct KBlockLds {
   bf16_t v[64 * kHeadDim];
 };
 
-// dq of four query tiles of one (sequence, KV head): grid (row group, kv head,
-// sequence); the window and compressed key sets.
+// dq of eight query tiles of one (sequence, KV head), two per wave, so each
+// K and V operand read from LDS feeds both tiles' products: grid (row group,
+// kv head, sequence); the window and compressed key sets.
 template <int G, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -401,7 +403,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
     const int* __restrict__ cu_kv, int window, int accumulate, int heads, int kv_heads,
     float scale_log2, float scale, float* __restrict__ dq) {
   constexpr int kRowsPerTile = 16 / G;
-  constexpr int kRowsPerWg = 4 * kRowsPerTile;
+  constexpr int kTw = 2;  // query tiles per wave
+  constexpr int kRowsPerWg = 4 * kTw * kRowsPerTile;
   __shared__ KBlockLds S;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, r4 = lane >> 4;
@@ -413,22 +416,30 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
   if (rbase >= lq) return;  // uniform
   const int kstart = cu_kv[b], klen = cu_kv[b + 1] - kstart;
 
-  // this wave's query tile: column c16 = (row rbase + 16/G * wave + c16 / G, head c16 % G)
-  const int rr = rbase + kRowsPerTile * wave + c16 / G;
-  const bool col_ok = rr < lq;
-  const int t = col_ok ? rr + shift : -1;
-  const size_t hrow = size_t(q0 + min(rr, lq - 1)) * heads + size_t(g) * G + (c16 % G);
-  uint4 qb[4], db[4];
+  // this wave's query tiles u = 0, 1: column c16 = (row rbase + 16/G (2 wave + u)
+  // + c16 / G, head c16 % G)
+  int t[kTw];
+  bool col_ok[kTw];
+  size_t hrow[kTw];
+  uint4 qb[kTw][4], db[kTw][4];
+  float lse2[kTw], dlt[kTw];
+  f32x4_t acc[kTw][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    qb[i] = col_ok ? ld16(q + hrow * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
-    db[i] = col_ok ? ld16(dout + hrow * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
+  for (int u = 0; u < kTw; ++u) {
+    const int rr = rbase + kRowsPerTile * (kTw * wave + u) + c16 / G;
+    col_ok[u] = rr < lq;
+    t[u] = col_ok[u] ? rr + shift : -1;
+    hrow[u] = size_t(q0 + min(rr, lq - 1)) * heads + size_t(g) * G + (c16 % G);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qb[u][i] = col_ok[u] ? ld16(q + hrow[u] * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
+      db[u][i] = col_ok[u] ? ld16(dout + hrow[u] * kHeadDim + 32 * i + 8 * kslot(r4)) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    lse2[u] = col_ok[u] ? lse[hrow[u]] * kLog2e : 0.f;
+    dlt[u] = col_ok[u] ? delta[hrow[u]] : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[u][dt] = {0.f, 0.f, 0.f, 0.f};
   }
-  const float lse2 = col_ok ? lse[hrow] * kLog2e : 0.f;
-  const float dlt = col_ok ? delta[hrow] : 0.f;
-  f32x4_t acc[8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = {0.f, 0.f, 0.f, 0.f};
 
   // key blocks seen by the workgroup's rows
   const int t_first = rbase + shift;
@@ -473,48 +484,67 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
     if (blk + 1 <= bhi) fetch(blk + 1);
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp) {
-      uint2 dsb[2];
+      uint2 dsb[kTw][2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int sl = 2 * sp + h;
         // S^T = K Q^T and dP^T = V dO^T: (key 16 sl + 4 r4 + e, query c16)
-        f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t st[kTw], dpt[kTw];
+#pragma unroll
+        for (int u = 0; u < kTw; ++u) {
+          st[u] = {0.f, 0.f, 0.f, 0.f};
+          dpt[u] = {0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          st = mfma32(*reinterpret_cast<const uint4*>(&S.k[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), qb[i], st);
-          dpt = mfma32(*reinterpret_cast<const uint4*>(&S.v[tile_at(16 * sl + c16, 4 * i + kslot(r4))]), db[i], dpt);
-        }
-        float dst[4];
+          const uint4 ka = *reinterpret_cast<const uint4*>(&S.k[tile_at(16 * sl + c16, 4 * i + kslot(r4))]);
+          const uint4 va = *reinterpret_cast<const uint4*>(&S.v[tile_at(16 * sl + c16, 4 * i + kslot(r4))]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = kBlock * blk + 16 * sl + 4 * r4 + e;
-          const bool ok = t >= 0 && kk < klen && key_visible<MODE>(kk, t, klen, window);
-          const float p = ok ? fast_exp2(st[e] * scale_log2 - lse2) : 0.f;
-          dst[e] = p * (dpt[e] - dlt);
+          for (int u = 0; u < kTw; ++u) {
+            st[u] = mfma32(ka, qb[u][i], st[u]);
+            dpt[u] = mfma32(va, db[u][i], dpt[u]);
+          }
         }
-        dsb[h] = pack4(dst);
+#pragma unroll
+        for (int u = 0; u < kTw; ++u) {
+          float dst[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kk = kBlock * blk + 16 * sl + 4 * r4 + e;
+            const bool ok = t[u] >= 0 && kk < klen && key_visible<MODE>(kk, t[u], klen, window);
+            const float p = ok ? fast_exp2(st[u][e] * scale_log2 - lse2[u]) : 0.f;
+            dst[e] = p * (dpt[u][e] - dlt[u]);
+          }
+          dsb[u][h] = pack4(dst);
+        }
       }
       // dQ^T += K^T dS^T over the two slices' 32 keys on one 16x16x32 tile per
       // 16 dims: k slots 8 r4 + j hold keys 32 sp + 4 r4 + j (j < 4) and
       // 32 sp + 16 + 4 r4 + j - 4 (j >= 4) in both operands
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        acc[dt] = mfma32(cat(read_tr(S.k, 32 * sp, dt), read_tr(S.k, 32 * sp + 16, dt)),
-                         cat(dsb[0], dsb[1]), acc[dt]);
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint4 kt = cat(read_tr(S.k, 32 * sp, dt), read_tr(S.k, 32 * sp + 16, dt));
+#pragma unroll
+        for (int u = 0; u < kTw; ++u) acc[u][dt] = mfma32(kt, cat(dsb[u][0], dsb[u][1]), acc[u][dt]);
+      }
     }
   }
-  // lane (c16, r4): dims 16 dt + 4 r4 .. +3 of query vector c16
-  if (!col_ok) return;
-  float* out = dq + hrow * kHeadDim + 4 * r4;
+  // lane (c16, r4): dims 16 dt + 4 r4 .. +3 of query vector c16 of each tile
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    float4 x = make_float4(scale * acc[dt][0], scale * acc[dt][1], scale * acc[dt][2], scale * acc[dt][3]);
-    float4* po = reinterpret_cast<float4*>(out + 16 * dt);
-    if (accumulate & 1) {
-      const float4 a = *po;
-      x = make_float4(a.x + x.x, a.y + x.y, a.z + x.z, a.w + x.w);
+  for (int u = 0; u < kTw; ++u) {
+    if (!col_ok[u]) continue;
+    float* out = dq + hrow[u] * kHeadDim + 4 * r4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      float4 x = make_float4(scale * acc[u][dt][0], scale * acc[u][dt][1], scale * acc[u][dt][2],
+                             scale * acc[u][dt][3]);
+      float4* po = reinterpret_cast<float4*>(out + 16 * dt);
+      if (accumulate & 1) {
+        const float4 a = *po;
+        x = make_float4(a.x + x.x, a.y + x.y, a.z + x.z, a.w + x.w);
+      }
+      *po = x;
     }
-    *po = x;
   }
 }
 
@@ -658,7 +688,7 @@ hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
                          a.v, a.dout, a.lse, static_cast<const float*>(a.delta), a.indices,
                          a.k_sel, a.cu_q, a.cu_k, a.batch, a.accumulate, a.heads, a.kv_heads,
                          scale_log2, a.scale, a.dq);
-  constexpr int kRowsPerWg = 4 * (16 / G);
+  constexpr int kRowsPerWg = 8 * (16 / G);  // four waves of two query tiles
   const unsigned gx = unsigned((a.max_seqlen_k + kRowsPerWg - 1) / kRowsPerWg);
   return launch_kernel(kKindBwdQ, bwd_dq_mfma_kernel<G, MODE>,
                        dim3(std::max(1u, gx), unsigned(a.kv_heads), unsigned(a.batch)),

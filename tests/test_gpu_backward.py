@@ -93,7 +93,7 @@ def _compare(d, dq, dk, dv, tag):
 
 @pytest.mark.parametrize("H,H_kv,lengths", [(16, 2, [500, 900]), (16, 1, [300, 420]),
                                             (4, 4, [700, 90]), (8, 4, [500, 900]),
-                                            (8, 2, [300, 420])])
+                                            (8, 2, [300, 420]), (8, 2, [1500, 700])])
 @pytest.mark.parametrize("path", ["blocks", "rows"])
 def test_selected_bwd_matches_oracle(H, H_kv, lengths, path):
     """Every row of a ragged batch (several 64-token blocks and a ragged tail;

@@ -57,11 +57,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 // Rows of a key block's list one dk/dv workgroup takes: the chunks of one block
 // add their sums with fp32 atomics, so the compressed branch, whose blocks are
-// seen by nearly every later row, takes longer chunks (fewer atomics); 1024 for
-// the selected branch (256 and 2048 measured slower), 512 for the window.
-constexpr int rows_per_chunk(int mode) {
-  return mode == kBwdCompressed ? 2048 : mode == kBwdSelected ? 1024 : 512;
-}
+// seen by nearly every later row, takes longer chunks (fewer atomics); 1024
+// elsewhere (selected: 256 and 2048 measured slower; a window block's rows,
+// 64 + window - 1, then fit one chunk for windows up to 961).
+constexpr int rows_per_chunk(int mode) { return mode == kBwdCompressed ? 2048 : 1024; }
 
 // Unpadded 256-byte rows whose sixteen 16-byte chunks are XOR-swizzled by
 // swz(row) = 2 (row % 8) + (row / 8) % 2.  The transposing reads below

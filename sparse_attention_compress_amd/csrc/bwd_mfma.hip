@@ -25,9 +25,10 @@
 //   half the work per instruction); dO^T and Q^T are read from the staged rows
 //   with gfx950's transposing LDS read (ds_read_b64_tr_b16).
 // bwd_dq_mfma_kernel -- query-tile stationary (window and compressed branches).
-//   A workgroup holds eight query tiles (two per wave, so each operand read
-//   from LDS feeds two products; consecutive rows, which see nearly the same
-//   keys) with Q and dO in registers as B operands, and
+//   A workgroup holds eight query tiles for the compressed branch (two per
+//   wave, so each operand read from LDS feeds two products; four for the
+//   window; consecutive rows, which see nearly the same keys) with Q and dO in
+//   registers as B operands, and
 //   walks the 64-key blocks they see, each staged in LDS once for the four
 //   waves (K rows, V rows).  Per 16-key slice: S^T = K Q^T and
 //   dP^T = V dO^T (accumulators (key 4r4+e, query c16)); per two slices
@@ -393,9 +394,14 @@ struct KBlockLds {
   bf16_t v[64 * kHeadDim];
 };
 
-// dq of eight query tiles of one (sequence, KV head), two per wave, so each
-// K and V operand read from LDS feeds both tiles' products: grid (row group,
-// kv head, sequence); the window and compressed key sets.
+// query tiles per wave of the dq kernel: two for the compressed branch (each
+// operand read from LDS feeds both), one for the window (its short key ranges
+// leave less to share, and one tile keeps three waves per SIMD)
+constexpr int dq_tiles_per_wave(int mode) { return mode == kBwdWindow ? 1 : 2; }
+
+// dq of 4 dq_tiles_per_wave query tiles of one (sequence, KV head); with two
+// per wave each K and V operand read from LDS feeds both tiles' products:
+// grid (row group, kv head, sequence); the window and compressed key sets.
 template <int G, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -404,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(
     const int* __restrict__ cu_kv, int window, int accumulate, int heads, int kv_heads,
     float scale_log2, float scale, float* __restrict__ dq) {
   constexpr int kRowsPerTile = 16 / G;
-  constexpr int kTw = 2;  // query tiles per wave
+  constexpr int kTw = dq_tiles_per_wave(MODE);  // query tiles per wave
   constexpr int kRowsPerWg = 4 * kTw * kRowsPerTile;
   __shared__ KBlockLds S;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -689,7 +695,7 @@ hipError_t launch_mfma_g(const SelectedBwdArgs& a, hipStream_t s) {
                          a.v, a.dout, a.lse, static_cast<const float*>(a.delta), a.indices,
                          a.k_sel, a.cu_q, a.cu_k, a.batch, a.accumulate, a.heads, a.kv_heads,
                          scale_log2, a.scale, a.dq);
-  constexpr int kRowsPerWg = 8 * (16 / G);  // four waves of two query tiles
+  constexpr int kRowsPerWg = 4 * dq_tiles_per_wave(MODE) * (16 / G);
   const unsigned gx = unsigned((a.max_seqlen_k + kRowsPerWg - 1) / kRowsPerWg);
   return launch_kernel(kKindBwdQ, bwd_dq_mfma_kernel<G, MODE>,
                        dim3(std::max(1u, gx), unsigned(a.kv_heads), unsigned(a.batch)),
